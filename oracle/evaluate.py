@@ -1,0 +1,85 @@
+"""Op-by-op, unfused evaluation of a graph (oracle, test infrastructure only).
+
+Each op runs on its own, in the graph's (topological) order, and every
+intermediate is kept as an fp32 array.  Two things decide where values get
+rounded to a narrower type:
+
+* graph outputs are stored in their declared dtype;
+* a tensor listed in ``stored`` (an intermediate that crosses from one fused
+  group to another, or every intermediate when nothing is fused) is written
+  to memory in its declared dtype and read back, so later ops see the
+  rounded value.
+
+Inside a fused group the intermediates never leave the chip (DisCo section
+1; TVM "Operator Fusion", FuseTIR), so they stay fp32; that is the only
+difference between a fused and an unfused run.
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, Tuple
+
+import numpy as np
+
+from . import numerics, ops
+
+
+def norm_shape(shape: Tuple[int, ...]) -> Tuple[int, int]:
+    """Rank-1 [N] is the row vector [1, N]; rank 2 is kept."""
+    if len(shape) == 1:
+        return (1, int(shape[0]))
+    if len(shape) == 2:
+        return (int(shape[0]), int(shape[1]))
+    raise ValueError(f"rank {len(shape)} not supported")
+
+
+def broadcast_shape(shapes) -> Tuple[int, int]:
+    R = max(s[0] for s in shapes)
+    C = max(s[1] for s in shapes)
+    for r, c in shapes:
+        if r not in (1, R) or c not in (1, C):
+            raise ValueError(f"shapes {shapes} do not broadcast")
+    return (R, C)
+
+
+def result_shape(op: str, in_shapes) -> Tuple[int, int]:
+    if op in ("row_sum", "row_mean"):
+        return (in_shapes[0][0], 1)
+    return broadcast_shape(in_shapes)
+
+
+def evaluate(graph, inputs: Dict[int, np.ndarray],
+             stored: Iterable[int] = ()) -> Dict[int, np.ndarray]:
+    """fp32 value of every tensor, each shaped [R, C]."""
+    stored = set(stored)
+    vals: Dict[int, np.ndarray] = {}
+    for t in graph.inputs():
+        d = graph.tensors[t]
+        vals[t] = numerics.decode(inputs[t], d.dtype).reshape(norm_shape(d.shape))
+    for o in graph.ops:
+        args = [vals[i] for i in o.inputs]
+        want = result_shape(o.op, [a.shape for a in args])
+        d = graph.tensors[o.output]
+        if norm_shape(d.shape) != want:
+            raise ValueError(f"{o.op} -> {d.name}: declared {d.shape}, computes {want}")
+        r = ops.apply(o.op, args, o.imm)
+        r = np.broadcast_to(r, want).astype(np.float32)
+        if o.output in stored or d.role == "out":
+            r = numerics.round_to(r, d.dtype)
+        vals[o.output] = r
+    return vals
+
+
+def outputs(graph, vals: Dict[int, np.ndarray]) -> Dict[int, np.ndarray]:
+    """Graph outputs encoded in their declared dtype (bf16 as uint16 bits),
+    in the declared shape."""
+    res = {}
+    for t in graph.outputs():
+        d = graph.tensors[t]
+        res[t] = numerics.encode(vals[t], d.dtype).reshape(d.shape)
+    return res
+
+
+def run(graph, inputs: Dict[int, np.ndarray], stored: Iterable[int] = ()):
+    """Convenience: evaluate and return (all fp32 values, encoded outputs)."""
+    vals = evaluate(graph, inputs, stored)
+    return vals, outputs(graph, vals)

@@ -1,0 +1,250 @@
+"""Pattern annotation, post-dominators and the grouping rule (oracle, test
+infrastructure only).
+
+Follows Apache TVM, "Operator Fusion" (docs/arch/fusion.rst), in its order:
+
+1. Annotate (section "Operator Pattern Classification", the OpPatternKind
+   table): kElemWise 0 when every operand has the result's shape,
+   kBroadcast 1 when some operand is broadcast, kInjective 2 for copy,
+   kCommReduce 3 for the row reductions, kOpaque 8 when forced.  A group's
+   pattern is the max over its members (CombinePattern).
+2. Forward graph (section "Algorithm", step 1): one node per op, an edge
+   from an op to every op that reads its output.
+3. Post-dominators (step 2): here from their definition, not from the LCA
+   construction the page describes.  A virtual exit follows every node
+   whose output is a graph output or has no reader; pdom(exit) = {exit} and
+   pdom(n) = {n} u (intersection of pdom(s) over n's successors s).  The
+   immediate post-dominator is the strict post-dominator nearest to n.
+4. Fuse (step 3 and "Fusion rules"): three phases; in each, nodes in
+   topological order.  A node is skipped when it already shares a group
+   with its immediate post-dominator d, or has none.  Its group's pattern
+   picks the rule:
+     <= kBroadcast : every node strictly between n and d on any path is
+                     <= kInjective, and d's group is <= kCommReduce;
+     kInjective    : (phase 1 and later) everything on the paths and d's
+                     group are <= kInjective;
+     kCommReduce   : never initiates (reductions are sinks only);
+     kOpaque       : never fuses (a barrier).
+   Limits: at most 256 ops per group (kMaxFusedOps) and at most
+   MAX_GROUP_ARGS external tensors per group (the page names an argument
+   limit without its value; 16 is this build's reading).  CommitFuse puts
+   n, d and every node on a path between them into one group (union-find).
+
+Readings where the page is silent: the source's pattern is its group's
+pattern; path nodes are judged by their own pattern; a node whose output
+is a graph output has no post-dominator.
+
+Pinned in tests/test_oracle_partition.py: the page's add/exp/squeeze example
+and its diamond, the sink-only and barrier rules, the 256 limit, and the
+post-dominator sets against path enumeration on every small DAG.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Set
+
+from .evaluate import norm_shape
+
+K_ELEMWISE, K_BROADCAST, K_INJECTIVE, K_COMM_REDUCE = 0, 1, 2, 3
+K_OUT_EWISE_FUSABLE, K_TUPLE, K_OPAQUE = 4, 7, 8
+
+MAX_FUSED_OPS = 256
+MAX_GROUP_ARGS = 16
+
+
+def pattern(graph, i: int) -> int:
+    o = graph.ops[i]
+    if o.opaque:
+        return K_OPAQUE
+    if o.op in ("row_sum", "row_mean"):
+        return K_COMM_REDUCE
+    if o.op == "copy":
+        return K_INJECTIVE
+    out = norm_shape(graph.tensors[o.output].shape)
+    if any(norm_shape(graph.tensors[t].shape) != out for t in o.inputs):
+        return K_BROADCAST
+    return K_ELEMWISE
+
+
+def successors(graph) -> List[List[int]]:
+    readers: Dict[int, List[int]] = {}
+    for j, o in enumerate(graph.ops):
+        for t in set(o.inputs):
+            readers.setdefault(t, []).append(j)
+    succ = []
+    for i, o in enumerate(graph.ops):
+        succ.append(sorted(set(readers.get(o.output, []))))
+    return succ
+
+
+def exits_to_end(graph, i: int, succ) -> bool:
+    o = graph.ops[i]
+    return graph.tensors[o.output].role == "out" or not succ[i]
+
+
+def postdominator_sets(graph) -> List[Set[int]]:
+    """pdom(n) as sets of op indices; -1 stands for the virtual exit."""
+    n = len(graph.ops)
+    succ = successors(graph)
+    pd: List[Optional[Set[int]]] = [None] * n
+    for i in range(n - 1, -1, -1):           # readers come later in the order
+        sets = [pd[s] for s in succ[i]]
+        if exits_to_end(graph, i, succ):
+            sets.append({-1})
+        common = set.intersection(*sets)
+        pd[i] = {i} | common
+    return pd  # type: ignore[return-value]
+
+
+def immediate_postdominators(graph) -> List[Optional[int]]:
+    pd = postdominator_sets(graph)
+    ipd: List[Optional[int]] = []
+    for i, s in enumerate(pd):
+        strict = s - {i}
+        if strict == {-1}:
+            ipd.append(None)
+            continue
+        # the nearest strict post-dominator is the one every other strict
+        # post-dominator of n also post-dominates
+        cand = [d for d in strict if d != -1 and strict - {d} <= pd[d]]
+        assert len(cand) == 1, (i, strict)
+        ipd.append(cand[0])
+    return ipd
+
+
+def _reach(succ, start: int) -> Set[int]:
+    seen, stack = set(), [start]
+    while stack:
+        v = stack.pop()
+        for s in succ[v]:
+            if s not in seen:
+                seen.add(s)
+                stack.append(s)
+    return seen
+
+
+def _between(succ, pred, a: int, b: int) -> Set[int]:
+    """Nodes strictly between a and b on some path a -> b."""
+    fwd = _reach(succ, a)
+    back = _reach(pred, b)
+    return (fwd & back) - {a, b}
+
+
+class _UnionFind:
+    def __init__(self, n: int, pats: List[int]):
+        self.parent = list(range(n))
+        self.pat = list(pats)
+        self.size = [1] * n
+
+    def find(self, x: int) -> int:
+        while self.parent[x] != x:
+            x = self.parent[x]
+        return x
+
+    def union_into(self, x: int, root_target: int) -> None:
+        rx, rt = self.find(x), self.find(root_target)
+        if rx == rt:
+            return
+        self.parent[rx] = rt
+        self.pat[rt] = max(self.pat[rt], self.pat[rx])
+        self.size[rt] += self.size[rx]
+
+
+def _group_args(graph, members: Set[int]) -> int:
+    produced = {graph.ops[i].output for i in members}
+    ext = set()
+    for i in members:
+        for t in graph.ops[i].inputs:
+            if t not in produced:
+                ext.add(t)
+    for j, o in enumerate(graph.ops):
+        if j in members:
+            continue
+        for t in o.inputs:
+            if t in produced:
+                ext.add(t)
+    for t in produced:
+        if graph.tensors[t].role == "out":
+            ext.add(t)
+    return len(ext)
+
+
+def partition(graph, fuse: bool = True) -> List[List[int]]:
+    """Groups of op indices, each sorted, listed in an order that respects
+    the dependencies between groups."""
+    n = len(graph.ops)
+    pats = [pattern(graph, i) for i in range(n)]
+    uf = _UnionFind(n, pats)
+    if fuse and n:
+        succ = successors(graph)
+        pred: List[List[int]] = [[] for _ in range(n)]
+        for i, ss in enumerate(succ):
+            for s in ss:
+                pred[s].append(i)
+        ipd = immediate_postdominators(graph)
+        for phase in range(3):
+            for i in range(n):
+                d = ipd[i]
+                if d is None or uf.find(i) == uf.find(d):
+                    continue
+                src_pat = uf.pat[uf.find(i)]
+                sink_pat = uf.pat[uf.find(d)]
+                mid = _between(succ, pred, i, d)
+                if src_pat <= K_BROADCAST:
+                    ok = (all(pats[m] <= K_INJECTIVE for m in mid)
+                          and sink_pat <= K_COMM_REDUCE)
+                elif src_pat == K_INJECTIVE and phase >= 1:
+                    ok = (all(pats[m] <= K_INJECTIVE for m in mid)
+                          and sink_pat <= K_INJECTIVE)
+                else:
+                    ok = False
+                if not ok:
+                    continue
+                roots = {uf.find(v) for v in mid | {i, d}}
+                members = {v for v in range(n) if uf.find(v) in roots}
+                if len(members) > MAX_FUSED_OPS:
+                    continue
+                if _group_args(graph, members) > MAX_GROUP_ARGS:
+                    continue
+                for v in mid | {i}:
+                    uf.union_into(v, d)
+    groups: Dict[int, List[int]] = {}
+    for i in range(n):
+        groups.setdefault(uf.find(i), []).append(i)
+    return _order_groups(graph, list(groups.values()))
+
+
+def _order_groups(graph, groups: List[List[int]]) -> List[List[int]]:
+    owner = {}
+    for gi, g in enumerate(groups):
+        for i in g:
+            owner[graph.ops[i].output] = gi
+    deps = [set() for _ in groups]
+    for gi, g in enumerate(groups):
+        for i in g:
+            for t in graph.ops[i].inputs:
+                if t in owner and owner[t] != gi:
+                    deps[gi].add(owner[t])
+    order, done = [], set()
+    while len(order) < len(groups):
+        ready = [gi for gi in range(len(groups)) if gi not in done and deps[gi] <= done]
+        if not ready:
+            raise ValueError("groups depend on each other in a cycle")
+        gi = min(ready, key=lambda k: min(groups[k]))
+        order.append(gi)
+        done.add(gi)
+    return [sorted(groups[gi]) for gi in order]
+
+
+def stored_tensors(graph, groups: List[List[int]]) -> Set[int]:
+    """Intermediates written to memory: read by an op of another group."""
+    owner = {}
+    for gi, g in enumerate(groups):
+        for i in g:
+            owner[graph.ops[i].output] = gi
+    stored = set()
+    for gi, g in enumerate(groups):
+        for i in g:
+            for t in graph.ops[i].inputs:
+                if t in owner and owner[t] != gi:
+                    stored.add(t)
+    return stored

@@ -1,0 +1,192 @@
+"""Pins for the oracle's grouping: the page's worked example and diamond, the
+sink-only, barrier and size rules, and post-dominators checked against path
+enumeration on small DAGs (TVM "Operator Fusion", FuseOps)."""
+import itertools
+import json
+import os
+
+import numpy as np
+
+from oracle import partition as pt
+from workloads import configs
+from workloads.graph import Graph, OpDesc, TensorDesc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def graph_from_json(d) -> Graph:
+    g = Graph()
+    for t in d["tensors"]:
+        g.tensors.append(TensorDesc(t["name"], t["dtype"], tuple(t["shape"]), t["role"]))
+    for o in d["ops"]:
+        g.ops.append(OpDesc(o["op"], tuple(o["inputs"]), o["output"], float(o.get("imm", 0.0)),
+                            bool(o.get("opaque", False))))
+    return g
+
+
+def as_sets(groups):
+    return sorted(sorted(x) for x in groups)
+
+
+def test_tvm_worked_example_is_one_group():
+    with open(os.path.join(GOLDEN, "tvm_add_exp_squeeze.json")) as f:
+        d = json.load(f)
+    g = graph_from_json(d)
+    assert as_sets(pt.partition(g)) == d["expected_groups"]
+    assert [pt.pattern(g, i) for i in range(3)] == [pt.K_ELEMWISE, pt.K_ELEMWISE, pt.K_INJECTIVE]
+
+
+def test_diamond_with_op_head_is_one_group_and_its_ipdom_is_the_join():
+    g = configs.c3_graph(8, 64, head_op=True)
+    ipd = pt.immediate_postdominators(g)
+    assert ipd[0] == 4              # head -> the 3-input add where the branches meet
+    assert ipd[1] == ipd[2] == ipd[3] == 4
+    assert ipd[4] == 5 and ipd[5] is None
+    assert as_sets(pt.partition(g)) == [[0, 1, 2, 3, 4, 5]]
+
+
+def test_config_groups():
+    assert as_sets(pt.partition(configs.c1_graph(4, 8))) == [[0, 1, 2]]
+    g2 = configs.c2_graph(4, 8)
+    assert as_sets(pt.partition(g2)) == [[0, 1, 2]]
+    assert pt.pattern(g2, 0) == pt.K_BROADCAST
+    assert as_sets(pt.partition(configs.c3_graph(4, 8))) == [[0, 1, 2, 3, 4]]
+    ln = configs.layernorm_graph(4, 8)
+    groups = pt.partition(ln)
+    # G1 mean; G2 x-mean, square, mean; G3 the normalise chain with rstd hoisted in
+    assert as_sets(groups) == [[0], [1, 2, 3], [4, 5, 6, 7, 8, 9, 10]]
+    stored = pt.stored_tensors(ln, groups)
+    assert {ln.tensors[t].name for t in stored} == {"mean", "var"}
+    assert as_sets(pt.partition(configs.gelu_graph(4, 8))) == [[0, 1]]
+    assert as_sets(pt.partition(configs.dropout_graph(4, 8))) == [[0, 1]]
+
+
+def test_unfused_mode_is_one_op_per_group():
+    ln = configs.layernorm_graph(4, 8)
+    assert as_sets(pt.partition(ln, fuse=False)) == [[i] for i in range(11)]
+
+
+def test_reduction_never_initiates():
+    g = Graph()
+    x = g.input("x", "f32", (4, 8))
+    r = g.op("row_sum", [x], "r", "f32", (4, 1))
+    g.op("mul_imm", [r], "y", "f32", (4, 1), role="out", imm=2.0)
+    assert as_sets(pt.partition(g)) == [[0], [1]]
+
+
+def test_opaque_is_a_barrier():
+    g = Graph()
+    x = g.input("x", "f32", (4, 8))
+    a = g.op("exp", [x], "a", "f32", (4, 8))
+    b = g.op("neg", [a], "b", "f32", (4, 8), opaque=True)
+    g.op("relu", [b], "c", "f32", (4, 8), role="out")
+    assert as_sets(pt.partition(g)) == [[0], [1], [2]]
+    # an opaque node on one branch of a diamond blocks the whole diamond
+    g = Graph()
+    x = g.input("x", "f32", (4, 8))
+    h = g.op("exp", [x], "h", "f32", (4, 8))
+    p = g.op("neg", [h], "p", "f32", (4, 8), opaque=True)
+    q = g.op("relu", [h], "q", "f32", (4, 8))
+    g.op("add", [p, q], "y", "f32", (4, 8), role="out")
+    assert as_sets(pt.partition(g)) == [[0], [1], [2, 3]]
+
+
+def test_long_chain_splits_at_256_ops():
+    g = Graph()
+    v = g.input("x", "f32", (2, 8))
+    for i in range(300):
+        v = g.op("neg", [v], f"t{i}", "f32", (2, 8), role="out" if i == 299 else "tmp")
+    sizes = [len(x) for x in pt.partition(g)]
+    assert sizes == [256, 44]
+
+
+def test_argument_limit_splits_groups():
+    g = Graph()
+    xs = [g.input(f"x{i}", "f32", (2, 8)) for i in range(21)]
+    v = xs[0]
+    for i in range(20):
+        v = g.op("add", [v, xs[i + 1]], f"s{i}", "f32", (2, 8), role="out" if i == 19 else "tmp")
+    # a group of m chained adds reads m+1 inputs and writes one output: m <= 14
+    assert [len(x) for x in pt.partition(g)] == [14, 6]
+
+
+def test_graph_output_in_the_middle_cuts_post_dominance():
+    g = Graph()
+    x = g.input("x", "f32", (4, 8))
+    a = g.op("exp", [x], "a", "f32", (4, 8))
+    b = g.op("neg", [a], "b", "f32", (4, 8), role="out")
+    g.op("relu", [b], "c", "f32", (4, 8), role="out")
+    assert pt.immediate_postdominators(g) == [1, None, None]
+    assert as_sets(pt.partition(g)) == [[0, 1], [2]]
+
+
+# ---------------------------------------------------- brute-force post-dominators
+def _paths_to_exit(g, succ, i):
+    out = []
+
+    def walk(v, path):
+        if pt.exits_to_end(g, v, succ):
+            out.append(path + [v])
+        for s in succ[v]:
+            walk(s, path + [v])
+    walk(i, [])
+    return out
+
+
+def _random_dags(seed, count, max_ops):
+    rng = np.random.default_rng(seed)
+    unary = ["exp", "neg", "relu", "square"]
+    for _ in range(count):
+        n = int(rng.integers(1, max_ops + 1))
+        g = Graph()
+        avail = [g.input("x0", "f32", (3, 5)), g.input("x1", "f32", (3, 5))]
+        for i in range(n):
+            k = int(rng.integers(1, 4))
+            ins = [avail[int(j)] for j in rng.integers(0, len(avail), size=k)]
+            op = {1: unary[int(rng.integers(0, 4))], 2: "add", 3: "add3"}[k]
+            avail.append(g.op(op, ins, f"t{i}", "f32", (3, 5)))
+        readers = {t for o in g.ops for t in o.inputs}
+        # every unread result is an output; some read ones too
+        for o in g.ops:
+            t = o.output
+            if t not in readers or rng.random() < 0.15:
+                g.tensors[t] = TensorDesc(g.tensors[t].name, "f32", (3, 5), "out")
+        yield g
+
+
+def test_postdominators_match_path_enumeration():
+    for g in _random_dags(11, 600, 7):
+        succ = pt.successors(g)
+        sets = pt.postdominator_sets(g)
+        for i in range(len(g.ops)):
+            paths = _paths_to_exit(g, succ, i)
+            on_all = set.intersection(*[set(p) for p in paths]) - {i}
+            assert sets[i] - {i, -1} == on_all
+            ipd = pt.immediate_postdominators(g)[i]
+            if on_all:
+                # the nearest one comes first on every path
+                firsts = {next(v for v in p[1:] if v in on_all) for p in paths}
+                assert firsts == {ipd}
+            else:
+                assert ipd is None
+
+
+def test_groups_are_convex_and_rule_abiding_on_random_dags():
+    for g in _random_dags(12, 400, 7):
+        groups = pt.partition(g)
+        succ = pt.successors(g)
+        owner = {i: gi for gi, grp in enumerate(groups) for i in grp}
+        for grp in groups:
+            s = set(grp)
+            # convex: nothing outside the group lies on a path between members
+            for a, b in itertools.permutations(grp, 2):
+                reach_a = pt._reach(succ, a)
+                for v in reach_a:
+                    if v not in s and b in pt._reach(succ, v):
+                        raise AssertionError((grp, a, b, v))
+            assert len(grp) <= pt.MAX_FUSED_OPS
+        # groups are listed in an order that respects dependencies
+        for gi, grp in enumerate(groups):
+            for i in grp:
+                for s2 in succ[i]:
+                    assert owner[s2] >= gi
