@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Throughput of the fused-group executor and the tensor-fusion buckets on
+one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic
+input.  The default workload (c5) is a 12-layer Transformer-block stack over
+8192 tokens x hidden 1024, bf16 activations: per layer a LayerNorm (three
+groups: row mean, row variance, normalise + affine), bias + GELU on
+[8192, 4096] and dropout (keep 0.9) + residual on [8192, 1024]; then the
+194 fp32 gradient tensors of such a model (151,156,736 elements) are packed
+into 25 MiB buckets scaled by 1/8 and unpacked again.  Every layer has its
+own buffers (~3 GB in all), so no step re-reads data the 256 MB Infinity
+Cache could hold.
+
+value = algorithmic bytes per step / time per step (GB/s), where the
+algorithmic bytes count each distinct external input of a group read once
+and each output written once, and 2 x payload for pack and for unpack.
+The roofline entry is for the dominant kernel (most time per step), timed
+launch by launch with HIP events on the stream the kernels run on.  The
+unfused baseline (one launch per op, intermediates stored) and the
+per-tensor bucket baseline run the same data after the timed region.  The
+CPU baseline times the oracle on a bounded sample of the same workload.
+
+Other workloads (--workload c1..c4) rotate through enough buffer sets to
+exceed 1 GiB, so the Infinity Cache cannot serve repeated reads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused-group HBM GB/s (% of peak) + speedup vs unfused; bucket pack GB/s"
+PEAK_GBS = 8000.0
+ELEM = {"f32": 4, "bf16": 2, "u8": 1}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--layers", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baselines", action="store_true",
+                    help="skip the unfused and per-tensor baselines")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------ accounting
+def group_bytes(graph, plan):
+    """Algorithmic bytes of each group: distinct external inputs read once,
+    outputs needed outside the group written once."""
+    out = []
+    for ops in plan.groups():
+        produced = {graph.ops[i].output for i in ops}
+        ext = set()
+        for i in ops:
+            for t in graph.ops[i].inputs:
+                if t not in produced:
+                    ext.add(t)
+        for t in produced:
+            if plan.is_materialized(t):
+                ext.add(t)
+        b = 0
+        for t in ext:
+            d = graph.tensors[t]
+            n = 1
+            for s in d.shape:
+                n *= s
+            b += n * ELEM[d.dtype]
+        out.append(b)
+    return out
+
+
+# ------------------------------------------------------------ device data
+def make_tensor(torch, gen, d, kind, a, b):
+    shape = tuple(d.shape)
+    if d.dtype == "u8":
+        u = torch.rand(shape, generator=gen, device="cuda")
+        return (u >= a).to(torch.uint8)
+    if kind == "normal":
+        x = torch.randn(shape, generator=gen, device="cuda") * b + a
+    else:
+        x = torch.rand(shape, generator=gen, device="cuda") * (b - a) + a
+    if d.dtype == "bf16":
+        return x.to(torch.bfloat16).view(torch.int16)
+    return x.float()
+
+
+def alloc_graph(torch, gtf, graph, plan, gen, dists):
+    bufs = {}
+    for t in plan.materialized():
+        d = graph.tensors[t]
+        if d.role == "in":
+            kind, a, b = dists[d.name]
+            bufs[t] = make_tensor(torch, gen, d, kind, a, b)
+        else:
+            dt = {"f32": torch.float32, "bf16": torch.int16}[d.dtype]
+            bufs[t] = torch.empty(tuple(d.shape), dtype=dt, device="cuda")
+    return bufs
+
+
+LN_D = {"X": ("normal", 0.0, 1.0), "gamma": ("normal", 1.0, 0.1), "beta": ("normal", 0.0, 0.1)}
+GELU_D = {"A": ("normal", 0.0, 1.0), "b1": ("normal", 0.0, 0.1)}
+DROP_D = {"h": ("normal", 0.0, 1.0), "mask": ("bernoulli", 0.1, 0.0), "R": ("normal", 0.0, 1.0)}
+
+
+class Timer:
+    """Event pairs around launches of one kernel, on the current stream."""
+
+    def __init__(self, torch, enabled):
+        self.torch, self.enabled, self.pairs = torch, enabled, []
+
+    def around(self, fn):
+        if not self.enabled:
+            fn()
+            return
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def total_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs)
+
+
+# ------------------------------------------------------------ c5 workload
+class C5:
+    def __init__(self, torch, gtf, configs, layers, fuse=True, seed=5000):
+        self.torch, self.gtf = torch, gtf
+        self.g_ln = configs.layernorm_graph()
+        self.g_ge = configs.gelu_graph()
+        self.g_do = configs.dropout_graph()
+        self.p = {k: gtf.FusePlan(g, fuse=fuse) for k, g in
+                  (("ln", self.g_ln), ("ge", self.g_ge), ("do", self.g_do))}
+        gen = torch.Generator(device="cuda")
+        self.layers = []
+        for l in range(layers):
+            gen.manual_seed(seed + l)
+            self.layers.append({
+                "ln": alloc_graph(torch, gtf, self.g_ln, self.p["ln"], gen, LN_D),
+                "ge": alloc_graph(torch, gtf, self.g_ge, self.p["ge"], gen, GELU_D),
+                "do": alloc_graph(torch, gtf, self.g_do, self.p["do"], gen, DROP_D)})
+        numel = configs.c5_numel()
+        self.bp = gtf.BucketPlan(numel, "f32", configs.BUCKET_CAP_BYTES)
+        _, _, bn = self.bp.query()
+        gen.manual_seed(configs.C5_GRAD_SEED)
+        self.grads = [torch.randn(n, generator=gen, device="cuda") * 1e-3 for n in numel]
+        self.buckets = [torch.empty(n, dtype=torch.float32, device="cuda") for n in bn]
+        self.ws = torch.empty(max(16, self.bp.workspace_bytes), dtype=torch.uint8, device="cuda")
+        self.bp.bind(self.ws)
+        self.scale = configs.AVG_SCALE
+        self.gbytes = {k: group_bytes(g, self.p[k]) for k, g in
+                       (("ln", self.g_ln), ("ge", self.g_ge), ("do", self.g_do))}
+        self.bucket_bytes = 2 * 4 * sum(numel)  # pack; unpack moves the same
+        self.launches = layers * sum(p.num_groups for p in self.p.values()) + 2
+
+    def bytes_per_step(self):
+        per_layer = sum(sum(v) for v in self.gbytes.values())
+        return per_layer * len(self.layers) + 2 * self.bucket_bytes
+
+    def exec_bytes_per_step(self):
+        return sum(sum(v) for v in self.gbytes.values()) * len(self.layers)
+
+    def step(self, exec_t=None, bucket_t=None, per_tensor=False):
+        for L in self.layers:
+            for k in ("ln", "ge", "do"):
+                plan, bufs = self.p[k], L[k]
+                for g in range(plan.num_groups):
+                    if exec_t is None:
+                        plan.run_group(g, bufs)
+                    else:
+                        exec_t.around(lambda: plan.run_group(g, bufs))
+        pack = (self.bp.pack_per_tensor if per_tensor else self.bp.pack)
+        if bucket_t is None:
+            pack(self.grads, self.buckets, self.scale)
+            self.bp.unpack(self.buckets, self.grads, 1.0)
+        else:
+            bucket_t.around(lambda: pack(self.grads, self.buckets, self.scale))
+            bucket_t.around(lambda: self.bp.unpack(self.buckets, self.grads, 1.0))
+
+
+def time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+# ------------------------------------------------------------ CPU baseline
+def cpu_baseline_c5(bytes_sample_target_s=15.0):
+    """The oracle, as it is, on a bounded sample of the c5 workload: one
+    layer's three graphs on the first rows, and a pack + unpack of the first
+    gradient tensors; rows grow until the sample takes about 10-30 s."""
+    import numpy as np
+    from oracle import bucket as obucket
+    from oracle import evaluate as oev
+    from oracle import partition as opart
+    from workloads import configs
+
+    def one(rows, n_grad_tensors):
+        gl = [configs.layernorm_graph(rows, 1024), configs.gelu_graph(rows, 4096),
+              configs.dropout_graph(rows, 1024)]
+        seed = configs.c5_layer_seed(0)
+        ins = [configs.layernorm_inputs(gl[0], seed), configs.gelu_inputs(gl[1], seed),
+               configs.dropout_inputs(gl[2], seed)]
+        stored = [opart.stored_tensors(g, opart.partition(g)) for g in gl]
+        numel = configs.c5_numel()[:n_grad_tensors]
+        grads = configs.gradient_values(numel, configs.C5_GRAD_SEED)
+        t0 = time.perf_counter()
+        for g, i, s in zip(gl, ins, stored):
+            oev.outputs(g, oev.evaluate(g, i, s))
+        bks = obucket.pack(numel, 4, configs.BUCKET_CAP_BYTES, grads, configs.AVG_SCALE)
+        obucket.unpack(numel, 4, configs.BUCKET_CAP_BYTES, bks, 1.0)
+        dt = time.perf_counter() - t0
+        nbytes = 0
+        for g in gl:
+            p = None
+            for grp in opart.partition(g):
+                nb = 0
+                produced = {g.ops[i].output for i in grp}
+                ext = {t for i in grp for t in g.ops[i].inputs if t not in produced}
+                st = opart.stored_tensors(g, opart.partition(g))
+                ext |= {t for t in produced if t in st or g.tensors[t].role == "out"}
+                for t in ext:
+                    d = g.tensors[t]
+                    nb += int(np.prod(d.shape)) * ELEM[d.dtype]
+                nbytes += nb
+        nbytes += 2 * 2 * 4 * sum(numel)
+        return dt, nbytes
+
+    rows, ngt = 128, 16
+    dt, nb = one(rows, ngt)
+    while dt < 10.0 and rows < 8192:
+        f = max(2.0, min(8.0, bytes_sample_target_s / max(dt, 1e-3)))
+        rows = min(8192, int(rows * f))
+        ngt = min(194, int(ngt * f))
+        dt, nb = one(rows, ngt)
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count()
+    return {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one layer at {rows} of 8192 rows (LayerNorm, bias+GELU, dropout+residual) "
+                      f"plus pack+unpack of the first {ngt} of 194 gradient tensors; "
+                      f"{nb} algorithmic bytes in {dt:.1f} s; NumPy/SciPy single-threaded "
+                      f"({ncpu} cores visible)"}
+
+
+# ------------------------------------------------------------ main
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the fused groups shard by rows with no exchange "
+              "and the buckets would feed an all-reduce that this build does not run; "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gradient_tensor_fusion_amd as gtf
+    from workloads import configs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.workload != "c5":
+        from bench_workloads import run_other  # noqa
+        return
+    w = C5(torch, gtf, configs, args.layers)
+    # timed region: K whole steps
+    ms, wall = time_steps(torch, w.step, args.steps, args.warmup)
+    nbytes = w.bytes_per_step()
+    value = nbytes / (ms * 1e-3) / 1e9
+    # per-kernel timing over a second pass of the same steps
+    et, bt = Timer(torch, True), Timer(torch, True)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        w.step(exec_t=et, bucket_t=bt)
+    torch.cuda.synchronize()
+    exec_ms = et.total_ms() / args.steps
+    bucket_ms = bt.total_ms() / args.steps
+    exec_gbs = w.exec_bytes_per_step() / (exec_ms * 1e-3) / 1e9
+    bucket_gbs = 2 * w.bucket_bytes / (bucket_ms * 1e-3) / 1e9
+    n_exec = len(et.pairs) // args.steps
+    if exec_ms >= bucket_ms:
+        dom = {"kernel": "exec_kernel", "launches_per_step": n_exec,
+               "avg_launch_us": round(exec_ms * 1e3 / n_exec, 3),
+               "bytes_per_launch": w.exec_bytes_per_step() / n_exec, "gbs": exec_gbs}
+    else:
+        dom = {"kernel": "bucket_kernel", "launches_per_step": 2,
+               "avg_launch_us": round(bucket_ms * 1e3 / 2, 3),
+               "bytes_per_launch": w.bucket_bytes, "gbs": bucket_gbs}
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "traffic_c5.json")
+    if os.path.exists(tf):
+        with open(tf) as f:
+            tj = json.load(f)
+        if tj.get("kernel") == dom["kernel"] and tj.get("source_hash") == _kernel_hash():
+            traffic = tj.get("bytes_per_launch")
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "c5: 12-layer Transformer-block fused groups (LayerNorm as 3 groups, "
+                               "bias+GELU [8192,4096], dropout+residual [8192,1024]) over 8192 tokens "
+                               "x hidden 1024, bf16 storage, + pack/unpack of 194 fp32 gradient "
+                               "tensors (151,156,736 elements) in 25 MiB buckets, scale 1/8",
+                   "layers": args.layers, "tokens": 8192, "hidden": 1024, "ffn": 4096,
+                   "storage": "bf16 activations, fp32 gradients; fp32 arithmetic",
+                   "bytes_per_step": nbytes, "launches_per_step": w.launches},
+        "roofline": {"bound": "hbm", "achieved": round(dom["gbs"], 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dom["gbs"] / PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": dom["kernel"],
+                     "avg_launch_us": dom["avg_launch_us"],
+                     "algorithmic_bytes_per_launch": round(dom["bytes_per_launch"])},
+        "breakdown": {"exec_ms_per_step": round(exec_ms, 4), "exec_gbs": round(exec_gbs, 1),
+                      "bucket_ms_per_step": round(bucket_ms, 4), "bucket_gbs": round(bucket_gbs, 1),
+                      "wall_s_timed": round(wall, 3)},
+    }
+    if not args.no_baselines:
+        del w
+        torch.cuda.empty_cache()
+        u = C5(torch, gtf, configs, args.layers, fuse=False)
+        ums, _ = time_steps(torch, lambda: u.step(per_tensor=True), max(2, args.steps // 2), 1)
+        result["speedup_vs_unfused"] = round(ums / ms, 3)
+        result["unfused"] = {"ms_per_step": round(ums, 4), "launches_per_step":
+                             args.layers * 15 + 2 * 194,
+                             "note": "one launch per op with bf16/fp32 intermediates stored; "
+                                     "one pack launch per gradient tensor"}
+        del u
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_c5()
+    print(json.dumps(result), flush=True)
+
+
+def _kernel_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "isa.h"):
+        with open(os.path.join(ROOT, "gradient_tensor_fusion_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

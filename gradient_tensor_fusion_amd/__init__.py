@@ -1,0 +1,182 @@
+"""Fused operator groups and tensor-fusion buckets on one AMD Instinct MI355X.
+
+Thin Python layer over libgtf.so (include/gtf.h); PyTorch supplies device
+memory and streams.  Planning (OpPatternKind annotation, post-dominator
+tree, grouping, op-program compilation, bucket planning) and every kernel
+run in the native library.
+
+    plan = FusePlan(graph)             # graph: .tensors and .ops (see below)
+    plan.run({tensor_id: torch_tensor, ...})
+    bp = BucketPlan(numel, cap_bytes=25 << 20)
+    bp.bind(torch.empty(bp.workspace_bytes, dtype=torch.uint8, device="cuda"))
+    bp.pack(grads, buckets, scale=1 / world_size)
+
+A graph is any object with ``tensors`` (each with name, dtype in
+{"f32","bf16","u8"}, shape, role in {"in","out","tmp"}) and ``ops`` (each
+with op name, inputs, output, imm, opaque), ops in topological order.
+"""
+from __future__ import annotations
+
+import ctypes
+from ctypes import byref, c_int32, c_int64, c_size_t, c_void_p
+from typing import Dict, List, Sequence
+
+from . import _capi as C
+from ._capi import GtfError
+
+__all__ = ["FusePlan", "BucketPlan", "device_copy", "GtfError", "PATTERN_NAMES"]
+
+PATTERN_NAMES = {0: "kElemWise", 1: "kBroadcast", 2: "kInjective", 3: "kCommReduce",
+                 4: "kOutEWiseFusable", 7: "kTuple", 8: "kOpaque"}
+
+
+def _program_desc(graph):
+    nt, no = len(graph.tensors), len(graph.ops)
+    tens = (C.TensorDesc * max(1, nt))()
+    for i, t in enumerate(graph.tensors):
+        d = tens[i]
+        d.dtype = C.DTYPE[t.dtype]
+        d.rank = len(t.shape)
+        for k, s in enumerate(t.shape[:2]):
+            d.shape[k] = int(s)
+        d.role = C.ROLE[t.role]
+        d.reserved = 0
+    ops = (C.OpDesc * max(1, no))()
+    for i, o in enumerate(graph.ops):
+        d = ops[i]
+        d.opcode = C.OPCODE[o.op]
+        d.n_in = len(o.inputs)
+        for k, t in enumerate(o.inputs[:3]):
+            d.inp[k] = int(t)
+        d.out = int(o.output)
+        d.imm = float(o.imm)
+        d.flags = C.OPF_OPAQUE if getattr(o, "opaque", False) else 0
+    desc = C.ProgramDesc(C.ABI_VERSION, nt, tens, no, ops)
+    return desc, tens, ops
+
+
+class FusePlan:
+    """fuse_plan_create and friends."""
+
+    def __init__(self, graph, fuse: bool = True):
+        self.graph = graph
+        self.n_tensors = len(graph.tensors)
+        self.n_ops = len(graph.ops)
+        desc, self._tens, self._ops = _program_desc(graph)
+        h = c_void_p()
+        C.check(C.lib().fuse_plan_create(byref(desc), 0 if fuse else C.NO_FUSE, byref(h)))
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and C._lib is not None:
+            C._lib.fuse_plan_destroy(h)
+            self._h = None
+
+    @property
+    def num_groups(self) -> int:
+        n = c_int32()
+        C.check(C.lib().fuse_plan_num_groups(self._h, byref(n)))
+        return n.value
+
+    def group_ops(self, g: int) -> List[int]:
+        n, pat = c_int32(), c_int32()
+        C.check(C.lib().fuse_plan_group_info(self._h, g, None, 0, byref(n), byref(pat)))
+        ids = (c_int32 * max(1, n.value))()
+        C.check(C.lib().fuse_plan_group_info(self._h, g, ids, n.value, byref(n), byref(pat)))
+        return list(ids[: n.value])
+
+    def group_pattern(self, g: int) -> int:
+        n, pat = c_int32(), c_int32()
+        C.check(C.lib().fuse_plan_group_info(self._h, g, None, 0, byref(n), byref(pat)))
+        return pat.value
+
+    def groups(self) -> List[List[int]]:
+        return [self.group_ops(g) for g in range(self.num_groups)]
+
+    def op_info(self):
+        pats = (c_int32 * max(1, self.n_ops))()
+        ipd = (c_int32 * max(1, self.n_ops))()
+        C.check(C.lib().fuse_plan_op_info(self._h, pats, ipd))
+        return list(pats[: self.n_ops]), [None if v < 0 else v for v in ipd[: self.n_ops]]
+
+    def is_materialized(self, t: int) -> bool:
+        y = c_int32()
+        C.check(C.lib().fuse_plan_is_materialized(self._h, t, byref(y)))
+        return bool(y.value)
+
+    def materialized(self) -> List[int]:
+        return [t for t in range(self.n_tensors) if self.is_materialized(t)]
+
+    def _ptrs(self, tensors) -> ctypes.Array:
+        if isinstance(tensors, dict):
+            ptrs = [C.data_ptr(tensors.get(t)) for t in range(self.n_tensors)]
+        else:
+            ptrs = [C.data_ptr(t) for t in tensors]
+        return C.ptr_array(ptrs)
+
+    def run_group(self, g: int, tensors, stream=None) -> None:
+        C.check(C.lib().fuse_group_run(self._h, g, self._ptrs(tensors), C.stream_handle(stream)))
+
+    def run(self, tensors, stream=None) -> None:
+        C.check(C.lib().fuse_plan_run(self._h, self._ptrs(tensors), C.stream_handle(stream)))
+
+
+class BucketPlan:
+    """bucket_plan_create / bind / pack / unpack."""
+
+    def __init__(self, numel: Sequence[int], dtype: str = "f32", cap_bytes: int = 25 << 20):
+        self.numel = [int(n) for n in numel]
+        arr = (c_int64 * max(1, len(self.numel)))(*self.numel)
+        h = c_void_p()
+        C.check(C.lib().bucket_plan_create(arr, len(self.numel), C.DTYPE[dtype], int(cap_bytes), 0,
+                                           byref(h)))
+        self._h = h
+        self.dtype = dtype
+        self.cap_bytes = int(cap_bytes)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and C._lib is not None:
+            C._lib.bucket_plan_destroy(h)
+            self._h = None
+
+    def query(self):
+        nb = c_int32()
+        C.check(C.lib().bucket_plan_query(self._h, byref(nb), None, None, None))
+        n = len(self.numel)
+        bof = (c_int32 * max(1, n))()
+        off = (c_int64 * max(1, n))()
+        bn = (c_int64 * max(1, nb.value))()
+        C.check(C.lib().bucket_plan_query(self._h, byref(nb), bof, off, bn))
+        return list(bof[:n]), list(off[:n]), list(bn[: nb.value])
+
+    @property
+    def workspace_bytes(self) -> int:
+        b = c_size_t()
+        C.check(C.lib().bucket_plan_workspace_bytes(self._h, byref(b)))
+        return b.value
+
+    def bind(self, workspace, stream=None) -> None:
+        self._ws = workspace  # keep it alive as long as the plan uses it
+        C.check(C.lib().bucket_plan_bind(self._h, C.data_ptr(workspace), C.stream_handle(stream)))
+
+    def pack(self, srcs, buckets, scale: float = 1.0, stream=None) -> None:
+        C.check(C.lib().bucket_pack(self._h, C.ptr_array([C.data_ptr(t) for t in srcs]),
+                                    C.ptr_array([C.data_ptr(b) for b in buckets]), float(scale),
+                                    C.stream_handle(stream)))
+
+    def unpack(self, buckets, dsts, scale: float = 1.0, stream=None) -> None:
+        C.check(C.lib().bucket_unpack(self._h, C.ptr_array([C.data_ptr(b) for b in buckets]),
+                                      C.ptr_array([C.data_ptr(t) for t in dsts]), float(scale),
+                                      C.stream_handle(stream)))
+
+    def pack_per_tensor(self, srcs, buckets, scale: float = 1.0, stream=None) -> None:
+        C.check(C.lib().bucket_pack_per_tensor(self._h, C.ptr_array([C.data_ptr(t) for t in srcs]),
+                                               C.ptr_array([C.data_ptr(b) for b in buckets]),
+                                               float(scale), C.stream_handle(stream)))
+
+
+def device_copy(dst, src, nbytes: int, stream=None) -> None:
+    C.check(C.lib().gtf_device_copy(C.data_ptr(dst), C.data_ptr(src), int(nbytes),
+                                    C.stream_handle(stream)))

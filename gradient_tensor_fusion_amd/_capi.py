@@ -1,0 +1,125 @@
+"""ctypes binding of libgtf.so (include/gtf.h).  Argument marshalling only:
+every step of planning and every kernel runs in the native library.
+
+The library is loaded from this package's directory; when it is missing the
+first call raises (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgtf.so")
+
+ABI_VERSION = 1
+
+GTF_OK, GTF_E_INVALID, GTF_E_UNSUPPORTED, GTF_E_SHAPE, GTF_E_LIMIT, GTF_E_STATE, GTF_E_HIP = (
+    0, -1, -2, -3, -4, -5, -6)
+
+DTYPE = {"f32": 0, "bf16": 1, "u8": 2}
+ROLE = {"in": 0, "out": 1, "tmp": 2}
+OPCODE = {
+    "copy": 0, "exp": 1, "tanh": 2, "sigmoid": 3, "relu": 4, "gelu": 5, "square": 6,
+    "sqrt": 7, "recip": 8, "neg": 9,
+    "add_imm": 16, "mul_imm": 17,
+    "add": 32, "sub": 33, "mul": 34, "div": 35, "max": 36, "min": 37,
+    "add3": 48, "dmul": 49,
+    "row_sum": 64, "row_mean": 65,
+}
+OPF_OPAQUE = 1
+NO_FUSE = 1
+
+EXPORTED = (
+    "fuse_plan_create", "fuse_plan_num_groups", "fuse_plan_group_info", "fuse_plan_op_info",
+    "fuse_plan_is_materialized", "fuse_group_run", "fuse_plan_run", "fuse_plan_destroy",
+    "bucket_plan_create", "bucket_plan_query", "bucket_plan_workspace_bytes",
+    "bucket_plan_bind", "bucket_pack", "bucket_unpack", "bucket_pack_per_tensor",
+    "bucket_plan_destroy", "gtf_device_copy", "gtf_last_error",
+)
+
+
+class TensorDesc(ctypes.Structure):
+    _fields_ = [("dtype", c_int32), ("rank", c_int32), ("shape", c_int64 * 2),
+                ("role", c_int32), ("reserved", c_int32)]
+
+
+class OpDesc(ctypes.Structure):
+    _fields_ = [("opcode", c_int32), ("n_in", c_int32), ("inp", c_int32 * 3), ("out", c_int32),
+                ("imm", c_float), ("flags", c_int32)]
+
+
+class ProgramDesc(ctypes.Structure):
+    _fields_ = [("abi_version", c_uint32), ("n_tensors", c_int32),
+                ("tensors", POINTER(TensorDesc)), ("n_ops", c_int32), ("ops", POINTER(OpDesc))]
+
+
+class GtfError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"gtf status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(python -m gradient_tensor_fusion_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = c_void_p
+        L.fuse_plan_create.argtypes = [POINTER(ProgramDesc), c_uint32, POINTER(vp)]
+        L.fuse_plan_num_groups.argtypes = [vp, POINTER(c_int32)]
+        L.fuse_plan_group_info.argtypes = [vp, c_int32, POINTER(c_int32), c_int32,
+                                           POINTER(c_int32), POINTER(c_int32)]
+        L.fuse_plan_op_info.argtypes = [vp, POINTER(c_int32), POINTER(c_int32)]
+        L.fuse_plan_is_materialized.argtypes = [vp, c_int32, POINTER(c_int32)]
+        L.fuse_group_run.argtypes = [vp, c_int32, POINTER(vp), vp]
+        L.fuse_plan_run.argtypes = [vp, POINTER(vp), vp]
+        L.fuse_plan_destroy.argtypes = [vp]
+        L.fuse_plan_destroy.restype = None
+        L.bucket_plan_create.argtypes = [POINTER(c_int64), c_int32, c_int32, c_int64, c_uint32,
+                                         POINTER(vp)]
+        L.bucket_plan_query.argtypes = [vp, POINTER(c_int32), POINTER(c_int32),
+                                        POINTER(c_int64), POINTER(c_int64)]
+        L.bucket_plan_workspace_bytes.argtypes = [vp, POINTER(c_size_t)]
+        L.bucket_plan_bind.argtypes = [vp, vp, vp]
+        L.bucket_pack.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
+        L.bucket_unpack.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
+        L.bucket_pack_per_tensor.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
+        L.bucket_plan_destroy.argtypes = [vp]
+        L.bucket_plan_destroy.restype = None
+        L.gtf_device_copy.argtypes = [vp, vp, c_size_t, vp]
+        L.gtf_last_error.argtypes = []
+        L.gtf_last_error.restype = c_char_p
+        _lib = L
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != GTF_OK:
+        raise GtfError(status, lib().gtf_last_error().decode())
+
+
+def stream_handle(stream=None) -> c_void_p:
+    """hipStream_t of a torch stream (default: the current one)."""
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return c_void_p(s.cuda_stream)
+
+
+def ptr_array(ptrs) -> ctypes.Array:
+    arr = (c_void_p * max(1, len(ptrs)))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+def data_ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()

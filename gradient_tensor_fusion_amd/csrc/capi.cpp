@@ -1,0 +1,319 @@
+// capi.cpp -- the extern "C" entry points declared in include/gtf.h.
+// Descriptor validation, plan ownership and error reporting live here;
+// planning is in plan.cpp / bucket_plan.cpp, kernels in kernels.hip.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+
+#include "gtf.h"
+#include "plan.h"
+
+struct gtf_fuse_plan {
+  gtf::FusePlan p;
+};
+struct gtf_bucket_plan {
+  gtf::BucketPlan b;
+};
+
+namespace gtf {
+
+thread_local std::string g_last_error = "no error";
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int launch_group(const CompiledGroup& cg, void* const* tensor_ptrs, hipStream_t stream);
+int launch_bucket(const BucketPlan& b, const void* const* tens, void* const* bk, float scale,
+                  bool unpack, bool per_tensor, hipStream_t stream);
+int upload_chunks(BucketPlan& b, void* ws, hipStream_t stream);
+int launch_copy(void* dst, const void* src, size_t nbytes, hipStream_t stream);
+
+namespace {
+
+int arity(int opc) {
+  switch (opc) {
+    case GTF_OP_COPY: case GTF_OP_EXP: case GTF_OP_TANH: case GTF_OP_SIGMOID:
+    case GTF_OP_RELU: case GTF_OP_GELU: case GTF_OP_SQUARE: case GTF_OP_SQRT:
+    case GTF_OP_RECIP: case GTF_OP_NEG: case GTF_OP_ADD_IMM: case GTF_OP_MUL_IMM:
+    case GTF_OP_ROW_SUM: case GTF_OP_ROW_MEAN:
+      return 1;
+    case GTF_OP_ADD: case GTF_OP_SUB: case GTF_OP_MUL: case GTF_OP_DIV:
+    case GTF_OP_MAX: case GTF_OP_MIN: case GTF_OP_DMUL:
+      return 2;
+    case GTF_OP_ADD3:
+      return 3;
+  }
+  return -1;
+}
+
+std::string op_name(int i) { return "op " + std::to_string(i); }
+
+int validate(const gtf_program_desc* d, FusePlan* p) {
+  if (d == nullptr) return fail(GTF_E_INVALID, "desc is NULL");
+  if (d->abi_version != GTF_ABI_VERSION)
+    return fail(GTF_E_INVALID, "abi_version " + std::to_string(d->abi_version) + " != " +
+                                   std::to_string(GTF_ABI_VERSION));
+  if (d->n_tensors < 0 || d->n_ops < 0) return fail(GTF_E_INVALID, "negative count");
+  if ((d->n_tensors > 0 && d->tensors == nullptr) || (d->n_ops > 0 && d->ops == nullptr))
+    return fail(GTF_E_INVALID, "NULL tensor or op array");
+  p->tensors.resize(d->n_tensors);
+  for (int t = 0; t < d->n_tensors; ++t) {
+    const gtf_tensor_desc& td = d->tensors[t];
+    TensorInfo& ti = p->tensors[t];
+    if (td.dtype != GTF_F32 && td.dtype != GTF_BF16 && td.dtype != GTF_U8)
+      return fail(GTF_E_UNSUPPORTED, "tensor " + std::to_string(t) + ": dtype");
+    if (td.rank != 1 && td.rank != 2)
+      return fail(GTF_E_UNSUPPORTED, "tensor " + std::to_string(t) + ": rank must be 1 or 2");
+    if (td.role != GTF_ROLE_IN && td.role != GTF_ROLE_OUT && td.role != GTF_ROLE_TMP)
+      return fail(GTF_E_INVALID, "tensor " + std::to_string(t) + ": role");
+    if (td.reserved != 0) return fail(GTF_E_INVALID, "tensor " + std::to_string(t) + ": reserved != 0");
+    for (int k = 0; k < td.rank; ++k)
+      if (td.shape[k] < 0) return fail(GTF_E_SHAPE, "tensor " + std::to_string(t) + ": negative extent");
+    ti.dtype = td.dtype;
+    ti.rank = td.rank;
+    ti.role = td.role;
+    ti.R = td.rank == 1 ? 1 : td.shape[0];
+    ti.C = td.rank == 1 ? td.shape[0] : td.shape[1];
+  }
+  std::vector<int> writer(d->n_tensors, -1);
+  std::vector<int> readers(d->n_tensors, 0);
+  p->ops.resize(d->n_ops);
+  for (int i = 0; i < d->n_ops; ++i) {
+    const gtf_op_desc& od = d->ops[i];
+    OpInfo& o = p->ops[i];
+    const int ar = arity(od.opcode);
+    if (ar < 0) return fail(GTF_E_UNSUPPORTED, op_name(i) + ": opcode " + std::to_string(od.opcode));
+    if (od.n_in != ar) return fail(GTF_E_INVALID, op_name(i) + ": n_in does not match the opcode");
+    if (od.flags & ~GTF_OPF_OPAQUE) return fail(GTF_E_INVALID, op_name(i) + ": unknown flags");
+    if (od.out < 0 || od.out >= d->n_tensors) return fail(GTF_E_INVALID, op_name(i) + ": output id");
+    for (int k = 0; k < ar; ++k) {
+      const int t = od.in[k];
+      if (t < 0 || t >= d->n_tensors) return fail(GTF_E_INVALID, op_name(i) + ": input id");
+      if (p->tensors[t].role != GTF_ROLE_IN && writer[t] < 0)
+        return fail(GTF_E_INVALID, op_name(i) + ": reads tensor " + std::to_string(t) +
+                                       " before any op writes it (ops must be topological)");
+      readers[t] += 1;
+    }
+    const int out = od.out;
+    if (p->tensors[out].role == GTF_ROLE_IN)
+      return fail(GTF_E_INVALID, op_name(i) + ": writes an input tensor");
+    if (writer[out] >= 0) return fail(GTF_E_INVALID, op_name(i) + ": tensor written twice");
+    if (p->tensors[out].dtype == GTF_U8)
+      return fail(GTF_E_UNSUPPORTED, op_name(i) + ": u8 outputs are not supported");
+    writer[out] = i;
+    o.opcode = od.opcode;
+    o.n_in = ar;
+    for (int k = 0; k < ar; ++k) o.in[k] = od.in[k];
+    o.out = out;
+    o.imm = od.imm;
+    o.flags = od.flags;
+    // shapes
+    const TensorInfo& to = p->tensors[out];
+    if (od.opcode == GTF_OP_ROW_SUM || od.opcode == GTF_OP_ROW_MEAN) {
+      const TensorInfo& ti = p->tensors[od.in[0]];
+      if (d->tensors[out].rank != 2 || to.R != ti.R || to.C != 1)
+        return fail(GTF_E_SHAPE, op_name(i) + ": a row reduction of [R,C] is declared [R,1]");
+    } else {
+      // NumPy broadcasting per axis: extents of 1 stretch to the other one
+      int64_t R = 1, C = 1;
+      for (int k = 0; k < ar; ++k) {
+        if (p->tensors[od.in[k]].R != 1) R = p->tensors[od.in[k]].R;
+        if (p->tensors[od.in[k]].C != 1) C = p->tensors[od.in[k]].C;
+      }
+      for (int k = 0; k < ar; ++k) {
+        const TensorInfo& ti = p->tensors[od.in[k]];
+        if ((ti.R != 1 && ti.R != R) || (ti.C != 1 && ti.C != C))
+          return fail(GTF_E_SHAPE, op_name(i) + ": operand shapes do not broadcast");
+      }
+      if (to.R != R || to.C != C)
+        return fail(GTF_E_SHAPE, op_name(i) + ": declared output shape differs from the result");
+    }
+  }
+  for (int t = 0; t < d->n_tensors; ++t) {
+    const int role = p->tensors[t].role;
+    if (role != GTF_ROLE_IN && writer[t] < 0)
+      return fail(GTF_E_INVALID, "tensor " + std::to_string(t) + ": no op writes it");
+    if (role == GTF_ROLE_TMP && readers[t] == 0)
+      return fail(GTF_E_INVALID, "tensor " + std::to_string(t) + ": tmp that no op reads");
+  }
+  return GTF_OK;
+}
+
+}  // namespace
+}  // namespace gtf
+
+using namespace gtf;
+
+extern "C" {
+
+const char* gtf_last_error(void) { return g_last_error.c_str(); }
+
+int fuse_plan_create(const gtf_program_desc* desc, uint32_t flags, gtf_fuse_plan** out) {
+  if (out == nullptr) return fail(GTF_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (flags & ~GTF_NO_FUSE) return fail(GTF_E_INVALID, "unknown flags");
+  gtf_fuse_plan* h = new (std::nothrow) gtf_fuse_plan();
+  if (h == nullptr) return fail(GTF_E_LIMIT, "out of host memory");
+  int st = validate(desc, &h->p);
+  if (st == GTF_OK) st = build_fuse_plan(&h->p, (flags & GTF_NO_FUSE) == 0);
+  if (st != GTF_OK) {
+    delete h;
+    return st;
+  }
+  *out = h;
+  return GTF_OK;
+}
+
+int fuse_plan_num_groups(const gtf_fuse_plan* plan, int32_t* n) {
+  if (plan == nullptr || n == nullptr) return fail(GTF_E_INVALID, "NULL argument");
+  *n = (int32_t)plan->p.groups.size();
+  return GTF_OK;
+}
+
+int fuse_plan_group_info(const gtf_fuse_plan* plan, int32_t g, int32_t* op_ids, int32_t cap,
+                         int32_t* n_ops, int32_t* pattern_kind) {
+  if (plan == nullptr) return fail(GTF_E_INVALID, "plan is NULL");
+  if (g < 0 || g >= (int32_t)plan->p.groups.size()) return fail(GTF_E_INVALID, "group index");
+  const Group& G = plan->p.groups[g];
+  if (n_ops) *n_ops = (int32_t)G.ops.size();
+  if (pattern_kind) *pattern_kind = G.pattern;
+  if (op_ids) {
+    if (cap < (int32_t)G.ops.size()) return fail(GTF_E_LIMIT, "op_ids capacity too small");
+    for (size_t k = 0; k < G.ops.size(); ++k) op_ids[k] = G.ops[k];
+  }
+  return GTF_OK;
+}
+
+int fuse_plan_op_info(const gtf_fuse_plan* plan, int32_t* pattern_kind, int32_t* ipdom) {
+  if (plan == nullptr) return fail(GTF_E_INVALID, "plan is NULL");
+  for (size_t i = 0; i < plan->p.ops.size(); ++i) {
+    if (pattern_kind) pattern_kind[i] = plan->p.ops[i].pattern;
+    if (ipdom) ipdom[i] = plan->p.ipdom[i];
+  }
+  return GTF_OK;
+}
+
+int fuse_plan_is_materialized(const gtf_fuse_plan* plan, int32_t tensor_id, int32_t* yes) {
+  if (plan == nullptr || yes == nullptr) return fail(GTF_E_INVALID, "NULL argument");
+  if (tensor_id < 0 || tensor_id >= (int32_t)plan->p.tensors.size())
+    return fail(GTF_E_INVALID, "tensor id");
+  *yes = plan->p.materialized[tensor_id] ? 1 : 0;
+  return GTF_OK;
+}
+
+int fuse_group_run(const gtf_fuse_plan* plan, int32_t g, void* const* tensor_ptrs, void* hip_stream) {
+  if (plan == nullptr || tensor_ptrs == nullptr) return fail(GTF_E_INVALID, "NULL argument");
+  if (g < 0 || g >= (int32_t)plan->p.groups.size()) return fail(GTF_E_INVALID, "group index");
+  return launch_group(plan->p.groups[g].code, tensor_ptrs, (hipStream_t)hip_stream);
+}
+
+int fuse_plan_run(const gtf_fuse_plan* plan, void* const* tensor_ptrs, void* hip_stream) {
+  if (plan == nullptr || tensor_ptrs == nullptr) return fail(GTF_E_INVALID, "NULL argument");
+  // check every pointer first so nothing is launched on error
+  for (const Group& G : plan->p.groups)
+    for (size_t s = 0; s < G.code.slot_tensor.size(); ++s)
+      if (tensor_ptrs[G.code.slot_tensor[s]] == nullptr && G.code.slot_numel[s] > 0)
+        return fail(GTF_E_INVALID, "tensor " + std::to_string(G.code.slot_tensor[s]) +
+                                       " has no device pointer");
+  for (const Group& G : plan->p.groups) {
+    int st = launch_group(G.code, tensor_ptrs, (hipStream_t)hip_stream);
+    if (st != GTF_OK) return st;
+  }
+  return GTF_OK;
+}
+
+void fuse_plan_destroy(gtf_fuse_plan* plan) { delete plan; }
+
+int bucket_plan_create(const int64_t* numel, int32_t n, int32_t dtype, int64_t cap_bytes,
+                       uint32_t flags, gtf_bucket_plan** out) {
+  if (out == nullptr) return fail(GTF_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (n < 0 || (n > 0 && numel == nullptr)) return fail(GTF_E_INVALID, "numel");
+  if (cap_bytes <= 0) return fail(GTF_E_INVALID, "cap_bytes must be positive");
+  if (flags != 0) return fail(GTF_E_INVALID, "flags must be 0");
+  if (dtype != GTF_F32 && dtype != GTF_BF16) return fail(GTF_E_UNSUPPORTED, "bucket dtype");
+  for (int i = 0; i < n; ++i)
+    if (numel[i] < 0) return fail(GTF_E_INVALID, "negative numel");
+  gtf_bucket_plan* h = new (std::nothrow) gtf_bucket_plan();
+  if (h == nullptr) return fail(GTF_E_LIMIT, "out of host memory");
+  h->b.dtype = dtype;
+  h->b.cap_bytes = cap_bytes;
+  h->b.numel.assign(numel, numel + n);
+  int st = build_bucket_plan(&h->b);
+  if (st != GTF_OK) {
+    delete h;
+    return st;
+  }
+  *out = h;
+  return GTF_OK;
+}
+
+int bucket_plan_query(const gtf_bucket_plan* plan, int32_t* n_buckets, int32_t* bucket_of,
+                      int64_t* offset, int64_t* bucket_numel) {
+  if (plan == nullptr) return fail(GTF_E_INVALID, "plan is NULL");
+  const BucketPlan& b = plan->b;
+  if (n_buckets) *n_buckets = (int32_t)b.bucket_numel.size();
+  for (size_t i = 0; i < b.numel.size(); ++i) {
+    if (bucket_of) bucket_of[i] = b.bucket_of[i];
+    if (offset) offset[i] = b.offset[i];
+  }
+  if (bucket_numel)
+    for (size_t k = 0; k < b.bucket_numel.size(); ++k) bucket_numel[k] = b.bucket_numel[k];
+  return GTF_OK;
+}
+
+int bucket_plan_workspace_bytes(const gtf_bucket_plan* plan, size_t* bytes) {
+  if (plan == nullptr || bytes == nullptr) return fail(GTF_E_INVALID, "NULL argument");
+  *bytes = plan->b.chunks.size() * sizeof(Chunk);
+  return GTF_OK;
+}
+
+int bucket_plan_bind(gtf_bucket_plan* plan, void* dev_workspace, void* hip_stream) {
+  if (plan == nullptr) return fail(GTF_E_INVALID, "plan is NULL");
+  if (dev_workspace == nullptr && !plan->b.chunks.empty())
+    return fail(GTF_E_INVALID, "workspace is NULL");
+  if (((uintptr_t)dev_workspace & 15) != 0) return fail(GTF_E_INVALID, "workspace not 16-byte aligned");
+  return upload_chunks(plan->b, dev_workspace, (hipStream_t)hip_stream);
+}
+
+static int bucket_run(const gtf_bucket_plan* plan, const void* const* tens, void* const* bk,
+                      float scale, bool unpack, bool per_tensor, void* hip_stream) {
+  if (plan == nullptr) return fail(GTF_E_INVALID, "plan is NULL");
+  const BucketPlan& b = plan->b;
+  if (b.numel.empty()) return GTF_OK;
+  if (tens == nullptr || bk == nullptr) return fail(GTF_E_INVALID, "NULL pointer array");
+  if (b.workspace == nullptr && !b.chunks.empty())
+    return fail(GTF_E_STATE, "bucket plan used before bucket_plan_bind");
+  return launch_bucket(b, tens, bk, scale, unpack, per_tensor, (hipStream_t)hip_stream);
+}
+
+int bucket_pack(const gtf_bucket_plan* plan, const void* const* src, void* const* buckets,
+                float scale, void* hip_stream) {
+  return bucket_run(plan, src, buckets, scale, false, false, hip_stream);
+}
+
+int bucket_unpack(const gtf_bucket_plan* plan, const void* const* buckets, void* const* dst,
+                  float scale, void* hip_stream) {
+  return bucket_run(plan, (const void* const*)dst, (void* const*)buckets, scale, true, false,
+                    hip_stream);
+}
+
+int bucket_pack_per_tensor(const gtf_bucket_plan* plan, const void* const* src,
+                           void* const* buckets, float scale, void* hip_stream) {
+  return bucket_run(plan, src, buckets, scale, false, true, hip_stream);
+}
+
+void bucket_plan_destroy(gtf_bucket_plan* plan) { delete plan; }
+
+int gtf_device_copy(void* dst, const void* src, size_t nbytes, void* hip_stream) {
+  if (dst == nullptr || src == nullptr) return fail(GTF_E_INVALID, "NULL pointer");
+  if ((((uintptr_t)dst | (uintptr_t)src) & 15) != 0 || (nbytes & 15) != 0)
+    return fail(GTF_E_INVALID, "copy needs 16-byte aligned pointers and size");
+  return launch_copy(dst, src, nbytes, (hipStream_t)hip_stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,895 @@
+// plan.cpp -- fusion planning on the host: OpPatternKind annotation, the
+// forward graph, the post-dominator tree, the three-phase grouping with
+// CheckPath / CommitFuse over a union-find, and group compilation.
+//
+// The grouping follows Apache TVM, "Operator Fusion" (docs/arch/fusion.rst):
+// "Operator Pattern Classification" (the kinds and CombinePattern = max),
+// "Algorithm" steps 1-4 and "Fusion rules" (the three phases, reductions
+// are sinks only, opaque ops are barriers, at most kMaxFusedOps = 256 ops
+// and a bounded argument count per group).
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "gtf.h"
+#include "plan.h"
+
+namespace gtf {
+
+namespace {
+
+bool is_reduce(int opc) { return opc == GTF_OP_ROW_SUM || opc == GTF_OP_ROW_MEAN; }
+
+// ---------------------------------------------------------------- union-find
+struct UnionFind {
+  std::vector<int> parent, pat, size;
+  explicit UnionFind(const std::vector<int>& pats)
+      : parent(pats.size()), pat(pats), size(pats.size(), 1) {
+    for (size_t i = 0; i < parent.size(); ++i) parent[i] = (int)i;
+  }
+  int find(int x) {
+    while (parent[x] != x) {
+      parent[x] = parent[parent[x]];
+      x = parent[x];
+    }
+    return x;
+  }
+  // merge x's set into target's set; the target's root stays the root
+  void merge_into(int x, int target) {
+    int rx = find(x), rt = find(target);
+    if (rx == rt) return;
+    parent[rx] = rt;
+    pat[rt] = std::max(pat[rt], pat[rx]);  // CombinePattern
+    size[rt] += size[rx];
+  }
+};
+
+std::vector<std::vector<int>> readers_of(const FusePlan& p) {
+  std::vector<int> producer(p.tensors.size(), -1);
+  for (size_t i = 0; i < p.ops.size(); ++i) producer[p.ops[i].out] = (int)i;
+  std::vector<std::vector<int>> rd(p.ops.size());
+  for (size_t j = 0; j < p.ops.size(); ++j) {
+    const OpInfo& o = p.ops[j];
+    for (int k = 0; k < o.n_in; ++k) {
+      int pr = producer[o.in[k]];
+      if (pr >= 0 && (rd[pr].empty() || rd[pr].back() != (int)j)) rd[pr].push_back((int)j);
+    }
+  }
+  return rd;
+}
+
+// Post-dominator tree (Algorithm step 2): visit ops in reverse topological
+// order; an op's parent is the least common ancestor, in the tree built so
+// far, of all ops that read its output.  An op whose output is a graph
+// output, or has no reader, hangs off the virtual root (-1).
+std::vector<int> postdom_tree(const FusePlan& p, const std::vector<std::vector<int>>& rd) {
+  int n = (int)p.ops.size();
+  std::vector<int> parent(n, -1), depth(n, 1);
+  auto dep = [&](int v) { return v < 0 ? 0 : depth[v]; };
+  auto lca = [&](int a, int b) {
+    while (a != b) {
+      if (dep(a) >= dep(b))
+        a = parent[a];  // a >= 0 here: depth 0 is only the root
+      else
+        b = parent[b];
+    }
+    return a;
+  };
+  for (int i = n - 1; i >= 0; --i) {
+    const OpInfo& o = p.ops[i];
+    if (p.tensors[o.out].role == GTF_ROLE_OUT || rd[i].empty()) {
+      parent[i] = -1;
+      depth[i] = 1;
+      continue;
+    }
+    int l = rd[i][0];
+    for (size_t k = 1; k < rd[i].size() && l >= 0; ++k) l = lca(l, rd[i][k]);
+    parent[i] = l;
+    depth[i] = dep(l) + 1;
+  }
+  return parent;
+}
+
+// External tensors of a member set: inputs read from outside plus outputs
+// needed outside (graph outputs or read by non-members).
+int count_args(const FusePlan& p, const std::vector<char>& in_set) {
+  std::set<int> produced, ext;
+  for (size_t i = 0; i < p.ops.size(); ++i)
+    if (in_set[i]) produced.insert(p.ops[i].out);
+  for (size_t i = 0; i < p.ops.size(); ++i) {
+    const OpInfo& o = p.ops[i];
+    for (int k = 0; k < o.n_in; ++k) {
+      bool inside = produced.count(o.in[k]) != 0;
+      if (in_set[i] && !inside) ext.insert(o.in[k]);
+      if (!in_set[i] && inside) ext.insert(o.in[k]);
+    }
+  }
+  for (int t : produced)
+    if (p.tensors[t].role == GTF_ROLE_OUT) ext.insert(t);
+  return (int)ext.size();
+}
+
+}  // namespace
+
+// ============================================================== compilation
+namespace {
+
+enum Cls { CLS_E = 0, CLS_ROW = 1, CLS_COL = 2 };
+
+struct MOp {
+  int kind;    // 0 unary form, 1 binary op, 2 imm op (slot op imm), 3 reduce, 4 copy
+  int form;    // F_* for unary, F_ADD..F_MIN for binary, XOp for imm
+  int in[2] = {-1, -1};
+  int out = -1;
+  float imm = 0.f;
+  bool commutative = false;
+};
+
+int unary_form(int opc) {
+  switch (opc) {
+    case GTF_OP_EXP: return F_EXP;
+    case GTF_OP_TANH: return F_TANH;
+    case GTF_OP_SIGMOID: return F_SIGMOID;
+    case GTF_OP_RELU: return F_RELU;
+    case GTF_OP_GELU: return F_GELU;
+    case GTF_OP_SQUARE: return F_SQUARE;
+    case GTF_OP_SQRT: return F_SQRT;
+    case GTF_OP_RECIP: return F_RECIP;
+    case GTF_OP_NEG: return F_NEG;
+  }
+  return -1;
+}
+
+int binary_form(int opc) {
+  switch (opc) {
+    case GTF_OP_ADD: return F_ADD;
+    case GTF_OP_SUB: return F_SUB;
+    case GTF_OP_MUL: return F_MUL;
+    case GTF_OP_DIV: return F_DIV;
+    case GTF_OP_MAX: return F_MAX;
+    case GTF_OP_MIN: return F_MIN;
+  }
+  return -1;
+}
+
+// x-op for "stack (op) X" and for "X (op) stack"
+int xop_of(int binform, bool x_on_left) {
+  switch (binform) {
+    case F_ADD: return X_ADD;
+    case F_MUL: return X_MUL;
+    case F_MAX: return X_MAX;
+    case F_MIN: return X_MIN;
+    case F_SUB: return x_on_left ? X_RSUB : X_SUB;
+    case F_DIV: return x_on_left ? X_RDIV : X_DIV;
+  }
+  return -1;
+}
+
+bool commutative(int binform) {
+  return binform == F_ADD || binform == F_MUL || binform == F_MAX || binform == F_MIN;
+}
+
+struct Codegen {
+  const FusePlan& p;
+  std::vector<Instr>* out;
+  int phase;  // CLS_E / CLS_ROW / CLS_COL
+  // value ids are tensor ids (>= 0) or synthetic temporaries (<= -2)
+  std::map<int, int> uses;       // remaining stack uses in this phase
+  std::set<int> loadable;        // external tensors this phase loads
+  std::set<int> loaded;
+  std::map<int, int> ext_slot;   // tensor -> external slot
+  std::map<int, int> lds_slot;   // value -> LDS slot (values read via X)
+  std::map<int, int> xcls;       // value -> CLS_ROW / CLS_COL for X operands
+  std::vector<int> stack;        // value id per slot
+  int max_depth = 0;
+  bool ok = true;
+  std::string why;
+
+  static constexpr int kDead = -1000000;
+
+  void emit(int form, int d, int arg = 0, float imm = 0.f) {
+    if (d < 0 || d >= kNR) {
+      ok = false;
+      why = "op-program needs more than the kernel's stack slots";
+      return;
+    }
+    Instr ins;
+    ins.code = (uint16_t)(form * kNR + d);
+    ins.arg = (uint16_t)arg;
+    ins.imm = imm;
+    out->push_back(ins);
+  }
+  int top() const { return (int)stack.size() - 1; }
+  void push(int v) {
+    stack.push_back(v);
+    max_depth = std::max(max_depth, (int)stack.size());
+    if ((int)stack.size() > kNR) {
+      ok = false;
+      why = "op-program needs more than the kernel's stack slots";
+    }
+  }
+  int slot_of(int v) const {
+    for (int i = top(); i >= 0; --i)
+      if (stack[i] == v) return i;
+    return -1;
+  }
+  bool is_x(int v) const { return xcls.count(v) != 0; }
+  int use(int v) const {
+    auto it = uses.find(v);
+    return it == uses.end() ? 0 : it->second;
+  }
+  bool unloaded(int v) const { return loadable.count(v) && !loaded.count(v); }
+
+  int load_form(int t) const {
+    switch (p.tensors[t].dtype) {
+      case GTF_F32: return F_LD_F32;
+      case GTF_BF16: return F_LD_BF16;
+      default: return F_LD_U8;
+    }
+  }
+  void load(int v) {
+    loaded.insert(v);
+    push(v);
+    emit(load_form(v), top(), ext_slot.at(v));
+  }
+  // A value read again later is loaded once, into a home slot that stays.
+  void ensure_home(int v) {
+    if (unloaded(v) && use(v) > 1) load(v);
+  }
+  // Push a consumable instance of v on top.
+  void fetch(int v) {
+    if (unloaded(v)) {
+      load(v);
+      return;
+    }
+    int s = slot_of(v);
+    if (s < 0) {
+      ok = false;
+      why = "internal: operand not on the stack";
+      return;
+    }
+    push(v);
+    emit(F_PICK, top(), s);
+  }
+  bool top_consumable(int v) const {
+    return top() >= 0 && stack[top()] == v && use(v) == 1;
+  }
+  void drop_dead_top() {
+    while (!stack.empty() && stack.back() == kDead) stack.pop_back();
+  }
+  void used_once(int v) {
+    if (--uses[v] == 0)
+      for (int i = 0; i <= top(); ++i)
+        if (stack[i] == v) stack[i] = kDead;
+  }
+  void x_info(int v, int* base, int* arg) {
+    *base = xcls.at(v) == CLS_COL ? F_ADD_C : F_ADD_R;
+    *arg = lds_slot.at(v);
+  }
+  // one stack operand, rewritten in place: returns the slot
+  int operand_on_top(int a) {
+    ensure_home(a);
+    if (!top_consumable(a)) fetch(a);
+    return top();
+  }
+  void finish_in_place(int a, int d, int result) {
+    stack[d] = kDead;  // the consumed instance
+    used_once(a);
+    stack[d] = result;
+  }
+
+  void run_unary(const MOp& m) {
+    int a = m.in[0];
+    int d = operand_on_top(a);
+    emit(m.form, d);
+    finish_in_place(a, d, m.out);
+  }
+  void run_copy(const MOp& m) {  // a rename; a copy only when a lives on
+    int a = m.in[0];
+    int d = operand_on_top(a);
+    finish_in_place(a, d, m.out);
+  }
+  void run_imm(const MOp& m) {  // slot (op) imm
+    int a = m.in[0];
+    int d = operand_on_top(a);
+    emit(F_ADD_I + m.form, d, 0, m.imm);
+    finish_in_place(a, d, m.out);
+  }
+  void run_binary(const MOp& m) {
+    int a = m.in[0], b = m.in[1];
+    bool xa = is_x(a), xb = is_x(b);
+    if (xa && xb) {  // both broadcast: push the left one, then X-op the right
+      int base, arg;
+      x_info(a, &base, &arg);
+      push(m.out);
+      emit(base == F_ADD_C ? F_PUSH_COL : F_PUSH_ROW, top(), arg);
+      x_info(b, &base, &arg);
+      emit(base + xop_of(m.form, false), top(), arg);
+      return;
+    }
+    if (xa || xb) {
+      int s = xa ? b : a, x = xa ? a : b;
+      int d = operand_on_top(s);
+      int base, arg;
+      x_info(x, &base, &arg);
+      emit(base + xop_of(m.form, xa), d, arg);
+      finish_in_place(s, d, m.out);
+      return;
+    }
+    ensure_home(a);
+    if (b != a) ensure_home(b);
+    bool in_place = a != b && top() >= 1 && use(a) == 1 && use(b) == 1;
+    if (in_place && stack[top() - 1] == a && stack[top()] == b) {
+      // operands already in order
+    } else if (in_place && m.commutative && stack[top() - 1] == b && stack[top()] == a) {
+      // commutative: either order gives the same IEEE result
+    } else if (a != b && top_consumable(a)) {
+      fetch(b);
+    } else if (m.commutative && a != b && top_consumable(b)) {
+      fetch(a);
+    } else {
+      fetch(a);
+      fetch(b);
+    }
+    int d = top() - 1;
+    emit(m.form, d);
+    stack[d] = kDead;
+    stack[d + 1] = kDead;
+    used_once(a);
+    used_once(b);
+    stack.pop_back();
+    stack[d] = m.out;
+  }
+  void run_reduce(const MOp& m) {  // reads a slot, writes nothing
+    int a = m.in[0];
+    int s = slot_of(a);
+    if (s < 0) {
+      fetch(a);
+      s = top();
+    }
+    emit(F_RED, s);
+    used_once(a);
+    drop_dead_top();
+  }
+};
+
+}  // namespace
+
+bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup* outp,
+                   std::string* why) {
+  CompiledGroup cg;
+  std::memset(&cg.args, 0, sizeof(cg.args));
+  auto bad = [&](const std::string& s) {
+    if (why) *why = s;
+    return false;
+  };
+  std::vector<char> member(p.ops.size(), 0);
+  for (int i : ops) member[i] = 1;
+  std::set<int> produced;
+  for (int i : ops) produced.insert(p.ops[i].out);
+
+  // ---- domain
+  int64_t R = 0, C = 0;
+  std::set<int> touched;
+  for (int i : ops) {
+    const OpInfo& o = p.ops[i];
+    for (int k = 0; k < o.n_in; ++k) touched.insert(o.in[k]);
+    touched.insert(o.out);
+  }
+  R = 1;
+  C = 1;
+  for (int t : touched) {  // extents of 1 broadcast (also to 0)
+    if (p.tensors[t].R != 1) R = p.tensors[t].R;
+    if (p.tensors[t].C != 1) C = p.tensors[t].C;
+  }
+  for (int t : touched) {
+    const TensorInfo& ti = p.tensors[t];
+    if ((ti.R != 1 && ti.R != R) || (ti.C != 1 && ti.C != C)) return bad("shapes in group do not broadcast");
+  }
+  int n_reduce = 0, red_op = -1;
+  for (int i : ops)
+    if (is_reduce(p.ops[i].opcode)) {
+      ++n_reduce;
+      red_op = i;
+    }
+  if (n_reduce > 1) return bad("more than one reduction in a group");
+  if (red_op >= 0) {
+    const TensorInfo& ri = p.tensors[p.ops[red_op].in[0]];
+    if (ri.R != R || ri.C != C) return bad("reduction input is not the group domain");
+    for (int i : ops)
+      for (int k = 0; k < p.ops[i].n_in; ++k)
+        if (p.ops[i].in[k] == p.ops[red_op].out) return bad("reduction is not the sink");
+  }
+  bool flat = red_op < 0;
+  for (int t : touched)
+    if (p.tensors[t].R != R || p.tensors[t].C != C) flat = false;
+  int64_t DR = flat ? 1 : R, DC = flat ? R * C : C;
+
+  auto cls_of = [&](int t) -> int {
+    const TensorInfo& ti = p.tensors[t];
+    if (flat) return CLS_E;
+    if (ti.R == R && ti.C == C) return CLS_E;
+    if (ti.R == 1 && ti.C == C) return CLS_COL;
+    return CLS_ROW;
+  };
+  auto op_cls = [&](int i) -> int {
+    if (is_reduce(p.ops[i].opcode)) return CLS_E;
+    return cls_of(p.ops[i].out);
+  };
+
+  // ---- external slots: inputs read from outside, outputs needed outside
+  std::vector<int> slots;
+  auto slot_for = [&](int t) {
+    for (size_t k = 0; k < slots.size(); ++k)
+      if (slots[k] == t) return (int)k;
+    slots.push_back(t);
+    return (int)slots.size() - 1;
+  };
+  std::set<int> outputs;
+  for (int t : produced) {
+    if (p.tensors[t].role == GTF_ROLE_OUT) outputs.insert(t);
+    for (size_t j = 0; j < p.ops.size(); ++j) {
+      if (member[j]) continue;
+      for (int k = 0; k < p.ops[j].n_in; ++k)
+        if (p.ops[j].in[k] == t) outputs.insert(t);
+    }
+  }
+  std::set<int> ext_in;
+  for (int i : ops)
+    for (int k = 0; k < p.ops[i].n_in; ++k)
+      if (!produced.count(p.ops[i].in[k])) ext_in.insert(p.ops[i].in[k]);
+  for (int t : ext_in) slot_for(t);
+  for (int t : outputs) slot_for(t);
+  if ((int)slots.size() > kMaxSlots) return bad("too many external tensors");
+
+  // ---- operand classes and LDS slots
+  // ROW/COL values read by element-phase ops live in LDS.
+  std::map<int, int> row_lds, col_lds;
+  for (int i : ops) {
+    if (op_cls(i) != CLS_E) continue;
+    const OpInfo& o = p.ops[i];
+    for (int k = 0; k < o.n_in; ++k) {
+      int c = cls_of(o.in[k]);
+      if (c == CLS_ROW && !row_lds.count(o.in[k])) {
+        int s = (int)row_lds.size();
+        row_lds[o.in[k]] = s;
+      }
+      if (c == CLS_COL && !col_lds.count(o.in[k])) {
+        int s = (int)col_lds.size();
+        col_lds[o.in[k]] = s;
+      }
+    }
+  }
+  if ((int)row_lds.size() > kMaxLdsRow) return bad("too many row operands");
+  if ((int)col_lds.size() > kMaxLdsCol) return bad("too many column operands");
+  // row / column ops may read only their own class (column ops may also
+  // load an external [1,1] scalar)
+  for (int i : ops) {
+    int c = op_cls(i);
+    if (c == CLS_E) continue;
+    const OpInfo& o = p.ops[i];
+    for (int k = 0; k < o.n_in; ++k) {
+      int ci = cls_of(o.in[k]);
+      if (ci == c) continue;
+      bool ext_scalar = !produced.count(o.in[k]) && p.tensors[o.in[k]].R == 1 &&
+                        p.tensors[o.in[k]].C == 1;
+      if (c == CLS_COL && ext_scalar) continue;
+      return bad("row/column operand mix not supported in one group");
+    }
+  }
+
+  // ---- lower ops to micro-ops per phase
+  std::vector<MOp> mops[3];
+  int synth = -1;
+  for (int i : ops) {
+    const OpInfo& o = p.ops[i];
+    int c = op_cls(i);
+    auto& L = mops[c];
+    if (o.opcode == GTF_OP_COPY) {
+      MOp m;
+      m.kind = 4;
+      m.form = 0;
+      m.in[0] = o.in[0];
+      m.out = o.out;
+      L.push_back(m);
+    } else if (unary_form(o.opcode) >= 0) {
+      MOp m;
+      m.kind = 0;
+      m.form = unary_form(o.opcode);
+      m.in[0] = o.in[0];
+      m.out = o.out;
+      L.push_back(m);
+    } else if (o.opcode == GTF_OP_ADD_IMM || o.opcode == GTF_OP_MUL_IMM) {
+      MOp m;
+      m.kind = 2;
+      m.form = o.opcode == GTF_OP_ADD_IMM ? X_ADD : X_MUL;
+      m.imm = o.imm;
+      m.in[0] = o.in[0];
+      m.out = o.out;
+      L.push_back(m);
+    } else if (binary_form(o.opcode) >= 0) {
+      MOp m;
+      m.kind = 1;
+      m.form = binary_form(o.opcode);
+      m.commutative = commutative(m.form);
+      m.in[0] = o.in[0];
+      m.in[1] = o.in[1];
+      m.out = o.out;
+      L.push_back(m);
+    } else if (o.opcode == GTF_OP_ADD3) {
+      MOp m1;
+      m1.kind = 1;
+      m1.form = F_ADD;
+      m1.commutative = true;
+      m1.in[0] = o.in[0];
+      m1.in[1] = o.in[1];
+      m1.out = --synth;
+      MOp m2 = m1;
+      m2.in[0] = m1.out;
+      m2.in[1] = o.in[2];
+      m2.out = o.out;
+      L.push_back(m1);
+      L.push_back(m2);
+    } else if (o.opcode == GTF_OP_DMUL) {
+      MOp m1;
+      m1.kind = 2;
+      m1.form = X_MUL;
+      m1.imm = o.imm;
+      m1.in[0] = o.in[0];
+      m1.out = --synth;
+      MOp m2;
+      m2.kind = 1;
+      m2.form = F_MUL;
+      m2.commutative = true;
+      m2.in[0] = m1.out;
+      m2.in[1] = o.in[1];
+      m2.out = o.out;
+      L.push_back(m1);
+      L.push_back(m2);
+    } else if (is_reduce(o.opcode)) {
+      MOp m;
+      m.kind = 3;
+      m.in[0] = o.in[0];
+      m.out = o.out;
+      L.push_back(m);
+    } else {
+      return bad("unsupported opcode in group");
+    }
+  }
+
+  // ---- code generation, phase by phase: column, row, element
+  std::vector<Instr> prog[3];
+  int max_depth = 0;
+  const int order[3] = {CLS_COL, CLS_ROW, CLS_E};
+  for (int ph : order) {
+    Codegen g{p, &prog[ph], ph};
+    for (size_t k = 0; k < slots.size(); ++k) g.ext_slot[slots[k]] = (int)k;
+    if (ph == CLS_E) {  // broadcast operands are read from LDS
+      for (auto& kv : row_lds) {
+        g.xcls[kv.first] = CLS_ROW;
+        g.lds_slot[kv.first] = kv.second;
+      }
+      for (auto& kv : col_lds) {
+        g.xcls[kv.first] = CLS_COL;
+        g.lds_slot[kv.first] = kv.second;
+      }
+    }
+    auto& L = mops[ph];
+    std::set<int> made_here;
+    for (auto& m : L) made_here.insert(m.out);
+    for (auto& m : L) {
+      int n_st = m.kind == 1 ? 2 : 1;
+      for (int k = 0; k < n_st; ++k) {
+        int v = m.in[k];
+        if (g.is_x(v)) continue;
+        g.uses[v] += 1;
+        if (v >= 0 && !produced.count(v)) g.loadable.insert(v);
+      }
+    }
+    // externals this phase stages into LDS for the element phase
+    const auto& lds_map = ph == CLS_ROW ? row_lds : col_lds;
+    if (ph != CLS_E) {
+      for (auto& kv : lds_map) {
+        int t = kv.first;
+        if (produced.count(t)) continue;
+        g.loadable.insert(t);
+        int s = g.slot_of(t);
+        if (s < 0) {
+          g.load(t);
+          s = g.top();
+        }
+        g.emit(F_ST_LDS, s, kv.second);
+        if (g.use(t) == 0) {
+          g.stack.pop_back();
+          g.drop_dead_top();
+        }
+      }
+    }
+    // list scheduling: among ready micro-ops prefer the one whose operand
+    // sits highest on the stack (fewest copies)
+    std::vector<char> done(L.size(), 0);
+    std::set<int> avail;
+    for (size_t step = 0; step < L.size() && g.ok; ++step) {
+      int best = -1, best_score = -1000;
+      for (size_t k = 0; k < L.size(); ++k) {
+        if (done[k]) continue;
+        int n_st = L[k].kind == 1 ? 2 : 1;
+        bool rdy = true;
+        int score = -1;
+        for (int q = 0; q < n_st; ++q) {
+          int v = L[k].in[q];
+          if (made_here.count(v) && !avail.count(v)) rdy = false;
+          int s = g.slot_of(v);
+          if (s >= 0) score = std::max(score, s);
+        }
+        if (rdy && score > best_score) {
+          best_score = score;
+          best = (int)k;
+        }
+      }
+      if (best < 0) return bad("internal: no ready op");
+      done[best] = 1;
+      const MOp& m = L[best];
+      switch (m.kind) {
+        case 0: g.run_unary(m); break;
+        case 1: g.run_binary(m); break;
+        case 2: g.run_imm(m); break;
+        case 3: g.run_reduce(m); break;
+        default: g.run_copy(m); break;
+      }
+      if (!g.ok) break;
+      if (m.kind == 3) continue;
+      avail.insert(m.out);
+      int v = m.out;
+      if (v >= 0 && outputs.count(v)) {
+        int dt = p.tensors[v].dtype;
+        g.emit(dt == GTF_BF16 ? F_ST_BF16 : F_ST_F32, g.top(), g.ext_slot.at(v));
+      }
+      if (ph != CLS_E && v >= 0 && lds_map.count(v)) g.emit(F_ST_LDS, g.top(), lds_map.at(v));
+      if (g.use(v) == 0) {
+        g.stack.pop_back();
+        g.drop_dead_top();
+      }
+    }
+    if (!g.ok) return bad(g.why);
+    max_depth = std::max(max_depth, g.max_depth);
+  }
+
+  size_t total = prog[0].size() + prog[1].size() + prog[2].size();
+  if (total > (size_t)kMaxInstr) return bad("op-program longer than the instruction buffer");
+
+  // ---- geometry
+  ExecArgs& a = cg.args;
+  a.R = DR;
+  a.C = DC;
+  int64_t C8 = (DC + kV - 1) / kV * kV;
+  int pw;
+  if (red_op >= 0) {
+    pw = (int)std::max<int64_t>(C8, kV);
+    if (!col_lds.empty() && (int64_t)col_lds.size() * C8 > 16384)
+      return bad("reduction group with column operands wider than the LDS panel");
+    if (C8 > (int64_t)1 << 30) return bad("row too wide");
+  } else {
+    pw = (int)std::min<int64_t>(std::max<int64_t>(C8, kV), kPanelMax);
+  }
+  int64_t n_panels = DC == 0 ? 1 : (DC + pw - 1) / pw;
+  int64_t nt = (pw + kV - 1) / kV;
+  int tpr = 1;
+  if (red_op >= 0) {
+    int64_t want = (nt + 7) / 8;
+    while (tpr < want && tpr < kBlock) tpr <<= 1;
+  } else {
+    while (tpr < nt && tpr < kBlock) tpr <<= 1;
+  }
+  if (const char* e = std::getenv("GTF_TPR")) {
+    int f = std::atoi(e);
+    if (f >= 1 && f <= kBlock && (f & (f - 1)) == 0) tpr = f;
+  }
+  int rpp = kBlock / tpr;
+  int64_t k = DR / ((int64_t)rpp * 1024);
+  k = std::max<int64_t>(1, std::min<int64_t>(k, kBlock / rpp));
+  int rb = (int)(rpp * k);
+  int64_t n_rb = DR == 0 ? 0 : (DR + rb - 1) / rb;
+  a.n_items = n_rb * n_panels;
+  a.n_panels = (int)n_panels;
+  a.RB = rb;
+  a.PW = pw;
+  int lg = 0;
+  while ((1 << lg) < tpr) ++lg;
+  a.tpr_log2 = lg;
+  a.n_col = (int)prog[CLS_COL].size();
+  a.n_row = (int)prog[CLS_ROW].size();
+  a.n_elem = (int)prog[CLS_E].size();
+  a.n_col_slots = (int)col_lds.size();
+  a.n_row_slots = (int)row_lds.size();
+  a.reduce = 0;
+  a.red_slot = 0;
+  a.red_dtype = 0;
+  if (red_op >= 0) {
+    a.reduce = p.ops[red_op].opcode == GTF_OP_ROW_MEAN ? 2 : 1;
+    int t = p.ops[red_op].out;
+    a.red_slot = slot_for(t);
+    a.red_dtype = p.tensors[t].dtype == GTF_BF16 ? DT_BF16 : DT_F32;
+  }
+  size_t pos = 0;
+  for (int ph : order)
+    for (const Instr& ins : prog[ph]) a.prog[pos++] = ins;
+  for (size_t s = 0; s < slots.size(); ++s) {
+    const TensorInfo& ti = p.tensors[slots[s]];
+    int c = cls_of(slots[s]);
+    if (flat) {
+      a.rstride[s] = 0;
+      a.cstride[s] = 1;
+    } else if (c == CLS_E) {
+      a.rstride[s] = C;
+      a.cstride[s] = 1;
+    } else if (c == CLS_COL) {
+      a.rstride[s] = 0;
+      a.cstride[s] = 1;
+    } else {
+      a.rstride[s] = ti.R == 1 ? 0 : 1;
+      a.cstride[s] = 0;
+    }
+  }
+  cg.slot_tensor = slots;
+  for (int t : slots) cg.slot_numel.push_back(p.tensors[t].R * p.tensors[t].C);
+  cg.n_slots = (int)slots.size();
+  cg.max_depth = max_depth;
+  cg.lds_bytes = (int)(a.n_col_slots * (int64_t)pw * 4 + a.n_row_slots * (int64_t)rb * 4 +
+                       kBlock / 64 * 4 * 4);
+  if (cg.lds_bytes > 64 * 1024) return bad("LDS staging exceeds 64 KiB");
+  if (outp) *outp = cg;
+  return true;
+}
+
+// ================================================================ planning
+int build_fuse_plan(FusePlan* p, bool fuse) {
+  int n = (int)p->ops.size();
+  // annotate (OpPatternKind)
+  for (OpInfo& o : p->ops) {
+    if (o.flags & GTF_OPF_OPAQUE) {
+      o.pattern = GTF_PAT_OPAQUE;
+    } else if (is_reduce(o.opcode)) {
+      o.pattern = GTF_PAT_COMM_REDUCE;
+    } else if (o.opcode == GTF_OP_COPY) {
+      o.pattern = GTF_PAT_INJECTIVE;
+    } else {
+      const TensorInfo& to = p->tensors[o.out];
+      o.pattern = GTF_PAT_ELEMWISE;
+      for (int k = 0; k < o.n_in; ++k) {
+        const TensorInfo& ti = p->tensors[o.in[k]];
+        if (ti.R != to.R || ti.C != to.C) o.pattern = GTF_PAT_BROADCAST;
+      }
+    }
+  }
+  auto rd = readers_of(*p);
+  p->ipdom = postdom_tree(*p, rd);
+
+  std::vector<int> pats(n);
+  for (int i = 0; i < n; ++i) pats[i] = p->ops[i].pattern;
+  UnionFind uf(pats);
+  if (fuse) {
+    std::vector<char> mark(n, 0), in_set(n, 0);
+    for (int phase = 0; phase < 3; ++phase) {
+      for (int i = 0; i < n; ++i) {
+        int d = p->ipdom[i];
+        if (d < 0 || uf.find(i) == uf.find(d)) continue;
+        int src = uf.pat[uf.find(i)];
+        int sink = uf.pat[uf.find(d)];
+        // CheckPath: ops strictly between i and d on any path
+        std::vector<int> between, stack(rd[i].begin(), rd[i].end());
+        std::fill(mark.begin(), mark.end(), 0);
+        bool path_ok = true;
+        while (!stack.empty()) {
+          int v = stack.back();
+          stack.pop_back();
+          if (v == d || mark[v]) continue;
+          mark[v] = 1;
+          between.push_back(v);
+          if (p->ops[v].pattern > GTF_PAT_INJECTIVE) path_ok = false;
+          for (int s : rd[v]) stack.push_back(s);
+        }
+        bool ok;
+        if (src <= GTF_PAT_BROADCAST)
+          ok = path_ok && sink <= GTF_PAT_COMM_REDUCE;
+        else if (src == GTF_PAT_INJECTIVE && phase >= 1)
+          ok = path_ok && sink <= GTF_PAT_INJECTIVE;
+        else
+          ok = false;
+        if (!ok) continue;
+        // members of the merged group
+        std::set<int> roots{uf.find(i), uf.find(d)};
+        for (int v : between) roots.insert(uf.find(v));
+        std::fill(in_set.begin(), in_set.end(), 0);
+        std::vector<int> members;
+        for (int v = 0; v < n; ++v)
+          if (roots.count(uf.find(v))) {
+            in_set[v] = 1;
+            members.push_back(v);
+          }
+        if ((int)members.size() > GTF_MAX_GROUP_OPS) continue;
+        if (count_args(*p, in_set) > GTF_MAX_GROUP_ARGS) continue;
+        if (!compile_group(*p, members, nullptr, nullptr)) continue;  // resources
+        // CommitFuse
+        uf.merge_into(i, d);
+        for (int v : between) uf.merge_into(v, d);
+      }
+    }
+  }
+  // collect groups, order them by their dependencies
+  std::map<int, std::vector<int>> byroot;
+  for (int i = 0; i < n; ++i) byroot[uf.find(i)].push_back(i);
+  std::vector<std::vector<int>> gl;
+  std::vector<int> gpat;
+  for (auto& kv : byroot) {
+    gl.push_back(kv.second);
+    gpat.push_back(uf.pat[kv.first]);
+  }
+  std::vector<int> owner(p->tensors.size(), -1);
+  for (size_t g = 0; g < gl.size(); ++g)
+    for (int i : gl[g]) owner[p->ops[i].out] = (int)g;
+  std::vector<std::set<int>> deps(gl.size());
+  for (size_t g = 0; g < gl.size(); ++g)
+    for (int i : gl[g])
+      for (int k = 0; k < p->ops[i].n_in; ++k) {
+        int o = owner[p->ops[i].in[k]];
+        if (o >= 0 && o != (int)g) deps[g].insert(o);
+      }
+  std::vector<char> placed(gl.size(), 0);
+  p->groups.clear();
+  for (size_t step = 0; step < gl.size(); ++step) {
+    int pick = -1;
+    for (size_t g = 0; g < gl.size(); ++g) {
+      if (placed[g]) continue;
+      bool r = true;
+      for (int d : deps[g])
+        if (!placed[d]) r = false;
+      if (r && (pick < 0 || gl[g][0] < gl[pick][0])) pick = (int)g;
+    }
+    if (pick < 0) return fail(GTF_E_INVALID, "groups depend on each other in a cycle");
+    placed[pick] = 1;
+    Group G;
+    G.ops = gl[pick];
+    G.pattern = gpat[pick];
+    std::string why;
+    if (!compile_group(*p, G.ops, &G.code, &why))
+      return fail(GTF_E_LIMIT, "group of op " + std::to_string(G.ops[0]) + ": " + why);
+    p->groups.push_back(G);
+  }
+  // materialised tensors
+  p->materialized.assign(p->tensors.size(), 0);
+  for (size_t t = 0; t < p->tensors.size(); ++t)
+    if (p->tensors[t].role != GTF_ROLE_TMP) p->materialized[t] = 1;
+  std::vector<int> gof(p->tensors.size(), -1);
+  for (size_t g = 0; g < p->groups.size(); ++g)
+    for (int i : p->groups[g].ops) gof[p->ops[i].out] = (int)g;
+  for (size_t g = 0; g < p->groups.size(); ++g)
+    for (int i : p->groups[g].ops)
+      for (int k = 0; k < p->ops[i].n_in; ++k) {
+        int t = p->ops[i].in[k];
+        if (gof[t] >= 0 && gof[t] != (int)g) p->materialized[t] = 1;
+      }
+  if (std::getenv("GTF_TRACE")) {
+    for (size_t g = 0; g < p->groups.size(); ++g) {
+      const Group& G = p->groups[g];
+      std::fprintf(stderr, "[gtf] group %zu pattern %d ops", g, G.pattern);
+      for (int i : G.ops) std::fprintf(stderr, " %d", i);
+      const ExecArgs& a = G.code.args;
+      std::fprintf(stderr, " | dom %lldx%lld items %lld PW %d RB %d tpr %d col %d row %d elem %d depth %d\n",
+                   (long long)a.R, (long long)a.C, (long long)a.n_items, a.PW, a.RB,
+                   1 << a.tpr_log2, a.n_col, a.n_row, a.n_elem, G.code.max_depth);
+      int tot = a.n_col + a.n_row + a.n_elem;
+      for (int k = 0; k < tot; ++k)
+        std::fprintf(stderr, "    %3d form %2d d %d arg %d imm %g\n", k, a.prog[k].code / kNR,
+                     a.prog[k].code % kNR, a.prog[k].arg, a.prog[k].imm);
+    }
+  }
+  return GTF_OK;
+}
+
+}  // namespace gtf

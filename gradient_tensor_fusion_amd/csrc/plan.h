@@ -1,0 +1,80 @@
+// plan.h -- host-side fusion plan and bucket plan (internal).
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "isa.h"
+
+namespace gtf {
+
+// Set the thread's last-error message and return the status.
+int fail(int status, const std::string& msg);
+
+struct TensorInfo {
+  int dtype = 0, rank = 0, role = 0;
+  int64_t R = 0, C = 0;   // normalised 2-D shape ([N] -> [1, N])
+};
+
+struct OpInfo {
+  int opcode = 0, n_in = 0;
+  int in[3] = {-1, -1, -1};
+  int out = -1;
+  float imm = 0.f;
+  int flags = 0;
+  int pattern = 0;
+};
+
+// A group compiled into an op-program plus its launch geometry.
+struct CompiledGroup {
+  ExecArgs args;                 // pointers filled per run
+  std::vector<int> slot_tensor;  // external slot -> tensor id
+  std::vector<int64_t> slot_numel;  // elements of each external tensor
+  int n_slots = 0;
+  int lds_bytes = 0;
+  int max_depth = 0;
+};
+
+struct Group {
+  std::vector<int> ops;  // ascending op ids
+  int pattern = 0;
+  CompiledGroup code;
+};
+
+struct FusePlan {
+  std::vector<TensorInfo> tensors;
+  std::vector<OpInfo> ops;
+  std::vector<int> ipdom;        // -1: none
+  std::vector<Group> groups;     // in run order
+  std::vector<char> materialized;
+};
+
+// Compile a set of ops (ascending ids) into an op-program.  Returns false,
+// with a reason, when the group does not fit the kernel's resources.
+bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup* out,
+                   std::string* why);
+
+int build_fuse_plan(FusePlan* p, bool fuse);
+
+struct BucketPlan {
+  int dtype = 0;
+  int64_t cap_bytes = 0;
+  std::vector<int64_t> numel;
+  std::vector<int32_t> bucket_of;
+  std::vector<int64_t> offset;
+  std::vector<int64_t> bucket_numel;
+  // launches: tensor range [t0, t1), bucket range [b0, b1], chunk range
+  struct Launch {
+    int t0, t1, b0, b1;
+    int64_t c0, c1;
+  };
+  std::vector<Launch> launches;
+  std::vector<Chunk> chunks;
+  void* workspace = nullptr;     // where the chunk table was bound
+};
+
+int build_bucket_plan(BucketPlan* b);
+
+}  // namespace gtf

@@ -1,0 +1,251 @@
+/*
+ * gtf.h -- fused operator groups and tensor-fusion buckets on one AMD
+ * Instinct MI355X (gfx950).  Plain C ABI: every function is extern "C",
+ * takes plain pointers and sizes, returns an int status (0 = GTF_OK,
+ * negative = error) and never throws.  After a negative status,
+ * gtf_last_error() returns a message for the calling thread.
+ *
+ * Two parts:
+ *
+ * 1. Fused operator groups.  A program (tensors + ops in topological order)
+ *    is annotated with TVM's OpPatternKind, its post-dominator tree is
+ *    built, and ops are grouped by the post-dominator fusion rules (Apache
+ *    TVM, "Operator Fusion": sections "Operator Pattern Classification",
+ *    "FuseOps: Automatic Fusion" / "Algorithm" and "Fusion rules").  Each
+ *    group then becomes one function over its external tensors (same page,
+ *    "Example" and "FuseTIR"): here, one launch of a register-resident
+ *    op-program kernel whose intermediates never touch device memory (DisCo,
+ *    arXiv 2209.12769, section 1: op fusion keeps intermediate results out of
+ *    device memory and saves launches).
+ *
+ * 2. Tensor-fusion buckets.  Many small gradient tensors are packed into
+ *    contiguous buckets whose size is the sum of the member sizes, under a
+ *    size threshold, scaled by 1/N for the data-parallel average, and
+ *    unpacked back (DisCo section 1 "tensor fusion" and "AllReduce ... sums
+ *    (or averages)"; section 7, Horovod's fusion threshold).  One launch
+ *    covers hundreds of tensors through a device-side chunk table.
+ *
+ * Memory ownership: the caller owns every device buffer (inputs, outputs,
+ * stored intermediates, bucket buffers, the bucket workspace).  The library
+ * owns only its host-side plan objects.  It never allocates device memory
+ * and never synchronises a stream.  All run calls are asynchronous on the
+ * HIP stream passed in (a hipStream_t cast to void*; NULL is the null
+ * stream).
+ *
+ * Tensors are dense, row-major, at most rank 2.  A rank-1 tensor [N] is
+ * treated as the row vector [1, N].  Binary and ternary ops broadcast
+ * NumPy-style: each operand is [R,C], [1,C], [R,1] or [1,1] against the
+ * result [R,C].  Arithmetic is fp32 (bf16 and u8 inputs widen exactly);
+ * a bf16 store rounds to nearest-even once.
+ */
+#ifndef GTF_H
+#define GTF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GTF_ABI_VERSION 1u
+
+/* ---- status codes ---------------------------------------------------- */
+enum {
+  GTF_OK = 0,
+  GTF_E_INVALID = -1,     /* NULL argument, bad index, order/cycle, bad version */
+  GTF_E_UNSUPPORTED = -2, /* opcode, dtype or rank this library does not run */
+  GTF_E_SHAPE = -3,       /* shapes that do not broadcast or do not match */
+  GTF_E_LIMIT = -4,       /* a per-group or per-plan resource limit */
+  GTF_E_STATE = -5,       /* call out of order (bucket run before bind) */
+  GTF_E_HIP = -6          /* a HIP runtime call or launch failed */
+};
+
+/* ---- element types, tensor roles ------------------------------------- */
+enum { GTF_F32 = 0, GTF_BF16 = 1, GTF_U8 = 2 };
+enum { GTF_ROLE_IN = 0, GTF_ROLE_OUT = 1, GTF_ROLE_TMP = 2 };
+
+/* ---- OpPatternKind (values as in TVM's table) ------------------------ */
+enum {
+  GTF_PAT_ELEMWISE = 0,
+  GTF_PAT_BROADCAST = 1,
+  GTF_PAT_INJECTIVE = 2,
+  GTF_PAT_COMM_REDUCE = 3,
+  GTF_PAT_OUT_EWISE_FUSABLE = 4,
+  GTF_PAT_TUPLE = 7,
+  GTF_PAT_OPAQUE = 8
+};
+
+/* ---- opcodes ---------------------------------------------------------
+ * unary (n_in 1):  copy (injective; same shape), exp, tanh,
+ *                  sigmoid = 1/(1+exp(-x)), relu = x>0 ? x : +0,
+ *                  gelu = x/2*erfc(-x/sqrt 2), square = x*x, sqrt,
+ *                  recip = 1/x, neg
+ * immediate:       add_imm = x + imm, mul_imm = x * imm
+ * binary (n_in 2): add, sub, mul, div (a op b), max, min
+ * ternary:         add3 = (a + b) + c
+ * dropout:         dmul (n_in 2: h, mask) = (h * imm) * mask
+ * row reduce:      row_sum, row_mean over the last axis; the output is
+ *                  declared [R, 1]; the mean divides the sum by the width.
+ * add/sub/mul/div/max/min/add3/dmul broadcast their operands; sqrt and
+ * div are correctly rounded; no multiply-add is ever contracted. */
+enum {
+  GTF_OP_COPY = 0, GTF_OP_EXP = 1, GTF_OP_TANH = 2, GTF_OP_SIGMOID = 3,
+  GTF_OP_RELU = 4, GTF_OP_GELU = 5, GTF_OP_SQUARE = 6, GTF_OP_SQRT = 7,
+  GTF_OP_RECIP = 8, GTF_OP_NEG = 9,
+  GTF_OP_ADD_IMM = 16, GTF_OP_MUL_IMM = 17,
+  GTF_OP_ADD = 32, GTF_OP_SUB = 33, GTF_OP_MUL = 34, GTF_OP_DIV = 35,
+  GTF_OP_MAX = 36, GTF_OP_MIN = 37,
+  GTF_OP_ADD3 = 48, GTF_OP_DMUL = 49,
+  GTF_OP_ROW_SUM = 64, GTF_OP_ROW_MEAN = 65
+};
+
+#define GTF_OPF_OPAQUE 1 /* op flag: force OpPatternKind kOpaque (a barrier) */
+
+typedef struct {
+  int32_t dtype;    /* GTF_F32 / GTF_BF16 / GTF_U8 (u8 only as an input)   */
+  int32_t rank;     /* 1 or 2                                              */
+  int64_t shape[2]; /* shape[0..rank-1], each >= 0                         */
+  int32_t role;     /* GTF_ROLE_*                                          */
+  int32_t reserved; /* must be 0                                           */
+} gtf_tensor_desc;
+
+typedef struct {
+  int32_t opcode; /* GTF_OP_*                                              */
+  int32_t n_in;   /* number of inputs, as the opcode requires             */
+  int32_t in[3];  /* input tensor ids (index into the tensor array)       */
+  int32_t out;    /* output tensor id                                     */
+  float imm;      /* immediate for add_imm / mul_imm / dmul               */
+  int32_t flags;  /* GTF_OPF_*                                            */
+} gtf_op_desc;
+
+typedef struct {
+  uint32_t abi_version; /* GTF_ABI_VERSION                                */
+  int32_t n_tensors;
+  const gtf_tensor_desc* tensors;
+  int32_t n_ops;
+  const gtf_op_desc* ops; /* topological: an op reads only inputs and
+                             outputs of earlier ops                       */
+} gtf_program_desc;
+
+/* ---- limits ------------------------------------------------------------
+ * kMaxFusedOps is 256 on the TVM page; the page names a maximum argument
+ * count without its value, here 16 external tensors per group.  A fusion
+ * whose compiled op-program would not fit the kernel's register stack or
+ * instruction buffer is refused like one over the argument limit. */
+#define GTF_MAX_GROUP_OPS 256
+#define GTF_MAX_GROUP_ARGS 16
+
+/* fuse_plan_create flags */
+#define GTF_NO_FUSE 1u /* one op per group: the unfused baseline            */
+
+typedef struct gtf_fuse_plan gtf_fuse_plan;
+typedef struct gtf_bucket_plan gtf_bucket_plan;
+
+/* Build a fusion plan from a program description (host only; no device
+ * call).  Steps, in the TVM page's order: annotate each op with an
+ * OpPatternKind; build the forward graph; build the post-dominator tree
+ * (immediate post-dominator = least common ancestor, in the tree, of the
+ * op's readers; an op whose output is a graph output or unread has none);
+ * run the three fusion phases with CheckPath / CommitFuse over a
+ * union-find; compile each group into an op-program.  The descriptor is
+ * copied; the caller may free it afterwards.
+ * Errors: GTF_E_INVALID (NULL, version, ids, order, a tmp nobody reads, an
+ * in tensor written, a tensor written twice), GTF_E_UNSUPPORTED (opcode,
+ * dtype, rank, u8 output), GTF_E_SHAPE (broadcast/declared shape
+ * mismatch), GTF_E_LIMIT (a single op that no kernel can run).  On error
+ * *out is set to NULL. */
+int fuse_plan_create(const gtf_program_desc* desc, uint32_t flags, gtf_fuse_plan** out);
+
+/* Number of groups; groups are numbered in an order that respects their
+ * dependencies, so running 0..n-1 in order runs the program. */
+int fuse_plan_num_groups(const gtf_fuse_plan* plan, int32_t* n);
+
+/* Ops of group g (ascending op ids) and the group's OpPatternKind (max over
+ * its members).  op_ids may be NULL to ask only for *n_ops; otherwise it
+ * must hold cap entries (GTF_E_LIMIT if cap < *n_ops). */
+int fuse_plan_group_info(const gtf_fuse_plan* plan, int32_t g, int32_t* op_ids, int32_t cap,
+                         int32_t* n_ops, int32_t* pattern_kind);
+
+/* Per-op annotation and post-dominator tree (both arrays hold n_ops
+ * entries; ipdom[i] = -1 when op i has no immediate post-dominator). */
+int fuse_plan_op_info(const gtf_fuse_plan* plan, int32_t* pattern_kind, int32_t* ipdom);
+
+/* *yes = 1 when tensor_id must live in device memory during a run: every
+ * in and out tensor, and each tmp read by a group other than its
+ * producer's.  The caller allocates those; other tmps need no memory. */
+int fuse_plan_is_materialized(const gtf_fuse_plan* plan, int32_t tensor_id, int32_t* yes);
+
+/* Launch group g on the stream.  tensor_ptrs has n_tensors entries indexed
+ * by tensor id; entries the group does not touch, and zero-size tensors,
+ * may be NULL.  Device
+ * pointers; any alignment is accepted (16-byte aligned pointers and rows
+ * take the vector path).  Error: GTF_E_INVALID for a NULL pointer the group
+ * needs, GTF_E_HIP when the launch fails.  Nothing is launched on error. */
+int fuse_group_run(const gtf_fuse_plan* plan, int32_t g, void* const* tensor_ptrs,
+                   void* hip_stream);
+
+/* All groups, in order, on one stream (one launch per group). */
+int fuse_plan_run(const gtf_fuse_plan* plan, void* const* tensor_ptrs, void* hip_stream);
+
+void fuse_plan_destroy(gtf_fuse_plan* plan);
+
+/* ---- tensor-fusion buckets --------------------------------------------
+ * Plan (host only): next-fit in the given (production) order: tensor i
+ * joins the open bucket if bucket_bytes + bytes_i <= cap_bytes or the open
+ * bucket is empty, else it opens a new bucket.  Offsets are dense element
+ * offsets (the fused size is the sum of the sizes; no padding, no
+ * splitting).  A zero-size tensor takes the open bucket's current offset.
+ * dtype: GTF_F32 or GTF_BF16.  flags must be 0.
+ * Errors: GTF_E_INVALID (NULL, n < 0, numel < 0, cap_bytes <= 0),
+ * GTF_E_UNSUPPORTED (dtype). */
+int bucket_plan_create(const int64_t* numel, int32_t n, int32_t dtype, int64_t cap_bytes,
+                       uint32_t flags, gtf_bucket_plan** out);
+
+/* Query the plan.  Any output pointer may be NULL.  bucket_of and offset
+ * hold n entries, bucket_numel holds *n_buckets entries. */
+int bucket_plan_query(const gtf_bucket_plan* plan, int32_t* n_buckets, int32_t* bucket_of,
+                      int64_t* offset, int64_t* bucket_numel);
+
+/* Bytes of device workspace the plan's chunk table needs. */
+int bucket_plan_workspace_bytes(const gtf_bucket_plan* plan, size_t* bytes);
+
+/* Copy the chunk table into dev_workspace (caller-owned, at least
+ * workspace_bytes, 16-byte aligned) asynchronously on the stream.  Later
+ * runs read it there: the caller keeps it intact and must bind again after
+ * writing into it.  Runs of one plan on different streams that may overlap
+ * need one plan each. */
+int bucket_plan_bind(gtf_bucket_plan* plan, void* dev_workspace, void* hip_stream);
+
+/* pack:   buckets[b][offset_i + j] = fl(src[i][j] * scale)
+ * unpack: dst[i][j] = fl(buckets[b][offset_i + j] * scale)
+ * with one fp32 multiply (bf16: widen, multiply, round once); scale == 1
+ * copies bits unchanged.  src/dst have n entries (NULL allowed only for
+ * zero-size tensors), buckets has n_buckets entries.  One launch per up to
+ * 256 tensors-plus-buckets (every workload here fits in one).
+ * Errors: GTF_E_STATE (not bound), GTF_E_INVALID (NULL), GTF_E_HIP. */
+int bucket_pack(const gtf_bucket_plan* plan, const void* const* src, void* const* buckets,
+                float scale, void* hip_stream);
+int bucket_unpack(const gtf_bucket_plan* plan, const void* const* buckets, void* const* dst,
+                  float scale, void* hip_stream);
+
+/* The same plan as one launch per tensor: the per-tensor baseline the
+ * single-launch path is measured against. */
+int bucket_pack_per_tensor(const gtf_bucket_plan* plan, const void* const* src,
+                           void* const* buckets, float scale, void* hip_stream);
+
+void bucket_plan_destroy(gtf_bucket_plan* plan);
+
+/* ---- measurement helper -------------------------------------------------
+ * A plain device-to-device copy kernel (16-byte vector loads and stores):
+ * the achievable-bandwidth ceiling and the reference for scaling hardware
+ * byte counters.  Both pointers 16-byte aligned; nbytes a multiple of 16. */
+int gtf_device_copy(void* dst, const void* src, size_t nbytes, void* hip_stream);
+
+/* Message for the last non-OK status on this thread (never NULL). */
+const char* gtf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GTF_H */

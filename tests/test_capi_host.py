@@ -1,0 +1,245 @@
+"""Host-side checks of libgtf.so through its C ABI (no GPU needed): every
+declared symbol is exported, and the native planner (annotation,
+post-dominator tree, grouping, materialisation, bucket plans) agrees with
+the oracle's independent implementation."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gradient_tensor_fusion_amd as gtf
+from gradient_tensor_fusion_amd import _capi as C
+from oracle import bucket as obucket
+from oracle import partition as opart
+from workloads import configs
+from workloads.graph import Graph, OpDesc, TensorDesc
+from tests.test_oracle_partition import _random_dags
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "gtf.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|void|char)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 18
+    lib = ctypes.CDLL(C.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(C.EXPORTED)
+
+
+def as_sets(groups):
+    return sorted(sorted(g) for g in groups)
+
+
+def check_against_oracle(g):
+    plan = gtf.FusePlan(g)
+    assert as_sets(plan.groups()) == as_sets(opart.partition(g))
+    pats, ipd = plan.op_info()
+    assert pats == [opart.pattern(g, i) for i in range(len(g.ops))]
+    assert ipd == opart.immediate_postdominators(g)
+    groups = opart.partition(g)
+    stored = opart.stored_tensors(g, groups)
+    want = {t for t, d in enumerate(g.tensors) if d.role != "tmp"} | stored
+    assert set(plan.materialized()) == want
+    # groups come in an order that respects their dependencies
+    owner = {}
+    for gi, grp in enumerate(plan.groups()):
+        for i in grp:
+            owner[g.ops[i].output] = gi
+    for gi, grp in enumerate(plan.groups()):
+        for i in grp:
+            for t in g.ops[i].inputs:
+                assert owner.get(t, -1) <= gi
+    unf = gtf.FusePlan(g, fuse=False)
+    assert as_sets(unf.groups()) == [[i] for i in range(len(g.ops))]
+
+
+@pytest.mark.parametrize("make", [
+    lambda: configs.c1_graph(4, 8), lambda: configs.c2_graph(4, 8),
+    lambda: configs.c3_graph(4, 8), lambda: configs.c3_graph(4, 8, head_op=True),
+    lambda: configs.layernorm_graph(4, 8), lambda: configs.gelu_graph(4, 8),
+    lambda: configs.dropout_graph(4, 8)])
+def test_config_graphs_plan_like_the_oracle(make):
+    check_against_oracle(make())
+
+
+def test_tvm_example_and_limits_plan_like_the_oracle():
+    from tests.test_oracle_partition import graph_from_json, GOLDEN
+    import json
+    with open(os.path.join(GOLDEN, "tvm_add_exp_squeeze.json")) as f:
+        check_against_oracle(graph_from_json(json.load(f)))
+    g = Graph()
+    v = g.input("x", "f32", (2, 8))
+    for i in range(300):
+        v = g.op("neg", [v], f"t{i}", "f32", (2, 8), role="out" if i == 299 else "tmp")
+    plan = gtf.FusePlan(g)
+    assert [len(x) for x in plan.groups()] == [256, 44]
+    check_against_oracle(g)
+    g = Graph()
+    xs = [g.input(f"x{i}", "f32", (2, 8)) for i in range(21)]
+    v = xs[0]
+    for i in range(20):
+        v = g.op("add", [v, xs[i + 1]], f"s{i}", "f32", (2, 8), role="out" if i == 19 else "tmp")
+    assert [len(x) for x in gtf.FusePlan(g).groups()] == [14, 6]
+
+
+def test_random_dags_plan_like_the_oracle():
+    for g in _random_dags(21, 300, 7):
+        check_against_oracle(g)
+
+
+def _broadcast_dags(seed, count):
+    """Small DAGs mixing [R,C], [1,C] and [R,1] operands, reductions and
+    opaque ops."""
+    rng = np.random.default_rng(seed)
+    R, Cc = 3, 5
+    for _ in range(count):
+        g = Graph()
+        full = [g.input("x0", "f32", (R, Cc)), g.input("x1", "bf16", (R, Cc))]
+        rowv = [g.input("r0", "f32", (R, 1))]
+        colv = [g.input("c0", "bf16", (Cc,))]
+        n = int(rng.integers(1, 8))
+        for i in range(n):
+            kind = rng.integers(0, 6)
+            if kind == 0:
+                a = full[rng.integers(len(full))]
+                out = g.op(["exp", "relu", "neg", "tanh"][rng.integers(4)], [a], f"t{i}", "f32",
+                           (R, Cc), opaque=bool(rng.random() < 0.1))
+                full.append(out)
+            elif kind == 1:
+                a, b = full[rng.integers(len(full))], full[rng.integers(len(full))]
+                full.append(g.op(["add", "mul", "sub"][rng.integers(3)], [a, b], f"t{i}", "f32", (R, Cc)))
+            elif kind == 2:
+                a, c = full[rng.integers(len(full))], colv[rng.integers(len(colv))]
+                full.append(g.op("add", [a, c], f"t{i}", "bf16", (R, Cc)))
+            elif kind == 3:
+                a, r = full[rng.integers(len(full))], rowv[rng.integers(len(rowv))]
+                full.append(g.op("mul", [a, r], f"t{i}", "f32", (R, Cc)))
+            elif kind == 4:
+                a = full[rng.integers(len(full))]
+                rowv.append(g.op("row_sum", [a], f"t{i}", "f32", (R, 1)))
+            else:
+                r = rowv[rng.integers(len(rowv))]
+                rowv.append(g.op("add_imm", [r], f"t{i}", "f32", (R, 1), imm=0.5))
+        readers = {t for o in g.ops for t in o.inputs}
+        for o in g.ops:
+            t = o.output
+            if t not in readers or rng.random() < 0.1:
+                d = g.tensors[t]
+                g.tensors[t] = TensorDesc(d.name, d.dtype, d.shape, "out")
+        yield g
+
+
+def test_broadcast_dags_plan_like_the_oracle():
+    for g in _broadcast_dags(5, 300):
+        check_against_oracle(g)
+
+
+# ------------------------------------------------------------------ errors
+def _desc_status(graph_tensors, graph_ops, flags=0, version=C.ABI_VERSION):
+    g = Graph(list(graph_tensors), list(graph_ops))
+    desc, t, o = gtf._program_desc(g)
+    desc.abi_version = version
+    h = ctypes.c_void_p()
+    st = C.lib().fuse_plan_create(ctypes.byref(desc), flags, ctypes.byref(h))
+    if st == 0:
+        C.lib().fuse_plan_destroy(h)
+    else:
+        assert h.value is None
+    return st
+
+
+T = TensorDesc
+
+
+def test_descriptor_errors():
+    x = T("x", "f32", (2, 3), "in")
+    y = T("y", "f32", (2, 3), "out")
+    ok = [OpDesc("exp", (0,), 1)]
+    assert _desc_status([x, y], ok) == C.GTF_OK
+    assert _desc_status([x, y], ok, version=99) == C.GTF_E_INVALID
+    assert _desc_status([x, y], ok, flags=8) == C.GTF_E_INVALID
+    # reads a tensor no earlier op wrote (not topological)
+    tmp = T("t", "f32", (2, 3), "tmp")
+    assert _desc_status([x, tmp, y], [OpDesc("exp", (1,), 2), OpDesc("exp", (0,), 1)]) == C.GTF_E_INVALID
+    # bad ids
+    assert _desc_status([x, y], [OpDesc("exp", (5,), 1)]) == C.GTF_E_INVALID
+    assert _desc_status([x, y], [OpDesc("exp", (0,), 7)]) == C.GTF_E_INVALID
+    # writes an input, writes twice, tmp nobody reads, output never written
+    assert _desc_status([x, y], [OpDesc("exp", (1,), 0)]) == C.GTF_E_INVALID
+    assert _desc_status([x, y], [OpDesc("exp", (0,), 1), OpDesc("neg", (0,), 1)]) == C.GTF_E_INVALID
+    assert _desc_status([x, tmp, y], [OpDesc("exp", (0,), 1), OpDesc("neg", (0,), 2)]) == C.GTF_E_INVALID
+    assert _desc_status([x, y], []) == C.GTF_E_INVALID
+    # unsupported: u8 output
+    assert _desc_status([x, T("u", "u8", (2, 3), "out")], [OpDesc("exp", (0,), 1)]) == C.GTF_E_UNSUPPORTED
+    # shapes
+    assert _desc_status([x, T("z", "f32", (3, 2), "in"), y], [OpDesc("add", (0, 1), 2)]) == C.GTF_E_SHAPE
+    assert _desc_status([x, T("z", "f32", (2, 4), "out")], [OpDesc("exp", (0,), 1)]) == C.GTF_E_SHAPE
+    assert _desc_status([x, T("s", "f32", (2,), "out")], [OpDesc("row_sum", (0,), 1)]) == C.GTF_E_SHAPE
+    assert _desc_status([x, T("s", "f32", (2, 1), "out")], [OpDesc("row_sum", (0,), 1)]) == C.GTF_OK
+
+
+def test_raw_abi_errors():
+    L = C.lib()
+    assert L.fuse_plan_create(None, 0, ctypes.byref(ctypes.c_void_p())) == C.GTF_E_INVALID
+    assert L.fuse_plan_create(None, 0, None) == C.GTF_E_INVALID
+    assert b"NULL" in L.gtf_last_error()
+    n = ctypes.c_int32()
+    assert L.fuse_plan_num_groups(None, ctypes.byref(n)) == C.GTF_E_INVALID
+    bad_op = C.ProgramDesc()
+    tens = (C.TensorDesc * 2)()
+    for t in tens:
+        t.dtype, t.rank, t.role = 0, 2, 0
+        t.shape[0], t.shape[1] = 2, 3
+    tens[1].role = 1
+    ops = (C.OpDesc * 1)()
+    ops[0].opcode, ops[0].n_in, ops[0].out = 999, 1, 1
+    desc = C.ProgramDesc(C.ABI_VERSION, 2, tens, 1, ops)
+    assert L.fuse_plan_create(ctypes.byref(desc), 0, ctypes.byref(ctypes.c_void_p())) == C.GTF_E_UNSUPPORTED
+    ops[0].opcode, ops[0].n_in = 1, 2
+    assert L.fuse_plan_create(ctypes.byref(desc), 0, ctypes.byref(ctypes.c_void_p())) == C.GTF_E_INVALID
+    tens[0].dtype = 7
+    ops[0].n_in = 1
+    assert L.fuse_plan_create(ctypes.byref(desc), 0, ctypes.byref(ctypes.c_void_p())) == C.GTF_E_UNSUPPORTED
+    tens[0].dtype, tens[0].rank = 0, 3
+    assert L.fuse_plan_create(ctypes.byref(desc), 0, ctypes.byref(ctypes.c_void_p())) == C.GTF_E_UNSUPPORTED
+    tens[0].rank, tens[0].reserved = 2, 1
+    assert L.fuse_plan_create(ctypes.byref(desc), 0, ctypes.byref(ctypes.c_void_p())) == C.GTF_E_INVALID
+    # bucket plan errors
+    arr = (ctypes.c_int64 * 2)(3, -1)
+    h = ctypes.c_void_p()
+    assert L.bucket_plan_create(arr, 2, 0, 64, 0, ctypes.byref(h)) == C.GTF_E_INVALID
+    arr[1] = 4
+    assert L.bucket_plan_create(arr, 2, 2, 64, 0, ctypes.byref(h)) == C.GTF_E_UNSUPPORTED
+    assert L.bucket_plan_create(arr, 2, 0, 0, 0, ctypes.byref(h)) == C.GTF_E_INVALID
+    assert L.bucket_plan_create(arr, 2, 0, 64, 1, ctypes.byref(h)) == C.GTF_E_INVALID
+    assert L.bucket_plan_create(arr, 2, 0, 64, 0, ctypes.byref(h)) == C.GTF_OK
+    # running before bind is a state error (checked before any device call)
+    ptrs = (ctypes.c_void_p * 2)(1, 2)
+    assert L.bucket_pack(h, ptrs, ptrs, 1.0, None) == C.GTF_E_STATE
+    L.bucket_plan_destroy(h)
+
+
+def test_bucket_plans_match_the_oracle():
+    cases = [(configs.c4_numel(), 4, configs.BUCKET_CAP_BYTES),
+             (configs.c5_numel(), 4, configs.BUCKET_CAP_BYTES),
+             (configs.c5_numel(), 2, configs.BUCKET_CAP_BYTES)]
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        numel = [int(v) for v in rng.integers(0, 60, size=int(rng.integers(0, 30)))]
+        cases.append((numel, 4, int(rng.integers(1, 100)) * 4))
+    for numel, eb, cap in cases:
+        bp = gtf.BucketPlan(numel, "f32" if eb == 4 else "bf16", cap)
+        assert bp.query() == obucket.plan(numel, eb, cap)
+        chunks = sum((n + 16383) // 16384 for n in numel)
+        assert bp.workspace_bytes == 24 * chunks
