@@ -281,7 +281,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     if args.workload != "c5":
-        from bench_workloads import run_other  # noqa
+        print(json.dumps(run_config(torch, gtf, configs, args)), flush=True)
         return
     w = C5(torch, gtf, configs, args.layers)
     # timed region: K whole steps
@@ -350,6 +350,96 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_c5()
     print(json.dumps(result), flush=True)
+
+
+# ------------------------------------------------------------ c1..c4
+def _rotation_sets(set_bytes, floor=1 << 30, cap=64):
+    k = 1
+    while k * set_bytes < floor and k < cap:
+        k += 1
+    return k
+
+
+def run_config(torch, gtf, configs, args):
+    """One config on its own, with buffer rotation past the Infinity Cache;
+    fused vs unfused (c1-c3) or one launch vs per-tensor launches (c4)."""
+    w = args.workload
+    res = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic"}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(int(w[1]))
+    if w == "c4":
+        numel = configs.c4_numel()
+        bp = gtf.BucketPlan(numel, "f32", configs.BUCKET_CAP_BYTES)
+        _, _, bn = bp.query()
+        ws = torch.empty(max(16, bp.workspace_bytes), dtype=torch.uint8, device="cuda")
+        bp.bind(ws)
+        payload = 4 * sum(numel)
+        k = _rotation_sets(2 * payload)
+        sets = [([torch.randn(n, generator=gen, device="cuda") * 1e-3 for n in numel],
+                 [torch.empty(n, dtype=torch.float32, device="cuda") for n in bn]) for _ in range(k)]
+        it = [0]
+
+        def pack():
+            g, b = sets[it[0] % k]
+            it[0] += 1
+            bp.pack(g, b, configs.AVG_SCALE)
+
+        def unpack():
+            g, b = sets[it[0] % k]
+            it[0] += 1
+            bp.unpack(b, g, 1.0)
+
+        def pack_pt():
+            g, b = sets[it[0] % k]
+            it[0] += 1
+            bp.pack_per_tensor(g, b, configs.AVG_SCALE)
+        ms_p, _ = time_steps(torch, pack, args.steps, args.warmup)
+        ms_u, _ = time_steps(torch, unpack, args.steps, args.warmup)
+        ms_t, _ = time_steps(torch, pack_pt, args.steps, args.warmup)
+        gbs = 2 * payload / (ms_p * 1e-3) / 1e9
+        res.update({"value": round(gbs, 2), "ms_per_step": round(ms_p, 4),
+                    "config": {"workload": "c4: pack 161 fp32 gradient tensors (25.6M elements) into "
+                                           "25 MiB buckets x 1/8", "rotation_sets": k},
+                    "unpack_gbs": round(2 * payload / (ms_u * 1e-3) / 1e9, 2),
+                    "per_tensor_pack_ms": round(ms_t, 4),
+                    "speedup_vs_per_tensor": round(ms_t / ms_p, 3),
+                    "launches": {"one_launch": 1, "per_tensor": len([n for n in numel if n])}})
+        return res
+    if w == "c1":
+        g = configs.c1_graph()
+        dists = {"x": ("uniform", -1, 1), "a": ("uniform", -1, 1), "b": ("uniform", -1, 1)}
+        desc = "c1: y = sigmoid((x*a)*b), f32[64,512]"
+    elif w == "c2":
+        g = configs.c2_graph()
+        dists = {"X": ("normal", 0, 1), "bias": ("normal", 0, 0.1), "R": ("normal", 0, 1)}
+        desc = "c2: relu(X + bias) + R, bf16[4096,4096]"
+    else:
+        g = configs.c3_graph()
+        dists = {"P": ("uniform", -2, 2)}
+        desc = "c3: rowsum((exp(P) + P/2) + tanh(P)), bf16[8192,4096] -> f32[8192]"
+    out = {}
+    for fuse in (True, False):
+        plan = gtf.FusePlan(g, fuse=fuse)
+        nbytes = sum(group_bytes(g, plan))
+        k = _rotation_sets(nbytes) if w != "c1" else 1
+        sets = [alloc_graph(torch, gtf, g, plan, gen, dists) for _ in range(k)]
+        it = [0]
+
+        def step():
+            plan.run(sets[it[0] % k])
+            it[0] += 1
+        ms, _ = time_steps(torch, step, args.steps * (50 if w == "c1" else 1), args.warmup)
+        out[fuse] = (ms, nbytes, plan.num_groups, k)
+    ms, nbytes, ng, k = out[True]
+    res.update({"value": round(nbytes / (ms * 1e-3) / 1e9, 2), "ms_per_step": round(ms, 5),
+                "config": {"workload": desc, "rotation_sets": k, "bytes_per_step": nbytes},
+                "speedup_vs_unfused": round(out[False][0] / ms, 3),
+                "unfused": {"ms_per_step": round(out[False][0], 5), "bytes": out[False][1],
+                            "launches": out[False][2]},
+                "launches": ng})
+    return res
 
 
 def _kernel_hash():

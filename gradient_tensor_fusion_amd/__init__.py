@@ -100,6 +100,13 @@ class FusePlan:
         C.check(C.lib().fuse_plan_op_info(self._h, pats, ipd))
         return list(pats[: self.n_ops]), [None if v < 0 else v for v in ipd[: self.n_ops]]
 
+    def geometry(self, g: int) -> dict:
+        geo = C.GroupGeometry()
+        C.check(C.lib().fuse_plan_group_geometry(self._h, g, byref(geo)))
+        d = {name: getattr(geo, name) for name, _ in C.GroupGeometry._fields_}
+        d["ring_tensor"] = list(geo.ring_tensor)[: geo.ring_inputs]
+        return d
+
     def is_materialized(self, t: int) -> bool:
         y = c_int32()
         C.check(C.lib().fuse_plan_is_materialized(self._h, t, byref(y)))

@@ -33,6 +33,7 @@ NO_FUSE = 1
 
 EXPORTED = (
     "fuse_plan_create", "fuse_plan_num_groups", "fuse_plan_group_info", "fuse_plan_op_info",
+    "fuse_plan_group_geometry",
     "fuse_plan_is_materialized", "fuse_group_run", "fuse_plan_run", "fuse_plan_destroy",
     "bucket_plan_create", "bucket_plan_query", "bucket_plan_workspace_bytes",
     "bucket_plan_bind", "bucket_pack", "bucket_unpack", "bucket_pack_per_tensor",
@@ -48,6 +49,14 @@ class TensorDesc(ctypes.Structure):
 class OpDesc(ctypes.Structure):
     _fields_ = [("opcode", c_int32), ("n_in", c_int32), ("inp", c_int32 * 3), ("out", c_int32),
                 ("imm", c_float), ("flags", c_int32)]
+
+
+class GroupGeometry(ctypes.Structure):
+    _fields_ = [("rows", c_int64), ("cols", c_int64), ("items", c_int64), ("panels", c_int32),
+                ("rows_per_item", c_int32), ("panel_width", c_int32), ("threads_per_row", c_int32),
+                ("ring_inputs", c_int32), ("ring_stages", c_int32), ("ring_stage_bytes", c_int32),
+                ("lds_bytes", c_int32), ("program_length", c_int32), ("spill_slots", c_int32),
+                ("reduce", c_int32), ("ring_tensor", c_int32 * 4)]
 
 
 class ProgramDesc(ctypes.Structure):
@@ -78,6 +87,7 @@ def lib() -> ctypes.CDLL:
                                            POINTER(c_int32), POINTER(c_int32)]
         L.fuse_plan_op_info.argtypes = [vp, POINTER(c_int32), POINTER(c_int32)]
         L.fuse_plan_is_materialized.argtypes = [vp, c_int32, POINTER(c_int32)]
+        L.fuse_plan_group_geometry.argtypes = [vp, c_int32, POINTER(GroupGeometry)]
         L.fuse_group_run.argtypes = [vp, c_int32, POINTER(vp), vp]
         L.fuse_plan_run.argtypes = [vp, POINTER(vp), vp]
         L.fuse_plan_destroy.argtypes = [vp]

@@ -197,6 +197,29 @@ int fuse_plan_op_info(const gtf_fuse_plan* plan, int32_t* pattern_kind, int32_t*
   return GTF_OK;
 }
 
+int fuse_plan_group_geometry(const gtf_fuse_plan* plan, int32_t g, gtf_group_geometry* out) {
+  if (plan == nullptr || out == nullptr) return fail(GTF_E_INVALID, "NULL argument");
+  if (g < 0 || g >= (int32_t)plan->p.groups.size()) return fail(GTF_E_INVALID, "group index");
+  const CompiledGroup& cg = plan->p.groups[g].code;
+  const ExecArgs& a = cg.args;
+  out->rows = a.R;
+  out->cols = a.C;
+  out->items = a.n_items;
+  out->panels = a.n_panels;
+  out->rows_per_item = a.RB;
+  out->panel_width = a.PW;
+  out->threads_per_row = 1 << a.tpr_log2;
+  out->ring_inputs = a.n_pipe;
+  out->ring_stages = a.n_stage;
+  out->ring_stage_bytes = a.stage_bytes;
+  out->lds_bytes = cg.lds_bytes;
+  out->program_length = a.n_col + a.n_row + a.n_elem;
+  out->spill_slots = cg.max_depth;
+  out->reduce = a.reduce;
+  for (int k = 0; k < 4; ++k) out->ring_tensor[k] = k < a.n_pipe ? cg.slot_tensor[a.pipe_slot[k]] : -1;
+  return GTF_OK;
+}
+
 int fuse_plan_is_materialized(const gtf_fuse_plan* plan, int32_t tensor_id, int32_t* yes) {
   if (plan == nullptr || yes == nullptr) return fail(GTF_E_INVALID, "NULL argument");
   if (tensor_id < 0 || tensor_id >= (int32_t)plan->p.tensors.size())

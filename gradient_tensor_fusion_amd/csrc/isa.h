@@ -3,9 +3,8 @@
 //
 // A fused group (TVM "Operator Fusion": FuseOps groups, FuseTIR merges the
 // group's functions so intermediates never reach device memory) runs as one
-// launch of an interpreter over a small stack machine whose slots are
-// vector registers.  The host compiles each group into up to three
-// programs:
+// launch of an interpreter whose values are vector registers.  The host
+// compiles each group into up to three programs:
 //
 //   column phase  once per column of the staged panel (values shaped [1,C]);
 //                 results go to LDS column slots.
@@ -14,11 +13,12 @@
 //   element phase once per tile of kV consecutive elements of one row;
 //                 reads rows/columns from LDS, streams [R,C] tensors.
 //
-// Each instruction is {code, arg, imm}.  code = form * kNR + d, where d is
-// the slot the instruction writes (or reads, for stores and reductions), so
-// every register access in the kernel has a compile-time index and the
-// slots stay in VGPRs.  Dispatch is wave-uniform (the program is the same
-// for every lane), a scalar branch per instruction.
+// The machine has two working registers A and B and kNS spill slots, each
+// holding one tile.  Every op reads A (and B) and writes A; moves between
+// A, B and the slots are explicit instructions.  Each instruction form has
+// exactly one body in the kernel, so the interpreter stays small enough for
+// the instruction cache, and every register index is a compile-time
+// constant, so the registers stay in VGPRs.
 #pragma once
 
 #include <stdint.h>
@@ -26,46 +26,50 @@
 namespace gtf {
 
 constexpr int kV = 8;            // elements per lane per tile
-constexpr int kNR = 8;           // stack slots
-constexpr int kMaxInstr = 288;   // instructions over all three phases
+constexpr int kNS = 6;           // spill slots
+constexpr int kMaxInstr = 320;   // instructions over all three phases
 constexpr int kMaxSlots = 16;    // external tensors of one group
 constexpr int kMaxLdsCol = 4;    // LDS column slots
 constexpr int kMaxLdsRow = 8;    // LDS row slots
 constexpr int kBlock = 256;      // threads per workgroup
 constexpr int kPanelMax = 4096;  // widest column panel staged in LDS
+constexpr int kMaxPipe = 4;      // element inputs streamed through the LDS ring
+constexpr int kRingBudget = 48 * 1024;  // LDS bytes for the rings of one workgroup
 
 enum Form : int {
-  // push from memory: arg = external tensor slot
-  F_LD_F32 = 0, F_LD_BF16, F_LD_U8,
-  // push a broadcast value: arg = LDS column slot / LDS row slot; imm
-  F_PUSH_COL, F_PUSH_ROW, F_PUSH_IMM,
-  // push a copy of slot arg
-  F_PICK,
-  // unary, in place on slot d
+  // load a tile of external tensor slot `arg` into A / into B
+  F_LD_F32_A = 0, F_LD_BF16_A, F_LD_U8_A, F_LD_F32_B, F_LD_BF16_B, F_LD_U8_B,
+  // broadcast value into A / B: LDS column slot arg, LDS row slot arg, imm
+  F_COL_A, F_ROW_A, F_IMM_A, F_COL_B, F_ROW_B, F_IMM_B,
+  // moves
+  F_A2B, F_B2A,
+  F_A2S0, F_A2S1, F_A2S2, F_A2S3, F_A2S4, F_A2S5,
+  F_B2S0, F_B2S1, F_B2S2, F_B2S3, F_B2S4, F_B2S5,
+  F_S02A, F_S12A, F_S22A, F_S32A, F_S42A, F_S52A,
+  F_S02B, F_S12B, F_S22B, F_S32B, F_S42B, F_S52B,
+  // A = f(A)
   F_EXP, F_TANH, F_SIGMOID, F_RELU, F_GELU, F_SQUARE, F_SQRT, F_RECIP, F_NEG,
-  // binary on slots d (left) and d+1 (right), result in d
-  F_ADD, F_SUB, F_MUL, F_DIV, F_MAX, F_MIN,
-  // slot d = slot d (op) X, X = LDS column slot arg
+  // A = A op B (RSUB: B - A, RDIV: B / A)
+  F_ADD, F_SUB, F_RSUB, F_MUL, F_DIV, F_RDIV, F_MAX, F_MIN,
+  // A = A op X, X = LDS column slot arg / LDS row slot arg / imm
   F_ADD_C, F_SUB_C, F_RSUB_C, F_MUL_C, F_DIV_C, F_RDIV_C, F_MAX_C, F_MIN_C,
-  // X = LDS row slot arg
   F_ADD_R, F_SUB_R, F_RSUB_R, F_MUL_R, F_DIV_R, F_RDIV_R, F_MAX_R, F_MIN_R,
-  // X = imm
   F_ADD_I, F_SUB_I, F_RSUB_I, F_MUL_I, F_DIV_I, F_RDIV_I, F_MAX_I, F_MIN_I,
-  // store slot d to external tensor slot arg (no pop)
+  // store A to external tensor slot arg
   F_ST_F32, F_ST_BF16,
-  // add slot d into the row accumulator (element phase only)
+  // add A into the row accumulator (element phase)
   F_RED,
-  // store slot d to LDS slot arg (column slot in the column phase, row slot
-  // in the row phase)
+  // store A to LDS slot arg (column slot in the column phase, row slot in
+  // the row phase)
   F_ST_LDS,
   F_COUNT
 };
 
-// binary-with-X forms are laid out as 8 consecutive ops per operand class
+// binary ops in the order of the A op B / A op X families
 enum XOp : int { X_ADD = 0, X_SUB, X_RSUB, X_MUL, X_DIV, X_RDIV, X_MAX, X_MIN };
 
 struct Instr {
-  uint16_t code;  // form * kNR + d
+  uint16_t code;  // Form
   uint16_t arg;
   float imm;
 };
@@ -85,7 +89,16 @@ struct ExecArgs {
   int32_t red_dtype;       // reduce output dtype
   int32_t red_slot;        // external slot of the reduce output
   int32_t vec_ok;          // element tensors and rows are 16-byte aligned
-  int32_t pad0;
+  // element-phase inputs streamed through a per-wave LDS ring, n_stage
+  // tiles ahead (direct global -> LDS loads)
+  int32_t n_pipe;          // pipelined inputs (<= kMaxPipe)
+  int32_t n_stage;         // ring depth in tiles
+  int32_t n_dma;           // DMA instructions per tile (all pipelined inputs)
+  int32_t stage_bytes;     // LDS bytes of one ring stage of one wave
+  int32_t ring_lds_off;    // byte offset of the ring in dynamic LDS
+  int32_t pipe_slot[4];    // external slot of each pipelined input
+  int32_t pipe_dt[4];      // its dtype
+  int32_t ring_off[kMaxSlots];  // byte offset of a slot inside a stage, -1 if direct
   void* ptr[kMaxSlots];
   int64_t rstride[kMaxSlots];
   int64_t cstride[kMaxSlots];

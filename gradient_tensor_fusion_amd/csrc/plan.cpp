@@ -120,6 +120,7 @@ int count_args(const FusePlan& p, const std::vector<char>& in_set) {
 namespace {
 
 enum Cls { CLS_E = 0, CLS_ROW = 1, CLS_COL = 2 };
+constexpr int kNoValue = -1;
 
 struct MOp {
   int kind;    // 0 unary form, 1 binary op, 2 imm op (slot op imm), 3 reduce, 4 copy
@@ -174,187 +175,178 @@ bool commutative(int binform) {
   return binform == F_ADD || binform == F_MUL || binform == F_MAX || binform == F_MIN;
 }
 
+// Register allocation for the A/B machine.  Values are tensor ids (>= 0) or
+// synthetic temporaries (<= -2).  A value lives in any of A, B and the
+// spill slots; it is spilled only when the register it sits in is about to
+// be overwritten while it still has readers.
 struct Codegen {
   const FusePlan& p;
   std::vector<Instr>* out;
   int phase;  // CLS_E / CLS_ROW / CLS_COL
-  // value ids are tensor ids (>= 0) or synthetic temporaries (<= -2)
-  std::map<int, int> uses;       // remaining stack uses in this phase
+  std::map<int, int> uses;       // remaining reads in this phase
   std::set<int> loadable;        // external tensors this phase loads
-  std::set<int> loaded;
   std::map<int, int> ext_slot;   // tensor -> external slot
   std::map<int, int> lds_slot;   // value -> LDS slot (values read via X)
   std::map<int, int> xcls;       // value -> CLS_ROW / CLS_COL for X operands
-  std::vector<int> stack;        // value id per slot
-  int max_depth = 0;
+  static constexpr int kEmpty = -1000000;
+  enum { RA = 0, RB = 1 };       // register ids: 0 = A, 1 = B, 2.. = spill slots
+  int reg[2 + kNS];
+  int max_live = 0;
   bool ok = true;
   std::string why;
 
-  static constexpr int kDead = -1000000;
-
-  void emit(int form, int d, int arg = 0, float imm = 0.f) {
-    if (d < 0 || d >= kNR) {
-      ok = false;
-      why = "op-program needs more than the kernel's stack slots";
-      return;
-    }
+  void init() {
+    for (int& r : reg) r = kEmpty;
+  }
+  void emit(int form, int arg = 0, float imm = 0.f) {
     Instr ins;
-    ins.code = (uint16_t)(form * kNR + d);
+    ins.code = (uint16_t)form;
     ins.arg = (uint16_t)arg;
     ins.imm = imm;
     out->push_back(ins);
   }
-  int top() const { return (int)stack.size() - 1; }
-  void push(int v) {
-    stack.push_back(v);
-    max_depth = std::max(max_depth, (int)stack.size());
-    if ((int)stack.size() > kNR) {
-      ok = false;
-      why = "op-program needs more than the kernel's stack slots";
-    }
-  }
-  int slot_of(int v) const {
-    for (int i = top(); i >= 0; --i)
-      if (stack[i] == v) return i;
-    return -1;
-  }
-  bool is_x(int v) const { return xcls.count(v) != 0; }
   int use(int v) const {
     auto it = uses.find(v);
     return it == uses.end() ? 0 : it->second;
   }
-  bool unloaded(int v) const { return loadable.count(v) && !loaded.count(v); }
-
-  int load_form(int t) const {
+  bool is_x(int v) const { return xcls.count(v) != 0; }
+  bool live(int r) const { return reg[r] != kEmpty && use(reg[r]) > 0; }
+  int where(int v, int avoid = -1) const {
+    for (int r = 0; r < 2 + kNS; ++r)
+      if (r != avoid && reg[r] == v) return r;
+    return -1;
+  }
+  int holders(int v) const {
+    int n = 0;
+    for (int r : reg)
+      if (r == v) ++n;
+    return n;
+  }
+  void count_live() {
+    int n = 0;
+    for (int r = 2; r < 2 + kNS; ++r)
+      if (live(r)) ++n;
+    max_live = std::max(max_live, n);
+  }
+  void move(int from, int to) {
+    static const int a2s = F_A2S0, b2s = F_B2S0, s2a = F_S02A, s2b = F_S02B;
+    int f;
+    if (from == RA && to == RB) f = F_A2B;
+    else if (from == RB && to == RA) f = F_B2A;
+    else if (from == RA) f = a2s + (to - 2);
+    else if (from == RB) f = b2s + (to - 2);
+    else if (to == RA) f = s2a + (from - 2);
+    else f = s2b + (from - 2);
+    emit(f);
+    reg[to] = reg[from];
+  }
+  // keep the value in register r alive elsewhere before r is overwritten
+  void save(int r) {
+    if (!live(r) || holders(reg[r]) > 1) return;
+    for (int s = 2; s < 2 + kNS; ++s)
+      if (!live(s)) {
+        move(r, s);
+        count_live();
+        return;
+      }
+    ok = false;
+    why = "op-program needs more than the kernel's spill slots";
+  }
+  int load_form(int t, int r) const {
+    const int base = r == RA ? F_LD_F32_A : F_LD_F32_B;
     switch (p.tensors[t].dtype) {
-      case GTF_F32: return F_LD_F32;
-      case GTF_BF16: return F_LD_BF16;
-      default: return F_LD_U8;
+      case GTF_F32: return base;
+      case GTF_BF16: return base + 1;
+      default: return base + 2;
     }
   }
-  void load(int v) {
-    loaded.insert(v);
-    push(v);
-    emit(load_form(v), top(), ext_slot.at(v));
-  }
-  // A value read again later is loaded once, into a home slot that stays.
-  void ensure_home(int v) {
-    if (unloaded(v) && use(v) > 1) load(v);
-  }
-  // Push a consumable instance of v on top.
-  void fetch(int v) {
-    if (unloaded(v)) {
-      load(v);
-      return;
-    }
-    int s = slot_of(v);
-    if (s < 0) {
+  // make register r (A or B) hold v, without disturbing the other of A/B
+  void bring(int v, int r) {
+    if (reg[r] == v) return;
+    save(r);
+    const int from = where(v, r);
+    if (from >= 0) {
+      move(from, r);
+    } else if (loadable.count(v)) {
+      emit(load_form(v, r), ext_slot.at(v));
+      reg[r] = v;
+    } else if (is_x(v)) {
+      const bool col = xcls.at(v) == CLS_COL;
+      emit(r == RA ? (col ? F_COL_A : F_ROW_A) : (col ? F_COL_B : F_ROW_B), lds_slot.at(v));
+      reg[r] = v;
+    } else {
       ok = false;
-      why = "internal: operand not on the stack";
-      return;
+      why = "internal: operand not available";
     }
-    push(v);
-    emit(F_PICK, top(), s);
   }
-  bool top_consumable(int v) const {
-    return top() >= 0 && stack[top()] == v && use(v) == 1;
-  }
-  void drop_dead_top() {
-    while (!stack.empty() && stack.back() == kDead) stack.pop_back();
-  }
-  void used_once(int v) {
-    if (--uses[v] == 0)
-      for (int i = 0; i <= top(); ++i)
-        if (stack[i] == v) stack[i] = kDead;
+  // A is about to be overwritten by the result of an op that read `a` there
+  void consume_a(int a) {
+    uses[a] -= 1;
+    save(RA);
   }
   void x_info(int v, int* base, int* arg) {
     *base = xcls.at(v) == CLS_COL ? F_ADD_C : F_ADD_R;
     *arg = lds_slot.at(v);
   }
-  // one stack operand, rewritten in place: returns the slot
-  int operand_on_top(int a) {
-    ensure_home(a);
-    if (!top_consumable(a)) fetch(a);
-    return top();
-  }
-  void finish_in_place(int a, int d, int result) {
-    stack[d] = kDead;  // the consumed instance
-    used_once(a);
-    stack[d] = result;
-  }
 
   void run_unary(const MOp& m) {
-    int a = m.in[0];
-    int d = operand_on_top(a);
-    emit(m.form, d);
-    finish_in_place(a, d, m.out);
+    bring(m.in[0], RA);
+    consume_a(m.in[0]);
+    emit(m.form);
+    reg[RA] = m.out;
   }
-  void run_copy(const MOp& m) {  // a rename; a copy only when a lives on
-    int a = m.in[0];
-    int d = operand_on_top(a);
-    finish_in_place(a, d, m.out);
+  void run_copy(const MOp& m) {
+    bring(m.in[0], RA);
+    consume_a(m.in[0]);
+    reg[RA] = m.out;
   }
-  void run_imm(const MOp& m) {  // slot (op) imm
-    int a = m.in[0];
-    int d = operand_on_top(a);
-    emit(F_ADD_I + m.form, d, 0, m.imm);
-    finish_in_place(a, d, m.out);
+  void run_imm(const MOp& m) {
+    bring(m.in[0], RA);
+    consume_a(m.in[0]);
+    emit(F_ADD_I + m.form, 0, m.imm);
+    reg[RA] = m.out;
   }
   void run_binary(const MOp& m) {
     int a = m.in[0], b = m.in[1];
-    bool xa = is_x(a), xb = is_x(b);
-    if (xa && xb) {  // both broadcast: push the left one, then X-op the right
-      int base, arg;
-      x_info(a, &base, &arg);
-      push(m.out);
-      emit(base == F_ADD_C ? F_PUSH_COL : F_PUSH_ROW, top(), arg);
-      x_info(b, &base, &arg);
-      emit(base + xop_of(m.form, false), top(), arg);
-      return;
-    }
-    if (xa || xb) {
-      int s = xa ? b : a, x = xa ? a : b;
-      int d = operand_on_top(s);
+    const bool xa = is_x(a), xb = is_x(b);
+    if (xb || (xa && !xb)) {
+      // one operand read as X straight from LDS
+      const int s = xb ? a : b, x = xb ? b : a;
+      if (xa && xb) {
+        bring(a, RA);  // a broadcast value pushed into A
+        uses[a] -= 0;
+      } else {
+        bring(s, RA);
+        consume_a(s);
+      }
       int base, arg;
       x_info(x, &base, &arg);
-      emit(base + xop_of(m.form, xa), d, arg);
-      finish_in_place(s, d, m.out);
+      emit(base + xop_of(m.form, /*x_on_left=*/!xb), arg);
+      reg[RA] = m.out;
       return;
     }
-    ensure_home(a);
-    if (b != a) ensure_home(b);
-    bool in_place = a != b && top() >= 1 && use(a) == 1 && use(b) == 1;
-    if (in_place && stack[top() - 1] == a && stack[top()] == b) {
-      // operands already in order
-    } else if (in_place && m.commutative && stack[top() - 1] == b && stack[top()] == a) {
-      // commutative: either order gives the same IEEE result
-    } else if (a != b && top_consumable(a)) {
-      fetch(b);
-    } else if (m.commutative && a != b && top_consumable(b)) {
-      fetch(a);
+    // both operands are values: A op B, or B (op) A with the reversed form
+    int cost_ab = (reg[RA] == a ? 0 : 1) + (reg[RB] == b ? 0 : 1);
+    int cost_ba = (reg[RA] == b ? 0 : 1) + (reg[RB] == a ? 0 : 1);
+    const bool swap = a != b && cost_ba < cost_ab;
+    const int first = swap ? b : a, second = swap ? a : b;
+    bring(first, RA);
+    if (a == b) {
+      save(RB);
+      move(RA, RB);
     } else {
-      fetch(a);
-      fetch(b);
+      bring(second, RB);
     }
-    int d = top() - 1;
-    emit(m.form, d);
-    stack[d] = kDead;
-    stack[d + 1] = kDead;
-    used_once(a);
-    used_once(b);
-    stack.pop_back();
-    stack[d] = m.out;
+    uses[a] -= 1;
+    uses[b] -= 1;
+    save(RA);  // B keeps its value
+    emit(swap ? F_ADD + xop_of(m.form, true) : F_ADD + xop_of(m.form, false));
+    reg[RA] = m.out;
   }
-  void run_reduce(const MOp& m) {  // reads a slot, writes nothing
-    int a = m.in[0];
-    int s = slot_of(a);
-    if (s < 0) {
-      fetch(a);
-      s = top();
-    }
-    emit(F_RED, s);
-    used_once(a);
-    drop_dead_top();
+  void run_reduce(const MOp& m) {
+    bring(m.in[0], RA);
+    uses[m.in[0]] -= 1;
+    emit(F_RED);
   }
 };
 
@@ -568,6 +560,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   const int order[3] = {CLS_COL, CLS_ROW, CLS_E};
   for (int ph : order) {
     Codegen g{p, &prog[ph], ph};
+    g.init();
     for (size_t k = 0; k < slots.size(); ++k) g.ext_slot[slots[k]] = (int)k;
     if (ph == CLS_E) {  // broadcast operands are read from LDS
       for (auto& kv : row_lds) {
@@ -583,9 +576,9 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     std::set<int> made_here;
     for (auto& m : L) made_here.insert(m.out);
     for (auto& m : L) {
-      int n_st = m.kind == 1 ? 2 : 1;
-      for (int k = 0; k < n_st; ++k) {
-        int v = m.in[k];
+      const int n_in = m.kind == 1 ? 2 : 1;
+      for (int k = 0; k < n_in; ++k) {
+        const int v = m.in[k];
         if (g.is_x(v)) continue;
         g.uses[v] += 1;
         if (v >= 0 && !produced.count(v)) g.loadable.insert(v);
@@ -595,39 +588,32 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     const auto& lds_map = ph == CLS_ROW ? row_lds : col_lds;
     if (ph != CLS_E) {
       for (auto& kv : lds_map) {
-        int t = kv.first;
-        if (produced.count(t)) continue;
-        g.loadable.insert(t);
-        int s = g.slot_of(t);
-        if (s < 0) {
-          g.load(t);
-          s = g.top();
-        }
-        g.emit(F_ST_LDS, s, kv.second);
-        if (g.use(t) == 0) {
-          g.stack.pop_back();
-          g.drop_dead_top();
-        }
+        if (produced.count(kv.first)) continue;
+        g.loadable.insert(kv.first);
+        g.bring(kv.first, Codegen::RA);
+        g.emit(F_ST_LDS, kv.second);
       }
     }
-    // list scheduling: among ready micro-ops prefer the one whose operand
-    // sits highest on the stack (fewest copies)
+    // list scheduling: among ready micro-ops prefer one whose operands
+    // already sit in A (and B)
     std::vector<char> done(L.size(), 0);
     std::set<int> avail;
     for (size_t step = 0; step < L.size() && g.ok; ++step) {
-      int best = -1, best_score = -1000;
+      int best = -1, best_score = -1;
       for (size_t k = 0; k < L.size(); ++k) {
         if (done[k]) continue;
-        int n_st = L[k].kind == 1 ? 2 : 1;
+        const int n_in = L[k].kind == 1 ? 2 : 1;
         bool rdy = true;
-        int score = -1;
-        for (int q = 0; q < n_st; ++q) {
-          int v = L[k].in[q];
-          if (made_here.count(v) && !avail.count(v)) rdy = false;
-          int s = g.slot_of(v);
-          if (s >= 0) score = std::max(score, s);
-        }
-        if (rdy && score > best_score) {
+        for (int q = 0; q < n_in; ++q)
+          if (made_here.count(L[k].in[q]) && !avail.count(L[k].in[q])) rdy = false;
+        if (!rdy) continue;
+        // every binary op has a reversed form, so either operand may sit in A
+        const int x0 = L[k].in[0], x1 = n_in == 2 ? L[k].in[1] : kNoValue;
+        const int ra = g.reg[Codegen::RA], rb = g.reg[Codegen::RB];
+        int score = 0;
+        if (ra == x0 || ra == x1) score += 2;
+        if (n_in == 2 && ((rb == x1 && ra != x1) || (rb == x0 && ra != x0))) score += 1;
+        if (score > best_score) {
           best_score = score;
           best = (int)k;
         }
@@ -645,19 +631,13 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
       if (!g.ok) break;
       if (m.kind == 3) continue;
       avail.insert(m.out);
-      int v = m.out;
-      if (v >= 0 && outputs.count(v)) {
-        int dt = p.tensors[v].dtype;
-        g.emit(dt == GTF_BF16 ? F_ST_BF16 : F_ST_F32, g.top(), g.ext_slot.at(v));
-      }
-      if (ph != CLS_E && v >= 0 && lds_map.count(v)) g.emit(F_ST_LDS, g.top(), lds_map.at(v));
-      if (g.use(v) == 0) {
-        g.stack.pop_back();
-        g.drop_dead_top();
-      }
+      const int v = m.out;
+      if (v >= 0 && outputs.count(v))
+        g.emit(p.tensors[v].dtype == GTF_BF16 ? F_ST_BF16 : F_ST_F32, g.ext_slot.at(v));
+      if (ph != CLS_E && v >= 0 && lds_map.count(v)) g.emit(F_ST_LDS, lds_map.at(v));
     }
     if (!g.ok) return bad(g.why);
-    max_depth = std::max(max_depth, g.max_depth);
+    max_depth = std::max(max_depth, g.max_live);
   }
 
   size_t total = prog[0].size() + prog[1].size() + prog[2].size();
@@ -736,12 +716,71 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
       a.cstride[s] = 0;
     }
   }
+  // element inputs streamed through the per-wave LDS ring: a tile of kV
+  // elements is 2 x 16 B (f32), 16 B (bf16) or 2 x 4 B (u8) per lane
+  for (int s = 0; s < kMaxSlots; ++s) a.ring_off[s] = -1;
+  a.n_pipe = 0;
+  a.n_dma = 0;
+  a.stage_bytes = 0;
+  {
+    std::set<int> elem_loads;
+    for (int i : ops) {
+      if (op_cls(i) != CLS_E) continue;
+      for (int k = 0; k < p.ops[i].n_in; ++k) {
+        int t = p.ops[i].in[k];
+        if (!produced.count(t) && cls_of(t) == CLS_E) elem_loads.insert(t);
+      }
+    }
+    for (size_t s = 0; s < slots.size() && a.n_pipe < kMaxPipe; ++s) {
+      if (!elem_loads.count(slots[s])) continue;
+      const int dt = p.tensors[slots[s]].dtype;
+      a.pipe_slot[a.n_pipe] = (int)s;
+      a.pipe_dt[a.n_pipe] = dt == GTF_F32 ? DT_F32 : dt == GTF_BF16 ? DT_BF16 : DT_U8;
+      a.ring_off[s] = a.stage_bytes;
+      a.stage_bytes += dt == GTF_F32 ? 2048 : dt == GTF_BF16 ? 1024 : 512;
+      a.n_dma += dt == GTF_BF16 ? 1 : 2;
+      a.n_pipe += 1;
+    }
+  }
+  // The ring needs at least one whole tile in the domain: a lane whose tile
+  // is out of range loads the tensor's first tile instead.  Its depth is
+  // bounded by the 63 loads vmcnt can count and by the LDS left over.
+  const int64_t staged_lds = (int64_t)col_lds.size() * pw * 4 + (int64_t)row_lds.size() * rb * 4 + 16 * 4 + 16;
+  const int64_t ring_room = std::min<int64_t>(kRingBudget, 64 * 1024 - staged_lds);
+  if (a.n_pipe > 0 && DC >= kV && DR >= 1 && ring_room >= 2 * (kBlock / 64) * (int64_t)a.stage_bytes) {
+    int st = std::min(8, 1 + 63 / a.n_dma);
+    st = std::min<int64_t>(st, ring_room / ((kBlock / 64) * a.stage_bytes));
+    a.n_stage = st;
+  } else {
+    a.n_pipe = 0;
+    a.n_stage = 0;
+    a.n_dma = 0;
+    a.stage_bytes = 0;
+    for (int s = 0; s < kMaxSlots; ++s) a.ring_off[s] = -1;
+  }
+  // element-phase loads carry their ring offset in the immediate field
+  // (-1: read the tensor directly); other phases always read directly
+  {
+    const int e0 = a.n_col + a.n_row;
+    for (int k = 0; k < a.n_col + a.n_row + a.n_elem; ++k) {
+      Instr& ins = a.prog[k];
+      const bool ld = ins.code == F_LD_F32_A || ins.code == F_LD_BF16_A || ins.code == F_LD_U8_A ||
+                      ins.code == F_LD_F32_B || ins.code == F_LD_BF16_B || ins.code == F_LD_U8_B;
+      if (!ld) continue;
+      const int32_t off = k >= e0 ? a.ring_off[ins.arg] : -1;
+      std::memcpy(&ins.imm, &off, sizeof(off));
+    }
+  }
   cg.slot_tensor = slots;
   for (int t : slots) cg.slot_numel.push_back(p.tensors[t].R * p.tensors[t].C);
   cg.n_slots = (int)slots.size();
   cg.max_depth = max_depth;
-  cg.lds_bytes = (int)(a.n_col_slots * (int64_t)pw * 4 + a.n_row_slots * (int64_t)rb * 4 +
-                       kBlock / 64 * 4 * 4);
+  {
+    int64_t off = a.n_col_slots * (int64_t)pw * 4 + a.n_row_slots * (int64_t)rb * 4 + 16 * 4;
+    off = (off + 15) / 16 * 16;
+    a.ring_lds_off = (int)off;
+    cg.lds_bytes = (int)(off + (int64_t)(kBlock / 64) * a.n_stage * a.stage_bytes);
+  }
   if (cg.lds_bytes > 64 * 1024) return bad("LDS staging exceeds 64 KiB");
   if (outp) *outp = cg;
   return true;
@@ -885,8 +924,8 @@ int build_fuse_plan(FusePlan* p, bool fuse) {
                    1 << a.tpr_log2, a.n_col, a.n_row, a.n_elem, G.code.max_depth);
       int tot = a.n_col + a.n_row + a.n_elem;
       for (int k = 0; k < tot; ++k)
-        std::fprintf(stderr, "    %3d form %2d d %d arg %d imm %g\n", k, a.prog[k].code / kNR,
-                     a.prog[k].code % kNR, a.prog[k].arg, a.prog[k].imm);
+        std::fprintf(stderr, "    %3d form %2d arg %d imm %g\n", k, a.prog[k].code, a.prog[k].arg,
+                     a.prog[k].imm);
     }
   }
   return GTF_OK;

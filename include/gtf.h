@@ -171,6 +171,28 @@ int fuse_plan_group_info(const gtf_fuse_plan* plan, int32_t g, int32_t* op_ids, 
  * entries; ipdom[i] = -1 when op i has no immediate post-dominator). */
 int fuse_plan_op_info(const gtf_fuse_plan* plan, int32_t* pattern_kind, int32_t* ipdom);
 
+/* Launch shape of group g, for diagnostics and for checking the kernel's
+ * address arithmetic on the host. */
+typedef struct {
+  int64_t rows, cols;     /* launch domain; a group with no broadcast operand
+                             and no reduction runs flat as 1 x numel        */
+  int64_t items;          /* work items = row blocks x column panels        */
+  int32_t panels;         /* column panels (staged in LDS one at a time)    */
+  int32_t rows_per_item;
+  int32_t panel_width;    /* columns per panel, a multiple of 8             */
+  int32_t threads_per_row;
+  int32_t ring_inputs;    /* element inputs streamed through the LDS ring   */
+  int32_t ring_stages;    /* tiles in flight per wave                       */
+  int32_t ring_stage_bytes;
+  int32_t lds_bytes;      /* dynamic LDS per workgroup                      */
+  int32_t program_length; /* op-program instructions, all phases            */
+  int32_t spill_slots;    /* op-program spill slots used (of 6)             */
+  int32_t reduce;         /* 0 none, 1 row sum, 2 row mean                  */
+  int32_t ring_tensor[4]; /* tensor id of each ring input                   */
+} gtf_group_geometry;
+
+int fuse_plan_group_geometry(const gtf_fuse_plan* plan, int32_t g, gtf_group_geometry* out);
+
 /* *yes = 1 when tensor_id must live in device memory during a run: every
  * in and out tensor, and each tmp read by a group other than its
  * producer's.  The caller allocates those; other tmps need no memory. */
