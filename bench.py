@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the unfused and per-tensor baselines")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a c5 run into profiles/traffic_c5.txt and exit (no GPU)")
     return ap.parse_args()
 
 
@@ -114,24 +117,28 @@ DROP_D = {"h": ("normal", 0.0, 1.0), "mask": ("bernoulli", 0.1, 0.0), "R": ("nor
 
 
 class Timer:
-    """Event pairs around launches of one kernel, on the current stream."""
+    """Event pairs around launches of one kernel, on the current stream (the
+    stream the kernels are launched on).  Events are created up front so
+    that recording one costs the host only the record call."""
 
-    def __init__(self, torch, enabled):
-        self.torch, self.enabled, self.pairs = torch, enabled, []
+    def __init__(self, torch, n):
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+        self.i = 0
 
     def around(self, fn):
-        if not self.enabled:
-            fn()
-            return
-        e0 = self.torch.cuda.Event(enable_timing=True)
-        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0, e1 = self.ev[self.i]
+        self.i += 1
         e0.record()
         fn()
         e1.record()
-        self.pairs.append((e0, e1))
 
     def total_ms(self):
-        return sum(a.elapsed_time(b) for a, b in self.pairs)
+        return sum(a.elapsed_time(b) for a, b in self.ev[: self.i])
+
+    @property
+    def count(self):
+        return self.i
 
 
 # ------------------------------------------------------------ c5 workload
@@ -164,6 +171,7 @@ class C5:
                        (("ln", self.g_ln), ("ge", self.g_ge), ("do", self.g_do))}
         self.bucket_bytes = 2 * 4 * sum(numel)  # pack; unpack moves the same
         self.launches = layers * sum(p.num_groups for p in self.p.values()) + 2
+        self.bind()
 
     def bytes_per_step(self):
         per_layer = sum(sum(v) for v in self.gbytes.values())
@@ -172,22 +180,33 @@ class C5:
     def exec_bytes_per_step(self):
         return sum(sum(v) for v in self.gbytes.values()) * len(self.layers)
 
-    def step(self, exec_t=None, bucket_t=None, per_tensor=False):
+    def bind(self):
+        """Marshal every launch of a step once (pointer arrays, stream)."""
+        self.exec_calls = []
         for L in self.layers:
             for k in ("ln", "ge", "do"):
-                plan, bufs = self.p[k], L[k]
-                for g in range(plan.num_groups):
-                    if exec_t is None:
-                        plan.run_group(g, bufs)
-                    else:
-                        exec_t.around(lambda: plan.run_group(g, bufs))
-        pack = (self.bp.pack_per_tensor if per_tensor else self.bp.pack)
-        if bucket_t is None:
-            pack(self.grads, self.buckets, self.scale)
+                plan = self.p[k]
+                self.exec_calls += [plan.launcher(g, L[k]) for g in range(plan.num_groups)]
+        self.bucket_calls = [self.bp.launcher(False, self.grads, self.buckets, self.scale),
+                             self.bp.launcher(True, self.grads, self.buckets, 1.0)]
+
+    def step(self, exec_t=None, bucket_t=None, per_tensor=False):
+        if per_tensor:
+            for f in self.exec_calls:
+                f()
+            self.bp.pack_per_tensor(self.grads, self.buckets, self.scale)
             self.bp.unpack(self.buckets, self.grads, 1.0)
-        else:
-            bucket_t.around(lambda: pack(self.grads, self.buckets, self.scale))
-            bucket_t.around(lambda: self.bp.unpack(self.buckets, self.grads, 1.0))
+            return
+        if exec_t is None:
+            for f in self.exec_calls:
+                f()
+            for f in self.bucket_calls:
+                f()
+            return
+        for f in self.exec_calls:
+            exec_t.around(f)
+        for f in self.bucket_calls:
+            bucket_t.around(f)
 
 
 def time_steps(torch, fn, steps, warmup):
@@ -207,68 +226,92 @@ def time_steps(torch, fn, steps, warmup):
 
 
 # ------------------------------------------------------------ CPU baseline
-def cpu_baseline_c5(bytes_sample_target_s=15.0):
-    """The oracle, as it is, on a bounded sample of the c5 workload: one
-    layer's three graphs on the first rows, and a pack + unpack of the first
-    gradient tensors; rows grow until the sample takes about 10-30 s."""
+def cpu_baseline_c5(target_s=12.0):
+    """The oracle, as it is, on a bounded sample of the c5 workload: whole
+    layers (LayerNorm, bias+GELU, dropout+residual at 8192 x 1024/4096, each
+    layer with its own seed) until about target_s seconds of evaluation have
+    passed, then one pack + unpack of all 194 gradient tensors.  Input
+    generation is outside the timed spans."""
     import numpy as np
     from oracle import bucket as obucket
     from oracle import evaluate as oev
     from oracle import partition as opart
     from workloads import configs
 
-    def one(rows, n_grad_tensors):
-        gl = [configs.layernorm_graph(rows, 1024), configs.gelu_graph(rows, 4096),
-              configs.dropout_graph(rows, 1024)]
-        seed = configs.c5_layer_seed(0)
-        ins = [configs.layernorm_inputs(gl[0], seed), configs.gelu_inputs(gl[1], seed),
-               configs.dropout_inputs(gl[2], seed)]
-        stored = [opart.stored_tensors(g, opart.partition(g)) for g in gl]
-        numel = configs.c5_numel()[:n_grad_tensors]
-        grads = configs.gradient_values(numel, configs.C5_GRAD_SEED)
+    gl = [configs.layernorm_graph(), configs.gelu_graph(), configs.dropout_graph()]
+    gen_in = [configs.layernorm_inputs, configs.gelu_inputs, configs.dropout_inputs]
+    parts = [opart.partition(g) for g in gl]
+    stored = [opart.stored_tensors(g, p) for g, p in zip(gl, parts)]
+    layer_bytes = 0
+    for g, part, st in zip(gl, parts, stored):
+        for grp in part:
+            produced = {g.ops[i].output for i in grp}
+            ext = {t for i in grp for t in g.ops[i].inputs if t not in produced}
+            ext |= {t for t in produced if t in st or g.tensors[t].role == "out"}
+            layer_bytes += sum(int(np.prod(g.tensors[t].shape)) * ELEM[g.tensors[t].dtype]
+                               for t in ext)
+    dt, nbytes, layers = 0.0, 0, 0
+    while layers < 12 and dt < target_s:
+        seed = configs.c5_layer_seed(layers)
+        ins = [f(g, seed) for f, g in zip(gen_in, gl)]
         t0 = time.perf_counter()
         for g, i, s in zip(gl, ins, stored):
             oev.outputs(g, oev.evaluate(g, i, s))
-        bks = obucket.pack(numel, 4, configs.BUCKET_CAP_BYTES, grads, configs.AVG_SCALE)
-        obucket.unpack(numel, 4, configs.BUCKET_CAP_BYTES, bks, 1.0)
-        dt = time.perf_counter() - t0
-        nbytes = 0
-        for g in gl:
-            p = None
-            for grp in opart.partition(g):
-                nb = 0
-                produced = {g.ops[i].output for i in grp}
-                ext = {t for i in grp for t in g.ops[i].inputs if t not in produced}
-                st = opart.stored_tensors(g, opart.partition(g))
-                ext |= {t for t in produced if t in st or g.tensors[t].role == "out"}
-                for t in ext:
-                    d = g.tensors[t]
-                    nb += int(np.prod(d.shape)) * ELEM[d.dtype]
-                nbytes += nb
-        nbytes += 2 * 2 * 4 * sum(numel)
-        return dt, nbytes
-
-    rows, ngt = 128, 16
-    dt, nb = one(rows, ngt)
-    while dt < 10.0 and rows < 8192:
-        f = max(2.0, min(8.0, bytes_sample_target_s / max(dt, 1e-3)))
-        rows = min(8192, int(rows * f))
-        ngt = min(194, int(ngt * f))
-        dt, nb = one(rows, ngt)
+        dt += time.perf_counter() - t0
+        nbytes += layer_bytes
+        layers += 1
+        del ins
+    numel = configs.c5_numel()
+    grads = configs.gradient_values(numel, configs.C5_GRAD_SEED)
+    t0 = time.perf_counter()
+    bks = obucket.pack(numel, 4, configs.BUCKET_CAP_BYTES, grads, configs.AVG_SCALE)
+    obucket.unpack(numel, 4, configs.BUCKET_CAP_BYTES, bks, 1.0)
+    dt += time.perf_counter() - t0
+    nbytes += 2 * 2 * 4 * sum(numel)
     try:
         ncpu = len(os.sched_getaffinity(0))
     except AttributeError:
         ncpu = os.cpu_count()
-    return {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one layer at {rows} of 8192 rows (LayerNorm, bias+GELU, dropout+residual) "
-                      f"plus pack+unpack of the first {ngt} of 194 gradient tensors; "
-                      f"{nb} algorithmic bytes in {dt:.1f} s; NumPy/SciPy single-threaded "
-                      f"({ncpu} cores visible)"}
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{layers} of 12 layers at full size (LayerNorm, bias+GELU, "
+                      f"dropout+residual; 8192 tokens) plus pack+unpack of all 194 gradient "
+                      f"tensors; {nbytes} algorithmic bytes in {dt:.1f} s; NumPy/SciPy "
+                      f"single-threaded ({ncpu} cores visible)"}
+
+
+# ------------------------------------------------------------ copy ceiling / lead
+class CopyBench:
+    """The library's plain dwordx4 copy kernel on 1 GiB: the achievable
+    streaming ceiling, the reference for the traffic counters (it moves a
+    known 1 GiB in and 1 GiB out), and a lead of queued GPU work that keeps
+    the host ahead while launches are timed one by one."""
+    NBYTES = 1 << 30
+
+    def __init__(self, torch, gtf):
+        self.torch, self.gtf = torch, gtf
+        self.src = torch.empty(self.NBYTES, dtype=torch.uint8, device="cuda")
+        self.src.random_(0, 256)
+        self.dst = torch.empty_like(self.src)
+
+    def run(self):
+        self.gtf.device_copy(self.dst, self.src, self.NBYTES)
+
+    def lead(self, n=12):
+        for _ in range(n):
+            self.run()
+
+    def gbs(self, reps=10):
+        self.run()
+        ms, _ = time_steps(self.torch, self.run, reps, 1)
+        return 2 * self.NBYTES / (ms * 1e-3) / 1e9, ms
 
 
 # ------------------------------------------------------------ main
 def main():
     args = parse()
+    if args.traffic_from:
+        print(json.dumps(summarise_traffic(*args.traffic_from)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused groups shard by rows with no exchange "
               "and the buckets would feed an all-reduce that this build does not run; "
@@ -288,17 +331,24 @@ def main():
     ms, wall = time_steps(torch, w.step, args.steps, args.warmup)
     nbytes = w.bytes_per_step()
     value = nbytes / (ms * 1e-3) / 1e9
-    # per-kernel timing over a second pass of the same steps
-    et, bt = Timer(torch, True), Timer(torch, True)
+    # per-kernel timing over a second pass of the same steps; queued copies
+    # first put the GPU ahead of the host, so that each event pair brackets
+    # its kernel back to back with the previous one rather than host latency
+    cb = CopyBench(torch, gtf)
+    et = Timer(torch, args.steps * len(w.exec_calls))
+    bt = Timer(torch, args.steps * len(w.bucket_calls))
     torch.cuda.synchronize()
+    cb.lead()
     for _ in range(args.steps):
         w.step(exec_t=et, bucket_t=bt)
     torch.cuda.synchronize()
+    copy_gbs, copy_ms = cb.gbs()
+    del cb
     exec_ms = et.total_ms() / args.steps
     bucket_ms = bt.total_ms() / args.steps
     exec_gbs = w.exec_bytes_per_step() / (exec_ms * 1e-3) / 1e9
     bucket_gbs = 2 * w.bucket_bytes / (bucket_ms * 1e-3) / 1e9
-    n_exec = len(et.pairs) // args.steps
+    n_exec = et.count // args.steps
     if exec_ms >= bucket_ms:
         dom = {"kernel": "exec_kernel", "launches_per_step": n_exec,
                "avg_launch_us": round(exec_ms * 1e3 / n_exec, 3),
@@ -308,12 +358,9 @@ def main():
                "avg_launch_us": round(bucket_ms * 1e3 / 2, 3),
                "bytes_per_launch": w.bucket_bytes, "gbs": bucket_gbs}
     traffic = None
-    tf = os.path.join(ROOT, "profiles", "traffic_c5.json")
-    if os.path.exists(tf):
-        with open(tf) as f:
-            tj = json.load(f)
-        if tj.get("kernel") == dom["kernel"] and tj.get("source_hash") == _kernel_hash():
-            traffic = tj.get("bytes_per_launch")
+    tj = read_traffic(dom["kernel"])
+    if tj is not None:
+        traffic = tj["bytes_per_launch"]
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -333,7 +380,9 @@ def main():
                      "algorithmic_bytes_per_launch": round(dom["bytes_per_launch"])},
         "breakdown": {"exec_ms_per_step": round(exec_ms, 4), "exec_gbs": round(exec_gbs, 1),
                       "bucket_ms_per_step": round(bucket_ms, 4), "bucket_gbs": round(bucket_gbs, 1),
-                      "wall_s_timed": round(wall, 3)},
+                      "wall_s_timed": round(wall, 3),
+                      "copy_kernel_gbs": round(copy_gbs, 1),
+                      "copy_kernel_note": "library dwordx4 copy of 1 GiB: achievable ceiling"},
     }
     if not args.no_baselines:
         del w
@@ -440,6 +489,76 @@ def run_config(torch, gtf, configs, args):
                             "launches": out[False][2]},
                 "launches": ng})
     return res
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c5.txt")
+TRAFFIC_CMDS = (
+    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE "
+    "-d $R/gpurun_out/pmc_fetch -o fetch --output-format csv -- python3 $R/bench.py --steps 3 "
+    "--warmup 1 --no-cpu-baseline --no-baselines",
+    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE "
+    "-d $R/gpurun_out/pmc_write -o write --output-format csv -- python3 $R/bench.py --steps 3 "
+    "--warmup 1 --no-cpu-baseline --no-baselines",
+    "python3 bench.py --traffic-from <fetch>_counter_collection.csv <write>_counter_collection.csv")
+
+
+def _counter_per_kernel(path, counter):
+    """{kernel short name: [per-dispatch values]} for one counter."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            for k in ("exec_kernel", "bucket_kernel", "copy_kernel"):
+                if "gtf::" + k in name:
+                    out.setdefault(k, {})[row["Dispatch_Id"]] = float(row["Counter_Value"])
+    return {k: list(v.values()) for k, v in out.items()}
+
+
+def summarise_traffic(fetch_csv, write_csv):
+    fe = _counter_per_kernel(fetch_csv, "FETCH_SIZE")
+    wr = _counter_per_kernel(write_csv, "WRITE_SIZE")
+    nb = CopyBench.NBYTES
+    f_copy = sum(fe["copy_kernel"]) / len(fe["copy_kernel"]) * 1024
+    w_copy = sum(wr["copy_kernel"]) / len(wr["copy_kernel"]) * 1024
+    kf, kw = nb / f_copy, nb / w_copy
+    res = {"source_hash": _kernel_hash(), "copy_bytes_each_way": nb,
+           "copy_fetch_bytes_counted": round(f_copy), "copy_write_bytes_counted": round(w_copy),
+           "fetch_scale": round(kf, 5), "write_scale": round(kw, 5), "kernels": {}}
+    for k in ("exec_kernel", "bucket_kernel"):
+        if k not in fe or k not in wr:
+            continue
+        f = sum(fe[k]) / len(fe[k]) * 1024 * kf
+        w = sum(wr[k]) / len(wr[k]) * 1024 * kw
+        res["kernels"][k] = {"dispatches": len(fe[k]), "fetch_bytes_per_launch": round(f),
+                             "write_bytes_per_launch": round(w),
+                             "bytes_per_launch": round(f + w)}
+    lines = ["# HBM traffic per launch of the c5 step's kernels: rocprofv3 FETCH_SIZE and "
+             "WRITE_SIZE (KiB per dispatch), each scaled so that the 1 GiB copy kernel in the "
+             "same run counts exactly 1 GiB read and 1 GiB written.",
+             "# commands (R = repository root):"]
+    lines += ["#   " + c for c in TRAFFIC_CMDS]
+    lines.append(json.dumps(res))
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return res
+
+
+def read_traffic(kernel):
+    """Traffic record of one kernel, or None when absent or taken from
+    another version of the kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        js = [ln for ln in f if ln.startswith("{")]
+    if not js:
+        return None
+    tj = json.loads(js[-1])
+    if tj.get("source_hash") != _kernel_hash():
+        return None
+    return tj["kernels"].get(kernel)
 
 
 def _kernel_hash():

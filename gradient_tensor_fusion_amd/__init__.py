@@ -103,9 +103,7 @@ class FusePlan:
     def geometry(self, g: int) -> dict:
         geo = C.GroupGeometry()
         C.check(C.lib().fuse_plan_group_geometry(self._h, g, byref(geo)))
-        d = {name: getattr(geo, name) for name, _ in C.GroupGeometry._fields_}
-        d["ring_tensor"] = list(geo.ring_tensor)[: geo.ring_inputs]
-        return d
+        return {name: getattr(geo, name) for name, _ in C.GroupGeometry._fields_}
 
     def is_materialized(self, t: int) -> bool:
         y = c_int32()
@@ -127,6 +125,19 @@ class FusePlan:
 
     def run(self, tensors, stream=None) -> None:
         C.check(C.lib().fuse_plan_run(self._h, self._ptrs(tensors), C.stream_handle(stream)))
+
+    def launcher(self, g: int, tensors, stream=None):
+        """fuse_group_run with its arguments marshalled once: returns a
+        callable that launches group g on the same tensors and stream."""
+        f, h, ptrs, st = C.lib().fuse_group_run, self._h, self._ptrs(tensors), C.stream_handle(stream)
+        keep = tensors
+
+        def run():
+            status = f(h, g, ptrs, st)
+            if status != C.GTF_OK:
+                C.check(status)
+        run.tensors = keep
+        return run
 
 
 class BucketPlan:
@@ -177,6 +188,24 @@ class BucketPlan:
         C.check(C.lib().bucket_unpack(self._h, C.ptr_array([C.data_ptr(b) for b in buckets]),
                                       C.ptr_array([C.data_ptr(t) for t in dsts]), float(scale),
                                       C.stream_handle(stream)))
+
+    def launcher(self, unpack: bool, tensors, buckets, scale: float, stream=None):
+        """bucket_pack (or bucket_unpack) with its arguments marshalled once."""
+        t = C.ptr_array([C.data_ptr(x) for x in tensors])
+        b = C.ptr_array([C.data_ptr(x) for x in buckets])
+        h, st, sc = self._h, C.stream_handle(stream), float(scale)
+        keep = (tensors, buckets)
+        if unpack:
+            f, a0, a1 = C.lib().bucket_unpack, b, t
+        else:
+            f, a0, a1 = C.lib().bucket_pack, t, b
+
+        def run():
+            status = f(h, a0, a1, sc, st)
+            if status != C.GTF_OK:
+                C.check(status)
+        run.tensors = keep
+        return run
 
     def pack_per_tensor(self, srcs, buckets, scale: float = 1.0, stream=None) -> None:
         C.check(C.lib().bucket_pack_per_tensor(self._h, C.ptr_array([C.data_ptr(t) for t in srcs]),

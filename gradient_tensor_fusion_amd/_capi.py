@@ -13,7 +13,7 @@ from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uin
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgtf.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 GTF_OK, GTF_E_INVALID, GTF_E_UNSUPPORTED, GTF_E_SHAPE, GTF_E_LIMIT, GTF_E_STATE, GTF_E_HIP = (
     0, -1, -2, -3, -4, -5, -6)
@@ -54,9 +54,8 @@ class OpDesc(ctypes.Structure):
 class GroupGeometry(ctypes.Structure):
     _fields_ = [("rows", c_int64), ("cols", c_int64), ("items", c_int64), ("panels", c_int32),
                 ("rows_per_item", c_int32), ("panel_width", c_int32), ("threads_per_row", c_int32),
-                ("ring_inputs", c_int32), ("ring_stages", c_int32), ("ring_stage_bytes", c_int32),
-                ("lds_bytes", c_int32), ("program_length", c_int32), ("spill_slots", c_int32),
-                ("reduce", c_int32), ("ring_tensor", c_int32 * 4)]
+                ("subtiles", c_int32), ("lds_bytes", c_int32), ("program_length", c_int32),
+                ("spill_slots", c_int32), ("spill_slots_max", c_int32), ("reduce", c_int32)]
 
 
 class ProgramDesc(ctypes.Structure):

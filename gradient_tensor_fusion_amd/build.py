@@ -13,6 +13,12 @@ library next to this file.  Every HIP translation unit is compiled with
                                              constant register indices into
                                              pointer phis and forces the
                                              op-program stack into scratch
+  -mllvm -structurizecfg-skip-uniform-regions=true
+                                             leave the interpreter's dispatch
+                                             switch (wave-uniform) a tree of
+                                             scalar branches; structurised,
+                                             every case writes a second copy
+                                             of the register state
 """
 from __future__ import annotations
 
@@ -35,7 +41,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
 DEVICE = ["--offload-arch=" + ARCH, "-ffp-contract=off",
           "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-simplifycfg-sink-common=false"]
+          "-mllvm", "-simplifycfg-sink-common=false",
+          "-mllvm", "-structurizecfg-skip-uniform-regions=true"]
 
 SOURCES = ["plan.cpp", "bucket_plan.cpp", "capi.cpp", "kernels.hip"]
 

@@ -209,14 +209,12 @@ int fuse_plan_group_geometry(const gtf_fuse_plan* plan, int32_t g, gtf_group_geo
   out->rows_per_item = a.RB;
   out->panel_width = a.PW;
   out->threads_per_row = 1 << a.tpr_log2;
-  out->ring_inputs = a.n_pipe;
-  out->ring_stages = a.n_stage;
-  out->ring_stage_bytes = a.stage_bytes;
+  out->subtiles = a.K;
   out->lds_bytes = cg.lds_bytes;
   out->program_length = a.n_col + a.n_row + a.n_elem;
   out->spill_slots = cg.max_depth;
+  out->spill_slots_max = a.NS;
   out->reduce = a.reduce;
-  for (int k = 0; k < 4; ++k) out->ring_tensor[k] = k < a.n_pipe ? cg.slot_tensor[a.pipe_slot[k]] : -1;
   return GTF_OK;
 }
 

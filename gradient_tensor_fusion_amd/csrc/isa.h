@@ -10,31 +10,36 @@
 //                 results go to LDS column slots.
 //   row phase     once per row of the row block (values shaped [R,1]);
 //                 results go to LDS row slots.
-//   element phase once per tile of kV consecutive elements of one row;
-//                 reads rows/columns from LDS, streams [R,C] tensors.
+//   element phase once per tile of one row; reads rows/columns from LDS,
+//                 streams [R,C] tensors.  A lane's tile is K sub-tiles of
+//                 kV consecutive elements, tpr * kV elements apart in the
+//                 row, so one dispatched instruction covers K * kV
+//                 elements per lane (K = 4 in the wide instance).
 //
-// The machine has two working registers A and B and kNS spill slots, each
+// The machine has two working registers A and B and NS spill slots, each
 // holding one tile.  Every op reads A (and B) and writes A; moves between
 // A, B and the slots are explicit instructions.  Each instruction form has
-// exactly one body in the kernel, so the interpreter stays small enough for
-// the instruction cache, and every register index is a compile-time
-// constant, so the registers stay in VGPRs.
+// exactly one body in the kernel, and every register index is a
+// compile-time constant, so the registers stay in VGPRs.  Two kernel
+// instances exist: wide (K = 4, NS = 2: 4 x 32 VGPRs of registers) for
+// programs that fit two spill slots, and narrow (K = 1, NS = 6) for the
+// rest.
 #pragma once
 
 #include <stdint.h>
 
 namespace gtf {
 
-constexpr int kV = 8;            // elements per lane per tile
-constexpr int kNS = 6;           // spill slots
+constexpr int kV = 8;            // elements per lane per sub-tile (one 16-byte bf16 load)
+constexpr int kNS = 6;           // spill slots of the narrow instance
+constexpr int kWideK = 4;        // sub-tiles per lane tile in the wide instance
+constexpr int kWideNS = 2;       // spill slots of the wide instance
 constexpr int kMaxInstr = 320;   // instructions over all three phases
 constexpr int kMaxSlots = 16;    // external tensors of one group
 constexpr int kMaxLdsCol = 4;    // LDS column slots
 constexpr int kMaxLdsRow = 8;    // LDS row slots
 constexpr int kBlock = 256;      // threads per workgroup
 constexpr int kPanelMax = 4096;  // widest column panel staged in LDS
-constexpr int kMaxPipe = 4;      // element inputs streamed through the LDS ring
-constexpr int kRingBudget = 48 * 1024;  // LDS bytes for the rings of one workgroup
 
 enum Form : int {
   // load a tile of external tensor slot `arg` into A / into B
@@ -89,16 +94,8 @@ struct ExecArgs {
   int32_t red_dtype;       // reduce output dtype
   int32_t red_slot;        // external slot of the reduce output
   int32_t vec_ok;          // element tensors and rows are 16-byte aligned
-  // element-phase inputs streamed through a per-wave LDS ring, n_stage
-  // tiles ahead (direct global -> LDS loads)
-  int32_t n_pipe;          // pipelined inputs (<= kMaxPipe)
-  int32_t n_stage;         // ring depth in tiles
-  int32_t n_dma;           // DMA instructions per tile (all pipelined inputs)
-  int32_t stage_bytes;     // LDS bytes of one ring stage of one wave
-  int32_t ring_lds_off;    // byte offset of the ring in dynamic LDS
-  int32_t pipe_slot[4];    // external slot of each pipelined input
-  int32_t pipe_dt[4];      // its dtype
-  int32_t ring_off[kMaxSlots];  // byte offset of a slot inside a stage, -1 if direct
+  int32_t K;               // sub-tiles per lane tile: kWideK (wide) or 1 (narrow)
+  int32_t NS;              // spill slots of the instance: kWideNS or kNS
   void* ptr[kMaxSlots];
   int64_t rstride[kMaxSlots];
   int64_t cstride[kMaxSlots];

@@ -128,17 +128,19 @@ __device__ __forceinline__ void pstore_b16(void* addr, uint32_t v, uint64_t mask
 __device__ __forceinline__ uint64_t lanes(bool c) { return __builtin_amdgcn_ballot_w64(c); }
 
 // ---------------------------------------------------------------- context
+// A lane's tile.  In the whole-tile (FAST) instance it is V / kV sub-tiles
+// of kV consecutive elements, kstride elements apart in the same row; in
+// the partial-tile instance it is one sub-tile of cnt valid elements.
 struct Tile {
   int64_t row;   // global row
   int64_t col;   // global column of the first element
   int64_t eoff;  // element offset of the tile in [R,C] tensors
   int cl;        // column inside the staged panel
   int rr;        // row inside the row block
-  int cnt;       // valid elements in the tile
+  int cnt;       // valid elements of a partial tile
+  int kstride;   // elements between sub-tiles
   bool valid;    // the tile exists (row and column in range)
-  bool vec;      // whole tile, 16-byte aligned: vector path
-  const char* ring;  // this tile's stage of the wave's LDS ring (or null)
-  int lane;      // lane within the wave
+  bool vec;      // whole sub-tile, 16-byte aligned: vector path
 };
 
 template <int V, int MODE>
@@ -148,117 +150,98 @@ __device__ __forceinline__ int64_t elem_offset(const ExecArgs& a, int slot, cons
   return t.col * a.cstride[slot];
 }
 
+__device__ __forceinline__ void expand_bf16(float* d, uint4 w) {
+  d[0] = bf16_lo(w.x); d[1] = bf16_hi(w.x); d[2] = bf16_lo(w.y); d[3] = bf16_hi(w.y);
+  d[4] = bf16_lo(w.z); d[5] = bf16_hi(w.z); d[6] = bf16_lo(w.w); d[7] = bf16_hi(w.w);
+}
+__device__ __forceinline__ void expand_u8(float* d, uint2 w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = (float)((w.x >> (8 * i)) & 0xFFu);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[4 + i] = (float)((w.y >> (8 * i)) & 0xFFu);
+}
+
+// Loads: whole tiles use 16-byte loads per sub-tile (u8: 8 bytes); partial
+// tiles read element by element at clamped in-range indices, without a
+// branch; row and column phases read one element.
 template <int V, int MODE, bool FAST>
-__device__ __forceinline__ void load_f32(float (&d)[V], const ExecArgs& a, int slot, const Tile& t,
-                                         int ring_off) {
-  if (MODE == M_ELEM && V == 8) {
-    if ((FAST || t.vec) && t.ring != nullptr && ring_off >= 0) {
-      const char* q = t.ring + ring_off + t.lane * 16;
-      const float4 x = *(const float4*)q;
-      const float4 y = *(const float4*)(q + 1024);
-      d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
-      d[4] = y.x; d[5] = y.y; d[6] = y.z; d[7] = y.w;
-      return;
-    }
-  }
-  const float* p = (const float*)a.ptr[slot] + elem_offset<V, MODE>(a, slot, t);
-  if (MODE == M_ELEM && V == 8) {
+__device__ __forceinline__ void load_f32(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
+  const float* b = (const float*)a.ptr[slot];
+  if (MODE == M_ELEM && V % kV == 0) {
     if (FAST || t.vec) {
-      const float4 x = *(const float4*)p;
-      const float4 y = *(const float4*)(p + 4);
-      d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
-      d[4] = y.x; d[5] = y.y; d[6] = y.z; d[7] = y.w;
+      const float* p = b + t.eoff;
+#pragma unroll
+      for (int k = 0; k < V / kV; ++k) {
+        const float4 x = *(const float4*)(p + k * t.kstride);
+        const float4 y = *(const float4*)(p + k * t.kstride + 4);
+        d[k * kV + 0] = x.x; d[k * kV + 1] = x.y; d[k * kV + 2] = x.z; d[k * kV + 3] = x.w;
+        d[k * kV + 4] = y.x; d[k * kV + 5] = y.y; d[k * kV + 6] = y.z; d[k * kV + 7] = y.w;
+      }
       return;
     }
   }
-  if (MODE == M_ELEM) {  // partial tile: clamped in-bounds reads, no branch
-    const float* b = (const float*)a.ptr[slot];
+  if (MODE == M_ELEM) {
 #pragma unroll
     for (int i = 0; i < V; ++i) d[i] = b[(t.valid && i < t.cnt) ? t.eoff + i : 0];
     return;
   }
-#pragma unroll
-  for (int i = 0; i < V; ++i) d[i] = p[i];
+  d[0] = b[elem_offset<V, MODE>(a, slot, t)];
 }
 
 template <int V, int MODE, bool FAST>
-__device__ __forceinline__ void load_bf16(float (&d)[V], const ExecArgs& a, int slot, const Tile& t,
-                                         int ring_off) {
-  if (MODE == M_ELEM && V == 8) {
-    if ((FAST || t.vec) && t.ring != nullptr && ring_off >= 0) {
-      const uint4 w = *(const uint4*)(t.ring + ring_off + t.lane * 16);
-      d[0] = bf16_lo(w.x); d[1] = bf16_hi(w.x); d[2] = bf16_lo(w.y); d[3] = bf16_hi(w.y);
-      d[4] = bf16_lo(w.z); d[5] = bf16_hi(w.z); d[6] = bf16_lo(w.w); d[7] = bf16_hi(w.w);
-      return;
-    }
-  }
-  const uint16_t* p = (const uint16_t*)a.ptr[slot] + elem_offset<V, MODE>(a, slot, t);
-  if (MODE == M_ELEM && V == 8) {
+__device__ __forceinline__ void load_bf16(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
+  const uint16_t* b = (const uint16_t*)a.ptr[slot];
+  if (MODE == M_ELEM && V % kV == 0) {
     if (FAST || t.vec) {
-      const uint4 w = *(const uint4*)p;
-      d[0] = bf16_lo(w.x); d[1] = bf16_hi(w.x); d[2] = bf16_lo(w.y); d[3] = bf16_hi(w.y);
-      d[4] = bf16_lo(w.z); d[5] = bf16_hi(w.z); d[6] = bf16_lo(w.w); d[7] = bf16_hi(w.w);
+      const uint16_t* p = b + t.eoff;
+#pragma unroll
+      for (int k = 0; k < V / kV; ++k) expand_bf16(d + k * kV, *(const uint4*)(p + k * t.kstride));
       return;
     }
   }
   if (MODE == M_ELEM) {
-    const uint16_t* b = (const uint16_t*)a.ptr[slot];
 #pragma unroll
     for (int i = 0; i < V; ++i) d[i] = bf16_at(b + ((t.valid && i < t.cnt) ? t.eoff + i : 0));
     return;
   }
-#pragma unroll
-  for (int i = 0; i < V; ++i) d[i] = bf16_at(p + i);
+  d[0] = bf16_at(b + elem_offset<V, MODE>(a, slot, t));
 }
 
 template <int V, int MODE, bool FAST>
-__device__ __forceinline__ void load_u8(float (&d)[V], const ExecArgs& a, int slot, const Tile& t,
-                                         int ring_off) {
-  if (MODE == M_ELEM && V == 8) {
-    if ((FAST || t.vec) && t.ring != nullptr && ring_off >= 0) {
-      const char* q = t.ring + ring_off + t.lane * 4;
-      const uint32_t w0 = *(const uint32_t*)q;
-      const uint32_t w1 = *(const uint32_t*)(q + 256);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = (float)((w0 >> (8 * i)) & 0xFFu);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[4 + i] = (float)((w1 >> (8 * i)) & 0xFFu);
-      return;
-    }
-  }
-  const uint8_t* p = (const uint8_t*)a.ptr[slot] + elem_offset<V, MODE>(a, slot, t);
-  if (MODE == M_ELEM && V == 8) {
+__device__ __forceinline__ void load_u8(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
+  const uint8_t* b = (const uint8_t*)a.ptr[slot];
+  if (MODE == M_ELEM && V % kV == 0) {
     if (FAST || t.vec) {
-      const uint2 w = *(const uint2*)p;
+      const uint8_t* p = b + t.eoff;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = (float)((w.x >> (8 * i)) & 0xFFu);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[4 + i] = (float)((w.y >> (8 * i)) & 0xFFu);
+      for (int k = 0; k < V / kV; ++k) expand_u8(d + k * kV, *(const uint2*)(p + k * t.kstride));
       return;
     }
   }
   if (MODE == M_ELEM) {
-    const uint8_t* b = (const uint8_t*)a.ptr[slot];
 #pragma unroll
     for (int i = 0; i < V; ++i) d[i] = (float)b[(t.valid && i < t.cnt) ? t.eoff + i : 0];
     return;
   }
-#pragma unroll
-  for (int i = 0; i < V; ++i) d[i] = (float)p[i];
+  d[0] = (float)b[elem_offset<V, MODE>(a, slot, t)];
 }
 
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void store_f32(const float (&s)[V], const ExecArgs& a, int slot, const Tile& t) {
-  float* p = (float*)a.ptr[slot] + elem_offset<V, MODE>(a, slot, t);
-  if (MODE == M_ELEM && V == 8) {
+  float* b = (float*)a.ptr[slot];
+  if (MODE == M_ELEM && V % kV == 0) {
     if (FAST || t.vec) {
-      *(float4*)p = make_float4(s[0], s[1], s[2], s[3]);
-      *(float4*)(p + 4) = make_float4(s[4], s[5], s[6], s[7]);
+      float* p = b + t.eoff;
+#pragma unroll
+      for (int k = 0; k < V / kV; ++k) {
+        *(float4*)(p + k * t.kstride) = make_float4(s[k * kV], s[k * kV + 1], s[k * kV + 2], s[k * kV + 3]);
+        *(float4*)(p + k * t.kstride + 4) =
+            make_float4(s[k * kV + 4], s[k * kV + 5], s[k * kV + 6], s[k * kV + 7]);
+      }
       return;
     }
   }
   if (MODE == M_ELEM) {  // partial tile: one predicated store per element
-    float* b = (float*)a.ptr[slot];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const bool on = t.valid && i < t.cnt;
@@ -266,22 +249,24 @@ __device__ __forceinline__ void store_f32(const float (&s)[V], const ExecArgs& a
     }
     return;
   }
-#pragma unroll
-  for (int i = 0; i < V; ++i) p[i] = s[i];
+  b[elem_offset<V, MODE>(a, slot, t)] = s[0];
 }
 
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void store_bf16(const float (&s)[V], const ExecArgs& a, int slot, const Tile& t) {
-  uint16_t* p = (uint16_t*)a.ptr[slot] + elem_offset<V, MODE>(a, slot, t);
-  if (MODE == M_ELEM && V == 8) {
+  uint16_t* b = (uint16_t*)a.ptr[slot];
+  if (MODE == M_ELEM && V % kV == 0) {
     if (FAST || t.vec) {
-      *(uint4*)p = make_uint4(pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3]),
-                              pack_bf16(s[4], s[5]), pack_bf16(s[6], s[7]));
+      uint16_t* p = b + t.eoff;
+#pragma unroll
+      for (int k = 0; k < V / kV; ++k)
+        *(uint4*)(p + k * t.kstride) =
+            make_uint4(pack_bf16(s[k * kV], s[k * kV + 1]), pack_bf16(s[k * kV + 2], s[k * kV + 3]),
+                       pack_bf16(s[k * kV + 4], s[k * kV + 5]), pack_bf16(s[k * kV + 6], s[k * kV + 7]));
       return;
     }
   }
   if (MODE == M_ELEM) {
-    uint16_t* b = (uint16_t*)a.ptr[slot];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const bool on = t.valid && i < t.cnt;
@@ -289,8 +274,7 @@ __device__ __forceinline__ void store_bf16(const float (&s)[V], const ExecArgs& 
     }
     return;
   }
-#pragma unroll
-  for (int i = 0; i < V; ++i) p[i] = (uint16_t)(pack_bf16(s[i], 0.f) & 0xFFFFu);
+  b[elem_offset<V, MODE>(a, slot, t)] = (uint16_t)(pack_bf16(s[0], 0.f) & 0xFFFFu);
 }
 
 // ---------------------------------------------------------------- ops
@@ -331,27 +315,42 @@ __device__ __forceinline__ void binop(float (&l)[V], const float (&r)[V]) {
   for (int i = 0; i < V; ++i) l[i] = xop<OP>(l[i], r[i]);
 }
 
-// x: V consecutive fp32 values in LDS (32-byte aligned for V == 8)
+// A tile's column-broadcast values from an LDS column slot: kV consecutive
+// fp32 values per sub-tile (32-byte aligned), sub-tiles kstride apart.
 template <int V>
-__device__ __forceinline__ void lds_vec(float (&d)[V], const float* x) {
-  if (V == 8) {
-    const float4 u = *(const float4*)x;
-    const float4 w = *(const float4*)(x + 4);
-    const float xs[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+__device__ __forceinline__ void lds_vec(float (&d)[V], const float* x, int kstride) {
+  if (V % kV == 0) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) d[i] = xs[i % 8];
+    for (int k = 0; k < V / kV; ++k) {
+      const float4 u = *(const float4*)(x + k * kstride);
+      const float4 w = *(const float4*)(x + k * kstride + 4);
+      d[k * kV + 0] = u.x; d[k * kV + 1] = u.y; d[k * kV + 2] = u.z; d[k * kV + 3] = u.w;
+      d[k * kV + 4] = w.x; d[k * kV + 5] = w.y; d[k * kV + 6] = w.z; d[k * kV + 7] = w.w;
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < V; ++i) d[i] = x[i];
   }
 }
 
+// A op (column values), one sub-tile at a time: a scheduling barrier
+// between sub-tiles keeps the compiler from reading all V values from LDS
+// ahead of the arithmetic, which would hold V more registers.
 template <int V, int OP>
-__device__ __forceinline__ void xvec(float (&r)[V], const float* x) {
-  float xs[V];
-  lds_vec<V>(xs, x);
+__device__ __forceinline__ void xvec(float (&r)[V], const float* x, int kstride) {
+  if (V % kV == 0) {
 #pragma unroll
-  for (int i = 0; i < V; ++i) r[i] = xop<OP>(r[i], xs[i]);
+    for (int k = 0; k < V / kV; ++k) {
+      float xs[kV];
+      lds_vec<kV>(xs, x + k * kstride, 0);
+#pragma unroll
+      for (int i = 0; i < kV; ++i) r[k * kV + i] = xop<OP>(r[k * kV + i], xs[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) r[i] = xop<OP>(r[i], x[i]);
+  }
 }
 
 template <int V, int OP>
@@ -373,18 +372,20 @@ __device__ __forceinline__ void fill(float (&d)[V], float x) {
 }
 
 // ---------------------------------------------------------------- interpreter
-// A, B and the spill slots hold one tile each.  The next instruction word is
-// fetched while the current one executes.  FAST is the instance for tiles
-// that are whole, in range and vector-aligned in every lane of the wave: it
-// has no lane-dependent branch, so the compiler keeps the dispatch switch a
-// tree of scalar branches (a lane-dependent branch anywhere in the loop
-// makes it linearise the switch into a chain of guarded blocks).  The other
-// instance handles partial tiles at row and tensor ends.
-template <int V, int MODE, bool FAST>
+// A, B and the NS spill slots hold one tile each (V values per lane).  The
+// next instruction word is fetched while the current one executes.  FAST is
+// the instance for tiles that are whole, in range and vector-aligned in
+// every lane of the wave: it has no lane-dependent branch, so the compiler
+// keeps the dispatch switch a tree of scalar branches (a lane-dependent
+// branch anywhere in the loop makes it linearise the switch into a chain of
+// guarded blocks).  The other instance handles partial sub-tiles at row and
+// tensor ends.  Forms naming a slot beyond NS never occur in a program
+// compiled for the instance and have empty bodies.
+template <int V, int MODE, bool FAST, int NS>
 __device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, int n,
                                           const Tile& t, float* lds_col, float* lds_row,
                                           float& acc, bool store_global) {
-  float A[V], B[V], S0[V], S1[V], S2[V], S3[V], S4[V], S5[V];
+  float A[V], B[V], S[NS][V];
   if (n <= 0) return;
   Instr cur = prog[0];
   for (int pc = 0; pc < n; ++pc) {
@@ -392,44 +393,27 @@ __device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, 
     const int arg = cur.arg;
     const float* col = lds_col + arg * a.PW + t.cl;
     switch (cur.code) {
-      case F_LD_F32_A: load_f32<V, MODE, FAST>(A, a, arg, t, __float_as_int(cur.imm)); break;
-      case F_LD_BF16_A: load_bf16<V, MODE, FAST>(A, a, arg, t, __float_as_int(cur.imm)); break;
-      case F_LD_U8_A: load_u8<V, MODE, FAST>(A, a, arg, t, __float_as_int(cur.imm)); break;
-      case F_LD_F32_B: load_f32<V, MODE, FAST>(B, a, arg, t, __float_as_int(cur.imm)); break;
-      case F_LD_BF16_B: load_bf16<V, MODE, FAST>(B, a, arg, t, __float_as_int(cur.imm)); break;
-      case F_LD_U8_B: load_u8<V, MODE, FAST>(B, a, arg, t, __float_as_int(cur.imm)); break;
-      case F_COL_A: if (MODE == M_ELEM) lds_vec<V>(A, col); break;
+      case F_LD_F32_A: load_f32<V, MODE, FAST>(A, a, arg, t); break;
+      case F_LD_BF16_A: load_bf16<V, MODE, FAST>(A, a, arg, t); break;
+      case F_LD_U8_A: load_u8<V, MODE, FAST>(A, a, arg, t); break;
+      case F_LD_F32_B: load_f32<V, MODE, FAST>(B, a, arg, t); break;
+      case F_LD_BF16_B: load_bf16<V, MODE, FAST>(B, a, arg, t); break;
+      case F_LD_U8_B: load_u8<V, MODE, FAST>(B, a, arg, t); break;
+      case F_COL_A: if (MODE == M_ELEM) lds_vec<V>(A, col, t.kstride); break;
       case F_ROW_A: if (MODE == M_ELEM) fill<V>(A, lds_row[arg * a.RB + t.rr]); break;
       case F_IMM_A: fill<V>(A, cur.imm); break;
-      case F_COL_B: if (MODE == M_ELEM) lds_vec<V>(B, col); break;
+      case F_COL_B: if (MODE == M_ELEM) lds_vec<V>(B, col, t.kstride); break;
       case F_ROW_B: if (MODE == M_ELEM) fill<V>(B, lds_row[arg * a.RB + t.rr]); break;
       case F_IMM_B: fill<V>(B, cur.imm); break;
       case F_A2B: copy<V>(B, A); break;
       case F_B2A: copy<V>(A, B); break;
-      case F_A2S0: copy<V>(S0, A); break;
-      case F_A2S1: copy<V>(S1, A); break;
-      case F_A2S2: copy<V>(S2, A); break;
-      case F_A2S3: copy<V>(S3, A); break;
-      case F_A2S4: copy<V>(S4, A); break;
-      case F_A2S5: copy<V>(S5, A); break;
-      case F_B2S0: copy<V>(S0, B); break;
-      case F_B2S1: copy<V>(S1, B); break;
-      case F_B2S2: copy<V>(S2, B); break;
-      case F_B2S3: copy<V>(S3, B); break;
-      case F_B2S4: copy<V>(S4, B); break;
-      case F_B2S5: copy<V>(S5, B); break;
-      case F_S02A: copy<V>(A, S0); break;
-      case F_S12A: copy<V>(A, S1); break;
-      case F_S22A: copy<V>(A, S2); break;
-      case F_S32A: copy<V>(A, S3); break;
-      case F_S42A: copy<V>(A, S4); break;
-      case F_S52A: copy<V>(A, S5); break;
-      case F_S02B: copy<V>(B, S0); break;
-      case F_S12B: copy<V>(B, S1); break;
-      case F_S22B: copy<V>(B, S2); break;
-      case F_S32B: copy<V>(B, S3); break;
-      case F_S42B: copy<V>(B, S4); break;
-      case F_S52B: copy<V>(B, S5); break;
+#define GTF_SLOT(K)                                                 \
+  case F_A2S0 + K: if constexpr (K < NS) copy<V>(S[K], A); break;   \
+  case F_B2S0 + K: if constexpr (K < NS) copy<V>(S[K], B); break;   \
+  case F_S02A + K: if constexpr (K < NS) copy<V>(A, S[K]); break;   \
+  case F_S02B + K: if constexpr (K < NS) copy<V>(B, S[K]); break;
+      GTF_SLOT(0) GTF_SLOT(1) GTF_SLOT(2) GTF_SLOT(3) GTF_SLOT(4) GTF_SLOT(5)
+#undef GTF_SLOT
       case F_EXP: unary<V, F_EXP>(A); break;
       case F_TANH: unary<V, F_TANH>(A); break;
       case F_SIGMOID: unary<V, F_SIGMOID>(A); break;
@@ -441,7 +425,7 @@ __device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, 
       case F_NEG: unary<V, F_NEG>(A); break;
 #define GTF_BIN(NAME, OP)                                                               \
   case F_##NAME: binop<V, OP>(A, B); break;                                             \
-  case F_##NAME##_C: if (MODE == M_ELEM) xvec<V, OP>(A, col); break;                  \
+  case F_##NAME##_C: if (MODE == M_ELEM) xvec<V, OP>(A, col, t.kstride); break;         \
   case F_##NAME##_R: if (MODE == M_ELEM) xscalar<V, OP>(A, lds_row[arg * a.RB + t.rr]); break; \
   case F_##NAME##_I: xscalar<V, OP>(A, cur.imm); break;
       GTF_BIN(ADD, X_ADD)
@@ -514,91 +498,17 @@ __device__ __forceinline__ void store_reduced(const ExecArgs& a, int64_t row, fl
     pstore_b32((float*)a.ptr[slot] + off, __float_as_uint(v), m);
 }
 
-// ---------------------------------------------------------------- LDS ring
-// Direct global -> LDS loads (gfx950 global_load_lds): lane i's bytes land
-// at M0 + i * size.  They are issued in inline assembly so the compiler does
-// not treat every later LDS read as a possible alias of an in-flight copy
-// (which would make it drain all of them); the kernel counts them itself
-// and waits with an explicit vmcnt.  Neither asm clobbers memory, so the
-// compiler keeps kernel arguments in registers across them; instead the
-// ring pointer passes through the wait as an operand, which orders every
-// ring read after the wait.  A stage is rewritten only one iteration after
-// its reads, across the loop's back edge.  M0 is saved and restored.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(g), "s"(lds));
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dword %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(g), "s"(lds));
-}
-
-// Wait until at most n vector-memory operations of this wave are in flight
-// (they complete in issue order; n <= 63).  Returns `ring` through the asm
-// so reads through the result cannot move above the wait.
-__device__ __forceinline__ const char* wait_vmcnt(int n, const char* ring) {
-  switch (n) {
-#define GTF_W(N) case N: asm volatile("s_waitcnt vmcnt(" #N ")" : "+s"(ring)); break;
-    GTF_W(0) GTF_W(1) GTF_W(2) GTF_W(3) GTF_W(4) GTF_W(5) GTF_W(6) GTF_W(7)
-    GTF_W(8) GTF_W(9) GTF_W(10) GTF_W(11) GTF_W(12) GTF_W(13) GTF_W(14) GTF_W(15)
-    GTF_W(16) GTF_W(17) GTF_W(18) GTF_W(19) GTF_W(20) GTF_W(21) GTF_W(22) GTF_W(23)
-    GTF_W(24) GTF_W(25) GTF_W(26) GTF_W(27) GTF_W(28) GTF_W(29) GTF_W(30) GTF_W(31)
-    GTF_W(32) GTF_W(33) GTF_W(34) GTF_W(35) GTF_W(36) GTF_W(37) GTF_W(38) GTF_W(39)
-    GTF_W(40) GTF_W(41) GTF_W(42) GTF_W(43) GTF_W(44) GTF_W(45) GTF_W(46) GTF_W(47)
-    GTF_W(48) GTF_W(49) GTF_W(50) GTF_W(51) GTF_W(52) GTF_W(53) GTF_W(54) GTF_W(55)
-    GTF_W(56) GTF_W(57) GTF_W(58) GTF_W(59) GTF_W(60) GTF_W(61) GTF_W(62)
-#undef GTF_W
-    default: asm volatile("s_waitcnt vmcnt(63)" : "+s"(ring)); break;
-  }
-  return ring;
-}
-
-// The pipelined inputs of a launch, read once from the kernel arguments.
-struct RingInputs {
-  const char* base[kMaxPipe];
-  uint32_t off[kMaxPipe];
-  int dt[kMaxPipe];
-  int n;
-};
-
-// Issue the loads of one tile of every pipelined input into one ring
-// stage.  All lanes take part; a lane whose tile is not a whole in-range
-// tile loads the tensor's first tile instead (never read).
-__device__ __forceinline__ void ring_issue(const RingInputs& in, uint32_t stage_lds, bool ok,
-                                           int64_t eoff) {
-  const int64_t off = ok ? eoff : 0;
-#pragma unroll
-  for (int k = 0; k < kMaxPipe; ++k) {
-    if (k >= in.n) break;
-    const uint32_t dst = stage_lds + in.off[k];
-    if (in.dt[k] == DT_BF16) {
-      dma16(in.base[k] + off * 2, dst);
-    } else if (in.dt[k] == DT_F32) {
-      const char* g = in.base[k] + off * 4;
-      dma16(g, dst);
-      dma16(g + 16, dst + 1024);
-    } else {
-      const char* g = in.base[k] + off;
-      dma4(g, dst);
-      dma4(g + 4, dst + 256);
-    }
-  }
-}
-
 // ---------------------------------------------------------------- executor
-__global__ void __launch_bounds__(kBlock) exec_kernel(const ExecArgs a) {
+// K sub-tiles per lane tile, NS spill slots (see isa.h).  Lane tiles of an
+// item are visited as q = (pass, s): pass = which rows of the block, s =
+// which run of K sub-tiles along the row; sub-tile k of run s sits at
+// column (lane_in_row + (s * K + k) * tpr) * kV.  A run whose K sub-tiles
+// are whole in every lane of the wave goes to the FAST instance at once;
+// any other run goes sub-tile by sub-tile to the partial instance.  Either
+// way each lane adds its elements to the row accumulator in the same order.
+template <int K, int NS>
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3)))
+exec_kernel(const ExecArgs a) {
   extern __shared__ float lds[];
   float* lds_col = lds;
   float* lds_row = lds + a.n_col_slots * a.PW;
@@ -612,30 +522,10 @@ __global__ void __launch_bounds__(kBlock) exec_kernel(const ExecArgs a) {
   const Instr* row_prog = a.prog + a.n_col;
   const Instr* el_prog = a.prog + a.n_col + a.n_row;
   const int64_t erow_stride = a.R == 1 ? 0 : a.C;
+  const bool vec_ok = a.vec_ok != 0;
+  const int ks = tpr * kV;  // elements between a lane's sub-tiles
   bool staged = false;
   float dummy = 0.f;
-  const int lane = tid & 63;
-  // the ring needs a whole first tile in every pipelined tensor (the
-  // fallback address of out-of-range tiles)
-  const bool ring_on = a.n_pipe > 0 && a.n_stage >= 2 && a.vec_ok && a.C >= kV && a.R >= 1;
-  const bool vec_ok = a.vec_ok != 0;
-  const int n_stage = ring_on ? a.n_stage : 1;
-  const int ring_wait = (a.n_stage - 1) * a.n_dma;
-  RingInputs rin;
-  rin.n = ring_on ? a.n_pipe : 0;
-#pragma unroll
-  for (int k = 0; k < kMaxPipe; ++k) {
-    const int slot = k < a.n_pipe ? a.pipe_slot[k] : 0;
-    rin.base[k] = (const char*)a.ptr[slot];
-    rin.off[k] = k < a.n_pipe ? (uint32_t)a.ring_off[slot] : 0u;
-    rin.dt[k] = a.pipe_dt[k];
-  }
-  // this wave's ring: generic pointer for reads, LDS address for the loads
-  const uint32_t wave = __builtin_amdgcn_readfirstlane((uint32_t)tid >> 6);
-  const int ring_wave_off = a.ring_lds_off + (int)wave * a.n_stage * a.stage_bytes;
-  const char* ring_gen = (const char*)lds + ring_wave_off;
-  const uint32_t ring_w =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)((char*)lds) + (uint32_t)ring_wave_off;
 
   for (int64_t item = blockIdx.x; item < a.n_items; item += gridDim.x) {
     const int64_t rb = item / a.n_panels;
@@ -648,8 +538,8 @@ __global__ void __launch_bounds__(kBlock) exec_kernel(const ExecArgs a) {
     if (a.n_col > 0 && (a.n_panels > 1 || !staged)) {
       __syncthreads();
       for (int c = tid; c < nc; c += kBlock) {
-        Tile t{0, c0 + c, 0, c, 0, 1, false};
-        interpret<1, M_COL, false>(a, col_prog, a.n_col, t, lds_col, lds_row, dummy, rb == 0);
+        Tile t{0, c0 + c, 0, c, 0, 1, 0, false, false};
+        interpret<1, M_COL, false, NS>(a, col_prog, a.n_col, t, lds_col, lds_row, dummy, rb == 0);
       }
       __syncthreads();
       staged = true;
@@ -657,78 +547,67 @@ __global__ void __launch_bounds__(kBlock) exec_kernel(const ExecArgs a) {
     if (a.n_row > 0) {
       __syncthreads();
       for (int r = tid; r < nr; r += kBlock) {
-        Tile t{r0 + r, 0, 0, 0, r, 1, false};
-        interpret<1, M_ROW, false>(a, row_prog, a.n_row, t, lds_col, lds_row, dummy, p == 0);
+        Tile t{r0 + r, 0, 0, 0, r, 1, 0, false, false};
+        interpret<1, M_ROW, false, NS>(a, row_prog, a.n_row, t, lds_col, lds_row, dummy, p == 0);
       }
       __syncthreads();
     }
 
-    // element phase: each lane walks its tiles q = (pass, j) in order; the
-    // pipelined inputs of tile q + n_stage - 1 are requested while tile q
-    // is interpreted.  Cursors advance by increments (no divisions).
     const int npass = (nr + rpp - 1) / rpp;
-    const int tpl = max(1, (nc + tpr * kV - 1) / (tpr * kV));  // tiles per lane per row
-    const int nq = npass * tpl;
-    int ip = 0, ij = 0, is = 0;  // issue cursor: pass, tile in row, stage
-    auto issue_next = [&]() {
-      const int rr = ip * rpp + sub;
-      const int cl = (lt + ij * tpr) * kV;
-      const bool ok = rr < nr && cl + kV <= nc;
-      ring_issue(rin, ring_w + (uint32_t)(is * a.stage_bytes), ok, (r0 + rr) * erow_stride + c0 + cl);
-      if (++ij == tpl) {
-        ij = 0;
-        ++ip;
-      }
-      if (++is == n_stage) is = 0;
-    };
-    if (ring_on) {
-      const int pre = min(n_stage - 1, nq);
-      for (int q = 0; q < pre; ++q) issue_next();
-    }
+    const int tpl = max(1, (nc + ks - 1) / ks);  // sub-tiles per lane per row
+    const int spl = (tpl + K - 1) / K;           // runs of K per lane per row
+    const int nq = npass * spl;
     float acc = 0.f;
-    int pass = 0, j = 0, stage = 0;
+    int pass = 0, s = 0;
     for (int q = 0; q < nq; ++q) {
-      const char* ring = nullptr;
-      if (ring_on) {
-        if (q + n_stage - 1 < nq) {
-          issue_next();
-          ring = wait_vmcnt(ring_wait, ring_gen);
-        } else {
-          ring = wait_vmcnt(0, ring_gen);
+      const int rr = pass * rpp + sub;
+      const int cl0 = (lt + s * K * tpr) * kV;
+      const bool row_ok = rr < nr;
+      const bool whole = vec_ok && row_ok && cl0 + (K - 1) * ks + kV <= nc;
+      // both branches are wave-uniform
+      if (__all(whole)) {
+        Tile t;
+        t.valid = true;
+        t.vec = true;
+        t.row = r0 + rr;
+        t.col = c0 + cl0;
+        t.eoff = t.row * erow_stride + t.col;
+        t.cl = cl0;
+        t.rr = rr;
+        t.cnt = kV;
+        t.kstride = ks;
+        interpret<K * kV, M_ELEM, true, NS>(a, el_prog, a.n_elem, t, lds_col, lds_row, acc, true);
+      } else {
+#pragma unroll 1
+        for (int k = 0; k < K; ++k) {
+          const int cl = cl0 + k * ks;
+          const bool valid = row_ok && cl < nc;
+          if (!__any(valid)) continue;
+          Tile t;
+          t.valid = valid;
+          t.row = r0 + rr;
+          t.col = c0 + cl;
+          t.eoff = t.row * erow_stride + t.col;
+          t.cl = cl;
+          t.rr = rr;
+          t.cnt = min(kV, nc - cl);
+          t.vec = vec_ok && valid && t.cnt == kV;
+          t.kstride = ks;
+          interpret<kV, M_ELEM, false, NS>(a, el_prog, a.n_elem, t, lds_col, lds_row, acc, true);
         }
       }
-      const int rr = pass * rpp + sub;
-      const int cl = (lt + j * tpr) * kV;
-      const bool valid = rr < nr && cl < nc;
-      Tile t;
-      t.valid = valid;
-      t.row = r0 + rr;
-      t.col = c0 + cl;
-      t.eoff = t.row * erow_stride + t.col;
-      t.cl = cl;
-      t.rr = rr;
-      t.cnt = min(kV, nc - cl);
-      t.vec = vec_ok && valid && t.cnt == kV;
-      t.ring = ring_on ? ring + stage * a.stage_bytes : nullptr;
-      t.lane = lane;
-      // both branches are wave-uniform
-      if (__all(t.vec)) {
-        interpret<kV, M_ELEM, true>(a, el_prog, a.n_elem, t, lds_col, lds_row, acc, true);
-      } else if (__any(valid)) {
-        interpret<kV, M_ELEM, false>(a, el_prog, a.n_elem, t, lds_col, lds_row, acc, true);
-      }
-      if (a.reduce && j == tpl - 1) {
+      if (a.reduce && s == spl - 1) {
         const int w = min(tpr, 64);
-        float s = segment_sum(acc, w);
+        float sum = segment_sum(acc, w);
         acc = 0.f;
         if (tpr <= 64) {
-          store_reduced(a, r0 + rr, s, lt == 0 && rr < nr);
+          store_reduced(a, r0 + rr, sum, lt == 0 && rr < nr);
         } else {
           // rows wider than a wave: combine the per-wave sums through LDS in
           // a fixed order (every lane of a wave holds the same sum and
           // writes it; every lane reads the totals of its own row)
-          const int wpr = tpr >> 6;        // waves per row
-          lds_red[tid >> 6] = s;
+          const int wpr = tpr >> 6;  // waves per row
+          lds_red[tid >> 6] = sum;
           __syncthreads();
           float tot = 0.f;
           for (int k = 0; k < wpr; ++k) tot += lds_red[sub * wpr + k];
@@ -736,14 +615,16 @@ __global__ void __launch_bounds__(kBlock) exec_kernel(const ExecArgs a) {
           __syncthreads();
         }
       }
-      if (++j == tpl) {
-        j = 0;
+      if (++s == spl) {
+        s = 0;
         ++pass;
       }
-      if (++stage == n_stage) stage = 0;
     }
   }
 }
+
+template __global__ void exec_kernel<kWideK, kWideNS>(const ExecArgs a);
+template __global__ void exec_kernel<1, kNS>(const ExecArgs a);
 
 // ---------------------------------------------------------------- buckets
 // One workgroup per chunk: a run of up to kChunkElems elements of one tensor
@@ -816,10 +697,24 @@ __global__ void __launch_bounds__(kBlock) bucket_kernel(const BucketArgs a) {
   }
 }
 
+// Plain copy of n16 16-byte words: each thread has kCopyUnroll loads in
+// flight before it stores; the last partial round is predicated.
+constexpr int kCopyUnroll = 4;
 __global__ void __launch_bounds__(kBlock) copy_kernel(uint4* __restrict__ dst,
                                                       const uint4* __restrict__ src, size_t n16) {
-  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < n16; i += (size_t)gridDim.x * kBlock)
-    dst[i] = src[i];
+  const size_t span = (size_t)kBlock * kCopyUnroll;
+  const size_t step = (size_t)gridDim.x * span;
+  size_t i = (size_t)blockIdx.x * span + threadIdx.x;
+  for (; i + (kCopyUnroll - 1) * kBlock < n16; i += step) {
+    uint4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) v[u] = src[i + u * kBlock];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) dst[i + u * kBlock] = v[u];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u)
+    if (i + u * kBlock < n16) dst[i + u * kBlock] = src[i + u * kBlock];
 }
 
 // ================================================================ host side
@@ -827,7 +722,7 @@ namespace {
 
 struct DevInfo {
   int cus = 0;
-  std::map<int, int> occ;  // lds bytes -> resident workgroups per CU
+  std::map<std::pair<int, int>, int> occ;  // (instance, lds bytes) -> resident workgroups per CU
 };
 std::mutex g_mu;
 std::map<int, DevInfo> g_dev;
@@ -844,16 +739,23 @@ int device_cus(int dev) {
   return d.cus;
 }
 
-int exec_occupancy(int dev, int lds_bytes) {
+typedef void (*ExecFn)(const ExecArgs);
+ExecFn exec_instance(int K) {
+  return K == kWideK ? exec_kernel<kWideK, kWideNS> : exec_kernel<1, kNS>;
+}
+
+int exec_occupancy(int dev, int K, int lds_bytes) {
   std::lock_guard<std::mutex> lk(g_mu);
   DevInfo& d = g_dev[dev];
-  auto it = d.occ.find(lds_bytes);
+  const std::pair<int, int> key(K, lds_bytes);
+  auto it = d.occ.find(key);
   if (it != d.occ.end()) return it->second;
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, exec_kernel, kBlock, lds_bytes) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, exec_instance(K), kBlock, lds_bytes) !=
+          hipSuccess ||
       nb <= 0)
     nb = 2;
-  d.occ[lds_bytes] = nb;
+  d.occ[key] = nb;
   return nb;
 }
 
@@ -880,9 +782,12 @@ int launch_group(const CompiledGroup& cg, void* const* tensor_ptrs, hipStream_t 
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  const int64_t resident = (int64_t)device_cus(dev) * exec_occupancy(dev, cg.lds_bytes);
-  const int64_t grid = a.n_items < resident ? a.n_items : resident;
-  hipLaunchKernelGGL(exec_kernel, dim3((unsigned)grid), dim3(kBlock), cg.lds_bytes, stream, a);
+  // As many workgroups as fit at once, spread so that every workgroup gets
+  // the same number of items (the last round is not left half empty).
+  const int64_t resident = (int64_t)device_cus(dev) * exec_occupancy(dev, a.K, cg.lds_bytes);
+  const int64_t rounds = (a.n_items + resident - 1) / resident;
+  const int64_t grid = (a.n_items + rounds - 1) / rounds;
+  hipLaunchKernelGGL(exec_instance(a.K), dim3((unsigned)grid), dim3(kBlock), cg.lds_bytes, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "exec_kernel launch");
   return GTF_OK;
@@ -948,7 +853,7 @@ int launch_copy(void* dst, const void* src, size_t nbytes, hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  size_t grid = (n16 + kBlock - 1) / kBlock;
+  size_t grid = (n16 + (size_t)kBlock * kCopyUnroll - 1) / ((size_t)kBlock * kCopyUnroll);
   const size_t cap = (size_t)device_cus(dev) * 8;
   if (grid > cap) grid = cap;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream, (uint4*)dst,

@@ -191,6 +191,7 @@ struct Codegen {
   static constexpr int kEmpty = -1000000;
   enum { RA = 0, RB = 1 };       // register ids: 0 = A, 1 = B, 2.. = spill slots
   int reg[2 + kNS];
+  int ns = kNS;                  // spill slots of the kernel instance
   int max_live = 0;
   bool ok = true;
   std::string why;
@@ -212,7 +213,7 @@ struct Codegen {
   bool is_x(int v) const { return xcls.count(v) != 0; }
   bool live(int r) const { return reg[r] != kEmpty && use(reg[r]) > 0; }
   int where(int v, int avoid = -1) const {
-    for (int r = 0; r < 2 + kNS; ++r)
+    for (int r = 0; r < 2 + ns; ++r)
       if (r != avoid && reg[r] == v) return r;
     return -1;
   }
@@ -224,7 +225,7 @@ struct Codegen {
   }
   void count_live() {
     int n = 0;
-    for (int r = 2; r < 2 + kNS; ++r)
+    for (int r = 2; r < 2 + ns; ++r)
       if (live(r)) ++n;
     max_live = std::max(max_live, n);
   }
@@ -243,7 +244,7 @@ struct Codegen {
   // keep the value in register r alive elsewhere before r is overwritten
   void save(int r) {
     if (!live(r) || holders(reg[r]) > 1) return;
-    for (int s = 2; s < 2 + kNS; ++s)
+    for (int s = 2; s < 2 + ns; ++s)
       if (!live(s)) {
         move(r, s);
         count_live();
@@ -554,13 +555,18 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     }
   }
 
-  // ---- code generation, phase by phase: column, row, element
+  // ---- code generation, phase by phase: column, row, element; first for
+  // the wide instance (two spill slots), else for the narrow one
   std::vector<Instr> prog[3];
   int max_depth = 0;
   const int order[3] = {CLS_COL, CLS_ROW, CLS_E};
+  auto generate = [&](int ns, std::string* gwhy) -> bool {
+    for (auto& pr : prog) pr.clear();
+    max_depth = 0;
   for (int ph : order) {
     Codegen g{p, &prog[ph], ph};
     g.init();
+    g.ns = ns;
     for (size_t k = 0; k < slots.size(); ++k) g.ext_slot[slots[k]] = (int)k;
     if (ph == CLS_E) {  // broadcast operands are read from LDS
       for (auto& kv : row_lds) {
@@ -618,7 +624,10 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
           best = (int)k;
         }
       }
-      if (best < 0) return bad("internal: no ready op");
+      if (best < 0) {
+        *gwhy = "internal: no ready op";
+        return false;
+      }
       done[best] = 1;
       const MOp& m = L[best];
       switch (m.kind) {
@@ -636,45 +645,67 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
         g.emit(p.tensors[v].dtype == GTF_BF16 ? F_ST_BF16 : F_ST_F32, g.ext_slot.at(v));
       if (ph != CLS_E && v >= 0 && lds_map.count(v)) g.emit(F_ST_LDS, lds_map.at(v));
     }
-    if (!g.ok) return bad(g.why);
+    if (!g.ok) {
+      *gwhy = g.why;
+      return false;
+    }
     max_depth = std::max(max_depth, g.max_live);
   }
+    return true;
+  };
+  int ns = kWideNS;
+  {
+    std::string w1, w2;
+    if (!generate(kWideNS, &w1)) {
+      ns = kNS;
+      if (!generate(kNS, &w2)) return bad(w2);
+    }
+  }
+  const int K = ns == kWideNS ? kWideK : 1;
 
   size_t total = prog[0].size() + prog[1].size() + prog[2].size();
   if (total > (size_t)kMaxInstr) return bad("op-program longer than the instruction buffer");
 
   // ---- geometry
+  // Work items are (row block, column panel).  A panel is staged in LDS
+  // when the group has column operands; a flat group (no broadcast, no
+  // reduction) is one row of numel elements cut into panels of one lane
+  // tile per thread.  Threads split into rows of tpr lanes; tpr is the
+  // largest power of two that still gives each lane K sub-tiles of the row
+  // (at most 64 for a reduction over many rows, so each row sums inside one
+  // wave).
   ExecArgs& a = cg.args;
   a.R = DR;
   a.C = DC;
-  int64_t C8 = (DC + kV - 1) / kV * kV;
+  a.K = K;
+  a.NS = ns;
+  const int64_t C8 = (DC + kV - 1) / kV * kV;
   int pw;
   if (red_op >= 0) {
     pw = (int)std::max<int64_t>(C8, kV);
     if (!col_lds.empty() && (int64_t)col_lds.size() * C8 > 16384)
       return bad("reduction group with column operands wider than the LDS panel");
     if (C8 > (int64_t)1 << 30) return bad("row too wide");
+  } else if (flat) {
+    pw = kBlock * kV * std::max(K, 2);
   } else {
     pw = (int)std::min<int64_t>(std::max<int64_t>(C8, kV), kPanelMax);
   }
   int64_t n_panels = DC == 0 ? 1 : (DC + pw - 1) / pw;
-  int64_t nt = (pw + kV - 1) / kV;
+  const int64_t nt = (pw + kV - 1) / kV;
   int tpr = 1;
-  if (red_op >= 0) {
-    int64_t want = (nt + 7) / 8;
-    while (tpr < want && tpr < kBlock) tpr <<= 1;
-  } else {
-    while (tpr < nt && tpr < kBlock) tpr <<= 1;
+  {
+    const int64_t want = std::max<int64_t>(1, nt / K);
+    while ((int64_t)tpr * 2 <= want && tpr * 2 <= kBlock) tpr <<= 1;
+    if (red_op >= 0 && tpr > 64 && DR >= 256) tpr = 64;
   }
   if (const char* e = std::getenv("GTF_TPR")) {
     int f = std::atoi(e);
     if (f >= 1 && f <= kBlock && (f & (f - 1)) == 0) tpr = f;
   }
-  int rpp = kBlock / tpr;
-  int64_t k = DR / ((int64_t)rpp * 1024);
-  k = std::max<int64_t>(1, std::min<int64_t>(k, kBlock / rpp));
-  int rb = (int)(rpp * k);
-  int64_t n_rb = DR == 0 ? 0 : (DR + rb - 1) / rb;
+  const int rpp = kBlock / tpr;
+  const int rb = rpp;
+  const int64_t n_rb = DR == 0 ? 0 : (DR + rb - 1) / rb;
   a.n_items = n_rb * n_panels;
   a.n_panels = (int)n_panels;
   a.RB = rb;
@@ -716,71 +747,11 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
       a.cstride[s] = 0;
     }
   }
-  // element inputs streamed through the per-wave LDS ring: a tile of kV
-  // elements is 2 x 16 B (f32), 16 B (bf16) or 2 x 4 B (u8) per lane
-  for (int s = 0; s < kMaxSlots; ++s) a.ring_off[s] = -1;
-  a.n_pipe = 0;
-  a.n_dma = 0;
-  a.stage_bytes = 0;
-  {
-    std::set<int> elem_loads;
-    for (int i : ops) {
-      if (op_cls(i) != CLS_E) continue;
-      for (int k = 0; k < p.ops[i].n_in; ++k) {
-        int t = p.ops[i].in[k];
-        if (!produced.count(t) && cls_of(t) == CLS_E) elem_loads.insert(t);
-      }
-    }
-    for (size_t s = 0; s < slots.size() && a.n_pipe < kMaxPipe; ++s) {
-      if (!elem_loads.count(slots[s])) continue;
-      const int dt = p.tensors[slots[s]].dtype;
-      a.pipe_slot[a.n_pipe] = (int)s;
-      a.pipe_dt[a.n_pipe] = dt == GTF_F32 ? DT_F32 : dt == GTF_BF16 ? DT_BF16 : DT_U8;
-      a.ring_off[s] = a.stage_bytes;
-      a.stage_bytes += dt == GTF_F32 ? 2048 : dt == GTF_BF16 ? 1024 : 512;
-      a.n_dma += dt == GTF_BF16 ? 1 : 2;
-      a.n_pipe += 1;
-    }
-  }
-  // The ring needs at least one whole tile in the domain: a lane whose tile
-  // is out of range loads the tensor's first tile instead.  Its depth is
-  // bounded by the 63 loads vmcnt can count and by the LDS left over.
-  const int64_t staged_lds = (int64_t)col_lds.size() * pw * 4 + (int64_t)row_lds.size() * rb * 4 + 16 * 4 + 16;
-  const int64_t ring_room = std::min<int64_t>(kRingBudget, 64 * 1024 - staged_lds);
-  if (a.n_pipe > 0 && DC >= kV && DR >= 1 && ring_room >= 2 * (kBlock / 64) * (int64_t)a.stage_bytes) {
-    int st = std::min(8, 1 + 63 / a.n_dma);
-    st = std::min<int64_t>(st, ring_room / ((kBlock / 64) * a.stage_bytes));
-    a.n_stage = st;
-  } else {
-    a.n_pipe = 0;
-    a.n_stage = 0;
-    a.n_dma = 0;
-    a.stage_bytes = 0;
-    for (int s = 0; s < kMaxSlots; ++s) a.ring_off[s] = -1;
-  }
-  // element-phase loads carry their ring offset in the immediate field
-  // (-1: read the tensor directly); other phases always read directly
-  {
-    const int e0 = a.n_col + a.n_row;
-    for (int k = 0; k < a.n_col + a.n_row + a.n_elem; ++k) {
-      Instr& ins = a.prog[k];
-      const bool ld = ins.code == F_LD_F32_A || ins.code == F_LD_BF16_A || ins.code == F_LD_U8_A ||
-                      ins.code == F_LD_F32_B || ins.code == F_LD_BF16_B || ins.code == F_LD_U8_B;
-      if (!ld) continue;
-      const int32_t off = k >= e0 ? a.ring_off[ins.arg] : -1;
-      std::memcpy(&ins.imm, &off, sizeof(off));
-    }
-  }
   cg.slot_tensor = slots;
   for (int t : slots) cg.slot_numel.push_back(p.tensors[t].R * p.tensors[t].C);
   cg.n_slots = (int)slots.size();
   cg.max_depth = max_depth;
-  {
-    int64_t off = a.n_col_slots * (int64_t)pw * 4 + a.n_row_slots * (int64_t)rb * 4 + 16 * 4;
-    off = (off + 15) / 16 * 16;
-    a.ring_lds_off = (int)off;
-    cg.lds_bytes = (int)(off + (int64_t)(kBlock / 64) * a.n_stage * a.stage_bytes);
-  }
+  cg.lds_bytes = (int)(a.n_col_slots * (int64_t)pw * 4 + a.n_row_slots * (int64_t)rb * 4 + 16 * 4);
   if (cg.lds_bytes > 64 * 1024) return bad("LDS staging exceeds 64 KiB");
   if (outp) *outp = cg;
   return true;

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define GTF_ABI_VERSION 1u
+#define GTF_ABI_VERSION 2u
 
 /* ---- status codes ---------------------------------------------------- */
 enum {
@@ -181,14 +181,13 @@ typedef struct {
   int32_t rows_per_item;
   int32_t panel_width;    /* columns per panel, a multiple of 8             */
   int32_t threads_per_row;
-  int32_t ring_inputs;    /* element inputs streamed through the LDS ring   */
-  int32_t ring_stages;    /* tiles in flight per wave                       */
-  int32_t ring_stage_bytes;
+  int32_t subtiles;       /* 8-element sub-tiles a lane holds per dispatched
+                             instruction: 4 (wide kernel) or 1 (narrow)     */
   int32_t lds_bytes;      /* dynamic LDS per workgroup                      */
   int32_t program_length; /* op-program instructions, all phases            */
-  int32_t spill_slots;    /* op-program spill slots used (of 6)             */
+  int32_t spill_slots;    /* op-program spill slots used                    */
+  int32_t spill_slots_max;/* spill slots of the kernel: 2 (wide), 6 (narrow) */
   int32_t reduce;         /* 0 none, 1 row sum, 2 row mean                  */
-  int32_t ring_tensor[4]; /* tensor id of each ring input                   */
 } gtf_group_geometry;
 
 int fuse_plan_group_geometry(const gtf_fuse_plan* plan, int32_t g, gtf_group_geometry* out);

@@ -1,11 +1,14 @@
 """Host-side replay of the executor's tile walk (no GPU): for every group of
-the workloads and of the edge shapes the GPU tests run, each lane's tiles
-and each ring prefetch address must stay inside the tensors they read.
+the workloads and of the edge shapes the GPU tests run, every element a lane
+loads or stores must lie inside the tensors, and every 8-element tile of the
+domain must be visited exactly once.
 
 The replay restates the element loop of the executor kernel: items are
 (row block, column panel); 256 threads split into rows of threads_per_row
-lanes; lane tiles q = (pass, j); a prefetch for a tile that is not a whole
-in-range tile falls back to the tensor's first tile."""
+(tpr) lanes; a lane's tiles are runs of K sub-tiles of 8 elements, tpr * 8
+elements apart in its row.  A run whose K sub-tiles are whole in all 64
+lanes of a wave is read with 16-byte loads at once; otherwise each sub-tile
+is handled on its own, partial ones element by element."""
 import numpy as np
 import pytest
 
@@ -13,55 +16,54 @@ import gradient_tensor_fusion_amd as gtf
 from workloads import configs
 from workloads.graph import Graph
 
-KV, BLOCK = 8, 256
-
-
-def _numel(graph, t):
-    n = 1
-    for s in graph.tensors[t].shape:
-        n *= s
-    return n
+KV, BLOCK, WAVE = 8, 256, 64
 
 
 def replay(graph, plan, g):
     geo = plan.geometry(g)
     R, C = geo["rows"], geo["cols"]
     tpr, RB, PW = geo["threads_per_row"], geo["rows_per_item"], geo["panel_width"]
-    panels, items = geo["panels"], geo["items"]
-    assert PW % KV == 0 and BLOCK % tpr == 0 and items == -(-R // RB) * panels or R == 0
+    panels, items, K = geo["panels"], geo["items"], geo["subtiles"]
+    assert K in (1, 4) and geo["spill_slots"] <= geo["spill_slots_max"]
+    assert geo["spill_slots_max"] == (2 if K == 4 else 6)
+    assert PW % KV == 0 and BLOCK % tpr == 0 and (items == -(-R // RB) * panels or R == 0)
+    assert geo["lds_bytes"] <= 64 * 1024
     rpp = BLOCK // tpr
+    ks = tpr * KV
     erow = 0 if R == 1 else C
+    vec_ok = R == 1 or C % KV == 0
+    numel = R * C
     tid = np.arange(BLOCK)
     sub, lt = tid // tpr, tid % tpr
-    ring_numel = [_numel(graph, t) for t in geo["ring_tensor"]]
-    if geo["ring_inputs"]:
-        assert geo["ring_stages"] >= 2 and C >= KV and geo["lds_bytes"] <= 64 * 1024
-        assert all(n >= KV for n in ring_numel)
-    n_tiles = 0
+    seen = []
     for item in range(items):
         rb, p = divmod(item, panels)
         r0, c0 = rb * RB, p * PW
         nr, nc = min(RB, R - r0), min(PW, C - c0)
         assert nr > 0 and nc >= 0
         npass = -(-nr // rpp)
-        tpl = max(1, -(-nc // (tpr * KV)))
-        q = np.arange(npass * tpl)
-        rr = (q // tpl)[None, :] * rpp + sub[:, None]
-        cl = (lt[:, None] + (q % tpl)[None, :] * tpr) * KV
-        ok = (rr < nr) & (cl + KV <= nc)
-        eoff = np.where(ok, (r0 + rr) * erow + c0 + cl, 0)
-        for n in ring_numel:
-            assert np.all(eoff >= 0) and np.all(eoff + KV <= n), (item, n)
-        valid = (rr < nr) & (cl < nc)
-        cnt = np.minimum(KV, nc - cl)
-        last = (r0 + rr) * erow + c0 + cl + cnt - 1
-        assert np.all(last[valid] < R * C)
-        # each tile of the item exactly once
-        ids = (rr * (nc // KV + 1) + cl // KV)[valid]
-        assert ids.size == np.unique(ids).size == nr * (-(-nc // KV))
-        n_tiles += int(valid.sum())
+        tpl = max(1, -(-nc // ks))
+        spl = -(-tpl // K)
+        for q in range(npass * spl):
+            ps, s = divmod(q, spl)
+            rr = ps * rpp + sub
+            cl0 = (lt + s * K * tpr) * KV
+            whole = vec_ok & (rr < nr) & (cl0 + (K - 1) * ks + KV <= nc)
+            fast = np.repeat(whole.reshape(-1, WAVE).all(axis=1), WAVE)
+            for k in range(K):
+                cl = cl0 + k * ks
+                valid = (rr < nr) & (cl < nc)
+                cnt = np.where(fast, KV, np.clip(nc - cl, 0, KV))
+                first = (r0 + rr) * erow + c0 + cl
+                on = valid | fast
+                assert np.all(fast <= valid)
+                assert np.all(first[on] >= 0) and np.all(first[on] + cnt[on] <= numel), (item, q, k)
+                # whole sub-tiles are 16-byte loads: 8 elements from first
+                assert np.all(first[fast] % KV == 0)
+                seen.append((r0 + rr)[on] * (C // KV + 1) + (c0 + cl)[on] // KV)
     want = R * sum(-(-min(PW, C - p * PW) // KV) for p in range(panels)) if C > 0 else 0
-    assert n_tiles == want
+    ids = np.concatenate(seen) if seen else np.zeros(0, dtype=np.int64)
+    assert ids.size == np.unique(ids).size == want
 
 
 def cases():
@@ -90,7 +92,7 @@ def cases():
 
 
 @pytest.mark.parametrize("name,graph", cases())
-def test_tile_walk_and_ring_stay_in_bounds(name, graph):
+def test_tile_walk_stays_in_bounds(name, graph):
     for fuse in (True, False):
         plan = gtf.FusePlan(graph, fuse=fuse)
         for g in range(plan.num_groups):
