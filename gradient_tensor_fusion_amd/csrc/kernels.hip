@@ -161,15 +161,33 @@ __device__ __forceinline__ void expand_u8(float* d, uint2 w) {
   for (int i = 0; i < 4; ++i) d[4 + i] = (float)((w.y >> (8 * i)) & 0xFFu);
 }
 
-// Loads: whole tiles use 16-byte loads per sub-tile (u8: 8 bytes); partial
-// tiles read element by element at clamped in-range indices, without a
-// branch; row and column phases read one element.
+// Loads.  Element phase: whole tiles use one 16-byte load per sub-tile
+// (u8: 8 bytes); partial tiles read element by element at clamped in-range
+// indices, without a branch.  Column phase (V = kV): a tile is kV
+// consecutive columns of a [C] tensor (cstride 1), or one [1,1] value
+// (cstride 0) broadcast.  Row phase (V = 1): one element.
+template <int V, int MODE>
+__device__ __forceinline__ bool tile_mode() {
+  return MODE == M_ELEM || (MODE == M_COL && V > 1);
+}
+template <int V, int MODE>
+__device__ __forceinline__ int64_t tile_base(const Tile& t) {
+  return MODE == M_ELEM ? t.eoff : t.col;
+}
+
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void load_f32(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
   const float* b = (const float*)a.ptr[slot];
-  if (MODE == M_ELEM && V % kV == 0) {
+  if (tile_mode<V, MODE>()) {
+    if (MODE == M_COL && a.cstride[slot] == 0) {
+      const float x = b[0];
+#pragma unroll
+      for (int i = 0; i < V; ++i) d[i] = x;
+      return;
+    }
+    const int64_t base = tile_base<V, MODE>(t);
     if (FAST || t.vec) {
-      const float* p = b + t.eoff;
+      const float* p = b + base;
 #pragma unroll
       for (int k = 0; k < V / kV; ++k) {
         const float4 x = *(const float4*)(p + k * t.kstride);
@@ -179,10 +197,8 @@ __device__ __forceinline__ void load_f32(float (&d)[V], const ExecArgs& a, int s
       }
       return;
     }
-  }
-  if (MODE == M_ELEM) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) d[i] = b[(t.valid && i < t.cnt) ? t.eoff + i : 0];
+    for (int i = 0; i < V; ++i) d[i] = b[(t.valid && i < t.cnt) ? base + i : 0];
     return;
   }
   d[0] = b[elem_offset<V, MODE>(a, slot, t)];
@@ -191,17 +207,22 @@ __device__ __forceinline__ void load_f32(float (&d)[V], const ExecArgs& a, int s
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void load_bf16(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
   const uint16_t* b = (const uint16_t*)a.ptr[slot];
-  if (MODE == M_ELEM && V % kV == 0) {
+  if (tile_mode<V, MODE>()) {
+    if (MODE == M_COL && a.cstride[slot] == 0) {
+      const float x = bf16_at(b);
+#pragma unroll
+      for (int i = 0; i < V; ++i) d[i] = x;
+      return;
+    }
+    const int64_t base = tile_base<V, MODE>(t);
     if (FAST || t.vec) {
-      const uint16_t* p = b + t.eoff;
+      const uint16_t* p = b + base;
 #pragma unroll
       for (int k = 0; k < V / kV; ++k) expand_bf16(d + k * kV, *(const uint4*)(p + k * t.kstride));
       return;
     }
-  }
-  if (MODE == M_ELEM) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) d[i] = bf16_at(b + ((t.valid && i < t.cnt) ? t.eoff + i : 0));
+    for (int i = 0; i < V; ++i) d[i] = bf16_at(b + ((t.valid && i < t.cnt) ? base + i : 0));
     return;
   }
   d[0] = bf16_at(b + elem_offset<V, MODE>(a, slot, t));
@@ -210,28 +231,37 @@ __device__ __forceinline__ void load_bf16(float (&d)[V], const ExecArgs& a, int 
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void load_u8(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
   const uint8_t* b = (const uint8_t*)a.ptr[slot];
-  if (MODE == M_ELEM && V % kV == 0) {
+  if (tile_mode<V, MODE>()) {
+    if (MODE == M_COL && a.cstride[slot] == 0) {
+      const float x = (float)b[0];
+#pragma unroll
+      for (int i = 0; i < V; ++i) d[i] = x;
+      return;
+    }
+    const int64_t base = tile_base<V, MODE>(t);
     if (FAST || t.vec) {
-      const uint8_t* p = b + t.eoff;
+      const uint8_t* p = b + base;
 #pragma unroll
       for (int k = 0; k < V / kV; ++k) expand_u8(d + k * kV, *(const uint2*)(p + k * t.kstride));
       return;
     }
-  }
-  if (MODE == M_ELEM) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) d[i] = (float)b[(t.valid && i < t.cnt) ? t.eoff + i : 0];
+    for (int i = 0; i < V; ++i) d[i] = (float)b[(t.valid && i < t.cnt) ? base + i : 0];
     return;
   }
   d[0] = (float)b[elem_offset<V, MODE>(a, slot, t)];
 }
 
+// Stores: whole tiles 16 bytes per sub-tile; partial tiles one predicated
+// store per element.  A column-phase store writes a [1,C] output (cstride
+// 1) and runs only in the workgroups of the first row block.
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void store_f32(const float (&s)[V], const ExecArgs& a, int slot, const Tile& t) {
   float* b = (float*)a.ptr[slot];
-  if (MODE == M_ELEM && V % kV == 0) {
+  if (tile_mode<V, MODE>()) {
+    const int64_t base = tile_base<V, MODE>(t);
     if (FAST || t.vec) {
-      float* p = b + t.eoff;
+      float* p = b + base;
 #pragma unroll
       for (int k = 0; k < V / kV; ++k) {
         *(float4*)(p + k * t.kstride) = make_float4(s[k * kV], s[k * kV + 1], s[k * kV + 2], s[k * kV + 3]);
@@ -240,12 +270,10 @@ __device__ __forceinline__ void store_f32(const float (&s)[V], const ExecArgs& a
       }
       return;
     }
-  }
-  if (MODE == M_ELEM) {  // partial tile: one predicated store per element
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const bool on = t.valid && i < t.cnt;
-      pstore_b32(b + (on ? t.eoff + i : 0), __float_as_uint(s[i]), lanes(on));
+      pstore_b32(b + (on ? base + i : 0), __float_as_uint(s[i]), lanes(on));
     }
     return;
   }
@@ -255,9 +283,10 @@ __device__ __forceinline__ void store_f32(const float (&s)[V], const ExecArgs& a
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void store_bf16(const float (&s)[V], const ExecArgs& a, int slot, const Tile& t) {
   uint16_t* b = (uint16_t*)a.ptr[slot];
-  if (MODE == M_ELEM && V % kV == 0) {
+  if (tile_mode<V, MODE>()) {
+    const int64_t base = tile_base<V, MODE>(t);
     if (FAST || t.vec) {
-      uint16_t* p = b + t.eoff;
+      uint16_t* p = b + base;
 #pragma unroll
       for (int k = 0; k < V / kV; ++k)
         *(uint4*)(p + k * t.kstride) =
@@ -265,12 +294,10 @@ __device__ __forceinline__ void store_bf16(const float (&s)[V], const ExecArgs& 
                        pack_bf16(s[k * kV + 4], s[k * kV + 5]), pack_bf16(s[k * kV + 6], s[k * kV + 7]));
       return;
     }
-  }
-  if (MODE == M_ELEM) {
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const bool on = t.valid && i < t.cnt;
-      pstore_b16(b + (on ? t.eoff + i : 0), pack_bf16(s[i], 0.f) & 0xFFFFu, lanes(on));
+      pstore_b16(b + (on ? base + i : 0), pack_bf16(s[i], 0.f) & 0xFFFFu, lanes(on));
     }
     return;
   }
@@ -451,7 +478,11 @@ __device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, 
         break;
       case F_ST_LDS:
         if (MODE == M_ROW) lds_row[arg * a.RB + t.rr] = A[0];
-        if (MODE == M_COL) lds_col[arg * a.PW + t.cl] = A[0];
+        if (MODE == M_COL) {
+#pragma unroll
+          for (int i = 0; i < V; ++i)
+            if (i < t.cnt) lds_col[arg * a.PW + t.cl + i] = A[i];
+        }
         break;
       default:
         break;
@@ -536,10 +567,12 @@ exec_kernel(const ExecArgs a) {
     const int nc = (int)min((int64_t)a.PW, a.C - c0);
 
     if (a.n_col > 0 && (a.n_panels > 1 || !staged)) {
+      // column phase: kV consecutive columns per thread per pass
       __syncthreads();
-      for (int c = tid; c < nc; c += kBlock) {
-        Tile t{0, c0 + c, 0, c, 0, 1, 0, false, false};
-        interpret<1, M_COL, false, NS>(a, col_prog, a.n_col, t, lds_col, lds_row, dummy, rb == 0);
+      for (int c = tid * kV; c < nc; c += kBlock * kV) {
+        const int cnt = min(kV, nc - c);
+        Tile t{0, c0 + c, 0, c, 0, cnt, 0, true, vec_ok && cnt == kV};
+        interpret<kV, M_COL, false, NS>(a, col_prog, a.n_col, t, lds_col, lds_row, dummy, rb == 0);
       }
       __syncthreads();
       staged = true;

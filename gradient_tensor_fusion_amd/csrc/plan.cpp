@@ -560,7 +560,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   std::vector<Instr> prog[3];
   int max_depth = 0;
   const int order[3] = {CLS_COL, CLS_ROW, CLS_E};
-  auto generate = [&](int ns, std::string* gwhy) -> bool {
+  auto generate = [&](int ns, bool hoist, std::string* gwhy) -> bool {
     for (auto& pr : prog) pr.clear();
     max_depth = 0;
   for (int ph : order) {
@@ -592,6 +592,28 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     }
     // externals this phase stages into LDS for the element phase
     const auto& lds_map = ph == CLS_ROW ? row_lds : col_lds;
+    if (ph != CLS_E)
+      for (auto& kv : lds_map)
+        if (!produced.count(kv.first)) g.loadable.insert(kv.first);
+    // load hoisting: the phase's first two external loads (in order of
+    // first use) go to A and B at once, so both are in flight together
+    if (hoist) {
+      std::vector<int> first_use;
+      auto note = [&](int v) {
+        if (g.loadable.count(v) && std::find(first_use.begin(), first_use.end(), v) == first_use.end())
+          first_use.push_back(v);
+      };
+      if (ph != CLS_E)
+        for (auto& kv : lds_map)
+          if (!produced.count(kv.first)) note(kv.first);
+      for (auto& m : L)
+        for (int k = 0; k < (m.kind == 1 ? 2 : 1); ++k) note(m.in[k]);
+      for (size_t i = 0; i < first_use.size() && i < 2; ++i) {
+        const int r = i == 0 ? Codegen::RA : Codegen::RB;
+        g.emit(g.load_form(first_use[i], r), g.ext_slot.at(first_use[i]));
+        g.reg[r] = first_use[i];
+      }
+    }
     if (ph != CLS_E) {
       for (auto& kv : lds_map) {
         if (produced.count(kv.first)) continue;
@@ -655,10 +677,10 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   };
   int ns = kWideNS;
   {
-    std::string w1, w2;
-    if (!generate(kWideNS, &w1)) {
+    std::string w;
+    if (!generate(kWideNS, true, &w) && !generate(kWideNS, false, &w)) {
       ns = kNS;
-      if (!generate(kNS, &w2)) return bad(w2);
+      if (!generate(kNS, true, &w) && !generate(kNS, false, &w)) return bad(w);
     }
   }
   const int K = ns == kWideNS ? kWideK : 1;
