@@ -16,7 +16,8 @@ value = algorithmic bytes per step / time per step (GB/s), where the
 algorithmic bytes count each distinct external input of a group read once
 and each output written once, and 2 x payload for pack and for unpack.
 The roofline entry is for the dominant kernel (most time per step), timed
-launch by launch with HIP events on the stream the kernels run on.  The
+with HIP events on the stream the kernels run on: one pair per step around
+that kernel's block of back-to-back launches.  The
 unfused baseline (one launch per op, intermediates stored) and the
 per-tensor bucket baseline run the same data after the timed region.  The
 CPU baseline times the oracle on a bounded sample of the same workload.
@@ -117,28 +118,33 @@ DROP_D = {"h": ("normal", 0.0, 1.0), "mask": ("bernoulli", 0.1, 0.0), "R": ("nor
 
 
 class Timer:
-    """Event pairs around launches of one kernel, on the current stream (the
-    stream the kernels are launched on).  Events are created up front so
-    that recording one costs the host only the record call."""
+    """One event pair around a block of consecutive launches of one kernel,
+    on the current stream (the stream the kernels are launched on).
+    Back-to-back launches run without gaps, so block time / launches is the
+    kernel's average duration; a pair around every single launch would add
+    the marker and dispatch latency of each.  Events are created up front."""
 
-    def __init__(self, torch, n):
+    def __init__(self, torch, n_blocks):
         self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(n)]
+                   for _ in range(n_blocks)]
         self.i = 0
+        self.launches = 0
 
-    def around(self, fn):
+    def block(self, fns):
         e0, e1 = self.ev[self.i]
         self.i += 1
         e0.record()
-        fn()
+        for f in fns:
+            f()
         e1.record()
+        self.launches += len(fns)
 
     def total_ms(self):
         return sum(a.elapsed_time(b) for a, b in self.ev[: self.i])
 
     @property
     def count(self):
-        return self.i
+        return self.launches
 
 
 # ------------------------------------------------------------ c5 workload
@@ -203,10 +209,8 @@ class C5:
             for f in self.bucket_calls:
                 f()
             return
-        for f in self.exec_calls:
-            exec_t.around(f)
-        for f in self.bucket_calls:
-            bucket_t.around(f)
+        exec_t.block(self.exec_calls)
+        bucket_t.block(self.bucket_calls)
 
 
 def time_steps(torch, fn, steps, warmup):
@@ -331,12 +335,12 @@ def main():
     ms, wall = time_steps(torch, w.step, args.steps, args.warmup)
     nbytes = w.bytes_per_step()
     value = nbytes / (ms * 1e-3) / 1e9
-    # per-kernel timing over a second pass of the same steps; queued copies
-    # first put the GPU ahead of the host, so that each event pair brackets
-    # its kernel back to back with the previous one rather than host latency
+    # per-kernel timing over a second pass of the same steps: per step, one
+    # event pair around the executor launches and one around the bucket
+    # launches; queued copies first put the GPU ahead of the host
     cb = CopyBench(torch, gtf)
-    et = Timer(torch, args.steps * len(w.exec_calls))
-    bt = Timer(torch, args.steps * len(w.bucket_calls))
+    et = Timer(torch, args.steps)
+    bt = Timer(torch, args.steps)
     torch.cuda.synchronize()
     cb.lead()
     for _ in range(args.steps):
