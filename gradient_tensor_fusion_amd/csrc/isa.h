@@ -20,10 +20,10 @@
 // holding one tile.  Every op reads A (and B) and writes A; moves between
 // A, B and the slots are explicit instructions.  Each instruction form has
 // exactly one body in the kernel, and every register index is a
-// compile-time constant, so the registers stay in VGPRs.  Two kernel
-// instances exist: wide (K = 4, NS = 2: 4 x 32 VGPRs of registers) for
-// programs that fit two spill slots, and narrow (K = 1, NS = 6) for the
-// rest.
+// compile-time constant, so the registers stay in VGPRs.  Three kernel
+// instances exist: wide with no spill slot (K = 4, NS = 0: A and B only,
+// the highest occupancy), wide with two (K = 4, NS = 2: 4 x 32 VGPRs of
+// registers), and narrow (K = 1, NS = 6) for programs that need more.
 #pragma once
 
 #include <stdint.h>
@@ -95,7 +95,7 @@ struct ExecArgs {
   int32_t red_slot;        // external slot of the reduce output
   int32_t vec_ok;          // element tensors and rows are 16-byte aligned
   int32_t K;               // sub-tiles per lane tile: kWideK (wide) or 1 (narrow)
-  int32_t NS;              // spill slots of the instance: kWideNS or kNS
+  int32_t NS;              // spill slots of the instance: 0, kWideNS or kNS
   void* ptr[kMaxSlots];
   int64_t rstride[kMaxSlots];
   int64_t cstride[kMaxSlots];

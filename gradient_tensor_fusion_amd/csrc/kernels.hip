@@ -431,7 +431,7 @@ template <int V, int MODE, bool FAST, int NS>
 __device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, int n,
                                           const Tile& t, float* lds_col, float* lds_row,
                                           float& acc, bool store_global) {
-  float A[V], B[V], S[NS][V];
+  float A[V], B[V], S[NS > 0 ? NS : 1][V];
   if (n <= 0) return;
   Instr cur = prog[0];
   for (int pc = 0; pc < n; ++pc) {
@@ -557,7 +557,7 @@ __device__ __forceinline__ void store_reduced(const ExecArgs& a, int64_t row, fl
 // any other run goes sub-tile by sub-tile to the partial instance.  Either
 // way each lane adds its elements to the row accumulator in the same order.
 template <int K, int NS>
-__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NS == 0 ? 4 : 3)))
 exec_kernel(const ExecArgs a) {
   extern __shared__ float lds[];
   float* lds_col = lds;
@@ -675,6 +675,7 @@ exec_kernel(const ExecArgs a) {
   }
 }
 
+template __global__ void exec_kernel<kWideK, 0>(const ExecArgs a);
 template __global__ void exec_kernel<kWideK, kWideNS>(const ExecArgs a);
 template __global__ void exec_kernel<1, kNS>(const ExecArgs a);
 
@@ -792,18 +793,19 @@ int device_cus(int dev) {
 }
 
 typedef void (*ExecFn)(const ExecArgs);
-ExecFn exec_instance(int K) {
-  return K == kWideK ? exec_kernel<kWideK, kWideNS> : exec_kernel<1, kNS>;
+ExecFn exec_instance(int K, int NS) {
+  if (K != kWideK) return exec_kernel<1, kNS>;
+  return NS == 0 ? exec_kernel<kWideK, 0> : exec_kernel<kWideK, kWideNS>;
 }
 
-int exec_occupancy(int dev, int K, int lds_bytes) {
+int exec_occupancy(int dev, int K, int NS, int lds_bytes) {
   std::lock_guard<std::mutex> lk(g_mu);
   DevInfo& d = g_dev[dev];
-  const std::pair<int, int> key(K, lds_bytes);
+  const std::pair<int, int> key(K * 16 + NS, lds_bytes);
   auto it = d.occ.find(key);
   if (it != d.occ.end()) return it->second;
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, exec_instance(K), kBlock, lds_bytes) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, exec_instance(K, NS), kBlock, lds_bytes) !=
           hipSuccess ||
       nb <= 0)
     nb = 2;
@@ -836,10 +838,10 @@ int launch_group(const CompiledGroup& cg, void* const* tensor_ptrs, hipStream_t 
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   // As many workgroups as fit at once, spread so that every workgroup gets
   // the same number of items (the last round is not left half empty).
-  const int64_t resident = (int64_t)device_cus(dev) * exec_occupancy(dev, a.K, cg.lds_bytes);
+  const int64_t resident = (int64_t)device_cus(dev) * exec_occupancy(dev, a.K, a.NS, cg.lds_bytes);
   const int64_t rounds = (a.n_items + resident - 1) / resident;
   const int64_t grid = (a.n_items + rounds - 1) / rounds;
-  hipLaunchKernelGGL(exec_instance(a.K), dim3((unsigned)grid), dim3(kBlock), cg.lds_bytes, stream, a);
+  hipLaunchKernelGGL(exec_instance(a.K, a.NS), dim3((unsigned)grid), dim3(kBlock), cg.lds_bytes, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "exec_kernel launch");
   return GTF_OK;

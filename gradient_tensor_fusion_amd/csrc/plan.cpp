@@ -675,15 +675,21 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   }
     return true;
   };
-  int ns = kWideNS;
+  // instances in order of preference: wide with no spill slot (highest
+  // occupancy), wide with two, narrow with six
+  int ns = -1;
   {
     std::string w;
-    if (!generate(kWideNS, true, &w) && !generate(kWideNS, false, &w)) {
-      ns = kNS;
-      if (!generate(kNS, true, &w) && !generate(kNS, false, &w)) return bad(w);
+    const int tries[3] = {0, kWideNS, kNS};
+    for (int n : tries) {
+      if (generate(n, true, &w) || generate(n, false, &w)) {
+        ns = n;
+        break;
+      }
     }
+    if (ns < 0) return bad(w);
   }
-  const int K = ns == kWideNS ? kWideK : 1;
+  const int K = ns == kNS ? 1 : kWideK;
 
   size_t total = prog[0].size() + prog[1].size() + prog[2].size();
   if (total > (size_t)kMaxInstr) return bad("op-program longer than the instruction buffer");

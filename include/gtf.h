@@ -186,7 +186,7 @@ typedef struct {
   int32_t lds_bytes;      /* dynamic LDS per workgroup                      */
   int32_t program_length; /* op-program instructions, all phases            */
   int32_t spill_slots;    /* op-program spill slots used                    */
-  int32_t spill_slots_max;/* spill slots of the kernel: 2 (wide), 6 (narrow) */
+  int32_t spill_slots_max;/* spill slots of the kernel: 0 or 2 (wide), 6 (narrow) */
   int32_t reduce;         /* 0 none, 1 row sum, 2 row mean                  */
 } gtf_group_geometry;
 
