@@ -427,14 +427,17 @@ __device__ __forceinline__ void fill(float (&d)[V], float x) {
 // guarded blocks).  The other instance handles partial sub-tiles at row and
 // tensor ends.  Forms naming a slot beyond NS never occur in a program
 // compiled for the instance and have empty bodies.
+// run_prog executes instructions [pc0, n) on registers the caller owns, so
+// a program can be started before a phase barrier (its leading loads) and
+// finished after it; interpret runs a whole program on its own registers.
 template <int V, int MODE, bool FAST, int NS>
-__device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, int n,
-                                          const Tile& t, float* lds_col, float* lds_row,
-                                          float& acc, bool store_global) {
-  float A[V], B[V], S[NS > 0 ? NS : 1][V];
-  if (n <= 0) return;
-  Instr cur = prog[0];
-  for (int pc = 0; pc < n; ++pc) {
+__device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, int pc0, int n,
+                                         const Tile& t, float (&A)[V], float (&B)[V],
+                                         float (&S)[NS > 0 ? NS : 1][V], float* lds_col,
+                                         float* lds_row, float& acc, bool store_global) {
+  if (pc0 >= n) return;
+  Instr cur = prog[pc0];
+  for (int pc = pc0; pc < n; ++pc) {
     const Instr nxt = prog[pc + 1 < n ? pc + 1 : pc];
     const int arg = cur.arg;
     const float* col = lds_col + arg * a.PW + t.cl;
@@ -508,6 +511,14 @@ __device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, 
     }
     cur = nxt;
   }
+}
+
+template <int V, int MODE, bool FAST, int NS>
+__device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, int n,
+                                          const Tile& t, float* lds_col, float* lds_row,
+                                          float& acc, bool store_global) {
+  float A[V], B[V], S[NS > 0 ? NS : 1][V];
+  run_prog<V, MODE, FAST, NS>(a, prog, 0, n, t, A, B, S, lds_col, lds_row, acc, store_global);
 }
 
 // ---------------------------------------------------------------- reduce tail
@@ -585,32 +596,62 @@ exec_kernel(const ExecArgs a) {
     const int64_t c0 = (int64_t)p * a.PW;
     const int nc = (int)min((int64_t)a.PW, a.C - c0);
 
-    if (a.n_col > 0 && (a.n_panels > 1 || !staged)) {
-      // column phase: kV consecutive columns per thread per pass
-      __syncthreads();
-      for (int c = tid * kV; c < nc; c += kBlock * kV) {
-        const int cnt = min(kV, nc - c);
-        Tile t{0, c0 + c, 0, c, 0, cnt, 0, true, vec_ok && cnt == kV};
-        interpret<kV, M_COL, false, NS>(a, col_prog, a.n_col, t, lds_col, lds_row, dummy, rb == 0);
-      }
-      __syncthreads();
-      staged = true;
-    }
-    if (a.n_row > 0) {
-      __syncthreads();
-      for (int r = tid; r < nr; r += kBlock) {
-        Tile t{r0 + r, 0, 0, 0, r, 1, 0, false, false};
-        interpret<1, M_ROW, false, NS>(a, row_prog, a.n_row, t, lds_col, lds_row, dummy, p == 0);
-      }
-      __syncthreads();
-    }
-
+    const bool col_now = a.n_col > 0 && (a.n_panels > 1 || !staged);
+    const bool row_now = a.n_row > 0;
     const int npass = (nr + rpp - 1) / rpp;
     const int tpl = max(1, (nc + ks - 1) / ks);  // sub-tiles per lane per row
     const int spl = (tpl + K - 1) / K;           // runs of K per lane per row
     const int nq = npass * spl;
+    // Column phase (kV consecutive columns per thread per pass, from thread
+    // 0 up) and row phase (one row per thread, from the last thread down)
+    // share one barrier pair, so their loads overlap too.
+    if (col_now || row_now) {
+      __syncthreads();
+      if (col_now) {
+        for (int c = tid * kV; c < nc; c += kBlock * kV) {
+          const int cnt = min(kV, nc - c);
+          Tile t{0, c0 + c, 0, c, 0, cnt, 0, true, vec_ok && cnt == kV};
+          interpret<kV, M_COL, false, NS>(a, col_prog, a.n_col, t, lds_col, lds_row, dummy, rb == 0);
+        }
+        staged = true;
+      }
+      if (row_now) {
+        for (int r = kBlock - 1 - tid; r < nr; r += kBlock) {
+          Tile t{r0 + r, 0, 0, 0, r, 1, 0, false, false};
+          interpret<1, M_ROW, false, NS>(a, row_prog, a.n_row, t, lds_col, lds_row, dummy, p == 0);
+        }
+      }
+      __syncthreads();
+    }
+
     float acc = 0.f;
     int pass = 0, s = 0;
+    // reduce tail after the last run of a row, then advance (pass, s)
+    auto finish = [&](int rr) {
+      if (a.reduce && s == spl - 1) {
+        const int w = min(tpr, 64);
+        float sum = segment_sum(acc, w);
+        acc = 0.f;
+        if (tpr <= 64) {
+          store_reduced(a, r0 + rr, sum, lt == 0 && rr < nr);
+        } else {
+          // rows wider than a wave: combine the per-wave sums through LDS in
+          // a fixed order (every lane of a wave holds the same sum and
+          // writes it; every lane reads the totals of its own row)
+          const int wpr = tpr >> 6;  // waves per row
+          lds_red[tid >> 6] = sum;
+          __syncthreads();
+          float tot = 0.f;
+          for (int k = 0; k < wpr; ++k) tot += lds_red[sub * wpr + k];
+          store_reduced(a, r0 + rr, tot, lt == 0 && rr < nr);
+          __syncthreads();
+        }
+      }
+      if (++s == spl) {
+        s = 0;
+        ++pass;
+      }
+    };
     for (int q = 0; q < nq; ++q) {
       const int rr = pass * rpp + sub;
       const int cl0 = (lt + s * K * tpr) * kV;
@@ -648,29 +689,7 @@ exec_kernel(const ExecArgs a) {
           interpret<kV, M_ELEM, false, NS>(a, el_prog, a.n_elem, t, lds_col, lds_row, acc, true);
         }
       }
-      if (a.reduce && s == spl - 1) {
-        const int w = min(tpr, 64);
-        float sum = segment_sum(acc, w);
-        acc = 0.f;
-        if (tpr <= 64) {
-          store_reduced(a, r0 + rr, sum, lt == 0 && rr < nr);
-        } else {
-          // rows wider than a wave: combine the per-wave sums through LDS in
-          // a fixed order (every lane of a wave holds the same sum and
-          // writes it; every lane reads the totals of its own row)
-          const int wpr = tpr >> 6;  // waves per row
-          lds_red[tid >> 6] = sum;
-          __syncthreads();
-          float tot = 0.f;
-          for (int k = 0; k < wpr; ++k) tot += lds_red[sub * wpr + k];
-          store_reduced(a, r0 + rr, tot, lt == 0 && rr < nr);
-          __syncthreads();
-        }
-      }
-      if (++s == spl) {
-        s = 0;
-        ++pass;
-      }
+      finish(rr);
     }
   }
 }

@@ -744,6 +744,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   a.n_col = (int)prog[CLS_COL].size();
   a.n_row = (int)prog[CLS_ROW].size();
   a.n_elem = (int)prog[CLS_E].size();
+
   a.n_col_slots = (int)col_lds.size();
   a.n_row_slots = (int)row_lds.size();
   a.reduce = 0;
