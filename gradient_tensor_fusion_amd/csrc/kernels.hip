@@ -730,10 +730,21 @@ __device__ __forceinline__ uint4 scale_vec(uint4 w, float s, bool one) {
                     pack_bf16(bf16_lo(w.w) * s, bf16_hi(w.w) * s));
 }
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// 16 bytes from a 4-byte aligned address: the run's source side (the
+// destination side is the one the head aligns to 16 bytes).
+__device__ __forceinline__ uint4 load16(const void* p) {
+  uint4 w;
+  __builtin_memcpy(&w, p, 16);
+  return w;
+}
+
 template <typename T>
 __device__ __forceinline__ void move_run(T* __restrict__ dst, const T* __restrict__ src, int n,
                                          float s) {
   constexpr int per16 = 16 / sizeof(T);
+  constexpr int kU = 4;  // 16-byte moves in flight per thread
   const bool one = s == 1.0f;
   const int tid = threadIdx.x;
   int head = (int)(((16 - ((uintptr_t)dst & 15)) & 15) / sizeof(T));
@@ -742,11 +753,15 @@ __device__ __forceinline__ void move_run(T* __restrict__ dst, const T* __restric
   const int body = (n - head) / per16;
   T* d = dst + head;
   const T* q = src + head;
-  for (int u = tid; u < body; u += kBlock) {
-    uint4 w;
-    __builtin_memcpy(&w, q + (size_t)u * per16, 16);  // source may be 4-byte aligned
-    *(uint4*)(d + (size_t)u * per16) = scale_vec<T>(w, s, one);
+  int u = tid;
+  for (; u + (kU - 1) * kBlock < body; u += kU * kBlock) {
+    uint4 w[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) w[j] = load16(q + (size_t)(u + j * kBlock) * per16);
+#pragma unroll
+    for (int j = 0; j < kU; ++j) *(uint4*)(d + (size_t)(u + j * kBlock) * per16) = scale_vec<T>(w[j], s, one);
   }
+  for (; u < body; u += kBlock) *(uint4*)(d + (size_t)u * per16) = scale_vec<T>(load16(q + (size_t)u * per16), s, one);
   const int done = head + body * per16;
   const int tail = n - done;
   if (tid < tail) dst[done + tid] = scale_elem<T>(src[done + tid], s, one);
@@ -769,8 +784,9 @@ __global__ void __launch_bounds__(kBlock) bucket_kernel(const BucketArgs a) {
   }
 }
 
-// Plain copy of n16 16-byte words: each thread has kCopyUnroll loads in
-// flight before it stores; the last partial round is predicated.
+// Plain copy of n16 16-byte words, streamed past the caches: each thread
+// has kCopyUnroll loads in flight before it stores; the last partial round
+// is predicated.
 constexpr int kCopyUnroll = 4;
 __global__ void __launch_bounds__(kBlock) copy_kernel(uint4* __restrict__ dst,
                                                       const uint4* __restrict__ src, size_t n16) {
@@ -778,11 +794,11 @@ __global__ void __launch_bounds__(kBlock) copy_kernel(uint4* __restrict__ dst,
   const size_t step = (size_t)gridDim.x * span;
   size_t i = (size_t)blockIdx.x * span + threadIdx.x;
   for (; i + (kCopyUnroll - 1) * kBlock < n16; i += step) {
-    uint4 v[kCopyUnroll];
+    v4u v[kCopyUnroll];
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) v[u] = src[i + u * kBlock];
+    for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load((const v4u*)(src + i + u * kBlock));
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) dst[i + u * kBlock] = v[u];
+    for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], (v4u*)(dst + i + u * kBlock));
   }
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u)
