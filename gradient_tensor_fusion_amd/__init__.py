@@ -24,7 +24,7 @@ from typing import Dict, List, Sequence
 from . import _capi as C
 from ._capi import GtfError
 
-__all__ = ["FusePlan", "BucketPlan", "device_copy", "GtfError", "PATTERN_NAMES"]
+__all__ = ["FusePlan", "FuseMulti", "BucketPlan", "device_copy", "GtfError", "PATTERN_NAMES"]
 
 PATTERN_NAMES = {0: "kElemWise", 1: "kBroadcast", 2: "kInjective", 3: "kCommReduce",
                  4: "kOutEWiseFusable", 7: "kTuple", 8: "kOpaque"}
@@ -140,6 +140,53 @@ class FusePlan:
         return run
 
 
+class FuseMulti:
+    """fuse_multi_create / bind / run: one launch of a flat group over many
+    tensor sets (set s: numel[s] elements per tensor)."""
+
+    def __init__(self, plan: "FusePlan", g: int, numel: Sequence[int]):
+        self.plan = plan  # the group's program lives in the plan's compiled copy; keep it alive
+        self.numel = [int(n) for n in numel]
+        arr = (c_int64 * max(1, len(self.numel)))(*self.numel)
+        h = c_void_p()
+        C.check(C.lib().fuse_multi_create(plan._h, int(g), len(self.numel), arr, byref(h)))
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and C._lib is not None:
+            C._lib.fuse_multi_destroy(h)
+            self._h = None
+
+    @property
+    def workspace_bytes(self) -> int:
+        b = c_size_t()
+        C.check(C.lib().fuse_multi_workspace_bytes(self._h, byref(b)))
+        return b.value
+
+    def bind(self, sets, workspace, stream=None) -> None:
+        """sets: one {tensor id: tensor} dict per set."""
+        nt = self.plan.n_tensors
+        ptrs = []
+        for d in sets:
+            ptrs += [C.data_ptr(d.get(t)) for t in range(nt)]
+        self._ws, self._sets = workspace, sets  # keep them alive while runs read them
+        C.check(C.lib().fuse_multi_bind(self._h, C.ptr_array(ptrs), C.data_ptr(workspace),
+                                        C.stream_handle(stream)))
+
+    def run(self, stream=None) -> None:
+        C.check(C.lib().fuse_multi_run(self._h, C.stream_handle(stream)))
+
+    def launcher(self, stream=None):
+        f, h, st = C.lib().fuse_multi_run, self._h, C.stream_handle(stream)
+
+        def run():
+            status = f(h, st)
+            if status != C.GTF_OK:
+                C.check(status)
+        return run
+
+
 class BucketPlan:
     """bucket_plan_create / bind / pack / unpack."""
 
@@ -206,6 +253,26 @@ class BucketPlan:
                 C.check(status)
         run.tensors = keep
         return run
+
+    def slot_address(self, buckets, i: int) -> int:
+        """bucket_plan_slot_address: device address of tensor i in its bucket."""
+        out = c_void_p()
+        C.check(C.lib().bucket_plan_slot_address(self._h, C.ptr_array([C.data_ptr(b) for b in buckets]),
+                                                 int(i), byref(out)))
+        return out.value or 0
+
+    def slot_view(self, buckets, i: int, shape):
+        """Tensor i's place in its bucket as a tensor view of the given shape
+        (its data_ptr() is slot_address(buckets, i)): an output for a fused
+        group whose stores then are the pack."""
+        if not hasattr(self, "_layout"):
+            self._layout = self.query()
+        bof, off, _ = self._layout
+        b = buckets[bof[i]]
+        n = self.numel[i]
+        v = b.reshape(-1).narrow(0, off[i], n).view(tuple(shape))
+        assert n == 0 or v.data_ptr() == self.slot_address(buckets, i)
+        return v
 
     def pack_per_tensor(self, srcs, buckets, scale: float = 1.0, stream=None) -> None:
         C.check(C.lib().bucket_pack_per_tensor(self._h, C.ptr_array([C.data_ptr(t) for t in srcs]),

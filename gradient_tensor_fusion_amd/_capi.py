@@ -35,9 +35,11 @@ EXPORTED = (
     "fuse_plan_create", "fuse_plan_num_groups", "fuse_plan_group_info", "fuse_plan_op_info",
     "fuse_plan_group_geometry",
     "fuse_plan_is_materialized", "fuse_group_run", "fuse_plan_run", "fuse_plan_destroy",
+    "fuse_multi_create", "fuse_multi_workspace_bytes", "fuse_multi_bind", "fuse_multi_run",
+    "fuse_multi_destroy",
     "bucket_plan_create", "bucket_plan_query", "bucket_plan_workspace_bytes",
     "bucket_plan_bind", "bucket_pack", "bucket_unpack", "bucket_pack_per_tensor",
-    "bucket_plan_destroy", "gtf_device_copy", "gtf_last_error",
+    "bucket_plan_slot_address", "bucket_plan_destroy", "gtf_device_copy", "gtf_last_error",
 )
 
 
@@ -91,6 +93,12 @@ def lib() -> ctypes.CDLL:
         L.fuse_plan_run.argtypes = [vp, POINTER(vp), vp]
         L.fuse_plan_destroy.argtypes = [vp]
         L.fuse_plan_destroy.restype = None
+        L.fuse_multi_create.argtypes = [vp, c_int32, c_int32, POINTER(c_int64), POINTER(vp)]
+        L.fuse_multi_workspace_bytes.argtypes = [vp, POINTER(c_size_t)]
+        L.fuse_multi_bind.argtypes = [vp, POINTER(vp), vp, vp]
+        L.fuse_multi_run.argtypes = [vp, vp]
+        L.fuse_multi_destroy.argtypes = [vp]
+        L.fuse_multi_destroy.restype = None
         L.bucket_plan_create.argtypes = [POINTER(c_int64), c_int32, c_int32, c_int64, c_uint32,
                                          POINTER(vp)]
         L.bucket_plan_query.argtypes = [vp, POINTER(c_int32), POINTER(c_int32),
@@ -100,6 +108,7 @@ def lib() -> ctypes.CDLL:
         L.bucket_pack.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
         L.bucket_unpack.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
         L.bucket_pack_per_tensor.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
+        L.bucket_plan_slot_address.argtypes = [vp, POINTER(vp), c_int32, POINTER(vp)]
         L.bucket_plan_destroy.argtypes = [vp]
         L.bucket_plan_destroy.restype = None
         L.gtf_device_copy.argtypes = [vp, vp, c_size_t, vp]

@@ -4,8 +4,10 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "gtf.h"
 #include "plan.h"
@@ -15,6 +17,15 @@ struct gtf_fuse_plan {
 };
 struct gtf_bucket_plan {
   gtf::BucketPlan b;
+};
+struct gtf_fuse_multi {
+  gtf::CompiledGroup cg;
+  int32_t n_tensors = 0;
+  std::vector<int64_t> numel;            // per set
+  std::vector<gtf::MultiItem> items;
+  std::vector<unsigned char> staged;     // host copy of the bound tables
+  size_t off_ptrs = 0, off_vec = 0, bytes = 0;
+  void* workspace = nullptr;
 };
 
 namespace gtf {
@@ -31,6 +42,9 @@ int launch_bucket(const BucketPlan& b, const void* const* tens, void* const* bk,
                   bool unpack, bool per_tensor, hipStream_t stream);
 int upload_chunks(BucketPlan& b, void* ws, hipStream_t stream);
 int launch_copy(void* dst, const void* src, size_t nbytes, hipStream_t stream);
+int launch_multi(const CompiledGroup& cg, const void* ws, size_t off_ptrs, size_t off_vec,
+                 int64_t n_items, hipStream_t stream);
+int upload_bytes(void* dst, const void* src, size_t n, hipStream_t stream);
 
 namespace {
 
@@ -328,7 +342,99 @@ int bucket_pack_per_tensor(const gtf_bucket_plan* plan, const void* const* src,
   return bucket_run(plan, src, buckets, scale, false, true, hip_stream);
 }
 
+int bucket_plan_slot_address(const gtf_bucket_plan* plan, void* const* buckets, int32_t i,
+                             void** out) {
+  if (plan == nullptr || buckets == nullptr || out == nullptr)
+    return fail(GTF_E_INVALID, "NULL argument");
+  const BucketPlan& b = plan->b;
+  if (i < 0 || i >= (int32_t)b.numel.size()) return fail(GTF_E_INVALID, "tensor index");
+  char* base = (char*)buckets[b.bucket_of[i]];
+  if (base == nullptr && b.numel[i] > 0) return fail(GTF_E_INVALID, "bucket pointer is NULL");
+  const int64_t elem = b.dtype == GTF_BF16 ? 2 : 4;
+  *out = base == nullptr ? nullptr : base + b.offset[i] * elem;
+  return GTF_OK;
+}
+
 void bucket_plan_destroy(gtf_bucket_plan* plan) { delete plan; }
+
+int fuse_multi_create(const gtf_fuse_plan* plan, int32_t g, int32_t n_sets, const int64_t* numel,
+                      gtf_fuse_multi** out) {
+  if (plan == nullptr || out == nullptr || (numel == nullptr && n_sets > 0))
+    return fail(GTF_E_INVALID, "NULL argument");
+  if (g < 0 || g >= (int32_t)plan->p.groups.size()) return fail(GTF_E_INVALID, "group index");
+  if (n_sets < 0) return fail(GTF_E_INVALID, "n_sets < 0");
+  const CompiledGroup& cg = plan->p.groups[g].code;
+  const ExecArgs& a = cg.args;
+  if (a.R > 1 || a.n_col > 0 || a.n_row > 0 || a.reduce != 0)
+    return fail(GTF_E_UNSUPPORTED, "group is not flat (broadcast operand or reduction)");
+  for (int32_t s = 0; s < n_sets; ++s)
+    if (numel[s] < 0) return fail(GTF_E_INVALID, "numel < 0");
+  gtf_fuse_multi* m = new (std::nothrow) gtf_fuse_multi;
+  if (m == nullptr) return fail(GTF_E_INVALID, "out of host memory");
+  m->cg = cg;
+  m->n_tensors = (int32_t)plan->p.tensors.size();
+  m->numel.assign(numel, numel + n_sets);
+  for (int32_t s = 0; s < n_sets; ++s)
+    for (int64_t off = 0; off < numel[s]; off += a.PW) {
+      MultiItem it;
+      it.off = off;
+      it.n = (int32_t)std::min<int64_t>(a.PW, numel[s] - off);
+      it.set = s;
+      m->items.push_back(it);
+    }
+  auto up16 = [](size_t x) { return (x + 15) / 16 * 16; };
+  m->off_ptrs = up16(m->items.size() * sizeof(MultiItem));
+  m->off_vec = up16(m->off_ptrs + (size_t)n_sets * cg.n_slots * sizeof(void*));
+  m->bytes = up16(m->off_vec + (size_t)n_sets * sizeof(uint32_t));
+  *out = m;
+  return GTF_OK;
+}
+
+int fuse_multi_workspace_bytes(const gtf_fuse_multi* m, size_t* bytes) {
+  if (m == nullptr || bytes == nullptr) return fail(GTF_E_INVALID, "NULL argument");
+  *bytes = m->bytes;
+  return GTF_OK;
+}
+
+int fuse_multi_bind(gtf_fuse_multi* m, void* const* tensor_ptrs, void* dev_workspace,
+                    void* hip_stream) {
+  if (m == nullptr || dev_workspace == nullptr || (tensor_ptrs == nullptr && !m->numel.empty()))
+    return fail(GTF_E_INVALID, "NULL argument");
+  if (((uintptr_t)dev_workspace & 15) != 0) return fail(GTF_E_INVALID, "workspace not 16-byte aligned");
+  const CompiledGroup& cg = m->cg;
+  const size_t n_sets = m->numel.size();
+  std::vector<unsigned char> st(m->bytes, 0);
+  std::memcpy(st.data(), m->items.data(), m->items.size() * sizeof(MultiItem));
+  void** ptrs = (void**)(st.data() + m->off_ptrs);
+  uint32_t* vec = (uint32_t*)(st.data() + m->off_vec);
+  for (size_t s = 0; s < n_sets; ++s) {
+    uint32_t mask = 0;
+    for (int k = 0; k < cg.n_slots; ++k) {
+      void* p = tensor_ptrs[s * m->n_tensors + cg.slot_tensor[k]];
+      if (p == nullptr && m->numel[s] > 0)
+        return fail(GTF_E_INVALID, "set " + std::to_string(s) + ": tensor " +
+                                       std::to_string(cg.slot_tensor[k]) + " has no device pointer");
+      ptrs[s * cg.n_slots + k] = p;
+      const uintptr_t align = cg.slot_dtype[k] == GTF_U8 ? 8 : 16;
+      if (((uintptr_t)p % align) == 0) mask |= 1u << k;
+    }
+    vec[s] = mask;
+  }
+  m->staged.swap(st);
+  int rc = upload_bytes(dev_workspace, m->staged.data(), m->bytes, (hipStream_t)hip_stream);
+  if (rc != GTF_OK) return rc;
+  m->workspace = dev_workspace;
+  return GTF_OK;
+}
+
+int fuse_multi_run(const gtf_fuse_multi* m, void* hip_stream) {
+  if (m == nullptr) return fail(GTF_E_INVALID, "NULL argument");
+  if (m->workspace == nullptr) return fail(GTF_E_STATE, "fuse_multi_bind has not been called");
+  return launch_multi(m->cg, m->workspace, m->off_ptrs, m->off_vec, (int64_t)m->items.size(),
+                      (hipStream_t)hip_stream);
+}
+
+void fuse_multi_destroy(gtf_fuse_multi* m) { delete m; }
 
 int gtf_device_copy(void* dst, const void* src, size_t nbytes, void* hip_stream) {
   if (dst == nullptr || src == nullptr) return fail(GTF_E_INVALID, "NULL pointer");

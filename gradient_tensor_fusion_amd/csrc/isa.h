@@ -81,6 +81,14 @@ struct Instr {
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_U8 = 2 };
 
+// One work item of a multi-set run: elements [off, off + n) (n <= the
+// panel width) of every tensor of set `set`.
+struct MultiItem {
+  int64_t off;
+  int32_t n;
+  int32_t set;
+};
+
 // Kernel arguments, passed by value (kernarg segment; read with scalar
 // loads).  Strides are in elements.
 struct ExecArgs {
@@ -93,9 +101,16 @@ struct ExecArgs {
   int32_t reduce;          // 0 none, 1 sum, 2 mean
   int32_t red_dtype;       // reduce output dtype
   int32_t red_slot;        // external slot of the reduce output
-  int32_t vec_ok;          // element tensors and rows are 16-byte aligned
+  uint32_t vec_slots;      // bit s: slot s takes 16-byte (u8: 8-byte) accesses
   int32_t K;               // sub-tiles per lane tile: kWideK (wide) or 1 (narrow)
   int32_t NS;              // spill slots of the instance: 0, kWideNS or kNS
+  // multi-set run of a flat group (null otherwise): item table, one row of
+  // n_slots pointers per set and one 16-byte-access mask per set
+  const MultiItem* m_items;
+  void* const* m_ptrs;
+  const uint32_t* m_vec;
+  int32_t n_slots;
+  int32_t pad_;
   void* ptr[kMaxSlots];
   int64_t rstride[kMaxSlots];
   int64_t cstride[kMaxSlots];

@@ -41,6 +41,16 @@ namespace gtf {
 
 enum Mode { M_ELEM = 0, M_ROW = 1, M_COL = 2 };
 
+// Address spaces made explicit, so that data accesses stay global_load /
+// global_store and slot-pointer reads stay scalar loads wherever the
+// pointers come from (kernel arguments or a device table).
+#define GAS __attribute__((address_space(1)))
+#define CAS __attribute__((address_space(4)))
+typedef void* const CAS SlotPtr;  // a slot's base pointer, read with s_load
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+
 // ---------------------------------------------------------------- numerics
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   // fp32 -> bf16 round to nearest even (one v_cvt_pk_bf16_f32 on gfx950)
@@ -160,6 +170,8 @@ struct Tile {
   int kstride;   // elements between sub-tiles
   bool valid;    // the tile exists (row and column in range)
   bool vec;      // whole sub-tile, 16-byte aligned: vector path
+  SlotPtr* ptrs;      // the slots' base pointers (wave-uniform)
+  uint32_t vmask;     // slots that take 16-byte accesses (wave-uniform)
 };
 
 template <int V, int MODE>
@@ -169,11 +181,11 @@ __device__ __forceinline__ int64_t elem_offset(const ExecArgs& a, int slot, cons
   return t.col * a.cstride[slot];
 }
 
-__device__ __forceinline__ void expand_bf16(float* d, uint4 w) {
+__device__ __forceinline__ void expand_bf16(float* d, u4 w) {
   d[0] = bf16_lo(w.x); d[1] = bf16_hi(w.x); d[2] = bf16_lo(w.y); d[3] = bf16_hi(w.y);
   d[4] = bf16_lo(w.z); d[5] = bf16_hi(w.z); d[6] = bf16_lo(w.w); d[7] = bf16_hi(w.w);
 }
-__device__ __forceinline__ void expand_u8(float* d, uint2 w) {
+__device__ __forceinline__ void expand_u8(float* d, u2 w) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) d[i] = (float)((w.x >> (8 * i)) & 0xFFu);
 #pragma unroll
@@ -181,10 +193,17 @@ __device__ __forceinline__ void expand_u8(float* d, uint2 w) {
 }
 
 // Loads.  Element phase: whole tiles use one 16-byte load per sub-tile
-// (u8: 8 bytes); partial tiles read element by element at clamped in-range
+// (u8: 8 bytes) when the slot is aligned for it, else one load per
+// element; partial tiles read element by element at clamped in-range
 // indices, without a branch.  Column phase (V = kV): a tile is kV
 // consecutive columns of a [C] tensor (cstride 1), or one [1,1] value
 // (cstride 0) broadcast.  Row phase (V = 1): one element.
+// A slot whose pointer (and, for [R,C] tensors, row pitch) allows 16-byte
+// accesses (u8: 8-byte); the host sets one bit per slot (per set in a
+// multi-set run).
+__device__ __forceinline__ bool slot_vec(const Tile& t, int slot) {
+  return (t.vmask >> slot) & 1u;
+}
 template <int V, int MODE>
 __device__ __forceinline__ bool tile_mode() {
   return MODE == M_ELEM || (MODE == M_COL && V > 1);
@@ -194,9 +213,11 @@ __device__ __forceinline__ int64_t tile_base(const Tile& t) {
   return MODE == M_ELEM ? t.eoff : t.col;
 }
 
+__device__ __forceinline__ float bf16_g(const GAS uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
+
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void load_f32(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
-  const float* b = (const float*)a.ptr[slot];
+  const GAS float* b = (const GAS float*)t.ptrs[slot];
   if (tile_mode<V, MODE>()) {
     if (MODE == M_COL && a.cstride[slot] == 0) {
       const float x = b[0];
@@ -205,15 +226,22 @@ __device__ __forceinline__ void load_f32(float (&d)[V], const ExecArgs& a, int s
       return;
     }
     const int64_t base = tile_base<V, MODE>(t);
-    if (FAST || t.vec) {
-      const float* p = b + base;
+    if ((FAST || t.vec) && slot_vec(t, slot)) {
+      const GAS float* p = b + base;
 #pragma unroll
       for (int k = 0; k < V / kV; ++k) {
-        const float4 x = *(const float4*)(p + k * t.kstride);
-        const float4 y = *(const float4*)(p + k * t.kstride + 4);
+        const f4 x = *(const GAS f4*)(p + k * t.kstride);
+        const f4 y = *(const GAS f4*)(p + k * t.kstride + 4);
         d[k * kV + 0] = x.x; d[k * kV + 1] = x.y; d[k * kV + 2] = x.z; d[k * kV + 3] = x.w;
         d[k * kV + 4] = y.x; d[k * kV + 5] = y.y; d[k * kV + 6] = y.z; d[k * kV + 7] = y.w;
       }
+      return;
+    }
+    if (FAST || t.vec) {  // whole tile, element-aligned only
+#pragma unroll
+      for (int k = 0; k < V / kV; ++k)
+#pragma unroll
+        for (int i = 0; i < kV; ++i) d[k * kV + i] = b[base + k * t.kstride + i];
       return;
     }
 #pragma unroll
@@ -225,31 +253,38 @@ __device__ __forceinline__ void load_f32(float (&d)[V], const ExecArgs& a, int s
 
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void load_bf16(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
-  const uint16_t* b = (const uint16_t*)a.ptr[slot];
+  const GAS uint16_t* b = (const GAS uint16_t*)t.ptrs[slot];
   if (tile_mode<V, MODE>()) {
     if (MODE == M_COL && a.cstride[slot] == 0) {
-      const float x = bf16_at(b);
+      const float x = bf16_g(b);
 #pragma unroll
       for (int i = 0; i < V; ++i) d[i] = x;
       return;
     }
     const int64_t base = tile_base<V, MODE>(t);
-    if (FAST || t.vec) {
-      const uint16_t* p = b + base;
+    if ((FAST || t.vec) && slot_vec(t, slot)) {
+      const GAS uint16_t* p = b + base;
 #pragma unroll
-      for (int k = 0; k < V / kV; ++k) expand_bf16(d + k * kV, *(const uint4*)(p + k * t.kstride));
+      for (int k = 0; k < V / kV; ++k) expand_bf16(d + k * kV, *(const GAS u4*)(p + k * t.kstride));
+      return;
+    }
+    if (FAST || t.vec) {  // whole tile, element-aligned only
+#pragma unroll
+      for (int k = 0; k < V / kV; ++k)
+#pragma unroll
+        for (int i = 0; i < kV; ++i) d[k * kV + i] = bf16_g(b + base + k * t.kstride + i);
       return;
     }
 #pragma unroll
-    for (int i = 0; i < V; ++i) d[i] = bf16_at(b + ((t.valid && i < t.cnt) ? base + i : 0));
+    for (int i = 0; i < V; ++i) d[i] = bf16_g(b + ((t.valid && i < t.cnt) ? base + i : 0));
     return;
   }
-  d[0] = bf16_at(b + elem_offset<V, MODE>(a, slot, t));
+  d[0] = bf16_g(b + elem_offset<V, MODE>(a, slot, t));
 }
 
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void load_u8(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
-  const uint8_t* b = (const uint8_t*)a.ptr[slot];
+  const GAS uint8_t* b = (const GAS uint8_t*)t.ptrs[slot];
   if (tile_mode<V, MODE>()) {
     if (MODE == M_COL && a.cstride[slot] == 0) {
       const float x = (float)b[0];
@@ -258,10 +293,17 @@ __device__ __forceinline__ void load_u8(float (&d)[V], const ExecArgs& a, int sl
       return;
     }
     const int64_t base = tile_base<V, MODE>(t);
-    if (FAST || t.vec) {
-      const uint8_t* p = b + base;
+    if ((FAST || t.vec) && slot_vec(t, slot)) {
+      const GAS uint8_t* p = b + base;
 #pragma unroll
-      for (int k = 0; k < V / kV; ++k) expand_u8(d + k * kV, *(const uint2*)(p + k * t.kstride));
+      for (int k = 0; k < V / kV; ++k) expand_u8(d + k * kV, *(const GAS u2*)(p + k * t.kstride));
+      return;
+    }
+    if (FAST || t.vec) {  // whole tile, element-aligned only
+#pragma unroll
+      for (int k = 0; k < V / kV; ++k)
+#pragma unroll
+        for (int i = 0; i < kV; ++i) d[k * kV + i] = (float)b[base + k * t.kstride + i];
       return;
     }
 #pragma unroll
@@ -271,28 +313,38 @@ __device__ __forceinline__ void load_u8(float (&d)[V], const ExecArgs& a, int sl
   d[0] = (float)b[elem_offset<V, MODE>(a, slot, t)];
 }
 
-// Stores: whole tiles 16 bytes per sub-tile; partial tiles one predicated
-// store per element.  A column-phase store writes a [1,C] output (cstride
+// Stores: whole tiles 16 bytes per sub-tile (one store per element when
+// the slot is not 16-byte aligned); partial tiles one predicated store per
+// element.  A column-phase store writes a [1,C] output (cstride
 // 1) and runs only in the workgroups of the first row block.
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void store_f32(const float (&s)[V], const ExecArgs& a, int slot, const Tile& t) {
-  float* b = (float*)a.ptr[slot];
+  GAS float* b = (GAS float*)t.ptrs[slot];
   if (tile_mode<V, MODE>()) {
     const int64_t base = tile_base<V, MODE>(t);
-    if (FAST || t.vec) {
-      float* p = b + base;
+    if ((FAST || t.vec) && slot_vec(t, slot)) {
+      GAS float* p = b + base;
 #pragma unroll
       for (int k = 0; k < V / kV; ++k) {
-        *(float4*)(p + k * t.kstride) = make_float4(s[k * kV], s[k * kV + 1], s[k * kV + 2], s[k * kV + 3]);
-        *(float4*)(p + k * t.kstride + 4) =
-            make_float4(s[k * kV + 4], s[k * kV + 5], s[k * kV + 6], s[k * kV + 7]);
+        const f4 x = {s[k * kV], s[k * kV + 1], s[k * kV + 2], s[k * kV + 3]};
+        const f4 y = {s[k * kV + 4], s[k * kV + 5], s[k * kV + 6], s[k * kV + 7]};
+        *(GAS f4*)(p + k * t.kstride) = x;
+        *(GAS f4*)(p + k * t.kstride + 4) = y;
       }
+      return;
+    }
+    if (FAST || t.vec) {  // whole tile, element-aligned only
+      GAS float* p = b + base;
+#pragma unroll
+      for (int k = 0; k < V / kV; ++k)
+#pragma unroll
+        for (int i = 0; i < kV; ++i) p[k * t.kstride + i] = s[k * kV + i];
       return;
     }
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const bool on = t.valid && i < t.cnt;
-      pstore_b32(b + (on ? base + i : 0), __float_as_uint(s[i]), lanes(on));
+      pstore_b32((void*)(b + (on ? base + i : 0)), __float_as_uint(s[i]), lanes(on));
     }
     return;
   }
@@ -301,22 +353,31 @@ __device__ __forceinline__ void store_f32(const float (&s)[V], const ExecArgs& a
 
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void store_bf16(const float (&s)[V], const ExecArgs& a, int slot, const Tile& t) {
-  uint16_t* b = (uint16_t*)a.ptr[slot];
+  GAS uint16_t* b = (GAS uint16_t*)t.ptrs[slot];
   if (tile_mode<V, MODE>()) {
     const int64_t base = tile_base<V, MODE>(t);
-    if (FAST || t.vec) {
-      uint16_t* p = b + base;
+    if ((FAST || t.vec) && slot_vec(t, slot)) {
+      GAS uint16_t* p = b + base;
+#pragma unroll
+      for (int k = 0; k < V / kV; ++k) {
+        const u4 w = {pack_bf16(s[k * kV], s[k * kV + 1]), pack_bf16(s[k * kV + 2], s[k * kV + 3]),
+                      pack_bf16(s[k * kV + 4], s[k * kV + 5]), pack_bf16(s[k * kV + 6], s[k * kV + 7])};
+        *(GAS u4*)(p + k * t.kstride) = w;
+      }
+      return;
+    }
+    if (FAST || t.vec) {  // whole tile, element-aligned only
+      GAS uint16_t* p = b + base;
 #pragma unroll
       for (int k = 0; k < V / kV; ++k)
-        *(uint4*)(p + k * t.kstride) =
-            make_uint4(pack_bf16(s[k * kV], s[k * kV + 1]), pack_bf16(s[k * kV + 2], s[k * kV + 3]),
-                       pack_bf16(s[k * kV + 4], s[k * kV + 5]), pack_bf16(s[k * kV + 6], s[k * kV + 7]));
+#pragma unroll
+        for (int i = 0; i < kV; ++i) p[k * t.kstride + i] = (uint16_t)(pack_bf16(s[k * kV + i], 0.f) & 0xFFFFu);
       return;
     }
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const bool on = t.valid && i < t.cnt;
-      pstore_b16(b + (on ? base + i : 0), pack_bf16(s[i], 0.f) & 0xFFFFu, lanes(on));
+      pstore_b16((void*)(b + (on ? base + i : 0)), pack_bf16(s[i], 0.f) & 0xFFFFu, lanes(on));
     }
     return;
   }
@@ -583,18 +644,34 @@ exec_kernel(const ExecArgs a) {
   const Instr* row_prog = a.prog + a.n_col;
   const Instr* el_prog = a.prog + a.n_col + a.n_row;
   const int64_t erow_stride = a.R == 1 ? 0 : a.C;
-  const bool vec_ok = a.vec_ok != 0;
   const int ks = tpr * kV;  // elements between a lane's sub-tiles
   bool staged = false;
   float dummy = 0.f;
 
   for (int64_t item = blockIdx.x; item < a.n_items; item += gridDim.x) {
-    const int64_t rb = item / a.n_panels;
-    const int p = (int)(item - rb * a.n_panels);
-    const int64_t r0 = rb * a.RB;
-    const int nr = (int)min((int64_t)a.RB, a.R - r0);
-    const int64_t c0 = (int64_t)p * a.PW;
-    const int nc = (int)min((int64_t)a.PW, a.C - c0);
+    int64_t rb, r0, c0;
+    int p, nr, nc;
+    SlotPtr* ptrs = (SlotPtr*)a.ptr;
+    uint32_t vmask = a.vec_slots;
+    if (a.m_items != nullptr) {
+      // multi-set run of a flat group: this item's elements of its set
+      const MultiItem mi = a.m_items[item];
+      rb = 0;
+      p = 0;
+      r0 = 0;
+      nr = 1;
+      c0 = mi.off;
+      nc = mi.n;
+      ptrs = (SlotPtr*)(a.m_ptrs + (int64_t)mi.set * a.n_slots);
+      vmask = a.m_vec[mi.set];
+    } else {
+      rb = item / a.n_panels;
+      p = (int)(item - rb * a.n_panels);
+      r0 = rb * a.RB;
+      nr = (int)min((int64_t)a.RB, a.R - r0);
+      c0 = (int64_t)p * a.PW;
+      nc = (int)min((int64_t)a.PW, a.C - c0);
+    }
 
     const bool col_now = a.n_col > 0 && (a.n_panels > 1 || !staged);
     const bool row_now = a.n_row > 0;
@@ -610,14 +687,14 @@ exec_kernel(const ExecArgs a) {
       if (col_now) {
         for (int c = tid * kV; c < nc; c += kBlock * kV) {
           const int cnt = min(kV, nc - c);
-          Tile t{0, c0 + c, 0, c, 0, cnt, 0, true, vec_ok && cnt == kV};
+          Tile t{0, c0 + c, 0, c, 0, cnt, 0, true, cnt == kV, ptrs, vmask};
           interpret<kV, M_COL, false, NS>(a, col_prog, a.n_col, t, lds_col, lds_row, dummy, rb == 0);
         }
         staged = true;
       }
       if (row_now) {
         for (int r = kBlock - 1 - tid; r < nr; r += kBlock) {
-          Tile t{r0 + r, 0, 0, 0, r, 1, 0, false, false};
+          Tile t{r0 + r, 0, 0, 0, r, 1, 0, false, false, ptrs, vmask};
           interpret<1, M_ROW, false, NS>(a, row_prog, a.n_row, t, lds_col, lds_row, dummy, p == 0);
         }
       }
@@ -656,7 +733,7 @@ exec_kernel(const ExecArgs a) {
       const int rr = pass * rpp + sub;
       const int cl0 = (lt + s * K * tpr) * kV;
       const bool row_ok = rr < nr;
-      const bool whole = vec_ok && row_ok && cl0 + (K - 1) * ks + kV <= nc;
+      const bool whole = row_ok && cl0 + (K - 1) * ks + kV <= nc;
       // both branches are wave-uniform
       if (__all(whole)) {
         Tile t;
@@ -669,6 +746,8 @@ exec_kernel(const ExecArgs a) {
         t.rr = rr;
         t.cnt = kV;
         t.kstride = ks;
+        t.ptrs = ptrs;
+        t.vmask = vmask;
         interpret<K * kV, M_ELEM, true, NS>(a, el_prog, a.n_elem, t, lds_col, lds_row, acc, true);
       } else {
 #pragma unroll 1
@@ -684,8 +763,10 @@ exec_kernel(const ExecArgs a) {
           t.cl = cl;
           t.rr = rr;
           t.cnt = min(kV, nc - cl);
-          t.vec = vec_ok && valid && t.cnt == kV;
+          t.vec = valid && t.cnt == kV;
           t.kstride = ks;
+          t.ptrs = ptrs;
+          t.vmask = vmask;
           interpret<kV, M_ELEM, false, NS>(a, el_prog, a.n_elem, t, lds_col, lds_row, acc, true);
         }
       }
@@ -854,32 +935,61 @@ int hip_fail(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace {
+// As many workgroups as fit at once, spread so that every workgroup gets the
+// same number of items (the last round is not left half empty).
+int launch_exec(const ExecArgs& a, int lds_bytes, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  const int64_t resident = (int64_t)device_cus(dev) * exec_occupancy(dev, a.K, a.NS, lds_bytes);
+  const int64_t rounds = (a.n_items + resident - 1) / resident;
+  const int64_t grid = (a.n_items + rounds - 1) / rounds;
+  hipLaunchKernelGGL(exec_instance(a.K, a.NS), dim3((unsigned)grid), dim3(kBlock), lds_bytes, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "exec_kernel launch");
+  return GTF_OK;
+}
+}  // namespace
+
+int launch_multi(const CompiledGroup& cg, const void* ws, size_t off_ptrs, size_t off_vec,
+                 int64_t n_items, hipStream_t stream) {
+  if (n_items == 0) return GTF_OK;
+  ExecArgs a = cg.args;
+  a.n_items = n_items;
+  a.m_items = (const MultiItem*)ws;
+  a.m_ptrs = (void* const*)((const char*)ws + off_ptrs);
+  a.m_vec = (const uint32_t*)((const char*)ws + off_vec);
+  a.n_slots = cg.n_slots;
+  return launch_exec(a, cg.lds_bytes, stream);
+}
+
+int upload_bytes(void* dst, const void* src, size_t n, hipStream_t stream) {
+  if (n == 0) return GTF_OK;
+  hipError_t e = hipMemcpyAsync(dst, src, n, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "table upload");
+  return GTF_OK;
+}
+
 int launch_group(const CompiledGroup& cg, void* const* tensor_ptrs, hipStream_t stream) {
   ExecArgs a = cg.args;
   if (a.n_items == 0) return GTF_OK;
   if (a.C == 0 && a.reduce == 0) return GTF_OK;
-  bool vec = true;
+  // per slot: 16-byte accesses (u8: 8-byte) need an aligned pointer and,
+  // for [R,C] tensors of more than one row, rows a multiple of 8 elements
+  const bool rows8 = a.R <= 1 || (a.C % kV) == 0;
+  a.vec_slots = 0;
   for (int s = 0; s < cg.n_slots; ++s) {
     void* ptr = tensor_ptrs[cg.slot_tensor[s]];
     if (ptr == nullptr && cg.slot_numel[s] > 0)
       return fail(GTF_E_INVALID, "tensor " + std::to_string(cg.slot_tensor[s]) + " has no device pointer");
     a.ptr[s] = ptr;
-    if (((uintptr_t)ptr & 15) != 0) vec = false;
+    const uintptr_t align = cg.slot_dtype[s] == GTF_U8 ? 8 : 16;
+    const bool contiguous = a.cstride[s] == 1 && (a.rstride[s] == 0 || rows8);
+    if (contiguous && ((uintptr_t)ptr % align) == 0) a.vec_slots |= 1u << s;
   }
-  if (a.R > 1 && (a.C % kV) != 0) vec = false;
-  a.vec_ok = vec ? 1 : 0;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  // As many workgroups as fit at once, spread so that every workgroup gets
-  // the same number of items (the last round is not left half empty).
-  const int64_t resident = (int64_t)device_cus(dev) * exec_occupancy(dev, a.K, a.NS, cg.lds_bytes);
-  const int64_t rounds = (a.n_items + resident - 1) / resident;
-  const int64_t grid = (a.n_items + rounds - 1) / rounds;
-  hipLaunchKernelGGL(exec_instance(a.K, a.NS), dim3((unsigned)grid), dim3(kBlock), cg.lds_bytes, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "exec_kernel launch");
-  return GTF_OK;
+  a.m_items = nullptr;
+  return launch_exec(a, cg.lds_bytes, stream);
 }
 
 int launch_bucket(const BucketPlan& b, const void* const* tens, void* const* bk, float scale,

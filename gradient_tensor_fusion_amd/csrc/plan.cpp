@@ -778,6 +778,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   }
   cg.slot_tensor = slots;
   for (int t : slots) cg.slot_numel.push_back(p.tensors[t].R * p.tensors[t].C);
+  for (int t : slots) cg.slot_dtype.push_back(p.tensors[t].dtype);
   cg.n_slots = (int)slots.size();
   cg.max_depth = max_depth;
   cg.lds_bytes = (int)(a.n_col_slots * (int64_t)pw * 4 + a.n_row_slots * (int64_t)rb * 4 + 16 * 4);

@@ -32,6 +32,7 @@ struct CompiledGroup {
   ExecArgs args;                 // pointers filled per run
   std::vector<int> slot_tensor;  // external slot -> tensor id
   std::vector<int64_t> slot_numel;  // elements of each external tensor
+  std::vector<int> slot_dtype;      // GTF_F32 / GTF_BF16 / GTF_U8 of each
   int n_slots = 0;
   int lds_bytes = 0;
   int max_depth = 0;

@@ -211,6 +211,42 @@ int fuse_plan_run(const gtf_fuse_plan* plan, void* const* tensor_ptrs, void* hip
 
 void fuse_plan_destroy(gtf_fuse_plan* plan);
 
+/* ---- one launch over many tensor sets ---------------------------------
+ * Joint op and tensor fusion in one kernel (DisCo: op fusion and tensor
+ * fusion chosen together; tensor fusion sends many small tensors as one):
+ * group g of a plan, which must be flat (elementwise only: no broadcast
+ * operand and no reduction), runs over n_sets independent sets of tensors
+ * in a single launch.  Set s binds every tensor of the group to buffers of
+ * numel[s] elements of their own; the plan's shapes only fix the program,
+ * the dtypes and the roles.  Typical use: the elementwise epilogue of every
+ * parameter gradient of a model, each set's output bound to its bucket
+ * slot (bucket_plan_slot_address) with the 1/N average in the program, so
+ * the epilogue and the pack are one kernel.
+ * Errors: GTF_E_INVALID (NULL, bad g, n_sets < 0, numel < 0),
+ * GTF_E_UNSUPPORTED (the group is not flat). */
+typedef struct gtf_fuse_multi gtf_fuse_multi;
+int fuse_multi_create(const gtf_fuse_plan* plan, int32_t g, int32_t n_sets, const int64_t* numel,
+                      gtf_fuse_multi** out);
+
+/* Bytes of device workspace for the run's item table, pointer table and
+ * per-set alignment masks. */
+int fuse_multi_workspace_bytes(const gtf_fuse_multi* m, size_t* bytes);
+
+/* tensor_ptrs holds n_sets * n_tensors device pointers, set-major: entry
+ * s * n_tensors + t is set s's buffer for tensor id t (entries the group
+ * does not touch, and zero-size sets, may be NULL; any element alignment is
+ * accepted).  Copies the tables into dev_workspace (caller-owned, at least
+ * workspace_bytes, 16-byte aligned) asynchronously on the stream; runs read
+ * them there, so bind again when a pointer changes.
+ * Errors: GTF_E_INVALID (NULL, or a NULL pointer the group needs). */
+int fuse_multi_bind(gtf_fuse_multi* m, void* const* tensor_ptrs, void* dev_workspace,
+                    void* hip_stream);
+
+/* One launch on the stream.  Errors: GTF_E_STATE (not bound), GTF_E_HIP. */
+int fuse_multi_run(const gtf_fuse_multi* m, void* hip_stream);
+
+void fuse_multi_destroy(gtf_fuse_multi* m);
+
 /* ---- tensor-fusion buckets --------------------------------------------
  * Plan (host only): next-fit in the given (production) order: tensor i
  * joins the open bucket if bucket_bytes + bytes_i <= cap_bytes or the open
@@ -254,6 +290,20 @@ int bucket_unpack(const gtf_bucket_plan* plan, const void* const* buckets, void*
  * single-launch path is measured against. */
 int bucket_pack_per_tensor(const gtf_bucket_plan* plan, const void* const* src,
                            void* const* buckets, float scale, void* hip_stream);
+
+/* Joint op and tensor fusion (DisCo: op fusion and tensor fusion decided
+ * together; the fused tensor is the concatenation of its members).  *out =
+ * the device address of tensor i's place in its bucket, buckets[bucket_of[i]]
+ * + offset[i] elements.  A fused group whose output is gradient i can be run
+ * with that address as the output pointer and a final mul_imm(1/N) in its
+ * program: its stores then are the pack (x * scale in one fp32 multiply, as
+ * bucket_pack computes), and bucket_pack is not needed for tensor i.  The
+ * address is generally only 4-byte (bf16: 2-byte) aligned; the executor takes
+ * element-wide accesses for such a slot.  Host arithmetic only.
+ * Errors: GTF_E_INVALID (NULL plan, buckets or out; i out of range; NULL
+ * bucket pointer for a tensor of nonzero size). */
+int bucket_plan_slot_address(const gtf_bucket_plan* plan, void* const* buckets, int32_t i,
+                             void** out);
 
 void bucket_plan_destroy(gtf_bucket_plan* plan);
 

@@ -243,3 +243,51 @@ def test_bucket_plans_match_the_oracle():
         assert bp.query() == obucket.plan(numel, eb, cap)
         chunks = sum((n + 16383) // 16384 for n in numel)
         assert bp.workspace_bytes == 24 * chunks
+
+
+def test_bucket_slot_addresses_follow_the_oracle_offsets():
+    """bucket_plan_slot_address is base + offset * element size, with the
+    oracle's next-fit offsets (host arithmetic only: the bucket pointers
+    here are fake and never dereferenced)."""
+    for numel, dtype, eb in [(configs.c5_numel(), "f32", 4), (configs.c4_numel(), "bf16", 2),
+                             ([5, 0, 7, 3, 0], "f32", 4)]:
+        bp = gtf.BucketPlan(numel, dtype, configs.BUCKET_CAP_BYTES if len(numel) > 5 else 24)
+        bof, off, bn = obucket.plan(numel, eb, configs.BUCKET_CAP_BYTES if len(numel) > 5 else 24)
+        bases = [(k + 1) << 32 for k in range(len(bn))]
+        arr = C.ptr_array(bases)
+        for i in range(len(numel)):
+            out = ctypes.c_void_p()
+            assert C.lib().bucket_plan_slot_address(bp._h, arr, i, ctypes.byref(out)) == C.GTF_OK
+            assert out.value == bases[bof[i]] + off[i] * eb
+    bp = gtf.BucketPlan([4, 4], "f32", 16)
+    out = ctypes.c_void_p()
+    arr = C.ptr_array([1 << 32])
+    assert C.lib().bucket_plan_slot_address(bp._h, arr, 2, ctypes.byref(out)) == C.GTF_E_INVALID
+    assert C.lib().bucket_plan_slot_address(bp._h, None, 0, ctypes.byref(out)) == C.GTF_E_INVALID
+    assert C.lib().bucket_plan_slot_address(bp._h, C.ptr_array([None]), 0,
+                                            ctypes.byref(out)) == C.GTF_E_INVALID
+
+
+def test_multi_set_runs_on_the_host():
+    """fuse_multi_*: workspace sized from the items (one per panel of each
+    set), a group with a broadcast operand or a reduction refused, run
+    before bind refused, a missing pointer refused (no device work)."""
+    g = configs.grad_epilogue_graph(1000, avg=configs.AVG_SCALE)
+    plan = gtf.FusePlan(g)
+    pw = plan.geometry(0)["panel_width"]
+    numel = [1000, 0, 8192, 8193, 5, 123457]
+    m = gtf.FuseMulti(plan, 0, numel)
+    items = sum(-(-n // pw) for n in numel)
+    up = lambda x: -(-x // 16) * 16
+    nslots = 3
+    want = up(up(up(16 * items) + 8 * nslots * len(numel)) + 4 * len(numel))
+    assert m.workspace_bytes == want
+    assert C.lib().fuse_multi_run(m._h, None) == C.GTF_E_STATE
+    ptrs = C.ptr_array([None] * (len(g.tensors) * len(numel)))
+    assert C.lib().fuse_multi_bind(m._h, ptrs, ctypes.c_void_p(1 << 20), None) == C.GTF_E_INVALID
+    with pytest.raises(gtf.GtfError):
+        gtf.FuseMulti(gtf.FusePlan(configs.layernorm_graph(16, 64)), 0, [5])
+    with pytest.raises(gtf.GtfError):
+        gtf.FuseMulti(gtf.FusePlan(configs.c2_graph(4, 64)), 0, [5])
+    with pytest.raises(gtf.GtfError):
+        gtf.FuseMulti(plan, 0, [4, -1])

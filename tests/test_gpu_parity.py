@@ -387,3 +387,125 @@ def test_misaligned_views_take_the_scalar_path():
     torch.cuda.synchronize()
     _, want = oracle_run(g, ins)
     assert_bits_equal(to_host(dev[_out(g)], "bf16"), want[_out(g)])
+
+
+def test_joint_epilogue_stores_are_the_pack():
+    """Joint op and tensor fusion: each gradient's epilogue group ends in
+    mul_imm(1/N) and stores straight into its bucket slot (4-byte aligned
+    addresses, element-wide stores).  The buckets must equal, bit for bit,
+    the oracle's epilogue outputs placed at the oracle's offsets, and the
+    separate path (epilogue to a tensor, then bucket_pack with 1/N)."""
+    numel = [1000, 4096, 37, 65536, 5, 0, 8192, 3, 123457, 64, 1]
+    cap = 4 * 70000
+    bp = gtf.BucketPlan(numel, "f32", cap)
+    bof, off, bn = bp.query()
+    assert len(bn) >= 3
+    ws = torch.empty(max(16, bp.workspace_bytes), dtype=torch.uint8, device="cuda")
+    bp.bind(ws)
+    joint = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") for n in bn]
+    sep = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") for n in bn]
+    want = []
+    outs = []
+    for k, n in enumerate(numel):
+        gj = configs.grad_epilogue_graph(n, avg=configs.AVG_SCALE)
+        gs = configs.grad_epilogue_graph(n)
+        inp = configs.grad_epilogue_inputs(gj, k)
+        gi, wi = gj.inputs()
+        dev = {gi: to_device(inp[gi], "f32"), wi: to_device(inp[wi], "f32")}
+        pj = gtf.FusePlan(gj)
+        assert pj.num_groups == 1
+        pj.run({**dev, _out(gj): bp.slot_view(joint, k, (n,))})
+        ps = gtf.FusePlan(gs)
+        o = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+        ps.run({**dev, _out(gs): o})
+        outs.append(o)
+        want.append(np.asarray(oracle_run(gj, inp)[1][_out(gj)], dtype=np.float32).reshape(-1))
+    bp.pack(outs, sep, configs.AVG_SCALE)
+    torch.cuda.synchronize()
+    wb = obucket.pack(numel, 4, cap, want, 1.0)
+    for a, b, c in zip(joint, sep, wb):
+        a = a.cpu().numpy()
+        assert_bits_equal(a, c)
+        assert_bits_equal(b.cpu().numpy(), c)
+
+
+def test_joint_epilogue_graph_replays_match_eager():
+    """The joint launches captured once in a HIP graph (as bench.py times
+    them) and replayed three times, with eager work and synchronisations in
+    between: every replay's buckets equal the eager run's bit for bit."""
+    numel = [1000, 4096, 37, 65536, 5, 8192, 123457]
+    bp = gtf.BucketPlan(numel, "f32", 4 * 70000)
+    _, _, bn = bp.query()
+    ws = torch.empty(max(16, bp.workspace_bytes), dtype=torch.uint8, device="cuda")
+    bp.bind(ws)
+    torch.cuda.synchronize()
+    eager = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") for n in bn]
+    replay = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") for n in bn]
+    plans, feeds = [], []
+    for k, n in enumerate(numel):
+        g = configs.grad_epilogue_graph(n, avg=configs.AVG_SCALE)
+        inp = configs.grad_epilogue_inputs(g, k)
+        gi, wi = g.inputs()
+        feeds.append((g, {gi: to_device(inp[gi], "f32"), wi: to_device(inp[wi], "f32")}))
+        plans.append(gtf.FusePlan(g))
+    for k, ((g, dev), p) in enumerate(zip(feeds, plans)):
+        p.run({**dev, _out(g): bp.slot_view(eager, k, (numel[k],))})
+    torch.cuda.synchronize()
+    want = [e.cpu().numpy() for e in eager]
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for k, ((g, dev), p) in enumerate(zip(feeds, plans)):
+            p.run({**dev, _out(g): bp.slot_view(replay, k, (numel[k],))})
+    for _ in range(3):
+        for r in replay:
+            r.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(replay, want):
+            assert_bits_equal(a.cpu().numpy(), b)
+
+
+def test_joint_epilogue_in_one_launch():
+    """fuse_multi_run: one launch runs every gradient's epilogue (sets of
+    sizes from 0 to 123457, misaligned bucket slots) and its stores are the
+    pack: the buckets equal the oracle's epilogue outputs at the oracle's
+    offsets, bit for bit, eagerly and on three HIP-graph replays."""
+    numel = [1000, 4096, 37, 65536, 5, 0, 8192, 3, 123457, 64, 1, 8193]
+    cap = 4 * 70000
+    bp = gtf.BucketPlan(numel, "f32", cap)
+    _, _, bn = bp.query()
+    bws = torch.empty(max(16, bp.workspace_bytes), dtype=torch.uint8, device="cuda")
+    bp.bind(bws)
+    g = configs.grad_epilogue_graph(1000, avg=configs.AVG_SCALE)
+    gi, wi = g.inputs()
+    plan = gtf.FusePlan(g)
+    multi = gtf.FuseMulti(plan, 0, numel)
+    buckets = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") for n in bn]
+    sets, want = [], []
+    for k, n in enumerate(numel):
+        gk = configs.grad_epilogue_graph(n, avg=configs.AVG_SCALE)
+        inp = configs.grad_epilogue_inputs(gk, k)
+        sets.append({gi: to_device(inp[gk.inputs()[0]], "f32"), wi: to_device(inp[gk.inputs()[1]], "f32"),
+                     _out(g): bp.slot_view(buckets, k, (n,))})
+        want.append(np.asarray(oracle_run(gk, inp)[1][_out(gk)], dtype=np.float32).reshape(-1))
+    mws = torch.empty(max(16, multi.workspace_bytes), dtype=torch.uint8, device="cuda")
+    multi.bind(sets, mws)
+    multi.run()
+    torch.cuda.synchronize()
+    wb = obucket.pack(numel, 4, cap, want, 1.0)
+    for a, b in zip(buckets, wb):
+        assert_bits_equal(a.cpu().numpy(), b)
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        multi.run()
+    for _ in range(3):
+        for b in buckets:
+            b.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(buckets, wb):
+            assert_bits_equal(a.cpu().numpy(), b)

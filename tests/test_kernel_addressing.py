@@ -7,8 +7,9 @@ The replay restates the element loop of the executor kernel: items are
 (row block, column panel); 256 threads split into rows of threads_per_row
 (tpr) lanes; a lane's tiles are runs of K sub-tiles of 8 elements, tpr * 8
 elements apart in its row.  A run whose K sub-tiles are whole in all 64
-lanes of a wave is read with 16-byte loads at once; otherwise each sub-tile
-is handled on its own, partial ones element by element."""
+lanes of a wave goes to the whole-tile interpreter at once (16-byte accesses
+for tensors aligned for them, else one access per element); otherwise each
+sub-tile is handled on its own, partial ones element by element."""
 import numpy as np
 import pytest
 
@@ -48,7 +49,7 @@ def replay(graph, plan, g):
             ps, s = divmod(q, spl)
             rr = ps * rpp + sub
             cl0 = (lt + s * K * tpr) * KV
-            whole = vec_ok & (rr < nr) & (cl0 + (K - 1) * ks + KV <= nc)
+            whole = (rr < nr) & (cl0 + (K - 1) * ks + KV <= nc)
             fast = np.repeat(whole.reshape(-1, WAVE).all(axis=1), WAVE)
             for k in range(K):
                 cl = cl0 + k * ks
@@ -58,8 +59,10 @@ def replay(graph, plan, g):
                 on = valid | fast
                 assert np.all(fast <= valid)
                 assert np.all(first[on] >= 0) and np.all(first[on] + cnt[on] <= numel), (item, q, k)
-                # whole sub-tiles are 16-byte loads: 8 elements from first
-                assert np.all(first[fast] % KV == 0)
+                # whole sub-tiles of tensors whose rows are a multiple of 8
+                # take 16-byte accesses: they start on a multiple of 8
+                if vec_ok:
+                    assert np.all(first[fast] % KV == 0)
                 seen.append((r0 + rr)[on] * (C // KV + 1) + (c0 + cl)[on] // KV)
     want = R * sum(-(-min(PW, C - p * PW) // KV) for p in range(panels)) if C > 0 else 0
     ids = np.concatenate(seen) if seen else np.zeros(0, dtype=np.int64)

@@ -97,3 +97,28 @@ def test_pack_places_each_tensor_at_its_offset():
     assert bks[0].tolist() == [0, 1, 2, 10, 11, 12, 13, 14]
     assert bks[1].tolist() == [20, 21]
     assert bks[2].tolist() == list(range(30, 37))
+
+
+def test_joint_epilogue_equals_separate_pack():
+    """Folding the 1/N average into a gradient epilogue (joint op and tensor
+    fusion) gives the same bucket bits as running the epilogue and packing
+    with scale 1/N: scaling by a power of two is exact for normal values,
+    so the one multiply lands on the same float either way."""
+    from oracle import evaluate as oev
+    numel = [1000, 37, 4096, 5, 0, 333]
+    joint, sep = [], []
+    for k, n in enumerate(numel):
+        gj = configs.grad_epilogue_graph(n, avg=configs.AVG_SCALE)
+        gs = configs.grad_epilogue_graph(n)
+        inp = configs.grad_epilogue_inputs(gj, k)
+        oj = oev.outputs(gj, oev.evaluate(gj, inp))[gj.outputs()[0]]
+        # same input ids in both graphs: g and w are the first two tensors
+        os_ = oev.outputs(gs, oev.evaluate(gs, inp))[gs.outputs()[0]]
+        joint.append(np.asarray(oj, dtype=np.float32).reshape(-1))
+        sep.append(np.asarray(os_, dtype=np.float32).reshape(-1))
+        assert np.all(np.abs(sep[-1][sep[-1] != 0]) > 1e-30)
+    cap = 4 * 2048
+    a = bucket.pack(numel, 4, cap, joint, 1.0)
+    b = bucket.pack(numel, 4, cap, sep, configs.AVG_SCALE)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))

@@ -14,6 +14,11 @@ c5  12 layers of Transformer-block groups over 8192 tokens x 1024 hidden:
         LayerNorm (mean, variance, normalise), bias + GELU on [8192,4096],
         dropout (keep 0.9) + residual; plus 194 fp32 gradient tensors.
 
+joint  op and tensor fusion together: each of c5's 194 parameter gradients
+       goes through an elementwise epilogue g' = g * (1/loss_scale) + wd * w
+       (loss-scale removal and weight decay), and the epilogue's store puts
+       g' * (1/N) straight into the gradient's bucket slot.
+
 Every builder takes the sizes as arguments so tests can run the same graph
 at small shapes.
 """
@@ -186,6 +191,38 @@ def dropout_inputs(g: Graph, seed: int, p: float = DROP_P) -> Dict[int, np.ndarr
 
 def c5_layer_seed(layer: int) -> int:
     return 5000 + layer
+
+
+LOSS_SCALE_INV = 1.0 / 1024.0  # exact in fp32
+WEIGHT_DECAY = 0.01
+JOINT_SEED = 5200
+
+
+def grad_epilogue_graph(n: int, avg=None, inv_scale: float = LOSS_SCALE_INV,
+                        wd: float = WEIGHT_DECAY) -> Graph:
+    """g' = g * inv_scale + wd * w over one fp32 gradient of n elements;
+    with avg, the output is g' * avg (the data-parallel average folded into
+    the epilogue, whose output then lives in a bucket slot)."""
+    g = Graph()
+    gr = g.input("g", "f32", (n,))
+    w = g.input("w", "f32", (n,))
+    a = g.op("mul_imm", [gr], "g_unscaled", "f32", (n,), imm=inv_scale)
+    b = g.op("mul_imm", [w], "decay", "f32", (n,), imm=wd)
+    if avg is None:
+        g.op("add", [a, b], "g_out", "f32", (n,), role="out")
+    else:
+        c = g.op("add", [a, b], "g_sum", "f32", (n,))
+        g.op("mul_imm", [c], "g_avg", "f32", (n,), role="out", imm=avg)
+    return g
+
+
+def grad_epilogue_inputs(g: Graph, index: int, seed: int = JOINT_SEED) -> Dict[int, np.ndarray]:
+    """Loss-scaled gradient ~ N(0, 1) and weights ~ N(0, 0.02), two streams
+    per tensor index."""
+    gr, w = g.inputs()
+    n = int(np.prod(g.tensors[gr].shape))
+    return {gr: _f32(rng.normal(seed, 2 * index, n, 0.0, 1.0)),
+            w: _f32(rng.normal(seed, 2 * index + 1, n, 0.0, 0.02))}
 
 
 # ---------------------------------------------------------------- buckets
