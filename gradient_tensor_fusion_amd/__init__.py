@@ -58,13 +58,14 @@ def _program_desc(graph):
 class FusePlan:
     """fuse_plan_create and friends."""
 
-    def __init__(self, graph, fuse: bool = True):
+    def __init__(self, graph, fuse: bool = True, row_resident: bool = False):
         self.graph = graph
         self.n_tensors = len(graph.tensors)
         self.n_ops = len(graph.ops)
         desc, self._tens, self._ops = _program_desc(graph)
         h = c_void_p()
-        C.check(C.lib().fuse_plan_create(byref(desc), 0 if fuse else C.NO_FUSE, byref(h)))
+        flags = (0 if fuse else C.NO_FUSE) | (C.ROW_RESIDENT if row_resident else 0)
+        C.check(C.lib().fuse_plan_create(byref(desc), flags, byref(h)))
         self._h = h
 
     def __del__(self):

@@ -30,6 +30,7 @@ OPCODE = {
 }
 OPF_OPAQUE = 1
 NO_FUSE = 1
+ROW_RESIDENT = 2
 
 EXPORTED = (
     "fuse_plan_create", "fuse_plan_num_groups", "fuse_plan_group_info", "fuse_plan_op_info",
@@ -57,7 +58,8 @@ class GroupGeometry(ctypes.Structure):
     _fields_ = [("rows", c_int64), ("cols", c_int64), ("items", c_int64), ("panels", c_int32),
                 ("rows_per_item", c_int32), ("panel_width", c_int32), ("threads_per_row", c_int32),
                 ("subtiles", c_int32), ("lds_bytes", c_int32), ("program_length", c_int32),
-                ("spill_slots", c_int32), ("spill_slots_max", c_int32), ("reduce", c_int32)]
+                ("spill_slots", c_int32), ("spill_slots_max", c_int32), ("reduce", c_int32),
+                ("stages", c_int32), ("reserved", c_int32)]
 
 
 class ProgramDesc(ctypes.Structure):

@@ -169,11 +169,12 @@ const char* gtf_last_error(void) { return g_last_error.c_str(); }
 int fuse_plan_create(const gtf_program_desc* desc, uint32_t flags, gtf_fuse_plan** out) {
   if (out == nullptr) return fail(GTF_E_INVALID, "out is NULL");
   *out = nullptr;
-  if (flags & ~GTF_NO_FUSE) return fail(GTF_E_INVALID, "unknown flags");
+  if (flags & ~(GTF_NO_FUSE | GTF_ROW_RESIDENT)) return fail(GTF_E_INVALID, "unknown flags");
   gtf_fuse_plan* h = new (std::nothrow) gtf_fuse_plan();
   if (h == nullptr) return fail(GTF_E_LIMIT, "out of host memory");
   int st = validate(desc, &h->p);
-  if (st == GTF_OK) st = build_fuse_plan(&h->p, (flags & GTF_NO_FUSE) == 0);
+  if (st == GTF_OK)
+    st = build_fuse_plan(&h->p, (flags & GTF_NO_FUSE) == 0, (flags & GTF_ROW_RESIDENT) != 0);
   if (st != GTF_OK) {
     delete h;
     return st;
@@ -225,10 +226,13 @@ int fuse_plan_group_geometry(const gtf_fuse_plan* plan, int32_t g, gtf_group_geo
   out->threads_per_row = 1 << a.tpr_log2;
   out->subtiles = a.K;
   out->lds_bytes = cg.lds_bytes;
-  out->program_length = a.n_col + a.n_row + a.n_elem;
+  out->program_length = a.stage[a.n_stages - 1].el_off + a.stage[a.n_stages - 1].el_len;
   out->spill_slots = cg.max_depth;
   out->spill_slots_max = a.NS;
-  out->reduce = a.reduce;
+  out->reduce = 0;
+  for (int st = 0; st < a.n_stages; ++st)
+    if (a.stage[st].red) out->reduce = a.stage[st].red;
+  out->stages = a.n_stages;
   return GTF_OK;
 }
 
@@ -365,7 +369,7 @@ int fuse_multi_create(const gtf_fuse_plan* plan, int32_t g, int32_t n_sets, cons
   if (n_sets < 0) return fail(GTF_E_INVALID, "n_sets < 0");
   const CompiledGroup& cg = plan->p.groups[g].code;
   const ExecArgs& a = cg.args;
-  if (a.R > 1 || a.n_col > 0 || a.n_row > 0 || a.reduce != 0)
+  if (a.R > 1 || a.n_col > 0 || a.n_stages != 1 || a.stage[0].row_len > 0 || a.stage[0].red != 0)
     return fail(GTF_E_UNSUPPORTED, "group is not flat (broadcast operand or reduction)");
   for (int32_t s = 0; s < n_sets; ++s)
     if (numel[s] < 0) return fail(GTF_E_INVALID, "numel < 0");

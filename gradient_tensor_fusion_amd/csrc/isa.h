@@ -9,7 +9,11 @@
 //   column phase  once per column of the staged panel (values shaped [1,C]);
 //                 results go to LDS column slots.
 //   row phase     once per row of the row block (values shaped [R,1]);
-//                 results go to LDS row slots.
+//                 results go to LDS row slots.  A group may hold up to
+//                 kMaxStages element stages, each ending in a row
+//                 reduction whose result later stages read (row-resident
+//                 reduce-then-broadcast, e.g. a one-kernel LayerNorm); a
+//                 row program runs before each stage.
 //   element phase once per tile of one row; reads rows/columns from LDS,
 //                 streams [R,C] tensors.  A lane's tile is K sub-tiles of
 //                 kV consecutive elements, tpr * kV elements apart in the
@@ -40,6 +44,7 @@ constexpr int kMaxLdsCol = 4;    // LDS column slots
 constexpr int kMaxLdsRow = 8;    // LDS row slots
 constexpr int kBlock = 256;      // threads per workgroup
 constexpr int kPanelMax = 4096;  // widest column panel staged in LDS
+constexpr int kMaxStages = 4;    // element stages of one group (row-resident reductions)
 
 enum Form : int {
   // load a tile of external tensor slot `arg` into A / into B
@@ -89,6 +94,20 @@ struct MultiItem {
   int32_t set;
 };
 
+// One element stage: the row program that runs before it, its element
+// program, and the row reduction it ends in (if any), whose per-row result
+// goes to an LDS row slot (read by later stages and row programs) and/or
+// to an external slot.  A group without row-resident reductions has one
+// stage.
+struct StageDesc {
+  int32_t row_off, row_len;  // row program (instruction offset, length)
+  int32_t el_off, el_len;    // element program
+  int32_t red;               // 0 none, 1 row sum, 2 row mean
+  int32_t red_lds;           // LDS row slot for the result, or -1
+  int32_t red_slot;          // external slot for the result, or -1
+  int32_t red_dtype;         // its dtype
+};
+
 // Kernel arguments, passed by value (kernarg segment; read with scalar
 // loads).  Strides are in elements.
 struct ExecArgs {
@@ -96,11 +115,10 @@ struct ExecArgs {
   int64_t n_items;         // row blocks x panels
   int32_t n_panels, RB, PW;    // panels, rows per block, panel width
   int32_t tpr_log2;        // threads per row = 1 << tpr_log2 (<= kBlock)
-  int32_t n_col, n_row, n_elem;  // program lengths (programs back to back)
+  int32_t n_col;           // column program length (at offset 0)
+  int32_t n_stages;        // element stages (>= 1)
+  StageDesc stage[kMaxStages];
   int32_t n_col_slots, n_row_slots;
-  int32_t reduce;          // 0 none, 1 sum, 2 mean
-  int32_t red_dtype;       // reduce output dtype
-  int32_t red_slot;        // external slot of the reduce output
   uint32_t vec_slots;      // bit s: slot s takes 16-byte (u8: 8-byte) accesses
   int32_t K;               // sub-tiles per lane tile: kWideK (wide) or 1 (narrow)
   int32_t NS;              // spill slots of the instance: 0, kWideNS or kNS

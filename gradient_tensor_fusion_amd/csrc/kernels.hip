@@ -510,10 +510,10 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
       case F_LD_BF16_B: load_bf16<V, MODE, FAST>(B, a, arg, t); break;
       case F_LD_U8_B: load_u8<V, MODE, FAST>(B, a, arg, t); break;
       case F_COL_A: if (MODE == M_ELEM) lds_vec<V>(A, col, t.kstride); break;
-      case F_ROW_A: if (MODE == M_ELEM) fill<V>(A, lds_row[arg * a.RB + t.rr]); break;
+      case F_ROW_A: if (MODE != M_COL) fill<V>(A, lds_row[arg * a.RB + t.rr]); break;
       case F_IMM_A: fill<V>(A, cur.imm); break;
       case F_COL_B: if (MODE == M_ELEM) lds_vec<V>(B, col, t.kstride); break;
-      case F_ROW_B: if (MODE == M_ELEM) fill<V>(B, lds_row[arg * a.RB + t.rr]); break;
+      case F_ROW_B: if (MODE != M_COL) fill<V>(B, lds_row[arg * a.RB + t.rr]); break;
       case F_IMM_B: fill<V>(B, cur.imm); break;
       case F_A2B: copy<V>(B, A); break;
       case F_B2A: copy<V>(A, B); break;
@@ -536,7 +536,7 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
 #define GTF_BIN(NAME, OP)                                                               \
   case F_##NAME: binop<V, OP>(A, B); break;                                             \
   case F_##NAME##_C: if (MODE == M_ELEM) xvec<V, OP>(A, col, t.kstride); break;         \
-  case F_##NAME##_R: if (MODE == M_ELEM) xscalar<V, OP>(A, lds_row[arg * a.RB + t.rr]); break; \
+  case F_##NAME##_R: if (MODE != M_COL) xscalar<V, OP>(A, lds_row[arg * a.RB + t.rr]); break; \
   case F_##NAME##_I: xscalar<V, OP>(A, cur.imm); break;
       GTF_BIN(ADD, X_ADD)
       GTF_BIN(SUB, X_SUB)
@@ -607,14 +607,18 @@ __device__ __forceinline__ float segment_sum(float v, int width) {
   return v;
 }
 
-// Row result of the reduce tail, written by the lanes in `on` (one lane per
-// row) with a predicated store.
-__device__ __forceinline__ void store_reduced(const ExecArgs& a, int64_t row, float s, bool on) {
-  const float v = a.reduce == 2 ? s / (float)a.C : s;
-  const int slot = a.red_slot;
+// Row result of a stage's reduce tail, for the lanes in `on` (one lane per
+// row): to the stage's LDS row slot, where later stages and row programs
+// read it, and/or with a predicated store to its external slot.
+__device__ __forceinline__ void store_reduced(const ExecArgs& a, const StageDesc& S, float* lds_row,
+                                              int64_t row, int rr, float s, bool on) {
+  const float v = S.red == 2 ? s / (float)a.C : s;
+  if (S.red_lds >= 0 && on) lds_row[S.red_lds * a.RB + rr] = v;
+  if (S.red_slot < 0) return;
+  const int slot = S.red_slot;
   const int64_t off = on ? row * a.rstride[slot] : 0;
   const uint64_t m = lanes(on);
-  if (a.red_dtype == DT_BF16)
+  if (S.red_dtype == DT_BF16)
     pstore_b16((uint16_t*)a.ptr[slot] + off, pack_bf16(v, 0.f) & 0xFFFFu, m);
   else
     pstore_b32((float*)a.ptr[slot] + off, __float_as_uint(v), m);
@@ -628,6 +632,8 @@ __device__ __forceinline__ void store_reduced(const ExecArgs& a, int64_t row, fl
 // are whole in every lane of the wave goes to the FAST instance at once;
 // any other run goes sub-tile by sub-tile to the partial instance.  Either
 // way each lane adds its elements to the row accumulator in the same order.
+// A group with row-resident reductions walks the item once per stage,
+// with a row program (and barriers) between stages.
 template <int K, int NS>
 __global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NS == 0 ? 4 : 3)))
 exec_kernel(const ExecArgs a) {
@@ -641,8 +647,6 @@ exec_kernel(const ExecArgs a) {
   const int sub = tid >> a.tpr_log2;
   const int lt = tid & (tpr - 1);
   const Instr* col_prog = a.prog;
-  const Instr* row_prog = a.prog + a.n_col;
-  const Instr* el_prog = a.prog + a.n_col + a.n_row;
   const int64_t erow_stride = a.R == 1 ? 0 : a.C;
   const int ks = tpr * kV;  // elements between a lane's sub-tiles
   bool staged = false;
@@ -674,104 +678,119 @@ exec_kernel(const ExecArgs a) {
     }
 
     const bool col_now = a.n_col > 0 && (a.n_panels > 1 || !staged);
-    const bool row_now = a.n_row > 0;
     const int npass = (nr + rpp - 1) / rpp;
     const int tpl = max(1, (nc + ks - 1) / ks);  // sub-tiles per lane per row
     const int spl = (tpl + K - 1) / K;           // runs of K per lane per row
     const int nq = npass * spl;
-    // Column phase (kV consecutive columns per thread per pass, from thread
-    // 0 up) and row phase (one row per thread, from the last thread down)
-    // share one barrier pair, so their loads overlap too.
-    if (col_now || row_now) {
-      __syncthreads();
-      if (col_now) {
-        for (int c = tid * kV; c < nc; c += kBlock * kV) {
-          const int cnt = min(kV, nc - c);
-          Tile t{0, c0 + c, 0, c, 0, cnt, 0, true, cnt == kV, ptrs, vmask};
-          interpret<kV, M_COL, false, NS>(a, col_prog, a.n_col, t, lds_col, lds_row, dummy, rb == 0);
-        }
-        staged = true;
-      }
-      if (row_now) {
-        for (int r = kBlock - 1 - tid; r < nr; r += kBlock) {
-          Tile t{r0 + r, 0, 0, 0, r, 1, 0, false, false, ptrs, vmask};
-          interpret<1, M_ROW, false, NS>(a, row_prog, a.n_row, t, lds_col, lds_row, dummy, p == 0);
-        }
-      }
-      __syncthreads();
-    }
+    // later stages write LDS row slots that the previous item's last stage
+    // may still be reading
+    if (a.n_stages > 1) __syncthreads();
 
-    float acc = 0.f;
-    int pass = 0, s = 0;
-    // reduce tail after the last run of a row, then advance (pass, s)
-    auto finish = [&](int rr) {
-      if (a.reduce && s == spl - 1) {
-        const int w = min(tpr, 64);
-        float sum = segment_sum(acc, w);
-        acc = 0.f;
-        if (tpr <= 64) {
-          store_reduced(a, r0 + rr, sum, lt == 0 && rr < nr);
-        } else {
-          // rows wider than a wave: combine the per-wave sums through LDS in
-          // a fixed order (every lane of a wave holds the same sum and
-          // writes it; every lane reads the totals of its own row)
-          const int wpr = tpr >> 6;  // waves per row
-          lds_red[tid >> 6] = sum;
-          __syncthreads();
-          float tot = 0.f;
-          for (int k = 0; k < wpr; ++k) tot += lds_red[sub * wpr + k];
-          store_reduced(a, r0 + rr, tot, lt == 0 && rr < nr);
-          __syncthreads();
+    // one walk of the item per stage
+    auto run_stage = [&](const int st) __attribute__((always_inline)) {
+      const StageDesc& S = a.stage[st];
+      const bool row_now = S.row_len > 0;
+      // Column phase (kV consecutive columns per thread per pass, from
+      // thread 0 up, once) and the stage's row program (one row per thread,
+      // from the last thread down) share one barrier pair, so their loads
+      // overlap too.  A later stage always starts behind a barrier: its
+      // row program and element program read the previous stage's results.
+      if ((st == 0 && col_now) || row_now || st > 0) {
+        __syncthreads();
+        if (st == 0 && col_now) {
+          for (int c = tid * kV; c < nc; c += kBlock * kV) {
+            const int cnt = min(kV, nc - c);
+            Tile t{0, c0 + c, 0, c, 0, cnt, 0, true, cnt == kV, ptrs, vmask};
+            interpret<kV, M_COL, false, NS>(a, col_prog, a.n_col, t, lds_col, lds_row, dummy, rb == 0);
+          }
+          staged = true;
         }
+        if (row_now) {
+          for (int r = kBlock - 1 - tid; r < nr; r += kBlock) {
+            Tile t{r0 + r, 0, 0, 0, r, 1, 0, false, false, ptrs, vmask};
+            interpret<1, M_ROW, false, NS>(a, a.prog + S.row_off, S.row_len, t, lds_col, lds_row,
+                                           dummy, p == 0);
+          }
+        }
+        __syncthreads();
       }
-      if (++s == spl) {
-        s = 0;
-        ++pass;
-      }
-    };
-    for (int q = 0; q < nq; ++q) {
-      const int rr = pass * rpp + sub;
-      const int cl0 = (lt + s * K * tpr) * kV;
-      const bool row_ok = rr < nr;
-      const bool whole = row_ok && cl0 + (K - 1) * ks + kV <= nc;
-      // both branches are wave-uniform
-      if (__all(whole)) {
-        Tile t;
-        t.valid = true;
-        t.vec = true;
-        t.row = r0 + rr;
-        t.col = c0 + cl0;
-        t.eoff = t.row * erow_stride + t.col;
-        t.cl = cl0;
-        t.rr = rr;
-        t.cnt = kV;
-        t.kstride = ks;
-        t.ptrs = ptrs;
-        t.vmask = vmask;
-        interpret<K * kV, M_ELEM, true, NS>(a, el_prog, a.n_elem, t, lds_col, lds_row, acc, true);
-      } else {
-#pragma unroll 1
-        for (int k = 0; k < K; ++k) {
-          const int cl = cl0 + k * ks;
-          const bool valid = row_ok && cl < nc;
-          if (!__any(valid)) continue;
+      const Instr* el_prog = a.prog + S.el_off;
+      const int n_el = S.el_len;
+      if (n_el == 0) return;
+
+      float acc = 0.f;
+      int pass = 0, s = 0;
+      // reduce tail after the last run of a row, then advance (pass, s)
+      auto finish = [&](int rr) {
+        if (S.red && s == spl - 1) {
+          const int w = min(tpr, 64);
+          float sum = segment_sum(acc, w);
+          acc = 0.f;
+          if (tpr <= 64) {
+            store_reduced(a, S, lds_row, r0 + rr, rr, sum, lt == 0 && rr < nr);
+          } else {
+            // rows wider than a wave: combine the per-wave sums through LDS
+            // in a fixed order (every lane of a wave holds the same sum and
+            // writes it; every lane reads the totals of its own row)
+            const int wpr = tpr >> 6;  // waves per row
+            lds_red[tid >> 6] = sum;
+            __syncthreads();
+            float tot = 0.f;
+            for (int k = 0; k < wpr; ++k) tot += lds_red[sub * wpr + k];
+            store_reduced(a, S, lds_row, r0 + rr, rr, tot, lt == 0 && rr < nr);
+            __syncthreads();
+          }
+        }
+        if (++s == spl) {
+          s = 0;
+          ++pass;
+        }
+      };
+      for (int q = 0; q < nq; ++q) {
+        const int rr = pass * rpp + sub;
+        const int cl0 = (lt + s * K * tpr) * kV;
+        const bool row_ok = rr < nr;
+        const bool whole = row_ok && cl0 + (K - 1) * ks + kV <= nc;
+        // both branches are wave-uniform
+        if (__all(whole)) {
           Tile t;
-          t.valid = valid;
+          t.valid = true;
+          t.vec = true;
           t.row = r0 + rr;
-          t.col = c0 + cl;
+          t.col = c0 + cl0;
           t.eoff = t.row * erow_stride + t.col;
-          t.cl = cl;
+          t.cl = cl0;
           t.rr = rr;
-          t.cnt = min(kV, nc - cl);
-          t.vec = valid && t.cnt == kV;
+          t.cnt = kV;
           t.kstride = ks;
           t.ptrs = ptrs;
           t.vmask = vmask;
-          interpret<kV, M_ELEM, false, NS>(a, el_prog, a.n_elem, t, lds_col, lds_row, acc, true);
+          interpret<K * kV, M_ELEM, true, NS>(a, el_prog, n_el, t, lds_col, lds_row, acc, true);
+        } else {
+#pragma unroll 1
+          for (int k = 0; k < K; ++k) {
+            const int cl = cl0 + k * ks;
+            const bool valid = row_ok && cl < nc;
+            if (!__any(valid)) continue;
+            Tile t;
+            t.valid = valid;
+            t.row = r0 + rr;
+            t.col = c0 + cl;
+            t.eoff = t.row * erow_stride + t.col;
+            t.cl = cl;
+            t.rr = rr;
+            t.cnt = min(kV, nc - cl);
+            t.vec = valid && t.cnt == kV;
+            t.kstride = ks;
+            t.ptrs = ptrs;
+            t.vmask = vmask;
+            interpret<kV, M_ELEM, false, NS>(a, el_prog, n_el, t, lds_col, lds_row, acc, true);
+          }
         }
+        finish(rr);
       }
-      finish(rr);
-    }
+    };
+    for (int st = 0; st < a.n_stages; ++st) run_stage(st);
   }
 }
 
@@ -974,7 +993,10 @@ int upload_bytes(void* dst, const void* src, size_t n, hipStream_t stream) {
 int launch_group(const CompiledGroup& cg, void* const* tensor_ptrs, hipStream_t stream) {
   ExecArgs a = cg.args;
   if (a.n_items == 0) return GTF_OK;
-  if (a.C == 0 && a.reduce == 0) return GTF_OK;
+  bool any_reduce = false;
+  for (int st = 0; st < a.n_stages; ++st)
+    if (a.stage[st].red) any_reduce = true;
+  if (a.C == 0 && !any_reduce) return GTF_OK;
   // per slot: 16-byte accesses (u8: 8-byte) need an aligned pointer and,
   // for [R,C] tensors of more than one row, rows a multiple of 8 elements
   const bool rows8 = a.R <= 1 || (a.C % kV) == 0;

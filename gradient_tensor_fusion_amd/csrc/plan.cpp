@@ -353,6 +353,53 @@ struct Codegen {
 
 }  // namespace
 
+// Every index a compiled program hands the executor, checked against what
+// the launch provides: external slots, LDS slots, spill slots of the
+// instance and the phase each form may appear in.  A failure here is a
+// compiler bug, reported before anything is launched.
+const char* check_program(const ExecArgs& a, int n_slots) {
+  if (a.n_stages < 1 || a.n_stages > kMaxStages) return "stage count out of range";
+  if (a.n_col < 0 || a.n_col > kMaxInstr) return "column program out of range";
+  if (a.n_col_slots < 0 || a.n_col_slots > kMaxLdsCol) return "column slots out of range";
+  if (a.n_row_slots < 0 || a.n_row_slots > kMaxLdsRow) return "row slots out of range";
+  if (n_slots < 0 || n_slots > kMaxSlots) return "slot count out of range";
+  if (a.RB < 1 || (a.RB << a.tpr_log2) != kBlock) return "row block does not fill the workgroup";
+  const int ns = a.NS;
+  auto check = [&](int off, int len, int phase) -> const char* {
+    // phase 0 column, 1 row, 2 element
+    if (off < 0 || len < 0 || off + len > kMaxInstr) return "program out of the buffer";
+    for (int i = off; i < off + len; ++i) {
+      const int f = a.prog[i].code, arg = a.prog[i].arg;
+      if (f < 0 || f >= F_COUNT) return "unknown form";
+      if (f <= F_LD_U8_B || f == F_ST_F32 || f == F_ST_BF16) {
+        if (arg >= n_slots) return "external slot out of range";
+      } else if (f == F_COL_A || f == F_COL_B || (f >= F_ADD_C && f <= F_MIN_C)) {
+        if (phase == 0 || arg >= a.n_col_slots) return "LDS column slot out of range";
+      } else if (f == F_ROW_A || f == F_ROW_B || (f >= F_ADD_R && f <= F_MIN_R)) {
+        if (phase == 0 || arg >= a.n_row_slots) return "LDS row slot out of range";
+      } else if (f == F_ST_LDS) {
+        if (phase == 2 || arg >= (phase == 0 ? a.n_col_slots : a.n_row_slots))
+          return "LDS store out of range";
+      } else if (f == F_RED) {
+        if (phase != 2) return "reduction outside the element phase";
+      } else if (f >= F_A2S0 && f <= F_S52B) {
+        if ((f - F_A2S0) % kNS >= ns) return "spill slot beyond the instance";
+      }
+    }
+    return nullptr;
+  };
+  if (const char* e = check(0, a.n_col, 0)) return e;
+  for (int st = 0; st < a.n_stages; ++st) {
+    const StageDesc& S = a.stage[st];
+    if (const char* e = check(S.row_off, S.row_len, 1)) return e;
+    if (const char* e = check(S.el_off, S.el_len, 2)) return e;
+    if (S.red < 0 || S.red > 2) return "reduction kind out of range";
+    if (S.red_lds >= a.n_row_slots || S.red_slot >= n_slots) return "reduction target out of range";
+    if (S.red == 0 && (S.red_lds >= 0 || S.red_slot >= 0)) return "reduction target without a reduction";
+  }
+  return nullptr;
+}
+
 bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup* outp,
                    std::string* why) {
   CompiledGroup cg;
@@ -384,21 +431,15 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     const TensorInfo& ti = p.tensors[t];
     if ((ti.R != 1 && ti.R != R) || (ti.C != 1 && ti.C != C)) return bad("shapes in group do not broadcast");
   }
-  int n_reduce = 0, red_op = -1;
+  // ---- reductions
+  std::vector<int> reds;
   for (int i : ops)
-    if (is_reduce(p.ops[i].opcode)) {
-      ++n_reduce;
-      red_op = i;
-    }
-  if (n_reduce > 1) return bad("more than one reduction in a group");
-  if (red_op >= 0) {
-    const TensorInfo& ri = p.tensors[p.ops[red_op].in[0]];
+    if (is_reduce(p.ops[i].opcode)) reds.push_back(i);
+  for (int r : reds) {
+    const TensorInfo& ri = p.tensors[p.ops[r].in[0]];
     if (ri.R != R || ri.C != C) return bad("reduction input is not the group domain");
-    for (int i : ops)
-      for (int k = 0; k < p.ops[i].n_in; ++k)
-        if (p.ops[i].in[k] == p.ops[red_op].out) return bad("reduction is not the sink");
   }
-  bool flat = red_op < 0;
+  bool flat = reds.empty();
   for (int t : touched)
     if (p.tensors[t].R != R || p.tensors[t].C != C) flat = false;
   int64_t DR = flat ? 1 : R, DC = flat ? R * C : C;
@@ -440,21 +481,69 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   for (int t : outputs) slot_for(t);
   if ((int)slots.size() > kMaxSlots) return bad("too many external tensors");
 
-  // ---- operand classes and LDS slots
-  // ROW/COL values read by element-phase ops live in LDS.
-  std::map<int, int> row_lds, col_lds;
+  // ---- stages.  A row reduction's result can be read in the group only
+  // one stage later: it is known once every element of the row has been
+  // added.  Element ops (and reductions) run in the stage of their latest
+  // input; row ops in the row program before that stage; column ops in the
+  // column phase.  Reading an in-group reduction result is the
+  // row-resident extension: the fusion pass keeps a reduction as the last
+  // op of its group unless asked to merge across it.
+  std::map<int, int> avail;     // produced tensor -> first stage that can read it
+  std::map<int, int> stage_of;  // op -> element stage / row program index
+  std::map<int, int> producer;  // produced tensor -> op
+  for (int i : ops) producer[p.ops[i].out] = i;
+  int n_stages = 1;
   for (int i : ops) {
-    if (op_cls(i) != CLS_E) continue;
     const OpInfo& o = p.ops[i];
+    int st = 0;
+    for (int k = 0; k < o.n_in; ++k)
+      if (produced.count(o.in[k])) st = std::max(st, avail.at(o.in[k]));
+    const int c = op_cls(i);
+    if (c == CLS_COL && st > 0) return bad("column op after a row reduction");
+    stage_of[i] = st;
+    avail[o.out] = is_reduce(o.opcode) ? st + 1 : st;
+    n_stages = std::max(n_stages, st + 1);
+  }
+  for (int r : reds) {
+    bool read_in_group = false;
+    for (int i : ops)
+      for (int k = 0; k < p.ops[i].n_in; ++k)
+        if (p.ops[i].in[k] == p.ops[r].out) read_in_group = true;
+    if (read_in_group && cls_of(p.ops[r].out) != CLS_ROW)
+      return bad("row reduction over a single column read in its group");
+  }
+  if (n_stages > kMaxStages) return bad("more row-resident stages than the kernel holds");
+  std::vector<int> stage_red(n_stages, -1);
+  for (int r : reds) {
+    if (stage_red[stage_of[r]] >= 0) return bad("two row reductions in one stage");
+    stage_red[stage_of[r]] = r;
+  }
+
+  // ---- operand classes and LDS slots.  ROW/COL values read by element
+  // ops live in LDS; so do row values that cross from one row program (or
+  // a reduction) to a later row program.
+  std::map<int, int> row_lds, col_lds;
+  auto need_row = [&](int t) {
+    if (!row_lds.count(t)) {
+      const int s = (int)row_lds.size();
+      row_lds[t] = s;
+    }
+  };
+  for (int i : ops) {
+    const OpInfo& o = p.ops[i];
+    const int c = op_cls(i);
     for (int k = 0; k < o.n_in; ++k) {
-      int c = cls_of(o.in[k]);
-      if (c == CLS_ROW && !row_lds.count(o.in[k])) {
-        int s = (int)row_lds.size();
-        row_lds[o.in[k]] = s;
-      }
-      if (c == CLS_COL && !col_lds.count(o.in[k])) {
-        int s = (int)col_lds.size();
-        col_lds[o.in[k]] = s;
+      const int t = o.in[k];
+      const int ci = cls_of(t);
+      if (c == CLS_E) {
+        if (ci == CLS_ROW) need_row(t);
+        if (ci == CLS_COL && !col_lds.count(t)) {
+          const int s = (int)col_lds.size();
+          col_lds[t] = s;
+        }
+      } else if (c == CLS_ROW && produced.count(t)) {
+        const int j = producer.at(t);
+        if (is_reduce(p.ops[j].opcode) || stage_of.at(j) != stage_of.at(i)) need_row(t);
       }
     }
   }
@@ -476,13 +565,12 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     }
   }
 
-  // ---- lower ops to micro-ops per phase
-  std::vector<MOp> mops[3];
+  // ---- lower each op to micro-ops
+  std::map<int, std::vector<MOp>> mops_of;
   int synth = -1;
   for (int i : ops) {
     const OpInfo& o = p.ops[i];
-    int c = op_cls(i);
-    auto& L = mops[c];
+    auto& L = mops_of[i];
     if (o.opcode == GTF_OP_COPY) {
       MOp m;
       m.kind = 4;
@@ -555,124 +643,189 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     }
   }
 
-  // ---- code generation, phase by phase: column, row, element; first for
-  // the wide instance (two spill slots), else for the narrow one
-  std::vector<Instr> prog[3];
+  // ---- programs: the column program, then per stage a row program and an
+  // element program.  A stage's element program is the cone of element ops
+  // its sinks need (its reduction, and the outputs first available in it),
+  // recomputed from reloaded inputs rather than carried between stages.
+  enum PKind { P_COL = 0, P_ROW = 1, P_EL = 2 };
+  struct Prog {
+    int kind, stage;
+    std::vector<MOp> L;
+    std::set<int> store;  // values this program stores to their external slots
+  };
+  std::vector<Prog> progs;
+  {
+    Prog pc{P_COL, 0, {}, {}};
+    for (int i : ops)
+      if (op_cls(i) == CLS_COL) {
+        for (auto& m : mops_of[i]) pc.L.push_back(m);
+        if (outputs.count(p.ops[i].out)) pc.store.insert(p.ops[i].out);
+      }
+    progs.push_back(pc);
+  }
+  for (int st = 0; st < n_stages; ++st) {
+    Prog pr{P_ROW, st, {}, {}};
+    for (int i : ops)
+      if (op_cls(i) == CLS_ROW && stage_of[i] == st) {
+        for (auto& m : mops_of[i]) pr.L.push_back(m);
+        if (outputs.count(p.ops[i].out)) pr.store.insert(p.ops[i].out);
+      }
+    progs.push_back(pr);
+    Prog pe{P_EL, st, {}, {}};
+    std::set<int> cone;
+    std::vector<int> work;
+    if (stage_red[st] >= 0) work.push_back(stage_red[st]);
+    for (int i : ops)
+      if (op_cls(i) == CLS_E && !is_reduce(p.ops[i].opcode) && stage_of[i] == st &&
+          outputs.count(p.ops[i].out)) {
+        work.push_back(i);
+        pe.store.insert(p.ops[i].out);
+      }
+    while (!work.empty()) {
+      const int i = work.back();
+      work.pop_back();
+      if (cone.count(i)) continue;
+      cone.insert(i);
+      for (int k = 0; k < p.ops[i].n_in; ++k) {
+        const int t = p.ops[i].in[k];
+        if (!produced.count(t)) continue;
+        const int j = producer.at(t);
+        if (op_cls(j) == CLS_E && !is_reduce(p.ops[j].opcode)) work.push_back(j);
+      }
+    }
+    for (int i : ops)
+      if (cone.count(i))
+        for (auto& m : mops_of[i]) pe.L.push_back(m);
+    progs.push_back(pe);
+  }
+
+  // ---- code generation, program by program; first for the wide instance
+  // without spill slots, then with two, else for the narrow one
+  std::vector<std::vector<Instr>> code(progs.size());
   int max_depth = 0;
-  const int order[3] = {CLS_COL, CLS_ROW, CLS_E};
   auto generate = [&](int ns, bool hoist, std::string* gwhy) -> bool {
-    for (auto& pr : prog) pr.clear();
+    for (auto& c : code) c.clear();
     max_depth = 0;
-  for (int ph : order) {
-    Codegen g{p, &prog[ph], ph};
-    g.init();
-    g.ns = ns;
-    for (size_t k = 0; k < slots.size(); ++k) g.ext_slot[slots[k]] = (int)k;
-    if (ph == CLS_E) {  // broadcast operands are read from LDS
-      for (auto& kv : row_lds) {
-        g.xcls[kv.first] = CLS_ROW;
-        g.lds_slot[kv.first] = kv.second;
+    for (size_t pi = 0; pi < progs.size(); ++pi) {
+      const Prog& P = progs[pi];
+      const int ph = P.kind == P_COL ? CLS_COL : P.kind == P_ROW ? CLS_ROW : CLS_E;
+      Codegen g{p, &code[pi], ph};
+      g.init();
+      g.ns = ns;
+      for (size_t k = 0; k < slots.size(); ++k) g.ext_slot[slots[k]] = (int)k;
+      const auto& L = P.L;
+      std::set<int> made_here;
+      for (auto& m : L) made_here.insert(m.out);
+      // values read from LDS: in element programs every row / column
+      // operand; in row programs the row values made elsewhere
+      if (P.kind == P_EL) {
+        for (auto& kv : row_lds) {
+          g.xcls[kv.first] = CLS_ROW;
+          g.lds_slot[kv.first] = kv.second;
+        }
+        for (auto& kv : col_lds) {
+          g.xcls[kv.first] = CLS_COL;
+          g.lds_slot[kv.first] = kv.second;
+        }
+      } else if (P.kind == P_ROW) {
+        for (auto& kv : row_lds)
+          if (produced.count(kv.first) && !made_here.count(kv.first)) {
+            g.xcls[kv.first] = CLS_ROW;
+            g.lds_slot[kv.first] = kv.second;
+          }
       }
-      for (auto& kv : col_lds) {
-        g.xcls[kv.first] = CLS_COL;
-        g.lds_slot[kv.first] = kv.second;
+      for (auto& m : L) {
+        const int n_in = m.kind == 1 ? 2 : 1;
+        for (int k = 0; k < n_in; ++k) {
+          const int v = m.in[k];
+          if (g.is_x(v)) continue;
+          g.uses[v] += 1;
+          if (v >= 0 && !produced.count(v)) g.loadable.insert(v);
+        }
       }
-    }
-    auto& L = mops[ph];
-    std::set<int> made_here;
-    for (auto& m : L) made_here.insert(m.out);
-    for (auto& m : L) {
-      const int n_in = m.kind == 1 ? 2 : 1;
-      for (int k = 0; k < n_in; ++k) {
-        const int v = m.in[k];
-        if (g.is_x(v)) continue;
-        g.uses[v] += 1;
-        if (v >= 0 && !produced.count(v)) g.loadable.insert(v);
+      // externals staged into LDS for the element programs: column operands
+      // in the column program, row operands in the first row program
+      std::vector<std::pair<int, int>> staging;
+      if (P.kind == P_COL)
+        for (auto& kv : col_lds)
+          if (!produced.count(kv.first)) staging.push_back(kv);
+      if (P.kind == P_ROW && P.stage == 0)
+        for (auto& kv : row_lds)
+          if (!produced.count(kv.first)) staging.push_back(kv);
+      for (auto& kv : staging) g.loadable.insert(kv.first);
+      // load hoisting: the program's first two external loads (in order of
+      // first use) go to A and B at once, so both are in flight together
+      if (hoist) {
+        std::vector<int> first_use;
+        auto note = [&](int v) {
+          if (g.loadable.count(v) && std::find(first_use.begin(), first_use.end(), v) == first_use.end())
+            first_use.push_back(v);
+        };
+        for (auto& kv : staging) note(kv.first);
+        for (auto& m : L)
+          for (int k = 0; k < (m.kind == 1 ? 2 : 1); ++k) note(m.in[k]);
+        for (size_t i = 0; i < first_use.size() && i < 2; ++i) {
+          const int r = i == 0 ? Codegen::RA : Codegen::RB;
+          g.emit(g.load_form(first_use[i], r), g.ext_slot.at(first_use[i]));
+          g.reg[r] = first_use[i];
+        }
       }
-    }
-    // externals this phase stages into LDS for the element phase
-    const auto& lds_map = ph == CLS_ROW ? row_lds : col_lds;
-    if (ph != CLS_E)
-      for (auto& kv : lds_map)
-        if (!produced.count(kv.first)) g.loadable.insert(kv.first);
-    // load hoisting: the phase's first two external loads (in order of
-    // first use) go to A and B at once, so both are in flight together
-    if (hoist) {
-      std::vector<int> first_use;
-      auto note = [&](int v) {
-        if (g.loadable.count(v) && std::find(first_use.begin(), first_use.end(), v) == first_use.end())
-          first_use.push_back(v);
-      };
-      if (ph != CLS_E)
-        for (auto& kv : lds_map)
-          if (!produced.count(kv.first)) note(kv.first);
-      for (auto& m : L)
-        for (int k = 0; k < (m.kind == 1 ? 2 : 1); ++k) note(m.in[k]);
-      for (size_t i = 0; i < first_use.size() && i < 2; ++i) {
-        const int r = i == 0 ? Codegen::RA : Codegen::RB;
-        g.emit(g.load_form(first_use[i], r), g.ext_slot.at(first_use[i]));
-        g.reg[r] = first_use[i];
-      }
-    }
-    if (ph != CLS_E) {
-      for (auto& kv : lds_map) {
-        if (produced.count(kv.first)) continue;
-        g.loadable.insert(kv.first);
+      for (auto& kv : staging) {
         g.bring(kv.first, Codegen::RA);
         g.emit(F_ST_LDS, kv.second);
       }
-    }
-    // list scheduling: among ready micro-ops prefer one whose operands
-    // already sit in A (and B)
-    std::vector<char> done(L.size(), 0);
-    std::set<int> avail;
-    for (size_t step = 0; step < L.size() && g.ok; ++step) {
-      int best = -1, best_score = -1;
-      for (size_t k = 0; k < L.size(); ++k) {
-        if (done[k]) continue;
-        const int n_in = L[k].kind == 1 ? 2 : 1;
-        bool rdy = true;
-        for (int q = 0; q < n_in; ++q)
-          if (made_here.count(L[k].in[q]) && !avail.count(L[k].in[q])) rdy = false;
-        if (!rdy) continue;
-        // every binary op has a reversed form, so either operand may sit in A
-        const int x0 = L[k].in[0], x1 = n_in == 2 ? L[k].in[1] : kNoValue;
-        const int ra = g.reg[Codegen::RA], rb = g.reg[Codegen::RB];
-        int score = 0;
-        if (ra == x0 || ra == x1) score += 2;
-        if (n_in == 2 && ((rb == x1 && ra != x1) || (rb == x0 && ra != x0))) score += 1;
-        if (score > best_score) {
-          best_score = score;
-          best = (int)k;
+      // list scheduling: among ready micro-ops prefer one whose operands
+      // already sit in A (and B)
+      std::vector<char> done(L.size(), 0);
+      std::set<int> ready_vals;
+      for (size_t step = 0; step < L.size() && g.ok; ++step) {
+        int best = -1, best_score = -1;
+        for (size_t k = 0; k < L.size(); ++k) {
+          if (done[k]) continue;
+          const int n_in = L[k].kind == 1 ? 2 : 1;
+          bool rdy = true;
+          for (int q = 0; q < n_in; ++q)
+            if (made_here.count(L[k].in[q]) && !ready_vals.count(L[k].in[q])) rdy = false;
+          if (!rdy) continue;
+          // every binary op has a reversed form, so either operand may sit in A
+          const int x0 = L[k].in[0], x1 = n_in == 2 ? L[k].in[1] : kNoValue;
+          const int ra = g.reg[Codegen::RA], rb = g.reg[Codegen::RB];
+          int score = 0;
+          if (ra == x0 || ra == x1) score += 2;
+          if (n_in == 2 && ((rb == x1 && ra != x1) || (rb == x0 && ra != x0))) score += 1;
+          if (score > best_score) {
+            best_score = score;
+            best = (int)k;
+          }
         }
+        if (best < 0) {
+          *gwhy = "internal: no ready op";
+          return false;
+        }
+        done[best] = 1;
+        const MOp& m = L[best];
+        switch (m.kind) {
+          case 0: g.run_unary(m); break;
+          case 1: g.run_binary(m); break;
+          case 2: g.run_imm(m); break;
+          case 3: g.run_reduce(m); break;
+          default: g.run_copy(m); break;
+        }
+        if (!g.ok) break;
+        if (m.kind == 3) continue;
+        ready_vals.insert(m.out);
+        const int v = m.out;
+        if (v >= 0 && P.store.count(v))
+          g.emit(p.tensors[v].dtype == GTF_BF16 ? F_ST_BF16 : F_ST_F32, g.ext_slot.at(v));
+        if (P.kind == P_COL && v >= 0 && col_lds.count(v)) g.emit(F_ST_LDS, col_lds.at(v));
+        if (P.kind == P_ROW && v >= 0 && row_lds.count(v)) g.emit(F_ST_LDS, row_lds.at(v));
       }
-      if (best < 0) {
-        *gwhy = "internal: no ready op";
+      if (!g.ok) {
+        *gwhy = g.why;
         return false;
       }
-      done[best] = 1;
-      const MOp& m = L[best];
-      switch (m.kind) {
-        case 0: g.run_unary(m); break;
-        case 1: g.run_binary(m); break;
-        case 2: g.run_imm(m); break;
-        case 3: g.run_reduce(m); break;
-        default: g.run_copy(m); break;
-      }
-      if (!g.ok) break;
-      if (m.kind == 3) continue;
-      avail.insert(m.out);
-      const int v = m.out;
-      if (v >= 0 && outputs.count(v))
-        g.emit(p.tensors[v].dtype == GTF_BF16 ? F_ST_BF16 : F_ST_F32, g.ext_slot.at(v));
-      if (ph != CLS_E && v >= 0 && lds_map.count(v)) g.emit(F_ST_LDS, lds_map.at(v));
+      max_depth = std::max(max_depth, g.max_live);
     }
-    if (!g.ok) {
-      *gwhy = g.why;
-      return false;
-    }
-    max_depth = std::max(max_depth, g.max_live);
-  }
     return true;
   };
   // instances in order of preference: wide with no spill slot (highest
@@ -691,7 +844,8 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   }
   const int K = ns == kNS ? 1 : kWideK;
 
-  size_t total = prog[0].size() + prog[1].size() + prog[2].size();
+  size_t total = 0;
+  for (auto& c : code) total += c.size();
   if (total > (size_t)kMaxInstr) return bad("op-program longer than the instruction buffer");
 
   // ---- geometry
@@ -709,7 +863,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   a.NS = ns;
   const int64_t C8 = (DC + kV - 1) / kV * kV;
   int pw;
-  if (red_op >= 0) {
+  if (!reds.empty()) {
     pw = (int)std::max<int64_t>(C8, kV);
     if (!col_lds.empty() && (int64_t)col_lds.size() * C8 > 16384)
       return bad("reduction group with column operands wider than the LDS panel");
@@ -725,7 +879,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   {
     const int64_t want = std::max<int64_t>(1, nt / K);
     while ((int64_t)tpr * 2 <= want && tpr * 2 <= kBlock) tpr <<= 1;
-    if (red_op >= 0 && tpr > 64 && DR >= 256) tpr = 64;
+    if (!reds.empty() && tpr > 64 && DR >= 256) tpr = 64;
   }
   if (const char* e = std::getenv("GTF_TPR")) {
     int f = std::atoi(e);
@@ -741,24 +895,36 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   int lg = 0;
   while ((1 << lg) < tpr) ++lg;
   a.tpr_log2 = lg;
-  a.n_col = (int)prog[CLS_COL].size();
-  a.n_row = (int)prog[CLS_ROW].size();
-  a.n_elem = (int)prog[CLS_E].size();
-
   a.n_col_slots = (int)col_lds.size();
   a.n_row_slots = (int)row_lds.size();
-  a.reduce = 0;
-  a.red_slot = 0;
-  a.red_dtype = 0;
-  if (red_op >= 0) {
-    a.reduce = p.ops[red_op].opcode == GTF_OP_ROW_MEAN ? 2 : 1;
-    int t = p.ops[red_op].out;
-    a.red_slot = slot_for(t);
-    a.red_dtype = p.tensors[t].dtype == GTF_BF16 ? DT_BF16 : DT_F32;
-  }
+  // program layout: column program, then per stage row and element programs
   size_t pos = 0;
-  for (int ph : order)
-    for (const Instr& ins : prog[ph]) a.prog[pos++] = ins;
+  a.n_col = (int)code[0].size();
+  for (const Instr& ins : code[0]) a.prog[pos++] = ins;
+  a.n_stages = n_stages;
+  for (int st = 0; st < n_stages; ++st) {
+    StageDesc& S = a.stage[st];
+    const auto& cr = code[1 + 2 * st];
+    const auto& ce = code[2 + 2 * st];
+    S.row_off = (int)pos;
+    S.row_len = (int)cr.size();
+    for (const Instr& ins : cr) a.prog[pos++] = ins;
+    S.el_off = (int)pos;
+    S.el_len = (int)ce.size();
+    for (const Instr& ins : ce) a.prog[pos++] = ins;
+    S.red = 0;
+    S.red_lds = -1;
+    S.red_slot = -1;
+    S.red_dtype = DT_F32;
+    const int r = stage_red[st];
+    if (r >= 0) {
+      const int t = p.ops[r].out;
+      S.red = p.ops[r].opcode == GTF_OP_ROW_MEAN ? 2 : 1;
+      if (row_lds.count(t)) S.red_lds = row_lds.at(t);
+      if (outputs.count(t)) S.red_slot = slot_for(t);
+      S.red_dtype = p.tensors[t].dtype == GTF_BF16 ? DT_BF16 : DT_F32;
+    }
+  }
   for (size_t s = 0; s < slots.size(); ++s) {
     const TensorInfo& ti = p.tensors[slots[s]];
     int c = cls_of(slots[s]);
@@ -783,12 +949,13 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   cg.max_depth = max_depth;
   cg.lds_bytes = (int)(a.n_col_slots * (int64_t)pw * 4 + a.n_row_slots * (int64_t)rb * 4 + 16 * 4);
   if (cg.lds_bytes > 64 * 1024) return bad("LDS staging exceeds 64 KiB");
+  if (const char* why = check_program(a, cg.n_slots)) return bad(why);
   if (outp) *outp = cg;
   return true;
 }
 
 // ================================================================ planning
-int build_fuse_plan(FusePlan* p, bool fuse) {
+int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident) {
   int n = (int)p->ops.size();
   // annotate (OpPatternKind)
   for (OpInfo& o : p->ops) {
@@ -861,6 +1028,62 @@ int build_fuse_plan(FusePlan* p, bool fuse) {
       }
     }
   }
+  // Row-resident extension (opt-in): a group that ends in a row reduction
+  // is merged with a group on the same [R,C] domain that reads the
+  // reduction's [R,1] result, so the result never leaves the kernel (a
+  // one-kernel LayerNorm).  The merge must keep the group graph acyclic
+  // (no op outside the two groups on a path from one to the other) and the
+  // op and argument limits, and the kernel must hold the stages it makes.
+  if (fuse && row_resident) {
+    std::vector<char> in_set(n, 0);
+    bool changed = true;
+    while (changed) {
+      changed = false;
+      for (int r = 0; r < n && !changed; ++r) {
+        if (!is_reduce(p->ops[r].opcode)) continue;
+        const int t = p->ops[r].out;
+        for (int c = 0; c < n && !changed; ++c) {
+          bool reads = false;
+          for (int k = 0; k < p->ops[c].n_in; ++k)
+            if (p->ops[c].in[k] == t) reads = true;
+          if (!reads || uf.find(c) == uf.find(r)) continue;
+          if (p->ops[c].pattern == GTF_PAT_OPAQUE) continue;
+          const int gr = uf.find(r), gc = uf.find(c);
+          std::fill(in_set.begin(), in_set.end(), 0);
+          std::vector<int> members;
+          for (int v = 0; v < n; ++v)
+            if (uf.find(v) == gr || uf.find(v) == gc) {
+              in_set[v] = 1;
+              members.push_back(v);
+            }
+          // convexity: walk forward from the members through non-members; a
+          // walk that re-enters the set would become a cycle
+          std::vector<char> seen(n, 0);
+          std::vector<int> stack;
+          for (int v : members)
+            for (int w : rd[v])
+              if (!in_set[w]) stack.push_back(w);
+          bool convex = true;
+          while (!stack.empty() && convex) {
+            const int v = stack.back();
+            stack.pop_back();
+            if (seen[v]) continue;
+            seen[v] = 1;
+            for (int w : rd[v]) {
+              if (in_set[w]) convex = false;
+              else stack.push_back(w);
+            }
+          }
+          if (!convex) continue;
+          if ((int)members.size() > GTF_MAX_GROUP_OPS) continue;
+          if (count_args(*p, in_set) > GTF_MAX_GROUP_ARGS) continue;
+          if (!compile_group(*p, members, nullptr, nullptr)) continue;
+          uf.merge_into(r, c);
+          changed = true;
+        }
+      }
+    }
+  }
   // collect groups, order them by their dependencies
   std::map<int, std::vector<int>> byroot;
   for (int i = 0; i < n; ++i) byroot[uf.find(i)].push_back(i);
@@ -920,10 +1143,14 @@ int build_fuse_plan(FusePlan* p, bool fuse) {
       std::fprintf(stderr, "[gtf] group %zu pattern %d ops", g, G.pattern);
       for (int i : G.ops) std::fprintf(stderr, " %d", i);
       const ExecArgs& a = G.code.args;
-      std::fprintf(stderr, " | dom %lldx%lld items %lld PW %d RB %d tpr %d col %d row %d elem %d depth %d\n",
+      std::fprintf(stderr, " | dom %lldx%lld items %lld PW %d RB %d tpr %d K %d NS %d col %d stages %d depth %d\n",
                    (long long)a.R, (long long)a.C, (long long)a.n_items, a.PW, a.RB,
-                   1 << a.tpr_log2, a.n_col, a.n_row, a.n_elem, G.code.max_depth);
-      int tot = a.n_col + a.n_row + a.n_elem;
+                   1 << a.tpr_log2, a.K, a.NS, a.n_col, a.n_stages, G.code.max_depth);
+      for (int st = 0; st < a.n_stages; ++st)
+        std::fprintf(stderr, "    stage %d: row %d+%d elem %d+%d red %d lds %d slot %d\n", st,
+                     a.stage[st].row_off, a.stage[st].row_len, a.stage[st].el_off, a.stage[st].el_len,
+                     a.stage[st].red, a.stage[st].red_lds, a.stage[st].red_slot);
+      int tot = a.stage[a.n_stages - 1].el_off + a.stage[a.n_stages - 1].el_len;
       for (int k = 0; k < tot; ++k)
         std::fprintf(stderr, "    %3d form %2d arg %d imm %g\n", k, a.prog[k].code, a.prog[k].arg,
                      a.prog[k].imm);

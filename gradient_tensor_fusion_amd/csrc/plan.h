@@ -54,10 +54,14 @@ struct FusePlan {
 
 // Compile a set of ops (ascending ids) into an op-program.  Returns false,
 // with a reason, when the group does not fit the kernel's resources.
+// Range check of a compiled program's slot, LDS and spill indices; null
+// when every index is inside what the launch provides.
+const char* check_program(const ExecArgs& a, int n_slots);
+
 bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup* out,
                    std::string* why);
 
-int build_fuse_plan(FusePlan* p, bool fuse);
+int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident = false);
 
 struct BucketPlan {
   int dtype = 0;

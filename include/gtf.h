@@ -138,6 +138,13 @@ typedef struct {
 
 /* fuse_plan_create flags */
 #define GTF_NO_FUSE 1u /* one op per group: the unfused baseline            */
+/* Row-resident extension of the fusion rules: after TVM's three phases, a
+ * group ending in a row reduction is merged with a group on the same [R,C]
+ * domain that reads the reduction's result (reduce-then-broadcast, e.g. a
+ * LayerNorm in one kernel); the group then runs in stages, one per
+ * reduction it reads.  TVM keeps a reduction as the last op of its group
+ * ("Fusion rules"); this flag lifts that for row reductions only. */
+#define GTF_ROW_RESIDENT 2u
 
 typedef struct gtf_fuse_plan gtf_fuse_plan;
 typedef struct gtf_bucket_plan gtf_bucket_plan;
@@ -187,7 +194,10 @@ typedef struct {
   int32_t program_length; /* op-program instructions, all phases            */
   int32_t spill_slots;    /* op-program spill slots used                    */
   int32_t spill_slots_max;/* spill slots of the kernel: 0 or 2 (wide), 6 (narrow) */
-  int32_t reduce;         /* 0 none, 1 row sum, 2 row mean                  */
+  int32_t reduce;         /* 0 none, 1 row sum, 2 row mean (the last one)   */
+  int32_t stages;         /* element stages: 1, or more in a group that reads
+                             its own row reductions (GTF_ROW_RESIDENT)      */
+  int32_t reserved;
 } gtf_group_geometry;
 
 int fuse_plan_group_geometry(const gtf_fuse_plan* plan, int32_t g, gtf_group_geometry* out);

@@ -34,6 +34,22 @@ Readings where the page is silent: the source's pattern is its group's
 pattern; path nodes are judged by their own pattern; a node whose output
 is a graph output has no post-dominator.
 
+Row-resident extension (opt-in, row_resident=True; beyond the page, whose
+fusion rules keep a reduction as the last op of its group): after the
+three phases, a group holding a row reduction r is merged with the group of
+an op c that reads r's result, scanning r then c in ascending order and
+starting over after every merge, when
+  * the merge is convex: no op outside the two groups lies on a path from
+    one to the other;
+  * the merged set keeps the op and argument limits;
+  * it is row-resident feasible: every tensor it touches broadcasts to one
+    [R,C] domain, every reduction reads that domain, its stages (an op runs
+    in the stage of its latest input; a reduction's result is readable one
+    stage later) number at most MAX_STAGES with at most one reduction each,
+    column ops ([1,C] results) run in stage 0, a reduction result read in
+    the group is a [R,1] column of a C > 1 domain, and row / column ops read
+    only their own class (column ops may also read a [1,1] input).
+
 Pinned in tests/test_oracle_partition.py: the page's add/exp/squeeze example
 and its diamond, the sink-only and barrier rules, the 256 limit, and the
 post-dominator sets against path enumeration on every small DAG.
@@ -49,6 +65,8 @@ K_OUT_EWISE_FUSABLE, K_TUPLE, K_OPAQUE = 4, 7, 8
 
 MAX_FUSED_OPS = 256
 MAX_GROUP_ARGS = 16
+MAX_STAGES = 4
+_REDUCES = ("row_sum", "row_mean")
 
 
 def pattern(graph, i: int) -> int:
@@ -168,7 +186,79 @@ def _group_args(graph, members: Set[int]) -> int:
     return len(ext)
 
 
-def partition(graph, fuse: bool = True) -> List[List[int]]:
+def _row_resident_ok(graph, members: Set[int]) -> bool:
+    ms = sorted(members)
+    touched = set()
+    for i in ms:
+        touched.update(graph.ops[i].inputs)
+        touched.add(graph.ops[i].output)
+    shape = {t: norm_shape(graph.tensors[t].shape) for t in touched}
+    reds = [i for i in ms if graph.ops[i].op in _REDUCES]
+    if not reds:
+        return False
+    R, C = shape[graph.ops[reds[0]].inputs[0]]
+    for t in touched:
+        r, c = shape[t]
+        if r not in (1, R) or c not in (1, C):
+            return False
+    if any(shape[graph.ops[i].inputs[0]] != (R, C) for i in reds):
+        return False
+
+    def cls(t):
+        r, c = shape[t]
+        if (r, c) == (R, C):
+            return "E"
+        if r == 1 and c == C:
+            return "COL"
+        return "ROW"
+    produced = {graph.ops[i].output: i for i in ms}
+    avail, stage = {}, {}
+    for i in ms:
+        o = graph.ops[i]
+        st = max([avail[t] for t in o.inputs if t in produced], default=0)
+        stage[i] = st
+        avail[o.output] = st + 1 if o.op in _REDUCES else st
+    n_stages = max(stage.values()) + 1
+    if n_stages > MAX_STAGES:
+        return False
+    per_stage = [stage[i] for i in reds]
+    if len(per_stage) != len(set(per_stage)):
+        return False
+    for i in ms:
+        o = graph.ops[i]
+        c = "E" if o.op in _REDUCES else cls(o.output)
+        if c == "COL" and stage[i] > 0:
+            return False
+        if c != "E":
+            for t in o.inputs:
+                if cls(t) == c:
+                    continue
+                if c == "COL" and t not in produced and shape[t] == (1, 1):
+                    continue
+                return False
+        for t in o.inputs:
+            if t in produced and graph.ops[produced[t]].op in _REDUCES and cls(t) != "ROW":
+                return False
+    return True
+
+
+def _convex(succ, members: Set[int]) -> bool:
+    """No path leaves the set and comes back into it."""
+    outside = {s for v in members for s in succ[v] if s not in members}
+    seen, stack = set(), list(outside)
+    while stack:
+        v = stack.pop()
+        if v in seen:
+            continue
+        seen.add(v)
+        for s in succ[v]:
+            if s in members:
+                return False
+            stack.append(s)
+    return True
+
+
+def partition(graph, fuse: bool = True, row_resident: bool = False) -> List[List[int]]:
     """Groups of op indices, each sorted, listed in an order that respects
     the dependencies between groups."""
     n = len(graph.ops)
@@ -207,6 +297,30 @@ def partition(graph, fuse: bool = True) -> List[List[int]]:
                     continue
                 for v in mid | {i}:
                     uf.union_into(v, d)
+        if row_resident:
+            changed = True
+            while changed:
+                changed = False
+                for r in range(n):
+                    if changed or graph.ops[r].op not in _REDUCES:
+                        continue
+                    out = graph.ops[r].output
+                    for c in range(n):
+                        if out not in graph.ops[c].inputs or uf.find(c) == uf.find(r):
+                            continue
+                        if pats[c] == K_OPAQUE:
+                            continue
+                        roots = {uf.find(r), uf.find(c)}
+                        members = {v for v in range(n) if uf.find(v) in roots}
+                        if not _convex(succ, members):
+                            continue
+                        if len(members) > MAX_FUSED_OPS or _group_args(graph, members) > MAX_GROUP_ARGS:
+                            continue
+                        if not _row_resident_ok(graph, members):
+                            continue
+                        uf.union_into(r, c)
+                        changed = True
+                        break
     groups: Dict[int, List[int]] = {}
     for i in range(n):
         groups.setdefault(uf.find(i), []).append(i)

@@ -39,10 +39,11 @@ def empty_device(shape, dtype: str) -> torch.Tensor:
     return torch.empty(tuple(shape), dtype=TORCH_DT[dtype], device="cuda")
 
 
-def gpu_run(graph, inputs: Dict[int, np.ndarray], fuse: bool = True, plan=None):
+def gpu_run(graph, inputs: Dict[int, np.ndarray], fuse: bool = True, plan=None,
+            row_resident: bool = False):
     """Run the graph on the GPU; returns (plan, {tensor id: host array}) for
     every materialised tensor (bf16 as uint16 bits)."""
-    plan = plan or gtf.FusePlan(graph, fuse=fuse)
+    plan = plan or gtf.FusePlan(graph, fuse=fuse, row_resident=row_resident)
     dev = {}
     for t in plan.materialized():
         d = graph.tensors[t]
@@ -60,8 +61,8 @@ def gpu_run(graph, inputs: Dict[int, np.ndarray], fuse: bool = True, plan=None):
     return plan, host
 
 
-def oracle_run(graph, inputs, fuse: bool = True, given=None):
-    groups = opart.partition(graph, fuse=fuse)
+def oracle_run(graph, inputs, fuse: bool = True, given=None, row_resident: bool = False):
+    groups = opart.partition(graph, fuse=fuse, row_resident=row_resident)
     stored = opart.stored_tensors(graph, groups)
     return oev.run(graph, inputs, stored=stored, given=given)
 

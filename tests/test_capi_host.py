@@ -291,3 +291,24 @@ def test_multi_set_runs_on_the_host():
         gtf.FuseMulti(gtf.FusePlan(configs.c2_graph(4, 64)), 0, [5])
     with pytest.raises(gtf.GtfError):
         gtf.FuseMulti(plan, 0, [4, -1])
+
+
+def test_row_resident_plans_match_the_oracle():
+    """GTF_ROW_RESIDENT: the library's merged groups equal the oracle's on
+    the extension's pinned graphs, the LayerNorm at its c5 size and small
+    random DAGs with row reductions, row ops and broadcasts."""
+    from tests.test_oracle_partition import _rr_graphs
+    graphs = [g for g, _, _ in _rr_graphs().values()]
+    graphs.append(configs.layernorm_graph())
+    graphs += list(_broadcast_dags(11, 300))
+    merged = 0
+    for g in graphs:
+        plan = gtf.FusePlan(g, row_resident=True)
+        want = opart.partition(g, row_resident=True)
+        assert as_sets(plan.groups()) == as_sets(want)
+        merged += len(want) < len(opart.partition(g))
+        for k in range(plan.num_groups):
+            geo = plan.geometry(k)
+            n_red = sum(g.ops[i].op in ("row_sum", "row_mean") for i in plan.group_ops(k))
+            assert geo["stages"] >= 1 and (n_red <= geo["stages"])
+    assert merged >= 20

@@ -248,11 +248,11 @@ def _ieee_only(g):
     return all(o.op not in ("exp", "tanh", "sigmoid", "gelu") for o in g.ops)
 
 
-def _check_graph(g, ins):
+def _check_graph(g, ins, modes=((True, False), (False, False))):
     has_red = any(o.op in ("row_sum", "row_mean") for o in g.ops)
-    for fuse in (True, False):
-        plan, got = gpu_run(g, ins, fuse=fuse)
-        vals, want = oracle_run(g, ins, fuse=fuse)
+    for fuse, rr in modes:
+        plan, got = gpu_run(g, ins, fuse=fuse, row_resident=rr)
+        vals, want = oracle_run(g, ins, fuse=fuse, row_resident=rr)
         big = max([float(np.nanmax(np.abs(v))) if v.size else 0.0 for v in vals.values()] + [1.0])
         for t in g.outputs():
             d = g.tensors[t]
@@ -509,3 +509,117 @@ def test_joint_epilogue_in_one_launch():
         torch.cuda.synchronize()
         for a, b in zip(buckets, wb):
             assert_bits_equal(a.cpu().numpy(), b)
+
+
+# ---------------------------------------------------------------- row-resident groups
+def _promote(g, names):
+    """The same graph with the named intermediates also stored as outputs."""
+    for t, d in enumerate(g.tensors):
+        if d.name in names:
+            g.tensors[t] = type(d)(d.name, d.dtype, d.shape, "out")
+    return g
+
+
+def _ids(g):
+    return {d.name: t for t, d in enumerate(g.tensors)}
+
+
+@pytest.mark.parametrize("rows,hidden", [(8192, 1024), (37, 1024), (16, 264), (3, 5), (2, 67)])
+def test_row_resident_layernorm_is_the_three_launch_pipeline(rows, hidden):
+    """One launch with mean and var held in LDS gives the bits of the three
+    launches that pass them through HBM: same lane geometry, so the same
+    summation order, and fp32 statistics either way."""
+    g = configs.layernorm_graph(rows, hidden)
+    ins = configs.layernorm_inputs(g, configs.c5_layer_seed(0))
+    plan = gtf.FusePlan(g, row_resident=True)
+    assert plan.num_groups == 1 and plan.geometry(0)["stages"] == 3
+    _, got = gpu_run(g, ins, plan=plan)
+    _, ref = gpu_run(g, ins)
+    y = _ids(g)["y"]
+    assert sorted(got) == sorted(g.inputs() + [y])
+    assert_bits_equal(got[y], ref[y])
+
+
+@pytest.mark.parametrize("rows,hidden", [(4096, 1024), (37, 1000), (3, 5), (300, 4104)])
+def test_row_resident_layernorm_statistics_against_the_oracle(rows, hidden):
+    """mean and var also stored: each against the oracle's reduction, and y
+    bit for bit against the oracle's normalisation of the GPU's statistics."""
+    g = _promote(configs.layernorm_graph(rows, hidden), {"mean", "var"})
+    ins = configs.layernorm_inputs(g, configs.c5_layer_seed(0) + 17)
+    plan = gtf.FusePlan(g, row_resident=True)
+    assert plan.num_groups == 1
+    _, got = gpu_run(g, ins, plan=plan)
+    n = _ids(g)
+    vals, _ = oracle_run(g, ins, row_resident=True)
+    X = numerics.bf16_to_f32(ins[n["X"]]).reshape(rows, hidden)
+    assert_reduce_close(got[n["mean"]], vals[n["mean"]], reduce_bound(X, True), 1e-5)
+    given = {n["mean"]: got[n["mean"]].reshape(rows, 1)}
+    vals2, _ = oracle_run(g, ins, given=given, row_resident=True)
+    assert_reduce_close(got[n["var"]], vals2[n["var"]], reduce_bound(vals2[n["sq"]], True), 1e-5)
+    given[n["var"]] = got[n["var"]].reshape(rows, 1)
+    _, want = oracle_run(g, ins, given=given, row_resident=True)
+    assert_bits_equal(got[n["y"]], want[n["y"]])
+    # the statistics are the ones the plain group computes
+    _, plain = gpu_run(configs.layernorm_graph(rows, hidden), ins, row_resident=True)
+    assert_bits_equal(plain[n["y"]], got[n["y"]])
+
+
+def _scale_by_sum(R, C, store_sum):
+    g = Graph()
+    x = g.input("x", "f32", (R, C))
+    s = g.op("row_sum", [x], "s", "f32", (R, 1), role="out" if store_sum else "tmp")
+    g.op("mul", [x, s], "y", "f32", (R, C), role="out")
+    return g
+
+
+def _softmax_like(R, C, store_sum):
+    g = Graph()
+    x = g.input("x", "f32", (R, C))
+    e = g.op("exp", [x], "e", "f32", (R, C))
+    s = g.op("row_sum", [e], "s", "f32", (R, 1), role="out" if store_sum else "tmp")
+    g.op("div", [e, s], "y", "f32", (R, C), role="out")
+    return g
+
+
+@pytest.mark.parametrize("rows,cols", [(2048, 4096), (37, 1000), (4, 65536), (3, 5), (1, 1),
+                                       (300, 24)])
+@pytest.mark.parametrize("build", [_scale_by_sum, _softmax_like])
+def test_row_resident_reduce_then_broadcast(build, rows, cols):
+    """The reduced value is stored once more so it can be checked: against
+    the oracle's sum, and the broadcast consumer bit for bit against one IEEE
+    operation on the stored operands; without the extra store the consumer's
+    bits do not change."""
+    g = build(rows, cols, True)
+    ins = _inputs_for(g, 400 + rows)
+    plan = gtf.FusePlan(g, row_resident=True)
+    n = _ids(g)
+    assert plan.num_groups == len(opart.partition(g, row_resident=True))
+    # one-column rows: the sum has the shape of its input, nothing to merge
+    assert cols == 1 or any(plan.geometry(k)["stages"] == 2 and len(plan.group_ops(k)) == 2
+                            for k in range(plan.num_groups))
+    _, got = gpu_run(g, ins, plan=plan)
+    vals, want = oracle_run(g, ins, row_resident=True)
+    s, y = n["s"], n["y"]
+    src = n.get("e", n["x"])
+    if src != n["x"]:
+        assert_f32_rel(got[src], vals[src], 1e-6)
+    term = got[src] if src != n["x"] else ins[n["x"]]
+    assert_reduce_close(got[s], vals[s], reduce_bound(vals[src], False), 1e-5)
+    sv = got[s].reshape(rows, 1)
+    expect = (term * sv) if build is _scale_by_sum else (term / sv)
+    assert_bits_equal(got[y], expect.astype(np.float32))
+    g2 = build(rows, cols, False)
+    _, got2 = gpu_run(g2, ins, row_resident=True)
+    assert_bits_equal(got2[y], got[y])
+
+
+def test_random_broadcast_dags_row_resident():
+    n = 0
+    for gi, g in enumerate(_broadcast_dags(7, 200)):
+        if len(opart.partition(g, row_resident=True)) == len(opart.partition(g)):
+            continue
+        for R, C in [(3, 5), (2, 67), (5, 130), (300, 24)]:
+            gg = _reshape(g, R, C)
+            _check_graph(gg, _inputs_for(gg, 200 + gi), modes=((True, True),))
+        n += 1
+    assert n >= 15

@@ -190,3 +190,62 @@ def test_groups_are_convex_and_rule_abiding_on_random_dags():
             for i in grp:
                 for s2 in succ[i]:
                     assert owner[s2] >= gi
+
+
+# ---------------------------------------------------------------- row-resident extension
+def _rr_graphs():
+    """Graphs for the row-resident merge: name -> (graph, groups without
+    the extension, groups with it)."""
+    out = {}
+    g = configs.layernorm_graph(16, 64)
+    out["layernorm"] = (g, [[0], [1, 2, 3], [4, 5, 6, 7, 8, 9, 10]], [list(range(11))])
+    g = Graph()
+    x = g.input("x", "f32", (8, 40))
+    s = g.op("row_sum", [x], "s", "f32", (8, 1))
+    g.op("mul", [x, s], "y", "f32", (8, 40), role="out")
+    out["scale_by_sum"] = (g, [[0], [1]], [[0, 1]])
+    g = Graph()
+    x = g.input("x", "f32", (8, 40))
+    e = g.op("exp", [x], "e", "f32", (8, 40))
+    s = g.op("row_sum", [e], "s", "f32", (8, 1))
+    g.op("div", [e, s], "y", "f32", (8, 40), role="out")
+    out["softmax_like"] = (g, [[0], [1], [2]], [[0], [1, 2]])
+    g = Graph()
+    x = g.input("x", "f32", (8, 40))
+    g.op("row_mean", [x], "m", "f32", (8, 1), role="out")
+    out["reduce_only"] = (g, [[0]], [[0]])
+    g = Graph()
+    x = g.input("x", "f32", (8, 40))
+    s = g.op("row_sum", [x], "s", "f32", (8, 1))
+    u = g.op("copy", [s], "u", "f32", (8, 1), opaque=True)
+    t = g.op("mul", [x, s], "t", "f32", (8, 40))
+    g.op("add", [t, u], "y", "f32", (8, 40), role="out")
+    out["opaque_on_path"] = (g, [[0], [1], [2, 3]], [[0], [1], [2, 3]])
+    g = Graph()
+    v = g.input("x", "f32", (8, 40))
+    for k in range(6):
+        m = g.op("row_mean", [v], f"m{k}", "f32", (8, 1))
+        v = g.op("sub", [v, m], f"c{k}", "f32", (8, 40), role="out" if k == 5 else "tmp")
+    out["six_reductions"] = (g, None, None)
+    return out
+
+
+def test_row_resident_merges():
+    for name, (g, plain, merged) in _rr_graphs().items():
+        if plain is None:
+            continue
+        assert pt.partition(g) == plain, name
+        assert pt.partition(g, row_resident=True) == merged, name
+
+
+def test_row_resident_stage_limit():
+    """A chain of six reduce-then-broadcast steps cannot be one group: the
+    kernel holds at most four stages, so every merged group has at most four
+    reductions and each stage at most one."""
+    g, _, _ = _rr_graphs()["six_reductions"]
+    groups = pt.partition(g, row_resident=True)
+    assert len(groups) < len(pt.partition(g))
+    for grp in groups:
+        reds = [i for i in grp if g.ops[i].op == "row_mean"]
+        assert len(reds) <= 4
+    assert sorted(i for grp in groups for i in grp) == list(range(len(g.ops)))
