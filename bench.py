@@ -47,8 +47,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "joint"])
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "joint", "ln"])
     ap.add_argument("--layers", type=int, default=12)
+    ap.add_argument("--ln-variant", default="all",
+                    choices=["all", "row_resident", "tvm_groups", "unfused"],
+                    help="--workload ln: time only this variant (for per-kernel profiles)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the unfused and per-tensor baselines")
@@ -314,7 +317,7 @@ class CopyBench:
 def main():
     args = parse()
     if args.traffic_from:
-        print(json.dumps(summarise_traffic(*args.traffic_from)))
+        print(json.dumps(summarise_traffic(*args.traffic_from, workload=args.workload)))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused groups shard by rows with no exchange "
@@ -465,6 +468,8 @@ def run_config(torch, gtf, configs, args):
         return res
     if w == "joint":
         return run_joint(torch, gtf, configs, args, res, gen)
+    if w == "ln":
+        return run_ln(torch, gtf, configs, args, res, gen)
     if w == "c1":
         g = configs.c1_graph()
         dists = {"x": ("uniform", -1, 1), "a": ("uniform", -1, 1), "b": ("uniform", -1, 1)}
@@ -500,15 +505,80 @@ def run_config(torch, gtf, configs, args):
     return res
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c5.txt")
-TRAFFIC_CMDS = (
-    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE "
-    "-d $R/gpurun_out/pmc_fetch -o fetch --output-format csv -- python3 $R/bench.py --steps 3 "
-    "--warmup 1 --no-cpu-baseline --no-baselines",
-    "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE "
-    "-d $R/gpurun_out/pmc_write -o write --output-format csv -- python3 $R/bench.py --steps 3 "
-    "--warmup 1 --no-cpu-baseline --no-baselines",
-    "python3 bench.py --traffic-from <fetch>_counter_collection.csv <write>_counter_collection.csv")
+def run_ln(torch, gtf, configs, args, res, gen):
+    """The c5 LayerNorm, bf16[8192,1024], three ways: one row-resident
+    launch (mean and var held in LDS), TVM's three groups (mean and var
+    through HBM) and one launch per op.  Each is captured in a HIP graph
+    over its rotation sets and replayed, so host launch cost is not in the
+    times."""
+    g = configs.layernorm_graph()
+    plans = {"row_resident": gtf.FusePlan(g, row_resident=True), "tvm_groups": gtf.FusePlan(g),
+             "unfused": gtf.FusePlan(g, fuse=False)}
+    if args.ln_variant != "all":
+        plans = {args.ln_variant: plans[args.ln_variant]}
+    # the 1 GiB copy: the achievable ceiling, and the reference the
+    # traffic counters are scaled by
+    cb = CopyBench(torch, gtf)
+    copy_gbs, _ = cb.gbs(5)
+    del cb
+    torch.cuda.empty_cache()
+    out = {}
+    for name, plan in plans.items():
+        nbytes = sum(group_bytes(g, plan))
+        k = _rotation_sets(nbytes)
+        sets = [alloc_graph(torch, gtf, g, plan, gen, LN_D) for _ in range(k)]
+        def rotation():
+            # marshalled at each call: the launches go to the current
+            # (capturing) stream
+            for st in sets:
+                plan.run(st)
+        # one replay runs the LayerNorm once on each of the k rotation sets
+        graph = _captured(torch, rotation)
+        ms, _ = time_steps(torch, graph.replay, args.steps, args.warmup)
+        ms /= k
+        out[name] = {"ms_per_step": round(ms, 5), "bytes": nbytes, "launches": plan.num_groups,
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+    if "row_resident" not in out or len(out) < 3:
+        name, v = next(iter(out.items()))
+        res.update({"value": v["gbs"], "ms_per_step": v["ms_per_step"], "dtype": "bf16",
+                    "config": {"workload": f"ln: LayerNorm bf16[8192,1024], {name} only",
+                               "bytes_per_step": v["bytes"]},
+                    "timing": "graph replays over the rotation sets", "variants": out})
+        return res
+    rr = out["row_resident"]
+    tj = read_traffic("exec_kernel", "ln")
+    res.update({"value": rr["gbs"], "ms_per_step": rr["ms_per_step"], "dtype": "bf16",
+                "config": {"workload": "ln: LayerNorm bf16[8192,1024] with bf16 gamma/beta[1024], "
+                                       "one row-resident launch",
+                           "bytes_per_step": rr["bytes"]},
+                "roofline": {"bound": "hbm", "achieved": rr["gbs"], "peak": PEAK_GBS, "unit": "GB/s",
+                             "frac": round(rr["gbs"] / PEAK_GBS, 4),
+                             "traffic": tj["bytes_per_launch"] if tj else None,
+                             "kernel": "exec_kernel", "avg_launch_us": round(rr["ms_per_step"] * 1e3, 3),
+                             "algorithmic_bytes_per_launch": rr["bytes"]},
+                "copy_kernel_gbs": round(copy_gbs, 1),
+                "timing": "graph replays over the rotation sets",
+                "speedup_vs_tvm_groups": round(out["tvm_groups"]["ms_per_step"] / rr["ms_per_step"], 3),
+                "speedup_vs_unfused": round(out["unfused"]["ms_per_step"] / rr["ms_per_step"], 3),
+                "variants": out})
+    return res
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+
+
+def traffic_cmds(workload):
+    """The commands that make profiles/traffic_<workload>.txt."""
+    extra = "" if workload == "c5" else f" --workload {workload} --ln-variant row_resident"
+    run = f"python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-baselines{extra}"
+    return (
+        "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE "
+        f"-d $R/gpurun_out/pmc_fetch -o fetch --output-format csv -- {run}",
+        "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE "
+        f"-d $R/gpurun_out/pmc_write -o write --output-format csv -- {run}",
+        f"python3 bench.py --workload {workload} --traffic-from <fetch>_counter_collection.csv "
+        "<write>_counter_collection.csv")
 
 
 def _counter_per_kernel(path, counter):
@@ -526,7 +596,7 @@ def _counter_per_kernel(path, counter):
     return {k: list(v.values()) for k, v in out.items()}
 
 
-def summarise_traffic(fetch_csv, write_csv):
+def summarise_traffic(fetch_csv, write_csv, workload="c5"):
     fe = _counter_per_kernel(fetch_csv, "FETCH_SIZE")
     wr = _counter_per_kernel(write_csv, "WRITE_SIZE")
     nb = CopyBench.NBYTES
@@ -544,23 +614,24 @@ def summarise_traffic(fetch_csv, write_csv):
         res["kernels"][k] = {"dispatches": len(fe[k]), "fetch_bytes_per_launch": round(f),
                              "write_bytes_per_launch": round(w),
                              "bytes_per_launch": round(f + w)}
-    lines = ["# HBM traffic per launch of the c5 step's kernels: rocprofv3 FETCH_SIZE and "
-             "WRITE_SIZE (KiB per dispatch), each scaled so that the 1 GiB copy kernel in the "
-             "same run counts exactly 1 GiB read and 1 GiB written.",
+    lines = [f"# HBM traffic per launch of the {workload} workload's kernels: rocprofv3 FETCH_SIZE "
+             "and WRITE_SIZE (KiB per dispatch), each scaled so that the 1 GiB copy kernel in "
+             "the same run counts exactly 1 GiB read and 1 GiB written.",
              "# commands (R = repository root):"]
-    lines += ["#   " + c for c in TRAFFIC_CMDS]
+    lines += ["#   " + c for c in traffic_cmds(workload)]
     lines.append(json.dumps(res))
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(workload), "w") as f:
         f.write("\n".join(lines) + "\n")
     return res
 
 
-def read_traffic(kernel):
+def read_traffic(kernel, workload="c5"):
     """Traffic record of one kernel, or None when absent or taken from
     another version of the kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         js = [ln for ln in f if ln.startswith("{")]
     if not js:
         return None
@@ -568,6 +639,17 @@ def read_traffic(kernel):
     if tj.get("source_hash") != _kernel_hash():
         return None
     return tj["kernels"].get(kernel)
+
+
+def _captured(torch, fn):
+    """fn's launches captured once in a HIP graph (on a side stream, which
+    the launchers pick up as the current stream) after one eager run."""
+    fn()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        fn()
+    return g
 
 
 def run_joint(torch, gtf, configs, args, res, gen):
@@ -610,13 +692,7 @@ def run_joint(torch, gtf, configs, args, res, gen):
             a, b = g.inputs()
             plan.run_group(0, {a: grads[k], b: weights[k], g.outputs()[0]: bp.slot_view(buckets, k, (n,))})
 
-    def captured(fn):
-        fn()  # eager once, outside the capture
-        side = torch.cuda.Stream()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            fn()
-        return g
+    captured = lambda fn: _captured(torch, fn)  # noqa: E731
     g_joint = captured(lambda: mj.run())
     g_sep = captured(lambda: (ms_.run(), bp.pack(outs, buckets, configs.AVG_SCALE)))
     g_per = captured(per_tensor)

@@ -129,7 +129,9 @@ class FusePlan:
 
     def launcher(self, g: int, tensors, stream=None):
         """fuse_group_run with its arguments marshalled once: returns a
-        callable that launches group g on the same tensors and stream."""
+        callable that launches group g on the same tensors and stream.  The
+        stream is fixed here (the current one unless given), so a launcher
+        made before a graph capture does not launch into the capture."""
         f, h, ptrs, st = C.lib().fuse_group_run, self._h, self._ptrs(tensors), C.stream_handle(stream)
         keep = tensors
 
