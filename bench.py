@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "joint", "ln"])
     ap.add_argument("--layers", type=int, default=12)
     ap.add_argument("--ln-variant", default="all",
-                    choices=["all", "row_resident", "tvm_groups", "unfused"],
+                    choices=["all", "row_resident", "tvm_groups", "unfused", "shared_center",
+                             "shared_center_duplicated"],
                     help="--workload ln: time only this variant (for per-kernel profiles)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baselines", action="store_true",
@@ -63,21 +64,12 @@ def parse():
 
 # ------------------------------------------------------------ accounting
 def group_bytes(graph, plan):
-    """Algorithmic bytes of each group: distinct external inputs read once,
-    outputs needed outside the group written once."""
+    """Algorithmic bytes of each group: every tensor the launch reads or
+    writes in device memory, once."""
     out = []
-    for ops in plan.groups():
-        produced = {graph.ops[i].output for i in ops}
-        ext = set()
-        for i in ops:
-            for t in graph.ops[i].inputs:
-                if t not in produced:
-                    ext.add(t)
-        for t in produced:
-            if plan.is_materialized(t):
-                ext.add(t)
+    for g in range(plan.num_groups):
         b = 0
-        for t in ext:
+        for t in plan.group_tensors(g):
             d = graph.tensors[t]
             n = 1
             for s in d.shape:
@@ -506,14 +498,21 @@ def run_config(torch, gtf, configs, args):
 
 
 def run_ln(torch, gtf, configs, args, res, gen):
-    """The c5 LayerNorm, bf16[8192,1024], three ways: one row-resident
-    launch (mean and var held in LDS), TVM's three groups (mean and var
-    through HBM) and one launch per op.  Each is captured in a HIP graph
+    """The c5 LayerNorm, bf16[8192,1024]: one row-resident launch (mean and
+    var held in LDS), TVM's three groups (mean and var through HBM), one
+    launch per op, and the form with x - mean written once, planned without
+    and with duplicate fusion.  Each is captured in a HIP graph
     over its rotation sets and replayed, so host launch cost is not in the
     times."""
     g = configs.layernorm_graph()
-    plans = {"row_resident": gtf.FusePlan(g, row_resident=True), "tvm_groups": gtf.FusePlan(g),
-             "unfused": gtf.FusePlan(g, fuse=False)}
+    gs = configs.layernorm_shared_graph()
+    plans = {"row_resident": (g, lambda: gtf.FusePlan(g, row_resident=True)),
+             "tvm_groups": (g, lambda: gtf.FusePlan(g)),
+             "unfused": (g, lambda: gtf.FusePlan(g, fuse=False)),
+             # x - mean written once: stored and read back by TVM's groups,
+             # or recomputed in both readers by duplicate fusion
+             "shared_center": (gs, lambda: gtf.FusePlan(gs)),
+             "shared_center_duplicated": (gs, lambda: gtf.FusePlan(gs, duplicate=True))}
     if args.ln_variant != "all":
         plans = {args.ln_variant: plans[args.ln_variant]}
     # the 1 GiB copy: the achievable ceiling, and the reference the
@@ -523,7 +522,8 @@ def run_ln(torch, gtf, configs, args, res, gen):
     del cb
     torch.cuda.empty_cache()
     out = {}
-    for name, plan in plans.items():
+    for name, (g, make) in plans.items():
+        plan = make()
         nbytes = sum(group_bytes(g, plan))
         k = _rotation_sets(nbytes)
         sets = [alloc_graph(torch, gtf, g, plan, gen, LN_D) for _ in range(k)]
@@ -538,7 +538,7 @@ def run_ln(torch, gtf, configs, args, res, gen):
         ms /= k
         out[name] = {"ms_per_step": round(ms, 5), "bytes": nbytes, "launches": plan.num_groups,
                      "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2)}
-    if "row_resident" not in out or len(out) < 3:
+    if len(out) == 1:
         name, v = next(iter(out.items()))
         res.update({"value": v["gbs"], "ms_per_step": v["ms_per_step"], "dtype": "bf16",
                     "config": {"workload": f"ln: LayerNorm bf16[8192,1024], {name} only",
@@ -560,6 +560,8 @@ def run_ln(torch, gtf, configs, args, res, gen):
                 "timing": "graph replays over the rotation sets",
                 "speedup_vs_tvm_groups": round(out["tvm_groups"]["ms_per_step"] / rr["ms_per_step"], 3),
                 "speedup_vs_unfused": round(out["unfused"]["ms_per_step"] / rr["ms_per_step"], 3),
+                "duplicate_fusion_speedup": round(out["shared_center"]["ms_per_step"]
+                                                  / out["shared_center_duplicated"]["ms_per_step"], 3),
                 "variants": out})
     return res
 

@@ -58,15 +58,25 @@ def _program_desc(graph):
 class FusePlan:
     """fuse_plan_create and friends."""
 
-    def __init__(self, graph, fuse: bool = True, row_resident: bool = False):
+    def __init__(self, graph, fuse: bool = True, row_resident: bool = False,
+                 duplicate: bool = False):
         self.graph = graph
         self.n_tensors = len(graph.tensors)
-        self.n_ops = len(graph.ops)
         desc, self._tens, self._ops = _program_desc(graph)
         h = c_void_p()
-        flags = (0 if fuse else C.NO_FUSE) | (C.ROW_RESIDENT if row_resident else 0)
+        flags = ((0 if fuse else C.NO_FUSE) | (C.ROW_RESIDENT if row_resident else 0)
+                 | (C.DUPLICATE if duplicate else 0))
         C.check(C.lib().fuse_plan_create(byref(desc), flags, byref(h)))
         self._h = h
+        n = c_int32()
+        C.check(C.lib().fuse_plan_num_ops(self._h, byref(n)))
+        self.n_ops = n.value  # ops of the plan's program (copies included)
+
+    def op_origin(self) -> List[int]:
+        """Per program op, the graph op it computes."""
+        arr = (c_int32 * max(1, self.n_ops))()
+        C.check(C.lib().fuse_plan_op_origin(self._h, arr))
+        return list(arr[: self.n_ops])
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -85,6 +95,14 @@ class FusePlan:
         C.check(C.lib().fuse_plan_group_info(self._h, g, None, 0, byref(n), byref(pat)))
         ids = (c_int32 * max(1, n.value))()
         C.check(C.lib().fuse_plan_group_info(self._h, g, ids, n.value, byref(n), byref(pat)))
+        return list(ids[: n.value])
+
+    def group_tensors(self, g: int) -> List[int]:
+        """Tensors group g reads or writes in device memory, each once."""
+        n = c_int32()
+        C.check(C.lib().fuse_plan_group_tensors(self._h, g, None, 0, byref(n)))
+        ids = (c_int32 * max(1, n.value))()
+        C.check(C.lib().fuse_plan_group_tensors(self._h, g, ids, n.value, byref(n)))
         return list(ids[: n.value])
 
     def group_pattern(self, g: int) -> int:

@@ -31,9 +31,11 @@ OPCODE = {
 OPF_OPAQUE = 1
 NO_FUSE = 1
 ROW_RESIDENT = 2
+DUPLICATE = 4
 
 EXPORTED = (
     "fuse_plan_create", "fuse_plan_num_groups", "fuse_plan_group_info", "fuse_plan_op_info",
+    "fuse_plan_num_ops", "fuse_plan_op_origin", "fuse_plan_group_tensors",
     "fuse_plan_group_geometry",
     "fuse_plan_is_materialized", "fuse_group_run", "fuse_plan_run", "fuse_plan_destroy",
     "fuse_multi_create", "fuse_multi_workspace_bytes", "fuse_multi_bind", "fuse_multi_run",
@@ -89,6 +91,10 @@ def lib() -> ctypes.CDLL:
         L.fuse_plan_group_info.argtypes = [vp, c_int32, POINTER(c_int32), c_int32,
                                            POINTER(c_int32), POINTER(c_int32)]
         L.fuse_plan_op_info.argtypes = [vp, POINTER(c_int32), POINTER(c_int32)]
+        L.fuse_plan_num_ops.argtypes = [vp, POINTER(c_int32)]
+        L.fuse_plan_op_origin.argtypes = [vp, POINTER(c_int32)]
+        L.fuse_plan_group_tensors.argtypes = [vp, c_int32, POINTER(c_int32), c_int32,
+                                              POINTER(c_int32)]
         L.fuse_plan_is_materialized.argtypes = [vp, c_int32, POINTER(c_int32)]
         L.fuse_plan_group_geometry.argtypes = [vp, c_int32, POINTER(GroupGeometry)]
         L.fuse_group_run.argtypes = [vp, c_int32, POINTER(vp), vp]

@@ -169,12 +169,14 @@ const char* gtf_last_error(void) { return g_last_error.c_str(); }
 int fuse_plan_create(const gtf_program_desc* desc, uint32_t flags, gtf_fuse_plan** out) {
   if (out == nullptr) return fail(GTF_E_INVALID, "out is NULL");
   *out = nullptr;
-  if (flags & ~(GTF_NO_FUSE | GTF_ROW_RESIDENT)) return fail(GTF_E_INVALID, "unknown flags");
+  if (flags & ~(GTF_NO_FUSE | GTF_ROW_RESIDENT | GTF_DUPLICATE))
+    return fail(GTF_E_INVALID, "unknown flags");
   gtf_fuse_plan* h = new (std::nothrow) gtf_fuse_plan();
   if (h == nullptr) return fail(GTF_E_LIMIT, "out of host memory");
   int st = validate(desc, &h->p);
   if (st == GTF_OK)
-    st = build_fuse_plan(&h->p, (flags & GTF_NO_FUSE) == 0, (flags & GTF_ROW_RESIDENT) != 0);
+    st = build_fuse_plan(&h->p, (flags & GTF_NO_FUSE) == 0, (flags & GTF_ROW_RESIDENT) != 0,
+                         (flags & GTF_DUPLICATE) != 0);
   if (st != GTF_OK) {
     delete h;
     return st;
@@ -189,6 +191,18 @@ int fuse_plan_num_groups(const gtf_fuse_plan* plan, int32_t* n) {
   return GTF_OK;
 }
 
+int fuse_plan_num_ops(const gtf_fuse_plan* plan, int32_t* n) {
+  if (plan == nullptr || n == nullptr) return fail(GTF_E_INVALID, "NULL argument");
+  *n = (int32_t)plan->p.ops.size();
+  return GTF_OK;
+}
+
+int fuse_plan_op_origin(const gtf_fuse_plan* plan, int32_t* origin) {
+  if (plan == nullptr || origin == nullptr) return fail(GTF_E_INVALID, "NULL argument");
+  for (size_t i = 0; i < plan->p.ops.size(); ++i) origin[i] = plan->p.origin[i];
+  return GTF_OK;
+}
+
 int fuse_plan_group_info(const gtf_fuse_plan* plan, int32_t g, int32_t* op_ids, int32_t cap,
                          int32_t* n_ops, int32_t* pattern_kind) {
   if (plan == nullptr) return fail(GTF_E_INVALID, "plan is NULL");
@@ -199,6 +213,19 @@ int fuse_plan_group_info(const gtf_fuse_plan* plan, int32_t g, int32_t* op_ids, 
   if (op_ids) {
     if (cap < (int32_t)G.ops.size()) return fail(GTF_E_LIMIT, "op_ids capacity too small");
     for (size_t k = 0; k < G.ops.size(); ++k) op_ids[k] = G.ops[k];
+  }
+  return GTF_OK;
+}
+
+int fuse_plan_group_tensors(const gtf_fuse_plan* plan, int32_t g, int32_t* tensor_ids,
+                            int32_t cap, int32_t* n) {
+  if (plan == nullptr) return fail(GTF_E_INVALID, "plan is NULL");
+  if (g < 0 || g >= (int32_t)plan->p.groups.size()) return fail(GTF_E_INVALID, "group index");
+  const std::vector<int>& st = plan->p.groups[g].code.slot_tensor;
+  if (n) *n = (int32_t)st.size();
+  if (tensor_ids) {
+    if (cap < (int32_t)st.size()) return fail(GTF_E_LIMIT, "tensor_ids capacity too small");
+    for (size_t k = 0; k < st.size(); ++k) tensor_ids[k] = st[k];
   }
   return GTF_OK;
 }
@@ -238,7 +265,7 @@ int fuse_plan_group_geometry(const gtf_fuse_plan* plan, int32_t g, gtf_group_geo
 
 int fuse_plan_is_materialized(const gtf_fuse_plan* plan, int32_t tensor_id, int32_t* yes) {
   if (plan == nullptr || yes == nullptr) return fail(GTF_E_INVALID, "NULL argument");
-  if (tensor_id < 0 || tensor_id >= (int32_t)plan->p.tensors.size())
+  if (tensor_id < 0 || tensor_id >= (int32_t)plan->p.n_desc_tensors)
     return fail(GTF_E_INVALID, "tensor id");
   *yes = plan->p.materialized[tensor_id] ? 1 : 0;
   return GTF_OK;
@@ -376,7 +403,7 @@ int fuse_multi_create(const gtf_fuse_plan* plan, int32_t g, int32_t n_sets, cons
   gtf_fuse_multi* m = new (std::nothrow) gtf_fuse_multi;
   if (m == nullptr) return fail(GTF_E_INVALID, "out of host memory");
   m->cg = cg;
-  m->n_tensors = (int32_t)plan->p.tensors.size();
+  m->n_tensors = (int32_t)plan->p.n_desc_tensors;
   m->numel.assign(numel, numel + n_sets);
   for (int32_t s = 0; s < n_sets; ++s)
     for (int64_t off = 0; off < numel[s]; off += a.PW) {

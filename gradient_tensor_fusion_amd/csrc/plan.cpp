@@ -955,9 +955,11 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
 }
 
 // ================================================================ planning
-int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident) {
-  int n = (int)p->ops.size();
-  // annotate (OpPatternKind)
+namespace {
+
+// OpPatternKind per op ("Operator Pattern Classification") and the
+// post-dominator tree ("Algorithm" step 2).
+void annotate(FusePlan* p) {
   for (OpInfo& o : p->ops) {
     if (o.flags & GTF_OPF_OPAQUE) {
       o.pattern = GTF_PAT_OPAQUE;
@@ -976,7 +978,15 @@ int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident) {
   }
   auto rd = readers_of(*p);
   p->ipdom = postdom_tree(*p, rd);
+}
 
+// The grouping ("Algorithm" step 3, "Fusion rules"), then the optional
+// row-resident merge.  Groups are member lists, each ascending, listed in
+// the order of their union-find roots.
+std::vector<std::vector<int>> partition_groups(const FusePlan& pl, bool fuse, bool row_resident) {
+  const FusePlan* p = &pl;
+  const int n = (int)p->ops.size();
+  auto rd = readers_of(*p);
   std::vector<int> pats(n);
   for (int i = 0; i < n; ++i) pats[i] = p->ops[i].pattern;
   UnionFind uf(pats);
@@ -1084,15 +1094,170 @@ int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident) {
       }
     }
   }
-  // collect groups, order them by their dependencies
   std::map<int, std::vector<int>> byroot;
   for (int i = 0; i < n; ++i) byroot[uf.find(i)].push_back(i);
   std::vector<std::vector<int>> gl;
-  std::vector<int> gpat;
-  for (auto& kv : byroot) {
-    gl.push_back(kv.second);
-    gpat.push_back(uf.pat[kv.first]);
+  for (auto& kv : byroot) gl.push_back(kv.second);
+  return gl;
+}
+
+int64_t tensor_bytes(const TensorInfo& t) {
+  return t.R * t.C * (t.dtype == GTF_F32 ? 4 : t.dtype == GTF_BF16 ? 2 : 1);
+}
+
+// Cost of a grouping: HBM bytes (every distinct tensor a group reads from
+// memory, every tensor it stores) and launches.
+std::pair<int64_t, int64_t> plan_cost(const FusePlan& p, const std::vector<std::vector<int>>& gl) {
+  std::vector<int> owner(p.tensors.size(), -1);
+  for (size_t g = 0; g < gl.size(); ++g)
+    for (int i : gl[g]) owner[p.ops[i].out] = (int)g;
+  std::vector<char> stored(p.tensors.size(), 0);
+  for (size_t t = 0; t < p.tensors.size(); ++t)
+    if (p.tensors[t].role == GTF_ROLE_OUT) stored[t] = 1;
+  for (size_t g = 0; g < gl.size(); ++g)
+    for (int i : gl[g])
+      for (int k = 0; k < p.ops[i].n_in; ++k) {
+        const int t = p.ops[i].in[k];
+        if (owner[t] >= 0 && owner[t] != (int)g) stored[t] = 1;
+      }
+  int64_t bytes = 0;
+  for (size_t g = 0; g < gl.size(); ++g) {
+    std::set<int> touched;
+    for (int i : gl[g]) {
+      for (int k = 0; k < p.ops[i].n_in; ++k) {
+        const int t = p.ops[i].in[k];
+        if (owner[t] != (int)g) touched.insert(t);
+      }
+      if (stored[p.ops[i].out]) touched.insert(p.ops[i].out);
+    }
+    for (int t : touched) bytes += tensor_bytes(p.tensors[t]);
   }
+  return {bytes, (int64_t)gl.size()};
+}
+
+// Duplicate op v for each reader in `targets`: a copy of v, writing a new
+// internal tensor, goes right before its reader, which then reads the copy.
+// v itself goes when it is an intermediate left without readers.  Returns
+// the copies' op ids in the new program.
+std::vector<int> duplicate_op(FusePlan* p, int v, const std::vector<int>& targets) {
+  const int n = (int)p->ops.size();
+  const int tv = p->ops[v].out;
+  std::vector<char> is_target(n, 0);
+  for (int r : targets) is_target[r] = 1;
+  std::vector<int> new_t(n, -1);
+  for (int r : targets) {
+    TensorInfo ti = p->tensors[tv];
+    ti.role = GTF_ROLE_TMP;
+    p->tensors.push_back(ti);
+    new_t[r] = (int)p->tensors.size() - 1;
+  }
+  bool v_read = false;
+  for (int j = 0; j < n; ++j)
+    if (!is_target[j])
+      for (int k = 0; k < p->ops[j].n_in; ++k)
+        if (p->ops[j].in[k] == tv) v_read = true;
+  const bool drop_v = !v_read && p->tensors[tv].role == GTF_ROLE_TMP;
+  std::vector<OpInfo> ops;
+  std::vector<int> origin, copies;
+  for (int j = 0; j < n; ++j) {
+    if (is_target[j]) {
+      OpInfo c = p->ops[v];
+      c.out = new_t[j];
+      copies.push_back((int)ops.size());
+      ops.push_back(c);
+      origin.push_back(p->origin[v]);
+      OpInfo r = p->ops[j];
+      for (int k = 0; k < r.n_in; ++k)
+        if (r.in[k] == tv) r.in[k] = new_t[j];
+      ops.push_back(r);
+      origin.push_back(p->origin[j]);
+    } else if (!(j == v && drop_v)) {
+      ops.push_back(p->ops[j]);
+      origin.push_back(p->origin[j]);
+    }
+  }
+  p->ops.swap(ops);
+  p->origin.swap(origin);
+  annotate(p);
+  return copies;
+}
+
+// Duplicate fusion (DisCo, the fusion approach for a predecessor with
+// several successors): an elementwise or broadcast op whose value crosses
+// into other groups is recomputed inside each of those readers' groups
+// instead of being stored and read back.  Ops are tried in program order;
+// a duplication is kept when every copy lands in its reader's group and
+// the plan's (HBM bytes, launches) strictly drops, and the scan then starts
+// over; an op whose duplication is not kept is not tried again.  "Lands"
+// means no copy's value is ever stored: every reader of every copy, this
+// rewrite's or an earlier one's, shares the copy's group.
+void duplicate_pass(FusePlan* p, bool row_resident) {
+  std::set<int> blocked;  // descriptor op ids
+  for (;;) {
+    const auto gl = partition_groups(*p, true, row_resident);
+    const auto cost = plan_cost(*p, gl);
+    std::vector<int> gof(p->ops.size(), -1);
+    for (size_t g = 0; g < gl.size(); ++g)
+      for (int i : gl[g]) gof[i] = (int)g;
+    const auto rd = readers_of(*p);
+    bool kept = false;
+    for (int v = 0; v < (int)p->ops.size() && !kept; ++v) {
+      if (blocked.count(p->origin[v]) || p->ops[v].pattern > GTF_PAT_BROADCAST) continue;
+      if (rd[v].size() < 2) continue;
+      std::vector<int> targets;
+      for (int r : rd[v])
+        if (gof[r] != gof[v] && p->ops[r].pattern != GTF_PAT_OPAQUE) targets.push_back(r);
+      if (targets.empty()) continue;
+      FusePlan q = *p;
+      const std::vector<int> copies = duplicate_op(&q, v, targets);
+      const auto gl2 = partition_groups(q, true, row_resident);
+      std::vector<int> gof2(q.ops.size(), -1);
+      for (size_t g = 0; g < gl2.size(); ++g)
+        for (int i : gl2[g]) gof2[i] = (int)g;
+      // no value of a copy (this rewrite's or an earlier one's) is stored:
+      // every reader of a copy shares the copy's group
+      bool fused = !copies.empty();
+      std::vector<int> prod(q.tensors.size(), -1);
+      for (size_t i = 0; i < q.ops.size(); ++i) prod[q.ops[i].out] = (int)i;
+      for (size_t j = 0; j < q.ops.size(); ++j)
+        for (int k = 0; k < q.ops[j].n_in; ++k) {
+          const int t = q.ops[j].in[k];
+          if (t >= q.n_desc_tensors && gof2[prod[t]] != gof2[j]) fused = false;
+        }
+      if (fused && plan_cost(q, gl2) < cost) {
+        *p = std::move(q);
+        kept = true;
+      } else {
+        blocked.insert(p->origin[v]);
+      }
+    }
+    if (!kept) return;
+  }
+}
+
+}  // namespace
+
+int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident, bool duplicate) {
+  if (p->origin.size() != p->ops.size()) {
+    p->n_desc_ops = (int)p->ops.size();
+    p->n_desc_tensors = (int)p->tensors.size();
+    p->origin.resize(p->ops.size());
+    for (size_t i = 0; i < p->ops.size(); ++i) p->origin[i] = (int)i;
+  }
+  annotate(p);
+  if (fuse && duplicate) duplicate_pass(p, row_resident);
+  const int n = (int)p->ops.size();
+  const auto gl0 = partition_groups(*p, fuse, row_resident);
+  std::vector<std::vector<int>> gl;
+  std::vector<int> gpat;
+  for (const auto& g : gl0) {
+    gl.push_back(g);
+    int pat = 0;
+    for (int i : g) pat = std::max(pat, p->ops[i].pattern);
+    gpat.push_back(pat);
+  }
+  (void)n;
+  // order the groups by their dependencies
   std::vector<int> owner(p->tensors.size(), -1);
   for (size_t g = 0; g < gl.size(); ++g)
     for (int i : gl[g]) owner[p->ops[i].out] = (int)g;
@@ -1137,6 +1302,10 @@ int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident) {
         int t = p->ops[i].in[k];
         if (gof[t] >= 0 && gof[t] != (int)g) p->materialized[t] = 1;
       }
+  // the caller provides memory for descriptor tensors only
+  for (const Group& G : p->groups)
+    for (int t : G.code.slot_tensor)
+      if (t >= p->n_desc_tensors) return fail(GTF_E_LIMIT, "an internal tensor would be stored");
   if (std::getenv("GTF_TRACE")) {
     for (size_t g = 0; g < p->groups.size(); ++g) {
       const Group& G = p->groups[g];

@@ -45,23 +45,27 @@ struct Group {
 };
 
 struct FusePlan {
+  // The program: the descriptor's tensors and ops, plus (with duplicate
+  // fusion) internal tensors after them and copies of ops among them.
   std::vector<TensorInfo> tensors;
   std::vector<OpInfo> ops;
+  std::vector<int> origin;       // per op: the descriptor op it computes
+  int n_desc_ops = 0, n_desc_tensors = 0;
   std::vector<int> ipdom;        // -1: none
   std::vector<Group> groups;     // in run order
   std::vector<char> materialized;
 };
 
-// Compile a set of ops (ascending ids) into an op-program.  Returns false,
-// with a reason, when the group does not fit the kernel's resources.
 // Range check of a compiled program's slot, LDS and spill indices; null
 // when every index is inside what the launch provides.
 const char* check_program(const ExecArgs& a, int n_slots);
 
+// Compile a set of ops (ascending ids) into an op-program.  Returns false,
+// with a reason, when the group does not fit the kernel's resources.
 bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup* out,
                    std::string* why);
 
-int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident = false);
+int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident = false, bool duplicate = false);
 
 struct BucketPlan {
   int dtype = 0;

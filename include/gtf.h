@@ -145,6 +145,20 @@ typedef struct {
  * reduction it reads.  TVM keeps a reduction as the last op of its group
  * ("Fusion rules"); this flag lifts that for row reductions only. */
 #define GTF_ROW_RESIDENT 2u
+/* Duplicate fusion (DisCo, "Background and Motivation": the fusion
+ * approaches for a predecessor with several successors; "Strategy Maker":
+ * duplicating a predecessor for its other successors).  Before grouping,
+ * an elementwise or broadcast op whose value would cross into other groups
+ * is recomputed inside each of those readers' groups.  Ops are tried in
+ * program order.  A duplication is kept when no copy's value would be
+ * stored (every reader of a copy shares its group) and the plan's HBM
+ * bytes (then launches) strictly drop;
+ * then the scan starts over.  An op whose duplication is not kept is not
+ * tried again.  Copies are ops of the plan's program
+ * (fuse_plan_num_ops, fuse_plan_op_origin); their outputs are never stored,
+ * so tensor ids and the caller's pointer arrays are those of the
+ * descriptor. */
+#define GTF_DUPLICATE 4u
 
 typedef struct gtf_fuse_plan gtf_fuse_plan;
 typedef struct gtf_bucket_plan gtf_bucket_plan;
@@ -168,14 +182,30 @@ int fuse_plan_create(const gtf_program_desc* desc, uint32_t flags, gtf_fuse_plan
  * dependencies, so running 0..n-1 in order runs the program. */
 int fuse_plan_num_groups(const gtf_fuse_plan* plan, int32_t* n);
 
-/* Ops of group g (ascending op ids) and the group's OpPatternKind (max over
- * its members).  op_ids may be NULL to ask only for *n_ops; otherwise it
- * must hold cap entries (GTF_E_LIMIT if cap < *n_ops). */
+/* Ops of the plan's program: the descriptor's n_ops, or more when
+ * GTF_DUPLICATE added copies (and fewer originals it left unread). */
+int fuse_plan_num_ops(const gtf_fuse_plan* plan, int32_t* n);
+
+/* origin[i] = the descriptor op that program op i computes (i itself
+ * without GTF_DUPLICATE).  origin holds fuse_plan_num_ops entries. */
+int fuse_plan_op_origin(const gtf_fuse_plan* plan, int32_t* origin);
+
+/* Ops of group g (ascending program op ids) and the group's OpPatternKind
+ * (max over its members).  op_ids may be NULL to ask only for *n_ops;
+ * otherwise it must hold cap entries (GTF_E_LIMIT if cap < *n_ops). */
 int fuse_plan_group_info(const gtf_fuse_plan* plan, int32_t g, int32_t* op_ids, int32_t cap,
                          int32_t* n_ops, int32_t* pattern_kind);
 
-/* Per-op annotation and post-dominator tree (both arrays hold n_ops
- * entries; ipdom[i] = -1 when op i has no immediate post-dominator). */
+/* External tensors of group g (descriptor tensor ids): every tensor the
+ * launch reads or writes in device memory, each once.  tensor_ids may be
+ * NULL to ask only for *n; otherwise it must hold cap entries
+ * (GTF_E_LIMIT if cap < *n). */
+int fuse_plan_group_tensors(const gtf_fuse_plan* plan, int32_t g, int32_t* tensor_ids,
+                            int32_t cap, int32_t* n);
+
+/* Per-op annotation and post-dominator tree of the plan's program (both
+ * arrays hold fuse_plan_num_ops entries; ipdom[i] = -1 when op i has no
+ * immediate post-dominator). */
 int fuse_plan_op_info(const gtf_fuse_plan* plan, int32_t* pattern_kind, int32_t* ipdom);
 
 /* Launch shape of group g, for diagnostics and for checking the kernel's

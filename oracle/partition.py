@@ -50,6 +50,23 @@ starting over after every merge, when
     the group is a [R,1] column of a C > 1 domain, and row / column ops read
     only their own class (column ops may also read a [1,1] input).
 
+Duplicate fusion (opt-in, duplicate(); DisCo, "Background and Motivation"
+on the two fusion approaches for a predecessor with several successors,
+and "Strategy Maker", method (ii): duplicate the predecessor for its other
+successors).  The page leaves the choice to its search; the rule here
+decides it by the bytes it moves, the reason the page gives for
+duplicating.  Before grouping, ops are scanned in program order.  For an
+elementwise or broadcast op p with two or more readers, some of which are
+in another group than p (and not opaque):
+  * each such reader r gets its own copy of p, placed right before r and
+    writing a new intermediate that r reads instead of p's output;
+  * p itself is dropped when its output is an intermediate that no op
+    reads any more.
+The rewrite is kept when every reader of every copy (this rewrite's and
+earlier ones') then shares the copy's group, so no copy's value is ever
+stored, and the plan's cost (HBM bytes, then launches; plan_cost) strictly
+drops; the scan then starts over.  Otherwise p is not tried again.
+
 Pinned in tests/test_oracle_partition.py: the page's add/exp/squeeze example
 and its diamond, the sink-only and barrier rules, the 256 limit, and the
 post-dominator sets against path enumeration on every small DAG.
@@ -362,3 +379,103 @@ def stored_tensors(graph, groups: List[List[int]]) -> Set[int]:
                 if t in owner and owner[t] != gi:
                     stored.add(t)
     return stored
+
+
+_DT_BYTES = {"f32": 4, "bf16": 2, "u8": 1}
+
+
+def _tensor_bytes(graph, t: int) -> int:
+    d = graph.tensors[t]
+    n = 1
+    for e in d.shape:
+        n *= e
+    return n * _DT_BYTES[d.dtype]
+
+
+def plan_cost(graph, groups: List[List[int]]):
+    """(HBM bytes, launches) of a grouping: per group, every distinct tensor
+    it reads from memory (graph inputs and values stored by other groups)
+    and every tensor it stores (graph outputs and values other groups
+    read)."""
+    owner = {}
+    for gi, g in enumerate(groups):
+        for i in g:
+            owner[graph.ops[i].output] = gi
+    stored = stored_tensors(graph, groups) | set(graph.outputs())
+    total = 0
+    for gi, g in enumerate(groups):
+        touched = set()
+        for i in g:
+            for t in graph.ops[i].inputs:
+                if owner.get(t) != gi:
+                    touched.add(t)
+            if graph.ops[i].output in stored:
+                touched.add(graph.ops[i].output)
+        total += sum(_tensor_bytes(graph, t) for t in touched)
+    return total, len(groups)
+
+
+def _duplicate_op(graph, origin: List[int], p: int, targets: List[int]):
+    """The program with op p copied for each reader in targets (see the
+    module docstring); returns (graph, origin, copy op ids)."""
+    from workloads.graph import Graph, OpDesc, TensorDesc
+    op = graph.ops[p]
+    tensors = list(graph.tensors)
+    new_t = {}
+    for r in targets:
+        d = graph.tensors[op.output]
+        tensors.append(TensorDesc(f"{d.name}@{r}", d.dtype, d.shape, "tmp"))
+        new_t[r] = len(tensors) - 1
+    still_read = any(op.output in graph.ops[j].inputs
+                     for j in range(len(graph.ops)) if j not in new_t)
+    drop = not still_read and graph.tensors[op.output].role == "tmp"
+    ops, org, copies = [], [], []
+    for j, o in enumerate(graph.ops):
+        if j in new_t:
+            copies.append(len(ops))
+            ops.append(OpDesc(op.op, op.inputs, new_t[j], op.imm, op.opaque))
+            org.append(origin[p])
+            ins = tuple(new_t[j] if t == op.output else t for t in o.inputs)
+            ops.append(OpDesc(o.op, ins, o.output, o.imm, o.opaque))
+            org.append(origin[j])
+        elif not (j == p and drop):
+            ops.append(o)
+            org.append(origin[j])
+    return Graph(tensors, ops), org, copies
+
+
+def duplicate(graph, row_resident: bool = False):
+    """Duplicate fusion (module docstring).  Returns (program, origin):
+    the rewritten graph, whose tensors extend the input graph's, and for
+    each of its ops the op of the input graph it computes."""
+    g, origin = graph, list(range(len(graph.ops)))
+    blocked: Set[int] = set()
+    while True:
+        groups = partition(g, row_resident=row_resident)
+        cost = plan_cost(g, groups)
+        gof = {i: k for k, grp in enumerate(groups) for i in grp}
+        kept = False
+        for p in range(len(g.ops)):
+            if origin[p] in blocked or pattern(g, p) > K_BROADCAST:
+                continue
+            out = g.ops[p].output
+            readers = [r for r in range(len(g.ops)) if out in g.ops[r].inputs]
+            if len(readers) < 2:
+                continue
+            targets = [r for r in readers if gof[r] != gof[p] and pattern(g, r) != K_OPAQUE]
+            if not targets:
+                continue
+            g2, org2, copies = _duplicate_op(g, origin, p, targets)
+            groups2 = partition(g2, row_resident=row_resident)
+            gof2 = {i: k for k, grp in enumerate(groups2) for i in grp}
+            # no value of a copy (this rewrite's or an earlier one's) is
+            # stored: every reader of a copy shares the copy's group
+            fused = all(gof2[j] == gof2[i]
+                        for i, o in enumerate(g2.ops) if o.output >= len(graph.tensors)
+                        for j, q in enumerate(g2.ops) if o.output in q.inputs)
+            if fused and plan_cost(g2, groups2) < cost:
+                g, origin, kept = g2, org2, True
+                break
+            blocked.add(origin[p])
+        if not kept:
+            return g, origin

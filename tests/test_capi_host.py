@@ -312,3 +312,28 @@ def test_row_resident_plans_match_the_oracle():
             n_red = sum(g.ops[i].op in ("row_sum", "row_mean") for i in plan.group_ops(k))
             assert geo["stages"] >= 1 and (n_red <= geo["stages"])
     assert merged >= 20
+
+
+def test_duplicate_plans_match_the_oracle():
+    """GTF_DUPLICATE: the library's rewritten program (op origins) and its
+    groups equal the oracle's duplicate() followed by partition(), with and
+    without the row-resident merge."""
+    from tests.test_oracle_partition import _f32_reduce_dags
+    graphs = [configs.layernorm_shared_graph(), configs.layernorm_shared_graph(37, 1000),
+              configs.layernorm_graph(), configs.c3_graph(64, 256, head_op=True)]
+    graphs += list(_f32_reduce_dags(23, 300)) + list(_broadcast_dags(31, 300))
+    changed = 0
+    for g in graphs:
+        for rr in (False, True):
+            plan = gtf.FusePlan(g, row_resident=rr, duplicate=True)
+            g2, origin = opart.duplicate(g, row_resident=rr)
+            assert plan.op_origin() == origin
+            assert plan.n_ops == len(g2.ops)
+            assert as_sets(plan.groups()) == as_sets(opart.partition(g2, row_resident=rr))
+            changed += g2 is not g
+            # internal tensors are never stored: the caller's arrays suffice
+            stored = set(plan.materialized())
+            want = {t for t in opart.stored_tensors(g2, opart.partition(g2, row_resident=rr))} | \
+                set(g.inputs()) | set(g.outputs())
+            assert stored == want and max(stored) < len(g.tensors)
+    assert changed >= 40

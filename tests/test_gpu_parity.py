@@ -623,3 +623,61 @@ def test_random_broadcast_dags_row_resident():
             _check_graph(gg, _inputs_for(gg, 200 + gi), modes=((True, True),))
         n += 1
     assert n >= 15
+
+
+# ---------------------------------------------------------------- duplicate fusion
+@pytest.mark.parametrize("rows,hidden", [(8192, 1024), (37, 1000), (3, 5)])
+@pytest.mark.parametrize("rr", [False, True])
+def test_duplicate_layernorm_is_the_hand_duplicated_one(rows, hidden, rr):
+    """x - mean written once, duplicated by the planner: the same groups,
+    launches and bits as the descriptor that writes it twice."""
+    shared = configs.layernorm_shared_graph(rows, hidden)
+    hand = configs.layernorm_graph(rows, hidden)
+    ins = configs.layernorm_inputs(shared, configs.c5_layer_seed(0) + 3)
+    plan = gtf.FusePlan(shared, row_resident=rr, duplicate=True)
+    assert plan.num_groups == (1 if rr else 3)
+    _, got = gpu_run(shared, ins, plan=plan)
+    _, ref = gpu_run(hand, ins, row_resident=rr)
+    y_s, y_h = _ids(shared)["y"], _ids(hand)["y"]
+    xc = _ids(shared)["xc"]
+    assert xc not in got                          # never stored
+    assert_bits_equal(got[y_s], ref[y_h])
+    # and against the oracle's evaluation of the rewritten program, given
+    # the GPU's statistics when they are stored
+    g2, _ = opart.duplicate(shared, row_resident=rr)
+    if not rr:
+        n = _ids(shared)
+        given = {n["mean"]: got[n["mean"]].reshape(rows, 1), n["var"]: got[n["var"]].reshape(rows, 1)}
+        groups = opart.partition(g2)
+        _, want = oev.run(g2, ins, stored=opart.stored_tensors(g2, groups), given=given)
+        assert_bits_equal(got[y_s], want[y_s])
+
+
+def test_random_dags_with_duplicate_fusion():
+    from tests.test_oracle_partition import _f32_reduce_dags
+    n = 0
+    for gi, g in enumerate(list(_f32_reduce_dags(23, 120)) + list(_broadcast_dags(31, 120))):
+        g2, _ = opart.duplicate(g)
+        if g2 is g:
+            continue
+        for R, C in [(3, 5), (5, 130), (300, 24)]:
+            gg = _reshape(g, R, C)
+            gg2, _ = opart.duplicate(gg)
+            ins = _inputs_for(gg, 500 + gi)
+            plan = gtf.FusePlan(gg, duplicate=True)
+            assert plan.n_ops == len(gg2.ops)
+            _, got = gpu_run(gg, ins, plan=plan)
+            groups = opart.partition(gg2)
+            vals, want = oev.run(gg2, ins, stored=opart.stored_tensors(gg2, groups))
+            big = max([float(np.nanmax(np.abs(v))) if v.size else 0.0 for v in vals.values()] + [1.0])
+            for t in gg.outputs():
+                prod = gg2.ops[gg2.producer(t)]  # its operand may now be a copy's value
+                if prod.op in ("row_sum", "row_mean"):
+                    assert_reduce_close(got[t], want[t], reduce_bound(vals[prod.inputs[0]], False), 1e-5)
+                elif gg.tensors[t].dtype == "bf16":
+                    assert_close_scaled(numerics.bf16_to_f32(got[t]), numerics.bf16_to_f32(want[t]),
+                                        2.0 ** -8, 1e-3 * big)
+                else:
+                    assert_close_scaled(got[t], want[t], 1e-5, big)
+        n += 1
+    assert n >= 20

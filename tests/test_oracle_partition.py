@@ -249,3 +249,152 @@ def test_row_resident_stage_limit():
         reds = [i for i in grp if g.ops[i].op == "row_mean"]
         assert len(reds) <= 4
     assert sorted(i for grp in groups for i in grp) == list(range(len(g.ops)))
+
+
+# ---------------------------------------------------------------- duplicate fusion
+def _canon(g):
+    """Each op's value as an expression tree over the graph's named inputs,
+    so graphs that compute the same things in another op order compare
+    equal."""
+    prod = {o.output: i for i, o in enumerate(g.ops)}
+    memo = {}
+
+    def of(t):
+        if t not in prod:
+            return ("in", g.tensors[t].name)
+        if t not in memo:
+            o = g.ops[prod[t]]
+            memo[t] = (o.op, o.imm, g.tensors[t].dtype, tuple(of(x) for x in o.inputs))
+        return memo[t]
+    return [of(o.output) for o in g.ops], of
+
+
+def test_plan_cost_counts_bytes_by_hand():
+    # c2: one group reading X, bias, R and writing y (bf16 [4,16], bias [16])
+    g = configs.c2_graph(4, 16)
+    assert pt.plan_cost(g, pt.partition(g)) == (2 * (3 * 64 + 16), 1)
+    # unfused: bias_add writes t (read by relu), relu writes u (read by add)
+    assert pt.plan_cost(g, pt.partition(g, fuse=False)) == (2 * (64 + 16 + 64) + 2 * (64 + 64)
+                                                            + 2 * (64 + 64 + 64), 3)
+
+
+def test_duplicate_layernorm_is_the_hand_duplicated_layernorm():
+    """x - mean written once is recomputed in both groups that read it: the
+    result computes exactly what the descriptor with x - mean written twice
+    computes, in the same three groups, at the same cost."""
+    for rr in (False, True):
+        shared = configs.layernorm_shared_graph(16, 64)
+        hand = configs.layernorm_graph(16, 64)
+        g2, origin = pt.duplicate(shared, row_resident=rr)
+        assert len(pt.partition(shared, row_resident=rr)) == (4 if not rr else 2)
+        ops2, of2 = _canon(g2)
+        opsh, ofh = _canon(hand)
+        assert sorted(map(repr, ops2)) == sorted(map(repr, opsh))
+        groups2 = {frozenset(repr(ops2[i]) for i in grp) for grp in pt.partition(g2, row_resident=rr)}
+        groupsh = {frozenset(repr(opsh[i]) for i in grp) for grp in pt.partition(hand, row_resident=rr)}
+        assert groups2 == groupsh
+        assert pt.plan_cost(g2, pt.partition(g2, row_resident=rr)) == \
+            pt.plan_cost(hand, pt.partition(hand, row_resident=rr))
+        # the copy of x - mean computes op 1 of the shared graph; the shared op is gone
+        assert origin.count(1) == 2 and len(g2.ops) == len(shared.ops) + 1
+        for i, o in enumerate(g2.ops):
+            assert (o.op, o.imm) == (shared.ops[origin[i]].op, shared.ops[origin[i]].imm)
+
+
+def test_duplicate_is_not_kept_when_it_moves_more_bytes():
+    """p = a + b (f32 inputs, bf16 result) read by three row sums in three
+    groups: recomputing p in each reads 8 bytes per element three times
+    instead of storing 2 and reading them back three times."""
+    g = Graph()
+    a = g.input("a", "f32", (8, 32))
+    b = g.input("b", "f32", (8, 32))
+    p = g.op("add", [a, b], "p", "bf16", (8, 32))
+    for k in range(3):
+        g.op("row_sum", [p], f"s{k}", "f32", (8, 1), role="out")
+    g2, origin = pt.duplicate(g)
+    assert g2 is g and origin == [0, 1, 2, 3]
+    # with a bf16 input and an f32 result the same rewrite pays off
+    h = Graph()
+    a = h.input("a", "bf16", (8, 32))
+    p = h.op("exp", [a], "p", "f32", (8, 32))
+    for k in range(3):
+        h.op("row_sum", [p], f"s{k}", "f32", (8, 1), role="out")
+    h2, origin = pt.duplicate(h)
+    assert origin == [0, 1, 0, 2, 0, 3] and len(pt.partition(h2)) == 3
+    assert pt.plan_cost(h2, pt.partition(h2)) == (3 * (2 * 256 + 4 * 8), 3)
+
+
+def test_duplicate_leaves_readers_in_the_same_group_alone():
+    g = configs.c3_graph(8, 64, head_op=True)  # the head's three readers share its group
+    g2, origin = pt.duplicate(g)
+    assert g2 is g and origin == list(range(len(g.ops)))
+
+
+def _f32_reduce_dags(seed, count):
+    """Small all-f32 DAGs with row sums, row and column operands and opaque
+    ops: values crossing groups are stored without rounding, so a
+    duplicated program computes the same bits."""
+    rng = np.random.default_rng(seed)
+    R, C = 3, 5
+    for _ in range(count):
+        g = Graph()
+        full = [g.input("x0", "f32", (R, C)), g.input("x1", "f32", (R, C))]
+        rowv = [g.input("r0", "f32", (R, 1))]
+        col = g.input("c0", "f32", (C,))
+        for i in range(int(rng.integers(2, 9))):
+            kind = int(rng.integers(0, 6))
+            pick = lambda xs: xs[int(rng.integers(len(xs)))]  # noqa: E731
+            if kind == 0:
+                full.append(g.op(["exp", "relu", "neg", "square"][int(rng.integers(4))], [pick(full)],
+                                 f"t{i}", "f32", (R, C), opaque=bool(rng.random() < 0.1)))
+            elif kind == 1:
+                full.append(g.op(["add", "mul", "sub"][int(rng.integers(3))], [pick(full), pick(full)],
+                                 f"t{i}", "f32", (R, C)))
+            elif kind == 2:
+                full.append(g.op("add", [pick(full), col], f"t{i}", "f32", (R, C)))
+            elif kind == 3:
+                full.append(g.op("mul", [pick(full), pick(rowv)], f"t{i}", "f32", (R, C)))
+            elif kind == 4:
+                rowv.append(g.op("row_sum", [pick(full)], f"t{i}", "f32", (R, 1)))
+            else:
+                rowv.append(g.op("add_imm", [pick(rowv)], f"t{i}", "f32", (R, 1), imm=0.5))
+        readers = {t for o in g.ops for t in o.inputs}
+        for o in g.ops:
+            t = o.output
+            if t not in readers or rng.random() < 0.1:
+                d = g.tensors[t]
+                g.tensors[t] = TensorDesc(d.name, d.dtype, d.shape, "out")
+        yield g
+
+
+def test_duplicate_preserves_values_and_never_raises_the_cost():
+    from oracle import evaluate as oev
+    changed = 0
+    for k, g in enumerate(_f32_reduce_dags(23, 400)):
+        for rr in (False, True):
+            g2, origin = pt.duplicate(g, row_resident=rr)
+            p1, p2 = pt.partition(g, row_resident=rr), pt.partition(g2, row_resident=rr)
+            assert pt.plan_cost(g2, p2) <= pt.plan_cost(g, p1)
+            if g2 is g:
+                continue
+            changed += 1
+            assert pt.plan_cost(g2, p2) < pt.plan_cost(g, p1)
+            assert g2.tensors[:len(g.tensors)] == g.tensors
+            for i, o in enumerate(g2.ops):
+                src = g.ops[origin[i]]
+                assert (o.op, o.imm, o.opaque) == (src.op, src.imm, src.opaque)
+                assert g2.tensors[o.output].shape == g.tensors[src.output].shape
+            # every copy shares a group with its single reader
+            gof = {i: j for j, grp in enumerate(p2) for i in grp}
+            for i, o in enumerate(g2.ops):
+                if o.output >= len(g.tensors):
+                    rd = [j for j, q in enumerate(g2.ops) if o.output in q.inputs]
+                    assert len(rd) == 1 and rd[0] > i and gof[i] == gof[rd[0]]
+            ins = {}
+            for j, t in enumerate(g.inputs()):
+                ins[t] = configs.tensor_values("f32", g.tensors[t].shape, "uniform", 900 + k, j, -1.5, 1.5)
+            _, want = oev.run(g, ins, stored=pt.stored_tensors(g, p1))
+            _, got = oev.run(g2, ins, stored=pt.stored_tensors(g2, p2))
+            for t in g.outputs():
+                assert np.array_equal(got[t].view(np.uint32), want[t].view(np.uint32))
+    assert changed >= 30

@@ -144,6 +144,26 @@ def layernorm_graph(rows: int = 8192, hidden: int = 1024, eps: float = LN_EPS) -
     return g
 
 
+def layernorm_shared_graph(rows: int = 8192, hidden: int = 1024, eps: float = LN_EPS) -> Graph:
+    """The same LayerNorm with x - mean written once and read twice (by the
+    square and by the normalisation): what duplicate fusion starts from."""
+    g = Graph()
+    X = g.input("X", "bf16", (rows, hidden))
+    gamma = g.input("gamma", "bf16", (hidden,))
+    beta = g.input("beta", "bf16", (hidden,))
+    mean = g.op("row_mean", [X], "mean", "f32", (rows, 1))
+    xc = g.op("sub", [X, mean], "xc", "bf16", (rows, hidden))
+    sq = g.op("square", [xc], "sq", "bf16", (rows, hidden))
+    var = g.op("row_mean", [sq], "var", "f32", (rows, 1))
+    ve = g.op("add_imm", [var], "var_eps", "f32", (rows, 1), imm=eps)
+    sd = g.op("sqrt", [ve], "std", "f32", (rows, 1))
+    rs = g.op("recip", [sd], "rstd", "f32", (rows, 1))
+    nrm = g.op("mul", [xc, rs], "norm", "bf16", (rows, hidden))
+    sc = g.op("mul", [nrm, gamma], "scaled", "bf16", (rows, hidden))
+    g.op("add", [sc, beta], "y", "bf16", (rows, hidden), role="out")
+    return g
+
+
 def gelu_graph(rows: int = 8192, ffn: int = 4096) -> Graph:
     g = Graph()
     A = g.input("A", "bf16", (rows, ffn))
