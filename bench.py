@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "joint", "ln"])
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "joint", "ln", "search"])
     ap.add_argument("--layers", type=int, default=12)
     ap.add_argument("--ln-variant", default="all",
                     choices=["all", "row_resident", "tvm_groups", "unfused", "shared_center",
@@ -254,8 +254,8 @@ def cpu_baseline_c5(target_s=12.0):
         seed = configs.c5_layer_seed(layers)
         ins = [f(g, seed) for f, g in zip(gen_in, gl)]
         t0 = time.perf_counter()
-        for g, i, s in zip(gl, ins, stored):
-            oev.outputs(g, oev.evaluate(g, i, s))
+        for g, i, s, p in zip(gl, ins, stored, parts):
+            oev.outputs(g, oev.evaluate(g, i, s, groups=p))
         dt += time.perf_counter() - t0
         nbytes += layer_bytes
         layers += 1
@@ -462,6 +462,8 @@ def run_config(torch, gtf, configs, args):
         return run_joint(torch, gtf, configs, args, res, gen)
     if w == "ln":
         return run_ln(torch, gtf, configs, args, res, gen)
+    if w == "search":
+        return run_search(torch, gtf, configs, args, res, gen)
     if w == "c1":
         g = configs.c1_graph()
         dists = {"x": ("uniform", -1, 1), "a": ("uniform", -1, 1), "b": ("uniform", -1, 1)}
@@ -641,6 +643,97 @@ def read_traffic(kernel, workload="c5"):
     if tj.get("source_hash") != _kernel_hash():
         return None
     return tj["kernels"].get(kernel)
+
+
+class MeasuredCost:
+    """Cost of a candidate plan for the search: the sum over its groups of
+    each group's launch time, measured with HIP events around `reps`
+    back-to-back launches on one set of device tensors (every tensor of the
+    graph allocated once), cached per group (its ops' origins and the
+    tensors it touches)."""
+
+    def __init__(self, torch, graph, gen, dists, reps=10):
+        self.torch, self.reps = torch, reps
+        self.dev = {}
+        for t, d in enumerate(graph.tensors):
+            kind, a, b = dists.get(d.name, ("normal", 0.0, 1.0))
+            self.dev[t] = make_tensor(torch, gen, d, kind, a, b)
+        self.cache = {}
+        self.measured = 0
+
+    def __call__(self, plan):
+        torch = self.torch
+        origin = plan.op_origin()
+        total = 0.0
+        for k in range(plan.num_groups):
+            key = (tuple(sorted(origin[i] for i in plan.group_ops(k))), tuple(plan.group_tensors(k)))
+            if key not in self.cache:
+                run = plan.launcher(k, self.dev)
+                run()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(self.reps):
+                    run()
+                e1.record()
+                torch.cuda.synchronize()
+                self.cache[key] = e0.elapsed_time(e1) / self.reps
+                self.measured += 1
+            total += self.cache[key]
+        return total
+
+
+def time_plan(torch, gtf, graph, plan, gen, dists, steps, warmup):
+    """A plan's time per run as HIP-graph replays over rotation sets."""
+    nbytes = sum(group_bytes(graph, plan))
+    k = _rotation_sets(nbytes)
+    sets = [alloc_graph(torch, gtf, graph, plan, gen, dists) for _ in range(k)]
+
+    def rotation():
+        for st in sets:
+            plan.run(st)
+    g = _captured(torch, rotation)
+    ms, _ = time_steps(torch, g.replay, steps, warmup)
+    del sets
+    return ms / k, nbytes
+
+
+def run_search(torch, gtf, configs, args, res, gen):
+    """DisCo's backtracking search (alpha 1.05, beta 10, 1000 steps without
+    improvement) on the c5 LayerNorm with x - mean written once, costed by
+    measured launch times, against the rule-based plans of the same graph.
+    Every plan is then timed the same way: HIP-graph replays over rotation
+    sets."""
+    import time as _time
+    g = configs.layernorm_shared_graph()
+    cost = MeasuredCost(torch, g, gen, LN_D)
+    t0 = _time.perf_counter()
+    best, st = gtf.search(g, cost, seed=int(os.environ.get("GTF_SEARCH_SEED", "1")))
+    wall = _time.perf_counter() - t0
+    del cost
+    torch.cuda.empty_cache()
+    variants = {"searched": best, "tvm_groups": gtf.FusePlan(g),
+                "duplicate": gtf.FusePlan(g, duplicate=True),
+                "duplicate_row_resident": gtf.FusePlan(g, duplicate=True, row_resident=True),
+                "unfused": gtf.FusePlan(g, fuse=False)}
+    out = {}
+    for name, plan in variants.items():
+        ms, nbytes = time_plan(torch, gtf, g, plan, gen, LN_D, args.steps, args.warmup)
+        out[name] = {"ms_per_step": round(ms, 5), "launches": plan.num_groups, "bytes": nbytes,
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+    s = out["searched"]
+    res.update({"value": s["gbs"], "ms_per_step": s["ms_per_step"], "dtype": "bf16",
+                "config": {"workload": "search: DisCo backtracking search over fusion plans of the "
+                                       "LayerNorm bf16[8192,1024] with x - mean written once, "
+                                       "measured launch times as the cost",
+                           "alpha": 1.05, "beta": 10, "max_stall": 1000,
+                           "bytes_per_step": s["bytes"]},
+                "search": {"steps": st["steps"], "evaluations": st["evaluations"],
+                           "start_cost_ms": round(st["start_cost"], 5),
+                           "best_cost_ms": round(st["best_cost"], 5), "wall_s": round(wall, 2),
+                           "groups": best.groups(), "op_origin": best.op_origin()},
+                "speedup_vs_tvm_groups": round(out["tvm_groups"]["ms_per_step"] / s["ms_per_step"], 3),
+                "timing": "graph replays over the rotation sets", "variants": out})
+    return res
 
 
 def _captured(torch, fn):

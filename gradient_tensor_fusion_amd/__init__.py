@@ -24,7 +24,8 @@ from typing import Dict, List, Sequence
 from . import _capi as C
 from ._capi import GtfError
 
-__all__ = ["FusePlan", "FuseMulti", "BucketPlan", "device_copy", "GtfError", "PATTERN_NAMES"]
+__all__ = ["FusePlan", "FuseMulti", "BucketPlan", "device_copy", "search", "GtfError",
+           "PATTERN_NAMES"]
 
 PATTERN_NAMES = {0: "kElemWise", 1: "kBroadcast", 2: "kInjective", 3: "kCommReduce",
                  4: "kOutEWiseFusable", 7: "kTuple", 8: "kOpaque"}
@@ -71,6 +72,52 @@ class FusePlan:
         n = c_int32()
         C.check(C.lib().fuse_plan_num_ops(self._h, byref(n)))
         self.n_ops = n.value  # ops of the plan's program (copies included)
+
+    @classmethod
+    def _adopt(cls, graph, h, keep) -> "FusePlan":
+        self = cls.__new__(cls)
+        self.graph = graph
+        self.n_tensors = len(graph.tensors)
+        self._tens, self._ops = keep
+        self._h = h
+        n = c_int32()
+        C.check(C.lib().fuse_plan_num_ops(self._h, byref(n)))
+        self.n_ops = n.value
+        return self
+
+    @classmethod
+    def grouped(cls, graph, group_of: Sequence[int]) -> "FusePlan":
+        """fuse_plan_create_grouped: ops with equal labels form one group."""
+        desc, tens, ops = _program_desc(graph)
+        arr = (c_int32 * max(1, len(graph.ops)))(*[int(x) for x in group_of])
+        h = c_void_p()
+        C.check(C.lib().fuse_plan_create_grouped(byref(desc), arr, byref(h)))
+        return cls._adopt(graph, h, (tens, ops))
+
+    def program(self):
+        """fuse_plan_program: the plan's program as a Graph (the graph's
+        tensors, then internal ones named "~<id>"; its ops in run order)."""
+        from workloads.graph import Graph, OpDesc, TensorDesc
+        nt, no = c_int32(), c_int32()
+        C.check(C.lib().fuse_plan_program(self._h, None, 0, byref(nt), None, 0, byref(no)))
+        tens = (C.TensorDesc * max(1, nt.value))()
+        ops = (C.OpDesc * max(1, no.value))()
+        C.check(C.lib().fuse_plan_program(self._h, tens, nt.value, byref(nt), ops, no.value,
+                                          byref(no)))
+        dt = {v: k for k, v in C.DTYPE.items()}
+        rl = {v: k for k, v in C.ROLE.items()}
+        op_names = {v: k for k, v in C.OPCODE.items()}
+        g = Graph()
+        for t in range(nt.value):
+            d = tens[t]
+            name = self.graph.tensors[t].name if t < self.n_tensors else f"~{t}"
+            g.tensors.append(TensorDesc(name, dt[d.dtype], tuple(int(d.shape[k]) for k in range(d.rank)),
+                                        rl[d.role]))
+        for i in range(no.value):
+            d = ops[i]
+            g.ops.append(OpDesc(op_names[d.opcode], tuple(int(d.inp[k]) for k in range(d.n_in)),
+                                int(d.out), float(d.imm), bool(d.flags & C.OPF_OPAQUE)))
+        return g
 
     def op_origin(self) -> List[int]:
         """Per program op, the graph op it computes."""
@@ -159,6 +206,42 @@ class FusePlan:
                 C.check(status)
         run.tensors = keep
         return run
+
+
+class _Candidate(FusePlan):
+    """A candidate plan handed to a search cost callback: borrowed, valid
+    only during the call."""
+
+    def __del__(self):
+        pass
+
+
+def search(graph, cost, alpha: float = 1.05, beta: int = 10, max_stall: int = 1000,
+           seed: int = 0, max_steps: int = 0):
+    """fuse_plan_search: DisCo's backtracking search over fusion plans.
+    cost(candidate) gets a FusePlan valid only during the call (runnable on
+    the graph's tensors) and returns its cost.  Returns (best FusePlan,
+    stats dict)."""
+    desc, tens, ops = _program_desc(graph)
+    err = []
+
+    def cb(_ctx, handle):
+        try:
+            cand = _Candidate._adopt(graph, c_void_p(handle), (tens, ops))
+            return float(cost(cand))
+        except BaseException as e:  # reported after the search stops
+            err.append(e)
+            return float("nan")
+    fn = C.COST_FN(cb)
+    prm = C.SearchParams(alpha, beta, max_stall, seed, max_steps, 0)
+    st = C.SearchStats()
+    h = c_void_p()
+    status = C.lib().fuse_plan_search(byref(desc), byref(prm), fn, None, byref(h), byref(st))
+    if err:
+        raise err[0]
+    C.check(status)
+    stats = {name: getattr(st, name) for name, _ in C.SearchStats._fields_}
+    return FusePlan._adopt(graph, h, (tens, ops)), stats
 
 
 class FuseMulti:

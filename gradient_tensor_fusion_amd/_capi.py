@@ -8,7 +8,8 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+from ctypes import (CFUNCTYPE, POINTER, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t,
+                    c_uint32, c_uint64, c_void_p)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgtf.so")
@@ -36,6 +37,7 @@ DUPLICATE = 4
 EXPORTED = (
     "fuse_plan_create", "fuse_plan_num_groups", "fuse_plan_group_info", "fuse_plan_op_info",
     "fuse_plan_num_ops", "fuse_plan_op_origin", "fuse_plan_group_tensors",
+    "fuse_plan_create_grouped", "fuse_plan_search", "fuse_plan_program",
     "fuse_plan_group_geometry",
     "fuse_plan_is_materialized", "fuse_group_run", "fuse_plan_run", "fuse_plan_destroy",
     "fuse_multi_create", "fuse_multi_workspace_bytes", "fuse_multi_bind", "fuse_multi_run",
@@ -69,6 +71,19 @@ class ProgramDesc(ctypes.Structure):
                 ("tensors", POINTER(TensorDesc)), ("n_ops", c_int32), ("ops", POINTER(OpDesc))]
 
 
+class SearchParams(ctypes.Structure):
+    _fields_ = [("alpha", c_double), ("beta", c_int32), ("max_stall", c_int32), ("seed", c_uint64),
+                ("max_steps", c_int32), ("reserved", c_int32)]
+
+
+class SearchStats(ctypes.Structure):
+    _fields_ = [("steps", c_int64), ("evaluations", c_int64), ("queue_left", c_int64),
+                ("start_cost", c_double), ("best_cost", c_double)]
+
+
+COST_FN = CFUNCTYPE(c_double, c_void_p, c_void_p)
+
+
 class GtfError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"gtf status {status}: {msg}")
@@ -93,6 +108,11 @@ def lib() -> ctypes.CDLL:
         L.fuse_plan_op_info.argtypes = [vp, POINTER(c_int32), POINTER(c_int32)]
         L.fuse_plan_num_ops.argtypes = [vp, POINTER(c_int32)]
         L.fuse_plan_op_origin.argtypes = [vp, POINTER(c_int32)]
+        L.fuse_plan_program.argtypes = [vp, POINTER(TensorDesc), c_int32, POINTER(c_int32),
+                                        POINTER(OpDesc), c_int32, POINTER(c_int32)]
+        L.fuse_plan_create_grouped.argtypes = [POINTER(ProgramDesc), POINTER(c_int32), POINTER(vp)]
+        L.fuse_plan_search.argtypes = [POINTER(ProgramDesc), POINTER(SearchParams), COST_FN, vp,
+                                       POINTER(vp), POINTER(SearchStats)]
         L.fuse_plan_group_tensors.argtypes = [vp, c_int32, POINTER(c_int32), c_int32,
                                               POINTER(c_int32)]
         L.fuse_plan_is_materialized.argtypes = [vp, c_int32, POINTER(c_int32)]

@@ -185,6 +185,67 @@ int fuse_plan_create(const gtf_program_desc* desc, uint32_t flags, gtf_fuse_plan
   return GTF_OK;
 }
 
+int fuse_plan_create_grouped(const gtf_program_desc* desc, const int32_t* group_of,
+                             gtf_fuse_plan** out) {
+  if (out == nullptr) return fail(GTF_E_INVALID, "out is NULL");
+  *out = nullptr;
+  gtf_fuse_plan* h = new (std::nothrow) gtf_fuse_plan();
+  if (h == nullptr) return fail(GTF_E_LIMIT, "out of host memory");
+  int st = validate(desc, &h->p);
+  if (st == GTF_OK && group_of == nullptr && !h->p.ops.empty())
+    st = fail(GTF_E_INVALID, "group_of is NULL");
+  if (st == GTF_OK) {
+    std::vector<int> labels(group_of, group_of + h->p.ops.size());
+    st = build_grouped_plan(&h->p, labels);
+  }
+  if (st != GTF_OK) {
+    delete h;
+    return st;
+  }
+  *out = h;
+  return GTF_OK;
+}
+
+int fuse_plan_search(const gtf_program_desc* desc, const gtf_search_params* params,
+                     gtf_cost_fn cost, void* ctx, gtf_fuse_plan** best,
+                     gtf_search_stats* stats) {
+  if (best == nullptr || params == nullptr || cost == nullptr)
+    return fail(GTF_E_INVALID, "NULL argument");
+  *best = nullptr;
+  gtf_fuse_plan* h = new (std::nothrow) gtf_fuse_plan();
+  if (h == nullptr) return fail(GTF_E_LIMIT, "out of host memory");
+  int st = validate(desc, &h->p);
+  if (st == GTF_OK) {
+    SearchParams prm;
+    prm.alpha = params->alpha;
+    prm.beta = params->beta;
+    prm.max_stall = params->max_stall;
+    prm.seed = params->seed;
+    prm.max_steps = params->max_steps;
+    SearchStats ss;
+    gtf_fuse_plan cand;
+    st = search_plan(&h->p, prm,
+                     [&](const FusePlan& fp) {
+                       cand.p = fp;
+                       return cost(ctx, &cand);
+                     },
+                     &ss);
+    if (st == GTF_OK && stats) {
+      stats->steps = ss.steps;
+      stats->evaluations = ss.evaluations;
+      stats->queue_left = ss.queue_left;
+      stats->start_cost = ss.start_cost;
+      stats->best_cost = ss.best_cost;
+    }
+  }
+  if (st != GTF_OK) {
+    delete h;
+    return st;
+  }
+  *best = h;
+  return GTF_OK;
+}
+
 int fuse_plan_num_groups(const gtf_fuse_plan* plan, int32_t* n) {
   if (plan == nullptr || n == nullptr) return fail(GTF_E_INVALID, "NULL argument");
   *n = (int32_t)plan->p.groups.size();
@@ -213,6 +274,41 @@ int fuse_plan_group_info(const gtf_fuse_plan* plan, int32_t g, int32_t* op_ids, 
   if (op_ids) {
     if (cap < (int32_t)G.ops.size()) return fail(GTF_E_LIMIT, "op_ids capacity too small");
     for (size_t k = 0; k < G.ops.size(); ++k) op_ids[k] = G.ops[k];
+  }
+  return GTF_OK;
+}
+
+int fuse_plan_program(const gtf_fuse_plan* plan, gtf_tensor_desc* tensors, int32_t cap_tensors,
+                      int32_t* n_tensors, gtf_op_desc* ops, int32_t cap_ops, int32_t* n_ops) {
+  if (plan == nullptr) return fail(GTF_E_INVALID, "plan is NULL");
+  const FusePlan& p = plan->p;
+  if (n_tensors) *n_tensors = (int32_t)p.tensors.size();
+  if (n_ops) *n_ops = (int32_t)p.ops.size();
+  if (tensors) {
+    if (cap_tensors < (int32_t)p.tensors.size()) return fail(GTF_E_LIMIT, "tensor capacity too small");
+    for (size_t t = 0; t < p.tensors.size(); ++t) {
+      const TensorInfo& ti = p.tensors[t];
+      gtf_tensor_desc& d = tensors[t];
+      d.dtype = ti.dtype;
+      d.rank = ti.rank;
+      d.shape[0] = ti.rank == 1 ? ti.C : ti.R;
+      d.shape[1] = ti.rank == 1 ? 0 : ti.C;
+      d.role = ti.role;
+      d.reserved = 0;
+    }
+  }
+  if (ops) {
+    if (cap_ops < (int32_t)p.ops.size()) return fail(GTF_E_LIMIT, "op capacity too small");
+    for (size_t i = 0; i < p.ops.size(); ++i) {
+      const OpInfo& o = p.ops[i];
+      gtf_op_desc& d = ops[i];
+      d.opcode = o.opcode;
+      d.n_in = o.n_in;
+      for (int k = 0; k < 3; ++k) d.in[k] = k < o.n_in ? o.in[k] : 0;
+      d.out = o.out;
+      d.imm = o.imm;
+      d.flags = o.flags;
+    }
   }
   return GTF_OK;
 }

@@ -11,7 +11,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <map>
+#include <queue>
 #include <set>
 #include <string>
 #include <vector>
@@ -1237,27 +1239,33 @@ void duplicate_pass(FusePlan* p, bool row_resident) {
 
 }  // namespace
 
-int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident, bool duplicate) {
+namespace {
+void init_origin(FusePlan* p) {
   if (p->origin.size() != p->ops.size()) {
     p->n_desc_ops = (int)p->ops.size();
     p->n_desc_tensors = (int)p->tensors.size();
     p->origin.resize(p->ops.size());
     for (size_t i = 0; i < p->ops.size(); ++i) p->origin[i] = (int)i;
   }
+}
+}  // namespace
+
+int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident, bool duplicate) {
+  init_origin(p);
   annotate(p);
   if (fuse && duplicate) duplicate_pass(p, row_resident);
-  const int n = (int)p->ops.size();
-  const auto gl0 = partition_groups(*p, fuse, row_resident);
-  std::vector<std::vector<int>> gl;
+  return finish_plan(p, partition_groups(*p, fuse, row_resident));
+}
+
+// Order the groups by their dependencies, compile each, and mark the
+// tensors that go through memory.
+int finish_plan(FusePlan* p, const std::vector<std::vector<int>>& gl) {
   std::vector<int> gpat;
-  for (const auto& g : gl0) {
-    gl.push_back(g);
+  for (const auto& g : gl) {
     int pat = 0;
     for (int i : g) pat = std::max(pat, p->ops[i].pattern);
     gpat.push_back(pat);
   }
-  (void)n;
-  // order the groups by their dependencies
   std::vector<int> owner(p->tensors.size(), -1);
   for (size_t g = 0; g < gl.size(); ++g)
     for (int i : gl[g]) owner[p->ops[i].out] = (int)g;
@@ -1325,6 +1333,290 @@ int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident, bool duplicate) {
                      a.prog[k].imm);
     }
   }
+  return GTF_OK;
+}
+
+// ================================================================ explicit groupings and search
+namespace {
+
+// Groups from per-op labels, in order of each label's first op.
+std::vector<std::vector<int>> groups_from_labels(const std::vector<int>& labels) {
+  std::vector<std::vector<int>> gl;
+  std::map<int, int> index;
+  for (size_t i = 0; i < labels.size(); ++i) {
+    auto it = index.find(labels[i]);
+    if (it == index.end()) {
+      index[labels[i]] = (int)gl.size();
+      gl.push_back({(int)i});
+    } else {
+      gl[it->second].push_back((int)i);
+    }
+  }
+  return gl;
+}
+
+// A valid plan: an acyclic group graph (so every group is convex), every
+// group within the op limit and compilable (argument limit, shapes, stages
+// and the kernel's resources).
+bool plan_ok(const FusePlan& p, const std::vector<int>& labels, std::string* why) {
+  const auto gl = groups_from_labels(labels);
+  std::map<int, int> gidx;
+  for (size_t g = 0; g < gl.size(); ++g) gidx[labels[gl[g][0]]] = (int)g;
+  for (const auto& g : gl) {
+    if ((int)g.size() > GTF_MAX_GROUP_OPS) {
+      if (why) *why = "group over the op limit";
+      return false;
+    }
+    if (!compile_group(p, g, nullptr, why)) return false;
+  }
+  std::vector<int> owner(p.tensors.size(), -1);
+  for (size_t i = 0; i < p.ops.size(); ++i) owner[p.ops[i].out] = gidx[labels[i]];
+  std::vector<std::set<int>> succ(gl.size());
+  for (size_t j = 0; j < p.ops.size(); ++j)
+    for (int k = 0; k < p.ops[j].n_in; ++k) {
+      const int o = owner[p.ops[j].in[k]];
+      const int gj = gidx[labels[j]];
+      if (o >= 0 && o != gj) succ[o].insert(gj);
+    }
+  std::vector<int> indeg(gl.size(), 0);
+  for (const auto& ss : succ)
+    for (int b : ss) ++indeg[b];
+  std::vector<int> ready;
+  for (size_t g = 0; g < gl.size(); ++g)
+    if (indeg[g] == 0) ready.push_back((int)g);
+  size_t seen = 0;
+  while (!ready.empty()) {
+    const int a = ready.back();
+    ready.pop_back();
+    ++seen;
+    for (int b : succ[a])
+      if (--indeg[b] == 0) ready.push_back(b);
+  }
+  if (seen != gl.size()) {
+    if (why) *why = "groups depend on each other in a cycle";
+    return false;
+  }
+  return true;
+}
+
+// SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014): a Weyl sequence mixed by two xor-shift-multiply
+// rounds; below(n) is the next output modulo n.
+struct SplitMix64 {
+  uint64_t state;
+  explicit SplitMix64(uint64_t seed) : state(seed) {}
+  uint64_t next() {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }
+  int below(int n) { return (int)(next() % (uint64_t)n); }
+};
+
+struct SearchState {
+  FusePlan prog;            // ops, tensors, origin (no groups)
+  std::vector<int> labels;  // group label per op
+};
+
+std::vector<int> predecessors(const FusePlan& p, int v) {
+  std::vector<int> prod(p.tensors.size(), -1);
+  for (size_t i = 0; i < p.ops.size(); ++i) prod[p.ops[i].out] = (int)i;
+  std::set<int> ps;
+  for (int k = 0; k < p.ops[v].n_in; ++k)
+    if (prod[p.ops[v].in[k]] >= 0) ps.insert(prod[p.ops[v].in[k]]);
+  return std::vector<int>(ps.begin(), ps.end());
+}
+
+int readers_of_tensor(const FusePlan& p, int t) {
+  int n = 0;
+  for (const OpInfo& o : p.ops) {
+    bool reads = false;
+    for (int k = 0; k < o.n_in; ++k)
+      if (o.in[k] == t) reads = true;
+    n += reads;
+  }
+  return n;
+}
+
+// Copy op pi right before op v; v reads the copy, which joins v's group.
+SearchState with_copy(const SearchState& s, int pi, int v) {
+  SearchState c;
+  c.prog.n_desc_ops = s.prog.n_desc_ops;
+  c.prog.n_desc_tensors = s.prog.n_desc_tensors;
+  c.prog.tensors = s.prog.tensors;
+  TensorInfo ti = s.prog.tensors[s.prog.ops[pi].out];
+  ti.role = GTF_ROLE_TMP;
+  c.prog.tensors.push_back(ti);
+  const int nt = (int)c.prog.tensors.size() - 1;
+  for (size_t j = 0; j < s.prog.ops.size(); ++j) {
+    if ((int)j == v) {
+      OpInfo cp = s.prog.ops[pi];
+      cp.out = nt;
+      c.prog.ops.push_back(cp);
+      c.prog.origin.push_back(s.prog.origin[pi]);
+      c.labels.push_back(s.labels[v]);
+      OpInfo r = s.prog.ops[v];
+      for (int k = 0; k < r.n_in; ++k)
+        if (r.in[k] == s.prog.ops[pi].out) r.in[k] = nt;
+      c.prog.ops.push_back(r);
+    } else {
+      c.prog.ops.push_back(s.prog.ops[j]);
+    }
+    c.prog.origin.push_back(s.prog.origin[j]);
+    c.labels.push_back(s.labels[j]);
+  }
+  annotate(&c.prog);
+  return c;
+}
+
+// One application of DisCo's method (i) (dup false: non-duplicate fusion)
+// or (ii) (dup true: duplicate fusion).  v is drawn over the ops that have
+// a predecessor op in another group, p over those predecessors (both in
+// program order).  A move whose result is not a valid plan is not applied.
+void fuse_move(SearchState* s, SplitMix64* rng, bool dup) {
+  // v: an op with a predecessor op in another group; p: one of those
+  const int n = (int)s->prog.ops.size();
+  std::vector<std::vector<int>> cross(n);
+  std::vector<int> eligible;
+  for (int v = 0; v < n; ++v) {
+    for (int q : predecessors(s->prog, v))
+      if (s->labels[q] != s->labels[v]) cross[v].push_back(q);
+    if (!cross[v].empty()) eligible.push_back(v);
+  }
+  if (eligible.empty()) return;
+  const int v = eligible[rng->below((int)eligible.size())];
+  const int pi = cross[v][rng->below((int)cross[v].size())];
+  if (dup && readers_of_tensor(s->prog, s->prog.ops[pi].out) > 1) {
+    SearchState c = with_copy(*s, pi, v);
+    if (plan_ok(c.prog, c.labels, nullptr)) *s = std::move(c);
+  } else {
+    std::vector<int> lab = s->labels;
+    const int lp = lab[pi], lv = lab[v];
+    for (int& x : lab)
+      if (x == lp) x = lv;
+    if (plan_ok(s->prog, lab, nullptr)) s->labels.swap(lab);
+  }
+}
+
+// A plan's identity: its program and its grouping, labels renumbered in
+// order of first appearance.
+std::string state_key(const SearchState& s) {
+  std::string k;
+  auto put = [&](const void* d, size_t n) { k.append((const char*)d, n); };
+  for (const OpInfo& o : s.prog.ops) {
+    put(&o.opcode, sizeof o.opcode);
+    put(&o.n_in, sizeof o.n_in);
+    put(o.in, sizeof o.in);
+    put(&o.out, sizeof o.out);
+    put(&o.imm, sizeof o.imm);
+    put(&o.flags, sizeof o.flags);
+  }
+  std::map<int, int> ren;
+  for (int x : s.labels) {
+    auto it = ren.find(x);
+    const int r = it == ren.end() ? (ren[x] = (int)ren.size()) : it->second;
+    put(&r, sizeof r);
+  }
+  return k;
+}
+
+}  // namespace
+
+int build_grouped_plan(FusePlan* p, const std::vector<int>& labels) {
+  init_origin(p);
+  annotate(p);
+  if (labels.size() != p->ops.size()) return fail(GTF_E_INVALID, "one group label per op");
+  for (int x : labels)
+    if (x < 0) return fail(GTF_E_INVALID, "group labels must be >= 0");
+  std::string why;
+  if (!plan_ok(*p, labels, &why)) return fail(GTF_E_INVALID, "grouping not runnable: " + why);
+  return finish_plan(p, groups_from_labels(labels));
+}
+
+// DisCo's backtracking search (its "Strategy Maker"): a queue of candidate
+// plans ordered by cost (ties by insertion order), initially the program
+// with every op its own launch.  Each step dequeues the cheapest, and for
+// method (i) and then method (ii) applies that method to it n times (n drawn
+// from 0..beta), costs the result once, keeps it as the best when cheaper,
+// and enqueues it when its cost is at most alpha times the best.  Ends when the queue is empty, the
+// best has not changed for max_stall steps, or after max_steps steps (0: no
+// bound).  Method (iii), combining AllReduce instructions, has nothing to
+// act on with one GPU.
+int search_plan(FusePlan* p, const SearchParams& prm,
+                const std::function<double(const FusePlan&)>& cost, SearchStats* st) {
+  init_origin(p);
+  annotate(p);
+  if (!(prm.alpha >= 1.0) || prm.beta < 0 || prm.max_stall < 1 || prm.max_steps < 0)
+    return fail(GTF_E_INVALID, "search parameters: alpha >= 1, beta >= 0, max_stall >= 1");
+  SplitMix64 rng(prm.seed);
+  std::vector<SearchState> states;
+  SearchState start;
+  start.prog.tensors = p->tensors;
+  start.prog.ops = p->ops;
+  start.prog.origin = p->origin;
+  start.prog.n_desc_ops = p->n_desc_ops;
+  start.prog.n_desc_tensors = p->n_desc_tensors;
+  start.prog.ipdom = p->ipdom;
+  for (size_t i = 0; i < p->ops.size(); ++i) start.labels.push_back((int)i);
+  auto evaluate = [&](const SearchState& s, double* c) -> int {
+    FusePlan fp = s.prog;
+    int rc = finish_plan(&fp, groups_from_labels(s.labels));
+    if (rc != GTF_OK) return rc;
+    *c = cost(fp);
+    if (!(*c >= 0.0)) return fail(GTF_E_INVALID, "cost callback returned a negative or NaN cost");
+    return GTF_OK;
+  };
+  double c0 = 0.0;
+  int rc = evaluate(start, &c0);
+  if (rc != GTF_OK) return rc;
+  states.push_back(start);
+  typedef std::pair<double, int64_t> Key;  // (cost, insertion tick); the state index is the tick
+  std::priority_queue<Key, std::vector<Key>, std::greater<Key>> queue;
+  queue.push({c0, 0});
+  std::set<std::string> seen{state_key(start)};
+  SearchState best_state = start;
+  int64_t stall = 0, steps = 0, evals = 0;
+  double c_best = c0;
+  while (!queue.empty() && stall < prm.max_stall && (prm.max_steps == 0 || steps < prm.max_steps)) {
+    const int64_t h = queue.top().second;
+    queue.pop();
+    ++steps;
+    bool improved = false;
+    for (int dup = 0; dup < 2; ++dup) {
+      SearchState cand = states[h];
+      const int n = rng.below(prm.beta + 1);
+      for (int k = 0; k < n; ++k) fuse_move(&cand, &rng, dup != 0);
+      double cc = 0.0;
+      rc = evaluate(cand, &cc);
+      if (rc != GTF_OK) return rc;
+      ++evals;
+      if (cc < c_best) {
+        c_best = cc;
+        improved = true;
+        best_state = cand;
+      }
+      // a plan enqueued before is not enqueued again
+      if (cc <= prm.alpha * c_best && seen.insert(state_key(cand)).second) {
+        queue.push({cc, (int64_t)states.size()});
+        states.push_back(std::move(cand));
+      }
+    }
+    stall = improved ? 0 : stall + 1;
+  }
+  if (st) {
+    st->steps = steps;
+    st->evaluations = evals;
+    st->queue_left = (int64_t)queue.size();
+    st->start_cost = c0;
+    st->best_cost = c_best;
+  }
+  const SearchState& b = best_state;
+  FusePlan out = b.prog;
+  rc = finish_plan(&out, groups_from_labels(b.labels));
+  if (rc != GTF_OK) return rc;
+  *p = std::move(out);
   return GTF_OK;
 }
 

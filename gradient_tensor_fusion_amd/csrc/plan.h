@@ -3,6 +3,7 @@
 
 #include <stdint.h>
 
+#include <functional>
 #include <string>
 #include <vector>
 
@@ -66,6 +67,31 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
                    std::string* why);
 
 int build_fuse_plan(FusePlan* p, bool fuse, bool row_resident = false, bool duplicate = false);
+
+// Order the groups (member lists) by their dependencies, compile each and
+// mark the tensors that go through memory.
+int finish_plan(FusePlan* p, const std::vector<std::vector<int>>& groups);
+
+// A plan from an explicit grouping (one label per op; equal labels share a
+// group), refused unless the group graph is acyclic and every group runs.
+int build_grouped_plan(FusePlan* p, const std::vector<int>& labels);
+
+struct SearchParams {
+  double alpha = 1.05;
+  int beta = 10;
+  int max_stall = 1000;
+  uint64_t seed = 0;
+  int max_steps = 0;
+};
+struct SearchStats {
+  int64_t steps = 0, evaluations = 0, queue_left = 0;
+  double start_cost = 0.0, best_cost = 0.0;
+};
+
+// DisCo's backtracking search over fusion plans; on success *p is the best
+// plan found (its program may hold duplicated ops).
+int search_plan(FusePlan* p, const SearchParams& prm,
+                const std::function<double(const FusePlan&)>& cost, SearchStats* st);
 
 struct BucketPlan {
   int dtype = 0;

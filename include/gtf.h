@@ -178,6 +178,65 @@ typedef struct gtf_bucket_plan gtf_bucket_plan;
  * *out is set to NULL. */
 int fuse_plan_create(const gtf_program_desc* desc, uint32_t flags, gtf_fuse_plan** out);
 
+/* A plan from an explicit grouping: group_of[i] (>= 0) labels descriptor
+ * op i; ops with equal labels form one group.  Refused (GTF_E_INVALID, with
+ * the reason) unless the group graph is acyclic, which makes every group
+ * convex, and every group is within the op limit and runs as one launch
+ * (argument limit, one broadcast domain, reduction stages, the kernel's
+ * registers, LDS and instruction buffer).  This is how a searched or
+ * hand-made plan outside the fusion rules is given to the library. */
+int fuse_plan_create_grouped(const gtf_program_desc* desc, const int32_t* group_of,
+                             gtf_fuse_plan** out);
+
+/* DisCo's backtracking search over fusion plans (DisCo, "Strategy Maker";
+ * strategy space of its Sec. 3.2).  A queue of candidate plans ordered by
+ * cost (ties: insertion order) starts with the program unfused, every op
+ * its own launch.  Each step:
+ *  - dequeue the cheapest plan H;
+ *  - for method (i) and then method (ii), make one candidate by applying
+ *    that method to H n times, n drawn from 0..beta:
+ *    - (i) non-duplicate fusion: a random op v among those with a
+ *      predecessor op in another group, and a random such predecessor p;
+ *      p's group merges into v's group;
+ *    - (ii) duplicate fusion: the same, but when p has other readers, a copy
+ *      of p joins v's group and feeds v instead;
+ *    - a move whose result is not a valid plan (as fuse_plan_create_grouped
+ *      checks it) is not applied;
+ *  - cost each candidate once through the caller's callback;
+ *  - keep it as the best when it is cheaper;
+ *  - enqueue it when its cost is at most alpha times the best.
+ * The search ends when the queue is empty, the best has not changed for
+ * max_stall steps, or after max_steps steps (0: unbounded).  Method (iii),
+ * combining AllReduce instructions, has nothing to act on with one GPU and
+ * no AllReduce.
+ * Random numbers come from SplitMix64 (Steele, Lea and Flood, OOPSLA 2014)
+ * seeded with `seed`; draws per step: n for (i), each move's v then p, n
+ * for (ii), each move's v then p.  A step without a new best counts
+ * towards max_stall.
+ * The callback gets a compiled candidate plan, valid only during the call
+ * and runnable on the descriptor's tensors.  It returns the candidate's
+ * cost, e.g. its measured time; a negative or NaN value stops the search
+ * with GTF_E_INVALID.  On success *best is the best plan (destroy it with
+ * fuse_plan_destroy); its program may hold copies (fuse_plan_op_origin).
+ * stats may be NULL.  The page's defaults: alpha 1.05, beta 10, max_stall
+ * 1000. */
+typedef double (*gtf_cost_fn)(void* ctx, const gtf_fuse_plan* candidate);
+typedef struct {
+  double alpha;      /* >= 1 */
+  int32_t beta;      /* >= 0 */
+  int32_t max_stall; /* >= 1 */
+  uint64_t seed;
+  int32_t max_steps; /* 0: unbounded */
+  int32_t reserved;
+} gtf_search_params;
+typedef struct {
+  int64_t steps, evaluations, queue_left;
+  double start_cost, best_cost;
+} gtf_search_stats;
+int fuse_plan_search(const gtf_program_desc* desc, const gtf_search_params* params,
+                     gtf_cost_fn cost, void* ctx, gtf_fuse_plan** best,
+                     gtf_search_stats* stats);
+
 /* Number of groups; groups are numbered in an order that respects their
  * dependencies, so running 0..n-1 in order runs the program. */
 int fuse_plan_num_groups(const gtf_fuse_plan* plan, int32_t* n);
@@ -195,6 +254,14 @@ int fuse_plan_op_origin(const gtf_fuse_plan* plan, int32_t* origin);
  * otherwise it must hold cap entries (GTF_E_LIMIT if cap < *n_ops). */
 int fuse_plan_group_info(const gtf_fuse_plan* plan, int32_t g, int32_t* op_ids, int32_t cap,
                          int32_t* n_ops, int32_t* pattern_kind);
+
+/* The plan's program, in the descriptor's format: its tensors (the
+ * descriptor's, then internal ones written by copies, role GTF_ROLE_TMP)
+ * and its ops (topological; group_info's op ids index them).  Either array
+ * may be NULL to ask only for the count; otherwise it must hold cap
+ * entries (GTF_E_LIMIT if fewer). */
+int fuse_plan_program(const gtf_fuse_plan* plan, gtf_tensor_desc* tensors, int32_t cap_tensors,
+                      int32_t* n_tensors, gtf_op_desc* ops, int32_t cap_ops, int32_t* n_ops);
 
 /* External tensors of group g (descriptor tensor ids): every tensor the
  * launch reads or writes in device memory, each once.  tensor_ids may be

@@ -56,31 +56,52 @@ def result_shape(op: str, in_shapes) -> Tuple[int, int]:
 
 
 def evaluate(graph, inputs: Dict[int, np.ndarray],
-             stored: Iterable[int] = (), given: Dict[int, np.ndarray] = None
-             ) -> Dict[int, np.ndarray]:
-    """fp32 value of every tensor, each shaped [R, C].
+             stored: Iterable[int] = (), given: Dict[int, np.ndarray] = None,
+             groups=None) -> Dict[int, np.ndarray]:
+    """fp32 value of every tensor as it is in memory (rounded to its dtype
+    where it is stored: graph outputs and ``stored`` intermediates), each
+    shaped [R, C].
 
     ``given`` maps tensor ids to fp32 values used instead of computing them
     (their producing ops are skipped): a later group can then be checked on
-    exactly the inputs another implementation handed it."""
+    exactly the inputs another implementation handed it.
+
+    ``groups`` (lists of op indices): an op reading a value produced in its
+    own group gets the value before the store's rounding, since inside a
+    fused group every intermediate is fp32 and rounding happens only at the
+    store (TVM "FuseTIR": the group is one function whose intermediates
+    never go through memory).  Without groups, every reader of a stored
+    value gets the rounded value (each op its own group)."""
     stored = set(stored)
     given = {} if given is None else given
+    group_of = {}
+    for k, grp in enumerate(groups or []):
+        for i in grp:
+            group_of[i] = k
+    producer = {o.output: i for i, o in enumerate(graph.ops)}
+    raw: Dict[int, np.ndarray] = {}
     vals: Dict[int, np.ndarray] = {}
     for t in graph.inputs():
         d = graph.tensors[t]
         vals[t] = numerics.decode(inputs[t], d.dtype).reshape(norm_shape(d.shape))
-    for o in graph.ops:
+    for j, o in enumerate(graph.ops):
         if o.output in given:
             d = graph.tensors[o.output]
             vals[o.output] = np.asarray(given[o.output], dtype=np.float32).reshape(norm_shape(d.shape))
+            raw[o.output] = vals[o.output]
             continue
-        args = [vals[i] for i in o.inputs]
+        args = []
+        for i in o.inputs:
+            p = producer.get(i)
+            same = p is not None and groups is not None and group_of.get(p) == group_of.get(j)
+            args.append(raw[i] if same else vals[i])
         want = result_shape(o.op, [a.shape for a in args])
         d = graph.tensors[o.output]
         if norm_shape(d.shape) != want:
             raise ValueError(f"{o.op} -> {d.name}: declared {d.shape}, computes {want}")
         r = ops.apply(o.op, args, o.imm)
         r = np.broadcast_to(r, want).astype(np.float32)
+        raw[o.output] = r
         if o.output in stored or d.role == "out":
             r = numerics.round_to(r, d.dtype)
         vals[o.output] = r
@@ -97,7 +118,8 @@ def outputs(graph, vals: Dict[int, np.ndarray]) -> Dict[int, np.ndarray]:
     return res
 
 
-def run(graph, inputs: Dict[int, np.ndarray], stored: Iterable[int] = (), given=None):
+def run(graph, inputs: Dict[int, np.ndarray], stored: Iterable[int] = (), given=None,
+        groups=None):
     """Convenience: evaluate and return (all fp32 values, encoded outputs)."""
-    vals = evaluate(graph, inputs, stored, given)
+    vals = evaluate(graph, inputs, stored, given, groups)
     return vals, outputs(graph, vals)

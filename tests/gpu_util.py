@@ -64,7 +64,7 @@ def gpu_run(graph, inputs: Dict[int, np.ndarray], fuse: bool = True, plan=None,
 def oracle_run(graph, inputs, fuse: bool = True, given=None, row_resident: bool = False):
     groups = opart.partition(graph, fuse=fuse, row_resident=row_resident)
     stored = opart.stored_tensors(graph, groups)
-    return oev.run(graph, inputs, stored=stored, given=given)
+    return oev.run(graph, inputs, stored=stored, given=given, groups=groups)
 
 
 def bf16_ulps(a: np.ndarray, b: np.ndarray) -> np.ndarray:

@@ -337,3 +337,77 @@ def test_duplicate_plans_match_the_oracle():
                 set(g.inputs()) | set(g.outputs())
             assert stored == want and max(stored) < len(g.tensors)
     assert changed >= 40
+
+
+def _lib_bytes_cost(plan):
+    """The oracle's bytes_cost, from what the library reports: every tensor
+    each launch touches in memory, plus 65536 per launch."""
+    b = 0
+    for k in range(plan.num_groups):
+        for t in plan.group_tensors(k):
+            d = plan.graph.tensors[t]
+            n = 1
+            for e in d.shape:
+                n *= e
+            b += n * {"f32": 4, "bf16": 2, "u8": 1}[d.dtype]
+    return float(b + 65536 * plan.num_groups)
+
+
+def test_grouped_plans_agree_with_the_oracle_rule():
+    """fuse_plan_create_grouped accepts exactly the groupings the oracle's
+    plan_ok accepts, on random labelings of random DAGs (most of them
+    invalid) and on merges of the fusion pass's groups."""
+    from oracle import search as osr
+    from tests.test_oracle_partition import _f32_reduce_dags
+    rng = np.random.default_rng(77)
+    graphs = list(_f32_reduce_dags(61, 150)) + list(_broadcast_dags(62, 150))
+    graphs += [configs.layernorm_graph(16, 64), configs.layernorm_shared_graph(16, 64)]
+    n_ok = n_bad = 0
+    for g in graphs:
+        n = len(g.ops)
+        tries = [list(rng.integers(0, max(1, n // 2 + 1), size=n)) for _ in range(6)]
+        groups = opart.partition(g)
+        for _ in range(3):  # merge two of the fusion pass's groups
+            if len(groups) >= 2:
+                a, b = rng.choice(len(groups), size=2, replace=False)
+                lab = [0] * n
+                for k, grp in enumerate(groups):
+                    for i in grp:
+                        lab[i] = int(a) if k == b else k
+                tries.append(lab)
+        for lab in tries:
+            want = osr.plan_ok(g, [int(x) for x in lab])
+            try:
+                plan = gtf.FusePlan.grouped(g, lab)
+                got = True
+            except gtf.GtfError as e:
+                assert e.status == C.GTF_E_INVALID
+                got = False
+            assert got == want, (lab, [(o.op, o.inputs, o.output) for o in g.ops])
+            if got:
+                n_ok += 1
+                assert as_sets(plan.groups()) == as_sets(osr.groups_of([int(x) for x in lab]))
+            else:
+                n_bad += 1
+    assert n_ok >= 300 and n_bad >= 300
+
+
+def test_search_matches_the_oracle():
+    """fuse_plan_search with the same seed and the same (byte-count) cost
+    follows the oracle's search step for step: the same statistics, the
+    same best program and grouping."""
+    from oracle import search as osr
+    from tests.test_oracle_partition import _f32_reduce_dags
+    graphs = [configs.layernorm_shared_graph(16, 64), configs.layernorm_graph(16, 64),
+              configs.c3_graph(8, 64, head_op=True), configs.c2_graph(4, 16)]
+    graphs += list(_f32_reduce_dags(63, 25)) + list(_broadcast_dags(64, 25))
+    for k, g in enumerate(graphs):
+        for seed in (1, 2):
+            plan, st = gtf.search(g, _lib_bytes_cost, seed=seed, max_stall=200)
+            (prog, origin, lab), ost = osr.search(g, osr.bytes_cost, seed=seed, max_stall=200)
+            assert st == ost, (k, seed, st, ost)
+            assert plan.op_origin() == origin
+            p2 = plan.program()
+            assert [(o.op, o.inputs, o.output, np.float32(o.imm)) for o in p2.ops] == \
+                [(o.op, o.inputs, o.output, np.float32(o.imm)) for o in prog.ops]
+            assert as_sets(plan.groups()) == as_sets(osr.groups_of(lab))

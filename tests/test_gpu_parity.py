@@ -649,7 +649,8 @@ def test_duplicate_layernorm_is_the_hand_duplicated_one(rows, hidden, rr):
         n = _ids(shared)
         given = {n["mean"]: got[n["mean"]].reshape(rows, 1), n["var"]: got[n["var"]].reshape(rows, 1)}
         groups = opart.partition(g2)
-        _, want = oev.run(g2, ins, stored=opart.stored_tensors(g2, groups), given=given)
+        _, want = oev.run(g2, ins, stored=opart.stored_tensors(g2, groups), given=given,
+                          groups=groups)
         assert_bits_equal(got[y_s], want[y_s])
 
 
@@ -668,7 +669,7 @@ def test_random_dags_with_duplicate_fusion():
             assert plan.n_ops == len(gg2.ops)
             _, got = gpu_run(gg, ins, plan=plan)
             groups = opart.partition(gg2)
-            vals, want = oev.run(gg2, ins, stored=opart.stored_tensors(gg2, groups))
+            vals, want = oev.run(gg2, ins, stored=opart.stored_tensors(gg2, groups), groups=groups)
             big = max([float(np.nanmax(np.abs(v))) if v.size else 0.0 for v in vals.values()] + [1.0])
             for t in gg.outputs():
                 prod = gg2.ops[gg2.producer(t)]  # its operand may now be a copy's value
@@ -681,3 +682,89 @@ def test_random_dags_with_duplicate_fusion():
                     assert_close_scaled(got[t], want[t], 1e-5, big)
         n += 1
     assert n >= 20
+
+
+# ---------------------------------------------------------------- explicit groupings and search
+def _check_program(g, plan, ins):
+    """The plan's outputs against the oracle's evaluation of the plan's own
+    program with the plan's grouping (stored values rounded as stored)."""
+    prog = plan.program()
+    groups = plan.groups()
+    _, got = gpu_run(g, ins, plan=plan)
+    vals, want = oev.run(prog, ins, stored=opart.stored_tensors(prog, groups), groups=groups)
+    big = max([float(np.nanmax(np.abs(v))) if v.size else 0.0 for v in vals.values()] + [1.0])
+    for t in g.outputs():
+        prod = prog.ops[prog.producer(t)]
+        if prod.op in ("row_sum", "row_mean"):
+            assert_reduce_close(got[t], want[t], reduce_bound(vals[prod.inputs[0]], prod.op == "row_mean"),
+                                1e-5)
+        elif g.tensors[t].dtype == "bf16":
+            assert_close_scaled(numerics.bf16_to_f32(got[t]), numerics.bf16_to_f32(want[t]),
+                                2.0 ** -8, 1e-3 * big)
+        else:
+            assert_close_scaled(got[t], want[t], 1e-5, big)
+
+
+def test_random_grouped_plans_run_correctly():
+    """Groupings outside the fusion rules (random valid labelings: several
+    outputs per group, reductions read in their own group) through
+    fuse_plan_create_grouped, against the oracle on the same grouping."""
+    from oracle import search as osr
+    from tests.test_oracle_partition import _f32_reduce_dags
+    rng = np.random.default_rng(91)
+    n = 0
+    for gi, g in enumerate(list(_f32_reduce_dags(65, 80)) + list(_broadcast_dags(66, 80))):
+        for R, C in [(3, 5), (300, 24), (5, 130)]:
+            gg = _reshape(g, R, C)
+            m = len(gg.ops)
+            for _ in range(4):
+                lab = [int(x) for x in rng.integers(0, max(1, m // 2 + 1), size=m)]
+                if not osr.plan_ok(gg, lab):
+                    continue
+                plan = gtf.FusePlan.grouped(gg, lab)
+                announce("grouped", gi, (R, C), lab)
+                _check_program(gg, plan, _inputs_for(gg, 800 + gi))
+                n += 1
+    assert n >= 100
+
+
+def _measured_cost(g, reps=5):
+    """Cost of a candidate plan: the sum over its groups of each group's
+    launch time, measured with HIP events around `reps` back-to-back
+    launches on one set of device tensors; cached per group."""
+    dev = {}
+    for t, d in enumerate(g.tensors):
+        dev[t] = torch.zeros(d.shape, dtype=torch.float32 if d.dtype == "f32" else torch.int16,
+                             device="cuda")
+    cache = {}
+
+    def cost(plan):
+        total = 0.0
+        origin = plan.op_origin()
+        for k in range(plan.num_groups):
+            key = (tuple(sorted(origin[i] for i in plan.group_ops(k))), tuple(plan.group_tensors(k)))
+            if key not in cache:
+                run = plan.launcher(k, dev)
+                run()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    run()
+                e1.record()
+                torch.cuda.synchronize()
+                cache[key] = e0.elapsed_time(e1) / reps
+            total += cache[key]
+        return total
+    return cost
+
+
+def test_searched_plan_runs_correctly():
+    """DisCo's search with measured launch times on the LayerNorm whose
+    x - mean is written once: the best plan is valid, no costlier than the
+    unfused start, and computes what the oracle computes for its program
+    and grouping."""
+    g = configs.layernorm_shared_graph(512, 1024)
+    plan, st = gtf.search(g, _measured_cost(g), seed=5, max_stall=60)
+    assert st["best_cost"] <= st["start_cost"] and plan.num_groups < len(g.ops)
+    ins = configs.layernorm_inputs(g, configs.c5_layer_seed(0) + 5)
+    _check_program(g, plan, ins)

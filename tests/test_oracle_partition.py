@@ -393,8 +393,31 @@ def test_duplicate_preserves_values_and_never_raises_the_cost():
             ins = {}
             for j, t in enumerate(g.inputs()):
                 ins[t] = configs.tensor_values("f32", g.tensors[t].shape, "uniform", 900 + k, j, -1.5, 1.5)
-            _, want = oev.run(g, ins, stored=pt.stored_tensors(g, p1))
-            _, got = oev.run(g2, ins, stored=pt.stored_tensors(g2, p2))
+            _, want = oev.run(g, ins, stored=pt.stored_tensors(g, p1), groups=p1)
+            _, got = oev.run(g2, ins, stored=pt.stored_tensors(g2, p2), groups=p2)
             for t in g.outputs():
                 assert np.array_equal(got[t].view(np.uint32), want[t].view(np.uint32))
     assert changed >= 30
+
+
+def test_values_read_inside_their_group_are_not_rounded():
+    """Inside a group every intermediate is fp32; rounding to the tensor's
+    dtype happens at the store.  a = x / 3 is a bf16 graph output that b
+    also reads: in one group b sees the fp32 quotient, across groups the
+    stored bf16 value."""
+    from oracle import evaluate as oev
+    from oracle import numerics
+    g = Graph()
+    x = g.input("x", "f32", (1, 4))
+    a = g.op("mul_imm", [x], "a", "bf16", (1, 4), role="out", imm=1.0 / 3.0)
+    b = g.op("mul_imm", [a], "b", "f32", (1, 4), role="out", imm=3.0)
+    xs = np.array([[1.0, 2.0, 5.0, 7.0]], dtype=np.float32)
+    q = (xs * np.float32(1.0 / 3.0)).astype(np.float32)
+    one = oev.evaluate(g, {x: xs}, groups=[[0, 1]])
+    two = oev.evaluate(g, {x: xs}, groups=[[0], [1]])
+    assert np.array_equal(one[b], (q * np.float32(3.0)).astype(np.float32))
+    qb = numerics.bf16_to_f32(numerics.encode(q, "bf16"))
+    assert np.array_equal(two[b], (qb * np.float32(3.0)).astype(np.float32))
+    assert not np.array_equal(one[b], two[b])
+    # the stored output is the rounded quotient either way
+    assert np.array_equal(one[a], qb.reshape(1, 4)) and np.array_equal(two[a], qb.reshape(1, 4))
