@@ -64,10 +64,28 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p) {
   return __uint_as_float((uint32_t)(*p) << 16);
 }
 
+// e^x for x <= 0: 2^(x log2 e) on the hardware base-2 exponential
+// (v_exp_f32, about 1 ulp), with x log2 e carried as yh + yl: yh = fl(x L)
+// with L = log2 e rounded to fp32, yl = the exact error of that product
+// (one fma) plus x times the rest of log2 e.  Then e^x = 2^yh (1 + yl ln 2)
+// up to (yl ln 2)^2 / 2 < 1e-10 relative.  About 1.5 ulp in all; 5 VALU
+// slots against about 12 for the library expf, which also handles
+// overflow, which a non-positive argument cannot reach.  Results below
+// the normal range come out of v_exp_f32 flushed.
+__device__ __forceinline__ float exp_nonpos(float x) {
+  constexpr float kL = 1.44269502e+00f;       // log2(e) rounded to fp32
+  constexpr float kLlo = 1.92596299e-08f;     // log2(e) - kL
+  constexpr float kLn2 = 6.93147182e-01f;
+  const float yh = x * kL;
+  const float yl = __builtin_fmaf(x, kL, -yh) + x * kLlo;
+  const float p = __builtin_amdgcn_exp2f(yh);
+  return __builtin_fmaf(p, yl * kLn2, p);
+}
+
 __device__ __forceinline__ float f_sigmoid(float x) {
   // 1 / (1 + e^-x), written as e^x / (1 + e^x) for x < 0 so the tail keeps
   // its relative accuracy; one correctly rounded division
-  const float e = expf(-fabsf(x));
+  const float e = exp_nonpos(-fabsf(x));
   const float num = x >= 0.f ? 1.f : e;
   return num / (1.f + e);
 }
@@ -82,17 +100,17 @@ __device__ __forceinline__ float f_sigmoid(float x) {
 //    iteratively reweighted least squares toward the minimax relative error
 //    on t in [0, 13.5] against the float64 reference 0.5 * erfcx(t/sqrt(2)):
 //    fit error 2.0e-8, Horner condition number below 2.4.
-// End to end in fp32 (with IEEE expf and a 1-ulp reciprocal) the relative
-// error stays near 4e-7.  t is clamped at 20 for the exponential, where it
+// End to end in fp32 (with exp_nonpos and a 1-ulp reciprocal) the relative
+// error stays below 1e-6.  t is clamped at 20 for the exponential, where it
 // is 0 in fp32, so +inf gives +inf and -inf gives NaN (inf * 0) as the
-// definition does.  About 38 VALU slots per element.
+// definition does.  About 31 VALU slots per element.
 constexpr float kGeluP = 3.45e-01f;
 __device__ __forceinline__ float f_gelu(float x) {
   const float t = fabsf(x);
   const float tc = fminf(t, 20.0f);
   const float hi = tc * tc;
   const float lo = __builtin_fmaf(tc, tc, -hi);
-  float e = expf(-0.5f * hi);
+  float e = exp_nonpos(-0.5f * hi);
   e = __builtin_fmaf(e, -0.5f * lo, e);
   const float u = __builtin_amdgcn_rcpf(__builtin_fmaf(kGeluP, t, 1.0f));
   float P = -2.8428646e-02f;
@@ -114,8 +132,9 @@ __device__ __forceinline__ float f_relu(float x) { return x > 0.f ? x : 0.f; }
 // would make the compiler linearise the whole dispatch switch): both forms
 // are computed and one is selected.  |x| < 0.625: x + x^3 P(x^2), with P of
 // degree 4 fitted here by weighted least squares on Chebyshev nodes (max
-// relative error 7.4e-8 in fp32); otherwise 1 - 2 / (e^{2|x|} + 1), which
-// has no cancellation there (the result is at least 0.55).
+// relative error 7.4e-8 in fp32); otherwise 1 - 2 e / (1 + e) with
+// e = e^{-2|x|} <= 0.29, which has no cancellation there (the result is at
+// least 0.55).
 __device__ __forceinline__ float f_tanh(float x) {
   const float ax = fabsf(x);
   const float u = ax * ax;
@@ -125,8 +144,8 @@ __device__ __forceinline__ float f_tanh(float x) {
   p = __builtin_fmaf(p, u, 1.3331381976604462e-01f);
   p = __builtin_fmaf(p, u, -3.333328068256378e-01f);
   const float small = __builtin_fmaf(ax * u, p, ax);
-  const float e = expf(2.0f * ax);
-  const float big = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  const float e = exp_nonpos(-2.0f * ax);
+  const float big = 1.0f - 2.0f * e * __builtin_amdgcn_rcpf(e + 1.0f);
   return copysignf(ax < 0.625f ? small : big, x);
 }
 
