@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "joint", "ln", "search"])
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "joint", "ln", "search", "transpose"])
     ap.add_argument("--layers", type=int, default=12)
     ap.add_argument("--ln-variant", default="all",
                     choices=["all", "row_resident", "tvm_groups", "unfused", "shared_center",
@@ -464,6 +464,8 @@ def run_config(torch, gtf, configs, args):
         return run_ln(torch, gtf, configs, args, res, gen)
     if w == "search":
         return run_search(torch, gtf, configs, args, res, gen)
+    if w == "transpose":
+        return run_transpose(torch, gtf, configs, args, res, gen)
     if w == "c1":
         g = configs.c1_graph()
         dists = {"x": ("uniform", -1, 1), "a": ("uniform", -1, 1), "b": ("uniform", -1, 1)}
@@ -732,6 +734,37 @@ def run_search(torch, gtf, configs, args, res, gen):
                            "best_cost_ms": round(st["best_cost"], 5), "wall_s": round(wall, 2),
                            "groups": best.groups(), "op_origin": best.op_origin()},
                 "speedup_vs_tvm_groups": round(out["tvm_groups"]["ms_per_step"] / s["ms_per_step"], 3),
+                "timing": "graph replays over the rotation sets", "variants": out})
+    return res
+
+
+def run_transpose(torch, gtf, configs, args, res, gen):
+    """y = gelu(transpose(X) + b) with X bf16[4096,8192] -> y bf16[8192,4096]
+    (the c5 bias+GELU group's bytes, with its input stored transposed): one
+    launch whose transpose is an addressed load, against one launch per op
+    and against the same group on an input already in layout."""
+    from workloads.graph import Graph
+    g = Graph()
+    X = g.input("X", "bf16", (4096, 8192))
+    b = g.input("b1", "bf16", (4096,))
+    t = g.op("transpose", [X], "t", "bf16", (8192, 4096))
+    u = g.op("add", [t, b], "u", "bf16", (8192, 4096))
+    g.op("gelu", [u], "y", "bf16", (8192, 4096), role="out")
+    dists = {"X": ("normal", 0.0, 1.0), "b1": ("normal", 0.0, 0.1)}
+    plain = configs.gelu_graph()
+    out = {}
+    for name, (gg, plan, d) in {"fused": (g, gtf.FusePlan(g), dists),
+                                "unfused": (g, gtf.FusePlan(g, fuse=False), dists),
+                                "no_transpose": (plain, gtf.FusePlan(plain), GELU_D)}.items():
+        ms, nbytes = time_plan(torch, gtf, gg, plan, gen, d, args.steps, args.warmup)
+        out[name] = {"ms_per_step": round(ms, 5), "launches": plan.num_groups, "bytes": nbytes,
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+    f = out["fused"]
+    res.update({"value": f["gbs"], "ms_per_step": f["ms_per_step"], "dtype": "bf16",
+                "config": {"workload": "transpose: gelu(transpose(X) + b), X bf16[4096,8192] -> "
+                                       "y bf16[8192,4096], one launch",
+                           "bytes_per_step": f["bytes"]},
+                "speedup_vs_unfused": round(out["unfused"]["ms_per_step"] / f["ms_per_step"], 3),
                 "timing": "graph replays over the rotation sets", "variants": out})
     return res
 

@@ -53,10 +53,10 @@ int arity(int opc) {
     case GTF_OP_COPY: case GTF_OP_EXP: case GTF_OP_TANH: case GTF_OP_SIGMOID:
     case GTF_OP_RELU: case GTF_OP_GELU: case GTF_OP_SQUARE: case GTF_OP_SQRT:
     case GTF_OP_RECIP: case GTF_OP_NEG: case GTF_OP_ADD_IMM: case GTF_OP_MUL_IMM:
-    case GTF_OP_ROW_SUM: case GTF_OP_ROW_MEAN:
+    case GTF_OP_ROW_SUM: case GTF_OP_ROW_MEAN: case GTF_OP_TRANSPOSE: case GTF_OP_RESHAPE:
       return 1;
     case GTF_OP_ADD: case GTF_OP_SUB: case GTF_OP_MUL: case GTF_OP_DIV:
-    case GTF_OP_MAX: case GTF_OP_MIN: case GTF_OP_DMUL:
+    case GTF_OP_MAX: case GTF_OP_MIN: case GTF_OP_DMUL: case GTF_OP_CONCAT:
       return 2;
     case GTF_OP_ADD3:
       return 3;
@@ -131,6 +131,22 @@ int validate(const gtf_program_desc* d, FusePlan* p) {
       const TensorInfo& ti = p->tensors[od.in[0]];
       if (d->tensors[out].rank != 2 || to.R != ti.R || to.C != 1)
         return fail(GTF_E_SHAPE, op_name(i) + ": a row reduction of [R,C] is declared [R,1]");
+    } else if (od.opcode == GTF_OP_TRANSPOSE) {
+      const TensorInfo& ti = p->tensors[od.in[0]];
+      if (ti.rank != 2 || d->tensors[out].rank != 2 || to.R != ti.C || to.C != ti.R)
+        return fail(GTF_E_SHAPE, op_name(i) + ": transpose of [R,C] (rank 2) is declared [C,R]");
+    } else if (od.opcode == GTF_OP_RESHAPE) {
+      const TensorInfo& ti = p->tensors[od.in[0]];
+      if (ti.R * ti.C != to.R * to.C)
+        return fail(GTF_E_SHAPE, op_name(i) + ": reshape changes the element count");
+    } else if (od.opcode == GTF_OP_CONCAT) {
+      const TensorInfo& a = p->tensors[od.in[0]];
+      const TensorInfo& b = p->tensors[od.in[1]];
+      if (a.rank != 2 || b.rank != 2 || d->tensors[out].rank != 2 || a.R != b.R || to.R != a.R ||
+          a.C < 1 || b.C < 1 || to.C != a.C + b.C)
+        return fail(GTF_E_SHAPE, op_name(i) + ": concat of [R,C1], [R,C2] (rank 2, C1, C2 >= 1) "
+                                              "is declared [R,C1+C2]");
+      if (a.dtype != b.dtype) return fail(GTF_E_UNSUPPORTED, op_name(i) + ": concat of two dtypes");
     } else {
       // NumPy broadcasting per axis: extents of 1 stretch to the other one
       int64_t R = 1, C = 1;

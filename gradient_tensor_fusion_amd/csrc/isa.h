@@ -72,6 +72,12 @@ enum Form : int {
   // store A to LDS slot arg (column slot in the column phase, row slot in
   // the row phase)
   F_ST_LDS,
+  // addressed loads into A (element phase): element (row, col) of slot arg
+  // at row * rstride + col * cstride, element by element (a transpose)
+  F_LDG_F32_A, F_LDG_BF16_A,
+  // concat along columns (element or column phase): slots arg & 0xFF and
+  // arg >> 8, split at column imm; each side at its own strides
+  F_LDC_F32_A, F_LDC_BF16_A,
   F_COUNT
 };
 
@@ -128,7 +134,7 @@ struct ExecArgs {
   void* const* m_ptrs;
   const uint32_t* m_vec;
   int32_t n_slots;
-  int32_t pad_;
+  int32_t slow_only;       // 1: every tile goes sub-tile by sub-tile (addressed loads)
   void* ptr[kMaxSlots];
   int64_t rstride[kMaxSlots];
   int64_t cstride[kMaxSlots];

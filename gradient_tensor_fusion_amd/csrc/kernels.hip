@@ -301,6 +301,49 @@ __device__ __forceinline__ void load_bf16(float (&d)[V], const ExecArgs& a, int 
   d[0] = bf16_g(b + elem_offset<V, MODE>(a, slot, t));
 }
 
+// Addressed loads.  Element j of a tile sits at row t.row, column
+// t.col + (j / kV) * kstride + j % kV; a transposed source is read there at
+// row * rstride + col * cstride, one element per load.  A concat reads
+// columns left of the split from slot arg & 0xFF and the rest, shifted by
+// the split, from slot arg >> 8.  Elements outside a partial tile read the
+// first element of the first slot.
+template <bool BF>
+__device__ __forceinline__ float load_one(const void* base, int64_t off) {
+  if (BF) return bf16_g((const GAS uint16_t*)base + off);
+  return ((const GAS float*)base)[off];
+}
+template <int V, int MODE, bool FAST, bool BF>
+__device__ __forceinline__ void load_gather(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
+  const void* base = t.ptrs[slot];
+  const int64_t rowoff = t.row * a.rstride[slot], cs = a.cstride[slot];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i = j % kV;
+    const bool ok = FAST || (t.valid && i < t.cnt);
+    const int64_t col = t.col + (int64_t)(j / kV) * t.kstride + i;
+    d[j] = load_one<BF>(base, ok ? rowoff + col * cs : 0);
+  }
+}
+template <int V, int MODE, bool FAST, bool BF>
+__device__ __forceinline__ void load_concat(float (&d)[V], const ExecArgs& a, int arg, float split_f,
+                                            const Tile& t) {
+  const int sa = arg & 0xFF, sb = arg >> 8;
+  const int64_t split = (int64_t)split_f;
+  const void* pa = t.ptrs[sa];
+  const void* pb = t.ptrs[sb];
+  const int64_t ra = t.row * a.rstride[sa], rb = t.row * a.rstride[sb];
+  const int64_t ca = a.cstride[sa], cb = a.cstride[sb];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i = j % kV;
+    const bool ok = FAST || (t.valid && i < t.cnt);
+    const int64_t col = t.col + (int64_t)(j / kV) * t.kstride + i;
+    const bool left = !ok || col < split;
+    const int64_t off = !ok ? 0 : left ? ra + col * ca : rb + (col - split) * cb;
+    d[j] = load_one<BF>(left ? pa : pb, off);
+  }
+}
+
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void load_u8(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
   const GAS uint8_t* b = (const GAS uint8_t*)t.ptrs[slot];
@@ -528,6 +571,20 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
       case F_LD_F32_B: load_f32<V, MODE, FAST>(B, a, arg, t); break;
       case F_LD_BF16_B: load_bf16<V, MODE, FAST>(B, a, arg, t); break;
       case F_LD_U8_B: load_u8<V, MODE, FAST>(B, a, arg, t); break;
+      // addressed loads exist only for one sub-tile at a time (a program
+      // holding one runs with slow_only set, never on the whole-run path)
+      case F_LDG_F32_A:
+        if constexpr (MODE == M_ELEM && V == kV) load_gather<V, MODE, FAST, false>(A, a, arg, t);
+        break;
+      case F_LDG_BF16_A:
+        if constexpr (MODE == M_ELEM && V == kV) load_gather<V, MODE, FAST, true>(A, a, arg, t);
+        break;
+      case F_LDC_F32_A:
+        if constexpr (MODE != M_ROW && V == kV) load_concat<V, MODE, FAST, false>(A, a, arg, cur.imm, t);
+        break;
+      case F_LDC_BF16_A:
+        if constexpr (MODE != M_ROW && V == kV) load_concat<V, MODE, FAST, true>(A, a, arg, cur.imm, t);
+        break;
       case F_COL_A: if (MODE == M_ELEM) lds_vec<V>(A, col, t.kstride); break;
       case F_ROW_A: if (MODE != M_COL) fill<V>(A, lds_row[arg * a.RB + t.rr]); break;
       case F_IMM_A: fill<V>(A, cur.imm); break;
@@ -771,7 +828,7 @@ exec_kernel(const ExecArgs a) {
         const bool row_ok = rr < nr;
         const bool whole = row_ok && cl0 + (K - 1) * ks + kV <= nc;
         // both branches are wave-uniform
-        if (__all(whole)) {
+        if (!a.slow_only && __all(whole)) {
           Tile t;
           t.valid = true;
           t.vec = true;

@@ -125,13 +125,23 @@ enum Cls { CLS_E = 0, CLS_ROW = 1, CLS_COL = 2 };
 constexpr int kNoValue = -1;
 
 struct MOp {
-  int kind;    // 0 unary form, 1 binary op, 2 imm op (slot op imm), 3 reduce, 4 copy
+  int kind;    // 0 unary form, 1 binary op, 2 imm op (slot op imm), 3 reduce, 4 copy,
+               // 5 addressed load (transpose / reshape / concat of tensors in memory)
   int form;    // F_* for unary, F_ADD..F_MIN for binary, XOp for imm
   int in[2] = {-1, -1};
   int out = -1;
   float imm = 0.f;
   bool commutative = false;
+  int gkind = 0;           // kind 5: 0 plain load, 1 strided gather, 2 concat of two slots
+  int src[2] = {-1, -1};   // kind 5: the tensors read from memory
 };
+
+// register operands of a micro-op
+int mop_arity(const MOp& m) { return m.kind == 1 ? 2 : m.kind == 5 ? 0 : 1; }
+
+bool is_gather(int opc) {
+  return opc == GTF_OP_TRANSPOSE || opc == GTF_OP_RESHAPE || opc == GTF_OP_CONCAT;
+}
 
 int unary_form(int opc) {
   switch (opc) {
@@ -303,6 +313,21 @@ struct Codegen {
     consume_a(m.in[0]);
     reg[RA] = m.out;
   }
+  // an addressed load into A: the source's slot carries the strides that
+  // map a domain position to the source element
+  void run_vload(const MOp& m) {
+    save(RA);
+    if (!ok) return;
+    const bool bf = p.tensors[m.src[0]].dtype == GTF_BF16;
+    if (m.gkind == 0)
+      emit(load_form(m.src[0], RA), ext_slot.at(m.src[0]));
+    else if (m.gkind == 1)
+      emit(bf ? F_LDG_BF16_A : F_LDG_F32_A, ext_slot.at(m.src[0]));
+    else
+      emit(bf ? F_LDC_BF16_A : F_LDC_F32_A, ext_slot.at(m.src[0]) | (ext_slot.at(m.src[1]) << 8),
+           m.imm);
+    reg[RA] = m.out;
+  }
   void run_imm(const MOp& m) {
     bring(m.in[0], RA);
     consume_a(m.in[0]);
@@ -375,6 +400,11 @@ const char* check_program(const ExecArgs& a, int n_slots) {
       if (f < 0 || f >= F_COUNT) return "unknown form";
       if (f <= F_LD_U8_B || f == F_ST_F32 || f == F_ST_BF16) {
         if (arg >= n_slots) return "external slot out of range";
+      } else if (f == F_LDG_F32_A || f == F_LDG_BF16_A) {
+        if (phase != 2 || arg >= n_slots) return "gather slot out of range";
+      } else if (f == F_LDC_F32_A || f == F_LDC_BF16_A) {
+        if (phase == 1 || (arg & 0xFF) >= n_slots || (arg >> 8) >= n_slots)
+          return "concat slots out of range";
       } else if (f == F_COL_A || f == F_COL_B || (f >= F_ADD_C && f <= F_MIN_C)) {
         if (phase == 0 || arg >= a.n_col_slots) return "LDS column slot out of range";
       } else if (f == F_ROW_A || f == F_ROW_B || (f >= F_ADD_R && f <= F_MIN_R)) {
@@ -415,12 +445,33 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   std::set<int> produced;
   for (int i : ops) produced.insert(p.ops[i].out);
 
-  // ---- domain
+  // ---- addressed loads: a transpose, reshape or concat reads its inputs
+  // from memory (none made in the group, none read by another member), so
+  // each input's slot carries one mapping from domain positions to its
+  // elements
+  bool gathers2d = false;
+  for (int i : ops) {
+    const OpInfo& o = p.ops[i];
+    if (!is_gather(o.opcode)) continue;
+    if (o.opcode != GTF_OP_RESHAPE) gathers2d = true;
+    for (int k = 0; k < o.n_in; ++k) {
+      if (produced.count(o.in[k])) return bad("transpose/reshape/concat of a value made in the group");
+      for (int j : ops)
+        if (j != i)
+          for (int q = 0; q < p.ops[j].n_in; ++q)
+            if (p.ops[j].in[q] == o.in[k])
+              return bad("transpose/reshape/concat input also read by another op of the group");
+    }
+    if ((o.opcode == GTF_OP_TRANSPOSE || o.opcode == GTF_OP_CONCAT) && p.tensors[o.in[0]].dtype == GTF_U8)
+      return bad("transpose/concat of u8");
+  }
+  // ---- domain (a gather's input is addressed through it, not broadcast)
   int64_t R = 0, C = 0;
   std::set<int> touched;
   for (int i : ops) {
     const OpInfo& o = p.ops[i];
-    for (int k = 0; k < o.n_in; ++k) touched.insert(o.in[k]);
+    if (!is_gather(o.opcode))
+      for (int k = 0; k < o.n_in; ++k) touched.insert(o.in[k]);
     touched.insert(o.out);
   }
   R = 1;
@@ -441,7 +492,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     const TensorInfo& ri = p.tensors[p.ops[r].in[0]];
     if (ri.R != R || ri.C != C) return bad("reduction input is not the group domain");
   }
-  bool flat = reds.empty();
+  bool flat = reds.empty() && !gathers2d;
   for (int t : touched)
     if (p.tensors[t].R != R || p.tensors[t].C != C) flat = false;
   int64_t DR = flat ? 1 : R, DC = flat ? R * C : C;
@@ -533,6 +584,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   };
   for (int i : ops) {
     const OpInfo& o = p.ops[i];
+    if (is_gather(o.opcode)) continue;  // its inputs are loaded, addressed
     const int c = op_cls(i);
     for (int k = 0; k < o.n_in; ++k) {
       const int t = o.in[k];
@@ -555,7 +607,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   // load an external [1,1] scalar)
   for (int i : ops) {
     int c = op_cls(i);
-    if (c == CLS_E) continue;
+    if (c == CLS_E || is_gather(p.ops[i].opcode)) continue;
     const OpInfo& o = p.ops[i];
     for (int k = 0; k < o.n_in; ++k) {
       int ci = cls_of(o.in[k]);
@@ -569,10 +621,49 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
 
   // ---- lower each op to micro-ops
   std::map<int, std::vector<MOp>> mops_of;
+  std::map<int, std::pair<int64_t, int64_t>> gather_stride;  // source tensor -> (rstride, cstride)
   int synth = -1;
   for (int i : ops) {
     const OpInfo& o = p.ops[i];
     auto& L = mops_of[i];
+    if (is_gather(o.opcode)) {
+      // the source's element for domain position (r, c), by the op's own
+      // index map; a plain load when that map is the value's own layout
+      MOp m;
+      m.kind = 5;
+      m.out = o.out;
+      m.src[0] = o.in[0];
+      const TensorInfo& to = p.tensors[o.out];
+      const int ct = cls_of(o.out);
+      auto own = [&](int64_t Rt, int64_t Ct) -> std::pair<int64_t, int64_t> {
+        if (flat) return {0, 1};
+        if (ct == CLS_E) return {Ct, 1};
+        if (ct == CLS_COL) return {0, 1};
+        return {Rt == 1 ? 0 : 1, 0};
+      };
+      if (o.opcode == GTF_OP_CONCAT) {
+        if (ct == CLS_ROW) return bad("concat of per-row values");
+        const TensorInfo& a = p.tensors[o.in[0]];
+        const TensorInfo& b = p.tensors[o.in[1]];
+        m.gkind = 2;
+        m.src[1] = o.in[1];
+        m.imm = (float)a.C;
+        if (a.C > (1 << 24)) return bad("concat split column beyond fp32 integers");
+        gather_stride[o.in[0]] = {a.R == 1 ? 0 : a.C, 1};
+        gather_stride[o.in[1]] = {b.R == 1 ? 0 : b.C, 1};
+      } else if (o.opcode == GTF_OP_TRANSPOSE && ct == CLS_E) {
+        // T[r][c] = X[c][r]: X is [C, R] in domain terms
+        m.gkind = 1;
+        gather_stride[o.in[0]] = {1, p.tensors[o.in[0]].C};
+      } else {
+        // reshape (row-major order kept), or a transpose of a vector, is
+        // the result's own layout over the source's memory
+        m.gkind = 0;
+        gather_stride[o.in[0]] = own(to.R, to.C);
+      }
+      L.push_back(m);
+      continue;
+    }
     if (o.opcode == GTF_OP_COPY) {
       MOp m;
       m.kind = 4;
@@ -737,7 +828,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
           }
       }
       for (auto& m : L) {
-        const int n_in = m.kind == 1 ? 2 : 1;
+        const int n_in = mop_arity(m);
         for (int k = 0; k < n_in; ++k) {
           const int v = m.in[k];
           if (g.is_x(v)) continue;
@@ -765,7 +856,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
         };
         for (auto& kv : staging) note(kv.first);
         for (auto& m : L)
-          for (int k = 0; k < (m.kind == 1 ? 2 : 1); ++k) note(m.in[k]);
+          for (int k = 0; k < mop_arity(m); ++k) note(m.in[k]);
         for (size_t i = 0; i < first_use.size() && i < 2; ++i) {
           const int r = i == 0 ? Codegen::RA : Codegen::RB;
           g.emit(g.load_form(first_use[i], r), g.ext_slot.at(first_use[i]));
@@ -784,7 +875,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
         int best = -1, best_score = -1;
         for (size_t k = 0; k < L.size(); ++k) {
           if (done[k]) continue;
-          const int n_in = L[k].kind == 1 ? 2 : 1;
+          const int n_in = mop_arity(L[k]);
           bool rdy = true;
           for (int q = 0; q < n_in; ++q)
             if (made_here.count(L[k].in[q]) && !ready_vals.count(L[k].in[q])) rdy = false;
@@ -811,6 +902,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
           case 1: g.run_binary(m); break;
           case 2: g.run_imm(m); break;
           case 3: g.run_reduce(m); break;
+          case 5: g.run_vload(m); break;
           default: g.run_copy(m); break;
         }
         if (!g.ok) break;
@@ -930,7 +1022,11 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   for (size_t s = 0; s < slots.size(); ++s) {
     const TensorInfo& ti = p.tensors[slots[s]];
     int c = cls_of(slots[s]);
-    if (flat) {
+    auto gs = gather_stride.find(slots[s]);
+    if (gs != gather_stride.end()) {
+      a.rstride[s] = gs->second.first;
+      a.cstride[s] = gs->second.second;
+    } else if (flat) {
       a.rstride[s] = 0;
       a.cstride[s] = 1;
     } else if (c == CLS_E) {
@@ -951,6 +1047,11 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   cg.max_depth = max_depth;
   cg.lds_bytes = (int)(a.n_col_slots * (int64_t)pw * 4 + a.n_row_slots * (int64_t)rb * 4 + 16 * 4);
   if (cg.lds_bytes > 64 * 1024) return bad("LDS staging exceeds 64 KiB");
+  a.slow_only = 0;
+  for (size_t k = 0; k < pos; ++k) {
+    const int f = a.prog[k].code;
+    if (f == F_LDG_F32_A || f == F_LDG_BF16_A || f == F_LDC_F32_A || f == F_LDC_BF16_A) a.slow_only = 1;
+  }
   if (const char* why = check_program(a, cg.n_slots)) return bad(why);
   if (outp) *outp = cg;
   return true;
@@ -967,7 +1068,7 @@ void annotate(FusePlan* p) {
       o.pattern = GTF_PAT_OPAQUE;
     } else if (is_reduce(o.opcode)) {
       o.pattern = GTF_PAT_COMM_REDUCE;
-    } else if (o.opcode == GTF_OP_COPY) {
+    } else if (o.opcode == GTF_OP_COPY || is_gather(o.opcode)) {
       o.pattern = GTF_PAT_INJECTIVE;
     } else {
       const TensorInfo& to = p->tensors[o.out];

@@ -87,6 +87,15 @@ enum {
  * dropout:         dmul (n_in 2: h, mask) = (h * imm) * mask
  * row reduce:      row_sum, row_mean over the last axis; the output is
  *                  declared [R, 1]; the mean divides the sum by the width.
+ * injective data movement (kInjective, TVM "Operator Pattern
+ * Classification": each output element is one input element, moved):
+ *                  transpose: [R, C] (rank 2) -> [C, R];
+ *                  reshape: any shape -> the declared shape of the same
+ *                  element count, row-major order kept;
+ *                  concat (n_in 2): [R, C1] ++ [R, C2] -> [R, C1 + C2]
+ *                  along the last axis (rank 2, C1, C2 >= 1, one dtype).
+ *                  Inside a group these run as addressed loads: their
+ *                  inputs come from memory.
  * add/sub/mul/div/max/min/add3/dmul broadcast their operands; sqrt and
  * div are correctly rounded; no multiply-add is ever contracted. */
 enum {
@@ -97,7 +106,8 @@ enum {
   GTF_OP_ADD = 32, GTF_OP_SUB = 33, GTF_OP_MUL = 34, GTF_OP_DIV = 35,
   GTF_OP_MAX = 36, GTF_OP_MIN = 37,
   GTF_OP_ADD3 = 48, GTF_OP_DMUL = 49,
-  GTF_OP_ROW_SUM = 64, GTF_OP_ROW_MEAN = 65
+  GTF_OP_ROW_SUM = 64, GTF_OP_ROW_MEAN = 65,
+  GTF_OP_TRANSPOSE = 80, GTF_OP_RESHAPE = 81, GTF_OP_CONCAT = 82
 };
 
 #define GTF_OPF_OPAQUE 1 /* op flag: force OpPatternKind kOpaque (a barrier) */

@@ -49,9 +49,21 @@ def broadcast_shape(shapes) -> Tuple[int, int]:
     return (R, C)
 
 
-def result_shape(op: str, in_shapes) -> Tuple[int, int]:
+def result_shape(op: str, in_shapes, declared=None) -> Tuple[int, int]:
     if op in ("row_sum", "row_mean"):
         return (in_shapes[0][0], 1)
+    if op == "transpose":
+        return (in_shapes[0][1], in_shapes[0][0])
+    if op == "reshape":
+        # the declared shape, provided the element count is kept
+        if declared[0] * declared[1] != in_shapes[0][0] * in_shapes[0][1]:
+            raise ValueError(f"reshape of {in_shapes[0]} to {declared}")
+        return declared
+    if op == "concat":
+        (r1, c1), (r2, c2) = in_shapes
+        if r1 != r2:
+            raise ValueError(f"concat of {in_shapes}: row counts differ")
+        return (r1, c1 + c2)
     return broadcast_shape(in_shapes)
 
 
@@ -95,11 +107,11 @@ def evaluate(graph, inputs: Dict[int, np.ndarray],
             p = producer.get(i)
             same = p is not None and groups is not None and group_of.get(p) == group_of.get(j)
             args.append(raw[i] if same else vals[i])
-        want = result_shape(o.op, [a.shape for a in args])
         d = graph.tensors[o.output]
+        want = result_shape(o.op, [a.shape for a in args], norm_shape(d.shape))
         if norm_shape(d.shape) != want:
             raise ValueError(f"{o.op} -> {d.name}: declared {d.shape}, computes {want}")
-        r = ops.apply(o.op, args, o.imm)
+        r = ops.apply(o.op, args, o.imm, want)
         r = np.broadcast_to(r, want).astype(np.float32)
         raw[o.output] = r
         if o.output in stored or d.role == "out":

@@ -69,11 +69,19 @@ def row_mean(x):
     return (_f64(x).sum(axis=-1, keepdims=True) / x.shape[-1]).astype(F32)
 
 
-def apply(op: str, args, imm: float = 0.0) -> np.ndarray:
+def apply(op: str, args, imm: float = 0.0, shape=None) -> np.ndarray:
+    """One op on fp32 arrays (2-D [R, C]); shape is the result's shape,
+    needed by reshape."""
     a = [np.asarray(v, dtype=F32) for v in args]
     with np.errstate(all="ignore"):
         if op == "copy":
             r = a[0].copy()
+        elif op == "transpose":
+            r = a[0].T.copy()
+        elif op == "reshape":
+            r = a[0].reshape(shape).copy()   # row-major element order kept
+        elif op == "concat":
+            r = np.concatenate([a[0], a[1]], axis=1)
         elif op == "exp":
             r = exp(a[0])
         elif op == "tanh":

@@ -34,6 +34,13 @@ Readings where the page is silent: the source's pattern is its group's
 pattern; path nodes are judged by their own pattern; a node whose output
 is a graph output has no post-dominator.
 
+Injective ops that move elements (transpose, reshape, concat; kInjective
+in the page's table) fuse by the same phases, within what the executor
+runs: such an op reads its inputs from memory, as an addressed load, so a
+merge that would put one after a producer of its input, or next to another
+reader of that input, is not made (gathers_ok), like a merge over the
+argument limit.
+
 Row-resident extension (opt-in, row_resident=True; beyond the page, whose
 fusion rules keep a reduction as the last op of its group): after the
 three phases, a group holding a row reduction r is merged with the group of
@@ -80,6 +87,11 @@ from .evaluate import norm_shape
 K_ELEMWISE, K_BROADCAST, K_INJECTIVE, K_COMM_REDUCE = 0, 1, 2, 3
 K_OUT_EWISE_FUSABLE, K_TUPLE, K_OPAQUE = 4, 7, 8
 
+# injective ops that move elements to other positions: the executor runs
+# one only on a value read from memory (its input comes from outside its
+# group), as an addressed load
+GATHERS = ("transpose", "reshape", "concat")
+
 MAX_FUSED_OPS = 256
 MAX_GROUP_ARGS = 16
 MAX_STAGES = 4
@@ -92,7 +104,7 @@ def pattern(graph, i: int) -> int:
         return K_OPAQUE
     if o.op in ("row_sum", "row_mean"):
         return K_COMM_REDUCE
-    if o.op == "copy":
+    if o.op in ("copy",) + GATHERS:
         return K_INJECTIVE
     out = norm_shape(graph.tensors[o.output].shape)
     if any(norm_shape(graph.tensors[t].shape) != out for t in o.inputs):
@@ -201,6 +213,23 @@ def _group_args(graph, members: Set[int]) -> int:
         if graph.tensors[t].role == "out":
             ext.add(t)
     return len(ext)
+
+
+def gathers_ok(graph, members: Set[int]) -> bool:
+    """A transpose, reshape or concat runs inside a group only as a load:
+    its inputs come from memory (not made in the group) and no other op of
+    the group reads them."""
+    produced = {graph.ops[i].output for i in members}
+    for i in members:
+        o = graph.ops[i]
+        if o.op not in GATHERS:
+            continue
+        for t in o.inputs:
+            if t in produced:
+                return False
+            if any(t in graph.ops[j].inputs for j in members if j != i):
+                return False
+    return True
 
 
 def _row_resident_ok(graph, members: Set[int]) -> bool:
@@ -312,6 +341,8 @@ def partition(graph, fuse: bool = True, row_resident: bool = False) -> List[List
                     continue
                 if _group_args(graph, members) > MAX_GROUP_ARGS:
                     continue
+                if not gathers_ok(graph, members):
+                    continue
                 for v in mid | {i}:
                     uf.union_into(v, d)
         if row_resident:
@@ -332,6 +363,8 @@ def partition(graph, fuse: bool = True, row_resident: bool = False) -> List[List
                         if not _convex(succ, members):
                             continue
                         if len(members) > MAX_FUSED_OPS or _group_args(graph, members) > MAX_GROUP_ARGS:
+                            continue
+                        if not gathers_ok(graph, members):
                             continue
                         if not _row_resident_ok(graph, members):
                             continue

@@ -90,10 +90,13 @@ def group_ok(graph, members: Set[int]) -> bool:
     column op may also read a [1,1] input); at most 16 tensors in memory,
     8 per-row and 4 per-column operands held on chip."""
     ms = sorted(members)
+    if not pt.gathers_ok(graph, members):
+        return False
     produced = {graph.ops[i].output: i for i in ms}
     touched = set()
     for i in ms:
-        touched.update(graph.ops[i].inputs)
+        if graph.ops[i].op not in pt.GATHERS:   # a gather's input is addressed, not broadcast
+            touched.update(graph.ops[i].inputs)
         touched.add(graph.ops[i].output)
     shape = {t: norm_shape(graph.tensors[t].shape) for t in touched}
     R = C = 1
@@ -110,7 +113,9 @@ def group_ok(graph, members: Set[int]) -> bool:
     reds = [i for i in ms if graph.ops[i].op in pt._REDUCES]
     if any(shape[graph.ops[i].inputs[0]] != (R, C) for i in reds):
         return False
-    flat = not reds and all(shape[t] == (R, C) for t in touched)
+    # a transpose or concat of a full-domain value addresses rows and columns
+    gathers2d = any(graph.ops[i].op in ("transpose", "concat") for i in ms)
+    flat = not reds and not gathers2d and all(shape[t] == (R, C) for t in touched)
 
     def cls(t):
         r, c = shape[t]
@@ -128,6 +133,10 @@ def group_ok(graph, members: Set[int]) -> bool:
         if j not in members:
             outside.update(t for t in o.inputs if t in produced)
     ext = {t for i in ms for t in graph.ops[i].inputs if t not in produced}
+    for i in ms:   # a concat of column values stages two slots in the column phase
+        o = graph.ops[i]
+        if o.op == "concat" and cls(o.output) == "ROW":
+            return False
     ext |= {t for t in produced if graph.tensors[t].role == "out" or t in outside}
     if len(ext) > pt.MAX_GROUP_ARGS:
         return False
@@ -152,6 +161,8 @@ def group_ok(graph, members: Set[int]) -> bool:
     for i in ms:
         o = graph.ops[i]
         c = op_cls(i)
+        if o.op in pt.GATHERS:
+            continue
         for t in o.inputs:
             if c == "E":
                 if cls(t) == "ROW":
@@ -166,7 +177,7 @@ def group_ok(graph, members: Set[int]) -> bool:
         return False
     for i in ms:
         c = op_cls(i)
-        if c == "E":
+        if c == "E" or graph.ops[i].op in pt.GATHERS:
             continue
         for t in graph.ops[i].inputs:
             if cls(t) == c:

@@ -362,6 +362,7 @@ def test_grouped_plans_agree_with_the_oracle_rule():
     rng = np.random.default_rng(77)
     graphs = list(_f32_reduce_dags(61, 150)) + list(_broadcast_dags(62, 150))
     graphs += [configs.layernorm_graph(16, 64), configs.layernorm_shared_graph(16, 64)]
+    graphs += list(_gather_dags(60, 150))
     n_ok = n_bad = 0
     for g in graphs:
         n = len(g.ops)
@@ -400,7 +401,7 @@ def test_search_matches_the_oracle():
     from tests.test_oracle_partition import _f32_reduce_dags
     graphs = [configs.layernorm_shared_graph(16, 64), configs.layernorm_graph(16, 64),
               configs.c3_graph(8, 64, head_op=True), configs.c2_graph(4, 16)]
-    graphs += list(_f32_reduce_dags(63, 25)) + list(_broadcast_dags(64, 25))
+    graphs += list(_f32_reduce_dags(63, 25)) + list(_broadcast_dags(64, 25)) + list(_gather_dags(65, 25))
     for k, g in enumerate(graphs):
         for seed in (1, 2):
             plan, st = gtf.search(g, _lib_bytes_cost, seed=seed, max_stall=200)
@@ -411,3 +412,67 @@ def test_search_matches_the_oracle():
             assert [(o.op, o.inputs, o.output, np.float32(o.imm)) for o in p2.ops] == \
                 [(o.op, o.inputs, o.output, np.float32(o.imm)) for o in prog.ops]
             assert as_sets(plan.groups()) == as_sets(osr.groups_of(lab))
+
+
+def _gather_dags(seed, count):
+    """Small DAGs over [R,C] and [C,R] values (R=3, C=5) with transposes
+    between the two, reshapes, concats of [R,C] and [R,2] values, row sums
+    and elementwise work."""
+    rng = np.random.default_rng(seed)
+    R, Cc = 3, 5
+    for _ in range(count):
+        g = Graph()
+        rc = [g.input("x0", "f32", (R, Cc)), g.input("x1", "bf16", (R, Cc))]
+        cr = [g.input("y0", "f32", (Cc, R))]
+        side = [g.input("w0", "f32", (R, 2))]
+        rows = []
+        for i in range(int(rng.integers(1, 8))):
+            kind = int(rng.integers(0, 8))
+            pick = lambda xs: xs[int(rng.integers(len(xs)))]  # noqa: E731
+            if kind == 0:
+                rc.append(g.op(["exp", "relu", "neg"][int(rng.integers(3))], [pick(rc)], f"t{i}", "f32",
+                               (R, Cc)))
+            elif kind == 1:
+                rc.append(g.op(["add", "mul"][int(rng.integers(2))], [pick(rc), pick(rc)], f"t{i}", "f32",
+                               (R, Cc)))
+            elif kind == 2:
+                rc.append(g.op("transpose", [pick(cr)], f"t{i}", "f32", (R, Cc)))
+            elif kind == 3:
+                cr.append(g.op("transpose", [pick(rc)], f"t{i}", "f32", (Cc, R)))
+            elif kind == 4:
+                cr.append(g.op("reshape", [pick(rc)], f"t{i}", "f32", (Cc, R)))
+            elif kind == 5:
+                cr.append(g.op("neg", [pick(cr)], f"t{i}", "f32", (Cc, R)))
+            elif kind == 6:
+                a = pick(rc)
+                if g.tensors[a].dtype == "f32":
+                    c7 = g.op("concat", [a, side[0]], f"t{i}", "f32", (R, Cc + 2))
+                    g.op("row_sum", [c7], f"s{i}", "f32", (R, 1), role="out")
+            else:
+                rows.append(g.op("row_sum", [pick(rc)], f"t{i}", "f32", (R, 1)))
+        readers = {t for o in g.ops for t in o.inputs}
+        for o in g.ops:
+            t = o.output
+            if t not in readers or rng.random() < 0.1:
+                d = g.tensors[t]
+                g.tensors[t] = TensorDesc(d.name, d.dtype, d.shape, "out")
+        if g.ops:
+            yield g
+
+
+def test_gather_plans_match_the_oracle():
+    """Plans with transposes, reshapes and concats: the library's groups
+    equal the oracle's (phase 1 for injective sources; a gathering op only
+    as a load), with and without duplicate fusion and the row-resident
+    merge."""
+    n_fused = 0
+    for g in _gather_dags(71, 300):
+        for kw in ({}, {"row_resident": True}):
+            plan = gtf.FusePlan(g, **kw)
+            want = opart.partition(g, **kw)
+            assert as_sets(plan.groups()) == as_sets(want), [(o.op, o.inputs, o.output) for o in g.ops]
+            n_fused += any(len(grp) > 1 and any(g.ops[i].op in opart.GATHERS for i in grp) for grp in want)
+        plan = gtf.FusePlan(g, duplicate=True)
+        g2, origin = opart.duplicate(g)
+        assert plan.op_origin() == origin and as_sets(plan.groups()) == as_sets(opart.partition(g2))
+    assert n_fused >= 30

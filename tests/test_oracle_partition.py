@@ -421,3 +421,64 @@ def test_values_read_inside_their_group_are_not_rounded():
     assert not np.array_equal(one[b], two[b])
     # the stored output is the rounded quotient either way
     assert np.array_equal(one[a], qb.reshape(1, 4)) and np.array_equal(two[a], qb.reshape(1, 4))
+
+
+# ---------------------------------------------------------------- injective data movement
+def test_transpose_reshape_concat_values():
+    """The oracle's transpose, reshape and concat against their
+    definitions, element by element."""
+    from oracle import evaluate as oev
+    g = Graph()
+    x = g.input("x", "f32", (3, 5))
+    y = g.input("y", "bf16", (3, 2))
+    t = g.op("transpose", [x], "t", "f32", (5, 3), role="out")
+    r = g.op("reshape", [x], "r", "f32", (5, 3), role="out")
+    v = g.op("reshape", [x], "v", "f32", (15,), role="out")
+    c = g.op("concat", [x, g.input("z", "f32", (3, 2))], "c", "f32", (3, 7), role="out")
+    xs = np.arange(15, dtype=np.float32).reshape(3, 5)
+    zs = np.array([[100, 101], [102, 103], [104, 105]], dtype=np.float32)
+    out = oev.outputs(g, oev.evaluate(g, {x: xs, y: np.zeros((3, 2), np.uint16), 5: zs}))
+    for i in range(3):
+        for j in range(5):
+            assert out[t][j, i] == xs[i, j]                  # transpose
+            assert out[r].ravel()[i * 5 + j] == xs[i, j]     # row-major order kept
+            assert out[v][i * 5 + j] == xs[i, j]
+            assert out[c][i, j] == xs[i, j]
+        assert out[c][i, 5] == zs[i, 0] and out[c][i, 6] == zs[i, 1]
+    assert [pt.pattern(g, i) for i in range(4)] == [pt.K_INJECTIVE] * 4
+
+
+def test_injective_ops_fuse_by_phase_one_and_only_as_loads():
+    # transpose -> exp: an injective source fuses in phase 1 into an
+    # elementwise post-dominator
+    g = Graph()
+    x = g.input("x", "f32", (3, 5))
+    t = g.op("transpose", [x], "t", "f32", (5, 3))
+    g.op("exp", [t], "y", "f32", (5, 3), role="out")
+    assert as_sets(pt.partition(g)) == [[0, 1]]
+    # ... but not into a reduction (kInjective needs an injective-or-simpler sink)
+    g = Graph()
+    x = g.input("x", "f32", (3, 5))
+    t = g.op("transpose", [x], "t", "f32", (5, 3))
+    g.op("row_sum", [t], "s", "f32", (5, 1), role="out")
+    assert as_sets(pt.partition(g)) == [[0], [1]]
+    # exp -> transpose: TVM would fuse the elementwise producer into it; the
+    # executor reads a transpose's input from memory, so it stays apart
+    g = Graph()
+    x = g.input("x", "f32", (3, 5))
+    e = g.op("exp", [x], "e", "f32", (3, 5))
+    g.op("transpose", [e], "y", "f32", (5, 3), role="out")
+    assert as_sets(pt.partition(g)) == [[0], [1]]
+    # concat of two inputs feeding elementwise work: one group
+    g = Graph()
+    a = g.input("a", "f32", (4, 3))
+    b = g.input("b", "f32", (4, 5))
+    c = g.op("concat", [a, b], "c", "f32", (4, 8))
+    g.op("relu", [c], "y", "f32", (4, 8), role="out")
+    assert as_sets(pt.partition(g)) == [[0, 1]]
+    # a gathered input also read directly by another op of the would-be group
+    g = Graph()
+    x = g.input("x", "f32", (4, 4))
+    t = g.op("transpose", [x], "t", "f32", (4, 4))
+    g.op("add", [t, x], "y", "f32", (4, 4), role="out")
+    assert as_sets(pt.partition(g)) == [[0], [1]]

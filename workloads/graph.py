@@ -27,6 +27,10 @@ OP_ARITY = {
     "add": 2, "sub": 2, "mul": 2, "div": 2, "max": 2, "min": 2,
     "add3": 3, "dmul": 2,
     "row_sum": 1, "row_mean": 1,
+    # injective data movement: [R,C] -> [C,R]; any shape to any shape of
+    # the same element count (row-major order kept); [R,C1] ++ [R,C2] along
+    # the last axis
+    "transpose": 1, "reshape": 1, "concat": 2,
 }
 
 
