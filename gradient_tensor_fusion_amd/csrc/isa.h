@@ -78,6 +78,8 @@ enum Form : int {
   // concat along columns (element or column phase): slots arg & 0xFF and
   // arg >> 8, split at column imm; each side at its own strides
   F_LDC_F32_A, F_LDC_BF16_A,
+  // the item's transposed tile staged in LDS, into A (element phase)
+  F_LDT_A,
   F_COUNT
 };
 
@@ -135,6 +137,14 @@ struct ExecArgs {
   const uint32_t* m_vec;
   int32_t n_slots;
   int32_t slow_only;       // 1: every tile goes sub-tile by sub-tile (addressed loads)
+  // a transposed source staged per item in LDS (n_tr = 0 or 1): slot
+  // tr_slot holds X, the item's tile is X rows c0.. (domain columns) by
+  // elements r0.. (domain rows); tile row stride tr_stride > PW floats
+  // (every column a lane of a run may read, plus one)
+  int32_t n_tr, tr_slot, tr_bf16, tr_stride;
+  int32_t tr_off;          // the tile's offset in LDS, in floats
+  int32_t tr_vec;          // 1: the source allows 16-byte reads along its rows
+  int32_t tr_pad_;
   void* ptr[kMaxSlots];
   int64_t rstride[kMaxSlots];
   int64_t cstride[kMaxSlots];

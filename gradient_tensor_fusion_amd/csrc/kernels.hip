@@ -502,6 +502,14 @@ __device__ __forceinline__ void lds_vec(float (&d)[V], const float* x, int kstri
   }
 }
 
+// V values of one row of the staged transposed tile (row stride PW + 1,
+// so only 4-byte aligned): sub-tile k at x + k * kstride.
+template <int V>
+__device__ __forceinline__ void lds_tile(float (&d)[V], const float* x, int kstride) {
+#pragma unroll
+  for (int j = 0; j < V; ++j) d[j] = x[(j / kV) * kstride + j % kV];
+}
+
 // A op (column values), one sub-tile at a time: a scheduling barrier
 // between sub-tiles keeps the compiler from reading all V values from LDS
 // ahead of the arithmetic, which would hold V more registers.
@@ -553,7 +561,7 @@ __device__ __forceinline__ void fill(float (&d)[V], float x) {
 // run_prog executes instructions [pc0, n) on registers the caller owns, so
 // a program can be started before a phase barrier (its leading loads) and
 // finished after it; interpret runs a whole program on its own registers.
-template <int V, int MODE, bool FAST, int NS>
+template <int V, int MODE, bool FAST, int NS, bool TR = false>
 __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, int pc0, int n,
                                          const Tile& t, float (&A)[V], float (&B)[V],
                                          float (&S)[NS > 0 ? NS : 1][V], float* lds_col,
@@ -584,6 +592,9 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
         break;
       case F_LDC_BF16_A:
         if constexpr (MODE != M_ROW && V == kV) load_concat<V, MODE, FAST, true>(A, a, arg, cur.imm, t);
+        break;
+      case F_LDT_A:
+        if constexpr (MODE == M_ELEM && TR) lds_tile<V>(A, lds_col + a.tr_off + t.rr * a.tr_stride + t.cl, t.kstride);
         break;
       case F_COL_A: if (MODE == M_ELEM) lds_vec<V>(A, col, t.kstride); break;
       case F_ROW_A: if (MODE != M_COL) fill<V>(A, lds_row[arg * a.RB + t.rr]); break;
@@ -650,12 +661,12 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
   }
 }
 
-template <int V, int MODE, bool FAST, int NS>
+template <int V, int MODE, bool FAST, int NS, bool TR = false>
 __device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, int n,
                                           const Tile& t, float* lds_col, float* lds_row,
                                           float& acc, bool store_global) {
   float A[V], B[V], S[NS > 0 ? NS : 1][V];
-  run_prog<V, MODE, FAST, NS>(a, prog, 0, n, t, A, B, S, lds_col, lds_row, acc, store_global);
+  run_prog<V, MODE, FAST, NS, TR>(a, prog, 0, n, t, A, B, S, lds_col, lds_row, acc, store_global);
 }
 
 // ---------------------------------------------------------------- reduce tail
@@ -710,7 +721,7 @@ __device__ __forceinline__ void store_reduced(const ExecArgs& a, const StageDesc
 // way each lane adds its elements to the row accumulator in the same order.
 // A group with row-resident reductions walks the item once per stage,
 // with a row program (and barriers) between stages.
-template <int K, int NS>
+template <int K, int NS, bool TR>
 __global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NS == 0 ? 4 : 3)))
 exec_kernel(const ExecArgs a) {
   extern __shared__ float lds[];
@@ -771,8 +782,53 @@ exec_kernel(const ExecArgs a) {
       // from the last thread down) share one barrier pair, so their loads
       // overlap too.  A later stage always starts behind a barrier: its
       // row program and element program read the previous stage's results.
-      if ((st == 0 && col_now) || row_now || st > 0) {
+      if ((st == 0 && (col_now || TR)) || row_now || st > 0) {
         __syncthreads();
+        if constexpr (TR) {
+          // the item's tile of the transposed source X: tile row rr holds
+          // X[c0 + cl][r0 + rr] at column cl (row stride PW + 1, so a
+          // wave's column writes fall in different banks).  Thread tid
+          // covers row rr = tid % RB and columns tid / RB, + kBlock / RB,
+          // ...: consecutive threads read consecutive elements of one X
+          // row, a wave whole 64-element runs.
+          if (st == 0 && a.tr_bf16 && a.tr_vec && nr == a.RB) {
+            // whole row blocks of a 16-byte aligned bf16 source: each
+            // thread reads 8 consecutive elements (rows rr8 .. rr8 + 7 of
+            // the tile) of one X row with one 16-byte load
+            const int per = a.RB >> 3;                  // threads per X row
+            const int rr8 = (tid & (per - 1)) << 3;
+            const int step = kBlock / per;
+            const int64_t xrow = a.cstride[a.tr_slot];
+            const GAS uint16_t* src = (const GAS uint16_t*)ptrs[a.tr_slot] + c0 * xrow + r0 + rr8;
+            float* dst = lds + a.tr_off + rr8 * a.tr_stride;
+            for (int cl = tid / per; cl < a.PW; cl += step) {
+              float v[kV];
+              if (cl < nc) {
+                expand_bf16(v, *(const GAS u4*)(src + cl * xrow));
+              } else {
+#pragma unroll
+                for (int i = 0; i < kV; ++i) v[i] = 0.f;
+              }
+#pragma unroll
+              for (int i = 0; i < kV; ++i) dst[i * a.tr_stride + cl] = v[i];
+            }
+          } else if (st == 0) {
+            const int rr = tid & (a.RB - 1);
+            const int step = kBlock >> (8 - a.tpr_log2);  // kBlock / RB
+            const int64_t xrow = a.cstride[a.tr_slot];
+            float* dst = lds + a.tr_off + rr * a.tr_stride;
+            const bool row_ok = rr < nr;
+            if (a.tr_bf16) {
+              const GAS uint16_t* src = (const GAS uint16_t*)ptrs[a.tr_slot] + c0 * xrow + r0 + rr;
+              for (int cl = tid >> (8 - a.tpr_log2); cl < a.PW; cl += step)
+                dst[cl] = row_ok && cl < nc ? bf16_g(src + cl * xrow) : 0.f;
+            } else {
+              const GAS float* src = (const GAS float*)ptrs[a.tr_slot] + c0 * xrow + r0 + rr;
+              for (int cl = tid >> (8 - a.tpr_log2); cl < a.PW; cl += step)
+                dst[cl] = row_ok && cl < nc ? src[cl * xrow] : 0.f;
+            }
+          }
+        }
         if (st == 0 && col_now) {
           for (int c = tid * kV; c < nc; c += kBlock * kV) {
             const int cnt = min(kV, nc - c);
@@ -841,7 +897,7 @@ exec_kernel(const ExecArgs a) {
           t.kstride = ks;
           t.ptrs = ptrs;
           t.vmask = vmask;
-          interpret<K * kV, M_ELEM, true, NS>(a, el_prog, n_el, t, lds_col, lds_row, acc, true);
+          interpret<K * kV, M_ELEM, true, NS, TR>(a, el_prog, n_el, t, lds_col, lds_row, acc, true);
         } else {
 #pragma unroll 1
           for (int k = 0; k < K; ++k) {
@@ -860,7 +916,7 @@ exec_kernel(const ExecArgs a) {
             t.kstride = ks;
             t.ptrs = ptrs;
             t.vmask = vmask;
-            interpret<kV, M_ELEM, false, NS>(a, el_prog, n_el, t, lds_col, lds_row, acc, true);
+            interpret<kV, M_ELEM, false, NS, TR>(a, el_prog, n_el, t, lds_col, lds_row, acc, true);
           }
         }
         finish(rr);
@@ -870,9 +926,10 @@ exec_kernel(const ExecArgs a) {
   }
 }
 
-template __global__ void exec_kernel<kWideK, 0>(const ExecArgs a);
-template __global__ void exec_kernel<kWideK, kWideNS>(const ExecArgs a);
-template __global__ void exec_kernel<1, kNS>(const ExecArgs a);
+template __global__ void exec_kernel<kWideK, 0, false>(const ExecArgs a);
+template __global__ void exec_kernel<kWideK, 0, true>(const ExecArgs a);
+template __global__ void exec_kernel<kWideK, kWideNS, false>(const ExecArgs a);
+template __global__ void exec_kernel<1, kNS, false>(const ExecArgs a);
 
 // ---------------------------------------------------------------- buckets
 // One workgroup per chunk: a run of up to kChunkElems elements of one tensor
@@ -1004,19 +1061,20 @@ int device_cus(int dev) {
 }
 
 typedef void (*ExecFn)(const ExecArgs);
-ExecFn exec_instance(int K, int NS) {
-  if (K != kWideK) return exec_kernel<1, kNS>;
-  return NS == 0 ? exec_kernel<kWideK, 0> : exec_kernel<kWideK, kWideNS>;
+ExecFn exec_instance(int K, int NS, bool TR) {
+  if (K != kWideK) return exec_kernel<1, kNS, false>;
+  if (NS != 0) return exec_kernel<kWideK, kWideNS, false>;
+  return TR ? exec_kernel<kWideK, 0, true> : exec_kernel<kWideK, 0, false>;
 }
 
-int exec_occupancy(int dev, int K, int NS, int lds_bytes) {
+int exec_occupancy(int dev, int K, int NS, bool TR, int lds_bytes) {
   std::lock_guard<std::mutex> lk(g_mu);
   DevInfo& d = g_dev[dev];
-  const std::pair<int, int> key(K * 16 + NS, lds_bytes);
+  const std::pair<int, int> key(K * 16 + NS + (TR ? 256 : 0), lds_bytes);
   auto it = d.occ.find(key);
   if (it != d.occ.end()) return it->second;
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, exec_instance(K, NS), kBlock, lds_bytes) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, exec_instance(K, NS, TR), kBlock, lds_bytes) !=
           hipSuccess ||
       nb <= 0)
     nb = 2;
@@ -1037,10 +1095,10 @@ int launch_exec(const ExecArgs& a, int lds_bytes, hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  const int64_t resident = (int64_t)device_cus(dev) * exec_occupancy(dev, a.K, a.NS, lds_bytes);
+  const int64_t resident = (int64_t)device_cus(dev) * exec_occupancy(dev, a.K, a.NS, a.n_tr > 0, lds_bytes);
   const int64_t rounds = (a.n_items + resident - 1) / resident;
   const int64_t grid = (a.n_items + rounds - 1) / rounds;
-  hipLaunchKernelGGL(exec_instance(a.K, a.NS), dim3((unsigned)grid), dim3(kBlock), lds_bytes, stream, a);
+  hipLaunchKernelGGL(exec_instance(a.K, a.NS, a.n_tr > 0), dim3((unsigned)grid), dim3(kBlock), lds_bytes, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "exec_kernel launch");
   return GTF_OK;
@@ -1086,6 +1144,10 @@ int launch_group(const CompiledGroup& cg, void* const* tensor_ptrs, hipStream_t 
     const bool contiguous = a.cstride[s] == 1 && (a.rstride[s] == 0 || rows8);
     if (contiguous && ((uintptr_t)ptr % align) == 0) a.vec_slots |= 1u << s;
   }
+  // a staged bf16 transposed source reads 8 elements per load when its
+  // pointer and row pitch keep those loads 16-byte aligned
+  a.tr_vec = a.n_tr > 0 && a.tr_bf16 && ((uintptr_t)a.ptr[a.tr_slot] % 16) == 0 &&
+             (a.cstride[a.tr_slot] % kV) == 0;
   a.m_items = nullptr;
   return launch_exec(a, cg.lds_bytes, stream);
 }

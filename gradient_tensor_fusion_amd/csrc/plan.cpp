@@ -321,7 +321,9 @@ struct Codegen {
     const bool bf = p.tensors[m.src[0]].dtype == GTF_BF16;
     if (m.gkind == 0)
       emit(load_form(m.src[0], RA), ext_slot.at(m.src[0]));
-    else if (m.gkind == 1)
+    else if (m.gkind == 3 && ns == 0)  // the tile instance is the wide one without spill slots
+      emit(F_LDT_A, 0);
+    else if (m.gkind == 1 || m.gkind == 3)
       emit(bf ? F_LDG_BF16_A : F_LDG_F32_A, ext_slot.at(m.src[0]));
     else
       emit(bf ? F_LDC_BF16_A : F_LDC_F32_A, ext_slot.at(m.src[0]) | (ext_slot.at(m.src[1]) << 8),
@@ -405,6 +407,9 @@ const char* check_program(const ExecArgs& a, int n_slots) {
       } else if (f == F_LDC_F32_A || f == F_LDC_BF16_A) {
         if (phase == 1 || (arg & 0xFF) >= n_slots || (arg >> 8) >= n_slots)
           return "concat slots out of range";
+      } else if (f == F_LDT_A) {
+        if (phase != 2 || arg >= a.n_tr || a.tr_slot >= n_slots || a.tr_stride < a.PW + 1)
+          return "transposed tile out of range";
       } else if (f == F_COL_A || f == F_COL_B || (f >= F_ADD_C && f <= F_MIN_C)) {
         if (phase == 0 || arg >= a.n_col_slots) return "LDS column slot out of range";
       } else if (f == F_ROW_A || f == F_ROW_B || (f >= F_ADD_R && f <= F_MIN_R)) {
@@ -622,6 +627,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   // ---- lower each op to micro-ops
   std::map<int, std::vector<MOp>> mops_of;
   std::map<int, std::pair<int64_t, int64_t>> gather_stride;  // source tensor -> (rstride, cstride)
+  int n_tr = 0, tr_src = -1;  // the transposed source staged in LDS
   int synth = -1;
   for (int i : ops) {
     const OpInfo& o = p.ops[i];
@@ -652,9 +658,17 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
         gather_stride[o.in[0]] = {a.R == 1 ? 0 : a.C, 1};
         gather_stride[o.in[1]] = {b.R == 1 ? 0 : b.C, 1};
       } else if (o.opcode == GTF_OP_TRANSPOSE && ct == CLS_E) {
-        // T[r][c] = X[c][r]: X is [C, R] in domain terms
-        m.gkind = 1;
+        // T[r][c] = X[c][r]: X is [C, R] in domain terms.  One such source
+        // of a group without reductions is staged per item in LDS, read in
+        // coalesced X rows (tiled); others are read element by element
         gather_stride[o.in[0]] = {1, p.tensors[o.in[0]].C};
+        if (reds.empty() && n_tr == 0) {
+          m.gkind = 3;
+          n_tr = 1;
+          tr_src = o.in[0];
+        } else {
+          m.gkind = 1;
+        }
       } else {
         // reshape (row-major order kept), or a transpose of a vector, is
         // the result's own layout over the source's memory
@@ -936,6 +950,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     }
     if (ns < 0) return bad(w);
   }
+  if (ns != 0) n_tr = 0;  // the transposed source is read element by element instead
   const int K = ns == kNS ? 1 : kWideK;
 
   size_t total = 0;
@@ -964,6 +979,8 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     if (C8 > (int64_t)1 << 30) return bad("row too wide");
   } else if (flat) {
     pw = kBlock * kV * std::max(K, 2);
+  } else if (n_tr > 0) {
+    pw = (int)std::min<int64_t>(std::max<int64_t>(C8, kV), 128);  // 64-row by 128-column tiles
   } else {
     pw = (int)std::min<int64_t>(std::max<int64_t>(C8, kV), kPanelMax);
   }
@@ -979,6 +996,9 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     int f = std::atoi(e);
     if (f >= 1 && f <= kBlock && (f & (f - 1)) == 0) tpr = f;
   }
+  // a staged transposed tile is 64 rows (4 lanes per row) by at most 128
+  // columns: at most 64 x 129 floats of LDS
+  if (n_tr > 0) tpr = 4;
   const int rpp = kBlock / tpr;
   const int rb = rpp;
   const int64_t n_rb = DR == 0 ? 0 : (DR + rb - 1) / rb;
@@ -1045,7 +1065,20 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   for (int t : slots) cg.slot_dtype.push_back(p.tensors[t].dtype);
   cg.n_slots = (int)slots.size();
   cg.max_depth = max_depth;
-  cg.lds_bytes = (int)(a.n_col_slots * (int64_t)pw * 4 + a.n_row_slots * (int64_t)rb * 4 + 16 * 4);
+  a.n_tr = n_tr;
+  a.tr_slot = n_tr > 0 ? slot_for(tr_src) : 0;
+  a.tr_bf16 = n_tr > 0 && p.tensors[tr_src].dtype == GTF_BF16;
+  {
+    // a tile row spans every column a lane of a run may read, partial runs
+    // included (K sub-tiles of kV, tpr * kV apart), plus one float so that
+    // a wave's column writes fall in different banks
+    const int64_t ks_ = (int64_t)tpr * kV;
+    const int64_t span = ((pw + ks_ - 1) / ks_ + K - 1) / K * K * ks_;
+    a.tr_stride = (int)std::max<int64_t>(span, pw) + 1;
+  }
+  a.tr_off = a.n_col_slots * pw + a.n_row_slots * rb + 16;
+  cg.lds_bytes = (int)(a.n_col_slots * (int64_t)pw * 4 + a.n_row_slots * (int64_t)rb * 4 + 16 * 4 +
+                       (int64_t)n_tr * rb * a.tr_stride * 4);
   if (cg.lds_bytes > 64 * 1024) return bad("LDS staging exceeds 64 KiB");
   a.slow_only = 0;
   for (size_t k = 0; k < pos; ++k) {
