@@ -476,3 +476,67 @@ def test_gather_plans_match_the_oracle():
         g2, origin = opart.duplicate(g)
         assert plan.op_origin() == origin and as_sets(plan.groups()) == as_sets(opart.partition(g2))
     assert n_fused >= 30
+
+
+def test_new_entry_point_errors():
+    """Error behaviour of the grouped-plan, search and program entry points
+    and of the data-movement ops' shape checks (host only)."""
+    L = C.lib()
+    x = T("x", "f32", (2, 3), "in")
+    # transpose / reshape / concat shapes
+    assert _desc_status([x, T("t", "f32", (3, 2), "out")], [OpDesc("transpose", (0,), 1)]) == C.GTF_OK
+    assert _desc_status([x, T("t", "f32", (2, 3), "out")], [OpDesc("transpose", (0,), 1)]) == C.GTF_E_SHAPE
+    assert _desc_status([T("v", "f32", (6,), "in"), T("t", "f32", (6, 1), "out")],
+                        [OpDesc("transpose", (0,), 1)]) == C.GTF_E_SHAPE   # rank 1
+    assert _desc_status([x, T("r", "f32", (6,), "out")], [OpDesc("reshape", (0,), 1)]) == C.GTF_OK
+    assert _desc_status([x, T("r", "f32", (7,), "out")], [OpDesc("reshape", (0,), 1)]) == C.GTF_E_SHAPE
+    z = T("z", "f32", (2, 4), "in")
+    assert _desc_status([x, z, T("c", "f32", (2, 7), "out")], [OpDesc("concat", (0, 1), 2)]) == C.GTF_OK
+    assert _desc_status([x, z, T("c", "f32", (2, 8), "out")], [OpDesc("concat", (0, 1), 2)]) == C.GTF_E_SHAPE
+    assert _desc_status([x, T("w", "f32", (3, 4), "in"), T("c", "f32", (2, 7), "out")],
+                        [OpDesc("concat", (0, 1), 2)]) == C.GTF_E_SHAPE   # row counts differ
+    assert _desc_status([x, T("w", "bf16", (2, 4), "in"), T("c", "f32", (2, 7), "out")],
+                        [OpDesc("concat", (0, 1), 2)]) == C.GTF_E_UNSUPPORTED   # two dtypes
+    # grouped plans: a cycle, a negative label, NULL labels
+    g = Graph()
+    a = g.input("a", "f32", (4, 8))
+    b = g.op("exp", [a], "b", "f32", (4, 8))
+    c = g.op("neg", [b], "c", "f32", (4, 8))
+    g.op("relu", [c], "d", "f32", (4, 8), role="out")
+    assert gtf.FusePlan.grouped(g, [0, 0, 0]).num_groups == 1
+    for lab in ([0, 1, 0], [0, -1, 0]):
+        with pytest.raises(gtf.GtfError) as e:
+            gtf.FusePlan.grouped(g, lab)
+        assert e.value.status == C.GTF_E_INVALID
+    desc, tens, ops = gtf._program_desc(g)
+    h = ctypes.c_void_p()
+    assert L.fuse_plan_create_grouped(ctypes.byref(desc), None, ctypes.byref(h)) == C.GTF_E_INVALID
+    assert h.value is None
+    assert L.fuse_plan_create_grouped(ctypes.byref(desc), None, None) == C.GTF_E_INVALID
+    # search: bad parameters, a failing cost, an exception in the cost
+    with pytest.raises(gtf.GtfError) as e:
+        gtf.search(g, lambda p: 1.0, alpha=0.5)
+    assert e.value.status == C.GTF_E_INVALID
+    with pytest.raises(gtf.GtfError) as e:
+        gtf.search(g, lambda p: -1.0)
+    assert e.value.status == C.GTF_E_INVALID and b"cost" in L.gtf_last_error()
+    with pytest.raises(ZeroDivisionError):
+        gtf.search(g, lambda p: 1 / 0)
+    # the search's plan is the best it costed: a cost that prefers fewer
+    # launches ends with one group
+    best, st = gtf.search(g, lambda p: float(p.num_groups), max_stall=50)
+    assert best.num_groups == 1 and st["best_cost"] == 1.0 and st["start_cost"] == 3.0
+    # program: capacities
+    plan = gtf.FusePlan(g)
+    nt, no = ctypes.c_int32(), ctypes.c_int32()
+    assert L.fuse_plan_program(plan._h, None, 0, ctypes.byref(nt), None, 0, ctypes.byref(no)) == 0
+    assert (nt.value, no.value) == (4, 3)
+    small = (C.TensorDesc * 1)()
+    assert L.fuse_plan_program(plan._h, small, 1, None, None, 0, None) == C.GTF_E_LIMIT
+    assert plan.program().ops == g.ops
+    # group tensors: capacity and index
+    n = ctypes.c_int32()
+    assert L.fuse_plan_group_tensors(plan._h, 5, None, 0, ctypes.byref(n)) == C.GTF_E_INVALID
+    assert L.fuse_plan_group_tensors(plan._h, 0, None, 0, ctypes.byref(n)) == 0 and n.value == 2
+    one = (ctypes.c_int32 * 1)()
+    assert L.fuse_plan_group_tensors(plan._h, 0, one, 1, ctypes.byref(n)) == C.GTF_E_LIMIT
