@@ -22,6 +22,13 @@ unfused baseline (one launch per op, intermediates stored) and the
 per-tensor bucket baseline run the same data after the timed region.  The
 CPU baseline times the oracle on a bounded sample of the same workload.
 
+"groups" breaks the executor down per c5 group: its average launch time
+(one event pair around its 12 back-to-back launches, three times), its
+algorithmic bytes and GB/s against 8 TB/s, and, from the committed
+SQ_INSTS_VALU summary of the same kernel sources, its VALU lane-instruction
+rate against the non-packed fp32 issue peak (256 CUs x 4 SIMDs x 16 lanes x
+2.4 GHz); "bound" names the larger fraction.
+
 Other workloads (--workload c1..c4) rotate through enough buffer sets to
 exceed 1 GiB, so the Infinity Cache cannot serve repeated reads.
 """
@@ -39,6 +46,9 @@ if ROOT not in sys.path:
 
 METRIC = "fused-group HBM GB/s (% of peak) + speedup vs unfused; bucket pack GB/s"
 PEAK_GBS = 8000.0
+# fp32 VALU issue peak without packed math (this build compiles packed fp32
+# off): 256 CUs x 4 SIMDs x 16 lanes per cycle x 2.4 GHz lane-instructions/s
+VALU_PEAK = 256 * 4 * 16 * 2.4e9
 ELEM = {"f32": 4, "bf16": 2, "u8": 1}
 
 
@@ -47,8 +57,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "joint", "ln", "search", "transpose"])
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "joint", "ln", "search", "transpose",
+                             "groups"])
     ap.add_argument("--layers", type=int, default=12)
+    ap.add_argument("--valu-from", metavar="VALU_CSV",
+                    help="summarise a rocprofv3 SQ_INSTS_VALU/SQ_WAVES run of --workload groups "
+                         "into profiles/valu_c5_groups.txt")
     ap.add_argument("--ln-variant", default="all",
                     choices=["all", "row_resident", "tvm_groups", "unfused", "shared_center",
                              "shared_center_duplicated"],
@@ -191,6 +205,19 @@ class C5:
         self.bucket_calls = [self.bp.launcher(False, self.grads, self.buckets, self.scale),
                              self.bp.launcher(True, self.grads, self.buckets, 1.0)]
 
+    GROUP_NAMES = {"ln": ("ln_mean", "ln_var", "ln_normalise"), "ge": ("bias_gelu",),
+                   "do": ("dropout_residual",)}
+
+    def group_calls(self):
+        """Per c5 group, its launch in every layer (marshalled once)."""
+        out = {}
+        for k in ("ln", "ge", "do"):
+            plan = self.p[k]
+            for g in range(plan.num_groups):
+                out[self.GROUP_NAMES[k][g]] = ([plan.launcher(g, L[k]) for L in self.layers],
+                                               self.gbytes[k][g])
+        return out
+
     def step(self, exec_t=None, bucket_t=None, per_tensor=False):
         if per_tensor:
             for f in self.exec_calls:
@@ -311,6 +338,9 @@ def main():
     if args.traffic_from:
         print(json.dumps(summarise_traffic(*args.traffic_from, workload=args.workload)))
         return
+    if args.valu_from:
+        print(json.dumps(summarise_valu(args.valu_from, args.layers)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused groups shard by rows with no exchange "
               "and the buckets would feed an all-reduce that this build does not run; "
@@ -322,6 +352,17 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.workload == "groups":
+        # each c5 group launched once per layer, group after group, nothing
+        # else on the GPU: the dispatch order the VALU summary relies on
+        w = C5(torch, gtf, configs, args.layers)
+        torch.cuda.synchronize()
+        for name, (calls, nbytes) in w.group_calls().items():
+            for f in calls:
+                f()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": "groups", "order": list(w.group_calls())}), flush=True)
+        return
     if args.workload != "c5":
         print(json.dumps(run_config(torch, gtf, configs, args)), flush=True)
         return
@@ -341,6 +382,31 @@ def main():
     for _ in range(args.steps):
         w.step(exec_t=et, bucket_t=bt)
     torch.cuda.synchronize()
+    # per group: one event pair around its 12 back-to-back launches (one
+    # per layer), three times, behind a queued lead
+    groups = {}
+    gt = Timer(torch, 3 * 5)
+    torch.cuda.synchronize()
+    cb.lead()
+    for name, (calls, nbytes) in w.group_calls().items():
+        t0 = gt.i
+        for _ in range(3):
+            gt.block(calls)
+        groups[name] = (t0, len(calls), nbytes)
+    torch.cuda.synchronize()
+    valu = read_valu()
+    group_rows = {}
+    for name, (t0, n, nbytes) in groups.items():
+        gms = sum(gt.ev[i][0].elapsed_time(gt.ev[i][1]) for i in range(t0, t0 + 3)) / (3 * n)
+        row = {"avg_launch_us": round(gms * 1e3, 3), "bytes_per_launch": nbytes,
+               "gbs": round(nbytes / (gms * 1e-3) / 1e9, 1),
+               "hbm_frac": round(nbytes / (gms * 1e-3) / 1e9 / PEAK_GBS, 4)}
+        if valu and name in valu:
+            rate = valu[name] / (gms * 1e-3)
+            row["valu_lane_instr_per_launch"] = valu[name]
+            row["valu_frac"] = round(rate / VALU_PEAK, 4)
+        row["bound"] = "alu" if row.get("valu_frac", 0) > row["hbm_frac"] else "hbm"
+        group_rows[name] = row
     copy_gbs, copy_ms = cb.gbs()
     del cb
     exec_ms = et.total_ms() / args.steps
@@ -377,6 +443,7 @@ def main():
                      "traffic": traffic, "kernel": dom["kernel"],
                      "avg_launch_us": dom["avg_launch_us"],
                      "algorithmic_bytes_per_launch": round(dom["bytes_per_launch"])},
+        "groups": group_rows,
         "breakdown": {"exec_ms_per_step": round(exec_ms, 4), "exec_gbs": round(exec_gbs, 1),
                       "bucket_ms_per_step": round(bucket_ms, 4), "bucket_gbs": round(bucket_gbs, 1),
                       "wall_s_timed": round(wall, 3),
@@ -629,6 +696,55 @@ def summarise_traffic(fetch_csv, write_csv, workload="c5"):
     with open(traffic_file(workload), "w") as f:
         f.write("\n".join(lines) + "\n")
     return res
+
+
+VALU_FILE = os.path.join(ROOT, "profiles", "valu_c5_groups.txt")
+VALU_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc SQ_INSTS_VALU SQ_WAVES "
+            "-d $R/gpurun_out/pmc_valu -o valu --output-format csv -- python3 $R/bench.py "
+            "--workload groups")
+
+
+def summarise_valu(csv_path, layers):
+    """VALU lane-instructions per launch of each c5 group, from a rocprofv3
+    SQ_INSTS_VALU run of --workload groups (each group's launches back to
+    back, in C5.group_calls order).  SQ_INSTS_VALU counts wave instructions;
+    every wave of these launches is full, so lane instructions are 64x."""
+    import csv
+    per = {}
+    for row in csv.DictReader(open(csv_path, newline="")):
+        if "gtf::exec_kernel" not in row["Kernel_Name"]:
+            continue
+        per.setdefault(int(row["Dispatch_Id"]), {})[row["Counter_Name"]] = float(row["Counter_Value"])
+    ids = sorted(per)
+    names = [n for k in ("ln", "ge", "do") for n in C5.GROUP_NAMES[k]]
+    assert len(ids) == layers * len(names), (len(ids), layers)
+    res = {"source_hash": _kernel_hash(), "lanes_per_wave": 64, "groups": {}}
+    for gi, name in enumerate(names):
+        chunk = [per[i] for i in ids[gi * layers:(gi + 1) * layers]]
+        res["groups"][name] = {
+            "valu_lane_instr_per_launch": round(64 * sum(c["SQ_INSTS_VALU"] for c in chunk) / layers),
+            "waves_per_launch": round(sum(c["SQ_WAVES"] for c in chunk) / layers)}
+    with open(VALU_FILE, "w") as f:
+        f.write("# VALU lane-instructions per launch of each c5 group (rocprofv3 SQ_INSTS_VALU x 64)\n")
+        f.write("# command (R = repository root):\n#   " + VALU_CMD + "\n")
+        f.write("#   python3 bench.py --valu-from <valu>_counter_collection.csv\n")
+        f.write(json.dumps(res) + "\n")
+    return res
+
+
+def read_valu():
+    """{group: VALU lane-instructions per launch}, or None when absent or
+    taken from another version of the kernel sources."""
+    if not os.path.exists(VALU_FILE):
+        return None
+    with open(VALU_FILE) as f:
+        js = [ln for ln in f if ln.startswith("{")]
+    if not js:
+        return None
+    tj = json.loads(js[-1])
+    if tj.get("source_hash") != _kernel_hash():
+        return None
+    return {k: v["valu_lane_instr_per_launch"] for k, v in tj["groups"].items()}
 
 
 def read_traffic(kernel, workload="c5"):
