@@ -46,8 +46,8 @@ if ROOT not in sys.path:
 
 METRIC = "fused-group HBM GB/s (% of peak) + speedup vs unfused; bucket pack GB/s"
 PEAK_GBS = 8000.0
-# fp32 VALU issue peak without packed math (this build compiles packed fp32
-# off): 256 CUs x 4 SIMDs x 16 lanes per cycle x 2.4 GHz lane-instructions/s
+# fp32 VALU issue peak without packed math (the kernels are compiled with
+# packed fp32 off): 256 CUs x 4 SIMDs x 16 lanes per cycle x 2.4 GHz lane-instructions/s
 VALU_PEAK = 256 * 4 * 16 * 2.4e9
 ELEM = {"f32": 4, "bf16": 2, "u8": 1}
 
@@ -343,7 +343,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused groups shard by rows with no exchange "
-              "and the buckets would feed an all-reduce that this build does not run; "
+              "and the buckets would feed an all-reduce that is not part of this library; "
               "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
@@ -647,9 +647,9 @@ def traffic_cmds(workload):
     run = f"python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-baselines{extra}"
     return (
         "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE "
-        f"-d $R/gpurun_out/pmc_fetch -o fetch --output-format csv -- {run}",
+        f"-d $OUT/pmc_fetch -o fetch --output-format csv -- {run}",
         "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE "
-        f"-d $R/gpurun_out/pmc_write -o write --output-format csv -- {run}",
+        f"-d $OUT/pmc_write -o write --output-format csv -- {run}",
         f"python3 bench.py --workload {workload} --traffic-from <fetch>_counter_collection.csv "
         "<write>_counter_collection.csv")
 
@@ -690,7 +690,7 @@ def summarise_traffic(fetch_csv, write_csv, workload="c5"):
     lines = [f"# HBM traffic per launch of the {workload} workload's kernels: rocprofv3 FETCH_SIZE "
              "and WRITE_SIZE (KiB per dispatch), each scaled so that the 1 GiB copy kernel in "
              "the same run counts exactly 1 GiB read and 1 GiB written.",
-             "# commands (R = repository root):"]
+             "# commands (R = repository root, OUT = an output directory):"]
     lines += ["#   " + c for c in traffic_cmds(workload)]
     lines.append(json.dumps(res))
     with open(traffic_file(workload), "w") as f:
@@ -700,7 +700,7 @@ def summarise_traffic(fetch_csv, write_csv, workload="c5"):
 
 VALU_FILE = os.path.join(ROOT, "profiles", "valu_c5_groups.txt")
 VALU_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc SQ_INSTS_VALU SQ_WAVES "
-            "-d $R/gpurun_out/pmc_valu -o valu --output-format csv -- python3 $R/bench.py "
+            "-d $OUT/pmc_valu -o valu --output-format csv -- python3 $R/bench.py "
             "--workload groups")
 
 
@@ -726,7 +726,7 @@ def summarise_valu(csv_path, layers):
             "waves_per_launch": round(sum(c["SQ_WAVES"] for c in chunk) / layers)}
     with open(VALU_FILE, "w") as f:
         f.write("# VALU lane-instructions per launch of each c5 group (rocprofv3 SQ_INSTS_VALU x 64)\n")
-        f.write("# command (R = repository root):\n#   " + VALU_CMD + "\n")
+        f.write("# command (R = repository root, OUT = an output directory):\n#   " + VALU_CMD + "\n")
         f.write("#   python3 bench.py --valu-from <valu>_counter_collection.csv\n")
         f.write(json.dumps(res) + "\n")
     return res

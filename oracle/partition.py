@@ -27,7 +27,7 @@ Follows Apache TVM, "Operator Fusion" (docs/arch/fusion.rst), in its order:
      kOpaque       : never fuses (a barrier).
    Limits: at most 256 ops per group (kMaxFusedOps) and at most
    MAX_GROUP_ARGS external tensors per group (the page names an argument
-   limit without its value; 16 is this build's reading).  CommitFuse puts
+   limit without its value; 16 is the reading taken here).  CommitFuse puts
    n, d and every node on a path between them into one group (union-find).
 
 Readings where the page is silent: the source's pattern is its group's
