@@ -80,6 +80,9 @@ enum Form : int {
   F_LDC_F32_A, F_LDC_BF16_A,
   // the item's transposed tile staged in LDS, into A (element phase)
   F_LDT_A,
+  // A = gelu(A) to about 1e-5 relative, for a result that is rounded to
+  // bf16 and read by nothing else
+  F_GELU_BF,
   F_COUNT
 };
 

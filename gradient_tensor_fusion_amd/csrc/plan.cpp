@@ -805,6 +805,21 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
         for (auto& m : mops_of[i]) pe.L.push_back(m);
     progs.push_back(pe);
   }
+  // A GELU whose value is only rounded to bf16 and stored (no op of the
+  // plan reads the tensor) takes the cheaper form, accurate to far below
+  // bf16's half ulp
+  {
+    std::set<int> read;
+    for (const auto& o : p.ops)
+      for (int k = 0; k < o.n_in; ++k) read.insert(o.in[k]);
+    for (auto& P : progs) {
+      if (P.kind != P_EL) continue;
+      for (auto& m : P.L)
+        if (m.kind == 0 && m.form == F_GELU && m.out >= 0 && P.store.count(m.out) &&
+            !read.count(m.out) && p.tensors[m.out].dtype == GTF_BF16)
+          m.form = F_GELU_BF;
+    }
+  }
 
   // ---- code generation, program by program; first for the wide instance
   // without spill slots, then with two, else for the narrow one

@@ -18,7 +18,7 @@ from oracle import evaluate as oev
 from oracle import numerics
 from oracle import partition as opart
 from tests.gpu_util import (announce, assert_bf16_close, assert_bits_equal, assert_close_scaled,
-                            assert_f32_rel,
+                            assert_f32_rel, bf16_ulps,
                             assert_reduce_close, gpu_run, oracle_run, reduce_bound, to_device,
                             to_host)
 from tests.test_capi_host import _broadcast_dags
@@ -339,6 +339,60 @@ def test_transcendentals_fp32_accuracy():
             assert_f32_rel(got[t][keep], want[t][keep], 1e-6)
         else:
             assert_f32_rel(got[t], want[t], 1e-6)
+
+
+def _all_bf16_but_nan():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = numerics.bf16_to_f32(b)
+    return np.where(np.isnan(f), np.uint16(0), b).reshape(256, 256)
+
+
+def test_gelu_rounded_to_bf16_every_input():
+    """A GELU stored only as bf16 takes the short form; over every bf16
+    input it stays within one bf16 ulp of the exact GELU rounded, and off
+    it for very few normal inputs.  Below x = -12 the result nears fp32's
+    subnormal range, where the exponential flushes: there only closeness
+    in absolute terms is asked for."""
+    g = Graph()
+    x = g.input("x", "bf16", (256, 256))
+    g.op("gelu", [x], "y", "bf16", (256, 256), role="out")
+    ins = {x: _all_bf16_but_nan()}
+    _, got = gpu_run(g, ins)
+    _, want = oracle_run(g, ins)
+    xs = numerics.bf16_to_f32(ins[x]).ravel()
+    gy, wy = got[1].view(np.uint16).ravel(), want[1].view(np.uint16).ravel()
+    keep = xs > -12.0
+    assert_bf16_close(gy[keep], wy[keep], 1)
+    # a subnormal input's half is often a bf16 rounding tie, where any error
+    # at all picks the side; among normal inputs the two roundings differ
+    # for a handful of them
+    normal = keep & (np.abs(xs) >= 2.0 ** -125)
+    assert np.mean(bf16_ulps(gy[normal], wy[normal]) > 0) < 1e-3
+    tail = ~keep & np.isfinite(xs)
+    d = np.abs(numerics.bf16_to_f32(gy[tail]).astype(np.float64) -
+               numerics.bf16_to_f32(wy[tail]).astype(np.float64))
+    assert np.all(d <= 1e-36)
+
+
+def test_gelu_read_again_keeps_full_accuracy():
+    """A GELU stored as bf16 and also read by another op of its group (a
+    grouping the fusion rules do not make, since an output is a barrier
+    there) keeps the full form: the reader sees the unrounded fp32 value,
+    so its fp32 output z = y * 1 must match the oracle's evaluation of the
+    same grouping to fp32's elementwise tolerance."""
+    g = Graph()
+    x = g.input("x", "f32", (64, 1024))
+    y = g.op("gelu", [x], "y", "bf16", (64, 1024), role="out")
+    z = g.op("mul_imm", [y], "z", "f32", (64, 1024), role="out", imm=1.0)
+    xs = np.linspace(-10, 10, 64 * 1024).astype(np.float32).reshape(64, 1024)
+    ins = {x: xs}
+    plan = gtf.FusePlan.grouped(g, [0, 0])
+    assert plan.num_groups == 1
+    _, got = gpu_run(g, ins, plan=plan)
+    groups = plan.groups()
+    _, want = oev.run(g, ins, stored=opart.stored_tensors(g, groups), groups=groups)
+    assert_f32_rel(got[z], want[z], 1e-6)
+    assert_bf16_close(got[y], want[y], 1)
 
 
 def test_ieee_ops_bit_exact_including_division_and_sqrt():
