@@ -53,10 +53,21 @@ typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- numerics
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  // fp32 -> bf16 round to nearest even (one v_cvt_pk_bf16_f32 on gfx950)
+  // fp32 -> bf16 round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
   const __bf16 a = (__bf16)lo;
   const __bf16 b = (__bf16)hi;
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+// The same for two values stored side by side, both halves in one
+// v_cvt_pk_bf16_f32 (round to nearest even, like the compiler's own
+// conversion).  The compiler converts pack_bf16's halves one by one and
+// joins them with a shift and an or; written as a two-lane vector
+// conversion it does pair them, but then schedules the interpreter's
+// store case so that other instances spill.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -447,8 +458,8 @@ __device__ __forceinline__ void store_bf16(const float (&s)[V], const ExecArgs& 
       GAS uint16_t* p = b + base;
 #pragma unroll
       for (int k = 0; k < V / kV; ++k) {
-        const u4 w = {pack_bf16(s[k * kV], s[k * kV + 1]), pack_bf16(s[k * kV + 2], s[k * kV + 3]),
-                      pack_bf16(s[k * kV + 4], s[k * kV + 5]), pack_bf16(s[k * kV + 6], s[k * kV + 7])};
+        const u4 w = {pack2_bf16(s[k * kV], s[k * kV + 1]), pack2_bf16(s[k * kV + 2], s[k * kV + 3]),
+                      pack2_bf16(s[k * kV + 4], s[k * kV + 5]), pack2_bf16(s[k * kV + 6], s[k * kV + 7])};
         *(GAS u4*)(p + k * t.kstride) = w;
       }
       return;
@@ -693,6 +704,10 @@ __device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, 
                                           const Tile& t, float* lds_col, float* lds_row,
                                           float& acc, bool store_global) {
   float A[V], B[V], S[NS > 0 ? NS : 1][V];
+  // a program writes a register before reading it; left undefined, the
+  // registers would be zeroed on every call (one move each per tile)
+#pragma unroll
+  for (int i = 0; i < V; ++i) asm volatile("" : "=v"(A[i]), "=v"(B[i]));
   run_prog<V, MODE, FAST, NS, TR>(a, prog, 0, n, t, A, B, S, lds_col, lds_row, acc, store_global);
 }
 
