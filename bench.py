@@ -58,7 +58,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "joint", "ln", "search", "transpose",
-                             "groups"])
+                             "groups", "softmax"])
     ap.add_argument("--layers", type=int, default=12)
     ap.add_argument("--valu-from", metavar="VALU_CSV",
                     help="summarise a rocprofv3 SQ_INSTS_VALU/SQ_WAVES run of --workload groups "
@@ -531,6 +531,8 @@ def run_config(torch, gtf, configs, args):
         return run_ln(torch, gtf, configs, args, res, gen)
     if w == "search":
         return run_search(torch, gtf, configs, args, res, gen)
+    if w == "softmax":
+        return run_softmax(torch, gtf, configs, args, res, gen)
     if w == "transpose":
         return run_transpose(torch, gtf, configs, args, res, gen)
     if w == "c1":
@@ -633,6 +635,40 @@ def run_ln(torch, gtf, configs, args, res, gen):
                 "speedup_vs_unfused": round(out["unfused"]["ms_per_step"] / rr["ms_per_step"], 3),
                 "duplicate_fusion_speedup": round(out["shared_center"]["ms_per_step"]
                                                   / out["shared_center_duplicated"]["ms_per_step"], 3),
+                "variants": out})
+    return res
+
+
+SM_D = {"X": ("normal", 0.0, 2.0)}
+
+
+def run_softmax(torch, gtf, configs, args, res, gen):
+    """Row softmax over bf16[131072,128] (the attention probabilities of 8192
+    tokens in 64 sequences of 128, 16 heads): one row-resident launch (max
+    and sum held in LDS), TVM's three groups (max, then exp and sum, then
+    the output; max and sum through HBM), and one launch per op.  Each is
+    captured in a HIP graph over its rotation sets and replayed."""
+    g = configs.softmax_graph()
+    plans = {"row_resident": lambda: gtf.FusePlan(g, row_resident=True),
+             "tvm_groups": lambda: gtf.FusePlan(g),
+             "unfused": lambda: gtf.FusePlan(g, fuse=False)}
+    out = {}
+    for name, make in plans.items():
+        plan = make()
+        ms, nbytes = time_plan(torch, gtf, g, plan, gen, SM_D, args.steps, args.warmup)
+        out[name] = {"ms_per_step": round(ms, 5), "bytes": nbytes, "launches": plan.num_groups,
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+    rr = out["row_resident"]
+    res.update({"value": rr["gbs"], "ms_per_step": rr["ms_per_step"], "dtype": "bf16",
+                "config": {"workload": "softmax: row softmax bf16[131072,128], one row-resident "
+                                       "launch", "bytes_per_step": rr["bytes"]},
+                "roofline": {"bound": "hbm", "achieved": rr["gbs"], "peak": PEAK_GBS, "unit": "GB/s",
+                             "frac": round(rr["gbs"] / PEAK_GBS, 4), "traffic": None,
+                             "kernel": "exec_kernel", "avg_launch_us": round(rr["ms_per_step"] * 1e3, 3),
+                             "algorithmic_bytes_per_launch": rr["bytes"]},
+                "timing": "graph replays over the rotation sets",
+                "speedup_vs_tvm_groups": round(out["tvm_groups"]["ms_per_step"] / rr["ms_per_step"], 3),
+                "speedup_vs_unfused": round(out["unfused"]["ms_per_step"] / rr["ms_per_step"], 3),
                 "variants": out})
     return res
 

@@ -127,8 +127,11 @@ class FusePlan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value and C._lib is not None:
-            C._lib.fuse_plan_destroy(h)
+        # at interpreter exit the module's globals may already be gone; the
+        # process frees the plan then anyway
+        lib = getattr(C, "_lib", None) if C is not None else None
+        if h is not None and h.value and lib is not None:
+            lib.fuse_plan_destroy(h)
             self._h = None
 
     @property
@@ -258,8 +261,11 @@ class FuseMulti:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value and C._lib is not None:
-            C._lib.fuse_multi_destroy(h)
+        # at interpreter exit the module's globals may already be gone; the
+        # process frees the plan then anyway
+        lib = getattr(C, "_lib", None) if C is not None else None
+        if h is not None and h.value and lib is not None:
+            lib.fuse_multi_destroy(h)
             self._h = None
 
     @property
@@ -306,8 +312,11 @@ class BucketPlan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value and C._lib is not None:
-            C._lib.bucket_plan_destroy(h)
+        # at interpreter exit the module's globals may already be gone; the
+        # process frees the plan then anyway
+        lib = getattr(C, "_lib", None) if C is not None else None
+        if h is not None and h.value and lib is not None:
+            lib.bucket_plan_destroy(h)
             self._h = None
 
     def query(self):

@@ -53,7 +53,8 @@ int arity(int opc) {
     case GTF_OP_COPY: case GTF_OP_EXP: case GTF_OP_TANH: case GTF_OP_SIGMOID:
     case GTF_OP_RELU: case GTF_OP_GELU: case GTF_OP_SQUARE: case GTF_OP_SQRT:
     case GTF_OP_RECIP: case GTF_OP_NEG: case GTF_OP_ADD_IMM: case GTF_OP_MUL_IMM:
-    case GTF_OP_ROW_SUM: case GTF_OP_ROW_MEAN: case GTF_OP_TRANSPOSE: case GTF_OP_RESHAPE:
+    case GTF_OP_ROW_SUM: case GTF_OP_ROW_MEAN: case GTF_OP_ROW_MAX: case GTF_OP_TRANSPOSE:
+    case GTF_OP_RESHAPE:
       return 1;
     case GTF_OP_ADD: case GTF_OP_SUB: case GTF_OP_MUL: case GTF_OP_DIV:
     case GTF_OP_MAX: case GTF_OP_MIN: case GTF_OP_DMUL: case GTF_OP_CONCAT:
@@ -127,7 +128,7 @@ int validate(const gtf_program_desc* d, FusePlan* p) {
     o.flags = od.flags;
     // shapes
     const TensorInfo& to = p->tensors[out];
-    if (od.opcode == GTF_OP_ROW_SUM || od.opcode == GTF_OP_ROW_MEAN) {
+    if (od.opcode == GTF_OP_ROW_SUM || od.opcode == GTF_OP_ROW_MEAN || od.opcode == GTF_OP_ROW_MAX) {
       const TensorInfo& ti = p->tensors[od.in[0]];
       if (d->tensors[out].rank != 2 || to.R != ti.R || to.C != 1)
         return fail(GTF_E_SHAPE, op_name(i) + ": a row reduction of [R,C] is declared [R,1]");

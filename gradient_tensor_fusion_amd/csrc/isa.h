@@ -83,6 +83,8 @@ enum Form : int {
   // A = gelu(A) to about 1e-5 relative, for a result that is rounded to
   // bf16 and read by nothing else
   F_GELU_BF,
+  // fold A into the row accumulator with max (element phase)
+  F_RED_MAX,
   F_COUNT
 };
 
@@ -113,7 +115,7 @@ struct MultiItem {
 struct StageDesc {
   int32_t row_off, row_len;  // row program (instruction offset, length)
   int32_t el_off, el_len;    // element program
-  int32_t red;               // 0 none, 1 row sum, 2 row mean
+  int32_t red;               // 0 none, 1 row sum, 2 row mean, 3 row max
   int32_t red_lds;           // LDS row slot for the result, or -1
   int32_t red_slot;          // external slot for the result, or -1
   int32_t red_dtype;         // its dtype

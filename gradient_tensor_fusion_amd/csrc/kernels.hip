@@ -684,6 +684,12 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
           for (int i = 0; i < V; ++i) acc += (FAST || (t.valid && i < t.cnt)) ? A[i] : 0.f;
         }
         break;
+      case F_RED_MAX:
+        if (MODE == M_ELEM) {
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc = fmaxf(acc, (FAST || (t.valid && i < t.cnt)) ? A[i] : -INFINITY);
+        }
+        break;
       case F_ST_LDS:
         if (MODE == M_ROW) lds_row[arg * a.RB + t.rr] = A[0];
         if (MODE == M_COL) {
@@ -712,7 +718,8 @@ __device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, 
 }
 
 // ---------------------------------------------------------------- reduce tail
-__device__ __forceinline__ float dpp_add(float v, int ctrl_id) {
+// The value of lane ctrl_id's partner in the reduction tree (DPP).
+__device__ __forceinline__ float dpp_partner(float v, int ctrl_id) {
   int x = __float_as_int(v);
   int y;
   switch (ctrl_id) {
@@ -721,18 +728,24 @@ __device__ __forceinline__ float dpp_add(float v, int ctrl_id) {
     case 2: y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
     default: y = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false); break; // row_mirror
   }
-  return v + __int_as_float(y);
+  return __int_as_float(y);
 }
 
-// Sum over aligned segments of `width` lanes (a power of two <= 64); every
-// lane of a segment ends with the segment's sum.
-__device__ __forceinline__ float segment_sum(float v, int width) {
-  if (width >= 2) v = dpp_add(v, 0);
-  if (width >= 4) v = dpp_add(v, 1);
-  if (width >= 8) v = dpp_add(v, 2);
-  if (width >= 16) v = dpp_add(v, 3);
-  if (width >= 32) v += __shfl_xor(v, 16);
-  if (width >= 64) v += __shfl_xor(v, 32);
+// The sum (MAX false) or the largest value (MAX true) over aligned segments
+// of `width` lanes (a power of two <= 64); every lane of a segment ends
+// with the segment's result.
+template <bool MAX>
+__device__ __forceinline__ float red2(float a, float b) {
+  return MAX ? fmaxf(a, b) : a + b;
+}
+template <bool MAX>
+__device__ __forceinline__ float segment_reduce(float v, int width) {
+  if (width >= 2) v = red2<MAX>(v, dpp_partner(v, 0));
+  if (width >= 4) v = red2<MAX>(v, dpp_partner(v, 1));
+  if (width >= 8) v = red2<MAX>(v, dpp_partner(v, 2));
+  if (width >= 16) v = red2<MAX>(v, dpp_partner(v, 3));
+  if (width >= 32) v = red2<MAX>(v, __shfl_xor(v, 16));
+  if (width >= 64) v = red2<MAX>(v, __shfl_xor(v, 32));
   return v;
 }
 
@@ -892,25 +905,29 @@ exec_kernel(const ExecArgs a) {
       const int n_el = S.el_len;
       if (n_el == 0) return;
 
-      float acc = 0.f;
+      // the row accumulator starts at the reduction's identity
+      const bool rmax = S.red == 3;
+      const float ident = rmax ? -INFINITY : 0.f;
+      float acc = ident;
       int pass = 0, s = 0;
       // reduce tail after the last run of a row, then advance (pass, s)
       auto finish = [&](int rr) {
         if (S.red && s == spl - 1) {
           const int w = min(tpr, 64);
-          float sum = segment_sum(acc, w);
-          acc = 0.f;
+          float sum = rmax ? segment_reduce<true>(acc, w) : segment_reduce<false>(acc, w);
+          acc = ident;
           if (tpr <= 64) {
             store_reduced(a, S, lds_row, r0 + rr, rr, sum, lt == 0 && rr < nr);
           } else {
-            // rows wider than a wave: combine the per-wave sums through LDS
-            // in a fixed order (every lane of a wave holds the same sum and
-            // writes it; every lane reads the totals of its own row)
+            // rows wider than a wave: combine the per-wave results through
+            // LDS in a fixed order (every lane of a wave holds the same
+            // result and writes it; every lane reads those of its own row)
             const int wpr = tpr >> 6;  // waves per row
             lds_red[tid >> 6] = sum;
             __syncthreads();
-            float tot = 0.f;
-            for (int k = 0; k < wpr; ++k) tot += lds_red[sub * wpr + k];
+            float tot = ident;
+            for (int k = 0; k < wpr; ++k)
+              tot = rmax ? fmaxf(tot, lds_red[sub * wpr + k]) : tot + lds_red[sub * wpr + k];
             store_reduced(a, S, lds_row, r0 + rr, rr, tot, lt == 0 && rr < nr);
             __syncthreads();
           }

@@ -25,7 +25,9 @@ namespace gtf {
 
 namespace {
 
-bool is_reduce(int opc) { return opc == GTF_OP_ROW_SUM || opc == GTF_OP_ROW_MEAN; }
+bool is_reduce(int opc) {
+  return opc == GTF_OP_ROW_SUM || opc == GTF_OP_ROW_MEAN || opc == GTF_OP_ROW_MAX;
+}
 
 // ---------------------------------------------------------------- union-find
 struct UnionFind {
@@ -376,7 +378,7 @@ struct Codegen {
   void run_reduce(const MOp& m) {
     bring(m.in[0], RA);
     uses[m.in[0]] -= 1;
-    emit(F_RED);
+    emit(m.form);
   }
 };
 
@@ -417,7 +419,7 @@ const char* check_program(const ExecArgs& a, int n_slots) {
       } else if (f == F_ST_LDS) {
         if (phase == 2 || arg >= (phase == 0 ? a.n_col_slots : a.n_row_slots))
           return "LDS store out of range";
-      } else if (f == F_RED) {
+      } else if (f == F_RED || f == F_RED_MAX) {
         if (phase != 2) return "reduction outside the element phase";
       } else if (f >= F_A2S0 && f <= F_S52B) {
         if ((f - F_A2S0) % kNS >= ns) return "spill slot beyond the instance";
@@ -430,7 +432,7 @@ const char* check_program(const ExecArgs& a, int n_slots) {
     const StageDesc& S = a.stage[st];
     if (const char* e = check(S.row_off, S.row_len, 1)) return e;
     if (const char* e = check(S.el_off, S.el_len, 2)) return e;
-    if (S.red < 0 || S.red > 2) return "reduction kind out of range";
+    if (S.red < 0 || S.red > 3) return "reduction kind out of range";
     if (S.red_lds >= a.n_row_slots || S.red_slot >= n_slots) return "reduction target out of range";
     if (S.red == 0 && (S.red_lds >= 0 || S.red_slot >= 0)) return "reduction target without a reduction";
   }
@@ -742,6 +744,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     } else if (is_reduce(o.opcode)) {
       MOp m;
       m.kind = 3;
+      m.form = o.opcode == GTF_OP_ROW_MAX ? F_RED_MAX : F_RED;
       m.in[0] = o.in[0];
       m.out = o.out;
       L.push_back(m);
@@ -1048,7 +1051,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     const int r = stage_red[st];
     if (r >= 0) {
       const int t = p.ops[r].out;
-      S.red = p.ops[r].opcode == GTF_OP_ROW_MEAN ? 2 : 1;
+      S.red = p.ops[r].opcode == GTF_OP_ROW_MEAN ? 2 : p.ops[r].opcode == GTF_OP_ROW_MAX ? 3 : 1;
       if (row_lds.count(t)) S.red_lds = row_lds.at(t);
       if (outputs.count(t)) S.red_slot = slot_for(t);
       S.red_dtype = p.tensors[t].dtype == GTF_BF16 ? DT_BF16 : DT_F32;

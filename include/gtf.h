@@ -85,8 +85,11 @@ enum {
  * binary (n_in 2): add, sub, mul, div (a op b), max, min
  * ternary:         add3 = (a + b) + c
  * dropout:         dmul (n_in 2: h, mask) = (h * imm) * mask
- * row reduce:      row_sum, row_mean over the last axis; the output is
- *                  declared [R, 1]; the mean divides the sum by the width.
+ * row reduce:      row_sum, row_mean, row_max over the last axis; the
+ *                  output is declared [R, 1]; the mean divides the sum by
+ *                  the width; the max is exact (any order gives it), and
+ *                  of an empty row (C = 0) it is -inf.  All three are
+ *                  kCommReduce (TVM "Operator Pattern Classification").
  * injective data movement (kInjective, TVM "Operator Pattern
  * Classification": each output element is one input element, moved):
  *                  transpose: [R, C] (rank 2) -> [C, R];
@@ -106,7 +109,7 @@ enum {
   GTF_OP_ADD = 32, GTF_OP_SUB = 33, GTF_OP_MUL = 34, GTF_OP_DIV = 35,
   GTF_OP_MAX = 36, GTF_OP_MIN = 37,
   GTF_OP_ADD3 = 48, GTF_OP_DMUL = 49,
-  GTF_OP_ROW_SUM = 64, GTF_OP_ROW_MEAN = 65,
+  GTF_OP_ROW_SUM = 64, GTF_OP_ROW_MEAN = 65, GTF_OP_ROW_MAX = 66,
   GTF_OP_TRANSPOSE = 80, GTF_OP_RESHAPE = 81, GTF_OP_CONCAT = 82
 };
 

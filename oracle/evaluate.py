@@ -50,7 +50,7 @@ def broadcast_shape(shapes) -> Tuple[int, int]:
 
 
 def result_shape(op: str, in_shapes, declared=None) -> Tuple[int, int]:
-    if op in ("row_sum", "row_mean"):
+    if op in ("row_sum", "row_mean", "row_max"):
         return (in_shapes[0][0], 1)
     if op == "transpose":
         return (in_shapes[0][1], in_shapes[0][0])

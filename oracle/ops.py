@@ -13,6 +13,9 @@ Every op takes fp32 operands and gives an fp32 result:
 * row_sum / row_mean reduce the last axis: float64 accumulation of the fp32
   values, then one rounding to fp32; the mean divides the float64 sum by
   the row width before that rounding.
+* row_max is the largest value of each row (exact; -inf for an empty row,
+  the identity of max).  Sum, mean and max are the commutative reductions
+  of TVM "Operator Pattern Classification" (kCommReduce).
 
 Operands broadcast NumPy-style over two axes ([R,C], [1,C], [R,1], [1,1]).
 Op fusion does not change what a graph computes; it only keeps the
@@ -67,6 +70,13 @@ def row_sum(x):
 def row_mean(x):
     x = np.asarray(x, dtype=F32)
     return (_f64(x).sum(axis=-1, keepdims=True) / x.shape[-1]).astype(F32)
+
+
+def row_max(x):
+    x = np.asarray(x, dtype=F32)
+    if x.shape[-1] == 0:
+        return np.full(x.shape[:-1] + (1,), -np.inf, dtype=F32)
+    return x.max(axis=-1, keepdims=True).astype(F32)
 
 
 def apply(op: str, args, imm: float = 0.0, shape=None) -> np.ndarray:
@@ -124,6 +134,8 @@ def apply(op: str, args, imm: float = 0.0, shape=None) -> np.ndarray:
             r = row_sum(a[0])
         elif op == "row_mean":
             r = row_mean(a[0])
+        elif op == "row_max":
+            r = row_max(a[0])
         else:
             raise ValueError(f"unknown op {op}")
     return np.asarray(r, dtype=F32)

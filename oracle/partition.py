@@ -95,14 +95,14 @@ GATHERS = ("transpose", "reshape", "concat")
 MAX_FUSED_OPS = 256
 MAX_GROUP_ARGS = 16
 MAX_STAGES = 4
-_REDUCES = ("row_sum", "row_mean")
+_REDUCES = ("row_sum", "row_mean", "row_max")
 
 
 def pattern(graph, i: int) -> int:
     o = graph.ops[i]
     if o.opaque:
         return K_OPAQUE
-    if o.op in ("row_sum", "row_mean"):
+    if o.op in _REDUCES:
         return K_COMM_REDUCE
     if o.op in ("copy",) + GATHERS:
         return K_INJECTIVE

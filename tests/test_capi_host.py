@@ -68,7 +68,7 @@ def check_against_oracle(g):
     lambda: configs.c1_graph(4, 8), lambda: configs.c2_graph(4, 8),
     lambda: configs.c3_graph(4, 8), lambda: configs.c3_graph(4, 8, head_op=True),
     lambda: configs.layernorm_graph(4, 8), lambda: configs.gelu_graph(4, 8),
-    lambda: configs.dropout_graph(4, 8)])
+    lambda: configs.dropout_graph(4, 8), lambda: configs.softmax_graph(4, 8)])
 def test_config_graphs_plan_like_the_oracle(make):
     check_against_oracle(make())
 
@@ -127,7 +127,8 @@ def _broadcast_dags(seed, count):
                 full.append(g.op("mul", [a, r], f"t{i}", "f32", (R, Cc)))
             elif kind == 4:
                 a = full[rng.integers(len(full))]
-                rowv.append(g.op("row_sum", [a], f"t{i}", "f32", (R, 1)))
+                red = "row_max" if i % 3 == 1 else "row_sum"   # no draw: the DAGs stay as they were
+                rowv.append(g.op(red, [a], f"t{i}", "f32", (R, 1)))
             else:
                 r = rowv[rng.integers(len(rowv))]
                 rowv.append(g.op("add_imm", [r], f"t{i}", "f32", (R, 1), imm=0.5))
@@ -187,6 +188,8 @@ def test_descriptor_errors():
     assert _desc_status([x, T("z", "f32", (2, 4), "out")], [OpDesc("exp", (0,), 1)]) == C.GTF_E_SHAPE
     assert _desc_status([x, T("s", "f32", (2,), "out")], [OpDesc("row_sum", (0,), 1)]) == C.GTF_E_SHAPE
     assert _desc_status([x, T("s", "f32", (2, 1), "out")], [OpDesc("row_sum", (0,), 1)]) == C.GTF_OK
+    assert _desc_status([x, T("s", "f32", (2,), "out")], [OpDesc("row_max", (0,), 1)]) == C.GTF_E_SHAPE
+    assert _desc_status([x, T("s", "f32", (2, 1), "out")], [OpDesc("row_max", (0,), 1)]) == C.GTF_OK
 
 
 def test_raw_abi_errors():
@@ -309,7 +312,7 @@ def test_row_resident_plans_match_the_oracle():
         merged += len(want) < len(opart.partition(g))
         for k in range(plan.num_groups):
             geo = plan.geometry(k)
-            n_red = sum(g.ops[i].op in ("row_sum", "row_mean") for i in plan.group_ops(k))
+            n_red = sum(g.ops[i].op in ("row_sum", "row_mean", "row_max") for i in plan.group_ops(k))
             assert geo["stages"] >= 1 and (n_red <= geo["stages"])
     assert merged >= 20
 

@@ -249,7 +249,7 @@ def _ieee_only(g):
 
 
 def _check_graph(g, ins, modes=((True, False), (False, False))):
-    has_red = any(o.op in ("row_sum", "row_mean") for o in g.ops)
+    has_red = any(o.op in ("row_sum", "row_mean", "row_max") for o in g.ops)
     for fuse, rr in modes:
         plan, got = gpu_run(g, ins, fuse=fuse, row_resident=rr)
         vals, want = oracle_run(g, ins, fuse=fuse, row_resident=rr)
@@ -257,7 +257,7 @@ def _check_graph(g, ins, modes=((True, False), (False, False))):
         for t in g.outputs():
             d = g.tensors[t]
             prod = g.ops[g.producer(t)]
-            if prod.op in ("row_sum", "row_mean"):
+            if prod.op in ("row_sum", "row_mean", "row_max"):
                 scale = reduce_bound(vals[prod.inputs[0]], prod.op == "row_mean")
                 assert_reduce_close(got[t], want[t], scale, 1e-5)
             elif _ieee_only(g) and not has_red:
@@ -667,6 +667,60 @@ def test_row_resident_reduce_then_broadcast(build, rows, cols):
     assert_bits_equal(got2[y], got[y])
 
 
+# ---------------------------------------------------------------- row max and softmax
+def _row_max_graph(R, C, dtype):
+    g = Graph()
+    x = g.input("x", dtype, (R, C))
+    g.op("row_max", [x], "m", "f32", (R, 1), role="out")
+    return g
+
+
+@pytest.mark.parametrize("rows,cols", [(8192, 1024), (37, 1000), (4, 65536), (5, 4097), (3, 5),
+                                       (1, 1), (300, 24), (4, 0)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mean", [0.0, -8.0])
+def test_row_max_bit_exact(rows, cols, dtype, mean):
+    """The largest element of each row is exact, so it matches the oracle bit
+    for bit: rows wider than a wave (combined through LDS), ragged row ends
+    and an empty row (-inf) included.  Rows of only negative values check
+    that lanes past a row's end count as -inf, not 0."""
+    g = _row_max_graph(rows, cols, dtype)
+    x = configs.tensor_values("f32", (rows, cols), "normal", 900 + rows + cols, 0, mean, 1.0)
+    ins = {0: configs.to_bf16_bits(x.astype(np.float64)) if dtype == "bf16" else x}
+    plan, got = gpu_run(g, ins)
+    assert plan.num_groups == 1
+    _, want = oracle_run(g, ins)
+    assert_bits_equal(got[1], want[1])
+    if mean < 0 and cols > 0:
+        assert np.all(got[1] < 0)
+
+
+@pytest.mark.parametrize("rows,cols", [(131072, 128), (37, 1000), (5, 4097), (3, 5), (2, 67)])
+@pytest.mark.parametrize("rr", [False, True])
+def test_softmax_matches_the_oracle(rows, cols, rr):
+    """Row softmax, exp(x - max) * (1 / sum): TVM's three groups (max, then
+    exp and the sum, then the output) or one row-resident launch of three
+    stages.  y is within one bf16 ulp of the oracle's evaluation of the same
+    grouping, and each row of y sums to 1 within its rounding."""
+    g = configs.softmax_graph(rows, cols)
+    ins = configs.softmax_inputs(g, 70 + rows)
+    plan = gtf.FusePlan(g, row_resident=rr)
+    groups = opart.partition(g, row_resident=rr)
+    assert sorted(map(sorted, plan.groups())) == sorted(map(sorted, groups))
+    assert plan.num_groups == (1 if rr else 3)
+    _, got = gpu_run(g, ins, plan=plan)
+    vals, want = oracle_run(g, ins, row_resident=rr)
+    n = _ids(g)
+    assert_bf16_close(got[n["y"]], want[n["y"]], 1)
+    if not rr:
+        # the two row results go through memory between the groups
+        assert_bits_equal(got[n["max"]].reshape(rows, 1), vals[n["max"]])
+        assert_reduce_close(got[n["sum"]].reshape(rows, 1), vals[n["sum"]],
+                            reduce_bound(vals[n["e_sum"]], False), 1e-5)
+    y = numerics.bf16_to_f32(got[n["y"]]).astype(np.float64).reshape(rows, cols)
+    assert np.all(np.abs(y.sum(axis=1) - 1.0) <= cols * 2.0 ** -8 * y.max(axis=1) + 1e-6)
+
+
 def test_random_broadcast_dags_row_resident():
     n = 0
     for gi, g in enumerate(_broadcast_dags(7, 200)):
@@ -727,7 +781,7 @@ def test_random_dags_with_duplicate_fusion():
             big = max([float(np.nanmax(np.abs(v))) if v.size else 0.0 for v in vals.values()] + [1.0])
             for t in gg.outputs():
                 prod = gg2.ops[gg2.producer(t)]  # its operand may now be a copy's value
-                if prod.op in ("row_sum", "row_mean"):
+                if prod.op in ("row_sum", "row_mean", "row_max"):
                     assert_reduce_close(got[t], want[t], reduce_bound(vals[prod.inputs[0]], False), 1e-5)
                 elif gg.tensors[t].dtype == "bf16":
                     assert_close_scaled(numerics.bf16_to_f32(got[t]), numerics.bf16_to_f32(want[t]),
@@ -749,7 +803,7 @@ def _check_program(g, plan, ins):
     big = max([float(np.nanmax(np.abs(v))) if v.size else 0.0 for v in vals.values()] + [1.0])
     for t in g.outputs():
         prod = prog.ops[prog.producer(t)]
-        if prod.op in ("row_sum", "row_mean"):
+        if prod.op in ("row_sum", "row_mean", "row_max"):
             assert_reduce_close(got[t], want[t], reduce_bound(vals[prod.inputs[0]], prod.op == "row_mean"),
                                 1e-5)
         elif g.tensors[t].dtype == "bf16":

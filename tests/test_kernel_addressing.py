@@ -86,6 +86,8 @@ def cases():
         out.append(("gelu", configs.gelu_graph(*sh)))
     for sh in [(8192, 1024), (11, 1000), (2, 67), (64, 1024)]:
         out.append(("drop", configs.dropout_graph(*sh)))
+    for sh in [(131072, 128), (37, 1000), (5, 4097), (3, 5)]:
+        out.append(("softmax", configs.softmax_graph(*sh)))
     g = Graph()
     x = g.input("x", "f32", (64, 1024))
     for op in ("exp", "tanh", "sigmoid", "gelu"):

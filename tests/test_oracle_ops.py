@@ -207,6 +207,43 @@ def test_gelu_group_matches_torch():
     assert torch.equal(got[z > -5], wb[z > -5])
 
 
+def test_row_max_closed_cases_and_brute_force():
+    x = F32([[1.0, 5.0, -2.0], [0.0, -3.0, -1.0], [-7.0, -7.5, -6.25]])
+    assert ops.apply("row_max", [x]).ravel().tolist() == [5.0, 0.0, -6.25]
+    # an empty row gives the identity of max
+    e = ops.apply("row_max", [np.zeros((2, 0), dtype=F32)])
+    assert e.shape == (2, 1) and np.all(np.isneginf(e))
+    # a plain Python scan with ">" on small random rows
+    rng = np.random.default_rng(11)
+    for _ in range(50):
+        r, c = int(rng.integers(1, 5)), int(rng.integers(1, 9))
+        a = rng.normal(-1.0, 3.0, size=(r, c)).astype(F32)
+        got = ops.apply("row_max", [a]).ravel()
+        for i in range(r):
+            best = a[i, 0]
+            for v in a[i, 1:]:
+                if v > best:
+                    best = v
+            assert got[i] == best
+
+
+def test_softmax_group_matches_torch_softmax():
+    """The softmax graph (max, exp(x - max), sum, times 1/sum) against
+    torch's float64 softmax: the bf16 outputs are the float64 result
+    rounded, or its bf16 neighbour."""
+    g = configs.softmax_graph(8, 96)
+    ins = configs.softmax_inputs(g, 5001)
+    _, out = ev.run(g, ins)
+    (X,) = g.inputs()
+    x = torch.from_numpy(numerics.bf16_to_f32(ins[X]).astype(np.float64))
+    want = torch.softmax(x, dim=1).float().to(torch.bfloat16).view(torch.int16).numpy().astype(np.int32)
+    got = out[g.outputs()[0]].astype(np.int32)
+    assert np.abs(got - want).max() <= 1
+    # and the float64 rows of the rounded result sum to one within rounding
+    y = numerics.bf16_to_f32(out[g.outputs()[0]]).astype(np.float64)
+    assert np.all(np.abs(y.sum(axis=1) - 1.0) <= 96 * 2.0 ** -8 * y.max(axis=1))
+
+
 def test_dropout_special_masks():
     g = configs.dropout_graph(4, 32)
     ins = configs.dropout_inputs(g, 5000)

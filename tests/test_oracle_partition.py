@@ -59,6 +59,13 @@ def test_config_groups():
     assert {ln.tensors[t].name for t in stored} == {"mean", "var"}
     assert as_sets(pt.partition(configs.gelu_graph(4, 8))) == [[0, 1]]
     assert as_sets(pt.partition(configs.dropout_graph(4, 8))) == [[0, 1]]
+    sm = configs.softmax_graph(4, 8)
+    # G1 max (a reduction is a sink); G2 x-max, exp, sum; G3 x-max, exp and
+    # the product with 1/sum, the reciprocal hoisted in as a row operand
+    assert pt.pattern(sm, 0) == pt.K_COMM_REDUCE
+    groups = pt.partition(sm)
+    assert as_sets(groups) == [[0], [1, 2, 3], [4, 5, 6, 7]]
+    assert {sm.tensors[t].name for t in pt.stored_tensors(sm, groups)} == {"max", "sum"}
 
 
 def test_unfused_mode_is_one_op_per_group():
@@ -210,6 +217,7 @@ def _rr_graphs():
     s = g.op("row_sum", [e], "s", "f32", (8, 1))
     g.op("div", [e, s], "y", "f32", (8, 40), role="out")
     out["softmax_like"] = (g, [[0], [1], [2]], [[0], [1, 2]])
+    out["softmax"] = (configs.softmax_graph(16, 64), [[0], [1, 2, 3], [4, 5, 6, 7]], [list(range(8))])
     g = Graph()
     x = g.input("x", "f32", (8, 40))
     g.op("row_mean", [x], "m", "f32", (8, 1), role="out")
@@ -355,7 +363,8 @@ def _f32_reduce_dags(seed, count):
             elif kind == 3:
                 full.append(g.op("mul", [pick(full), pick(rowv)], f"t{i}", "f32", (R, C)))
             elif kind == 4:
-                rowv.append(g.op("row_sum", [pick(full)], f"t{i}", "f32", (R, 1)))
+                red = "row_max" if i % 3 == 1 else "row_sum"   # no draw: the DAGs stay as they were
+                rowv.append(g.op(red, [pick(full)], f"t{i}", "f32", (R, 1)))
             else:
                 rowv.append(g.op("add_imm", [pick(rowv)], f"t{i}", "f32", (R, 1), imm=0.5))
         readers = {t for o in g.ops for t in o.inputs}

@@ -164,6 +164,30 @@ def layernorm_shared_graph(rows: int = 8192, hidden: int = 1024, eps: float = LN
     return g
 
 
+def softmax_graph(rows: int = 131072, cols: int = 128) -> Graph:
+    """Row softmax written op by op, the way a framework writes it for
+    numerical range: y = exp(x - max x) * (1 / sum exp(x - max x)).  The
+    default shape is the attention probabilities of 8192 tokens cut into 64
+    sequences of 128 with 16 heads.  exp(x - max) appears twice (once for
+    the sum, once for the output), so neither later group needs it stored."""
+    g = Graph()
+    X = g.input("X", "bf16", (rows, cols))
+    m = g.op("row_max", [X], "max", "f32", (rows, 1))
+    d1 = g.op("sub", [X, m], "xm_sum", "bf16", (rows, cols))
+    e1 = g.op("exp", [d1], "e_sum", "bf16", (rows, cols))
+    s = g.op("row_sum", [e1], "sum", "f32", (rows, 1))
+    d2 = g.op("sub", [X, m], "xm_out", "bf16", (rows, cols))
+    e2 = g.op("exp", [d2], "e_out", "bf16", (rows, cols))
+    r = g.op("recip", [s], "rsum", "f32", (rows, 1))
+    g.op("mul", [e2, r], "y", "bf16", (rows, cols), role="out")
+    return g
+
+
+def softmax_inputs(g: Graph, seed: int) -> Dict[int, np.ndarray]:
+    (X,) = g.inputs()
+    return {X: tensor_values("bf16", g.tensors[X].shape, "normal", seed, 5, 0.0, 2.0)}
+
+
 def gelu_graph(rows: int = 8192, ffn: int = 4096) -> Graph:
     g = Graph()
     A = g.input("A", "bf16", (rows, ffn))

@@ -26,7 +26,7 @@ OP_ARITY = {
     "add_imm": 1, "mul_imm": 1,
     "add": 2, "sub": 2, "mul": 2, "div": 2, "max": 2, "min": 2,
     "add3": 3, "dmul": 2,
-    "row_sum": 1, "row_mean": 1,
+    "row_sum": 1, "row_mean": 1, "row_max": 1,
     # injective data movement: [R,C] -> [C,R]; any shape to any shape of
     # the same element count (row-major order kept); [R,C1] ++ [R,C2] along
     # the last axis
