@@ -85,6 +85,9 @@ enum Form : int {
   F_GELU_BF,
   // fold A into the row accumulator with max (element phase)
   F_RED_MAX,
+  // fold A into a paired accumulator (element phase): (mean, squared
+  // deviations, count), or (max, sum of exp(x - max))
+  F_RED_MV, F_RED_SE,
   F_COUNT
 };
 
@@ -115,10 +118,15 @@ struct MultiItem {
 struct StageDesc {
   int32_t row_off, row_len;  // row program (instruction offset, length)
   int32_t el_off, el_len;    // element program
-  int32_t red;               // 0 none, 1 row sum, 2 row mean, 3 row max
+  int32_t red;               // 0 none, 1 row sum, 2 row mean, 3 row max,
+                             // paired (two results in one pass): 4 mean and
+                             // mean of squared deviations from it, 5 max and
+                             // sum of exp(x - max)
   int32_t red_lds;           // LDS row slot for the result, or -1
   int32_t red_slot;          // external slot for the result, or -1
   int32_t red_dtype;         // its dtype
+  int32_t red2_lds, red2_slot, red2_dtype;  // the second result of a paired one
+  int32_t red2_pad_;
 };
 
 // Kernel arguments, passed by value (kernarg segment; read with scalar
@@ -155,6 +163,8 @@ struct ExecArgs {
   int64_t cstride[kMaxSlots];
   Instr prog[kMaxInstr];
 };
+
+static_assert(sizeof(ExecArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 // Bucket chunk: a run of at most kChunkElems elements of one tensor.
 constexpr int kChunkElems = 16384;

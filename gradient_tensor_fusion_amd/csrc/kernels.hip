@@ -482,6 +482,43 @@ __device__ __forceinline__ void store_bf16(const float (&s)[V], const ExecArgs& 
   b[elem_offset<V, MODE>(a, slot, t)] = (uint16_t)(pack_bf16(s[0], 0.f) & 0xFFFFu);
 }
 
+// ---------------------------------------------------------------- row accumulators
+// A lane's share of the row reduction its stage ends in.  a is the sum
+// (row_sum, row_mean) or the largest value (row_max).  The paired
+// reductions carry two results in one pass over the row:
+//  * mean and variance: a = mean, b = sum of squared deviations from it,
+//    c = count, merged by the pairwise update of Chan, Golub and LeVeque
+//    (1979) (a parallel form of Welford's);
+//  * max and sum of exponentials: a = largest value, b = sum of
+//    exp(x - a), the sum rescaled by exp(a_old - a_new) as the maximum grows.
+struct RowAcc {
+  float a, b, c;
+};
+
+// x then y (the order fixes the rounding; callers keep it canonical).  An
+// empty side (count 0, or max -inf) leaves the other as it is.
+__device__ __forceinline__ RowAcc merge_mv(RowAcc x, RowAcc y) {
+  const float n = x.c + y.c;
+  const float w = y.c / n;
+  const float d = y.a - x.a;
+  RowAcc r;
+  r.a = x.a + d * w;
+  r.b = (x.b + y.b) + (d * d) * (x.c * w);
+  r.c = n;
+  return n > 0.f ? r : x;
+}
+__device__ __forceinline__ RowAcc merge_se(RowAcc x, RowAcc y) {
+  const float m = fmaxf(x.a, y.a);
+  // an empty side's -inf would give exp_nonpos(-inf - m): select 0 instead
+  const float fx = x.a == -INFINITY ? 0.f : exp_nonpos(x.a - m);
+  const float fy = y.a == -INFINITY ? 0.f : exp_nonpos(y.a - m);
+  RowAcc r;
+  r.a = m;
+  r.b = x.b * fx + y.b * fy;
+  r.c = 0.f;
+  return m == -INFINITY ? x : r;
+}
+
 // ---------------------------------------------------------------- ops
 template <int V, int F>
 __device__ __forceinline__ void unary(float (&r)[V]) {
@@ -602,7 +639,7 @@ template <int V, int MODE, bool FAST, int NS, bool TR = false>
 __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, int pc0, int n,
                                          const Tile& t, float (&A)[V], float (&B)[V],
                                          float (&S)[NS > 0 ? NS : 1][V], float* lds_col,
-                                         float* lds_row, float& acc, bool store_global) {
+                                         float* lds_row, RowAcc& acc, bool store_global) {
   if (pc0 >= n) return;
   Instr cur = prog[pc0];
   for (int pc = pc0; pc < n; ++pc) {
@@ -681,13 +718,47 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
       case F_RED:
         if (MODE == M_ELEM) {
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc += (FAST || (t.valid && i < t.cnt)) ? A[i] : 0.f;
+          for (int i = 0; i < V; ++i) acc.a += (FAST || (t.valid && i < t.cnt)) ? A[i] : 0.f;
         }
         break;
       case F_RED_MAX:
         if (MODE == M_ELEM) {
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc = fmaxf(acc, (FAST || (t.valid && i < t.cnt)) ? A[i] : -INFINITY);
+          for (int i = 0; i < V; ++i) acc.a = fmaxf(acc.a, (FAST || (t.valid && i < t.cnt)) ? A[i] : -INFINITY);
+        }
+        break;
+      // (the staged-transpose instance runs no reductions)
+      case F_RED_MV:
+        // this tile's (mean, squared deviations, count), then merged in
+        if constexpr (MODE == M_ELEM && !TR) {
+          float s = 0.f, cnt = 0.f;
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            const bool ok = FAST || (t.valid && i < t.cnt);
+            s += ok ? A[i] : 0.f;
+            cnt += ok ? 1.f : 0.f;
+          }
+          const float m = FAST ? s * (1.0f / V) : (cnt > 0.f ? s / cnt : 0.f);
+          float q = 0.f;
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            const float d = A[i] - m;
+            q = (FAST || (t.valid && i < t.cnt)) ? __builtin_fmaf(d, d, q) : q;
+          }
+          acc = merge_mv(acc, RowAcc{m, q, cnt});
+        }
+        break;
+      case F_RED_SE:
+        // this tile's (max, sum of exp(x - max)), then merged in
+        if constexpr (MODE == M_ELEM && !TR) {
+          float m = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < V; ++i) m = fmaxf(m, (FAST || (t.valid && i < t.cnt)) ? A[i] : -INFINITY);
+          float s = 0.f;
+#pragma unroll
+          for (int i = 0; i < V; ++i)
+            s += (FAST || (t.valid && i < t.cnt)) ? exp_nonpos(A[i] - m) : 0.f;
+          acc = merge_se(acc, RowAcc{m, s, 0.f});
         }
         break;
       case F_ST_LDS:
@@ -708,7 +779,7 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
 template <int V, int MODE, bool FAST, int NS, bool TR = false>
 __device__ __forceinline__ void interpret(const ExecArgs& a, const Instr* prog, int n,
                                           const Tile& t, float* lds_col, float* lds_row,
-                                          float& acc, bool store_global) {
+                                          RowAcc& acc, bool store_global) {
   float A[V], B[V], S[NS > 0 ? NS : 1][V];
   // a program writes a register before reading it; left undefined, the
   // registers would be zeroed on every call (one move each per tile)
@@ -749,21 +820,61 @@ __device__ __forceinline__ float segment_reduce(float v, int width) {
   return v;
 }
 
-// Row result of a stage's reduce tail, for the lanes in `on` (one lane per
-// row): to the stage's LDS row slot, where later stages and row programs
-// read it, and/or with a predicated store to its external slot.
-__device__ __forceinline__ void store_reduced(const ExecArgs& a, const StageDesc& S, float* lds_row,
-                                              int64_t row, int rr, float s, bool on) {
-  const float v = S.red == 2 ? s / (float)a.C : s;
-  if (S.red_lds >= 0 && on) lds_row[S.red_lds * a.RB + rr] = v;
-  if (S.red_slot < 0) return;
-  const int slot = S.red_slot;
-  const int64_t off = on ? row * a.rstride[slot] : 0;
+// The reduction tree for a paired accumulator (KIND 4: mean and variance,
+// 5: max and sum of exponentials).  At each step a lane merges its value
+// with its partner's in a fixed order, the lower-half lane's first, so
+// both lanes of a pair compute the same bits and every lane of a segment
+// ends with the segment's result, as in segment_reduce.
+template <int KIND>
+__device__ __forceinline__ RowAcc merge_kind(RowAcc x, RowAcc y) {
+  return KIND == 4 ? merge_mv(x, y) : merge_se(x, y);
+}
+template <int KIND>
+__device__ __forceinline__ RowAcc pair_step(RowAcc v, RowAcc p, bool lower) {
+  return lower ? merge_kind<KIND>(v, p) : merge_kind<KIND>(p, v);
+}
+template <int KIND>
+__device__ __forceinline__ RowAcc segment_pair(RowAcc v, int width) {
+  const int lane = threadIdx.x & 63;
+  auto dpp = [&](int ctrl) {
+    return RowAcc{dpp_partner(v.a, ctrl), dpp_partner(v.b, ctrl), dpp_partner(v.c, ctrl)};
+  };
+  auto shf = [&](int m) { return RowAcc{__shfl_xor(v.a, m), __shfl_xor(v.b, m), __shfl_xor(v.c, m)}; };
+  if (width >= 2) v = pair_step<KIND>(v, dpp(0), (lane & 1) == 0);
+  if (width >= 4) v = pair_step<KIND>(v, dpp(1), (lane & 2) == 0);
+  if (width >= 8) v = pair_step<KIND>(v, dpp(2), (lane & 7) < 4);
+  if (width >= 16) v = pair_step<KIND>(v, dpp(3), (lane & 15) < 8);
+  if (width >= 32) v = pair_step<KIND>(v, shf(16), (lane & 16) == 0);
+  if (width >= 64) v = pair_step<KIND>(v, shf(32), (lane & 32) == 0);
+  return v;
+}
+
+// A row result, for the lanes in `on` (one lane per row): to an LDS row
+// slot, where later stages and row programs read it, and/or with a
+// predicated store to an external slot.
+__device__ __forceinline__ void store_row(const ExecArgs& a, float* lds_row, int lds_slot, int ext_slot,
+                                          int dtype, int64_t row, int rr, float v, bool on) {
+  if (lds_slot >= 0 && on) lds_row[lds_slot * a.RB + rr] = v;
+  if (ext_slot < 0) return;
+  const int64_t off = on ? row * a.rstride[ext_slot] : 0;
   const uint64_t m = lanes(on);
-  if (S.red_dtype == DT_BF16)
-    pstore_b16((uint16_t*)a.ptr[slot] + off, pack_bf16(v, 0.f) & 0xFFFFu, m);
+  if (dtype == DT_BF16)
+    pstore_b16((uint16_t*)a.ptr[ext_slot] + off, pack_bf16(v, 0.f) & 0xFFFFu, m);
   else
-    pstore_b32((float*)a.ptr[slot] + off, __float_as_uint(v), m);
+    pstore_b32((float*)a.ptr[ext_slot] + off, __float_as_uint(v), m);
+}
+
+// The row result(s) of a stage's reduction from the merged accumulator.
+__device__ __forceinline__ void store_reduced(const ExecArgs& a, const StageDesc& S, float* lds_row,
+                                              int64_t row, int rr, RowAcc r, bool on) {
+  float first = r.a, second = r.b;
+  if (S.red == 2) first = r.a / (float)a.C;
+  if (S.red == 4) {
+    first = r.c > 0.f ? r.a : __builtin_nanf("");  // an empty row's mean is 0 / 0
+    second = r.b / r.c;
+  }
+  store_row(a, lds_row, S.red_lds, S.red_slot, S.red_dtype, row, rr, first, on);
+  if (S.red >= 4) store_row(a, lds_row, S.red2_lds, S.red2_slot, S.red2_dtype, row, rr, second, on);
 }
 
 // ---------------------------------------------------------------- executor
@@ -792,7 +903,7 @@ exec_kernel(const ExecArgs a) {
   const int64_t erow_stride = a.R == 1 ? 0 : a.C;
   const int ks = tpr * kV;  // elements between a lane's sub-tiles
   bool staged = false;
-  float dummy = 0.f;
+  RowAcc dummy{0.f, 0.f, 0.f};
 
   for (int64_t item = blockIdx.x; item < a.n_items; item += gridDim.x) {
     int64_t rb, r0, c0;
@@ -906,31 +1017,42 @@ exec_kernel(const ExecArgs a) {
       if (n_el == 0) return;
 
       // the row accumulator starts at the reduction's identity
-      const bool rmax = S.red == 3;
-      const float ident = rmax ? -INFINITY : 0.f;
-      float acc = ident;
+      const bool rmax = S.red == 3 || S.red == 5;
+      const RowAcc ident{rmax ? -INFINITY : 0.f, 0.f, 0.f};
+      RowAcc acc = ident;
       int pass = 0, s = 0;
       // reduce tail after the last run of a row, then advance (pass, s)
       auto finish = [&](int rr) {
         if (S.red && s == spl - 1) {
           const int w = min(tpr, 64);
-          float sum = rmax ? segment_reduce<true>(acc, w) : segment_reduce<false>(acc, w);
+          RowAcc r = acc;
+          const bool paired = !TR && S.red >= 4;  // the staged-transpose instance runs no reductions
+          if (paired && S.red == 4) r = segment_pair<4>(acc, w);
+          else if (paired) r = segment_pair<5>(acc, w);
+          else r.a = S.red == 3 ? segment_reduce<true>(acc.a, w) : segment_reduce<false>(acc.a, w);
           acc = ident;
-          if (tpr <= 64) {
-            store_reduced(a, S, lds_row, r0 + rr, rr, sum, lt == 0 && rr < nr);
-          } else {
+          if (tpr > 64) {
             // rows wider than a wave: combine the per-wave results through
             // LDS in a fixed order (every lane of a wave holds the same
             // result and writes it; every lane reads those of its own row)
             const int wpr = tpr >> 6;  // waves per row
-            lds_red[tid >> 6] = sum;
+            float* cell = lds_red + (tid >> 6) * 3;
+            cell[0] = r.a;
+            cell[1] = r.b;
+            cell[2] = r.c;
             __syncthreads();
-            float tot = ident;
-            for (int k = 0; k < wpr; ++k)
-              tot = rmax ? fmaxf(tot, lds_red[sub * wpr + k]) : tot + lds_red[sub * wpr + k];
-            store_reduced(a, S, lds_row, r0 + rr, rr, tot, lt == 0 && rr < nr);
-            __syncthreads();
+            const float* rowc = lds_red + sub * wpr * 3;
+            RowAcc tot = ident;
+            for (int k = 0; k < wpr; ++k) {
+              const RowAcc x{rowc[3 * k], rowc[3 * k + 1], rowc[3 * k + 2]};
+              if (paired && S.red == 4) tot = merge_mv(tot, x);
+              else if (paired) tot = merge_se(tot, x);
+              else tot.a = rmax ? fmaxf(tot.a, x.a) : tot.a + x.a;
+            }
+            r = tot;
           }
+          store_reduced(a, S, lds_row, r0 + rr, rr, r, lt == 0 && rr < nr);
+          if (tpr > 64) __syncthreads();
         }
         if (++s == spl) {
           s = 0;

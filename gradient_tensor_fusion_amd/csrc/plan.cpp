@@ -419,7 +419,7 @@ const char* check_program(const ExecArgs& a, int n_slots) {
       } else if (f == F_ST_LDS) {
         if (phase == 2 || arg >= (phase == 0 ? a.n_col_slots : a.n_row_slots))
           return "LDS store out of range";
-      } else if (f == F_RED || f == F_RED_MAX) {
+      } else if (f == F_RED || f == F_RED_MAX || f == F_RED_MV || f == F_RED_SE) {
         if (phase != 2) return "reduction outside the element phase";
       } else if (f >= F_A2S0 && f <= F_S52B) {
         if ((f - F_A2S0) % kNS >= ns) return "spill slot beyond the instance";
@@ -432,9 +432,11 @@ const char* check_program(const ExecArgs& a, int n_slots) {
     const StageDesc& S = a.stage[st];
     if (const char* e = check(S.row_off, S.row_len, 1)) return e;
     if (const char* e = check(S.el_off, S.el_len, 2)) return e;
-    if (S.red < 0 || S.red > 3) return "reduction kind out of range";
+    if (S.red < 0 || S.red > 5) return "reduction kind out of range";
     if (S.red_lds >= a.n_row_slots || S.red_slot >= n_slots) return "reduction target out of range";
     if (S.red == 0 && (S.red_lds >= 0 || S.red_slot >= 0)) return "reduction target without a reduction";
+    if (S.red2_lds >= a.n_row_slots || S.red2_slot >= n_slots) return "reduction target out of range";
+    if (S.red < 4 && (S.red2_lds >= 0 || S.red2_slot >= 0)) return "second result without a paired reduction";
   }
   return nullptr;
 }
@@ -499,6 +501,50 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     const TensorInfo& ri = p.tensors[p.ops[r].in[0]];
     if (ri.R != R || ri.C != C) return bad("reduction input is not the group domain");
   }
+  // ---- paired reductions.  In a group that reads its own row results, a
+  // mean followed by the mean of squared deviations from it, or a max
+  // followed by the sum of exp(x - max), over one input, with nothing else
+  // reading the deviations or the squares / exponentials: one pass over the
+  // row gives both results (the executor's mean-and-variance and
+  // max-and-sum-of-exponentials accumulators), and the two element ops
+  // between them are not emitted.
+  std::map<int, int> pair_first;  // second reduction -> first
+  std::map<int, int> pair_second; // first reduction -> second
+  std::set<int> absorbed;         // element ops folded into a paired pass
+  {
+    std::map<int, int> made_by;
+    for (int i : ops) made_by[p.ops[i].out] = i;
+    auto n_readers = [&](int t) {
+      int n = 0;
+      for (const OpInfo& o : p.ops)
+        for (int k = 0; k < o.n_in; ++k) n += o.in[k] == t;
+      return n;
+    };
+    for (int r2 : reds) {
+      const OpInfo& o2 = p.ops[r2];
+      const bool mv = o2.opcode == GTF_OP_ROW_MEAN;
+      if (!mv && o2.opcode != GTF_OP_ROW_SUM) continue;
+      const int t1 = o2.in[0];
+      if (!made_by.count(t1)) continue;
+      const int j = made_by[t1];
+      if (p.ops[j].opcode != (mv ? GTF_OP_SQUARE : GTF_OP_EXP)) continue;
+      const int t2 = p.ops[j].in[0];
+      if (!made_by.count(t2)) continue;
+      const int k = made_by[t2];
+      if (p.ops[k].opcode != GTF_OP_SUB) continue;
+      const int x = p.ops[k].in[0], m = p.ops[k].in[1];
+      if (!made_by.count(m)) continue;
+      const int r1 = made_by[m];
+      if (p.ops[r1].opcode != (mv ? GTF_OP_ROW_MEAN : GTF_OP_ROW_MAX) || p.ops[r1].in[0] != x) continue;
+      if (n_readers(t1) != 1 || n_readers(t2) != 1) continue;
+      if (p.tensors[t1].role == GTF_ROLE_OUT || p.tensors[t2].role == GTF_ROLE_OUT) continue;
+      if (pair_second.count(r1) || pair_first.count(r1)) continue;
+      pair_first[r2] = r1;
+      pair_second[r1] = r2;
+      absorbed.insert(j);
+      absorbed.insert(k);
+    }
+  }
   bool flat = reds.empty() && !gathers2d;
   for (int t : touched)
     if (p.tensors[t].R != R || p.tensors[t].C != C) flat = false;
@@ -555,9 +601,14 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   int n_stages = 1;
   for (int i : ops) {
     const OpInfo& o = p.ops[i];
+    if (absorbed.count(i)) continue;
     int st = 0;
-    for (int k = 0; k < o.n_in; ++k)
-      if (produced.count(o.in[k])) st = std::max(st, avail.at(o.in[k]));
+    if (pair_first.count(i)) {
+      st = stage_of.at(pair_first.at(i));  // the first reduction's pass
+    } else {
+      for (int k = 0; k < o.n_in; ++k)
+        if (produced.count(o.in[k])) st = std::max(st, avail.at(o.in[k]));
+    }
     const int c = op_cls(i);
     if (c == CLS_COL && st > 0) return bad("column op after a row reduction");
     stage_of[i] = st;
@@ -573,8 +624,12 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
       return bad("row reduction over a single column read in its group");
   }
   if (n_stages > kMaxStages) return bad("more row-resident stages than the kernel holds");
-  std::vector<int> stage_red(n_stages, -1);
+  std::vector<int> stage_red(n_stages, -1), stage_red2(n_stages, -1);
   for (int r : reds) {
+    if (pair_first.count(r)) {
+      stage_red2[stage_of.at(r)] = r;
+      continue;
+    }
     if (stage_red[stage_of[r]] >= 0) return bad("two row reductions in one stage");
     stage_red[stage_of[r]] = r;
   }
@@ -591,7 +646,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   };
   for (int i : ops) {
     const OpInfo& o = p.ops[i];
-    if (is_gather(o.opcode)) continue;  // its inputs are loaded, addressed
+    if (is_gather(o.opcode) || absorbed.count(i)) continue;  // loaded addressed / not emitted
     const int c = op_cls(i);
     for (int k = 0; k < o.n_in; ++k) {
       const int t = o.in[k];
@@ -745,6 +800,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
       MOp m;
       m.kind = 3;
       m.form = o.opcode == GTF_OP_ROW_MAX ? F_RED_MAX : F_RED;
+      if (pair_second.count(i)) m.form = o.opcode == GTF_OP_ROW_MEAN ? F_RED_MV : F_RED_SE;
       m.in[0] = o.in[0];
       m.out = o.out;
       L.push_back(m);
@@ -786,7 +842,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     std::vector<int> work;
     if (stage_red[st] >= 0) work.push_back(stage_red[st]);
     for (int i : ops)
-      if (op_cls(i) == CLS_E && !is_reduce(p.ops[i].opcode) && stage_of[i] == st &&
+      if (op_cls(i) == CLS_E && !is_reduce(p.ops[i].opcode) && !absorbed.count(i) && stage_of.at(i) == st &&
           outputs.count(p.ops[i].out)) {
         work.push_back(i);
         pe.store.insert(p.ops[i].out);
@@ -1048,6 +1104,10 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     S.red_lds = -1;
     S.red_slot = -1;
     S.red_dtype = DT_F32;
+    S.red2_lds = -1;
+    S.red2_slot = -1;
+    S.red2_dtype = DT_F32;
+    S.red2_pad_ = 0;
     const int r = stage_red[st];
     if (r >= 0) {
       const int t = p.ops[r].out;
@@ -1055,6 +1115,14 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
       if (row_lds.count(t)) S.red_lds = row_lds.at(t);
       if (outputs.count(t)) S.red_slot = slot_for(t);
       S.red_dtype = p.tensors[t].dtype == GTF_BF16 ? DT_BF16 : DT_F32;
+      const int r2 = stage_red2[st];
+      if (r2 >= 0) {
+        const int t2 = p.ops[r2].out;
+        S.red = S.red == 2 ? 4 : 5;
+        if (row_lds.count(t2)) S.red2_lds = row_lds.at(t2);
+        if (outputs.count(t2)) S.red2_slot = slot_for(t2);
+        S.red2_dtype = p.tensors[t2].dtype == GTF_BF16 ? DT_BF16 : DT_F32;
+      }
     }
   }
   for (size_t s = 0; s < slots.size(); ++s) {

@@ -304,7 +304,10 @@ typedef struct {
   int32_t program_length; /* op-program instructions, all phases            */
   int32_t spill_slots;    /* op-program spill slots used                    */
   int32_t spill_slots_max;/* spill slots of the kernel: 0 or 2 (wide), 6 (narrow) */
-  int32_t reduce;         /* 0 none, 1 row sum, 2 row mean (the last one)   */
+  int32_t reduce;         /* the last stage's reduction: 0 none, 1 row sum,
+                             2 row mean, 3 row max; 4 mean and variance, 5
+                             max and sum of exponentials (each a pair taken
+                             in one pass, GTF_ROW_RESIDENT)                 */
   int32_t stages;         /* element stages: 1, or more in a group that reads
                              its own row reductions (GTF_ROW_RESIDENT)      */
   int32_t reserved;

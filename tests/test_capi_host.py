@@ -313,7 +313,8 @@ def test_row_resident_plans_match_the_oracle():
         for k in range(plan.num_groups):
             geo = plan.geometry(k)
             n_red = sum(g.ops[i].op in ("row_sum", "row_mean", "row_max") for i in plan.group_ops(k))
-            assert geo["stages"] >= 1 and (n_red <= geo["stages"])
+            # a paired reduction (mean and variance, max and sum of exps) shares a stage
+            assert geo["stages"] >= 1 and n_red <= 2 * geo["stages"]
     assert merged >= 20
 
 
