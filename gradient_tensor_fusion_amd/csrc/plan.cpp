@@ -1066,10 +1066,6 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     while ((int64_t)tpr * 2 <= want && tpr * 2 <= kBlock) tpr <<= 1;
     if (!reds.empty() && tpr > 64 && DR >= 256) tpr = 64;
   }
-  if (const char* e = std::getenv("GTF_TPR")) {
-    int f = std::atoi(e);
-    if (f >= 1 && f <= kBlock && (f & (f - 1)) == 0) tpr = f;
-  }
   // a staged transposed tile is 64 rows (4 lanes per row) by at most 128
   // columns: at most 64 x 129 floats of LDS
   if (n_tr > 0) tpr = 4;

@@ -188,7 +188,10 @@ typedef struct gtf_bucket_plan gtf_bucket_plan;
  * in tensor written, a tensor written twice), GTF_E_UNSUPPORTED (opcode,
  * dtype, rank, u8 output), GTF_E_SHAPE (broadcast/declared shape
  * mismatch), GTF_E_LIMIT (a single op that no kernel can run).  On error
- * *out is set to NULL. */
+ * *out is set to NULL.
+ * Diagnostics: with the environment variable GTF_TRACE set, every plan made
+ * prints one line per group to stderr (its ops, domain, items, panel and
+ * row-block shape, threads per row, sub-tiles, spill slots, stages). */
 int fuse_plan_create(const gtf_program_desc* desc, uint32_t flags, gtf_fuse_plan** out);
 
 /* A plan from an explicit grouping: group_of[i] (>= 0) labels descriptor
