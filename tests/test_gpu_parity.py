@@ -765,6 +765,45 @@ def test_softmax_one_pass_max_and_sum_wide_range(rows, cols):
     assert_bf16_close(got[y], want[y], 1)
 
 
+@pytest.mark.parametrize("make,names", [(configs.layernorm_graph, ("mean", "var")),
+                                        (configs.softmax_graph, ("max", "sum"))])
+@pytest.mark.parametrize("rows,cols", [(4, 0), (5, 1), (3, 7)])
+def test_paired_reductions_on_degenerate_rows(make, names, rows, cols):
+    """The one-pass pairs with both results stored, on empty rows (mean and
+    variance 0/0, max -inf and sum 0, as the oracle's definitions give), one
+    column and a partial tile: bit for bit where the result is exact, else
+    within the reduction bound."""
+    g = _promote(make(rows, cols), set(names))
+    X = g.inputs()[0]
+    ins = {X: configs.to_bf16_bits(configs.tensor_values("f32", (rows, cols), "normal", 91, 0, 0.0,
+                                                         2.0).astype(np.float64))}
+    for t in g.inputs()[1:]:
+        ins[t] = configs.to_bf16_bits(np.ones(g.tensors[t].shape, dtype=np.float64))
+    plan = gtf.FusePlan(g, row_resident=True)
+    _, got = gpu_run(g, ins, plan=plan)
+    vals, _ = oracle_run(g, ins, row_resident=True)
+    n = _ids(g)
+    first, second = n[names[0]], n[names[1]]
+    a1, w1 = got[first].reshape(rows, 1), vals[first]
+    a2, w2 = got[second].reshape(rows, 1), vals[second]
+    if cols == 0:
+        if names[0] == "mean":
+            assert np.all(np.isnan(a1)) and np.all(np.isnan(w1))
+            assert np.all(np.isnan(a2)) and np.all(np.isnan(w2))
+        else:
+            assert np.all(np.isneginf(a1)) and np.all(np.isneginf(w1))
+            assert np.all(a2 == 0) and np.all(w2 == 0)
+        return
+    xs = numerics.bf16_to_f32(ins[X]).astype(np.float64).reshape(rows, cols)
+    if names[0] == "max":
+        assert_bits_equal(a1, w1)
+        assert_reduce_close(a2, w2, reduce_bound(np.exp(xs - xs.max(axis=1, keepdims=True)), False), 1e-5)
+    else:
+        assert_reduce_close(a1, w1, reduce_bound(xs, True), 1e-5)
+        sq = (xs - xs.mean(axis=1, keepdims=True)) ** 2
+        assert_reduce_close(a2, w2, reduce_bound(sq, True) + 1e-30, 1e-5)
+
+
 def test_random_broadcast_dags_row_resident():
     n = 0
     for gi, g in enumerate(_broadcast_dags(7, 200)):
