@@ -182,11 +182,21 @@ class FusePlan:
     def materialized(self) -> List[int]:
         return [t for t in range(self.n_tensors) if self.is_materialized(t)]
 
+    def _tensor_bytes(self, t: int) -> int:
+        d = self.graph.tensors[t]
+        n = 1
+        for s in d.shape:
+            n *= int(s)
+        return n * C.ELEM_BYTES[d.dtype]
+
+    def _ptr(self, t: int, x):
+        return C.device_ptr(x, self._tensor_bytes(t), f"tensor {t} ({self.graph.tensors[t].name})")
+
     def _ptrs(self, tensors) -> ctypes.Array:
         if isinstance(tensors, dict):
-            ptrs = [C.data_ptr(tensors.get(t)) for t in range(self.n_tensors)]
+            ptrs = [self._ptr(t, tensors.get(t)) for t in range(self.n_tensors)]
         else:
-            ptrs = [C.data_ptr(t) for t in tensors]
+            ptrs = [self._ptr(t, x) for t, x in enumerate(tensors)]
         return C.ptr_array(ptrs)
 
     def run_group(self, g: int, tensors, stream=None) -> None:
@@ -278,10 +288,13 @@ class FuseMulti:
         """sets: one {tensor id: tensor} dict per set."""
         nt = self.plan.n_tensors
         ptrs = []
-        for d in sets:
-            ptrs += [C.data_ptr(d.get(t)) for t in range(nt)]
+        for s, d in enumerate(sets):
+            for t in range(nt):
+                el = C.ELEM_BYTES[self.plan.graph.tensors[t].dtype]
+                ptrs.append(C.device_ptr(d.get(t), self.numel[s] * el, f"set {s} tensor {t}"))
         self._ws, self._sets = workspace, sets  # keep them alive while runs read them
-        C.check(C.lib().fuse_multi_bind(self._h, C.ptr_array(ptrs), C.data_ptr(workspace),
+        C.check(C.lib().fuse_multi_bind(self._h, C.ptr_array(ptrs),
+                                        C.device_ptr(workspace, self.workspace_bytes, "workspace", True),
                                         C.stream_handle(stream)))
 
     def run(self, stream=None) -> None:
@@ -309,6 +322,7 @@ class BucketPlan:
         self._h = h
         self.dtype = dtype
         self.cap_bytes = int(cap_bytes)
+        self._bucket_numel = self.query()[2]
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -337,22 +351,35 @@ class BucketPlan:
 
     def bind(self, workspace, stream=None) -> None:
         self._ws = workspace  # keep it alive as long as the plan uses it
-        C.check(C.lib().bucket_plan_bind(self._h, C.data_ptr(workspace), C.stream_handle(stream)))
+        C.check(C.lib().bucket_plan_bind(self._h, C.device_ptr(workspace, self.workspace_bytes, "workspace", True),
+                                         C.stream_handle(stream)))
+
+    def _tensor_ptrs(self, tensors) -> ctypes.Array:
+        el = C.ELEM_BYTES[self.dtype]
+        if len(tensors) != len(self.numel):
+            raise ValueError(f"{len(tensors)} tensors for a plan of {len(self.numel)}")
+        return C.ptr_array([C.device_ptr(x, n * el, f"tensor {i}")
+                            for i, (x, n) in enumerate(zip(tensors, self.numel))])
+
+    def _bucket_ptrs(self, buckets) -> ctypes.Array:
+        el = C.ELEM_BYTES[self.dtype]
+        if len(buckets) != len(self._bucket_numel):
+            raise ValueError(f"{len(buckets)} buckets for a plan of {len(self._bucket_numel)}")
+        return C.ptr_array([C.device_ptr(x, n * el, f"bucket {k}")
+                            for k, (x, n) in enumerate(zip(buckets, self._bucket_numel))])
 
     def pack(self, srcs, buckets, scale: float = 1.0, stream=None) -> None:
-        C.check(C.lib().bucket_pack(self._h, C.ptr_array([C.data_ptr(t) for t in srcs]),
-                                    C.ptr_array([C.data_ptr(b) for b in buckets]), float(scale),
-                                    C.stream_handle(stream)))
+        C.check(C.lib().bucket_pack(self._h, self._tensor_ptrs(srcs), self._bucket_ptrs(buckets),
+                                    float(scale), C.stream_handle(stream)))
 
     def unpack(self, buckets, dsts, scale: float = 1.0, stream=None) -> None:
-        C.check(C.lib().bucket_unpack(self._h, C.ptr_array([C.data_ptr(b) for b in buckets]),
-                                      C.ptr_array([C.data_ptr(t) for t in dsts]), float(scale),
-                                      C.stream_handle(stream)))
+        C.check(C.lib().bucket_unpack(self._h, self._bucket_ptrs(buckets), self._tensor_ptrs(dsts),
+                                      float(scale), C.stream_handle(stream)))
 
     def launcher(self, unpack: bool, tensors, buckets, scale: float, stream=None):
         """bucket_pack (or bucket_unpack) with its arguments marshalled once."""
-        t = C.ptr_array([C.data_ptr(x) for x in tensors])
-        b = C.ptr_array([C.data_ptr(x) for x in buckets])
+        t = self._tensor_ptrs(tensors)
+        b = self._bucket_ptrs(buckets)
         h, st, sc = self._h, C.stream_handle(stream), float(scale)
         keep = (tensors, buckets)
         if unpack:
@@ -370,7 +397,7 @@ class BucketPlan:
     def slot_address(self, buckets, i: int) -> int:
         """bucket_plan_slot_address: device address of tensor i in its bucket."""
         out = c_void_p()
-        C.check(C.lib().bucket_plan_slot_address(self._h, C.ptr_array([C.data_ptr(b) for b in buckets]),
+        C.check(C.lib().bucket_plan_slot_address(self._h, self._bucket_ptrs(buckets),
                                                  int(i), byref(out)))
         return out.value or 0
 
@@ -388,11 +415,12 @@ class BucketPlan:
         return v
 
     def pack_per_tensor(self, srcs, buckets, scale: float = 1.0, stream=None) -> None:
-        C.check(C.lib().bucket_pack_per_tensor(self._h, C.ptr_array([C.data_ptr(t) for t in srcs]),
-                                               C.ptr_array([C.data_ptr(b) for b in buckets]),
+        C.check(C.lib().bucket_pack_per_tensor(self._h, self._tensor_ptrs(srcs),
+                                               self._bucket_ptrs(buckets),
                                                float(scale), C.stream_handle(stream)))
 
 
 def device_copy(dst, src, nbytes: int, stream=None) -> None:
-    C.check(C.lib().gtf_device_copy(C.data_ptr(dst), C.data_ptr(src), int(nbytes),
+    n = int(nbytes)
+    C.check(C.lib().gtf_device_copy(C.device_ptr(dst, n, "dst", True), C.device_ptr(src, n, "src", True), n,
                                     C.stream_handle(stream)))

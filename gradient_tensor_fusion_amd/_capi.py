@@ -170,3 +170,24 @@ def data_ptr(t) -> int | None:
     if t is None:
         return None
     return t.data_ptr()
+
+
+ELEM_BYTES = {"f32": 4, "bf16": 2, "u8": 1}
+
+
+def device_ptr(t, nbytes: int, what: str, at_least: bool = False) -> int | None:
+    """t's device address, after checking that a torch tensor lives on the
+    GPU, is contiguous and holds exactly nbytes (at least, for a workspace):
+    a host tensor or a wrong size would otherwise reach a kernel as a bad
+    address.  Objects that are not torch tensors pass through unchecked."""
+    if t is None:
+        return None
+    if hasattr(t, "is_cuda"):
+        if not t.is_cuda:
+            raise ValueError(f"{what}: not a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}: not contiguous")
+        have = t.numel() * t.element_size()
+        if have < nbytes or (have != nbytes and not at_least):
+            raise ValueError(f"{what}: {have} bytes where {nbytes} are needed")
+    return t.data_ptr()

@@ -544,3 +544,20 @@ def test_new_entry_point_errors():
     assert L.fuse_plan_group_tensors(plan._h, 0, None, 0, ctypes.byref(n)) == 0 and n.value == 2
     one = (ctypes.c_int32 * 1)()
     assert L.fuse_plan_group_tensors(plan._h, 0, one, 1, ctypes.byref(n)) == C.GTF_E_LIMIT
+
+
+def test_binding_refuses_host_tensors_before_any_launch():
+    """The binding checks every torch tensor it marshals (on the GPU,
+    contiguous, the plan's exact size): a host tensor is refused with
+    ValueError before the library is called."""
+    import torch
+    g = configs.gelu_graph(4, 8)
+    plan = gtf.FusePlan(g)
+    host = {t: torch.zeros(g.tensors[t].shape, dtype=torch.int16) for t in range(len(g.tensors))}
+    with pytest.raises(ValueError, match="not a GPU tensor"):
+        plan.run(host)
+    bp = gtf.BucketPlan([10, 20], "f32", 1 << 20)
+    with pytest.raises(ValueError, match="not a GPU tensor"):
+        bp.pack([torch.zeros(10), torch.zeros(20)], [torch.zeros(30)], 0.5)
+    with pytest.raises(ValueError, match="1 tensors for a plan of 2"):
+        bp.pack([torch.zeros(10)], [torch.zeros(30)], 0.5)
