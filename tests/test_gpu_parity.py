@@ -227,6 +227,32 @@ def test_c5_dropout_residual_bit_exact(rows, hidden):
     assert_bits_equal(got[_out(g)], want[_out(g)])
 
 
+def test_binding_refuses_wrong_sizes_on_the_gpu():
+    """A GPU tensor of the wrong byte size (an f32 buffer where the plan
+    declares bf16), a strided view, or a short bucket is refused with
+    ValueError before any launch; the right ones run."""
+    g = configs.gelu_graph(64, 512)
+    plan = gtf.FusePlan(g)
+    ok = {t: torch.zeros(g.tensors[t].shape, dtype=torch.int16, device="cuda") for t in plan.materialized()}
+    plan.run(ok)
+    wrong = dict(ok)
+    wrong[0] = torch.zeros(g.tensors[0].shape, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="bytes where"):
+        plan.run(wrong)
+    wrong[0] = torch.zeros((512, 64), dtype=torch.int16, device="cuda").t()
+    with pytest.raises(ValueError, match="not contiguous"):
+        plan.run(wrong)
+    bp = gtf.BucketPlan([100, 200], "f32", 1 << 20)
+    bp.bind(torch.empty(max(16, bp.workspace_bytes), dtype=torch.uint8, device="cuda"))
+    src = [torch.ones(100, device="cuda"), torch.ones(200, device="cuda")]
+    with pytest.raises(ValueError, match="bucket 0"):
+        bp.pack(src, [torch.empty(299, device="cuda")], 0.5)
+    bk = [torch.empty(300, device="cuda")]
+    bp.pack(src, bk, 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(bk[0].cpu(), torch.full((300,), 0.5))
+
+
 def test_c5_gradient_buckets_bit_exact():
     numel = configs.c5_numel()
     host, dev = _grads_dev(numel, configs.C5_GRAD_SEED)
