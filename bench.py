@@ -58,7 +58,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "joint", "ln", "search", "transpose",
-                             "groups", "softmax"])
+                             "groups", "softmax", "ceiling"])
     ap.add_argument("--layers", type=int, default=12)
     ap.add_argument("--valu-from", metavar="VALU_CSV",
                     help="summarise a rocprofv3 SQ_INSTS_VALU/SQ_WAVES run of --workload groups "
@@ -224,7 +224,7 @@ class C5:
             for f in self.exec_calls:
                 f()
             self.bp.pack_per_tensor(self.grads, self.buckets, self.scale)
-            self.bp.unpack(self.buckets, self.grads, 1.0)
+            self.bp.unpack_per_tensor(self.buckets, self.grads, 1.0)
             return
         if exec_t is None:
             for f in self.exec_calls:
@@ -236,20 +236,40 @@ class C5:
         bucket_t.block(self.bucket_calls)
 
 
+class Timing:
+    """Times of `steps` back-to-back steps: the mean (first to last event,
+    the figure the whole-job throughput uses), the wall time of the timed
+    region, and the distribution of per-step times from the events recorded
+    between consecutive steps."""
+
+    def __init__(self, mean, wall, per_step):
+        import numpy as np
+        self.mean, self.wall = mean, wall
+        p = np.asarray(per_step, dtype=np.float64)
+        self.median = float(np.median(p))
+        self.p10 = float(np.percentile(p, 10))
+        self.p90 = float(np.percentile(p, 90))
+
+    def dist(self, scale=1.0, digits=5):
+        """median, p10, p90 of the per-step times in ms (times `scale`)."""
+        return {"median": round(self.median * scale, digits), "p10": round(self.p10 * scale, digits),
+                "p90": round(self.p90 * scale, digits)}
+
+
 def time_steps(torch, fn, steps, warmup):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         fn()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return Timing(ev[0].elapsed_time(ev[steps]) / steps, wall, per)
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -329,7 +349,7 @@ class CopyBench:
 
     def gbs(self, reps=10):
         self.run()
-        ms, _ = time_steps(self.torch, self.run, reps, 1)
+        ms = time_steps(self.torch, self.run, reps, 1).median
         return 2 * self.NBYTES / (ms * 1e-3) / 1e9, ms
 
 
@@ -369,9 +389,10 @@ def main():
         return
     w = C5(torch, gtf, configs, args.layers)
     # timed region: K whole steps
-    ms, wall = time_steps(torch, w.step, args.steps, args.warmup)
-    nbytes = w.bytes_per_step()
-    value = nbytes / (ms * 1e-3) / 1e9
+    tm = time_steps(torch, w.step, args.steps, args.warmup)
+    ms, wall = tm.mean, tm.wall
+    step_bytes = w.bytes_per_step()
+    value = step_bytes / (ms * 1e-3) / 1e9
     # per-kernel timing over a second pass of the same steps: per step, one
     # event pair around the executor launches and one around the bucket
     # launches; queued copies first put the GPU ahead of the host
@@ -389,19 +410,19 @@ def main():
     gt = Timer(torch, 3 * 5)
     torch.cuda.synchronize()
     cb.lead()
-    for name, (calls, nbytes) in w.group_calls().items():
+    for name, (calls, gbytes) in w.group_calls().items():
         t0 = gt.i
         for _ in range(3):
             gt.block(calls)
-        groups[name] = (t0, len(calls), nbytes)
+        groups[name] = (t0, len(calls), gbytes)
     torch.cuda.synchronize()
     valu = read_valu()
     group_rows = {}
-    for name, (t0, n, nbytes) in groups.items():
+    for name, (t0, n, gbytes) in groups.items():
         gms = sum(gt.ev[i][0].elapsed_time(gt.ev[i][1]) for i in range(t0, t0 + 3)) / (3 * n)
-        row = {"avg_launch_us": round(gms * 1e3, 3), "bytes_per_launch": nbytes,
-               "gbs": round(nbytes / (gms * 1e-3) / 1e9, 1),
-               "hbm_frac": round(nbytes / (gms * 1e-3) / 1e9 / PEAK_GBS, 4)}
+        row = {"avg_launch_us": round(gms * 1e3, 3), "bytes_per_launch": gbytes,
+               "gbs": round(gbytes / (gms * 1e-3) / 1e9, 1),
+               "hbm_frac": round(gbytes / (gms * 1e-3) / 1e9 / PEAK_GBS, 4)}
         if valu and name in valu:
             rate = valu[name] / (gms * 1e-3)
             row["valu_lane_instr_per_launch"] = valu[name]
@@ -419,10 +440,20 @@ def main():
         dom = {"kernel": "exec_kernel", "launches_per_step": n_exec,
                "avg_launch_us": round(exec_ms * 1e3 / n_exec, 3),
                "bytes_per_launch": w.exec_bytes_per_step() / n_exec, "gbs": exec_gbs}
+        # VALU issue fraction of the executor over the step: its lane
+        # instructions per step (every group, every layer) over its time
+        if valu and all(k in valu for k in group_rows):
+            lanes = sum(valu[k] for k in group_rows) * len(w.layers)
+            dom["valu_frac"] = lanes / (exec_ms * 1e-3) / VALU_PEAK
     else:
         dom = {"kernel": "bucket_kernel", "launches_per_step": 2,
                "avg_launch_us": round(bucket_ms * 1e3 / 2, 3),
-               "bytes_per_launch": w.bucket_bytes, "gbs": bucket_gbs}
+               "bytes_per_launch": w.bucket_bytes, "gbs": bucket_gbs, "valu_frac": 0.0}
+    hbm_frac = dom["gbs"] / PEAK_GBS
+    # the roofline that binds is the larger of the two fractions (the
+    # executor's VALU count comes from the committed counter summary; without
+    # one for these sources the bound is not known)
+    bound = None if "valu_frac" not in dom else ("alu" if dom["valu_frac"] > hbm_frac else "hbm")
     traffic = None
     tj = read_traffic(dom["kernel"])
     if tj is not None:
@@ -438,12 +469,14 @@ def main():
                                "tensors (151,156,736 elements) in 25 MiB buckets, scale 1/8",
                    "layers": args.layers, "tokens": 8192, "hidden": 1024, "ffn": 4096,
                    "storage": "bf16 activations, fp32 gradients; fp32 arithmetic",
-                   "bytes_per_step": nbytes, "launches_per_step": w.launches},
-        "roofline": {"bound": "hbm", "achieved": round(dom["gbs"], 1), "peak": PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom["gbs"] / PEAK_GBS, 4),
+                   "bytes_per_step": step_bytes, "launches_per_step": w.launches},
+        "step_ms": tm.dist(digits=4),
+        "roofline": {"bound": bound, "achieved": round(dom["gbs"], 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(hbm_frac, 4),
                      "traffic": traffic, "kernel": dom["kernel"],
                      "avg_launch_us": dom["avg_launch_us"],
-                     "algorithmic_bytes_per_launch": round(dom["bytes_per_launch"])},
+                     "algorithmic_bytes_per_launch": round(dom["bytes_per_launch"]),
+                     "valu_frac": round(dom["valu_frac"], 4) if "valu_frac" in dom else None},
         "groups": group_rows,
         "breakdown": {"exec_ms_per_step": round(exec_ms, 4), "exec_gbs": round(exec_gbs, 1),
                       "bucket_ms_per_step": round(bucket_ms, 4), "bucket_gbs": round(bucket_gbs, 1),
@@ -455,12 +488,13 @@ def main():
         del w
         torch.cuda.empty_cache()
         u = C5(torch, gtf, configs, args.layers, fuse=False)
-        ums, _ = time_steps(torch, lambda: u.step(per_tensor=True), max(2, args.steps // 2), 1)
+        ums = time_steps(torch, lambda: u.step(per_tensor=True), max(2, args.steps // 2), 1).mean
+        n_grads = len([n for n in configs.c5_numel() if n])
         result["speedup_vs_unfused"] = round(ums / ms, 3)
         result["unfused"] = {"ms_per_step": round(ums, 4), "launches_per_step":
-                             args.layers * 15 + 2 * 194,
+                             len(u.exec_calls) + 2 * n_grads,
                              "note": "one launch per op with bf16/fp32 intermediates stored; "
-                                     "one pack launch per gradient tensor"}
+                                     "one pack and one unpack launch per gradient tensor"}
         del u
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
@@ -496,36 +530,54 @@ def run_config(torch, gtf, configs, args):
         sets = [([torch.randn(n, generator=gen, device="cuda") * 1e-3 for n in numel],
                  [torch.empty(n, dtype=torch.float32, device="cuda") for n in bn]) for _ in range(k)]
         it = [0]
+        # every launch marshalled once (pointer arrays for 161 tensors and
+        # the buckets), so the timed loop is not bound by the host
+        packs = [bp.launcher(False, g, b, configs.AVG_SCALE) for g, b in sets]
+        unpacks = [bp.launcher(True, g, b, 1.0) for g, b in sets]
 
         def pack():
-            g, b = sets[it[0] % k]
+            packs[it[0] % k]()
             it[0] += 1
-            bp.pack(g, b, configs.AVG_SCALE)
 
         def unpack():
-            g, b = sets[it[0] % k]
+            unpacks[it[0] % k]()
             it[0] += 1
-            bp.unpack(b, g, 1.0)
 
         def pack_pt():
             g, b = sets[it[0] % k]
             it[0] += 1
             bp.pack_per_tensor(g, b, configs.AVG_SCALE)
+
+        def warm_pack():
+            packs[0]()
         # every rotation set is touched in the warmup, so none is first used
         # inside the timed region
         wu = max(args.warmup, k)
-        ms_p, _ = time_steps(torch, pack, args.steps, wu)
-        ms_u, _ = time_steps(torch, unpack, args.steps, wu)
-        ms_t, _ = time_steps(torch, pack_pt, args.steps, wu)
+        tp = time_steps(torch, pack, args.steps, wu)
+        tu = time_steps(torch, unpack, args.steps, wu)
+        tt = time_steps(torch, pack_pt, args.steps, wu)
+        tw = time_steps(torch, warm_pack, args.steps, args.warmup)
+        ms_p = tp.mean
         gbs = 2 * payload / (ms_p * 1e-3) / 1e9
+        gb = lambda ms: round(2 * payload / (ms * 1e-3) / 1e9, 1)  # noqa: E731
         res.update({"value": round(gbs, 2), "ms_per_step": round(ms_p, 4),
                     "config": {"workload": "c4: pack 161 fp32 gradient tensors (25.6M elements) into "
-                                           "25 MiB buckets x 1/8", "rotation_sets": k},
-                    "unpack_gbs": round(2 * payload / (ms_u * 1e-3) / 1e9, 2),
-                    "per_tensor_pack_ms": round(ms_t, 4),
-                    "speedup_vs_per_tensor": round(ms_t / ms_p, 3),
+                                           "25 MiB buckets x 1/8", "rotation_sets": k,
+                               "bytes_per_step": 2 * payload},
+                    "step_ms": tp.dist(),
+                    "step_gbs": {"median": gb(tp.median), "p10_time": gb(tp.p10), "p90_time": gb(tp.p90)},
+                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(gbs / PEAK_GBS, 4), "kernel": "bucket_kernel",
+                                 "traffic": None},
+                    "unpack_gbs": gb(tu.mean), "unpack_step_ms": tu.dist(),
+                    "warm": {"ms_per_step": round(tw.mean, 5), "gbs": gb(tw.mean),
+                             "note": "one buffer set packed again and again (no rotation)"},
+                    "per_tensor_pack_ms": round(tt.mean, 4),
+                    "speedup_vs_per_tensor": round(tt.mean / ms_p, 3),
                     "launches": {"one_launch": 1, "per_tensor": len([n for n in numel if n])}})
         return res
+    if w == "ceiling":
+        return run_ceiling(torch, gtf, args, res)
     if w == "joint":
         return run_joint(torch, gtf, configs, args, res, gen)
     if w == "ln":
@@ -554,20 +606,85 @@ def run_config(torch, gtf, configs, args):
         nbytes = sum(group_bytes(g, plan))
         k = _rotation_sets(nbytes) if w != "c1" else 1
         sets = [alloc_graph(torch, gtf, g, plan, gen, dists) for _ in range(k)]
+        # every launch marshalled once, so the timed loop is not host-bound
+        calls = [[plan.launcher(q, st) for q in range(plan.num_groups)] for st in sets]
         it = [0]
 
         def step():
-            plan.run(sets[it[0] % k])
+            for f in calls[it[0] % k]:
+                f()
             it[0] += 1
-        ms, _ = time_steps(torch, step, args.steps * (50 if w == "c1" else 1), max(args.warmup, k))
-        out[fuse] = (ms, nbytes, plan.num_groups, k)
-    ms, nbytes, ng, k = out[True]
-    res.update({"value": round(nbytes / (ms * 1e-3) / 1e9, 2), "ms_per_step": round(ms, 5),
+
+        def warm():
+            for f in calls[0]:
+                f()
+        n = args.steps * (50 if w == "c1" else 1)
+        tm = time_steps(torch, step, n, max(args.warmup, k))
+        # warm: the first set again and again (the Infinity Cache may serve it)
+        tw = time_steps(torch, warm, n, args.warmup)
+        out[fuse] = (tm, nbytes, plan.num_groups, k, tw)
+        del sets
+    tm, nbytes, ng, k, tw = out[True]
+    ms = tm.mean
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res.update({"value": round(gbs, 2), "ms_per_step": round(ms, 5),
                 "config": {"workload": desc, "rotation_sets": k, "bytes_per_step": nbytes},
-                "speedup_vs_unfused": round(out[False][0] / ms, 3),
-                "unfused": {"ms_per_step": round(out[False][0], 5), "bytes": out[False][1],
-                            "launches": out[False][2]},
+                "step_ms": tm.dist(),
+                "warm": {"ms_per_step": round(tw.mean, 5), "gbs": round(nbytes / (tw.mean * 1e-3) / 1e9, 1),
+                         "note": "one buffer set run again and again (no rotation)"},
+                "speedup_vs_unfused": round(out[False][0].mean / ms, 3),
+                "unfused": {"ms_per_step": round(out[False][0].mean, 5), "bytes": out[False][1],
+                            "launches": out[False][2], "step_ms": out[False][0].dist(),
+                            "warm_ms_per_step": round(out[False][4].mean, 5)},
                 "launches": ng})
+    if w != "c1":
+        res["roofline"] = {"bound": None, "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                           "frac": round(gbs / PEAK_GBS, 4), "kernel": "exec_kernel", "traffic": None}
+    return res
+
+
+def run_ceiling(torch, gtf, args, res):
+    """The streaming ceiling of this part: 1 GiB copied, read or written by
+    the library's probe kernels (gtf_stream_probe) over every combination of
+    16-byte accesses in flight per thread (4, 8, 16), nontemporal or
+    ordinary accesses, and grid (one workgroup per span, or 8, 16, 32
+    resident workgroups per CU in a grid-stride loop).  Each point is the
+    median of `steps` launches; copy counts 2 bytes per byte moved, read and
+    write 1.  Ten launches of 1 GiB are far past the Infinity Cache."""
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    src.random_(0, 256)
+    dst = torch.empty_like(src)
+    kinds = {0: "copy", 1: "read", 2: "write"}
+    table = []
+    best = {}
+    for kind, kname in kinds.items():
+        for depth in (4, 8, 16):
+            for nt in (False, True):
+                for grid in (0, 8, 16, 32):
+                    def run():
+                        gtf.stream_probe(kind, depth, nt, grid, dst, src, nb)
+                    ms = time_steps(torch, run, max(5, args.steps // 2), 2).median
+                    gbs = (2 if kind == 0 else 1) * nb / (ms * 1e-3) / 1e9
+                    row = {"kind": kname, "depth": depth, "nontemporal": nt, "grid_per_cu": grid,
+                           "ms": round(ms, 4), "gbs": round(gbs, 1)}
+                    table.append(row)
+                    if kname not in best or gbs > best[kname]["gbs"]:
+                        best[kname] = row
+    cb = CopyBench(torch, gtf)
+    lib_copy, _ = cb.gbs(10)
+    del cb
+    torch.cuda.synchronize()
+    t = time_steps(torch, lambda: dst.copy_(src), 10, 2)
+    dtod = 2 * nb / (t.median * 1e-3) / 1e9
+    res.update({"value": best["copy"]["gbs"], "ms_per_step": best["copy"]["ms"],
+                "config": {"workload": "ceiling: 1 GiB streamed by copy, read-only and write-only "
+                                       "probe kernels over accesses in flight, nontemporal and grid",
+                           "bytes_per_step": 2 * nb},
+                "best": best, "library_copy_kernel_gbs": round(lib_copy, 1),
+                "torch_copy_gbs": round(dtod, 1),
+                "frac_of_8tbs": {k: round(v["gbs"] / PEAK_GBS, 4) for k, v in best.items()},
+                "table": table})
     return res
 
 
@@ -608,7 +725,7 @@ def run_ln(torch, gtf, configs, args, res, gen):
                 plan.run(st)
         # one replay runs the LayerNorm once on each of the k rotation sets
         graph = _captured(torch, rotation)
-        ms, _ = time_steps(torch, graph.replay, args.steps, args.warmup)
+        ms = time_steps(torch, graph.replay, args.steps, args.warmup).mean
         ms /= k
         out[name] = {"ms_per_step": round(ms, 5), "bytes": nbytes, "launches": plan.num_groups,
                      "gbs": round(nbytes / (ms * 1e-3) / 1e9, 2)}
@@ -866,7 +983,7 @@ def time_plan(torch, gtf, graph, plan, gen, dists, steps, warmup):
         for st in sets:
             plan.run(st)
     g = _captured(torch, rotation)
-    ms, _ = time_steps(torch, g.replay, steps, warmup)
+    ms = time_steps(torch, g.replay, steps, warmup).mean
     del sets
     return ms / k, nbytes
 
@@ -996,9 +1113,9 @@ def run_joint(torch, gtf, configs, args, res, gen):
     g_joint = captured(lambda: mj.run())
     g_sep = captured(lambda: (ms_.run(), bp.pack(outs, buckets, configs.AVG_SCALE)))
     g_per = captured(per_tensor)
-    ms_j, _ = time_steps(torch, g_joint.replay, args.steps, args.warmup)
-    ms_s, _ = time_steps(torch, g_sep.replay, args.steps, args.warmup)
-    ms_p, _ = time_steps(torch, g_per.replay, args.steps, args.warmup)
+    ms_j = time_steps(torch, g_joint.replay, args.steps, args.warmup).mean
+    ms_s = time_steps(torch, g_sep.replay, args.steps, args.warmup).mean
+    ms_p = time_steps(torch, g_per.replay, args.steps, args.warmup).mean
     bytes_j = 12 * total              # read g and w, write the bucket slot
     bytes_s = 12 * total + 8 * total  # ... plus the pack's read and write
     res.update({"value": round(bytes_j / (ms_j * 1e-3) / 1e9, 2), "ms_per_step": round(ms_j, 4),

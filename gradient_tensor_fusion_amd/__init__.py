@@ -24,7 +24,7 @@ from typing import Dict, List, Sequence
 from . import _capi as C
 from ._capi import GtfError
 
-__all__ = ["FusePlan", "FuseMulti", "BucketPlan", "device_copy", "search", "GtfError",
+__all__ = ["FusePlan", "FuseMulti", "BucketPlan", "device_copy", "stream_probe", "search", "GtfError",
            "PATTERN_NAMES"]
 
 PATTERN_NAMES = {0: "kElemWise", 1: "kBroadcast", 2: "kInjective", 3: "kCommReduce",
@@ -196,6 +196,9 @@ class FusePlan:
         if isinstance(tensors, dict):
             ptrs = [self._ptr(t, tensors.get(t)) for t in range(self.n_tensors)]
         else:
+            # the library reads one pointer per tensor of the graph
+            if len(tensors) != self.n_tensors:
+                raise ValueError(f"{len(tensors)} tensors for a graph of {self.n_tensors}")
             ptrs = [self._ptr(t, x) for t, x in enumerate(tensors)]
         return C.ptr_array(ptrs)
 
@@ -287,6 +290,9 @@ class FuseMulti:
     def bind(self, sets, workspace, stream=None) -> None:
         """sets: one {tensor id: tensor} dict per set."""
         nt = self.plan.n_tensors
+        # the library reads one row of pointers per set it was created with
+        if len(sets) != len(self.numel):
+            raise ValueError(f"{len(sets)} tensor sets for a run of {len(self.numel)}")
         ptrs = []
         for s, d in enumerate(sets):
             for t in range(nt):
@@ -418,6 +424,21 @@ class BucketPlan:
         C.check(C.lib().bucket_pack_per_tensor(self._h, self._tensor_ptrs(srcs),
                                                self._bucket_ptrs(buckets),
                                                float(scale), C.stream_handle(stream)))
+
+    def unpack_per_tensor(self, buckets, dsts, scale: float = 1.0, stream=None) -> None:
+        C.check(C.lib().bucket_unpack_per_tensor(self._h, self._bucket_ptrs(buckets),
+                                                 self._tensor_ptrs(dsts),
+                                                 float(scale), C.stream_handle(stream)))
+
+
+def stream_probe(kind: int, depth: int, nontemporal: bool, grid_per_cu: int, dst, src,
+                 nbytes: int, stream=None) -> None:
+    """gtf_stream_probe: copy (kind 0), read (1) or write (2) nbytes."""
+    n = int(nbytes)
+    sp = None if kind == 2 else C.device_ptr(src, n, "src", True)
+    C.check(C.lib().gtf_stream_probe(int(kind), int(depth), int(bool(nontemporal)), int(grid_per_cu),
+                                     C.device_ptr(dst, n, "dst", True), sp, n,
+                                     C.stream_handle(stream)))
 
 
 def device_copy(dst, src, nbytes: int, stream=None) -> None:

@@ -45,7 +45,8 @@ EXPORTED = (
     "fuse_multi_destroy",
     "bucket_plan_create", "bucket_plan_query", "bucket_plan_workspace_bytes",
     "bucket_plan_bind", "bucket_pack", "bucket_unpack", "bucket_pack_per_tensor",
-    "bucket_plan_slot_address", "bucket_plan_destroy", "gtf_device_copy", "gtf_last_error",
+    "bucket_unpack_per_tensor", "bucket_plan_slot_address", "bucket_plan_destroy",
+    "gtf_device_copy", "gtf_stream_probe", "gtf_last_error",
 )
 
 
@@ -137,10 +138,12 @@ def lib() -> ctypes.CDLL:
         L.bucket_pack.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
         L.bucket_unpack.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
         L.bucket_pack_per_tensor.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
+        L.bucket_unpack_per_tensor.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
         L.bucket_plan_slot_address.argtypes = [vp, POINTER(vp), c_int32, POINTER(vp)]
         L.bucket_plan_destroy.argtypes = [vp]
         L.bucket_plan_destroy.restype = None
         L.gtf_device_copy.argtypes = [vp, vp, c_size_t, vp]
+        L.gtf_stream_probe.argtypes = [c_int32, c_int32, c_int32, c_int32, vp, vp, c_size_t, vp]
         L.gtf_last_error.argtypes = []
         L.gtf_last_error.restype = c_char_p
         _lib = L

@@ -42,6 +42,8 @@ int launch_bucket(const BucketPlan& b, const void* const* tens, void* const* bk,
                   bool unpack, bool per_tensor, hipStream_t stream);
 int upload_chunks(BucketPlan& b, void* ws, hipStream_t stream);
 int launch_copy(void* dst, const void* src, size_t nbytes, hipStream_t stream);
+int launch_stream_probe(int kind, int depth, int nontemporal, int grid_per_cu, void* dst,
+                        const void* src, size_t nbytes, hipStream_t stream);
 int launch_multi(const CompiledGroup& cg, const void* ws, size_t off_ptrs, size_t off_vec,
                  int64_t n_items, hipStream_t stream);
 int upload_bytes(void* dst, const void* src, size_t n, hipStream_t stream);
@@ -486,6 +488,12 @@ int bucket_pack_per_tensor(const gtf_bucket_plan* plan, const void* const* src,
   return bucket_run(plan, src, buckets, scale, false, true, hip_stream);
 }
 
+int bucket_unpack_per_tensor(const gtf_bucket_plan* plan, const void* const* buckets,
+                             void* const* dst, float scale, void* hip_stream) {
+  return bucket_run(plan, (const void* const*)dst, (void* const*)buckets, scale, true, true,
+                    hip_stream);
+}
+
 int bucket_plan_slot_address(const gtf_bucket_plan* plan, void* const* buckets, int32_t i,
                              void** out) {
   if (plan == nullptr || buckets == nullptr || out == nullptr)
@@ -585,6 +593,15 @@ int gtf_device_copy(void* dst, const void* src, size_t nbytes, void* hip_stream)
   if ((((uintptr_t)dst | (uintptr_t)src) & 15) != 0 || (nbytes & 15) != 0)
     return fail(GTF_E_INVALID, "copy needs 16-byte aligned pointers and size");
   return launch_copy(dst, src, nbytes, (hipStream_t)hip_stream);
+}
+
+int gtf_stream_probe(int32_t kind, int32_t depth, int32_t nontemporal, int32_t grid_per_cu,
+                     void* dst, const void* src, size_t nbytes, void* hip_stream) {
+  if (dst == nullptr || (kind != 2 && src == nullptr)) return fail(GTF_E_INVALID, "NULL pointer");
+  if ((((uintptr_t)dst | (uintptr_t)src) & 15) != 0 || (nbytes & 15) != 0)
+    return fail(GTF_E_INVALID, "stream probe needs 16-byte aligned pointers and size");
+  return launch_stream_probe(kind, depth, nontemporal, grid_per_cu, dst, src, nbytes,
+                             (hipStream_t)hip_stream);
 }
 
 }  // extern "C"

@@ -29,6 +29,7 @@
 
 #include <stdint.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <string>
@@ -79,24 +80,47 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p) {
 // (v_exp_f32, about 1 ulp), with x log2 e carried as yh + yl: yh = fl(x L)
 // with L = log2 e rounded to fp32, yl = the exact error of that product
 // (one fma) plus x times the rest of log2 e.  Then e^x = 2^yh (1 + yl ln 2)
-// up to (yl ln 2)^2 / 2 < 1e-10 relative.  About 1.5 ulp in all; 5 VALU
-// slots against about 12 for the library expf, which also handles
-// overflow, which a non-positive argument cannot reach.  Results below
-// the normal range come out of v_exp_f32 flushed.
-__device__ __forceinline__ float exp_nonpos(float x) {
+// up to (yl ln 2)^2 / 2 < 1e-10 relative.  About 1.5 ulp in all, against
+// about 12 VALU slots for the library expf, which also handles overflow, out
+// of reach for a non-positive argument.  Results below the normal range
+// come out of v_exp_f32 flushed.
+// yl is computed from x clamped to [-104, 0] (one v_med3, no lane mask):
+// at -inf, or where x L overflows, the error term of the unclamped product
+// would be -inf + inf = NaN, while below -104 e^x rounds to 0 whatever yl
+// is.  yh keeps the unclamped x, so -inf gives 0 and NaN stays NaN.
+struct ExpSplit {
+  float yh, yl;
+};
+__device__ __forceinline__ ExpSplit exp_split(float x) {
   constexpr float kL = 1.44269502e+00f;       // log2(e) rounded to fp32
   constexpr float kLlo = 1.92596299e-08f;     // log2(e) - kL
+  const float xc = __builtin_amdgcn_fmed3f(x, -104.0f, 0.0f);
+  const float yc = xc * kL;
+  return ExpSplit{x * kL, __builtin_fmaf(xc, kL, -yc) + xc * kLlo};
+}
+__device__ __forceinline__ float exp_nonpos(float x) {
   constexpr float kLn2 = 6.93147182e-01f;
-  const float yh = x * kL;
-  const float yl = __builtin_fmaf(x, kL, -yh) + x * kLlo;
-  const float p = __builtin_amdgcn_exp2f(yh);
-  return __builtin_fmaf(p, yl * kLn2, p);
+  const ExpSplit y = exp_split(x);
+  const float p = __builtin_amdgcn_exp2f(y.yh);
+  return __builtin_fmaf(p, y.yl * kLn2, p);
+}
+// The same, keeping results in fp32's subnormal range (the tails of sigmoid
+// and the fp32 GELU are results in their own right): 2^yh is taken as the
+// square of 2^(yh / 2), which is normal down to yh = -252, so the square
+// underflows gradually, correctly rounded, instead of being flushed.  Two
+// VALU slots more and about one ulp more error.
+__device__ __forceinline__ float exp_nonpos_sub(float x) {
+  constexpr float kLn2 = 6.93147182e-01f;
+  const ExpSplit y = exp_split(x);
+  const float h = __builtin_amdgcn_exp2f(y.yh * 0.5f);
+  const float p = h * h;
+  return __builtin_fmaf(p, y.yl * kLn2, p);
 }
 
 __device__ __forceinline__ float f_sigmoid(float x) {
   // 1 / (1 + e^-x), written as e^x / (1 + e^x) for x < 0 so the tail keeps
   // its relative accuracy; one correctly rounded division
-  const float e = exp_nonpos(-fabsf(x));
+  const float e = exp_nonpos_sub(-fabsf(x));
   const float num = x >= 0.f ? 1.f : e;
   return num / (1.f + e);
 }
@@ -121,7 +145,7 @@ __device__ __forceinline__ float f_gelu(float x) {
   const float tc = fminf(t, 20.0f);
   const float hi = tc * tc;
   const float lo = __builtin_fmaf(tc, tc, -hi);
-  float e = exp_nonpos(-0.5f * hi);
+  float e = exp_nonpos_sub(-0.5f * hi);
   e = __builtin_fmaf(e, -0.5f * lo, e);
   const float u = __builtin_amdgcn_rcpf(__builtin_fmaf(kGeluP, t, 1.0f));
   float P = -2.8428646e-02f;
@@ -211,6 +235,22 @@ __device__ __forceinline__ void pstore_b16(void* addr, uint32_t v, uint64_t mask
 }
 __device__ __forceinline__ uint64_t lanes(bool c) { return __builtin_amdgcn_ballot_w64(c); }
 
+// A wave-uniform value the compiler must treat as produced right here: the
+// tests and arithmetic on it that follow cannot be hoisted out of the
+// enclosing loop.  The executor's loop-invariant conditions, hoisted, each
+// hold a pair of SGPRs for the whole kernel; past the SGPR budget they are
+// spilled to VGPR lanes.  Recomputing one is a scalar compare.
+template <typename T>
+__device__ __forceinline__ T here(T x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+// The same for a per-lane value (lane masks derived from the lane index).
+__device__ __forceinline__ int here_lane(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // ---------------------------------------------------------------- context
 // A lane's tile.  In the whole-tile (FAST) instance it is V / kV sub-tiles
 // of kV consecutive elements, kstride elements apart in the same row; in
@@ -270,6 +310,21 @@ __device__ __forceinline__ int64_t tile_base(const Tile& t) {
 
 __device__ __forceinline__ float bf16_g(const GAS uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
 
+// Streamed element tiles are read with nontemporal loads: data read once
+// need not displace what the caches hold for reuse (broadcast panels, the
+// op program), and on this part streaming loads reach a higher share of
+// HBM bandwidth (the stream probes: reads 7.0 TB/s against 6.2 with
+// ordinary loads).
+__device__ __forceinline__ u4 ld_nt16(const GAS void* p) {
+  return __builtin_nontemporal_load((const GAS u4*)p);
+}
+__device__ __forceinline__ f4 ld_nt16f(const GAS void* p) {
+  return __builtin_nontemporal_load((const GAS f4*)p);
+}
+__device__ __forceinline__ u2 ld_nt8(const GAS void* p) {
+  return __builtin_nontemporal_load((const GAS u2*)p);
+}
+
 template <int V, int MODE, bool FAST>
 __device__ __forceinline__ void load_f32(float (&d)[V], const ExecArgs& a, int slot, const Tile& t) {
   const GAS float* b = (const GAS float*)t.ptrs[slot];
@@ -285,8 +340,9 @@ __device__ __forceinline__ void load_f32(float (&d)[V], const ExecArgs& a, int s
       const GAS float* p = b + base;
 #pragma unroll
       for (int k = 0; k < V / kV; ++k) {
-        const f4 x = *(const GAS f4*)(p + k * t.kstride);
-        const f4 y = *(const GAS f4*)(p + k * t.kstride + 4);
+        const f4 x = MODE == M_ELEM ? ld_nt16f(p + k * here(t.kstride)) : *(const GAS f4*)(p + k * here(t.kstride));
+        const f4 y = MODE == M_ELEM ? ld_nt16f(p + k * here(t.kstride) + 4)
+                                    : *(const GAS f4*)(p + k * here(t.kstride) + 4);
         d[k * kV + 0] = x.x; d[k * kV + 1] = x.y; d[k * kV + 2] = x.z; d[k * kV + 3] = x.w;
         d[k * kV + 4] = y.x; d[k * kV + 5] = y.y; d[k * kV + 6] = y.z; d[k * kV + 7] = y.w;
       }
@@ -296,7 +352,7 @@ __device__ __forceinline__ void load_f32(float (&d)[V], const ExecArgs& a, int s
 #pragma unroll
       for (int k = 0; k < V / kV; ++k)
 #pragma unroll
-        for (int i = 0; i < kV; ++i) d[k * kV + i] = b[base + k * t.kstride + i];
+        for (int i = 0; i < kV; ++i) d[k * kV + i] = b[base + k * here(t.kstride) + i];
       return;
     }
 #pragma unroll
@@ -320,14 +376,16 @@ __device__ __forceinline__ void load_bf16(float (&d)[V], const ExecArgs& a, int 
     if ((FAST || t.vec) && slot_vec(t, slot)) {
       const GAS uint16_t* p = b + base;
 #pragma unroll
-      for (int k = 0; k < V / kV; ++k) expand_bf16(d + k * kV, *(const GAS u4*)(p + k * t.kstride));
+      for (int k = 0; k < V / kV; ++k)
+        expand_bf16(d + k * kV, MODE == M_ELEM ? ld_nt16(p + k * here(t.kstride))
+                                               : *(const GAS u4*)(p + k * here(t.kstride)));
       return;
     }
     if (FAST || t.vec) {  // whole tile, element-aligned only
 #pragma unroll
       for (int k = 0; k < V / kV; ++k)
 #pragma unroll
-        for (int i = 0; i < kV; ++i) d[k * kV + i] = bf16_g(b + base + k * t.kstride + i);
+        for (int i = 0; i < kV; ++i) d[k * kV + i] = bf16_g(b + base + k * here(t.kstride) + i);
       return;
     }
 #pragma unroll
@@ -335,6 +393,110 @@ __device__ __forceinline__ void load_bf16(float (&d)[V], const ExecArgs& a, int 
     return;
   }
   d[0] = bf16_g(b + elem_offset<V, MODE>(a, slot, t));
+}
+
+// Split loads (element phase).  The raw words of a bf16 or u8 tile go to
+// the top of the register -- bf16: word j (elements 2j, 2j + 1) at
+// d[V/2 + j]; u8: word j (elements 4j .. 4j + 3) at d[3V/4 + j] -- and the
+// expansion, a separate instruction, widens them in place in ascending
+// order: word j is read before elements 2j, 2j + 1 (4j .. 4j + 3) are
+// written, and no later word sits below those.  Between the two the
+// register holds no value, and the load is in flight while other
+// instructions issue.  Partial tiles read element by element at clamped
+// in-range indices and pack the words the same way.
+template <int V, bool FAST>
+__device__ __forceinline__ void load_raw_bf16(float (&d)[V], int slot, const Tile& t) {
+  const GAS uint16_t* b = (const GAS uint16_t*)t.ptrs[slot];
+  const int64_t base = t.eoff;
+  // the register's old values are dead from here on (the expansion writes
+  // every element): their VGPRs are free for the element-wise paths
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) asm volatile("" : "=v"(d[i]));
+  if ((FAST || t.vec) && slot_vec(t, slot)) {
+#pragma unroll
+    for (int k = 0; k < V / kV; ++k) {
+      const u4 w = ld_nt16(b + base + k * here(t.kstride));
+      d[V / 2 + 4 * k + 0] = __uint_as_float(w.x);
+      d[V / 2 + 4 * k + 1] = __uint_as_float(w.y);
+      d[V / 2 + 4 * k + 2] = __uint_as_float(w.z);
+      d[V / 2 + 4 * k + 3] = __uint_as_float(w.w);
+    }
+    return;
+  }
+  if (FAST || t.vec) {  // whole tile, element-aligned only
+#pragma unroll
+    for (int k = 0; k < V / kV; ++k) {
+      const GAS uint16_t* q = b + base + k * here(t.kstride);
+#pragma unroll
+      for (int j = 0; j < kV / 2; ++j)
+        d[V / 2 + k * (kV / 2) + j] = __uint_as_float((uint32_t)q[2 * j] | ((uint32_t)q[2 * j + 1] << 16));
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < V / 2; ++j) {
+    const int e0 = 2 * j, e1 = 2 * j + 1;
+    const int64_t i0 = (t.valid && e0 < t.cnt) ? base + e0 : 0;
+    const int64_t i1 = (t.valid && e1 < t.cnt) ? base + e1 : 0;
+    d[V / 2 + j] = __uint_as_float((uint32_t)b[i0] | ((uint32_t)b[i1] << 16));
+  }
+}
+template <int V, bool FAST>
+__device__ __forceinline__ void load_raw_u8(float (&d)[V], int slot, const Tile& t) {
+  const GAS uint8_t* b = (const GAS uint8_t*)t.ptrs[slot];
+  const int64_t base = t.eoff;
+#pragma unroll
+  for (int i = 0; i < 3 * V / 4; ++i) asm volatile("" : "=v"(d[i]));
+  if ((FAST || t.vec) && slot_vec(t, slot)) {
+#pragma unroll
+    for (int k = 0; k < V / kV; ++k) {
+      const u2 w = ld_nt8(b + base + k * here(t.kstride));
+      d[3 * V / 4 + 2 * k + 0] = __uint_as_float(w.x);
+      d[3 * V / 4 + 2 * k + 1] = __uint_as_float(w.y);
+    }
+    return;
+  }
+  if (FAST || t.vec) {  // whole tile, element-aligned only
+#pragma unroll
+    for (int k = 0; k < V / kV; ++k) {
+      const GAS uint8_t* q = b + base + k * here(t.kstride);
+#pragma unroll
+      for (int j = 0; j < kV / 4; ++j)
+        d[3 * V / 4 + k * (kV / 4) + j] =
+            __uint_as_float((uint32_t)q[4 * j] | ((uint32_t)q[4 * j + 1] << 8) |
+                            ((uint32_t)q[4 * j + 2] << 16) | ((uint32_t)q[4 * j + 3] << 24));
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < V / 4; ++j) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * j + i;
+      const int64_t ix = (t.valid && e < t.cnt) ? base + e : 0;
+      w |= (uint32_t)b[ix] << (8 * i);
+    }
+    d[3 * V / 4 + j] = __uint_as_float(w);
+  }
+}
+template <int V>
+__device__ __forceinline__ void expand_raw_bf16(float (&d)[V]) {
+#pragma unroll
+  for (int j = 0; j < V / 2; ++j) {
+    const uint32_t w = __float_as_uint(d[V / 2 + j]);
+    d[2 * j] = bf16_lo(w);
+    d[2 * j + 1] = bf16_hi(w);
+  }
+}
+template <int V>
+__device__ __forceinline__ void expand_raw_u8(float (&d)[V]) {
+#pragma unroll
+  for (int j = 0; j < V / 4; ++j) {
+    const uint32_t w = __float_as_uint(d[3 * V / 4 + j]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[4 * j + i] = (float)((w >> (8 * i)) & 0xFFu);
+  }
 }
 
 // Addressed loads.  Element j of a tile sits at row t.row, column
@@ -394,14 +556,16 @@ __device__ __forceinline__ void load_u8(float (&d)[V], const ExecArgs& a, int sl
     if ((FAST || t.vec) && slot_vec(t, slot)) {
       const GAS uint8_t* p = b + base;
 #pragma unroll
-      for (int k = 0; k < V / kV; ++k) expand_u8(d + k * kV, *(const GAS u2*)(p + k * t.kstride));
+      for (int k = 0; k < V / kV; ++k)
+        expand_u8(d + k * kV, MODE == M_ELEM ? ld_nt8(p + k * here(t.kstride))
+                                             : *(const GAS u2*)(p + k * here(t.kstride)));
       return;
     }
     if (FAST || t.vec) {  // whole tile, element-aligned only
 #pragma unroll
       for (int k = 0; k < V / kV; ++k)
 #pragma unroll
-        for (int i = 0; i < kV; ++i) d[k * kV + i] = (float)b[base + k * t.kstride + i];
+        for (int i = 0; i < kV; ++i) d[k * kV + i] = (float)b[base + k * here(t.kstride) + i];
       return;
     }
 #pragma unroll
@@ -426,8 +590,8 @@ __device__ __forceinline__ void store_f32(const float (&s)[V], const ExecArgs& a
       for (int k = 0; k < V / kV; ++k) {
         const f4 x = {s[k * kV], s[k * kV + 1], s[k * kV + 2], s[k * kV + 3]};
         const f4 y = {s[k * kV + 4], s[k * kV + 5], s[k * kV + 6], s[k * kV + 7]};
-        *(GAS f4*)(p + k * t.kstride) = x;
-        *(GAS f4*)(p + k * t.kstride + 4) = y;
+        *(GAS f4*)(p + k * here(t.kstride)) = x;
+        *(GAS f4*)(p + k * here(t.kstride) + 4) = y;
       }
       return;
     }
@@ -436,7 +600,7 @@ __device__ __forceinline__ void store_f32(const float (&s)[V], const ExecArgs& a
 #pragma unroll
       for (int k = 0; k < V / kV; ++k)
 #pragma unroll
-        for (int i = 0; i < kV; ++i) p[k * t.kstride + i] = s[k * kV + i];
+        for (int i = 0; i < kV; ++i) p[k * here(t.kstride) + i] = s[k * kV + i];
       return;
     }
 #pragma unroll
@@ -460,7 +624,7 @@ __device__ __forceinline__ void store_bf16(const float (&s)[V], const ExecArgs& 
       for (int k = 0; k < V / kV; ++k) {
         const u4 w = {pack2_bf16(s[k * kV], s[k * kV + 1]), pack2_bf16(s[k * kV + 2], s[k * kV + 3]),
                       pack2_bf16(s[k * kV + 4], s[k * kV + 5]), pack2_bf16(s[k * kV + 6], s[k * kV + 7])};
-        *(GAS u4*)(p + k * t.kstride) = w;
+        *(GAS u4*)(p + k * here(t.kstride)) = w;
       }
       return;
     }
@@ -469,7 +633,7 @@ __device__ __forceinline__ void store_bf16(const float (&s)[V], const ExecArgs& 
 #pragma unroll
       for (int k = 0; k < V / kV; ++k)
 #pragma unroll
-        for (int i = 0; i < kV; ++i) p[k * t.kstride + i] = (uint16_t)(pack_bf16(s[k * kV + i], 0.f) & 0xFFFFu);
+        for (int i = 0; i < kV; ++i) p[k * here(t.kstride) + i] = (uint16_t)(pack_bf16(s[k * kV + i], 0.f) & 0xFFFFu);
       return;
     }
 #pragma unroll
@@ -653,6 +817,17 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
       case F_LD_F32_B: load_f32<V, MODE, FAST>(B, a, arg, t); break;
       case F_LD_BF16_B: load_bf16<V, MODE, FAST>(B, a, arg, t); break;
       case F_LD_U8_B: load_u8<V, MODE, FAST>(B, a, arg, t); break;
+      // split loads exist only in the element phase of the instances
+      // without spill slots (in the others the registers they keep busy
+      // across the dispatch loop would spill)
+      case F_LDR_BF16_A: if constexpr (MODE == M_ELEM && NS == 0) load_raw_bf16<V, FAST>(A, arg, t); break;
+      case F_LDR_U8_A: if constexpr (MODE == M_ELEM && NS == 0) load_raw_u8<V, FAST>(A, arg, t); break;
+      case F_LDR_BF16_B: if constexpr (MODE == M_ELEM && NS == 0) load_raw_bf16<V, FAST>(B, arg, t); break;
+      case F_LDR_U8_B: if constexpr (MODE == M_ELEM && NS == 0) load_raw_u8<V, FAST>(B, arg, t); break;
+      case F_XP_BF16_A: if constexpr (MODE == M_ELEM && NS == 0) expand_raw_bf16<V>(A); break;
+      case F_XP_U8_A: if constexpr (MODE == M_ELEM && NS == 0) expand_raw_u8<V>(A); break;
+      case F_XP_BF16_B: if constexpr (MODE == M_ELEM && NS == 0) expand_raw_bf16<V>(B); break;
+      case F_XP_U8_B: if constexpr (MODE == M_ELEM && NS == 0) expand_raw_u8<V>(B); break;
       // addressed loads exist only for one sub-tile at a time (a program
       // holding one runs with slow_only set, never on the whole-run path)
       case F_LDG_F32_A:
@@ -754,10 +929,14 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
           float m = -INFINITY;
 #pragma unroll
           for (int i = 0; i < V; ++i) m = fmaxf(m, (FAST || (t.valid && i < t.cnt)) ? A[i] : -INFINITY);
+          // an element at -inf adds exp(-inf) = 0; a tile of only -inf has
+          // m = -inf too, where A[i] - m would be a NaN: it is taken
+          // against 0 instead (one select per tile) and adds 0
+          const float ms = m == -INFINITY ? 0.f : m;
           float s = 0.f;
 #pragma unroll
           for (int i = 0; i < V; ++i)
-            s += (FAST || (t.valid && i < t.cnt)) ? exp_nonpos(A[i] - m) : 0.f;
+            s += (FAST || (t.valid && i < t.cnt)) ? exp_nonpos(A[i] - ms) : 0.f;
           acc = merge_se(acc, RowAcc{m, s, 0.f});
         }
         break;
@@ -835,7 +1014,7 @@ __device__ __forceinline__ RowAcc pair_step(RowAcc v, RowAcc p, bool lower) {
 }
 template <int KIND>
 __device__ __forceinline__ RowAcc segment_pair(RowAcc v, int width) {
-  const int lane = threadIdx.x & 63;
+  const int lane = here_lane(threadIdx.x & 63);
   auto dpp = [&](int ctrl) {
     return RowAcc{dpp_partner(v.a, ctrl), dpp_partner(v.b, ctrl), dpp_partner(v.c, ctrl)};
   };
@@ -889,23 +1068,30 @@ __device__ __forceinline__ void store_reduced(const ExecArgs& a, const StageDesc
 // with a row program (and barriers) between stages.
 template <int K, int NS, bool TR>
 __global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(NS == 0 ? 4 : 3)))
-exec_kernel(const ExecArgs a) {
+exec_kernel(const ExecArgs a_in) {
+  // The arguments are read through a pointer the compiler takes as new at
+  // every item (here()): the header fields and what is derived from them are
+  // then loaded from the scalar cache where they are used, not held in
+  // SGPRs across the whole kernel (and spilled).
+  typedef const ExecArgs CAS KArgs;
+  KArgs* const ka = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();  // a_in is the first argument
   extern __shared__ float lds[];
-  float* lds_col = lds;
-  float* lds_row = lds + a.n_col_slots * a.PW;
-  float* lds_red = lds_row + a.n_row_slots * a.RB;
-  const int tid = threadIdx.x;
-  const int tpr = 1 << a.tpr_log2;
-  const int rpp = kBlock >> a.tpr_log2;
-  const int sub = tid >> a.tpr_log2;
-  const int lt = tid & (tpr - 1);
-  const Instr* col_prog = a.prog;
-  const int64_t erow_stride = a.R == 1 ? 0 : a.C;
-  const int ks = tpr * kV;  // elements between a lane's sub-tiles
   bool staged = false;
   RowAcc dummy{0.f, 0.f, 0.f};
 
-  for (int64_t item = blockIdx.x; item < a.n_items; item += gridDim.x) {
+  for (int64_t item = blockIdx.x; item < a_in.n_items; item += gridDim.x) {
+    const ExecArgs& a = *(const ExecArgs*)(KArgs*)here((uint64_t)ka);
+    float* lds_col = lds;
+    float* lds_row = lds + a.n_col_slots * a.PW;
+    float* lds_red = lds_row + a.n_row_slots * a.RB;
+    const int tid = threadIdx.x;
+    const int tpr = 1 << a.tpr_log2;
+    const int rpp = kBlock >> a.tpr_log2;
+    const int sub = tid >> a.tpr_log2;
+    const int lt = tid & (tpr - 1);
+    const Instr* col_prog = a.prog;
+    const int64_t erow_stride = a.R == 1 ? 0 : a.C;
+    const int ks = tpr * kV;  // elements between a lane's sub-tiles
     int64_t rb, r0, c0;
     int p, nr, nc;
     SlotPtr* ptrs = (SlotPtr*)a.ptr;
@@ -1024,7 +1210,7 @@ exec_kernel(const ExecArgs a) {
       // reduce tail after the last run of a row, then advance (pass, s)
       auto finish = [&](int rr) {
         if (S.red && s == spl - 1) {
-          const int w = min(tpr, 64);
+          const int w = here(min(tpr, 64));
           RowAcc r = acc;
           const bool paired = !TR && S.red >= 4;  // the staged-transpose instance runs no reductions
           if (paired && S.red == 4) r = segment_pair<4>(acc, w);
@@ -1148,10 +1334,11 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // 16 bytes from a 4-byte aligned address: the run's source side (the
 // destination side is the one the head aligns to 16 bytes).
+// Nontemporal: every byte is read once (see ld_nt16).
+typedef unsigned int u4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 __device__ __forceinline__ uint4 load16(const void* p) {
-  uint4 w;
-  __builtin_memcpy(&w, p, 16);
-  return w;
+  const u4_a4 v = __builtin_nontemporal_load((const GAS u4_a4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 template <typename T>
@@ -1217,6 +1404,60 @@ __global__ void __launch_bounds__(kBlock) copy_kernel(uint4* __restrict__ dst,
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u)
     if (i + u * kBlock < n16) dst[i + u * kBlock] = src[i + u * kBlock];
+}
+
+// Streaming-ceiling probes: the same 16-byte traffic as copy_kernel with
+// the knobs that decide how close a kernel gets to peak HBM bandwidth --
+// U loads in flight per thread, nontemporal (streaming) or ordinary
+// accesses, and the grid (a grid-stride loop over a resident grid, or one
+// workgroup per span of kBlock * U words).  KIND 0 copies, 1 only reads
+// (each workgroup stores one word of XORed data so the loads stay live),
+// 2 only writes.
+template <int KIND, int U, bool NT>
+__global__ void __launch_bounds__(kBlock) stream_kernel(uint4* __restrict__ dst,
+                                                        const uint4* __restrict__ src, size_t n16) {
+  const size_t span = (size_t)kBlock * U;
+  const size_t step = (size_t)gridDim.x * span;
+  size_t i = (size_t)blockIdx.x * span + threadIdx.x;
+  v4u acc = {0u, 0u, 0u, 0u};
+  const v4u fillv = {(unsigned)i, 1u, 2u, 3u};
+  for (; i + (U - 1) * kBlock < n16; i += step) {
+    v4u v[U];
+    if (KIND != 2) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = NT ? __builtin_nontemporal_load((const v4u*)(src + i + u * kBlock))
+                  : *(const v4u*)(src + i + u * kBlock);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (KIND == 1) {
+        acc ^= v[u];
+      } else {
+        const v4u w = KIND == 2 ? fillv : v[u];
+        if (NT) __builtin_nontemporal_store(w, (v4u*)(dst + i + u * kBlock));
+        else *(v4u*)(dst + i + u * kBlock) = w;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (i + u * kBlock < n16) {
+      if (KIND == 0) dst[i + u * kBlock] = src[i + u * kBlock];
+      else if (KIND == 1) acc ^= *(const v4u*)(src + i + u * kBlock);
+      else *(v4u*)(dst + i + u * kBlock) = fillv;
+    }
+  }
+  if (KIND == 1) {
+    // one word per workgroup: the XOR of the lanes' accumulators
+    for (int m = 1; m < 64; m <<= 1) {
+      acc.x ^= (unsigned)__shfl_xor((int)acc.x, m);
+      acc.y ^= (unsigned)__shfl_xor((int)acc.y, m);
+      acc.z ^= (unsigned)__shfl_xor((int)acc.z, m);
+      acc.w ^= (unsigned)__shfl_xor((int)acc.w, m);
+    }
+    if (threadIdx.x == 0) *(v4u*)(dst + blockIdx.x) = acc;
+  }
 }
 
 // ================================================================ host side
@@ -1384,6 +1625,40 @@ int upload_chunks(BucketPlan& b, void* ws, hipStream_t stream) {
     if (e != hipSuccess) return hip_fail(e, "chunk table upload");
   }
   b.workspace = ws;
+  return GTF_OK;
+}
+
+namespace {
+typedef void (*StreamFn)(uint4*, const uint4*, size_t);
+template <int KIND>
+StreamFn stream_instance(int depth, bool nt) {
+  switch (depth) {
+    case 4: return nt ? stream_kernel<KIND, 4, true> : stream_kernel<KIND, 4, false>;
+    case 8: return nt ? stream_kernel<KIND, 8, true> : stream_kernel<KIND, 8, false>;
+    case 16: return nt ? stream_kernel<KIND, 16, true> : stream_kernel<KIND, 16, false>;
+    default: return nullptr;
+  }
+}
+}  // namespace
+
+int launch_stream_probe(int kind, int depth, int nontemporal, int grid_per_cu, void* dst,
+                        const void* src, size_t nbytes, hipStream_t stream) {
+  StreamFn fn = kind == 0   ? stream_instance<0>(depth, nontemporal != 0)
+                : kind == 1 ? stream_instance<1>(depth, nontemporal != 0)
+                : kind == 2 ? stream_instance<2>(depth, nontemporal != 0)
+                            : nullptr;
+  if (fn == nullptr) return fail(GTF_E_INVALID, "stream probe: kind 0..2 and depth 4, 8 or 16");
+  if (grid_per_cu < 0) return fail(GTF_E_INVALID, "stream probe: grid_per_cu < 0");
+  const size_t n16 = nbytes / 16;
+  if (n16 == 0) return GTF_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  size_t grid = (n16 + (size_t)kBlock * depth - 1) / ((size_t)kBlock * depth);
+  if (grid_per_cu > 0) grid = std::min(grid, (size_t)device_cus(dev) * (size_t)grid_per_cu);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kBlock), 0, stream, (uint4*)dst, (const uint4*)src, n16);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "stream_kernel launch");
   return GTF_OK;
 }
 

@@ -416,6 +416,8 @@ int bucket_unpack(const gtf_bucket_plan* plan, const void* const* buckets, void*
  * single-launch path is measured against. */
 int bucket_pack_per_tensor(const gtf_bucket_plan* plan, const void* const* src,
                            void* const* buckets, float scale, void* hip_stream);
+int bucket_unpack_per_tensor(const gtf_bucket_plan* plan, const void* const* buckets,
+                             void* const* dst, float scale, void* hip_stream);
 
 /* Joint op and tensor fusion (DisCo: op fusion and tensor fusion decided
  * together; the fused tensor is the concatenation of its members).  *out =
@@ -438,6 +440,22 @@ void bucket_plan_destroy(gtf_bucket_plan* plan);
  * the achievable-bandwidth ceiling and the reference for scaling hardware
  * byte counters.  Both pointers 16-byte aligned; nbytes a multiple of 16. */
 int gtf_device_copy(void* dst, const void* src, size_t nbytes, void* hip_stream);
+
+/* Streaming-ceiling probes: nbytes of 16-byte words moved with the knobs
+ * that decide how close a streaming kernel comes to peak HBM bandwidth.
+ *   kind         0 copy src -> dst, 1 read src only (each workgroup stores
+ *                one 16-byte XOR of what it read at dst + 16 * workgroup),
+ *                2 write dst only (src unused, may be NULL)
+ *   depth        16-byte loads (or stores) in flight per thread: 4, 8, 16
+ *   nontemporal  1: streaming (nontemporal) loads and stores
+ *   grid_per_cu  0: one workgroup of 256 threads per 256 * depth words;
+ *                k > 0: at most k workgroups per compute unit, each looping
+ *                over the words with a grid stride
+ * dst (and src) 16-byte aligned and nbytes bytes long (the read probe writes
+ * at most that much); nbytes a multiple of 16.  Asynchronous on the stream.
+ * Errors: GTF_E_INVALID (NULL, misaligned, bad kind or depth), GTF_E_HIP. */
+int gtf_stream_probe(int32_t kind, int32_t depth, int32_t nontemporal, int32_t grid_per_cu,
+                     void* dst, const void* src, size_t nbytes, void* hip_stream);
 
 /* Message for the last non-OK status on this thread (never NULL). */
 const char* gtf_last_error(void);

@@ -35,27 +35,21 @@ pattern; path nodes are judged by their own pattern; a node whose output
 is a graph output has no post-dominator.
 
 Injective ops that move elements (transpose, reshape, concat; kInjective
-in the page's table) fuse by the same phases, within what the executor
-runs: such an op reads its inputs from memory, as an addressed load, so a
-merge that would put one after a producer of its input, or next to another
-reader of that input, is not made (gathers_ok), like a merge over the
-argument limit.
+in the page's table) fuse by the same phases.
 
 Row-resident extension (opt-in, row_resident=True; beyond the page, whose
 fusion rules keep a reduction as the last op of its group): after the
 three phases, a group holding a row reduction r is merged with the group of
-an op c that reads r's result, scanning r then c in ascending order and
-starting over after every merge, when
+an op c (not opaque) that reads r's result, scanning r then c in ascending
+order and starting over after every merge, when
   * the merge is convex: no op outside the two groups lies on a path from
-    one to the other;
-  * the merged set keeps the op and argument limits;
-  * it is row-resident feasible: every tensor it touches broadcasts to one
-    [R,C] domain, every reduction reads that domain, its stages (an op runs
-    in the stage of its latest input; a reduction's result is readable one
-    stage later) number at most MAX_STAGES with at most one reduction each,
-    column ops ([1,C] results) run in stage 0, a reduction result read in
-    the group is a [R,1] column of a C > 1 domain, and row / column ops read
-    only their own class (column ops may also read a [1,1] input).
+    one to the other (the group graph stays acyclic);
+  * the merged set keeps the op and argument limits.
+
+What runs a group may hold less than these rules allow (one kernel launch
+has finite registers, LDS and stages).  `feasible(graph, members)`, when
+given, is one more condition on every merge of the phases and of the
+row-resident pass; the oracle's own rules are those above and no more.
 
 Duplicate fusion (opt-in, duplicate(); DisCo, "Background and Motivation"
 on the two fusion approaches for a predecessor with several successors,
@@ -87,14 +81,12 @@ from .evaluate import norm_shape
 K_ELEMWISE, K_BROADCAST, K_INJECTIVE, K_COMM_REDUCE = 0, 1, 2, 3
 K_OUT_EWISE_FUSABLE, K_TUPLE, K_OPAQUE = 4, 7, 8
 
-# injective ops that move elements to other positions: the executor runs
-# one only on a value read from memory (its input comes from outside its
-# group), as an addressed load
-GATHERS = ("transpose", "reshape", "concat")
+# injective ops that move elements to other positions (the page's table
+# makes transpose, reshape and concatenate injective)
+MOVES = ("transpose", "reshape", "concat")
 
 MAX_FUSED_OPS = 256
 MAX_GROUP_ARGS = 16
-MAX_STAGES = 4
 _REDUCES = ("row_sum", "row_mean", "row_max")
 
 
@@ -104,7 +96,7 @@ def pattern(graph, i: int) -> int:
         return K_OPAQUE
     if o.op in _REDUCES:
         return K_COMM_REDUCE
-    if o.op in ("copy",) + GATHERS:
+    if o.op in ("copy",) + MOVES:
         return K_INJECTIVE
     out = norm_shape(graph.tensors[o.output].shape)
     if any(norm_shape(graph.tensors[t].shape) != out for t in o.inputs):
@@ -215,79 +207,6 @@ def _group_args(graph, members: Set[int]) -> int:
     return len(ext)
 
 
-def gathers_ok(graph, members: Set[int]) -> bool:
-    """A transpose, reshape or concat runs inside a group only as a load:
-    its inputs come from memory (not made in the group) and no other op of
-    the group reads them."""
-    produced = {graph.ops[i].output for i in members}
-    for i in members:
-        o = graph.ops[i]
-        if o.op not in GATHERS:
-            continue
-        for t in o.inputs:
-            if t in produced:
-                return False
-            if any(t in graph.ops[j].inputs for j in members if j != i):
-                return False
-    return True
-
-
-def _row_resident_ok(graph, members: Set[int]) -> bool:
-    ms = sorted(members)
-    touched = set()
-    for i in ms:
-        touched.update(graph.ops[i].inputs)
-        touched.add(graph.ops[i].output)
-    shape = {t: norm_shape(graph.tensors[t].shape) for t in touched}
-    reds = [i for i in ms if graph.ops[i].op in _REDUCES]
-    if not reds:
-        return False
-    R, C = shape[graph.ops[reds[0]].inputs[0]]
-    for t in touched:
-        r, c = shape[t]
-        if r not in (1, R) or c not in (1, C):
-            return False
-    if any(shape[graph.ops[i].inputs[0]] != (R, C) for i in reds):
-        return False
-
-    def cls(t):
-        r, c = shape[t]
-        if (r, c) == (R, C):
-            return "E"
-        if r == 1 and c == C:
-            return "COL"
-        return "ROW"
-    produced = {graph.ops[i].output: i for i in ms}
-    avail, stage = {}, {}
-    for i in ms:
-        o = graph.ops[i]
-        st = max([avail[t] for t in o.inputs if t in produced], default=0)
-        stage[i] = st
-        avail[o.output] = st + 1 if o.op in _REDUCES else st
-    n_stages = max(stage.values()) + 1
-    if n_stages > MAX_STAGES:
-        return False
-    per_stage = [stage[i] for i in reds]
-    if len(per_stage) != len(set(per_stage)):
-        return False
-    for i in ms:
-        o = graph.ops[i]
-        c = "E" if o.op in _REDUCES else cls(o.output)
-        if c == "COL" and stage[i] > 0:
-            return False
-        if c != "E":
-            for t in o.inputs:
-                if cls(t) == c:
-                    continue
-                if c == "COL" and t not in produced and shape[t] == (1, 1):
-                    continue
-                return False
-        for t in o.inputs:
-            if t in produced and graph.ops[produced[t]].op in _REDUCES and cls(t) != "ROW":
-                return False
-    return True
-
-
 def _convex(succ, members: Set[int]) -> bool:
     """No path leaves the set and comes back into it."""
     outside = {s for v in members for s in succ[v] if s not in members}
@@ -304,9 +223,11 @@ def _convex(succ, members: Set[int]) -> bool:
     return True
 
 
-def partition(graph, fuse: bool = True, row_resident: bool = False) -> List[List[int]]:
+def partition(graph, fuse: bool = True, row_resident: bool = False,
+              feasible=None) -> List[List[int]]:
     """Groups of op indices, each sorted, listed in an order that respects
-    the dependencies between groups."""
+    the dependencies between groups.  feasible(graph, members), when given,
+    must also hold for every merge (module docstring)."""
     n = len(graph.ops)
     pats = [pattern(graph, i) for i in range(n)]
     uf = _UnionFind(n, pats)
@@ -341,7 +262,7 @@ def partition(graph, fuse: bool = True, row_resident: bool = False) -> List[List
                     continue
                 if _group_args(graph, members) > MAX_GROUP_ARGS:
                     continue
-                if not gathers_ok(graph, members):
+                if feasible is not None and not feasible(graph, members):
                     continue
                 for v in mid | {i}:
                     uf.union_into(v, d)
@@ -364,9 +285,7 @@ def partition(graph, fuse: bool = True, row_resident: bool = False) -> List[List
                             continue
                         if len(members) > MAX_FUSED_OPS or _group_args(graph, members) > MAX_GROUP_ARGS:
                             continue
-                        if not gathers_ok(graph, members):
-                            continue
-                        if not _row_resident_ok(graph, members):
+                        if feasible is not None and not feasible(graph, members):
                             continue
                         uf.union_into(r, c)
                         changed = True
@@ -477,14 +396,15 @@ def _duplicate_op(graph, origin: List[int], p: int, targets: List[int]):
     return Graph(tensors, ops), org, copies
 
 
-def duplicate(graph, row_resident: bool = False):
+def duplicate(graph, row_resident: bool = False, feasible=None):
     """Duplicate fusion (module docstring).  Returns (program, origin):
     the rewritten graph, whose tensors extend the input graph's, and for
-    each of its ops the op of the input graph it computes."""
+    each of its ops the op of the input graph it computes.  feasible is
+    passed to every partition made on the way."""
     g, origin = graph, list(range(len(graph.ops)))
     blocked: Set[int] = set()
     while True:
-        groups = partition(g, row_resident=row_resident)
+        groups = partition(g, row_resident=row_resident, feasible=feasible)
         cost = plan_cost(g, groups)
         gof = {i: k for k, grp in enumerate(groups) for i in grp}
         kept = False
@@ -499,7 +419,7 @@ def duplicate(graph, row_resident: bool = False):
             if not targets:
                 continue
             g2, org2, copies = _duplicate_op(g, origin, p, targets)
-            groups2 = partition(g2, row_resident=row_resident)
+            groups2 = partition(g2, row_resident=row_resident, feasible=feasible)
             gof2 = {i: k for k, grp in enumerate(groups2) for i in grp}
             # no value of a copy (this rewrite's or an earlier one's) is
             # stored: every reader of a copy shares the copy's group

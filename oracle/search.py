@@ -35,9 +35,11 @@ text):
   where it is for its other readers.  With a single reader it is the same
   merge as non-duplicate fusion.
 * A move whose result is not a valid plan is not applied (the page's
-  validity check, made per move): the group graph must stay acyclic and
-  every group within the op and argument limits and runnable by the
-  executor (group_ok).
+  validity check, made per move).  Valid (plan_ok): the group graph is
+  acyclic, no opaque op (the page's parameter and control-flow ops, which
+  are never fused) shares a group, and every group keeps TVM's op and
+  argument limits.  What runs the plan may hold less: feasible(graph,
+  members), when the caller gives one, must hold for every group too.
 * Random numbers come from SplitMix64 (Steele, Lea and Flood, "Fast
   splittable pseudorandom number generators", OOPSLA 2014), seeded by the
   caller; below(n) is the next output modulo n.  Draw order: per step,
@@ -56,7 +58,6 @@ import heapq
 from typing import Callable, Dict, List, Set, Tuple
 
 from oracle import partition as pt
-from oracle.evaluate import norm_shape
 
 MASK64 = (1 << 64) - 1
 
@@ -81,113 +82,6 @@ class SplitMix64:
 
 
 # ---------------------------------------------------------------- validity
-def group_ok(graph, members: Set[int]) -> bool:
-    """Whether the executor runs this op set as one launch, from the shapes
-    and the dataflow alone: one broadcast domain [R,C]; reductions over it;
-    a reduction's result read in the group only by later stages, as a
-    per-row value, at most four stages and one reduction each; column ops
-    before any reduction; row and column ops reading their own kind (a
-    column op may also read a [1,1] input); at most 16 tensors in memory,
-    8 per-row and 4 per-column operands held on chip."""
-    ms = sorted(members)
-    if not pt.gathers_ok(graph, members):
-        return False
-    produced = {graph.ops[i].output: i for i in ms}
-    touched = set()
-    for i in ms:
-        if graph.ops[i].op not in pt.GATHERS:   # a gather's input is addressed, not broadcast
-            touched.update(graph.ops[i].inputs)
-        touched.add(graph.ops[i].output)
-    shape = {t: norm_shape(graph.tensors[t].shape) for t in touched}
-    R = C = 1
-    for t in touched:
-        r, c = shape[t]
-        if r != 1:
-            R = r
-        if c != 1:
-            C = c
-    for t in touched:
-        r, c = shape[t]
-        if r not in (1, R) or c not in (1, C):
-            return False
-    reds = [i for i in ms if graph.ops[i].op in pt._REDUCES]
-    if any(shape[graph.ops[i].inputs[0]] != (R, C) for i in reds):
-        return False
-    # a transpose or concat of a full-domain value addresses rows and columns
-    gathers2d = any(graph.ops[i].op in ("transpose", "concat") for i in ms)
-    flat = not reds and not gathers2d and all(shape[t] == (R, C) for t in touched)
-
-    def cls(t):
-        r, c = shape[t]
-        if flat or (r, c) == (R, C):
-            return "E"
-        if r == 1 and c == C:
-            return "COL"
-        return "ROW"
-
-    def op_cls(i):
-        return "E" if graph.ops[i].op in pt._REDUCES else cls(graph.ops[i].output)
-    # tensors in memory: inputs from outside, values needed outside
-    outside = set()
-    for j, o in enumerate(graph.ops):
-        if j not in members:
-            outside.update(t for t in o.inputs if t in produced)
-    ext = {t for i in ms for t in graph.ops[i].inputs if t not in produced}
-    for i in ms:   # a concat of column values stages two slots in the column phase
-        o = graph.ops[i]
-        if o.op == "concat" and cls(o.output) == "ROW":
-            return False
-    ext |= {t for t in produced if graph.tensors[t].role == "out" or t in outside}
-    if len(ext) > pt.MAX_GROUP_ARGS:
-        return False
-    avail: Dict[int, int] = {}
-    stage: Dict[int, int] = {}
-    for i in ms:
-        o = graph.ops[i]
-        st = max([avail[t] for t in o.inputs if t in produced], default=0)
-        if op_cls(i) == "COL" and st > 0:
-            return False
-        stage[i] = st
-        avail[o.output] = st + 1 if o.op in pt._REDUCES else st
-    for r in reds:
-        out = graph.ops[r].output
-        if any(out in graph.ops[i].inputs for i in ms) and cls(out) != "ROW":
-            return False
-    if max(stage.values()) + 1 > pt.MAX_STAGES:
-        return False
-    if len({stage[r] for r in reds}) != len(reds):
-        return False
-    row_lds, col_lds = set(), set()
-    for i in ms:
-        o = graph.ops[i]
-        c = op_cls(i)
-        if o.op in pt.GATHERS:
-            continue
-        for t in o.inputs:
-            if c == "E":
-                if cls(t) == "ROW":
-                    row_lds.add(t)
-                elif cls(t) == "COL":
-                    col_lds.add(t)
-            elif c == "ROW" and t in produced:
-                j = produced[t]
-                if graph.ops[j].op in pt._REDUCES or stage[j] != stage[i]:
-                    row_lds.add(t)
-    if len(row_lds) > 8 or len(col_lds) > 4:
-        return False
-    for i in ms:
-        c = op_cls(i)
-        if c == "E" or graph.ops[i].op in pt.GATHERS:
-            continue
-        for t in graph.ops[i].inputs:
-            if cls(t) == c:
-                continue
-            if c == "COL" and t not in produced and shape[t] == (1, 1):
-                continue
-            return False
-    return True
-
-
 def groups_of(labels: List[int]) -> List[List[int]]:
     by: Dict[int, List[int]] = {}
     for i, lab in enumerate(labels):
@@ -195,12 +89,29 @@ def groups_of(labels: List[int]) -> List[List[int]]:
     return list(by.values())
 
 
-def plan_ok(graph, labels: List[int]) -> bool:
-    """A valid plan: the group graph is acyclic (so every group is convex)
-    and every group is within the limits and runnable (group_ok)."""
+def _args(graph, members: Set[int]) -> int:
+    """Tensors a group touches in memory: inputs made outside it, and its
+    values read outside it or returned by the graph."""
+    produced = {graph.ops[i].output for i in members}
+    ext = {t for i in members for t in graph.ops[i].inputs if t not in produced}
+    for j, o in enumerate(graph.ops):
+        if j not in members:
+            ext.update(t for t in o.inputs if t in produced)
+    ext.update(t for t in produced if graph.tensors[t].role == "out")
+    return len(ext)
+
+
+def plan_ok(graph, labels: List[int], feasible=None) -> bool:
+    """A valid plan (module docstring): the group graph is acyclic (so
+    every group is convex), no opaque op is fused, every group keeps the op
+    and argument limits, and feasible(graph, members) holds when given."""
     groups = groups_of(labels)
     for g in groups:
-        if len(g) > pt.MAX_FUSED_OPS or not group_ok(graph, set(g)):
+        if len(g) > pt.MAX_FUSED_OPS or _args(graph, set(g)) > pt.MAX_GROUP_ARGS:
+            return False
+        if len(g) > 1 and any(pt.pattern(graph, i) == pt.K_OPAQUE for i in g):
+            return False
+        if feasible is not None and not feasible(graph, set(g)):
             return False
     owner = {graph.ops[i].output: labels[i] for i in range(len(graph.ops))}
     succ: Dict[int, Set[int]] = {lab: set() for lab in set(labels)}
@@ -249,7 +160,7 @@ def _with_copy(graph, origin, labels, p: int, v: int):
             labels[:v] + [labels[v]] + labels[v:])
 
 
-def fuse_move(state, rng: SplitMix64, duplicate: bool):
+def fuse_move(state, rng: SplitMix64, duplicate: bool, feasible=None):
     """One application of method (i) (duplicate False) or (ii) (True)."""
     graph, origin, labels = state
     cross = [[p for p in _predecessors(graph, v) if labels[p] != labels[v]]
@@ -264,7 +175,7 @@ def fuse_move(state, rng: SplitMix64, duplicate: bool):
     else:
         lp, lv = labels[p], labels[v]
         cand = (graph, origin, [lv if x == lp else x for x in labels])
-    return cand if plan_ok(cand[0], cand[2]) else state
+    return cand if plan_ok(cand[0], cand[2], feasible) else state
 
 
 def state_key(state):
@@ -278,9 +189,10 @@ def state_key(state):
 
 
 def search(graph, cost: Callable, alpha: float = 1.05, beta: int = 10, max_stall: int = 1000,
-           seed: int = 0, max_steps: int = 0):
+           seed: int = 0, max_steps: int = 0, feasible=None):
     """Returns ((program, origin, labels) of the best plan, stats).  cost is
-    called as cost(program, groups) with groups as lists of op indices."""
+    called as cost(program, groups) with groups as lists of op indices;
+    feasible, when given, bounds every group of every plan (plan_ok)."""
     rng = SplitMix64(seed)
     n = len(graph.ops)
     start = (graph, list(range(n)), list(range(n)))
@@ -297,7 +209,7 @@ def search(graph, cost: Callable, alpha: float = 1.05, beta: int = 10, max_stall
         for dup in (False, True):
             cand = h
             for _ in range(rng.below(beta + 1)):
-                cand = fuse_move(cand, rng, dup)
+                cand = fuse_move(cand, rng, dup, feasible)
             cc = float(cost(cand[0], groups_of(cand[2])))
             evals += 1
             if cc < c_best:

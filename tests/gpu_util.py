@@ -9,6 +9,7 @@ import numpy as np
 import torch
 
 import gradient_tensor_fusion_amd as gtf
+from tests import capacity as cap
 from oracle import evaluate as oev
 from oracle import numerics
 from oracle import partition as opart
@@ -62,7 +63,7 @@ def gpu_run(graph, inputs: Dict[int, np.ndarray], fuse: bool = True, plan=None,
 
 
 def oracle_run(graph, inputs, fuse: bool = True, given=None, row_resident: bool = False):
-    groups = opart.partition(graph, fuse=fuse, row_resident=row_resident)
+    groups = cap.partition(graph, fuse=fuse, row_resident=row_resident)
     stored = opart.stored_tensors(graph, groups)
     return oev.run(graph, inputs, stored=stored, given=given, groups=groups)
 

@@ -11,6 +11,7 @@ import pytest
 
 import gradient_tensor_fusion_amd as gtf
 from gradient_tensor_fusion_amd import _capi as C
+from tests import capacity as cap
 from oracle import bucket as obucket
 from oracle import partition as opart
 from workloads import configs
@@ -43,11 +44,11 @@ def as_sets(groups):
 
 def check_against_oracle(g):
     plan = gtf.FusePlan(g)
-    assert as_sets(plan.groups()) == as_sets(opart.partition(g))
+    assert as_sets(plan.groups()) == as_sets(cap.partition(g))
     pats, ipd = plan.op_info()
     assert pats == [opart.pattern(g, i) for i in range(len(g.ops))]
     assert ipd == opart.immediate_postdominators(g)
-    groups = opart.partition(g)
+    groups = cap.partition(g)
     stored = opart.stored_tensors(g, groups)
     want = {t for t, d in enumerate(g.tensors) if d.role != "tmp"} | stored
     assert set(plan.materialized()) == want
@@ -307,9 +308,9 @@ def test_row_resident_plans_match_the_oracle():
     merged = 0
     for g in graphs:
         plan = gtf.FusePlan(g, row_resident=True)
-        want = opart.partition(g, row_resident=True)
+        want = cap.partition(g, row_resident=True)
         assert as_sets(plan.groups()) == as_sets(want)
-        merged += len(want) < len(opart.partition(g))
+        merged += len(want) < len(cap.partition(g))
         for k in range(plan.num_groups):
             geo = plan.geometry(k)
             n_red = sum(g.ops[i].op in ("row_sum", "row_mean", "row_max") for i in plan.group_ops(k))
@@ -330,14 +331,14 @@ def test_duplicate_plans_match_the_oracle():
     for g in graphs:
         for rr in (False, True):
             plan = gtf.FusePlan(g, row_resident=rr, duplicate=True)
-            g2, origin = opart.duplicate(g, row_resident=rr)
+            g2, origin = opart.duplicate(g, row_resident=rr, feasible=cap.group_ok)
             assert plan.op_origin() == origin
             assert plan.n_ops == len(g2.ops)
-            assert as_sets(plan.groups()) == as_sets(opart.partition(g2, row_resident=rr))
+            assert as_sets(plan.groups()) == as_sets(cap.partition(g2, row_resident=rr))
             changed += g2 is not g
             # internal tensors are never stored: the caller's arrays suffice
             stored = set(plan.materialized())
-            want = {t for t in opart.stored_tensors(g2, opart.partition(g2, row_resident=rr))} | \
+            want = {t for t in opart.stored_tensors(g2, cap.partition(g2, row_resident=rr))} | \
                 set(g.inputs()) | set(g.outputs())
             assert stored == want and max(stored) < len(g.tensors)
     assert changed >= 40
@@ -371,7 +372,7 @@ def test_grouped_plans_agree_with_the_oracle_rule():
     for g in graphs:
         n = len(g.ops)
         tries = [list(rng.integers(0, max(1, n // 2 + 1), size=n)) for _ in range(6)]
-        groups = opart.partition(g)
+        groups = cap.partition(g)
         for _ in range(3):  # merge two of the fusion pass's groups
             if len(groups) >= 2:
                 a, b = rng.choice(len(groups), size=2, replace=False)
@@ -381,7 +382,7 @@ def test_grouped_plans_agree_with_the_oracle_rule():
                         lab[i] = int(a) if k == b else k
                 tries.append(lab)
         for lab in tries:
-            want = osr.plan_ok(g, [int(x) for x in lab])
+            want = osr.plan_ok(g, [int(x) for x in lab], cap.group_ok)
             try:
                 plan = gtf.FusePlan.grouped(g, lab)
                 got = True
@@ -409,7 +410,7 @@ def test_search_matches_the_oracle():
     for k, g in enumerate(graphs):
         for seed in (1, 2):
             plan, st = gtf.search(g, _lib_bytes_cost, seed=seed, max_stall=200)
-            (prog, origin, lab), ost = osr.search(g, osr.bytes_cost, seed=seed, max_stall=200)
+            (prog, origin, lab), ost = osr.search(g, osr.bytes_cost, seed=seed, max_stall=200, feasible=cap.group_ok)
             assert st == ost, (k, seed, st, ost)
             assert plan.op_origin() == origin
             p2 = plan.program()
@@ -473,12 +474,12 @@ def test_gather_plans_match_the_oracle():
     for g in _gather_dags(71, 300):
         for kw in ({}, {"row_resident": True}):
             plan = gtf.FusePlan(g, **kw)
-            want = opart.partition(g, **kw)
+            want = cap.partition(g, **kw)
             assert as_sets(plan.groups()) == as_sets(want), [(o.op, o.inputs, o.output) for o in g.ops]
-            n_fused += any(len(grp) > 1 and any(g.ops[i].op in opart.GATHERS for i in grp) for grp in want)
+            n_fused += any(len(grp) > 1 and any(g.ops[i].op in cap.GATHERS for i in grp) for grp in want)
         plan = gtf.FusePlan(g, duplicate=True)
-        g2, origin = opart.duplicate(g)
-        assert plan.op_origin() == origin and as_sets(plan.groups()) == as_sets(opart.partition(g2))
+        g2, origin = opart.duplicate(g, feasible=cap.group_ok)
+        assert plan.op_origin() == origin and as_sets(plan.groups()) == as_sets(cap.partition(g2))
     assert n_fused >= 30
 
 
@@ -561,3 +562,23 @@ def test_binding_refuses_host_tensors_before_any_launch():
         bp.pack([torch.zeros(10), torch.zeros(20)], [torch.zeros(30)], 0.5)
     with pytest.raises(ValueError, match="1 tensors for a plan of 2"):
         bp.pack([torch.zeros(10)], [torch.zeros(30)], 0.5)
+
+
+def test_binding_refuses_short_pointer_lists_before_any_launch():
+    """A list of tensors shorter than the graph, or fewer tensor sets than a
+    multi-set run was created for, would make the library read past the
+    pointer array: the binding refuses both with ValueError before the
+    library is called."""
+    import torch
+    g = configs.gelu_graph(4, 8)
+    plan = gtf.FusePlan(g)
+    short = [torch.zeros(g.tensors[t].shape, dtype=torch.int16) for t in range(len(g.tensors) - 1)]
+    with pytest.raises(ValueError, match=f"{len(short)} tensors for a graph of {len(g.tensors)}"):
+        plan.run(short)
+    with pytest.raises(ValueError, match="tensors for a graph of"):
+        plan.launcher(0, short)
+    ge = configs.grad_epilogue_graph(16)
+    pe = gtf.FusePlan(ge)
+    multi = gtf.FuseMulti(pe, 0, [16, 16, 16])
+    with pytest.raises(ValueError, match="2 tensor sets for a run of 3"):
+        multi.bind([{}, {}], torch.zeros(16, dtype=torch.uint8))

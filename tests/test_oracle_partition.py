@@ -246,17 +246,16 @@ def test_row_resident_merges():
         assert pt.partition(g, row_resident=True) == merged, name
 
 
-def test_row_resident_stage_limit():
-    """A chain of six reduce-then-broadcast steps cannot be one group: the
-    kernel holds at most four stages, so every merged group has at most four
-    reductions and each stage at most one."""
-    g, _, _ = _rr_graphs()["six_reductions"]
-    groups = pt.partition(g, row_resident=True)
-    assert len(groups) < len(pt.partition(g))
-    for grp in groups:
-        reds = [i for i in grp if g.ops[i].op == "row_mean"]
-        assert len(reds) <= 4
-    assert sorted(i for grp in groups for i in grp) == list(range(len(g.ops)))
+def test_row_resident_merge_keeps_the_group_graph_acyclic():
+    """The row-resident merge's own rules (beyond TVM's limits) are
+    convexity and nothing else: a reduction read through an opaque op and
+    directly stays apart where merging would put the opaque op on a path
+    out of and back into the group."""
+    g, plain, merged = _rr_graphs()["opaque_on_path"]
+    assert pt.partition(g, row_resident=True) == merged
+    for grp in pt.partition(g, row_resident=True):
+        succ = pt.successors(g)
+        assert pt._convex(succ, set(grp))
 
 
 # ---------------------------------------------------------------- duplicate fusion
@@ -457,7 +456,7 @@ def test_transpose_reshape_concat_values():
     assert [pt.pattern(g, i) for i in range(4)] == [pt.K_INJECTIVE] * 4
 
 
-def test_injective_ops_fuse_by_phase_one_and_only_as_loads():
+def test_injective_ops_fuse_by_the_phase_rules():
     # transpose -> exp: an injective source fuses in phase 1 into an
     # elementwise post-dominator
     g = Graph()
@@ -471,13 +470,14 @@ def test_injective_ops_fuse_by_phase_one_and_only_as_loads():
     t = g.op("transpose", [x], "t", "f32", (5, 3))
     g.op("row_sum", [t], "s", "f32", (5, 1), role="out")
     assert as_sets(pt.partition(g)) == [[0], [1]]
-    # exp -> transpose: TVM would fuse the elementwise producer into it; the
-    # executor reads a transpose's input from memory, so it stays apart
+    # exp -> transpose: the elementwise producer fuses into its injective
+    # post-dominator (phase 0's rule); whether one launch can run the
+    # result is the executor's matter, not the pages'
     g = Graph()
     x = g.input("x", "f32", (3, 5))
     e = g.op("exp", [x], "e", "f32", (3, 5))
     g.op("transpose", [e], "y", "f32", (5, 3), role="out")
-    assert as_sets(pt.partition(g)) == [[0], [1]]
+    assert as_sets(pt.partition(g)) == [[0, 1]]
     # concat of two inputs feeding elementwise work: one group
     g = Graph()
     a = g.input("a", "f32", (4, 3))
@@ -485,9 +485,9 @@ def test_injective_ops_fuse_by_phase_one_and_only_as_loads():
     c = g.op("concat", [a, b], "c", "f32", (4, 8))
     g.op("relu", [c], "y", "f32", (4, 8), role="out")
     assert as_sets(pt.partition(g)) == [[0, 1]]
-    # a gathered input also read directly by another op of the would-be group
+    # a transposed input also read directly: one group by the phases
     g = Graph()
     x = g.input("x", "f32", (4, 4))
     t = g.op("transpose", [x], "t", "f32", (4, 4))
     g.op("add", [t, x], "y", "f32", (4, 4), role="out")
-    assert as_sets(pt.partition(g)) == [[0], [1]]
+    assert as_sets(pt.partition(g)) == [[0, 1]]

@@ -43,7 +43,7 @@ def test_plan_ok_accepts_the_fusion_pass_groupings():
             assert sr.plan_ok(g, _labels(groups, len(g.ops))), (kw, groups)
 
 
-def test_plan_ok_rejects_a_cycle_and_a_column_op_after_a_reduction():
+def test_plan_ok_rejects_a_cycle_an_opaque_fusion_and_the_limits():
     # x -> a -> b -> c with {a, c} together and b alone: a path leaves the
     # group and comes back
     g = Graph()
@@ -53,20 +53,27 @@ def test_plan_ok_rejects_a_cycle_and_a_column_op_after_a_reduction():
     g.op("relu", [b], "c", "f32", (4, 8), role="out")
     assert sr.plan_ok(g, [0, 1, 2]) and sr.plan_ok(g, [0, 0, 0])
     assert not sr.plan_ok(g, [0, 1, 0])
-    # a [1,C] op cannot follow a reduction of the same group
+    # an opaque op (the page's parameters and control flow) is never fused
     g = Graph()
     x = g.input("x", "f32", (4, 8))
-    c = g.input("c", "f32", (8,))
+    a = g.op("exp", [x], "a", "f32", (4, 8))
+    g.op("relu", [a], "c", "f32", (4, 8), role="out", opaque=True)
+    assert sr.plan_ok(g, [0, 1]) and not sr.plan_ok(g, [0, 0])
+    # reduce, then broadcast back, in one group: the pages' rules allow it
+    g = Graph()
+    x = g.input("x", "f32", (4, 8))
     s = g.op("row_sum", [x], "s", "f32", (4, 1))
-    y = g.op("mul", [x, s], "y", "f32", (4, 8))
-    g.op("add", [y, c], "z", "f32", (4, 8), role="out")
-    assert sr.plan_ok(g, [0, 0, 0])          # reduce, then broadcast: two stages
-    g2 = Graph()
-    x = g2.input("x", "f32", (4, 8))
-    s = g2.op("row_sum", [x], "s", "f32", (4, 1))
-    m = g2.op("row_mean", [x], "m", "f32", (4, 1))
-    g2.op("add", [s, m], "t", "f32", (4, 1), role="out")
-    assert not sr.plan_ok(g2, [0, 0, 1])     # two reductions in one stage
+    g.op("mul", [x, s], "y", "f32", (4, 8), role="out")
+    assert sr.plan_ok(g, [0, 0])
+    # the argument limit: 17 inputs summed into one group
+    g = Graph()
+    xs = [g.input(f"x{k}", "f32", (4, 8)) for k in range(17)]
+    acc = g.op("add", [xs[0], xs[1]], "a1", "f32", (4, 8))
+    for k in range(2, 17):
+        acc = g.op("add", [acc, xs[k]], f"a{k}", "f32", (4, 8), role="out" if k == 16 else "tmp")
+    n = len(g.ops)
+    assert not sr.plan_ok(g, [0] * n)                  # 17 inputs and the output
+    assert sr.plan_ok(g, [0] * 8 + [1] * (n - 8))      # 10 tensors per group
 
 
 def _set_partitions(items):
