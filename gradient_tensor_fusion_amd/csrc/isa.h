@@ -88,13 +88,6 @@ enum Form : int {
   // fold A into a paired accumulator (element phase): (mean, squared
   // deviations, count), or (max, sum of exp(x - max))
   F_RED_MV, F_RED_SE,
-  // split loads of narrow types (element phase): issue the tile's load of
-  // slot arg into the top of A / B as raw words (bf16: V/2 words from
-  // element V/2 up, u8: V/4 words from 3V/4 up) without waiting for it ...
-  F_LDR_BF16_A, F_LDR_U8_A, F_LDR_BF16_B, F_LDR_U8_B,
-  // ... and widen the raw words in place to V fp32 values, right before the
-  // register's first use: loads issued together stay in flight together
-  F_XP_BF16_A, F_XP_U8_A, F_XP_BF16_B, F_XP_U8_B,
   F_COUNT
 };
 

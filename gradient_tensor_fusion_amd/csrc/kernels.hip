@@ -395,110 +395,6 @@ __device__ __forceinline__ void load_bf16(float (&d)[V], const ExecArgs& a, int 
   d[0] = bf16_g(b + elem_offset<V, MODE>(a, slot, t));
 }
 
-// Split loads (element phase).  The raw words of a bf16 or u8 tile go to
-// the top of the register -- bf16: word j (elements 2j, 2j + 1) at
-// d[V/2 + j]; u8: word j (elements 4j .. 4j + 3) at d[3V/4 + j] -- and the
-// expansion, a separate instruction, widens them in place in ascending
-// order: word j is read before elements 2j, 2j + 1 (4j .. 4j + 3) are
-// written, and no later word sits below those.  Between the two the
-// register holds no value, and the load is in flight while other
-// instructions issue.  Partial tiles read element by element at clamped
-// in-range indices and pack the words the same way.
-template <int V, bool FAST>
-__device__ __forceinline__ void load_raw_bf16(float (&d)[V], int slot, const Tile& t) {
-  const GAS uint16_t* b = (const GAS uint16_t*)t.ptrs[slot];
-  const int64_t base = t.eoff;
-  // the register's old values are dead from here on (the expansion writes
-  // every element): their VGPRs are free for the element-wise paths
-#pragma unroll
-  for (int i = 0; i < V / 2; ++i) asm volatile("" : "=v"(d[i]));
-  if ((FAST || t.vec) && slot_vec(t, slot)) {
-#pragma unroll
-    for (int k = 0; k < V / kV; ++k) {
-      const u4 w = ld_nt16(b + base + k * here(t.kstride));
-      d[V / 2 + 4 * k + 0] = __uint_as_float(w.x);
-      d[V / 2 + 4 * k + 1] = __uint_as_float(w.y);
-      d[V / 2 + 4 * k + 2] = __uint_as_float(w.z);
-      d[V / 2 + 4 * k + 3] = __uint_as_float(w.w);
-    }
-    return;
-  }
-  if (FAST || t.vec) {  // whole tile, element-aligned only
-#pragma unroll
-    for (int k = 0; k < V / kV; ++k) {
-      const GAS uint16_t* q = b + base + k * here(t.kstride);
-#pragma unroll
-      for (int j = 0; j < kV / 2; ++j)
-        d[V / 2 + k * (kV / 2) + j] = __uint_as_float((uint32_t)q[2 * j] | ((uint32_t)q[2 * j + 1] << 16));
-    }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < V / 2; ++j) {
-    const int e0 = 2 * j, e1 = 2 * j + 1;
-    const int64_t i0 = (t.valid && e0 < t.cnt) ? base + e0 : 0;
-    const int64_t i1 = (t.valid && e1 < t.cnt) ? base + e1 : 0;
-    d[V / 2 + j] = __uint_as_float((uint32_t)b[i0] | ((uint32_t)b[i1] << 16));
-  }
-}
-template <int V, bool FAST>
-__device__ __forceinline__ void load_raw_u8(float (&d)[V], int slot, const Tile& t) {
-  const GAS uint8_t* b = (const GAS uint8_t*)t.ptrs[slot];
-  const int64_t base = t.eoff;
-#pragma unroll
-  for (int i = 0; i < 3 * V / 4; ++i) asm volatile("" : "=v"(d[i]));
-  if ((FAST || t.vec) && slot_vec(t, slot)) {
-#pragma unroll
-    for (int k = 0; k < V / kV; ++k) {
-      const u2 w = ld_nt8(b + base + k * here(t.kstride));
-      d[3 * V / 4 + 2 * k + 0] = __uint_as_float(w.x);
-      d[3 * V / 4 + 2 * k + 1] = __uint_as_float(w.y);
-    }
-    return;
-  }
-  if (FAST || t.vec) {  // whole tile, element-aligned only
-#pragma unroll
-    for (int k = 0; k < V / kV; ++k) {
-      const GAS uint8_t* q = b + base + k * here(t.kstride);
-#pragma unroll
-      for (int j = 0; j < kV / 4; ++j)
-        d[3 * V / 4 + k * (kV / 4) + j] =
-            __uint_as_float((uint32_t)q[4 * j] | ((uint32_t)q[4 * j + 1] << 8) |
-                            ((uint32_t)q[4 * j + 2] << 16) | ((uint32_t)q[4 * j + 3] << 24));
-    }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < V / 4; ++j) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * j + i;
-      const int64_t ix = (t.valid && e < t.cnt) ? base + e : 0;
-      w |= (uint32_t)b[ix] << (8 * i);
-    }
-    d[3 * V / 4 + j] = __uint_as_float(w);
-  }
-}
-template <int V>
-__device__ __forceinline__ void expand_raw_bf16(float (&d)[V]) {
-#pragma unroll
-  for (int j = 0; j < V / 2; ++j) {
-    const uint32_t w = __float_as_uint(d[V / 2 + j]);
-    d[2 * j] = bf16_lo(w);
-    d[2 * j + 1] = bf16_hi(w);
-  }
-}
-template <int V>
-__device__ __forceinline__ void expand_raw_u8(float (&d)[V]) {
-#pragma unroll
-  for (int j = 0; j < V / 4; ++j) {
-    const uint32_t w = __float_as_uint(d[3 * V / 4 + j]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d[4 * j + i] = (float)((w >> (8 * i)) & 0xFFu);
-  }
-}
-
 // Addressed loads.  Element j of a tile sits at row t.row, column
 // t.col + (j / kV) * kstride + j % kV; a transposed source is read there at
 // row * rstride + col * cstride, one element per load.  A concat reads
@@ -817,17 +713,6 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
       case F_LD_F32_B: load_f32<V, MODE, FAST>(B, a, arg, t); break;
       case F_LD_BF16_B: load_bf16<V, MODE, FAST>(B, a, arg, t); break;
       case F_LD_U8_B: load_u8<V, MODE, FAST>(B, a, arg, t); break;
-      // split loads exist only in the element phase of the instances
-      // without spill slots (in the others the registers they keep busy
-      // across the dispatch loop would spill)
-      case F_LDR_BF16_A: if constexpr (MODE == M_ELEM && NS == 0) load_raw_bf16<V, FAST>(A, arg, t); break;
-      case F_LDR_U8_A: if constexpr (MODE == M_ELEM && NS == 0) load_raw_u8<V, FAST>(A, arg, t); break;
-      case F_LDR_BF16_B: if constexpr (MODE == M_ELEM && NS == 0) load_raw_bf16<V, FAST>(B, arg, t); break;
-      case F_LDR_U8_B: if constexpr (MODE == M_ELEM && NS == 0) load_raw_u8<V, FAST>(B, arg, t); break;
-      case F_XP_BF16_A: if constexpr (MODE == M_ELEM && NS == 0) expand_raw_bf16<V>(A); break;
-      case F_XP_U8_A: if constexpr (MODE == M_ELEM && NS == 0) expand_raw_u8<V>(A); break;
-      case F_XP_BF16_B: if constexpr (MODE == M_ELEM && NS == 0) expand_raw_bf16<V>(B); break;
-      case F_XP_U8_B: if constexpr (MODE == M_ELEM && NS == 0) expand_raw_u8<V>(B); break;
       // addressed loads exist only for one sub-tile at a time (a program
       // holding one runs with slow_only set, never on the whole-run path)
       case F_LDG_F32_A:

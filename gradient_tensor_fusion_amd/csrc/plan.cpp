@@ -205,9 +205,6 @@ struct Codegen {
   static constexpr int kEmpty = -1000000;
   enum { RA = 0, RB = 1 };       // register ids: 0 = A, 1 = B, 2.. = spill slots
   int reg[2 + kNS];
-  bool raw[2] = {false, false};  // A / B hold a split load's raw words, not yet widened
-  bool split = false;            // narrow loads split into issue and widen (element
-                                 // phase of an instance without spill slots)
   int ns = kNS;                  // spill slots of the kernel instance
   int max_live = 0;
   bool ok = true;
@@ -246,21 +243,8 @@ struct Codegen {
       if (live(r)) ++n;
     max_live = std::max(max_live, n);
   }
-  // widen a split load in A or B (its value is needed now)
-  void widen(int r) {
-    if (r > RB || !raw[r]) return;
-    const bool u8 = p.tensors[reg[r]].dtype == GTF_U8;
-    emit(r == RA ? (u8 ? F_XP_U8_A : F_XP_BF16_A) : (u8 ? F_XP_U8_B : F_XP_BF16_B));
-    raw[r] = false;
-  }
-  // register r (A or B) now holds v (widened)
-  void set(int r, int v) {
-    reg[r] = v;
-    if (r <= RB) raw[r] = false;
-  }
   void move(int from, int to) {
     static const int a2s = F_A2S0, b2s = F_B2S0, s2a = F_S02A, s2b = F_S02B;
-    widen(from);
     int f;
     if (from == RA && to == RB) f = F_A2B;
     else if (from == RB && to == RA) f = F_B2A;
@@ -269,7 +253,7 @@ struct Codegen {
     else if (to == RA) f = s2a + (from - 2);
     else f = s2b + (from - 2);
     emit(f);
-    set(to, reg[from]);
+    reg[to] = reg[from];
   }
   // keep the value in register r alive elsewhere before r is overwritten
   void save(int r) {
@@ -287,33 +271,24 @@ struct Codegen {
     const int base = r == RA ? F_LD_F32_A : F_LD_F32_B;
     switch (p.tensors[t].dtype) {
       case GTF_F32: return base;
-      case GTF_BF16: return split ? (r == RA ? F_LDR_BF16_A : F_LDR_BF16_B) : base + 1;
-      default: return split ? (r == RA ? F_LDR_U8_A : F_LDR_U8_B) : base + 2;
+      case GTF_BF16: return base + 1;
+      default: return base + 2;
     }
-  }
-  // issue the load of external tensor t into r (split when narrow)
-  void load(int t, int r) {
-    emit(load_form(t, r), ext_slot.at(t));
-    set(r, t);
-    raw[r] = split && p.tensors[t].dtype != GTF_F32;
   }
   // make register r (A or B) hold v, without disturbing the other of A/B
   void bring(int v, int r) {
-    if (reg[r] == v) {
-      widen(r);
-      return;
-    }
+    if (reg[r] == v) return;
     save(r);
     const int from = where(v, r);
     if (from >= 0) {
       move(from, r);
     } else if (loadable.count(v)) {
-      load(v, r);
-      widen(r);
+      emit(load_form(v, r), ext_slot.at(v));
+      reg[r] = v;
     } else if (is_x(v)) {
       const bool col = xcls.at(v) == CLS_COL;
       emit(r == RA ? (col ? F_COL_A : F_ROW_A) : (col ? F_COL_B : F_ROW_B), lds_slot.at(v));
-      set(r, v);
+      reg[r] = v;
     } else {
       ok = false;
       why = "internal: operand not available";
@@ -333,12 +308,12 @@ struct Codegen {
     bring(m.in[0], RA);
     consume_a(m.in[0]);
     emit(m.form);
-    set(RA, m.out);
+    reg[RA] = m.out;
   }
   void run_copy(const MOp& m) {
     bring(m.in[0], RA);
     consume_a(m.in[0]);
-    set(RA, m.out);
+    reg[RA] = m.out;
   }
   // an addressed load into A: the source's slot carries the strides that
   // map a domain position to the source element
@@ -355,13 +330,13 @@ struct Codegen {
     else
       emit(bf ? F_LDC_BF16_A : F_LDC_F32_A, ext_slot.at(m.src[0]) | (ext_slot.at(m.src[1]) << 8),
            m.imm);
-    set(RA, m.out);
+    reg[RA] = m.out;
   }
   void run_imm(const MOp& m) {
     bring(m.in[0], RA);
     consume_a(m.in[0]);
     emit(F_ADD_I + m.form, 0, m.imm);
-    set(RA, m.out);
+    reg[RA] = m.out;
   }
   void run_binary(const MOp& m) {
     int a = m.in[0], b = m.in[1];
@@ -379,7 +354,7 @@ struct Codegen {
       int base, arg;
       x_info(x, &base, &arg);
       emit(base + xop_of(m.form, /*x_on_left=*/!xb), arg);
-      set(RA, m.out);
+      reg[RA] = m.out;
       return;
     }
     // both operands are values: A op B, or B (op) A with the reversed form
@@ -398,7 +373,7 @@ struct Codegen {
     uses[b] -= 1;
     save(RA);  // B keeps its value
     emit(swap ? F_ADD + xop_of(m.form, true) : F_ADD + xop_of(m.form, false));
-    set(RA, m.out);
+    reg[RA] = m.out;
   }
   void run_reduce(const MOp& m) {
     bring(m.in[0], RA);
@@ -448,10 +423,6 @@ const char* check_program(const ExecArgs& a, int n_slots) {
         if (phase != 2) return "reduction outside the element phase";
       } else if (f >= F_A2S0 && f <= F_S52B) {
         if ((f - F_A2S0) % kNS >= ns) return "spill slot beyond the instance";
-      } else if (f >= F_LDR_BF16_A && f <= F_LDR_U8_B) {
-        if (phase != 2 || ns != 0 || arg >= n_slots) return "split load out of range";
-      } else if (f >= F_XP_BF16_A && f <= F_XP_U8_B) {
-        if (phase != 2 || ns != 0) return "widening outside the element phase";
       }
     }
     return nullptr;
@@ -922,7 +893,6 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
       Codegen g{p, &code[pi], ph};
       g.init();
       g.ns = ns;
-      g.split = ph == CLS_E && ns == 0;
       for (size_t k = 0; k < slots.size(); ++k) g.ext_slot[slots[k]] = (int)k;
       const auto& L = P.L;
       std::set<int> made_here;
@@ -975,8 +945,11 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
         for (auto& kv : staging) note(kv.first);
         for (auto& m : L)
           for (int k = 0; k < mop_arity(m); ++k) note(m.in[k]);
-        for (size_t i = 0; i < first_use.size() && i < 2; ++i)
-          g.load(first_use[i], i == 0 ? Codegen::RA : Codegen::RB);
+        for (size_t i = 0; i < first_use.size() && i < 2; ++i) {
+          const int r = i == 0 ? Codegen::RA : Codegen::RB;
+          g.emit(g.load_form(first_use[i], r), g.ext_slot.at(first_use[i]));
+          g.reg[r] = first_use[i];
+        }
       }
       for (auto& kv : staging) {
         g.bring(kv.first, Codegen::RA);
