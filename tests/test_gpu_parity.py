@@ -431,29 +431,17 @@ def _all_bf16_but_nan():
 
 def test_gelu_rounded_to_bf16_every_input():
     """A GELU stored only as bf16 takes the short form; over every bf16
-    input it stays within one bf16 ulp of the exact GELU rounded, and off
-    it for very few normal inputs.  Below x = -12 the result nears fp32's
-    subnormal range, where the exponential flushes: there only closeness
-    in absolute terms is asked for."""
+    input (infinities included, NaN patterns aside) it stays within one
+    bf16 ulp of the exact GELU rounded -- the stated bf16 bar -- down the
+    whole negative tail, where the results are bf16 subnormals."""
     g = Graph()
     x = g.input("x", "bf16", (256, 256))
     g.op("gelu", [x], "y", "bf16", (256, 256), role="out")
     ins = {x: _all_bf16_but_nan()}
     _, got = gpu_run(g, ins)
     _, want = oracle_run(g, ins)
-    xs = numerics.bf16_to_f32(ins[x]).ravel()
     gy, wy = got[1].view(np.uint16).ravel(), want[1].view(np.uint16).ravel()
-    keep = xs > -12.0
-    assert_bf16_close(gy[keep], wy[keep], 1)
-    # a subnormal input's half is often a bf16 rounding tie, where any error
-    # at all picks the side; among normal inputs the two roundings differ
-    # for a handful of them
-    normal = keep & (np.abs(xs) >= 2.0 ** -125)
-    assert np.mean(bf16_ulps(gy[normal], wy[normal]) > 0) < 1e-3
-    tail = ~keep & np.isfinite(xs)
-    d = np.abs(numerics.bf16_to_f32(gy[tail]).astype(np.float64) -
-               numerics.bf16_to_f32(wy[tail]).astype(np.float64))
-    assert np.all(d <= 1e-36)
+    assert_bf16_close(gy, wy, 1)
 
 
 def test_gelu_read_again_keeps_full_accuracy():
