@@ -671,6 +671,31 @@ def run_ceiling(torch, gtf, args, res):
                     table.append(row)
                     if kname not in best or gbs > best[kname]["gbs"]:
                         best[kname] = row
+    # launches the size of one fused group, back to back (the gap between
+    # dependent launches and each launch's ramp count, as they do for the
+    # groups), rotating through >= 1 GiB of buffers
+    small = []
+    for kname, kind in (("copy", 0), ("read", 1)):
+        bc = best[kname]
+        for size in (16 << 20, 32 << 20, 64 << 20, 128 << 20, 256 << 20):
+            k = max(1, (1 << 30) // size)
+            views = [(dst[i * size:(i + 1) * size], src[i * size:(i + 1) * size]) for i in range(k)]
+            calls = [lambda d=d, s_=s_: gtf.stream_probe(kind, bc["depth"], bc["nontemporal"],
+                                                         bc["grid_per_cu"], d, s_, size)
+                     for d, s_ in views]
+            for f in calls:
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for f in calls:
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / len(calls)
+            moved = (2 if kind == 0 else 1) * size
+            small.append({"kind": kname, "bytes_moved": moved, "us_per_launch": round(us, 2),
+                          "gbs": round(moved / (us * 1e-6) / 1e9, 1)})
     cb = CopyBench(torch, gtf)
     lib_copy, _ = cb.gbs(10)
     del cb
@@ -681,7 +706,8 @@ def run_ceiling(torch, gtf, args, res):
                 "config": {"workload": "ceiling: 1 GiB streamed by copy, read-only and write-only "
                                        "probe kernels over accesses in flight, nontemporal and grid",
                            "bytes_per_step": 2 * nb},
-                "best": best, "library_copy_kernel_gbs": round(lib_copy, 1),
+                "best": best, "back_to_back_launches": small,
+                "library_copy_kernel_gbs": round(lib_copy, 1),
                 "torch_copy_gbs": round(dtod, 1),
                 "frac_of_8tbs": {k: round(v["gbs"] / PEAK_GBS, 4) for k, v in best.items()},
                 "table": table})
