@@ -425,6 +425,12 @@ class BucketPlan:
                                                self._bucket_ptrs(buckets),
                                                float(scale), C.stream_handle(stream)))
 
+    def pack_static(self, srcs, buckets, scale: float = 1.0, stream=None) -> None:
+        """bucket_pack_static: pack with the chunk table in the library's
+        static device array (no workspace, no bind, allocates nothing)."""
+        C.check(C.lib().bucket_pack_static(self._h, self._tensor_ptrs(srcs), self._bucket_ptrs(buckets),
+                                           float(scale), C.stream_handle(stream)))
+
     def unpack_per_tensor(self, buckets, dsts, scale: float = 1.0, stream=None) -> None:
         C.check(C.lib().bucket_unpack_per_tensor(self._h, self._bucket_ptrs(buckets),
                                                  self._tensor_ptrs(dsts),

@@ -45,7 +45,7 @@ EXPORTED = (
     "fuse_multi_destroy",
     "bucket_plan_create", "bucket_plan_query", "bucket_plan_workspace_bytes",
     "bucket_plan_bind", "bucket_pack", "bucket_unpack", "bucket_pack_per_tensor",
-    "bucket_unpack_per_tensor", "bucket_plan_slot_address", "bucket_plan_destroy",
+    "bucket_unpack_per_tensor", "bucket_pack_static", "bucket_plan_slot_address", "bucket_plan_destroy",
     "gtf_device_copy", "gtf_stream_probe", "gtf_last_error",
 )
 
@@ -139,6 +139,7 @@ def lib() -> ctypes.CDLL:
         L.bucket_unpack.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
         L.bucket_pack_per_tensor.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
         L.bucket_unpack_per_tensor.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
+        L.bucket_pack_static.argtypes = [vp, POINTER(vp), POINTER(vp), c_float, vp]
         L.bucket_plan_slot_address.argtypes = [vp, POINTER(vp), c_int32, POINTER(vp)]
         L.bucket_plan_destroy.argtypes = [vp]
         L.bucket_plan_destroy.restype = None

@@ -41,6 +41,8 @@ int launch_group(const CompiledGroup& cg, void* const* tensor_ptrs, hipStream_t 
 int launch_bucket(const BucketPlan& b, const void* const* tens, void* const* bk, float scale,
                   bool unpack, bool per_tensor, hipStream_t stream);
 int upload_chunks(BucketPlan& b, void* ws, hipStream_t stream);
+int launch_bucket_static(const BucketPlan& b, const void* const* tens, void* const* bk, float scale,
+                         hipStream_t stream);
 int launch_copy(void* dst, const void* src, size_t nbytes, hipStream_t stream);
 int launch_stream_probe(int kind, int depth, int nontemporal, int grid_per_cu, void* dst,
                         const void* src, size_t nbytes, hipStream_t stream);
@@ -486,6 +488,15 @@ int bucket_unpack(const gtf_bucket_plan* plan, const void* const* buckets, void*
 int bucket_pack_per_tensor(const gtf_bucket_plan* plan, const void* const* src,
                            void* const* buckets, float scale, void* hip_stream) {
   return bucket_run(plan, src, buckets, scale, false, true, hip_stream);
+}
+
+int bucket_pack_static(const gtf_bucket_plan* plan, const void* const* src, void* const* buckets,
+                       float scale, void* hip_stream) {
+  if (plan == nullptr) return fail(GTF_E_INVALID, "plan is NULL");
+  const BucketPlan& b = plan->b;
+  if (b.numel.empty()) return GTF_OK;
+  if (src == nullptr || buckets == nullptr) return fail(GTF_E_INVALID, "NULL pointer array");
+  return launch_bucket_static(b, src, buckets, scale, (hipStream_t)hip_stream);
 }
 
 int bucket_unpack_per_tensor(const gtf_bucket_plan* plan, const void* const* buckets,

@@ -1495,9 +1495,9 @@ int launch_group(const CompiledGroup& cg, void* const* tensor_ptrs, hipStream_t 
   return launch_exec(a, cg.lds_bytes, stream);
 }
 
-int launch_bucket(const BucketPlan& b, const void* const* tens, void* const* bk, float scale,
-                  bool unpack, bool per_tensor, hipStream_t stream) {
-  const Chunk* table = (const Chunk*)b.workspace;
+namespace {
+int launch_bucket_table(const BucketPlan& b, const Chunk* table, const void* const* tens, void* const* bk,
+                        float scale, bool unpack, bool per_tensor, hipStream_t stream) {
   for (const BucketPlan::Launch& L : b.launches) {
     BucketArgs a;
     a.scale = scale;
@@ -1537,6 +1537,61 @@ int launch_bucket(const BucketPlan& b, const void* const* tens, void* const* bk,
     if (e != hipSuccess) return hip_fail(e, "bucket_kernel launch");
   }
   return GTF_OK;
+}
+}  // namespace
+
+int launch_bucket(const BucketPlan& b, const void* const* tens, void* const* bk, float scale,
+                  bool unpack, bool per_tensor, hipStream_t stream) {
+  return launch_bucket_table(b, (const Chunk*)b.workspace, tens, bk, scale, unpack, per_tensor, stream);
+}
+
+// ---------------------------------------------------------------- allocation-free pack
+// The chunk table of bucket_pack_static lives here, in device memory the
+// library holds for the life of the process on each GPU it runs on, rather
+// than in a workspace the caller allocates.  On the host, `scratch` only
+// names the symbol: its device address is taken once per device with
+// hipGetSymbolAddress (with that device current) and only that address is
+// ever handed to a kernel or a copy.  Every call on one GPU shares the one
+// array, so calls that overlap on a GPU race.
+constexpr size_t kStaticChunkBytes = size_t(1) << 20;  // 43,690 chunks of <= 16384 elements
+static __device__ __align__(256) unsigned char scratch[kStaticChunkBytes];
+
+namespace {
+std::map<int, void*> g_scratch;  // device -> address of its scratch (under g_mu)
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    it = g_scratch.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return GTF_OK;
+}
+}  // namespace
+
+int launch_bucket_static(const BucketPlan& b, const void* const* tens, void* const* bk, float scale,
+                         hipStream_t stream) {
+  const size_t bytes = b.chunks.size() * sizeof(Chunk);
+  if (bytes > kStaticChunkBytes)
+    return fail(GTF_E_LIMIT, "chunk table of " + std::to_string(bytes) + " bytes exceeds the " +
+                                 std::to_string(kStaticChunkBytes) + "-byte static scratch");
+  void* table = nullptr;
+  int st = scratch_address(&table);
+  if (st != GTF_OK) return st;
+  if (bytes > 0) {
+    // a copy, not a memset: the table overwrites what an earlier call left
+    hipError_t e = hipMemcpyAsync(table, b.chunks.data(), bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "chunk table upload to the static scratch");
+  }
+  return launch_bucket_table(b, (const Chunk*)table, tens, bk, scale, false, false, stream);
 }
 
 int upload_chunks(BucketPlan& b, void* ws, hipStream_t stream) {

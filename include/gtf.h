@@ -419,6 +419,21 @@ int bucket_pack_per_tensor(const gtf_bucket_plan* plan, const void* const* src,
 int bucket_unpack_per_tensor(const gtf_bucket_plan* plan, const void* const* buckets,
                              void* const* dst, float scale, void* hip_stream);
 
+/* bucket_pack for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it): the
+ * same pack, with the plan's chunk table copied (hipMemcpyAsync from the
+ * plan's host copy, on the stream) into a 1 MiB array the library holds in
+ * device memory on each GPU it runs on, instead of a workspace from
+ * bucket_plan_bind (which this call neither needs nor touches).  Allocates
+ * nothing.  Every call on one GPU shares that array: calls that overlap on
+ * one GPU race (serialize them, e.g. on one stream).  Arguments, layout and
+ * results as bucket_pack.
+ * Errors: GTF_E_INVALID (NULL plan or pointer arrays, NULL tensor or bucket
+ * pointer of nonzero size), GTF_E_LIMIT (a chunk table over 1 MiB: more
+ * than 43,690 chunks of at most 16384 elements), GTF_E_HIP. */
+int bucket_pack_static(const gtf_bucket_plan* plan, const void* const* src, void* const* buckets,
+                       float scale, void* hip_stream);
+
 /* Joint op and tensor fusion (DisCo: op fusion and tensor fusion decided
  * together; the fused tensor is the concatenation of its members).  *out =
  * the device address of tensor i's place in its bucket, buckets[bucket_of[i]]
