@@ -69,7 +69,7 @@ def result_shape(op: str, in_shapes, declared=None) -> Tuple[int, int]:
 
 def evaluate(graph, inputs: Dict[int, np.ndarray],
              stored: Iterable[int] = (), given: Dict[int, np.ndarray] = None,
-             groups=None) -> Dict[int, np.ndarray]:
+             groups=None, raw_out: Dict[int, np.ndarray] = None) -> Dict[int, np.ndarray]:
     """fp32 value of every tensor as it is in memory (rounded to its dtype
     where it is stored: graph outputs and ``stored`` intermediates), each
     shaped [R, C].
@@ -83,7 +83,10 @@ def evaluate(graph, inputs: Dict[int, np.ndarray],
     fused group every intermediate is fp32 and rounding happens only at the
     store (TVM "FuseTIR": the group is one function whose intermediates
     never go through memory).  Without groups, every reader of a stored
-    value gets the rounded value (each op its own group)."""
+    value gets the rounded value (each op its own group).
+    ``raw_out``, when given, receives each op's fp32 result before any
+    store rounding (what readers in the producer's own group see).
+    """
     stored = set(stored)
     given = {} if given is None else given
     group_of = {}
@@ -117,6 +120,8 @@ def evaluate(graph, inputs: Dict[int, np.ndarray],
         if o.output in stored or d.role == "out":
             r = numerics.round_to(r, d.dtype)
         vals[o.output] = r
+    if raw_out is not None:
+        raw_out.update(raw)
     return vals
 
 

@@ -18,6 +18,7 @@ from oracle import bucket as obucket
 from oracle import evaluate as oev
 from oracle import numerics
 from oracle import partition as opart
+from tests.error_bound import assert_within, run_with_bounds
 from tests.gpu_util import (announce, assert_bf16_close, assert_bits_equal, assert_close_scaled,
                             assert_f32_rel, bf16_ulps,
                             assert_reduce_close, gpu_run, oracle_run, reduce_bound, to_device,
@@ -276,33 +277,32 @@ def _ieee_only(g):
 
 
 def _check_graph(g, ins, modes=((True, False), (False, False))):
-    has_red = any(o.op in ("row_sum", "row_mean", "row_max") for o in g.ops)
+    """The GPU's outputs against the oracle's evaluation under the same
+    grouping, element by element within the bound the stated bars give
+    (tests/error_bound.py): bit-exact wherever only IEEE ops lead to a
+    value, 1e-6 of the value per transcendental, 1e-5 of the terms'
+    magnitudes per reduction, propagated through the graph."""
     for fuse, rr in modes:
         plan, got = gpu_run(g, ins, fuse=fuse, row_resident=rr)
-        vals, want = oracle_run(g, ins, fuse=fuse, row_resident=rr)
-        big = max([float(np.nanmax(np.abs(v))) if v.size else 0.0 for v in vals.values()] + [1.0])
+        groups = cap.partition(g, fuse=fuse, row_resident=rr)
+        assert sorted(map(sorted, plan.groups())) == sorted(map(sorted, groups))
+        vals, bound = run_with_bounds(g, ins, groups)
         for t in g.outputs():
-            d = g.tensors[t]
-            prod = g.ops[g.producer(t)]
-            if prod.op in ("row_sum", "row_mean", "row_max"):
-                scale = reduce_bound(vals[prod.inputs[0]], prod.op == "row_mean")
-                assert_reduce_close(got[t], want[t], scale, 1e-5)
-            elif _ieee_only(g) and not has_red:
-                assert_bits_equal(got[t], want[t])
-            elif d.dtype == "bf16":
-                assert_close_scaled(numerics.bf16_to_f32(got[t]), numerics.bf16_to_f32(want[t]),
-                                    2.0 ** -8, 1e-3 * big)
-            else:
-                assert_close_scaled(got[t], want[t], 1e-5, big)
+            assert_within(got[t], vals[t], bound[t], g.tensors[t].dtype, g.tensors[t].name)
     return plan
 
 
 def _inputs_for(g, seed):
+    """Seeded inputs: values uniform on [-1.5, 1.5) (bf16 rounded where the
+    tensor is bf16), masks keep 0.9."""
     ins = {}
     for k, t in enumerate(g.inputs()):
         d = g.tensors[t]
         x = configs.tensor_values("f32", d.shape, "uniform", seed, k, -1.5, 1.5)
-        ins[t] = configs.to_bf16_bits(x.astype(np.float64)) if d.dtype == "bf16" else x
+        if d.dtype == "u8":
+            ins[t] = (configs.tensor_values("f32", d.shape, "uniform", seed, k, 0.0, 1.0) >= 0.1).astype(np.uint8)
+        else:
+            ins[t] = configs.to_bf16_bits(x.astype(np.float64)) if d.dtype == "bf16" else x
     return ins
 
 
@@ -338,6 +338,50 @@ def test_random_elementwise_dags_fused_equals_unfused():
                     assert_bits_equal(a[t], b[t])
             n += 1
     assert n == 160
+
+
+@pytest.mark.parametrize("shape", [(3, 5), (5, 130)])
+def test_every_dag_of_two_ops_against_the_oracle(shape):
+    """Every DAG of one or two elementwise ops over two f32 inputs and a u8
+    mask, drawn from every opcode (exp, tanh, sigmoid, relu, gelu, square,
+    sqrt, recip, neg, add_imm, mul_imm, add, sub, mul, div, max, min, add3,
+    dmul) wherever its domain holds, fused and unfused: 5,280 DAGs, run as
+    components of one graph per chunk.  Each output within the per-element
+    bound of the stated bars, so bit-exact wherever only IEEE ops lead to
+    it; the fused and the unfused runs then agree bit for bit there too."""
+    from tests import dag_gen
+    dags = dag_gen.exhaustive_small()
+    assert len(dags) == 5280
+    for c0 in range(0, len(dags), 800):
+        g, finals = dag_gen.combine(dags[c0:c0 + 800], shape)
+        ins = _inputs_for(g, 1300 + c0)
+        announce("small dags", shape, c0)
+        res = {}
+        for fuse in (True, False):
+            plan, got = gpu_run(g, ins, fuse=fuse)
+            assert fuse or plan.num_groups == len(g.ops)
+            vals, bound = run_with_bounds(g, ins, plan.groups())
+            for t in g.outputs():
+                assert_within(got[t], vals[t], bound[t], "f32", g.tensors[t].name)
+            res[fuse] = (got, bound)
+        for t in g.outputs():
+            exact = np.asarray(res[True][1][t]) == 0
+            assert_bits_equal(np.where(exact, res[True][0][t], 0), np.where(exact, res[False][0][t], 0))
+
+
+def test_random_dags_over_every_opcode():
+    """Three- and four-op DAGs drawn from every elementwise opcode, at four
+    shapes (one element, a partial tile, several tiles with ragged ends),
+    fused and unfused, within the per-element bound."""
+    from tests import dag_gen
+    n = 0
+    for n_ops, seed in ((3, 41), (4, 42)):
+        for gi, g in enumerate(dag_gen.random_dags(seed, 60, n_ops)):
+            for R, C in SHAPES:
+                gg = _reshape(g, R, C)
+                _check_graph(gg, _inputs_for(gg, 1500 + gi))
+                n += 1
+    assert n == 480
 
 
 def test_random_broadcast_dags():
@@ -930,17 +974,9 @@ def test_random_dags_with_duplicate_fusion():
             assert plan.n_ops == len(gg2.ops)
             _, got = gpu_run(gg, ins, plan=plan)
             groups = cap.partition(gg2)
-            vals, want = oev.run(gg2, ins, stored=opart.stored_tensors(gg2, groups), groups=groups)
-            big = max([float(np.nanmax(np.abs(v))) if v.size else 0.0 for v in vals.values()] + [1.0])
+            vals, bound = run_with_bounds(gg2, ins, groups)
             for t in gg.outputs():
-                prod = gg2.ops[gg2.producer(t)]  # its operand may now be a copy's value
-                if prod.op in ("row_sum", "row_mean", "row_max"):
-                    assert_reduce_close(got[t], want[t], reduce_bound(vals[prod.inputs[0]], False), 1e-5)
-                elif gg.tensors[t].dtype == "bf16":
-                    assert_close_scaled(numerics.bf16_to_f32(got[t]), numerics.bf16_to_f32(want[t]),
-                                        2.0 ** -8, 1e-3 * big)
-                else:
-                    assert_close_scaled(got[t], want[t], 1e-5, big)
+                assert_within(got[t], vals[t], bound[t], gg.tensors[t].dtype, gg.tensors[t].name)
         n += 1
     assert n >= 20
 
@@ -948,22 +984,14 @@ def test_random_dags_with_duplicate_fusion():
 # ---------------------------------------------------------------- explicit groupings and search
 def _check_program(g, plan, ins):
     """The plan's outputs against the oracle's evaluation of the plan's own
-    program with the plan's grouping (stored values rounded as stored)."""
+    program with the plan's grouping (stored values rounded as stored),
+    within the per-element bound of the stated bars."""
     prog = plan.program()
     groups = plan.groups()
     _, got = gpu_run(g, ins, plan=plan)
-    vals, want = oev.run(prog, ins, stored=opart.stored_tensors(prog, groups), groups=groups)
-    big = max([float(np.nanmax(np.abs(v))) if v.size else 0.0 for v in vals.values()] + [1.0])
+    vals, bound = run_with_bounds(prog, ins, groups)
     for t in g.outputs():
-        prod = prog.ops[prog.producer(t)]
-        if prod.op in ("row_sum", "row_mean", "row_max"):
-            assert_reduce_close(got[t], want[t], reduce_bound(vals[prod.inputs[0]], prod.op == "row_mean"),
-                                1e-5)
-        elif g.tensors[t].dtype == "bf16":
-            assert_close_scaled(numerics.bf16_to_f32(got[t]), numerics.bf16_to_f32(want[t]),
-                                2.0 ** -8, 1e-3 * big)
-        else:
-            assert_close_scaled(got[t], want[t], 1e-5, big)
+        assert_within(got[t], vals[t], bound[t], g.tensors[t].dtype, g.tensors[t].name)
 
 
 def test_random_grouped_plans_run_correctly():
