@@ -113,8 +113,29 @@ __device__ __forceinline__ float exp_nonpos_sub(float x) {
   constexpr float kLn2 = 6.93147182e-01f;
   const ExpSplit y = exp_split(x);
   const float h = __builtin_amdgcn_exp2f(y.yh * 0.5f);
-  const float p = h * h;
-  return __builtin_fmaf(p, y.yl * kLn2, p);
+  // h (1 + yl ln 2) is normal, so the one rounding into the subnormal range
+  // is the last product's
+  return __builtin_fmaf(h, y.yl * kLn2, h) * h;
+}
+
+// e^x over the whole range: the split of x log2 e as in exp_nonpos (the
+// error term from x clamped to [-104, 89], one v_med3), 2^yh as the square
+// of 2^(yh / 2) so that results in fp32's subnormal range round gradually
+// and results past its top overflow to +inf, and the correction applied as
+// a factor 1 + yl ln 2 (as an fma against h, h = +inf would meet a negative
+// correction as inf - inf).  About 3 ulp; 9 VALU slots against 13 for the
+// library expf.  -inf gives 0, +inf gives +inf, NaN stays NaN.
+__device__ __forceinline__ float f_exp(float x) {
+  constexpr float kL = 1.44269502e+00f;
+  constexpr float kLlo = 1.92596299e-08f;
+  constexpr float kLn2 = 6.93147182e-01f;
+  const float xc = __builtin_amdgcn_fmed3f(x, -104.0f, 89.0f);
+  const float yc = xc * kL;
+  const float yl = __builtin_fmaf(xc, kLlo, __builtin_fmaf(xc, kL, -yc));
+  const float h = __builtin_amdgcn_exp2f(x * (0.5f * kL));
+  // h (1 + yl ln 2) is normal wherever h is, so the one rounding into the
+  // subnormal range is the last product's
+  return (h * __builtin_fmaf(yl, kLn2, 1.0f)) * h;
 }
 
 __device__ __forceinline__ float f_sigmoid(float x) {
@@ -196,7 +217,11 @@ __device__ __forceinline__ float f_relu(float x) { return x > 0.f ? x : 0.f; }
 // degree 4 fitted here by weighted least squares on Chebyshev nodes (max
 // relative error 7.4e-8 in fp32); otherwise 1 - 2 e / (1 + e) with
 // e = e^{-2|x|} <= 0.29, which has no cancellation there (the result is at
-// least 0.55).
+// least 0.55).  e enters only through 2e / (1 + e), whose absolute error is
+// under 2e times e's relative error; with e = 2^(-2 log2(e) |x|) taken in
+// one rounding of the argument that is e^{-2|x|} |x| 3.5e-7 at most (6e-8
+// at |x| = 0.5), so no split of the argument is needed: under 3e-7
+// relative in all at the branch point, less beyond.
 __device__ __forceinline__ float f_tanh(float x) {
   const float ax = fabsf(x);
   const float u = ax * ax;
@@ -206,8 +231,9 @@ __device__ __forceinline__ float f_tanh(float x) {
   p = __builtin_fmaf(p, u, 1.3331381976604462e-01f);
   p = __builtin_fmaf(p, u, -3.333328068256378e-01f);
   const float small = __builtin_fmaf(ax * u, p, ax);
-  const float e = exp_nonpos(-2.0f * ax);
-  const float big = 1.0f - 2.0f * e * __builtin_amdgcn_rcpf(e + 1.0f);
+  constexpr float kM2L = -2.88539004e+00f;  // -2 log2(e)
+  const float e = __builtin_amdgcn_exp2f(ax * kM2L);
+  const float big = __builtin_fmaf(-2.0f, e * __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
   return copysignf(ax < 0.625f ? small : big, x);
 }
 
@@ -588,7 +614,7 @@ __device__ __forceinline__ void unary(float (&r)[V]) {
   for (int i = 0; i < V; ++i) {
     const float x = r[i];
     float y;
-    if (F == F_EXP) y = expf(x);
+    if (F == F_EXP) y = f_exp(x);
     else if (F == F_TANH) y = f_tanh(x);
     else if (F == F_SIGMOID) y = f_sigmoid(x);
     else if (F == F_RELU) y = f_relu(x);

@@ -256,8 +256,18 @@ struct Codegen {
     reg[to] = reg[from];
   }
   // keep the value in register r alive elsewhere before r is overwritten
-  void save(int r) {
+  // keep register r's value, if it is still needed, somewhere else before r
+  // is overwritten.  to_b: B may take it (not when B holds an operand of
+  // the op about to be emitted, whose remaining reads are already counted
+  // down)
+  void save(int r, bool to_b = true) {
     if (!live(r) || holders(reg[r]) > 1) return;
+    // B holds nothing still needed: keep A's value there (a move within
+    // the two working registers, no spill slot)
+    if (r == RA && to_b && !live(RB)) {
+      move(RA, RB);
+      return;
+    }
     for (int s = 2; s < 2 + ns; ++s)
       if (!live(s)) {
         move(r, s);
@@ -371,7 +381,7 @@ struct Codegen {
     }
     uses[a] -= 1;
     uses[b] -= 1;
-    save(RA);  // B keeps its value
+    save(RA, false);  // B keeps its value: the op reads it
     emit(swap ? F_ADD + xop_of(m.form, true) : F_ADD + xop_of(m.form, false));
     reg[RA] = m.out;
   }
@@ -681,6 +691,47 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
     }
   }
 
+  // ---- sums reduced term by term.  A row sum or mean whose input is an
+  // add or add3 made in the group, read by nothing else and not stored, over
+  // full-domain values, adds each of its terms into the row accumulator
+  // instead: the sum of the terms' sums is the sum (only the order of the
+  // roundings moves, well inside the reduction tolerance), the adds are not
+  // run, and the group holds one value fewer at a time.  Nested adds expand
+  // the same way.
+  std::map<int, std::vector<int>> red_terms;  // reduction op -> the tensors it sums
+  {
+    std::map<int, int> n_read;
+    for (const OpInfo& o : p.ops)
+      for (int k = 0; k < o.n_in; ++k) n_read[o.in[k]] += 1;
+    std::set<int> summed;
+    std::function<void(int, std::vector<int>&, std::vector<int>&)> expand =
+        [&](int t, std::vector<int>& terms, std::vector<int>& adds) {
+          auto it = producer.find(t);
+          bool open = it != producer.end() && !absorbed.count(it->second) &&
+                      (p.ops[it->second].opcode == GTF_OP_ADD || p.ops[it->second].opcode == GTF_OP_ADD3) &&
+                      n_read[t] == 1 && !outputs.count(t) && cls_of(t) == CLS_E;
+          if (open)
+            for (int k = 0; k < p.ops[it->second].n_in; ++k)
+              if (cls_of(p.ops[it->second].in[k]) != CLS_E) open = false;
+          if (!open) {
+            terms.push_back(t);
+            return;
+          }
+          adds.push_back(it->second);
+          for (int k = 0; k < p.ops[it->second].n_in; ++k) expand(p.ops[it->second].in[k], terms, adds);
+        };
+    for (int r : reds) {
+      const OpInfo& o = p.ops[r];
+      if (o.opcode != GTF_OP_ROW_SUM && o.opcode != GTF_OP_ROW_MEAN) continue;
+      if (pair_first.count(r) || pair_second.count(r)) continue;
+      std::vector<int> terms, adds;
+      expand(o.in[0], terms, adds);
+      if (adds.empty()) continue;
+      red_terms[r] = terms;
+      for (int j : adds) summed.insert(j);
+    }
+  }
+
   // ---- lower each op to micro-ops
   std::map<int, std::vector<MOp>> mops_of;
   std::map<int, std::pair<int64_t, int64_t>> gather_stride;  // source tensor -> (rstride, cstride)
@@ -803,7 +854,14 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
       if (pair_second.count(i)) m.form = o.opcode == GTF_OP_ROW_MEAN ? F_RED_MV : F_RED_SE;
       m.in[0] = o.in[0];
       m.out = o.out;
-      L.push_back(m);
+      if (red_terms.count(i)) {
+        for (int t : red_terms.at(i)) {  // one accumulation per term
+          m.in[0] = t;
+          L.push_back(m);
+        }
+      } else {
+        L.push_back(m);
+      }
     } else {
       return bad("unsupported opcode in group");
     }
@@ -852,8 +910,11 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
       work.pop_back();
       if (cone.count(i)) continue;
       cone.insert(i);
-      for (int k = 0; k < p.ops[i].n_in; ++k) {
-        const int t = p.ops[i].in[k];
+      // a reduction summed term by term reads its terms, not the adds
+      const std::vector<int> ins = red_terms.count(i)
+                                       ? red_terms.at(i)
+                                       : std::vector<int>(p.ops[i].in, p.ops[i].in + p.ops[i].n_in);
+      for (int t : ins) {
         if (!produced.count(t)) continue;
         const int j = producer.at(t);
         if (op_cls(j) == CLS_E && !is_reduce(p.ops[j].opcode)) work.push_back(j);
