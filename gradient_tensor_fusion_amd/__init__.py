@@ -174,6 +174,23 @@ class FusePlan:
         C.check(C.lib().fuse_plan_group_geometry(self._h, g, byref(geo)))
         return {name: getattr(geo, name) for name, _ in C.GroupGeometry._fields_}
 
+    def code(self, g: int) -> dict:
+        """fuse_plan_group_code: group g's compiled op program (forms as
+        numbers, stages, slot strides), for host-side checks of the group
+        compiler."""
+        info = C.GroupCode()
+        C.check(C.lib().fuse_plan_group_code(self._h, g, byref(info), None, 0))
+        code = (C.Instr * max(1, info.n_instr))()
+        C.check(C.lib().fuse_plan_group_code(self._h, g, byref(info), code, info.n_instr))
+        stages = [{n: getattr(info.stage[k], n) for n, _ in C.StageCode._fields_}
+                  for k in range(info.n_stages)]
+        return {"n_col": info.n_col, "stages": stages,
+                "instr": [(int(code[i].form), int(code[i].arg), float(code[i].imm))
+                          for i in range(info.n_instr)],
+                "slots": self.group_tensors(g), "transposed_slot": info.transposed_slot,
+                "rstride": list(info.rstride[:info.n_slots]),
+                "cstride": list(info.cstride[:info.n_slots])}
+
     def is_materialized(self, t: int) -> bool:
         y = c_int32()
         C.check(C.lib().fuse_plan_is_materialized(self._h, t, byref(y)))

@@ -39,7 +39,7 @@ EXPORTED = (
     "fuse_plan_create", "fuse_plan_num_groups", "fuse_plan_group_info", "fuse_plan_op_info",
     "fuse_plan_num_ops", "fuse_plan_op_origin", "fuse_plan_group_tensors",
     "fuse_plan_create_grouped", "fuse_plan_search", "fuse_plan_program",
-    "fuse_plan_group_geometry",
+    "fuse_plan_group_geometry", "fuse_plan_group_code",
     "fuse_plan_is_materialized", "fuse_group_run", "fuse_plan_run", "fuse_plan_destroy",
     "fuse_multi_create", "fuse_multi_workspace_bytes", "fuse_multi_bind", "fuse_multi_run",
     "fuse_multi_destroy",
@@ -66,6 +66,26 @@ class GroupGeometry(ctypes.Structure):
                 ("subtiles", c_int32), ("lds_bytes", c_int32), ("program_length", c_int32),
                 ("spill_slots", c_int32), ("spill_slots_max", c_int32), ("reduce", c_int32),
                 ("stages", c_int32), ("reserved", c_int32)]
+
+
+class Instr(ctypes.Structure):
+    _fields_ = [("form", ctypes.c_uint16), ("arg", ctypes.c_uint16), ("imm", c_float)]
+
+
+class StageCode(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in ("row_off", "row_len", "elem_off", "elem_len", "reduce",
+                                       "reduce_lds", "reduce_slot", "reduce2_lds", "reduce2_slot")]
+
+
+MAX_STAGES = 4
+MAX_GROUP_ARGS = 16
+
+
+class GroupCode(ctypes.Structure):
+    _fields_ = [("n_col", c_int32), ("n_stages", c_int32), ("stage", StageCode * MAX_STAGES),
+                ("n_instr", c_int32), ("n_slots", c_int32), ("transposed_slot", c_int32),
+                ("reserved", c_int32), ("rstride", c_int64 * MAX_GROUP_ARGS),
+                ("cstride", c_int64 * MAX_GROUP_ARGS)]
 
 
 class ProgramDesc(ctypes.Structure):
@@ -119,6 +139,8 @@ def lib() -> ctypes.CDLL:
                                               POINTER(c_int32)]
         L.fuse_plan_is_materialized.argtypes = [vp, c_int32, POINTER(c_int32)]
         L.fuse_plan_group_geometry.argtypes = [vp, c_int32, POINTER(GroupGeometry)]
+        L.fuse_plan_group_code.argtypes = [vp, c_int32, POINTER(GroupCode), POINTER(Instr),
+                                           c_int32]
         L.fuse_group_run.argtypes = [vp, c_int32, POINTER(vp), vp]
         L.fuse_plan_run.argtypes = [vp, POINTER(vp), vp]
         L.fuse_plan_destroy.argtypes = [vp]

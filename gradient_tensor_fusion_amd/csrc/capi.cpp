@@ -380,6 +380,49 @@ int fuse_plan_group_geometry(const gtf_fuse_plan* plan, int32_t g, gtf_group_geo
   return GTF_OK;
 }
 
+static_assert(GTF_MAX_STAGES == kMaxStages && GTF_MAX_GROUP_ARGS == kMaxSlots,
+              "the program view's array sizes are the executor's");
+static_assert(sizeof(gtf_instr) == sizeof(Instr), "gtf_instr mirrors Instr");
+
+int fuse_plan_group_code(const gtf_fuse_plan* plan, int32_t g, gtf_group_code* info,
+                         gtf_instr* code, int32_t cap) {
+  if (plan == nullptr || info == nullptr) return fail(GTF_E_INVALID, "NULL argument");
+  if (g < 0 || g >= (int32_t)plan->p.groups.size()) return fail(GTF_E_INVALID, "group index");
+  const CompiledGroup& cg = plan->p.groups[g].code;
+  const ExecArgs& a = cg.args;
+  std::memset(info, 0, sizeof(*info));
+  info->n_col = a.n_col;
+  info->n_stages = a.n_stages;
+  for (int st = 0; st < a.n_stages; ++st) {
+    const StageDesc& S = a.stage[st];
+    gtf_stage_code& o = info->stage[st];
+    o.row_off = S.row_off;
+    o.row_len = S.row_len;
+    o.elem_off = S.el_off;
+    o.elem_len = S.el_len;
+    o.reduce = S.red;
+    o.reduce_lds = S.red_lds;
+    o.reduce_slot = S.red_slot;
+    o.reduce2_lds = S.red >= 4 ? S.red2_lds : -1;
+    o.reduce2_slot = S.red >= 4 ? S.red2_slot : -1;
+  }
+  info->n_instr = a.stage[a.n_stages - 1].el_off + a.stage[a.n_stages - 1].el_len;
+  info->n_slots = (int32_t)cg.slot_tensor.size();
+  info->transposed_slot = a.n_tr > 0 ? a.tr_slot : -1;
+  for (int s = 0; s < kMaxSlots; ++s) {
+    info->rstride[s] = a.rstride[s];
+    info->cstride[s] = a.cstride[s];
+  }
+  if (code == nullptr) return GTF_OK;
+  if (cap < info->n_instr) return fail(GTF_E_LIMIT, "code capacity too small");
+  for (int i = 0; i < info->n_instr; ++i) {
+    code[i].form = a.prog[i].code;
+    code[i].arg = a.prog[i].arg;
+    code[i].imm = a.prog[i].imm;
+  }
+  return GTF_OK;
+}
+
 int fuse_plan_is_materialized(const gtf_fuse_plan* plan, int32_t tensor_id, int32_t* yes) {
   if (plan == nullptr || yes == nullptr) return fail(GTF_E_INVALID, "NULL argument");
   if (tensor_id < 0 || tensor_id >= (int32_t)plan->p.n_desc_tensors)

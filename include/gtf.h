@@ -318,6 +318,51 @@ typedef struct {
 
 int fuse_plan_group_geometry(const gtf_fuse_plan* plan, int32_t g, gtf_group_geometry* out);
 
+/* The compiled op program of group g, for checking the group compiler on
+ * the host: a replay of the instructions must give the group's ops'
+ * results.  An instruction names one form of the executor's internal
+ * instruction set (numbered in the order of the library's form
+ * enumeration), its argument (a slot or register index) and an immediate.
+ * The column program is instructions [0, n_col); each stage runs its row
+ * program, then its element program, then ends in its reduction. */
+#define GTF_MAX_STAGES 4
+typedef struct {
+  uint16_t form;
+  uint16_t arg;
+  float imm;
+} gtf_instr;
+
+typedef struct {
+  int32_t row_off, row_len;    /* row program: [row_off, row_off + row_len)   */
+  int32_t elem_off, elem_len;  /* element program                              */
+  int32_t reduce;              /* as gtf_group_geometry.reduce (0: none)       */
+  int32_t reduce_lds;          /* LDS row slot of the (first) result, or -1    */
+  int32_t reduce_slot;         /* external slot of the (first) result, or -1   */
+  int32_t reduce2_lds;         /* the second result of a paired reduction      */
+  int32_t reduce2_slot;
+} gtf_stage_code;
+
+typedef struct {
+  int32_t n_col;               /* column program length                        */
+  int32_t n_stages;
+  gtf_stage_code stage[GTF_MAX_STAGES];
+  int32_t n_instr;             /* instructions over all phases                 */
+  int32_t n_slots;             /* external slots, in fuse_plan_group_tensors
+                                  order                                        */
+  int32_t transposed_slot;     /* the slot the staged-transpose form reads, -1 */
+  int32_t reserved;
+  int64_t rstride[GTF_MAX_GROUP_ARGS]; /* element strides of each slot: the
+                                          row and column phases and the
+                                          addressed loads read element
+                                          (r, c) at r * rstride + c * cstride */
+  int64_t cstride[GTF_MAX_GROUP_ARGS];
+} gtf_group_code;
+
+/* info must not be NULL; code may be NULL to ask only for info, otherwise
+ * it holds cap entries (GTF_E_LIMIT if cap < info->n_instr). */
+int fuse_plan_group_code(const gtf_fuse_plan* plan, int32_t g, gtf_group_code* info,
+                         gtf_instr* code, int32_t cap);
+
 /* *yes = 1 when tensor_id must live in device memory during a run: every
  * in and out tensor, and each tmp read by a group other than its
  * producer's.  The caller allocates those; other tmps need no memory. */
