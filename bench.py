@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the unfused and per-tensor baselines")
+    ap.add_argument("--trace-from", nargs=3, metavar=("STATS_CSV", "TRACE_CSV", "BENCH_JSON"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run of the workload (and the "
+                         "bench line it printed) into profiles/<kernel>_<workload>.md and exit (no GPU)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a c5 run into profiles/traffic_c5.txt and exit (no GPU)")
@@ -237,10 +240,12 @@ class C5:
 
 
 class Timing:
-    """Times of `steps` back-to-back steps: the mean (first to last event,
-    the figure the whole-job throughput uses), the wall time of the timed
-    region, and the distribution of per-step times from the events recorded
-    between consecutive steps."""
+    """Times of `steps` back-to-back steps: the mean (one event before the
+    first and one after the last, the figure the whole-job throughput
+    uses), the wall time of that timed region, and the distribution of
+    per-step times from a second pass with an event between consecutive
+    steps (each record puts a small gap in the stream, which matters only
+    for launches of tens of microseconds)."""
 
     def __init__(self, mean, wall, per_step):
         import numpy as np
@@ -256,20 +261,36 @@ class Timing:
                 "p90": round(self.p90 * scale, digits)}
 
 
-def time_steps(torch, fn, steps, warmup):
+def time_steps(torch, fn, steps, warmup, lead=None):
+    """Mean, wall time and per-step times of `steps` calls of fn after
+    `warmup` untimed ones.  lead: GPU work queued ahead of the first event
+    (not timed), so the host enqueues the steps while the GPU is still busy
+    and launches shorter than their host-side cost are not timed as gaps."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if lead is not None:
+        lead()
     t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean = e0.elapsed_time(e1) / steps
+    # the distribution: the same steps again, an event between each two
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    if lead is not None:
+        lead()
     ev[0].record()
     for i in range(steps):
         fn()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    return Timing(ev[0].elapsed_time(ev[steps]) / steps, wall, per)
+    return Timing(mean, wall, per)
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -360,7 +381,10 @@ def main():
         print(json.dumps(summarise_traffic(*args.traffic_from, workload=args.workload)))
         return
     if args.valu_from:
-        print(json.dumps(summarise_valu(args.valu_from, args.layers)))
+        print(json.dumps(summarise_valu(args.valu_from, args.layers, args.workload)))
+        return
+    if args.trace_from:
+        print(summarise_trace(*args.trace_from, workload=args.workload))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused groups shard by rows with no exchange "
@@ -519,6 +543,14 @@ def run_config(torch, gtf, configs, args):
            "vs_baseline": None, "dtype": "f32", "data": "synthetic"}
     gen = torch.Generator(device="cuda")
     gen.manual_seed(int(w[1]) if w[1].isdigit() else 7)
+    copy_gbs = lead = None
+    if w in ("c1", "c2", "c3", "c4"):
+        # the 1 GiB copy: the streaming ceiling beside the config, the
+        # reference the traffic counters are scaled by, and the lead queued
+        # ahead of each timed region
+        cb = CopyBench(torch, gtf)
+        copy_gbs = round(cb.gbs(5)[0], 1)
+        lead = cb.lead
     if w == "c4":
         numel = configs.c4_numel()
         bp = gtf.BucketPlan(numel, "f32", configs.BUCKET_CAP_BYTES)
@@ -553,28 +585,34 @@ def run_config(torch, gtf, configs, args):
         # every rotation set is touched in the warmup, so none is first used
         # inside the timed region
         wu = max(args.warmup, k)
-        tp = time_steps(torch, pack, args.steps, wu)
-        tu = time_steps(torch, unpack, args.steps, wu)
-        tt = time_steps(torch, pack_pt, args.steps, wu)
-        tw = time_steps(torch, warm_pack, args.steps, args.warmup)
+        tp = time_steps(torch, pack, args.steps, wu, lead)
         ms_p = tp.mean
         gbs = 2 * payload / (ms_p * 1e-3) / 1e9
         gb = lambda ms: round(2 * payload / (ms * 1e-3) / 1e9, 1)  # noqa: E731
+        tj = read_traffic("bucket_kernel", "c4")
         res.update({"value": round(gbs, 2), "ms_per_step": round(ms_p, 4),
                     "config": {"workload": "c4: pack 161 fp32 gradient tensors (25.6M elements) into "
                                            "25 MiB buckets x 1/8", "rotation_sets": k,
                                "bytes_per_step": 2 * payload},
                     "step_ms": tp.dist(),
                     "step_gbs": {"median": gb(tp.median), "p10_time": gb(tp.p10), "p90_time": gb(tp.p90)},
+                    # a copy with one multiply per element: bound by HBM
                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
                                  "frac": round(gbs / PEAK_GBS, 4), "kernel": "bucket_kernel",
-                                 "traffic": None},
-                    "unpack_gbs": gb(tu.mean), "unpack_step_ms": tu.dist(),
-                    "warm": {"ms_per_step": round(tw.mean, 5), "gbs": gb(tw.mean),
-                             "note": "one buffer set packed again and again (no rotation)"},
-                    "per_tensor_pack_ms": round(tt.mean, 4),
-                    "speedup_vs_per_tensor": round(tt.mean / ms_p, 3),
+                                 "avg_launch_us": round(ms_p * 1e3, 3),
+                                 "algorithmic_bytes_per_launch": 2 * payload,
+                                 "traffic": tj["bytes_per_launch"] if tj else None},
+                    "copy_kernel_gbs": copy_gbs,
                     "launches": {"one_launch": 1, "per_tensor": len([n for n in numel if n])}})
+        if not args.no_baselines:
+            tu = time_steps(torch, unpack, args.steps, wu, lead)
+            tt = time_steps(torch, pack_pt, args.steps, wu, lead)
+            tw = time_steps(torch, warm_pack, args.steps, args.warmup, lead)
+            res.update({"unpack_gbs": gb(tu.mean), "unpack_step_ms": tu.dist(),
+                        "warm": {"ms_per_step": round(tw.mean, 5), "gbs": gb(tw.mean),
+                                 "note": "one buffer set packed again and again (no rotation)"},
+                        "per_tensor_pack_ms": round(tt.mean, 4),
+                        "speedup_vs_per_tensor": round(tt.mean / ms_p, 3)})
         return res
     if w == "ceiling":
         return run_ceiling(torch, gtf, args, res)
@@ -601,7 +639,7 @@ def run_config(torch, gtf, configs, args):
         dists = {"P": ("uniform", -2, 2)}
         desc = "c3: rowsum((exp(P) + P/2) + tanh(P)), bf16[8192,4096] -> f32[8192]"
     out = {}
-    for fuse in (True, False):
+    for fuse in ((True,) if args.no_baselines else (True, False)):
         plan = gtf.FusePlan(g, fuse=fuse)
         nbytes = sum(group_bytes(g, plan))
         k = _rotation_sets(nbytes) if w != "c1" else 1
@@ -618,10 +656,10 @@ def run_config(torch, gtf, configs, args):
         def warm():
             for f in calls[0]:
                 f()
-        n = args.steps * (50 if w == "c1" else 1)
-        tm = time_steps(torch, step, n, max(args.warmup, k))
+        n = args.steps
+        tm = time_steps(torch, step, n, max(args.warmup, k), lead)
         # warm: the first set again and again (the Infinity Cache may serve it)
-        tw = time_steps(torch, warm, n, args.warmup)
+        tw = None if args.no_baselines else time_steps(torch, warm, n, args.warmup, lead)
         out[fuse] = (tm, nbytes, plan.num_groups, k, tw)
         del sets
     tm, nbytes, ng, k, tw = out[True]
@@ -629,17 +667,31 @@ def run_config(torch, gtf, configs, args):
     gbs = nbytes / (ms * 1e-3) / 1e9
     res.update({"value": round(gbs, 2), "ms_per_step": round(ms, 5),
                 "config": {"workload": desc, "rotation_sets": k, "bytes_per_step": nbytes},
-                "step_ms": tm.dist(),
-                "warm": {"ms_per_step": round(tw.mean, 5), "gbs": round(nbytes / (tw.mean * 1e-3) / 1e9, 1),
-                         "note": "one buffer set run again and again (no rotation)"},
-                "speedup_vs_unfused": round(out[False][0].mean / ms, 3),
-                "unfused": {"ms_per_step": round(out[False][0].mean, 5), "bytes": out[False][1],
-                            "launches": out[False][2], "step_ms": out[False][0].dist(),
-                            "warm_ms_per_step": round(out[False][4].mean, 5)},
-                "launches": ng})
-    if w != "c1":
-        res["roofline"] = {"bound": None, "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                           "frac": round(gbs / PEAK_GBS, 4), "kernel": "exec_kernel", "traffic": None}
+                "step_ms": tm.dist(), "launches": ng, "copy_kernel_gbs": copy_gbs})
+    if tw is not None:
+        res["warm"] = {"ms_per_step": round(tw.mean, 5), "gbs": round(nbytes / (tw.mean * 1e-3) / 1e9, 1),
+                       "note": "one buffer set run again and again (no rotation)"}
+    if False in out:
+        res["speedup_vs_unfused"] = round(out[False][0].mean / ms, 3)
+        res["unfused"] = {"ms_per_step": round(out[False][0].mean, 5), "bytes": out[False][1],
+                          "launches": out[False][2], "step_ms": out[False][0].dist(),
+                          "warm_ms_per_step": round(out[False][4].mean, 5)}
+    # the executor's roofline: HBM bytes against 8 TB/s, and VALU
+    # lane-instructions (from the committed SQ_INSTS_VALU summary of these
+    # kernel sources) against the issue peak; the larger fraction binds
+    hbm_frac = gbs / PEAK_GBS
+    valu = read_valu(w)
+    valu_frac = None
+    if valu and "exec_kernel" in valu:
+        valu_frac = valu["exec_kernel"] * ng / (ms * 1e-3) / VALU_PEAK
+    tj = read_traffic("exec_kernel", w)
+    res["roofline"] = {"bound": None if valu_frac is None else ("alu" if valu_frac > hbm_frac else "hbm"),
+                       "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                       "frac": round(hbm_frac, 4), "kernel": "exec_kernel",
+                       "avg_launch_us": round(ms * 1e3 / ng, 3),
+                       "algorithmic_bytes_per_launch": round(nbytes / ng),
+                       "traffic": tj["bytes_per_launch"] if tj else None,
+                       "valu_frac": None if valu_frac is None else round(valu_frac, 4)}
     return res
 
 
@@ -842,7 +894,8 @@ def traffic_file(workload):
 
 def traffic_cmds(workload):
     """The commands that make profiles/traffic_<workload>.txt."""
-    extra = "" if workload == "c5" else f" --workload {workload} --ln-variant row_resident"
+    extra = ("" if workload == "c5" else f" --workload {workload} --ln-variant row_resident"
+             if workload in ("ln", "softmax") else f" --workload {workload}")
     run = f"python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-baselines{extra}"
     return (
         "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE "
@@ -897,17 +950,25 @@ def summarise_traffic(fetch_csv, write_csv, workload="c5"):
     return res
 
 
-VALU_FILE = os.path.join(ROOT, "profiles", "valu_c5_groups.txt")
-VALU_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc SQ_INSTS_VALU SQ_WAVES "
-            "-d $OUT/pmc_valu -o valu --output-format csv -- python3 $R/bench.py "
-            "--workload groups")
+def valu_file(workload):
+    return os.path.join(ROOT, "profiles", "valu_c5_groups.txt" if workload == "c5"
+                        else f"valu_{workload}.txt")
 
 
-def summarise_valu(csv_path, layers):
-    """VALU lane-instructions per launch of each c5 group, from a rocprofv3
-    SQ_INSTS_VALU run of --workload groups (each group's launches back to
-    back, in C5.group_calls order).  SQ_INSTS_VALU counts wave instructions;
-    every wave of these launches is full, so lane instructions are 64x."""
+def valu_cmd(workload):
+    run = ("--workload groups" if workload == "c5" else
+           f"--workload {workload} --steps 3 --warmup 1 --no-baselines --no-cpu-baseline")
+    return ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc SQ_INSTS_VALU SQ_WAVES "
+            f"-d $OUT/pmc_valu -o valu --output-format csv -- python3 $R/bench.py {run}")
+
+
+def summarise_valu(csv_path, layers, workload="c5"):
+    """VALU lane-instructions per launch, from a rocprofv3 SQ_INSTS_VALU run:
+    for c5 of each group (--workload groups launches each group's 12
+    back-to-back, in C5.group_calls order), otherwise the average over the
+    workload's exec_kernel launches.  SQ_INSTS_VALU counts wave
+    instructions; every wave of these launches is full, so lane
+    instructions are 64x."""
     import csv
     per = {}
     for row in csv.DictReader(open(csv_path, newline="")):
@@ -915,41 +976,34 @@ def summarise_valu(csv_path, layers):
             continue
         per.setdefault(int(row["Dispatch_Id"]), {})[row["Counter_Name"]] = float(row["Counter_Value"])
     ids = sorted(per)
-    names = [n for k in ("ln", "ge", "do") for n in C5.GROUP_NAMES[k]]
-    assert len(ids) == layers * len(names), (len(ids), layers)
-    res = {"source_hash": _kernel_hash(), "lanes_per_wave": 64, "groups": {}}
-    for gi, name in enumerate(names):
-        chunk = [per[i] for i in ids[gi * layers:(gi + 1) * layers]]
-        res["groups"][name] = {
-            "valu_lane_instr_per_launch": round(64 * sum(c["SQ_INSTS_VALU"] for c in chunk) / layers),
-            "waves_per_launch": round(sum(c["SQ_WAVES"] for c in chunk) / layers)}
-    with open(VALU_FILE, "w") as f:
-        f.write("# VALU lane-instructions per launch of each c5 group (rocprofv3 SQ_INSTS_VALU x 64)\n")
-        f.write("# command (R = repository root, OUT = an output directory):\n#   " + VALU_CMD + "\n")
-        f.write("#   python3 bench.py --valu-from <valu>_counter_collection.csv\n")
+    res = {"source_hash": _kernel_hash(), "lanes_per_wave": 64}
+    if workload == "c5":
+        names = [n for k in ("ln", "ge", "do") for n in C5.GROUP_NAMES[k]]
+        assert len(ids) == layers * len(names), (len(ids), layers)
+        res["groups"] = {}
+        for gi, name in enumerate(names):
+            chunk = [per[i] for i in ids[gi * layers:(gi + 1) * layers]]
+            res["groups"][name] = {
+                "valu_lane_instr_per_launch": round(64 * sum(c["SQ_INSTS_VALU"] for c in chunk) / layers),
+                "waves_per_launch": round(sum(c["SQ_WAVES"] for c in chunk) / layers)}
+        what = "each c5 group"
+    else:
+        res["kernels"] = {"exec_kernel": {
+            "dispatches": len(ids),
+            "valu_lane_instr_per_launch": round(64 * sum(per[i]["SQ_INSTS_VALU"] for i in ids) / len(ids)),
+            "waves_per_launch": round(sum(per[i]["SQ_WAVES"] for i in ids) / len(ids))}}
+        what = f"the {workload} workload's exec_kernel"
+    with open(valu_file(workload), "w") as f:
+        f.write(f"# VALU lane-instructions per launch of {what} (rocprofv3 SQ_INSTS_VALU x 64)\n")
+        f.write("# command (R = repository root, OUT = an output directory):\n#   " + valu_cmd(workload) + "\n")
+        f.write(f"#   python3 bench.py --workload {workload} --valu-from <valu>_counter_collection.csv\n")
         f.write(json.dumps(res) + "\n")
     return res
 
 
-def read_valu():
-    """{group: VALU lane-instructions per launch}, or None when absent or
+def _summary_json(path):
+    """The last JSON line of a profiles/ summary, or None when absent or
     taken from another version of the kernel sources."""
-    if not os.path.exists(VALU_FILE):
-        return None
-    with open(VALU_FILE) as f:
-        js = [ln for ln in f if ln.startswith("{")]
-    if not js:
-        return None
-    tj = json.loads(js[-1])
-    if tj.get("source_hash") != _kernel_hash():
-        return None
-    return {k: v["valu_lane_instr_per_launch"] for k, v in tj["groups"].items()}
-
-
-def read_traffic(kernel, workload="c5"):
-    """Traffic record of one kernel, or None when absent or taken from
-    another version of the kernel sources."""
-    path = traffic_file(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -957,9 +1011,73 @@ def read_traffic(kernel, workload="c5"):
     if not js:
         return None
     tj = json.loads(js[-1])
-    if tj.get("source_hash") != _kernel_hash():
+    return tj if tj.get("source_hash") == _kernel_hash() else None
+
+
+def read_valu(workload="c5"):
+    """{group or kernel: VALU lane-instructions per launch}, or None."""
+    tj = _summary_json(valu_file(workload))
+    if tj is None:
         return None
-    return tj["kernels"].get(kernel)
+    return {k: v["valu_lane_instr_per_launch"] for k, v in tj.get("groups", tj.get("kernels", {})).items()}
+
+
+def summarise_trace(stats_csv, trace_csv, bench_json, workload):
+    """profiles/<kernel>_<workload>.md from a rocprofv3 kernel trace of
+    `bench.py --workload <workload> --no-baselines --no-cpu-baseline` and
+    the bench line that run printed: the library's kernels, and the timed
+    kernel's mean duration from the trace beside bench.py's own HIP-event
+    figure for the same launches."""
+    import csv
+    kernel = "bucket_kernel" if workload == "c4" else "exec_kernel"
+    rows = list(csv.DictReader(open(stats_csv, newline="")))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    ours = [r for r in rows if "gtf::" in r["Name"]]
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            for r in csv.DictReader(open(trace_csv, newline="")) if "gtf::" + kernel in r["Kernel_Name"]]
+    bench = None
+    with open(bench_json) as f:
+        for ln in f:
+            if ln.startswith("{"):
+                bench = json.loads(ln)
+    rf = bench["roofline"]
+    mean_us = sum(durs) / len(durs) / 1e3
+    nbytes = rf["algorithmic_bytes_per_launch"]
+    lines = [f"# {kernel} on {workload} — rocprofv3 kernel trace", "",
+             f"Workload: {bench['config']['workload']}.  MI355X, one GPU.", "",
+             "Command (R = repository root, OUT = an output directory):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $OUT/kt -o kt \\",
+             f"    --output-format csv -- python3 $R/bench.py --workload {workload} --no-baselines "
+             "--no-cpu-baseline > $OUT/bench.json",
+             f"python3 bench.py --workload {workload} --trace-from $OUT/kt/kt_kernel_stats.csv "
+             "$OUT/kt/kt_kernel_trace.csv $OUT/bench.json", "```", "",
+             "The library's kernels in that run (warmup and timed launches, and the 1 GiB copy "
+             "that gives the streaming ceiling):", "",
+             "| Kernel | Calls | Average (ns) | Min (ns) | Max (ns) | Share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in ours:
+        name = r["Name"].split("(")[0].replace("void ", "")
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                     f"{r['MaxNs']} | {100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    lines += ["", f"`{kernel}`: {len(durs)} dispatches, mean {mean_us:.3f} µs in the trace; bench.py's "
+              f"HIP events over its timed launches: {rf['avg_launch_us']:.3f} µs "
+              f"({100 * abs(mean_us - rf['avg_launch_us']) / rf['avg_launch_us']:.1f}% apart).",
+              f"Algorithmic bytes per launch: {nbytes:,} B, so {nbytes / (mean_us * 1e-6) / 1e9:.0f} GB/s "
+              f"by the trace = {nbytes / (mean_us * 1e-6) / 1e9 / PEAK_GBS:.3f} of 8 TB/s "
+              f"(bench.py: {rf['achieved']} GB/s; the 1 GiB copy in the same run: "
+              f"{bench.get('copy_kernel_gbs')} GB/s).",
+              f"Source hash {_kernel_hash()} (kernels.hip, isa.h, plan.cpp)."]
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+def read_traffic(kernel, workload="c5"):
+    """Traffic record of one kernel, or None when absent or taken from
+    another version of the kernel sources."""
+    tj = _summary_json(traffic_file(workload))
+    return None if tj is None else tj["kernels"].get(kernel)
 
 
 class MeasuredCost:
@@ -1164,7 +1282,7 @@ def run_joint(torch, gtf, configs, args, res, gen):
 def _kernel_hash():
     import hashlib
     h = hashlib.sha256()
-    for f in ("kernels.hip", "isa.h"):
+    for f in ("kernels.hip", "isa.h", "plan.cpp"):
         with open(os.path.join(ROOT, "gradient_tensor_fusion_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
