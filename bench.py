@@ -1065,7 +1065,7 @@ def summarise_trace(stats_csv, trace_csv, bench_json, workload):
               f"Algorithmic bytes per launch: {nbytes:,} B, so {nbytes / (mean_us * 1e-6) / 1e9:.0f} GB/s "
               f"by the trace = {nbytes / (mean_us * 1e-6) / 1e9 / PEAK_GBS:.3f} of 8 TB/s "
               f"(bench.py: {rf['achieved']} GB/s; the 1 GiB copy in the same run: "
-              f"{bench.get('copy_kernel_gbs')} GB/s).",
+              f"{bench.get('copy_kernel_gbs', bench.get('breakdown', {}).get('copy_kernel_gbs'))} GB/s).",
               f"Source hash {_kernel_hash()} (kernels.hip, isa.h, plan.cpp)."]
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
     with open(path, "w") as f:
