@@ -21,8 +21,9 @@
 //                 elements per lane (K = 4 in the wide instance).
 //
 // The machine has two working registers A and B and NS spill slots, each
-// holding one tile.  Every op reads A (and B) and writes A; moves between
-// A, B and the slots are explicit instructions.  Each instruction form has
+// holding one tile.  Every op writes A, reading A (and B), or B alone for
+// the unary and immediate forms that keep an operand needed later in B;
+// moves between A, B and the slots are explicit instructions.  Each instruction form has
 // exactly one body in the kernel, and every register index is a
 // compile-time constant, so the registers stay in VGPRs.  Three kernel
 // instances exist: wide with no spill slot (K = 4, NS = 0: A and B only,
@@ -88,6 +89,11 @@ enum Form : int {
   // fold A into a paired accumulator (element phase): (mean, squared
   // deviations, count), or (max, sum of exp(x - max))
   F_RED_MV, F_RED_SE,
+  // A = f(B), B unchanged, for the short unary forms (each form's body is
+  // one more copy of its code in every kernel instance)
+  F_EXP_B, F_TANH_B, F_RELU_B, F_SQUARE_B, F_NEG_B,
+  // A = B op imm, B unchanged (the order of the XOp family)
+  F_ADD_IB, F_SUB_IB, F_RSUB_IB, F_MUL_IB, F_DIV_IB, F_RDIV_IB, F_MAX_IB, F_MIN_IB,
   F_COUNT
 };
 

@@ -213,28 +213,24 @@ __device__ __forceinline__ float f_relu(float x) { return x > 0.f ? x : 0.f; }
 
 // tanh without a lane-dependent branch (a branch inside an interpreter case
 // would make the compiler linearise the whole dispatch switch): both forms
-// are computed and one is selected.  |x| < 0.625: x + x^3 P(x^2), with P of
-// degree 4 fitted here by weighted least squares on Chebyshev nodes (max
-// relative error 7.4e-8 in fp32); otherwise 1 - 2 e / (1 + e) with
-// e = e^{-2|x|} <= 0.29, which has no cancellation there (the result is at
-// least 0.55).  e enters only through 2e / (1 + e), whose absolute error is
-// under 2e times e's relative error; with e = 2^(-2 log2(e) |x|) taken in
-// one rounding of the argument that is e^{-2|x|} |x| 3.5e-7 at most (6e-8
-// at |x| = 0.5), so no split of the argument is needed: under 3e-7
-// relative in all at the branch point, less beyond.
+// are computed and one is selected.  |x| < 0.15: x - x^3/3 + 2x^5/15, the
+// series, whose first omitted term is under 6.2e-7 of the value there;
+// otherwise (1 - e) / (1 + e) with e = e^{-2|x|} = 2^(-2 log2(e) |x|) in
+// one rounding of the argument.  e's relative error is multiplied by
+// 2e / (1 - e^2) in the result, at most 3.3 at the branch point and
+// falling beyond it, so with the hardware exp2 and reciprocal within an
+// ulp each the result stays under 6.6e-7 relative everywhere (a host
+// replay of every operation, each result moved by up to an ulp either way,
+// over a fine grid and the subnormal range).  13 VALU slots.
 __device__ __forceinline__ float f_tanh(float x) {
   const float ax = fabsf(x);
   const float u = ax * ax;
-  float p = -5.691985599696636e-03f;
-  p = __builtin_fmaf(p, u, 2.0626291632652283e-02f);
-  p = __builtin_fmaf(p, u, -5.373531952500343e-02f);
-  p = __builtin_fmaf(p, u, 1.3331381976604462e-01f);
-  p = __builtin_fmaf(p, u, -3.333328068256378e-01f);
+  const float p = __builtin_fmaf(u, 0.133333333f, -0.333333343f);
   const float small = __builtin_fmaf(ax * u, p, ax);
   constexpr float kM2L = -2.88539004e+00f;  // -2 log2(e)
   const float e = __builtin_amdgcn_exp2f(ax * kM2L);
-  const float big = __builtin_fmaf(-2.0f, e * __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
-  return copysignf(ax < 0.625f ? small : big, x);
+  const float big = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+  return copysignf(ax < 0.15f ? small : big, x);
 }
 
 // ---------------------------------------------------------------- predicated stores
@@ -608,11 +604,12 @@ __device__ __forceinline__ RowAcc merge_se(RowAcc x, RowAcc y) {
 }
 
 // ---------------------------------------------------------------- ops
+// d = f(s) element by element (d and s may be the same register)
 template <int V, int F>
-__device__ __forceinline__ void unary(float (&r)[V]) {
+__device__ __forceinline__ void unary(float (&d)[V], const float (&s)[V]) {
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    const float x = r[i];
+    const float x = s[i];
     float y;
     if (F == F_EXP) y = f_exp(x);
     else if (F == F_TANH) y = f_tanh(x);
@@ -624,7 +621,7 @@ __device__ __forceinline__ void unary(float (&r)[V]) {
     else if (F == F_SQRT) y = sqrtf(x);
     else if (F == F_RECIP) y = 1.0f / x;
     else y = -x;  // F_NEG
-    r[i] = y;
+    d[i] = y;
   }
 }
 
@@ -696,6 +693,11 @@ template <int V, int OP>
 __device__ __forceinline__ void xscalar(float (&r)[V], float x) {
 #pragma unroll
   for (int i = 0; i < V; ++i) r[i] = xop<OP>(r[i], x);
+}
+template <int V, int OP>
+__device__ __forceinline__ void xscalar_from(float (&d)[V], const float (&s)[V], float x) {
+#pragma unroll
+  for (int i = 0; i < V; ++i) d[i] = xop<OP>(s[i], x);
 }
 
 template <int V>
@@ -773,21 +775,20 @@ __device__ __forceinline__ void run_prog(const ExecArgs& a, const Instr* prog, i
   case F_S02B + K: if constexpr (K < NS) copy<V>(B, S[K]); break;
       GTF_SLOT(0) GTF_SLOT(1) GTF_SLOT(2) GTF_SLOT(3) GTF_SLOT(4) GTF_SLOT(5)
 #undef GTF_SLOT
-      case F_EXP: unary<V, F_EXP>(A); break;
-      case F_TANH: unary<V, F_TANH>(A); break;
-      case F_SIGMOID: unary<V, F_SIGMOID>(A); break;
-      case F_RELU: unary<V, F_RELU>(A); break;
-      case F_GELU: unary<V, F_GELU>(A); break;
-      case F_GELU_BF: unary<V, F_GELU_BF>(A); break;
-      case F_SQUARE: unary<V, F_SQUARE>(A); break;
-      case F_SQRT: unary<V, F_SQRT>(A); break;
-      case F_RECIP: unary<V, F_RECIP>(A); break;
-      case F_NEG: unary<V, F_NEG>(A); break;
+#define GTF_UN(NAME) case F_##NAME: unary<V, F_##NAME>(A, A); break;
+#define GTF_UN_B(NAME)                                        \
+  case F_##NAME: unary<V, F_##NAME>(A, A); break;             \
+  case F_##NAME##_B: unary<V, F_##NAME>(A, B); break;
+      GTF_UN_B(EXP) GTF_UN_B(TANH) GTF_UN(SIGMOID) GTF_UN_B(RELU) GTF_UN(GELU) GTF_UN(GELU_BF)
+      GTF_UN_B(SQUARE) GTF_UN(SQRT) GTF_UN(RECIP) GTF_UN_B(NEG)
+#undef GTF_UN
+#undef GTF_UN_B
 #define GTF_BIN(NAME, OP)                                                               \
   case F_##NAME: binop<V, OP>(A, B); break;                                             \
   case F_##NAME##_C: if (MODE == M_ELEM) xvec<V, OP>(A, col, t.kstride); break;         \
   case F_##NAME##_R: if (MODE != M_COL) xscalar<V, OP>(A, lds_row[arg * a.RB + t.rr]); break; \
-  case F_##NAME##_I: xscalar<V, OP>(A, cur.imm); break;
+  case F_##NAME##_I: xscalar<V, OP>(A, cur.imm); break;                                \
+  case F_##NAME##_IB: xscalar_from<V, OP>(A, B, cur.imm); break;
       GTF_BIN(ADD, X_ADD)
       GTF_BIN(SUB, X_SUB)
       GTF_BIN(RSUB, X_RSUB)

@@ -314,7 +314,37 @@ struct Codegen {
     *arg = lds_slot.at(v);
   }
 
+  // A = f(B) or A = B op imm when the operand is (or is best loaded) in B:
+  // B keeps a value that is read again, with no move.  False when the
+  // operand is better taken in A.
+  bool from_b(int v, int form, float imm = 0.f) {
+    if (form < 0) return false;
+    if (where(v) < 0 && loadable.count(v) && use(v) > 1 && !live(RB)) {
+      // read again later: loaded into B, where it stays
+      emit(load_form(v, RB), ext_slot.at(v));
+      reg[RB] = v;
+    }
+    if (reg[RB] != v || reg[RA] == v) return false;
+    uses[v] -= 1;
+    save(RA, false);  // A's value, if still read, goes to a slot: B holds v
+    emit(form, 0, imm);
+    return true;
+  }
+  static int b_form(int form) {
+    switch (form) {
+      case F_EXP: return F_EXP_B;
+      case F_TANH: return F_TANH_B;
+      case F_RELU: return F_RELU_B;
+      case F_SQUARE: return F_SQUARE_B;
+      case F_NEG: return F_NEG_B;
+    }
+    return -1;
+  }
   void run_unary(const MOp& m) {
+    if (from_b(m.in[0], b_form(m.form))) {
+      reg[RA] = m.out;
+      return;
+    }
     bring(m.in[0], RA);
     consume_a(m.in[0]);
     emit(m.form);
@@ -343,6 +373,10 @@ struct Codegen {
     reg[RA] = m.out;
   }
   void run_imm(const MOp& m) {
+    if (from_b(m.in[0], F_ADD_IB + m.form, m.imm)) {
+      reg[RA] = m.out;
+      return;
+    }
     bring(m.in[0], RA);
     consume_a(m.in[0]);
     emit(F_ADD_I + m.form, 0, m.imm);
@@ -1006,8 +1040,11 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
         for (auto& kv : staging) note(kv.first);
         for (auto& m : L)
           for (int k = 0; k < mop_arity(m); ++k) note(m.in[k]);
+        // (a lone input read more than once goes to B, where the unary and
+        // immediate forms read it without moving it)
+        const bool lone_in_b = first_use.size() == 1 && g.use(first_use[0]) > 1;
         for (size_t i = 0; i < first_use.size() && i < 2; ++i) {
-          const int r = i == 0 ? Codegen::RA : Codegen::RB;
+          const int r = i == 0 && !lone_in_b ? Codegen::RA : Codegen::RB;
           g.emit(g.load_form(first_use[i], r), g.ext_slot.at(first_use[i]));
           g.reg[r] = first_use[i];
         }
@@ -1035,6 +1072,11 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
           int score = 0;
           if (ra == x0 || ra == x1) score += 2;
           if (n_in == 2 && ((rb == x1 && ra != x1) || (rb == x0 && ra != x0))) score += 1;
+          // a unary or immediate op reads its operand from B too (after ops
+          // that free A by reading it)
+          if (n_in == 1 && rb == x0 && ra != x0 &&
+              (L[k].kind == 2 || (L[k].kind == 0 && Codegen::b_form(L[k].form) >= 0)))
+            score += 1;
           if (score > best_score) {
             best_score = score;
             best = (int)k;

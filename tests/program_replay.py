@@ -6,8 +6,9 @@ launches them.
 The replay restates what each instruction form does in the executor: two
 working registers A and B and the spill slots hold one value each (a [1,C]
 column in the column phase, an [R,1] column of row values in the row
-phase, the [R,C] domain in the element phase); every op reads A (and B, or
-an LDS slot, or an immediate) and writes A; loads and stores address an
+phase, the [R,C] domain in the element phase); every op writes A, reading
+A (and B, or an LDS slot, or an immediate), or B alone for the unary and
+immediate forms that keep their operand in B; loads and stores address an
 external tensor by phase (the element phase walks the domain in row-major
 order, the row phase reads element r * rstride, the column phase element
 c * cstride, and the addressed loads element r * rstride + c * cstride);
@@ -189,6 +190,12 @@ class _Group:
             if name in ("EXP", "TANH", "SIGMOID", "RELU", "GELU", "GELU_BF", "SQUARE", "SQRT",
                         "RECIP", "NEG"):
                 reg["A"] = _unary(name, get("A"))
+                continue
+            if name.endswith("_B") and name[:-2] in ("EXP", "TANH", "RELU", "SQUARE", "NEG"):
+                reg["A"] = _unary(name[:-2], get("B"))
+                continue
+            if name.endswith("_IB") and name[:-3] in _XOPS:
+                reg["A"] = np.broadcast_to(_xop(name[:-3], get("B"), np.float32(imm)), shape).astype(np.float32)
                 continue
             if name in _XOPS:
                 reg["A"] = _xop(name, get("A"), get("B"))

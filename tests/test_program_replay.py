@@ -98,12 +98,15 @@ def test_workloads_at_small_shapes(rr):
 
 def test_c3_sums_each_term_of_the_diamond():
     """The diamond's sum runs as one reduction fed term by term: the
-    element program folds three values and stores nothing else."""
+    element program folds three values and stores nothing else.  Its one
+    input, read three times, is loaded into B and read there by the exp,
+    the scaling and the tanh: no register move."""
     g = configs.c3_graph(33, 1024)
     plan = check(g, configs.c3_inputs(g))
     assert plan.num_groups == 1
     names = [NAME[f] for f, _, _ in plan.code(0)["instr"]]
     assert names.count("RED") == 3 and not any(n.startswith("ST_") for n in names)
+    assert names == ["LD_BF16_B", "EXP_B", "RED", "MUL_IB", "RED", "TANH_B", "RED"], names
 
 
 def test_random_elementwise_dags():
