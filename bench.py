@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--trace-from", nargs=3, metavar=("STATS_CSV", "TRACE_CSV", "BENCH_JSON"),
                     help="summarise a rocprofv3 --kernel-trace --stats run of the workload (and the "
                          "bench line it printed) into profiles/<kernel>_<workload>.md and exit (no GPU)")
+    ap.add_argument("--ceiling-from", metavar="BENCH_JSON",
+                    help="summarise a --workload ceiling run's line into profiles/stream_ceiling.md "
+                         "and exit (no GPU)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a c5 run into profiles/traffic_c5.txt and exit (no GPU)")
@@ -385,6 +388,9 @@ def main():
         return
     if args.trace_from:
         print(summarise_trace(*args.trace_from, workload=args.workload))
+        return
+    if args.ceiling_from:
+        print(summarise_ceiling(args.ceiling_from))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused groups shard by rows with no exchange "
@@ -1068,6 +1074,43 @@ def summarise_trace(stats_csv, trace_csv, bench_json, workload):
               f"{bench.get('copy_kernel_gbs', bench.get('breakdown', {}).get('copy_kernel_gbs'))} GB/s).",
               f"Source hash {_kernel_hash()} (kernels.hip, isa.h, plan.cpp)."]
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+def summarise_ceiling(bench_json):
+    """profiles/stream_ceiling.md from the line of `bench.py --workload
+    ceiling`: every probe configuration, the best of each kind, and the
+    back-to-back launches the size of one fused group."""
+    d = None
+    with open(bench_json) as f:
+        for ln in f:
+            if ln.startswith("{"):
+                d = json.loads(ln)
+    lines = ["# Streaming ceiling of the part — gtf_stream_probe (copy, read, write of 1 GiB)", "",
+             "Command (R = repository root, OUT = an output directory):", "", "```",
+             "python3 $R/bench.py --workload ceiling --steps 10 > $OUT/ceiling.json",
+             "python3 bench.py --ceiling-from $OUT/ceiling.json", "```", "",
+             "Each point is the median of the launches' HIP-event times; copy counts 2 bytes per "
+             "byte moved.  Best of each kind:", "",
+             "| Kind | 16-byte accesses in flight | Nontemporal | Workgroups per CU (0: one per span) "
+             "| ms | GB/s | of 8 TB/s |", "|---|---|---|---|---|---|---|"]
+    for k, r in d["best"].items():
+        lines.append(f"| {k} | {r['depth']} | {r['nontemporal']} | {r['grid_per_cu']} | {r['ms']} | "
+                     f"{r['gbs']} | {r['gbs'] / PEAK_GBS:.3f} |")
+    lines += ["", "Back-to-back launches of the best copy and read, each the size of one fused "
+              "group, rotating through >= 1 GiB:", "", "| Kind | Bytes moved per launch | µs per launch | GB/s |",
+              "|---|---|---|---|"]
+    for r in d["back_to_back_launches"]:
+        lines.append(f"| {r['kind']} | {r['bytes_moved']:,} | {r['us_per_launch']} | {r['gbs']} |")
+    lines += ["", f"The library's dwordx4 copy kernel: {d['library_copy_kernel_gbs']} GB/s; torch's "
+              f"device copy: {d['torch_copy_gbs']} GB/s.", "", "Every configuration:", "",
+              "| Kind | In flight | Nontemporal | Per CU | ms | GB/s |", "|---|---|---|---|---|---|"]
+    for r in d["table"]:
+        lines.append(f"| {r['kind']} | {r['depth']} | {r['nontemporal']} | {r['grid_per_cu']} | "
+                     f"{r['ms']} | {r['gbs']} |")
+    path = os.path.join(ROOT, "profiles", "stream_ceiling.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     return path
