@@ -148,6 +148,38 @@ def exhaustive_small(shape=(3, 5)):
     return dags
 
 
+THREE_VOCAB = ("tanh", "mul_imm", "sub", "dmul")
+
+
+def exhaustive_three(vocab=THREE_VOCAB, shape=(3, 5)):
+    """Every connected DAG of three ops over x0, x1 (and the mask m) drawn
+    from `vocab` -- by default one transcendental, one immediate op, a
+    binary op that does not commute and the masked multiply, so every
+    operand wiring and every register path of three ops occurs: the first
+    op's value is read by the second or the third, and the third reads the
+    second's.  Same format as exhaustive_small (-1, -2: the first and second
+    op's values)."""
+    g, avail, m, ranges = _base(shape)
+
+    def choices(av, rg):
+        return [c for c in op_choices(av, rg, m) if c[0] in vocab]
+
+    def rng_of(c, rg):
+        return result_range(c[0], [rg[t] for t in c[1] if t != m], c[2])
+
+    dags = []
+    for c1 in choices(avail, ranges):
+        r1 = dict(ranges)
+        r1[-1] = rng_of(c1, ranges)
+        for c2 in choices(avail + [-1], r1):
+            r2 = dict(r1)
+            r2[-2] = rng_of(c2, r1)
+            for c3 in choices(avail + [-1, -2], r2):
+                if -2 in c3[1] and (-1 in c2[1] or -1 in c3[1]):
+                    dags.append(((c1, c2, c3), False))
+    return dags
+
+
 def combine(dags, shape):
     """One graph holding each small DAG as its own component over shared
     inputs x0, x1, m; returns (graph, per DAG its output tensor ids)."""
@@ -156,7 +188,7 @@ def combine(dags, shape):
     for k, (ops, t0_out) in enumerate(dags):
         made = []
         for j, (op, ins, imm) in enumerate(ops):
-            real = [made[0] if t == -1 else t for t in ins]
+            real = [made[-t - 1] if t < 0 else t for t in ins]
             made.append(_add(g, ranges, op, real, imm, f"d{k}_{j}", shape))
         outs.append(made)
     readers = {t for o in g.ops for t in o.inputs}

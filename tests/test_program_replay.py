@@ -129,6 +129,16 @@ def test_every_dag_of_two_ops(shape):
         check(g, ins, fuse=False)
 
 
+def test_every_connected_dag_of_three_ops():
+    dags = dag_gen.exhaustive_three()
+    assert len(dags) == 1000
+    for c0 in range(0, len(dags), 500):
+        g, _ = dag_gen.combine(dags[c0:c0 + 500], (5, 130))
+        ins = _inputs_for(g, 1500 + c0)
+        check(g, ins)
+        check(g, ins, fuse=False)
+
+
 def test_random_dags_over_every_opcode():
     used = set()
     for n_ops in (3, 6, 10, 16):
