@@ -591,12 +591,12 @@ def run_config(torch, gtf, configs, args):
         # every rotation set is touched in the warmup, so none is first used
         # inside the timed region
         wu = max(args.warmup, k)
-        tp = time_steps(torch, pack, args.steps, wu, lead)
+        tp = time_steps(torch, pack, 5 * args.steps, wu, lead)
         ms_p = tp.mean
         gbs = 2 * payload / (ms_p * 1e-3) / 1e9
         gb = lambda ms: round(2 * payload / (ms * 1e-3) / 1e9, 1)  # noqa: E731
         tj = read_traffic("bucket_kernel", "c4")
-        res.update({"value": round(gbs, 2), "ms_per_step": round(ms_p, 4),
+        res.update({"value": round(gbs, 2), "ms_per_step": round(ms_p, 4), "steps": 5 * args.steps,
                     "config": {"workload": "c4: pack 161 fp32 gradient tensors (25.6M elements) into "
                                            "25 MiB buckets x 1/8", "rotation_sets": k,
                                "bytes_per_step": 2 * payload},
@@ -662,7 +662,7 @@ def run_config(torch, gtf, configs, args):
         def warm():
             for f in calls[0]:
                 f()
-        n = args.steps
+        n = 5 * args.steps  # short launches: more steps for a steadier mean
         tm = time_steps(torch, step, n, max(args.warmup, k), lead)
         # warm: the first set again and again (the Infinity Cache may serve it)
         tw = None if args.no_baselines else time_steps(torch, warm, n, args.warmup, lead)
@@ -671,7 +671,7 @@ def run_config(torch, gtf, configs, args):
     tm, nbytes, ng, k, tw = out[True]
     ms = tm.mean
     gbs = nbytes / (ms * 1e-3) / 1e9
-    res.update({"value": round(gbs, 2), "ms_per_step": round(ms, 5),
+    res.update({"value": round(gbs, 2), "ms_per_step": round(ms, 5), "steps": 5 * args.steps,
                 "config": {"workload": desc, "rotation_sets": k, "bytes_per_step": nbytes},
                 "step_ms": tm.dist(), "launches": ng, "copy_kernel_gbs": copy_gbs})
     if tw is not None:
@@ -1046,15 +1046,19 @@ def summarise_trace(stats_csv, trace_csv, bench_json, workload):
         for ln in f:
             if ln.startswith("{"):
                 bench = json.loads(ln)
-    rf = bench["roofline"]
+    # a line with one variant timed (--ln-variant) has no roofline: one launch per step
+    rf = bench.get("roofline") or {"avg_launch_us": bench["ms_per_step"] * 1e3,
+                                   "algorithmic_bytes_per_launch": bench["config"]["bytes_per_step"],
+                                   "achieved": bench["value"]}
     mean_us = sum(durs) / len(durs) / 1e3
     nbytes = rf["algorithmic_bytes_per_launch"]
     lines = [f"# {kernel} on {workload} — rocprofv3 kernel trace", "",
              f"Workload: {bench['config']['workload']}.  MI355X, one GPU.", "",
              "Command (R = repository root, OUT = an output directory):", "", "```",
              "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $OUT/kt -o kt \\",
-             f"    --output-format csv -- python3 $R/bench.py --workload {workload} --no-baselines "
-             "--no-cpu-baseline > $OUT/bench.json",
+             f"    --output-format csv -- python3 $R/bench.py --workload {workload} "
+             + ("--ln-variant row_resident" if workload in ("ln", "softmax") else
+                "--no-baselines --no-cpu-baseline") + " > $OUT/bench.json",
              f"python3 bench.py --workload {workload} --trace-from $OUT/kt/kt_kernel_stats.csv "
              "$OUT/kt/kt_kernel_trace.csv $OUT/bench.json", "```", "",
              "The library's kernels in that run (warmup and timed launches, and the 1 GiB copy "
