@@ -28,7 +28,7 @@ OPCODE = {
     "add": 32, "sub": 33, "mul": 34, "div": 35, "max": 36, "min": 37,
     "add3": 48, "dmul": 49,
     "row_sum": 64, "row_mean": 65, "row_max": 66,
-    "transpose": 80, "reshape": 81, "concat": 82,
+    "transpose": 80, "reshape": 81, "concat": 82, "tuple": 83,
 }
 OPF_OPAQUE = 1
 NO_FUSE = 1

@@ -61,7 +61,7 @@ int arity(int opc) {
     case GTF_OP_RESHAPE:
       return 1;
     case GTF_OP_ADD: case GTF_OP_SUB: case GTF_OP_MUL: case GTF_OP_DIV:
-    case GTF_OP_MAX: case GTF_OP_MIN: case GTF_OP_DMUL: case GTF_OP_CONCAT:
+    case GTF_OP_MAX: case GTF_OP_MIN: case GTF_OP_DMUL: case GTF_OP_CONCAT: case GTF_OP_TUPLE:
       return 2;
     case GTF_OP_ADD3:
       return 3;
@@ -104,7 +104,8 @@ int validate(const gtf_program_desc* d, FusePlan* p) {
   for (int i = 0; i < d->n_ops; ++i) {
     const gtf_op_desc& od = d->ops[i];
     OpInfo& o = p->ops[i];
-    const int ar = arity(od.opcode);
+    // a concat reads two tensors, or one tuple
+    const int ar = od.opcode == GTF_OP_CONCAT && od.n_in == 1 ? 1 : arity(od.opcode);
     if (ar < 0) return fail(GTF_E_UNSUPPORTED, op_name(i) + ": opcode " + std::to_string(od.opcode));
     if (od.n_in != ar) return fail(GTF_E_INVALID, op_name(i) + ": n_in does not match the opcode");
     if (od.flags & ~GTF_OPF_OPAQUE) return fail(GTF_E_INVALID, op_name(i) + ": unknown flags");
@@ -144,14 +145,22 @@ int validate(const gtf_program_desc* d, FusePlan* p) {
       const TensorInfo& ti = p->tensors[od.in[0]];
       if (ti.R * ti.C != to.R * to.C)
         return fail(GTF_E_SHAPE, op_name(i) + ": reshape changes the element count");
-    } else if (od.opcode == GTF_OP_CONCAT) {
+    } else if (od.opcode == GTF_OP_CONCAT && ar == 1) {
+      const TensorInfo& ti = p->tensors[od.in[0]];
+      const int w = writer[od.in[0]];
+      if (w < 0 || p->ops[w].opcode != GTF_OP_TUPLE)
+        return fail(GTF_E_INVALID, op_name(i) + ": a concat of one operand reads a tuple");
+      if (to.R != ti.R || to.C != ti.C || d->tensors[out].rank != 2 || to.dtype != ti.dtype)
+        return fail(GTF_E_SHAPE, op_name(i) + ": a concat of a tuple is declared as the tuple");
+    } else if (od.opcode == GTF_OP_CONCAT || od.opcode == GTF_OP_TUPLE) {
       const TensorInfo& a = p->tensors[od.in[0]];
       const TensorInfo& b = p->tensors[od.in[1]];
       if (a.rank != 2 || b.rank != 2 || d->tensors[out].rank != 2 || a.R != b.R || to.R != a.R ||
           a.C < 1 || b.C < 1 || to.C != a.C + b.C)
         return fail(GTF_E_SHAPE, op_name(i) + ": concat of [R,C1], [R,C2] (rank 2, C1, C2 >= 1) "
                                               "is declared [R,C1+C2]");
-      if (a.dtype != b.dtype) return fail(GTF_E_UNSUPPORTED, op_name(i) + ": concat of two dtypes");
+      if (a.dtype != b.dtype || to.dtype != a.dtype)
+        return fail(GTF_E_UNSUPPORTED, op_name(i) + ": concat or tuple of two dtypes");
     } else {
       // NumPy broadcasting per axis: extents of 1 stretch to the other one
       int64_t R = 1, C = 1;
@@ -174,6 +183,17 @@ int validate(const gtf_program_desc* d, FusePlan* p) {
       return fail(GTF_E_INVALID, "tensor " + std::to_string(t) + ": no op writes it");
     if (role == GTF_ROLE_TMP && readers[t] == 0)
       return fail(GTF_E_INVALID, "tensor " + std::to_string(t) + ": tmp that no op reads");
+  }
+  // a tuple is read only by concats of one operand, and is not a graph output
+  for (int i = 0; i < d->n_ops; ++i) {
+    if (p->ops[i].opcode != GTF_OP_TUPLE) continue;
+    const int t = p->ops[i].out;
+    if (p->tensors[t].role != GTF_ROLE_TMP)
+      return fail(GTF_E_INVALID, op_name(i) + ": a tuple is not a graph output");
+    for (int j = 0; j < d->n_ops; ++j)
+      for (int k = 0; k < p->ops[j].n_in; ++k)
+        if (p->ops[j].in[k] == t && !(p->ops[j].opcode == GTF_OP_CONCAT && p->ops[j].n_in == 1))
+          return fail(GTF_E_INVALID, op_name(j) + ": a tuple is read only by a concat of it");
   }
   return GTF_OK;
 }

@@ -6,7 +6,8 @@
 // "Operator Pattern Classification" (the kinds and CombinePattern = max),
 // "Algorithm" steps 1-4 and "Fusion rules" (the three phases, reductions
 // are sinks only, opaque ops are barriers, at most kMaxFusedOps = 256 ops
-// and a bounded argument count per group).
+// and a bounded argument count per group).  A tuple (kTuple) fuses into the
+// injective concat after it in phase 1; its fields join it in phase 2.
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
@@ -48,7 +49,9 @@ struct UnionFind {
     int rx = find(x), rt = find(target);
     if (rx == rt) return;
     parent[rx] = rt;
-    pat[rt] = std::max(pat[rt], pat[rx]);  // CombinePattern
+    // CombinePattern; a tuple fused into the group after it is an injective
+    // member there
+    pat[rt] = std::max(pat[rt], pat[rx] == GTF_PAT_TUPLE ? (int)GTF_PAT_INJECTIVE : pat[rx]);
     size[rt] += size[rx];
   }
 };
@@ -141,8 +144,15 @@ struct MOp {
 // register operands of a micro-op
 int mop_arity(const MOp& m) { return m.kind == 1 ? 2 : m.kind == 5 ? 0 : 1; }
 
-bool is_gather(int opc) {
-  return opc == GTF_OP_TRANSPOSE || opc == GTF_OP_RESHAPE || opc == GTF_OP_CONCAT;
+// ops that run as addressed loads of tensors in memory: transpose, reshape,
+// a concat of two tensors and a tuple (a tuple's value is its fields side
+// by side; a concat of one tuple is a copy of it)
+bool is_gather(const OpInfo& o) {
+  return o.opcode == GTF_OP_TRANSPOSE || o.opcode == GTF_OP_RESHAPE || o.opcode == GTF_OP_TUPLE ||
+         (o.opcode == GTF_OP_CONCAT && o.n_in == 2);
+}
+bool is_join(const OpInfo& o) {
+  return o.opcode == GTF_OP_TUPLE || (o.opcode == GTF_OP_CONCAT && o.n_in == 2);
 }
 
 int unary_form(int opc) {
@@ -485,13 +495,54 @@ const char* check_program(const ExecArgs& a, int n_slots) {
   return nullptr;
 }
 
-bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup* outp,
+bool compile_group(const FusePlan& p, const std::vector<int>& ops_in, CompiledGroup* outp,
                    std::string* why) {
   CompiledGroup cg;
   std::memset(&cg.args, 0, sizeof(cg.args));
   auto bad = [&](const std::string& s) {
     if (why) *why = s;
     return false;
+  };
+  // ---- moves folded into a join: a transpose or reshape of a tensor in
+  // memory whose value only a concat or a tuple of the group reads (and
+  // that is no graph output, in its source's dtype) is that join's
+  // addressing of its source, and is not run on its own.  fold: moved value -> (source, (rstride,
+  // cstride)), the source's element for position (r, c) of the value.
+  std::map<int, std::pair<int, std::pair<int64_t, int64_t>>> fold;
+  std::vector<int> ops;
+  {
+    std::vector<char> in_group(p.ops.size(), 0);
+    std::set<int> made;
+    for (int i : ops_in) {
+      in_group[i] = 1;
+      made.insert(p.ops[i].out);
+    }
+    for (int i : ops_in) {
+      const OpInfo& o = p.ops[i];
+      if ((o.opcode == GTF_OP_TRANSPOSE || o.opcode == GTF_OP_RESHAPE) && !made.count(o.in[0]) &&
+          p.tensors[o.out].role != GTF_ROLE_OUT && p.tensors[o.in[0]].dtype == p.tensors[o.out].dtype) {
+        int reader = -1, n = 0;
+        for (size_t j = 0; j < p.ops.size(); ++j)
+          for (int k = 0; k < p.ops[j].n_in; ++k)
+            if (p.ops[j].in[k] == o.out) {
+              reader = (int)j;
+              ++n;
+            }
+        if (n == 1 && in_group[reader] && is_join(p.ops[reader])) {
+          const int x = o.in[0];
+          const TensorInfo& tv = p.tensors[o.out];
+          fold[o.out] = {x, o.opcode == GTF_OP_TRANSPOSE
+                                ? std::make_pair((int64_t)1, p.tensors[x].C)
+                                : std::make_pair(tv.R == 1 ? (int64_t)0 : tv.C, (int64_t)1)};
+          continue;
+        }
+      }
+      ops.push_back(i);
+    }
+  }
+  auto source_of = [&](int t) {
+    auto f = fold.find(t);
+    return f == fold.end() ? t : f->second.first;
   };
   std::vector<char> member(p.ops.size(), 0);
   for (int i : ops) member[i] = 1;
@@ -505,17 +556,18 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   bool gathers2d = false;
   for (int i : ops) {
     const OpInfo& o = p.ops[i];
-    if (!is_gather(o.opcode)) continue;
+    if (!is_gather(o)) continue;
     if (o.opcode != GTF_OP_RESHAPE) gathers2d = true;
     for (int k = 0; k < o.n_in; ++k) {
       if (produced.count(o.in[k])) return bad("transpose/reshape/concat of a value made in the group");
+      const int src = source_of(o.in[k]);
       for (int j : ops)
         if (j != i)
           for (int q = 0; q < p.ops[j].n_in; ++q)
-            if (p.ops[j].in[q] == o.in[k])
+            if (p.ops[j].in[q] == o.in[k] || source_of(p.ops[j].in[q]) == src)
               return bad("transpose/reshape/concat input also read by another op of the group");
     }
-    if ((o.opcode == GTF_OP_TRANSPOSE || o.opcode == GTF_OP_CONCAT) && p.tensors[o.in[0]].dtype == GTF_U8)
+    if (o.opcode != GTF_OP_RESHAPE && p.tensors[o.in[0]].dtype == GTF_U8)
       return bad("transpose/concat of u8");
   }
   // ---- domain (a gather's input is addressed through it, not broadcast)
@@ -523,7 +575,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   std::set<int> touched;
   for (int i : ops) {
     const OpInfo& o = p.ops[i];
-    if (!is_gather(o.opcode))
+    if (!is_gather(o))
       for (int k = 0; k < o.n_in; ++k) touched.insert(o.in[k]);
     touched.insert(o.out);
   }
@@ -626,7 +678,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   std::set<int> ext_in;
   for (int i : ops)
     for (int k = 0; k < p.ops[i].n_in; ++k)
-      if (!produced.count(p.ops[i].in[k])) ext_in.insert(p.ops[i].in[k]);
+      if (!produced.count(p.ops[i].in[k])) ext_in.insert(source_of(p.ops[i].in[k]));
   for (int t : ext_in) slot_for(t);
   for (int t : outputs) slot_for(t);
   if ((int)slots.size() > kMaxSlots) return bad("too many external tensors");
@@ -690,7 +742,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   };
   for (int i : ops) {
     const OpInfo& o = p.ops[i];
-    if (is_gather(o.opcode) || absorbed.count(i)) continue;  // loaded addressed / not emitted
+    if (is_gather(o) || absorbed.count(i)) continue;  // loaded addressed / not emitted
     const int c = op_cls(i);
     for (int k = 0; k < o.n_in; ++k) {
       const int t = o.in[k];
@@ -713,7 +765,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   // load an external [1,1] scalar)
   for (int i : ops) {
     int c = op_cls(i);
-    if (c == CLS_E || is_gather(p.ops[i].opcode)) continue;
+    if (c == CLS_E || is_gather(p.ops[i])) continue;
     const OpInfo& o = p.ops[i];
     for (int k = 0; k < o.n_in; ++k) {
       int ci = cls_of(o.in[k]);
@@ -774,7 +826,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
   for (int i : ops) {
     const OpInfo& o = p.ops[i];
     auto& L = mops_of[i];
-    if (is_gather(o.opcode)) {
+    if (is_gather(o)) {
       // the source's element for domain position (r, c), by the op's own
       // index map; a plain load when that map is the value's own layout
       MOp m;
@@ -789,16 +841,25 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
         if (ct == CLS_COL) return {0, 1};
         return {Rt == 1 ? 0 : 1, 0};
       };
-      if (o.opcode == GTF_OP_CONCAT) {
+      if (is_join(o)) {
         if (ct == CLS_ROW) return bad("concat of per-row values");
         const TensorInfo& a = p.tensors[o.in[0]];
-        const TensorInfo& b = p.tensors[o.in[1]];
+        // each side from memory at its own layout, or through a folded move
+        auto side = [&](int t) -> std::pair<int, std::pair<int64_t, int64_t>> {
+          auto f = fold.find(t);
+          if (f != fold.end()) return f->second;
+          const TensorInfo& ti = p.tensors[t];
+          return {t, {ti.R == 1 ? 0 : ti.C, 1}};
+        };
+        const auto sa = side(o.in[0]), sb = side(o.in[1]);
+        if (sa.first == sb.first && sa.second != sb.second) return bad("one tensor read at two layouts");
         m.gkind = 2;
-        m.src[1] = o.in[1];
+        m.src[0] = sa.first;
+        m.src[1] = sb.first;
         m.imm = (float)a.C;
         if (a.C > (1 << 24)) return bad("concat split column beyond fp32 integers");
-        gather_stride[o.in[0]] = {a.R == 1 ? 0 : a.C, 1};
-        gather_stride[o.in[1]] = {b.R == 1 ? 0 : b.C, 1};
+        gather_stride[sa.first] = sa.second;
+        gather_stride[sb.first] = sb.second;
       } else if (o.opcode == GTF_OP_TRANSPOSE && ct == CLS_E) {
         // T[r][c] = X[c][r]: X is [C, R] in domain terms.  One such source
         // of a group without reductions is staged per item in LDS, read in
@@ -820,7 +881,7 @@ bool compile_group(const FusePlan& p, const std::vector<int>& ops, CompiledGroup
       L.push_back(m);
       continue;
     }
-    if (o.opcode == GTF_OP_COPY) {
+    if (o.opcode == GTF_OP_COPY || o.opcode == GTF_OP_CONCAT) {  // (a concat of one tuple)
       MOp m;
       m.kind = 4;
       m.form = 0;
@@ -1286,7 +1347,9 @@ void annotate(FusePlan* p) {
       o.pattern = GTF_PAT_OPAQUE;
     } else if (is_reduce(o.opcode)) {
       o.pattern = GTF_PAT_COMM_REDUCE;
-    } else if (o.opcode == GTF_OP_COPY || is_gather(o.opcode)) {
+    } else if (o.opcode == GTF_OP_TUPLE) {
+      o.pattern = GTF_PAT_TUPLE;
+    } else if (o.opcode == GTF_OP_COPY || o.opcode == GTF_OP_CONCAT || is_gather(o)) {
       o.pattern = GTF_PAT_INJECTIVE;
     } else {
       const TensorInfo& to = p->tensors[o.out];
@@ -1333,9 +1396,11 @@ std::vector<std::vector<int>> partition_groups(const FusePlan& pl, bool fuse, bo
           for (int s : rd[v]) stack.push_back(s);
         }
         bool ok;
-        if (src <= GTF_PAT_BROADCAST)
+        if (p->ops[d].opcode == GTF_OP_TUPLE)  // phase 2: fields into a tuple already fused onward
+          ok = phase == 2 && src <= GTF_PAT_INJECTIVE && uf.find(d) != d && path_ok;
+        else if (src <= GTF_PAT_BROADCAST)
           ok = path_ok && sink <= GTF_PAT_COMM_REDUCE;
-        else if (src == GTF_PAT_INJECTIVE && phase >= 1)
+        else if ((src == GTF_PAT_INJECTIVE || src == GTF_PAT_TUPLE) && phase >= 1)
           ok = path_ok && sink <= GTF_PAT_INJECTIVE;
         else
           ok = false;

@@ -96,9 +96,22 @@ enum {
  *                  reshape: any shape -> the declared shape of the same
  *                  element count, row-major order kept;
  *                  concat (n_in 2): [R, C1] ++ [R, C2] -> [R, C1 + C2]
- *                  along the last axis (rank 2, C1, C2 >= 1, one dtype).
+ *                  along the last axis (rank 2, C1, C2 >= 1, one dtype);
+ *                  concat (n_in 1) of a tuple: its fields along the last
+ *                  axis.
  *                  Inside a group these run as addressed loads: their
- *                  inputs come from memory.
+ *                  inputs come from memory, or, for a concat or a tuple,
+ *                  from a transpose or reshape of a tensor in memory that
+ *                  nothing else reads and that keeps its dtype (folded
+ *                  into the load's addressing).
+ * tuple (kTuple, TVM "Operator Pattern Classification"; n_in 2): the
+ *                  fields [R, C1], [R, C2] (rank 2, one dtype), declared
+ *                  [R, C1 + C2]: a tuple's value is its fields side by
+ *                  side, so a concat of it is that value.  Read only by
+ *                  concats (n_in 1) and never a graph output.  A tuple
+ *                  fuses into the concat that reads it in phase 1, and
+ *                  producers of its fields no more complex than injective
+ *                  join that group in phase 2 (TVM "Fusion rules").
  * add/sub/mul/div/max/min/add3/dmul broadcast their operands; sqrt and
  * div are correctly rounded; no multiply-add is ever contracted. */
 enum {
@@ -110,7 +123,7 @@ enum {
   GTF_OP_MAX = 36, GTF_OP_MIN = 37,
   GTF_OP_ADD3 = 48, GTF_OP_DMUL = 49,
   GTF_OP_ROW_SUM = 64, GTF_OP_ROW_MEAN = 65, GTF_OP_ROW_MAX = 66,
-  GTF_OP_TRANSPOSE = 80, GTF_OP_RESHAPE = 81, GTF_OP_CONCAT = 82
+  GTF_OP_TRANSPOSE = 80, GTF_OP_RESHAPE = 81, GTF_OP_CONCAT = 82, GTF_OP_TUPLE = 83
 };
 
 #define GTF_OPF_OPAQUE 1 /* op flag: force OpPatternKind kOpaque (a barrier) */

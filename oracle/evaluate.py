@@ -59,7 +59,9 @@ def result_shape(op: str, in_shapes, declared=None) -> Tuple[int, int]:
         if declared[0] * declared[1] != in_shapes[0][0] * in_shapes[0][1]:
             raise ValueError(f"reshape of {in_shapes[0]} to {declared}")
         return declared
-    if op == "concat":
+    if op == "concat" and len(in_shapes) == 1:   # the concat of one tuple
+        return in_shapes[0]
+    if op in ("concat", "tuple"):
         (r1, c1), (r2, c2) = in_shapes
         if r1 != r2:
             raise ValueError(f"concat of {in_shapes}: row counts differ")

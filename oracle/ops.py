@@ -90,8 +90,12 @@ def apply(op: str, args, imm: float = 0.0, shape=None) -> np.ndarray:
             r = a[0].T.copy()
         elif op == "reshape":
             r = a[0].reshape(shape).copy()   # row-major element order kept
-        elif op == "concat":
+        elif op == "tuple":
+            # a tuple's fields, held as one [R, C1 + C2] value whose only
+            # reader is the concat of that tuple
             r = np.concatenate([a[0], a[1]], axis=1)
+        elif op == "concat":
+            r = np.concatenate(a, axis=1)   # two tensors, or the one tuple
         elif op == "exp":
             r = exp(a[0])
         elif op == "tanh":

@@ -5,9 +5,12 @@ Follows Apache TVM, "Operator Fusion" (docs/arch/fusion.rst), in its order:
 
 1. Annotate (section "Operator Pattern Classification", the OpPatternKind
    table): kElemWise 0 when every operand has the result's shape,
-   kBroadcast 1 when some operand is broadcast, kInjective 2 for copy,
-   kCommReduce 3 for the row reductions, kOpaque 8 when forced.  A group's
-   pattern is the max over its members (CombinePattern).
+   kBroadcast 1 when some operand is broadcast, kInjective 2 for copy
+   and the moves, kCommReduce 3 for the row reductions, kTuple 7 for a
+   tuple, kOpaque 8 when forced.  A group's pattern is the max over its
+   members (CombinePattern), a tuple that has fused into a later group
+   counting as kInjective there (the table: a tuple fuses into the
+   injective ops after it).
 2. Forward graph (section "Algorithm", step 1): one node per op, an edge
    from an op to every op that reads its output.
 3. Post-dominators (step 2): here from their definition, not from the LCA
@@ -21,10 +24,14 @@ Follows Apache TVM, "Operator Fusion" (docs/arch/fusion.rst), in its order:
    picks the rule:
      <= kBroadcast : every node strictly between n and d on any path is
                      <= kInjective, and d's group is <= kCommReduce;
-     kInjective    : (phase 1 and later) everything on the paths and d's
-                     group are <= kInjective;
+     kInjective, kTuple : (phase 1 and later) everything on the paths and
+                     d's group are <= kInjective;
      kCommReduce   : never initiates (reductions are sinks only);
      kOpaque       : never fuses (a barrier).
+   A post-dominator that is a tuple takes fields only by phase 2's rule:
+   in phase 2, a node <= kInjective whose d is a tuple that has already
+   fused into a later group (its group's root is no longer the tuple)
+   fuses when every node on the paths is <= kInjective.
    Limits: at most 256 ops per group (kMaxFusedOps) and at most
    MAX_GROUP_ARGS external tensors per group (the page names an argument
    limit without its value; 16 is the reading taken here).  CommitFuse puts
@@ -35,7 +42,8 @@ pattern; path nodes are judged by their own pattern; a node whose output
 is a graph output has no post-dominator.
 
 Injective ops that move elements (transpose, reshape, concat; kInjective
-in the page's table) fuse by the same phases.
+in the page's table) fuse by the same phases.  A tuple (kTuple) holds two
+fields; its only reader is a concat of that tuple alone.
 
 Row-resident extension (opt-in, row_resident=True; beyond the page, whose
 fusion rules keep a reduction as the last op of its group): after the
@@ -96,6 +104,8 @@ def pattern(graph, i: int) -> int:
         return K_OPAQUE
     if o.op in _REDUCES:
         return K_COMM_REDUCE
+    if o.op == "tuple":
+        return K_TUPLE
     if o.op in ("copy",) + MOVES:
         return K_INJECTIVE
     out = norm_shape(graph.tensors[o.output].shape)
@@ -184,7 +194,8 @@ class _UnionFind:
         if rx == rt:
             return
         self.parent[rx] = rt
-        self.pat[rt] = max(self.pat[rt], self.pat[rx])
+        # a tuple fused into the group after it is an injective member there
+        self.pat[rt] = max(self.pat[rt], K_INJECTIVE if self.pat[rx] == K_TUPLE else self.pat[rx])
         self.size[rt] += self.size[rx]
 
 
@@ -246,10 +257,14 @@ def partition(graph, fuse: bool = True, row_resident: bool = False,
                 src_pat = uf.pat[uf.find(i)]
                 sink_pat = uf.pat[uf.find(d)]
                 mid = _between(succ, pred, i, d)
-                if src_pat <= K_BROADCAST:
+                if graph.ops[d].op == "tuple":
+                    # phase 2: into a tuple already fused into a later group
+                    ok = (phase == 2 and src_pat <= K_INJECTIVE and uf.find(d) != d
+                          and all(pats[m] <= K_INJECTIVE for m in mid))
+                elif src_pat <= K_BROADCAST:
                     ok = (all(pats[m] <= K_INJECTIVE for m in mid)
                           and sink_pat <= K_COMM_REDUCE)
-                elif src_pat == K_INJECTIVE and phase >= 1:
+                elif src_pat in (K_INJECTIVE, K_TUPLE) and phase >= 1:
                     ok = (all(pats[m] <= K_INJECTIVE for m in mid)
                           and sink_pat <= K_INJECTIVE)
                 else:

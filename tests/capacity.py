@@ -33,9 +33,16 @@ The executor (kernels.hip, isa.h) runs a group on one [R,C] domain:
     between them are not run;
   * at most MAX_SLOTS tensors in memory, MAX_LDS_ROW per-row and
     MAX_LDS_COL per-column operands held in LDS;
-  * a transpose, reshape or concat is an addressed load of a tensor in
-    memory: its inputs are not made in the group and no other op of the
-    group reads them, and a concat of column values is not run.
+  * a transpose, reshape, tuple or concat of two tensors is an addressed
+    load of tensors in memory: its inputs are not made in the group and no
+    other op of the group reads them (nor their sources, below), a join (a
+    tuple or a concat of two) of column values is not run, and no move
+    reads a u8 tensor except a reshape;
+  * a transpose or reshape whose value only a join of the group reads,
+    that is no graph output and keeps its source's dtype, is folded into
+    that join: the join reads the move's source at the move's addressing
+    (one source at two addressings is not run), and the move is not run;
+  * a concat of one tuple is a copy of the tuple's value.
 """
 from __future__ import annotations
 
@@ -49,21 +56,68 @@ MAX_SLOTS = 16
 MAX_LDS_ROW = 8
 MAX_LDS_COL = 4
 REDUCES = ("row_sum", "row_mean", "row_max")
-GATHERS = ("transpose", "reshape", "concat")
 
 
-def gathers_ok(graph, members: Set[int]) -> bool:
-    """A transpose, reshape or concat runs inside a group only as a load:
-    its inputs come from memory and no other op of the group reads them."""
+def is_join(o) -> bool:
+    return o.op == "tuple" or (o.op == "concat" and len(o.inputs) == 2)
+
+
+def is_gather(o) -> bool:
+    return o.op in ("transpose", "reshape") or is_join(o)
+
+
+def folded(graph, members: Set[int]):
+    """The moves folded into a join of the group: ({moved value: (source,
+    (row stride, column stride))}, the members left to run)."""
+    made = {graph.ops[i].output for i in members}
+    fold, kept = {}, set()
+    for i in sorted(members):
+        o = graph.ops[i]
+        if (o.op in ("transpose", "reshape") and o.inputs[0] not in made
+                and graph.tensors[o.output].role != "out"
+                and graph.tensors[o.inputs[0]].dtype == graph.tensors[o.output].dtype):
+            readers = [j for j, q in enumerate(graph.ops) for t in q.inputs if t == o.output]
+            if len(readers) == 1 and readers[0] in members and is_join(graph.ops[readers[0]]):
+                x = o.inputs[0]
+                if o.op == "transpose":
+                    st = (1, norm_shape(graph.tensors[x].shape)[1])
+                else:
+                    r, c = norm_shape(graph.tensors[o.output].shape)
+                    st = (0 if r == 1 else c, 1)
+                fold[o.output] = (x, st)
+                continue
+        kept.add(i)
+    return fold, kept
+
+
+def gathers_ok(graph, members: Set[int], fold) -> bool:
+    """A move or a join runs inside a group only as a load: its inputs come
+    from memory and no other op of the group reads them or their sources;
+    a join reads each source at one addressing."""
     produced = {graph.ops[i].output for i in members}
+
+    def src(t):
+        return fold[t][0] if t in fold else t
+
+    def side(t):
+        if t in fold:
+            return fold[t]
+        r, c = norm_shape(graph.tensors[t].shape)
+        return (t, (0 if r == 1 else c, 1))
     for i in members:
         o = graph.ops[i]
-        if o.op not in GATHERS:
+        if not is_gather(o):
             continue
         for t in o.inputs:
             if t in produced:
                 return False
-            if any(t in graph.ops[j].inputs for j in members if j != i):
+            if any(u == t or src(u) == src(t) for j in members if j != i for u in graph.ops[j].inputs):
+                return False
+        if o.op != "reshape" and graph.tensors[o.inputs[0]].dtype == "u8":
+            return False
+        if is_join(o):
+            (sa, la), (sb, lb) = side(o.inputs[0]), side(o.inputs[1])
+            if sa == sb and la != lb:
                 return False
     return True
 
@@ -109,13 +163,14 @@ def layout(graph, members: Set[int]):
     """The executor's layout of an op set, or None when it cannot run it:
     {"stages": n, "row_slots": LDS per-row operands, "col_slots": LDS
     per-column operands, "slots": tensors in memory}."""
+    fold, members = folded(graph, members)
     ms = sorted(members)
-    if not gathers_ok(graph, members):
+    if not gathers_ok(graph, members, fold):
         return None
     produced = {graph.ops[i].output: i for i in ms}
     touched = set()
     for i in ms:
-        if graph.ops[i].op not in GATHERS:   # a gather's input is addressed, not broadcast
+        if not is_gather(graph.ops[i]):   # a gather's input is addressed, not broadcast
             touched.update(graph.ops[i].inputs)
         touched.add(graph.ops[i].output)
     shape = {t: norm_shape(graph.tensors[t].shape) for t in touched}
@@ -133,8 +188,8 @@ def layout(graph, members: Set[int]):
     reds = [i for i in ms if graph.ops[i].op in REDUCES]
     if any(shape[graph.ops[i].inputs[0]] != (R, C) for i in reds):
         return None
-    # a transpose or concat of a full-domain value addresses rows and columns
-    gathers2d = any(graph.ops[i].op in ("transpose", "concat") for i in ms)
+    # a transpose or a join of full-domain values addresses rows and columns
+    gathers2d = any(is_gather(graph.ops[i]) and graph.ops[i].op != "reshape" for i in ms)
     flat = not reds and not gathers2d and all(shape[t] == (R, C) for t in touched)
 
     def cls(t):
@@ -152,10 +207,10 @@ def layout(graph, members: Set[int]):
     for j, o in enumerate(graph.ops):
         if j not in members:
             outside.update(t for t in o.inputs if t in produced)
-    ext = {t for i in ms for t in graph.ops[i].inputs if t not in produced}
-    for i in ms:   # a concat of column values would stage two slots in the column phase
+    ext = {fold[t][0] if t in fold else t for i in ms for t in graph.ops[i].inputs if t not in produced}
+    for i in ms:   # a join of column values would stage two slots in the column phase
         o = graph.ops[i]
-        if o.op == "concat" and cls(o.output) == "ROW":
+        if is_join(o) and cls(o.output) == "ROW":
             return None
     ext |= {t for t in produced if graph.tensors[t].role == "out" or t in outside}
     if len(ext) > MAX_SLOTS:
@@ -189,7 +244,7 @@ def layout(graph, members: Set[int]):
     for i in ms:
         o = graph.ops[i]
         c = op_cls(i)
-        if o.op in GATHERS or i in absorbed:
+        if is_gather(o) or i in absorbed:
             continue
         for t in o.inputs:
             if c == "E":
@@ -205,7 +260,7 @@ def layout(graph, members: Set[int]):
         return None
     for i in ms:
         c = op_cls(i)
-        if c == "E" or graph.ops[i].op in GATHERS:
+        if c == "E" or is_gather(graph.ops[i]):
             continue
         for t in graph.ops[i].inputs:
             if cls(t) == c:

@@ -94,9 +94,8 @@ def _propagate(op, a, b, imm, out_shape):
             p = np.asarray(b[0]).T
         elif op in ("reshape",):
             p = np.broadcast_to(b[0], a[0].shape).reshape(out_shape)
-        elif op == "concat":
-            p = np.concatenate([np.broadcast_to(b[0], a[0].shape), np.broadcast_to(b[1], a[1].shape)],
-                               axis=1)
+        elif op in ("concat", "tuple"):
+            p = np.concatenate([np.broadcast_to(b[k], a[k].shape) for k in range(len(a))], axis=1)
         else:
             raise ValueError(op)
     return 2.0 * np.broadcast_to(p, out_shape)

@@ -476,11 +476,104 @@ def test_gather_plans_match_the_oracle():
             plan = gtf.FusePlan(g, **kw)
             want = cap.partition(g, **kw)
             assert as_sets(plan.groups()) == as_sets(want), [(o.op, o.inputs, o.output) for o in g.ops]
-            n_fused += any(len(grp) > 1 and any(g.ops[i].op in cap.GATHERS for i in grp) for grp in want)
+            n_fused += any(len(grp) > 1 and any(cap.is_gather(g.ops[i]) for i in grp) for grp in want)
         plan = gtf.FusePlan(g, duplicate=True)
         g2, origin = opart.duplicate(g, feasible=cap.group_ok)
         assert plan.op_origin() == origin and as_sets(plan.groups()) == as_sets(cap.partition(g2))
     assert n_fused >= 30
+
+
+def _tuple_dags(seed, count, R=3, Ca=5, Cb=2):
+    """Random graphs around a tuple and the concat of it (TVM's kTuple):
+    fields read straight from inputs or made by a transpose, a reshape or an
+    element op, moves that change the dtype or whose value is also a graph
+    output; the concat stored, scaled, added to a reshaped input, summed per
+    row, or the first field of a second tuple."""
+    rng = np.random.default_rng(seed)
+    for _ in range(count):
+        g = Graph()
+        dt = ["f32", "bf16"][int(rng.integers(2))]
+        other = "bf16" if dt == "f32" else "f32"
+        n = [0]
+
+        def name():
+            n[0] += 1
+            return f"t{n[0]}"
+
+        def field(C):
+            k = int(rng.integers(7))
+            if k == 0:
+                return g.input(name(), dt, (R, C))
+            if k in (1, 2):
+                return g.op("transpose", [g.input(name(), dt, (C, R))], name(), dt, (R, C))
+            if k == 3:
+                return g.op("reshape", [g.input(name(), dt, (C, R))], name(), dt, (R, C))
+            if k == 4:
+                return g.op("exp", [g.input(name(), dt, (R, C))], name(), dt, (R, C))
+            if k == 5:   # changes the dtype
+                return g.op("transpose", [g.input(name(), other, (C, R))], name(), dt, (R, C))
+            return g.op("transpose", [g.input(name(), dt, (C, R))], name(), dt, (R, C), role="out")
+
+        a, b = field(Ca), field(Cb)
+        W = Ca + Cb
+        c = g.op("concat", [g.op("tuple", [a, b], name(), dt, (R, W))], name(), dt, (R, W))
+        k = int(rng.integers(5))
+        if k == 0:
+            d = g.tensors[c]
+            g.tensors[c] = TensorDesc(d.name, d.dtype, d.shape, "out")
+        elif k == 1:
+            g.op("mul_imm", [c], name(), dt, (R, W), role="out", imm=0.5)
+        elif k == 2:
+            r = g.op("reshape", [g.input(name(), dt, (W, R))], name(), dt, (R, W))
+            g.op("add", [c, r], name(), dt, (R, W), role="out")
+        elif k == 3:
+            g.op("row_sum", [c], name(), "f32", (R, 1), role="out")
+        else:
+            e = field(Cb)
+            c2 = g.op("concat", [g.op("tuple", [c, e], name(), dt, (R, W + Cb))], name(), dt, (R, W + Cb))
+            g.op("neg", [c2], name(), dt, (R, W + Cb), role="out")
+        yield g
+
+
+def test_tuple_plans_match_the_oracle():
+    """Plans with tuples: the library's groups equal the oracle's (the tuple
+    into its concat in phase 1, its fields into it in phase 2, moves folded
+    into the join), with and without the row-resident merge and duplicate
+    fusion; in most graphs a move joins its tuple's group."""
+    n_phase2 = 0
+    for g in _tuple_dags(81, 300):
+        for kw in ({}, {"row_resident": True}):
+            plan = gtf.FusePlan(g, **kw)
+            want = cap.partition(g, **kw)
+            assert as_sets(plan.groups()) == as_sets(want), [(o.op, o.inputs, o.output) for o in g.ops]
+        tup = [i for i, o in enumerate(g.ops) if o.op == "tuple"]
+        n_phase2 += any(g.ops[j].op in ("transpose", "reshape") and
+                        any(j in grp and tup[0] in grp for grp in want) for j in range(len(g.ops)))
+        plan = gtf.FusePlan(g, duplicate=True)
+        g2, origin = opart.duplicate(g, feasible=cap.group_ok)
+        assert plan.op_origin() == origin and as_sets(plan.groups()) == as_sets(cap.partition(g2))
+    assert n_phase2 >= 100, n_phase2
+
+
+def test_tuple_and_concat_of_one_operand_errors():
+    """A tuple is an intermediate read only by a concat of it alone; a
+    concat of one operand reads a tuple and is declared as its shape."""
+    a, b = T("a", "f32", (2, 3), "in"), T("b", "f32", (2, 1), "in")
+    tup, cat = T("u", "f32", (2, 4), "tmp"), T("c", "f32", (2, 4), "out")
+    ok_ops = [OpDesc("tuple", (0, 1), 2), OpDesc("concat", (2,), 3)]
+    assert _desc_status([a, b, tup, cat], ok_ops) == C.GTF_OK
+    # a tuple as a graph output, or read by another op
+    assert _desc_status([a, b, T("u", "f32", (2, 4), "out")], [OpDesc("tuple", (0, 1), 2)]) == C.GTF_E_INVALID
+    assert _desc_status([a, b, tup, cat], [OpDesc("tuple", (0, 1), 2), OpDesc("neg", (2,), 3)]) == C.GTF_E_INVALID
+    # a concat of one tensor that is not a tuple
+    assert _desc_status([T("x", "f32", (2, 4), "in"), cat], [OpDesc("concat", (0,), 1)]) == C.GTF_E_INVALID
+    # a concat of a tuple declared at another shape or dtype
+    assert _desc_status([a, b, tup, T("c", "f32", (2, 5), "out")], ok_ops) == C.GTF_E_SHAPE
+    assert _desc_status([a, b, tup, T("c", "bf16", (2, 4), "out")], ok_ops) == C.GTF_E_SHAPE
+    # tuple shapes and dtypes follow concat's
+    assert _desc_status([a, T("b", "f32", (3, 1), "in"), tup, cat], ok_ops) == C.GTF_E_SHAPE
+    assert _desc_status([a, T("b", "bf16", (2, 1), "in"), tup, cat], ok_ops) == C.GTF_E_UNSUPPORTED
+    assert _desc_status([a, b, T("u", "bf16", (2, 4), "tmp"), cat], ok_ops) == C.GTF_E_UNSUPPORTED
 
 
 def test_new_entry_point_errors():

@@ -1125,6 +1125,37 @@ def test_random_gather_dags():
     assert n >= 300
 
 
+@pytest.mark.parametrize("shape", [(3, 5, 2), (40, 24, 7), (96, 64, 33), (1, 1, 1)])
+def test_random_tuple_dags(shape):
+    """Graphs around a tuple and the concat of it, fused (the moves folded
+    into the concat load) and unfused, against the oracle under the same
+    grouping."""
+    from tests.test_capi_host import _tuple_dags
+    for gi, g in enumerate(_tuple_dags(83, 60, *shape)):
+        announce("tuple dag", gi, shape, [(o.op, o.inputs) for o in g.ops])
+        _check_graph(g, _inputs_for(g, 1900 + gi))
+
+
+@pytest.mark.parametrize("rows,c1,c2", [(2048, 1024, 512), (4096, 48, 16), (37, 5, 130), (3, 1, 1)])
+def test_tuple_of_transposes_bit_exact(rows, c1, c2):
+    """y = 0.5 * concat((transpose(X), transpose(Y))) in one launch, bit for
+    bit: the fields are read through the concat load at the transposes'
+    addressing."""
+    g = Graph()
+    X = g.input("X", "f32", (c1, rows))
+    Y = g.input("Y", "f32", (c2, rows))
+    a = g.op("transpose", [X], "a", "f32", (rows, c1))
+    b = g.op("transpose", [Y], "b", "f32", (rows, c2))
+    t = g.op("tuple", [a, b], "t", "f32", (rows, c1 + c2))
+    c = g.op("concat", [t], "c", "f32", (rows, c1 + c2))
+    g.op("mul_imm", [c], "y", "f32", (rows, c1 + c2), role="out", imm=0.5)
+    ins = _inputs_for(g, 970)
+    plan, got = gpu_run(g, ins)
+    assert plan.num_groups == 1
+    _, want = oracle_run(g, ins)
+    assert_bits_equal(got[_out(g)], want[_out(g)])
+
+
 @pytest.mark.parametrize("rows,cols", [(4096, 1024), (1000, 37), (1, 64), (64, 1)])
 def test_transpose_bias_gelu_group(rows, cols):
     """y = gelu(transpose(X) + b) in one launch: the transpose is an

@@ -491,3 +491,66 @@ def test_injective_ops_fuse_by_the_phase_rules():
     t = g.op("transpose", [x], "t", "f32", (4, 4))
     g.op("add", [t, x], "y", "f32", (4, 4), role="out")
     assert as_sets(pt.partition(g)) == [[0, 1]]
+
+
+# ---------------------------------------------------------------- tuples (kTuple)
+def _tuple_graph(field="transpose", concat_opaque=False, tail="mul_imm"):
+    """y = f(concat((a, b))) with a, b fields made from inputs X [5,3] and
+    Y [2,3] by `field` (transpose, or exp of [3,5] / [3,2] inputs)."""
+    g = Graph()
+    if field == "transpose":
+        a = g.op("transpose", [g.input("X", "f32", (5, 3))], "a", "f32", (3, 5))
+        b = g.op("transpose", [g.input("Y", "f32", (2, 3))], "b", "f32", (3, 2))
+    else:
+        a = g.op("exp", [g.input("X", "f32", (3, 5))], "a", "f32", (3, 5))
+        b = g.op("transpose", [g.input("Y", "f32", (2, 3))], "b", "f32", (3, 2))
+    t = g.op("tuple", [a, b], "t", "f32", (3, 7))
+    c = g.op("concat", [t], "c", "f32", (3, 7), opaque=concat_opaque)
+    if tail == "mul_imm":
+        g.op("mul_imm", [c], "y", "f32", (3, 7), role="out", imm=0.5)
+    else:   # a reshaped input added after the concat, listed after it
+        r = g.op("reshape", [g.input("V", "f32", (7, 3))], "r", "f32", (3, 7))
+        g.op("add", [c, r], "y", "f32", (3, 7), role="out")
+    return g
+
+
+def test_tuple_values_and_pattern():
+    """A tuple's value is its fields side by side and the concat of it is
+    that value; the table makes a tuple kTuple (7)."""
+    from oracle import evaluate as oev
+    g = _tuple_graph()
+    xs = np.arange(15, dtype=np.float32).reshape(5, 3)
+    ys = 100 + np.arange(6, dtype=np.float32).reshape(2, 3)
+    out = oev.outputs(g, oev.evaluate(g, {0: xs, 2: ys}))[g.outputs()[0]]
+    for i in range(3):
+        assert list(out[i]) == [0.5 * v for v in list(xs[:, i]) + list(ys[:, i])]
+    assert [pt.pattern(g, i) for i in range(5)] == [pt.K_INJECTIVE, pt.K_INJECTIVE, pt.K_TUPLE,
+                                                    pt.K_INJECTIVE, pt.K_ELEMWISE]
+
+
+def test_tuple_fuses_into_its_concat_and_its_fields_follow_in_phase_two():
+    # the tuple fuses into the injective concat after it (phase 1), the
+    # concat into the scaling; then the transposes, whose post-dominator
+    # is the tuple, join the tuple's group in phase 2
+    assert as_sets(pt.partition(_tuple_graph())) == [[0, 1, 2, 3, 4]]
+    # an opaque concat keeps the tuple out of any later group, so phase 2
+    # has no absorbed tuple to fuse the fields into
+    assert as_sets(pt.partition(_tuple_graph(concat_opaque=True))) == [[0], [1], [2], [3], [4]]
+    # phase 2 takes any field no more complex than injective: by the rules
+    # the exp joins too ...
+    g = _tuple_graph(field="exp")
+    assert as_sets(pt.partition(g)) == [[0, 1, 2, 3, 4]]
+    # ... while the executor reads a join's fields from memory, so with its
+    # capacity the exp stays a group of its own
+    from tests import capacity as cap
+    assert as_sets(cap.partition(g)) == [[0], [1, 2, 3, 4]]
+
+
+def test_a_group_holding_an_absorbed_tuple_counts_as_injective():
+    """The reshape after the concat is visited in phase 1 after the tuple
+    fused onward: its post-dominator's group then holds the tuple as an
+    injective member, so the reshape (injective) fuses.  Were the tuple's
+    kTuple kept in the group's combined pattern, the reshape would stay
+    alone."""
+    g = _tuple_graph(tail="reshape")
+    assert as_sets(pt.partition(g)) == [[0, 1, 2, 3, 4, 5]]

@@ -5,7 +5,8 @@ lead to a value).  A wrong register, spill slot, LDS slot, form or stage in
 a compiled program changes a result here, on the CPU, before any launch:
 the workloads at small shapes, every DAG of two ops, random DAGs over
 every opcode, broadcast and row-resident groups, duplicated producers,
-explicit groupings and the addressed loads (transpose, concat, reshape)."""
+explicit groupings, the addressed loads (transpose, concat, reshape) and
+tuples with their moves folded into the concat load."""
 import numpy as np
 import pytest
 
@@ -227,3 +228,32 @@ def test_transpose_concat_and_reshape_groups():
     r = k.op("reshape", [x], "r", "f32", (135, 37))
     k.op("add", [r, k.input("v", "f32", (135, 1))], "y", "f32", (135, 37), role="out")
     check(k, _inputs_for(k, 961))
+
+
+@pytest.mark.parametrize("shape", [(3, 5, 2), (40, 24, 7), (7, 130, 1), (1, 1, 1), (96, 64, 33)])
+def test_random_tuple_dags(shape):
+    from tests.test_capi_host import _tuple_dags
+    for gi, g in enumerate(_tuple_dags(82, 60, *shape)):
+        ins = _inputs_for(g, 1900 + gi)
+        check(g, ins)
+        check(g, ins, fuse=False)
+
+
+def test_tuple_of_transposes_is_one_concat_load():
+    """concat((transpose(X), transpose(Y))) scaled: one group whose program
+    reads both fields through one concat load at the transposes'
+    addressing; neither transpose runs on its own."""
+    g = Graph()
+    X = g.input("X", "bf16", (24, 40))
+    Y = g.input("Y", "bf16", (9, 40))
+    a = g.op("transpose", [X], "a", "bf16", (40, 24))
+    b = g.op("transpose", [Y], "b", "bf16", (40, 9))
+    t = g.op("tuple", [a, b], "t", "bf16", (40, 33))
+    c = g.op("concat", [t], "c", "bf16", (40, 33))
+    g.op("mul_imm", [c], "y", "bf16", (40, 33), role="out", imm=0.5)
+    plan = check(g, _inputs_for(g, 1950))
+    assert plan.num_groups == 1
+    names = [NAME[f] for f, _, _ in plan.code(0)["instr"]]
+    assert names[0] == "LDC_BF16_A" and not any(n.startswith("LDG") or n == "LDT_A" for n in names), names
+    code = plan.code(0)
+    assert sorted(zip(code["rstride"], code["cstride"]))[:2] == [(1, 40), (1, 40)]

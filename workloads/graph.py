@@ -29,8 +29,10 @@ OP_ARITY = {
     "row_sum": 1, "row_mean": 1, "row_max": 1,
     # injective data movement: [R,C] -> [C,R]; any shape to any shape of
     # the same element count (row-major order kept); [R,C1] ++ [R,C2] along
-    # the last axis
-    "transpose": 1, "reshape": 1, "concat": 2,
+    # the last axis.  A tuple groups two [R,Ci] fields; its one reader is a
+    # concat of that tuple alone (one input), which joins the fields the
+    # same way.  Concat takes two tensors or one tuple.
+    "transpose": 1, "reshape": 1, "concat": 2, "tuple": 2,
 }
 
 
