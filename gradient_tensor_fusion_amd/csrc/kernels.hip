@@ -1251,7 +1251,9 @@ template __global__ void exec_kernel<1, kNS, false>(const ExecArgs a);
 // copied to or from its place in its bucket, times the scale.  The side that
 // lives in the bucket is usually not 16-byte aligned (offsets are dense), so
 // a few head elements bring the destination to a 16-byte boundary, the body
-// moves 16 bytes per lane per step, and a tail finishes.
+// moves 16 bytes per lane per step, and a tail finishes.  The body's loads
+// and stores are nontemporal: every byte is read once and written once (on
+// this part nontemporal stores took the C5 buckets from 5.3 to 5.7 TB/s).
 template <typename T>
 __device__ __forceinline__ T scale_elem(T v, float s, bool one);
 
@@ -1308,9 +1310,15 @@ __device__ __forceinline__ void move_run(T* __restrict__ dst, const T* __restric
 #pragma unroll
     for (int j = 0; j < kU; ++j) w[j] = load16(q + (size_t)(u + j * kBlock) * per16);
 #pragma unroll
-    for (int j = 0; j < kU; ++j) *(uint4*)(d + (size_t)(u + j * kBlock) * per16) = scale_vec<T>(w[j], s, one);
+    for (int j = 0; j < kU; ++j) {
+      const uint4 o = scale_vec<T>(w[j], s, one);
+      __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, (v4u*)(d + (size_t)(u + j * kBlock) * per16));
+    }
   }
-  for (; u < body; u += kBlock) *(uint4*)(d + (size_t)u * per16) = scale_vec<T>(load16(q + (size_t)u * per16), s, one);
+  for (; u < body; u += kBlock) {
+    const uint4 o = scale_vec<T>(load16(q + (size_t)u * per16), s, one);
+    __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, (v4u*)(d + (size_t)u * per16));
+  }
   const int done = head + body * per16;
   const int tail = n - done;
   if (tid < tail) dst[done + tid] = scale_elem<T>(src[done + tid], s, one);
