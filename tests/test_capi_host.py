@@ -367,7 +367,7 @@ def test_grouped_plans_agree_with_the_oracle_rule():
     rng = np.random.default_rng(77)
     graphs = list(_f32_reduce_dags(61, 150)) + list(_broadcast_dags(62, 150))
     graphs += [configs.layernorm_graph(16, 64), configs.layernorm_shared_graph(16, 64)]
-    graphs += list(_gather_dags(60, 150))
+    graphs += list(_gather_dags(60, 150)) + list(_tuple_dags(59, 100))
     n_ok = n_bad = 0
     for g in graphs:
         n = len(g.ops)
@@ -407,6 +407,7 @@ def test_search_matches_the_oracle():
     graphs = [configs.layernorm_shared_graph(16, 64), configs.layernorm_graph(16, 64),
               configs.c3_graph(8, 64, head_op=True), configs.c2_graph(4, 16)]
     graphs += list(_f32_reduce_dags(63, 25)) + list(_broadcast_dags(64, 25)) + list(_gather_dags(65, 25))
+    graphs += list(_tuple_dags(66, 25))
     for k, g in enumerate(graphs):
         for seed in (1, 2):
             plan, st = gtf.search(g, _lib_bytes_cost, seed=seed, max_stall=200)

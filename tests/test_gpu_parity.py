@@ -578,6 +578,14 @@ def test_empty_and_degenerate_shapes():
     ins = configs.c3_inputs(g)
     _, got = gpu_run(g, ins)
     assert np.all(got[_out(g)] == 0.0)
+    # a tuple of two transposed fields with no rows, fused and unfused
+    from tests.test_capi_host import _tuple_dags
+    for g in _tuple_dags(85, 12, 0, 5, 3):
+        announce("empty tuple dag", [(o.op, o.inputs) for o in g.ops])
+        for fuse in (True, False):
+            plan, got = gpu_run(g, _inputs_for(g, 1990), fuse=fuse)
+            for t in g.outputs():
+                assert got[t].size == 0
 
 
 def test_misaligned_views_take_the_scalar_path():
@@ -1055,6 +1063,32 @@ def test_random_grouped_plans_run_correctly():
                 _check_program(gg, plan, _inputs_for(gg, 800 + gi))
                 n += 1
     assert n >= 100
+
+
+def test_random_grouped_tuple_plans_run_correctly():
+    """Random valid groupings of tuple graphs (moves folded into a join
+    only where the grouping puts them with it) through
+    fuse_plan_create_grouped, and a byte-cost search's best plan, against
+    the oracle on the same program and grouping."""
+    from oracle import search as osr
+    from tests.test_capi_host import _lib_bytes_cost, _tuple_dags
+    rng = np.random.default_rng(93)
+    n = 0
+    for gi, g in enumerate(_tuple_dags(84, 40, 40, 24, 7)):
+        m = len(g.ops)
+        for _ in range(8):
+            lab = [int(x) for x in rng.integers(0, max(1, m // 2 + 1), size=m)]
+            if not osr.plan_ok(g, lab, cap.group_ok):
+                continue
+            plan = gtf.FusePlan.grouped(g, lab)
+            announce("grouped tuple", gi, lab)
+            _check_program(g, plan, _inputs_for(g, 1960 + gi))
+            n += 1
+        if gi % 4 == 0:
+            plan, _ = gtf.search(g, _lib_bytes_cost, seed=gi, max_stall=60)
+            announce("searched tuple", gi, plan.groups())
+            _check_program(g, plan, _inputs_for(g, 1980 + gi))
+    assert n >= 40
 
 
 def _measured_cost(g, reps=5):

@@ -257,3 +257,23 @@ def test_tuple_of_transposes_is_one_concat_load():
     assert names[0] == "LDC_BF16_A" and not any(n.startswith("LDG") or n == "LDT_A" for n in names), names
     code = plan.code(0)
     assert sorted(zip(code["rstride"], code["cstride"]))[:2] == [(1, 40), (1, 40)]
+
+
+def test_grouped_and_searched_tuple_plans():
+    """Random valid groupings of tuple graphs and byte-cost search results
+    replay to the oracle's values on the same program and grouping."""
+    from oracle import search as osr
+    from tests.test_capi_host import _lib_bytes_cost, _tuple_dags
+    rng = np.random.default_rng(93)
+    n = 0
+    for gi, g in enumerate(_tuple_dags(84, 40, 40, 24, 7)):
+        m = len(g.ops)
+        for _ in range(8):
+            lab = [int(x) for x in rng.integers(0, max(1, m // 2 + 1), size=m)]
+            if osr.plan_ok(g, lab, cap.group_ok):
+                check(g, _inputs_for(g, 1960 + gi), plan=gtf.FusePlan.grouped(g, lab))
+                n += 1
+        if gi % 4 == 0:
+            plan, _ = gtf.search(g, _lib_bytes_cost, seed=gi, max_stall=60)
+            check(g, _inputs_for(g, 1980 + gi), plan=plan)
+    assert n >= 40
