@@ -311,7 +311,7 @@ typedef struct {
                              and no reduction runs flat as 1 x numel        */
   int64_t items;          /* work items = row blocks x column panels        */
   int32_t panels;         /* column panels (staged in LDS one at a time)    */
-  int32_t rows_per_item;
+  int32_t rows_per_item;  /* one or two passes of 256 / threads_per_row rows */
   int32_t panel_width;    /* columns per panel, a multiple of 8             */
   int32_t threads_per_row;
   int32_t subtiles;       /* 8-element sub-tiles a lane holds per dispatched
