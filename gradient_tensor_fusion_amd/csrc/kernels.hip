@@ -1056,7 +1056,8 @@ exec_kernel(const ExecArgs a_in) {
       ptrs = (SlotPtr*)(a.m_ptrs + (int64_t)mi.set * a.n_slots);
       vmask = a.m_vec[mi.set];
     } else {
-      rb = item / a.n_panels;
+      // (one panel: no division)
+      rb = a.n_panels == 1 ? item : item / a.n_panels;
       p = (int)(item - rb * a.n_panels);
       r0 = rb * a.RB;
       nr = (int)min((int64_t)a.RB, a.R - r0);
@@ -1065,9 +1066,11 @@ exec_kernel(const ExecArgs a_in) {
     }
 
     const bool col_now = a.n_col > 0 && (a.n_panels > 1 || !staged);
-    const int npass = (nr + rpp - 1) / rpp;
-    const int tpl = max(1, (nc + ks - 1) / ks);  // sub-tiles per lane per row
-    const int spl = (tpl + K - 1) / K;           // runs of K per lane per row
+    // rpp and ks are powers of two: shifts, not divisions
+    static_assert(kBlock == 256 && kV == 8, "the shifts below take log2(kBlock) = 8, log2(kV) = 3");
+    const int npass = (nr + rpp - 1) >> (8 - a.tpr_log2);
+    const int tpl = max(1, (nc + ks - 1) >> (a.tpr_log2 + 3));  // sub-tiles per lane per row
+    const int spl = (tpl + K - 1) / K;                          // runs of K per lane per row
     const int nq = npass * spl;
     // later stages write LDS row slots that the previous item's last stage
     // may still be reading
