@@ -1161,19 +1161,22 @@ exec_kernel(const ExecArgs a_in) {
       // reduce tail after the last run of a row, then advance (pass, s)
       auto finish = [&](int rr) {
         if (S.red && s == spl - 1) {
-          const int w = here(min(tpr, 64));
+          // the tail's derived values are made here, at each use, rather
+          // than hoisted to the item and held in SGPRs (spilled) over it
+          const int tp = here(tpr);
+          const int w = min(tp, 64);
           RowAcc r = acc;
           const bool paired = !TR && S.red >= 4;  // the staged-transpose instance runs no reductions
           if (paired && S.red == 4) r = segment_pair<4>(acc, w);
           else if (paired) r = segment_pair<5>(acc, w);
           else r.a = S.red == 3 ? segment_reduce<true>(acc.a, w) : segment_reduce<false>(acc.a, w);
           acc = ident;
-          if (tpr > 64) {
+          if (tp > 64) {
             // rows wider than a wave: combine the per-wave results through
             // LDS in a fixed order (every lane of a wave holds the same
             // result and writes it; every lane reads those of its own row)
-            const int wpr = tpr >> 6;  // waves per row
-            float* cell = lds_red + (tid >> 6) * 3;
+            const int wpr = tp >> 6;  // waves per row
+            float* cell = lds_red + (here_lane(tid) >> 6) * 3;
             cell[0] = r.a;
             cell[1] = r.b;
             cell[2] = r.c;
@@ -1188,8 +1191,8 @@ exec_kernel(const ExecArgs a_in) {
             }
             r = tot;
           }
-          store_reduced(a, S, lds_row, r0 + rr, rr, r, lt == 0 && rr < nr);
-          if (tpr > 64) __syncthreads();
+          store_reduced(a, S, lds_row, r0 + rr, rr, r, here_lane(lt) == 0 && rr < here(nr));
+          if (tp > 64) __syncthreads();
         }
         if (++s == spl) {
           s = 0;
