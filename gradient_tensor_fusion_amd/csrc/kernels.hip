@@ -1133,7 +1133,7 @@ exec_kernel(const ExecArgs a_in) {
           }
         }
         if (st == 0 && col_now) {
-          for (int c = tid * kV; c < nc; c += kBlock * kV) {
+          for (int c = here_lane(tid) * kV; c < nc; c += kBlock * kV) {
             const int cnt = min(kV, nc - c);
             Tile t{0, c0 + c, 0, c, 0, cnt, 0, true, cnt == kV, ptrs, vmask};
             interpret<kV, M_COL, false, NS>(a, col_prog, a.n_col, t, lds_col, lds_row, dummy, rb == 0);
@@ -1141,7 +1141,7 @@ exec_kernel(const ExecArgs a_in) {
           staged = true;
         }
         if (row_now) {
-          for (int r = kBlock - 1 - tid; r < nr; r += kBlock) {
+          for (int r = kBlock - 1 - here_lane(tid); r < nr; r += kBlock) {
             Tile t{r0 + r, 0, 0, 0, r, 1, 0, false, false, ptrs, vmask};
             interpret<1, M_ROW, false, NS>(a, a.prog + S.row_off, S.row_len, t, lds_col, lds_row,
                                            dummy, p == 0);
