@@ -822,15 +822,16 @@ def run_ln(torch, gtf, configs, args, res, gen):
         return res
     rr = out["row_resident"]
     tj = read_traffic("exec_kernel", "ln")
+    bound, vf = one_launch_bound("ln", rr["gbs"], rr["ms_per_step"])
     res.update({"value": rr["gbs"], "ms_per_step": rr["ms_per_step"], "dtype": "bf16",
                 "config": {"workload": "ln: LayerNorm bf16[8192,1024] with bf16 gamma/beta[1024], "
                                        "one row-resident launch",
                            "bytes_per_step": rr["bytes"]},
-                "roofline": {"bound": "hbm", "achieved": rr["gbs"], "peak": PEAK_GBS, "unit": "GB/s",
+                "roofline": {"bound": bound, "achieved": rr["gbs"], "peak": PEAK_GBS, "unit": "GB/s",
                              "frac": round(rr["gbs"] / PEAK_GBS, 4),
                              "traffic": tj["bytes_per_launch"] if tj else None,
                              "kernel": "exec_kernel", "avg_launch_us": round(rr["ms_per_step"] * 1e3, 3),
-                             "algorithmic_bytes_per_launch": rr["bytes"]},
+                             "algorithmic_bytes_per_launch": rr["bytes"], "valu_frac": vf},
                 "copy_kernel_gbs": round(copy_gbs, 1),
                 "timing": "graph replays over the rotation sets",
                 "speedup_vs_tvm_groups": round(out["tvm_groups"]["ms_per_step"] / rr["ms_per_step"], 3),
@@ -878,14 +879,15 @@ def run_softmax(torch, gtf, configs, args, res, gen):
         return res
     rr = out["row_resident"]
     tj = read_traffic("exec_kernel", "softmax")
+    bound, vf = one_launch_bound("softmax", rr["gbs"], rr["ms_per_step"])
     res.update({"value": rr["gbs"], "ms_per_step": rr["ms_per_step"], "dtype": "bf16",
                 "config": {"workload": "softmax: row softmax bf16[131072,128], one row-resident "
                                        "launch", "bytes_per_step": rr["bytes"]},
-                "roofline": {"bound": "hbm", "achieved": rr["gbs"], "peak": PEAK_GBS, "unit": "GB/s",
+                "roofline": {"bound": bound, "achieved": rr["gbs"], "peak": PEAK_GBS, "unit": "GB/s",
                              "frac": round(rr["gbs"] / PEAK_GBS, 4),
                              "traffic": tj["bytes_per_launch"] if tj else None,
                              "kernel": "exec_kernel", "avg_launch_us": round(rr["ms_per_step"] * 1e3, 3),
-                             "algorithmic_bytes_per_launch": rr["bytes"]},
+                             "algorithmic_bytes_per_launch": rr["bytes"], "valu_frac": vf},
                 "copy_kernel_gbs": round(copy_gbs, 1),
                 "timing": "graph replays over the rotation sets",
                 "speedup_vs_tvm_groups": round(out["tvm_groups"]["ms_per_step"] / rr["ms_per_step"], 3),
@@ -963,7 +965,8 @@ def valu_file(workload):
 
 def valu_cmd(workload):
     run = ("--workload groups" if workload == "c5" else
-           f"--workload {workload} --steps 3 --warmup 1 --no-baselines --no-cpu-baseline")
+           f"--workload {workload} --steps 3 --warmup 1 --no-baselines --no-cpu-baseline"
+           + (" --ln-variant row_resident" if workload in ("ln", "softmax") else ""))
     return ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc SQ_INSTS_VALU SQ_WAVES "
             f"-d $OUT/pmc_valu -o valu --output-format csv -- python3 $R/bench.py {run}")
 
@@ -1018,6 +1021,18 @@ def _summary_json(path):
         return None
     tj = json.loads(js[-1])
     return tj if tj.get("source_hash") == _kernel_hash() else None
+
+
+def one_launch_bound(workload, gbs, ms):
+    """(bound, VALU fraction) of a workload whose step is one exec_kernel
+    launch: the larger of its HBM fraction and its VALU lane-instruction
+    rate (committed SQ_INSTS_VALU summary of these sources) against the
+    issue peak; (None, None) without a current summary."""
+    valu = read_valu(workload)
+    if not valu or "exec_kernel" not in valu:
+        return None, None
+    vf = valu["exec_kernel"] / (ms * 1e-3) / VALU_PEAK
+    return ("alu" if vf > gbs / PEAK_GBS else "hbm"), round(vf, 4)
 
 
 def read_valu(workload="c5"):
