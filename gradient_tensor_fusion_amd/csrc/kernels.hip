@@ -1259,7 +1259,8 @@ template __global__ void exec_kernel<1, kNS, false>(const ExecArgs a);
 // a few head elements bring the destination to a 16-byte boundary, the body
 // moves 16 bytes per lane per step, and a tail finishes.  The body's loads
 // and stores are nontemporal: every byte is read once and written once (on
-// this part nontemporal stores took the C5 buckets from 5.3 to 5.7 TB/s).
+// this part nontemporal stores took the packing of 194 gradients, 151M fp32
+// elements, from 5.3 to 5.7 TB/s).
 template <typename T>
 __device__ __forceinline__ T scale_elem(T v, float s, bool one);
 
