@@ -6,8 +6,9 @@ The stated bars fix what the library may differ by, op by op:
     relu, the immediate forms, add3, dmul, copy and the data movements) are
     correctly rounded on both sides: given identical operands the results
     are identical, so they add no error of their own -- only, once their
-    operands already differ, the propagated difference and one fp32 ulp of
-    rounding that may land on the other side;
+    operands already differ, the propagated difference and one fp32 ulp per
+    rounding that may land on the other side (add3, (a + b) + c, rounds
+    twice: one ulp of a + b and one of the result);
   * exp, tanh, sigmoid and gelu add at most 1e-6 of the oracle's value (the
     elementwise fp32 bar), plus a few units of fp32's smallest subnormal,
     where 1e-6 of a subnormal is below the format's resolution;
@@ -137,7 +138,10 @@ def run_with_bounds(graph, inputs, groups):
                 if o.op in TRANSCENDENTAL:
                     e = prop + REL * (np.abs(out) + prop) + TINY
                 else:
-                    e = prop + np.where(prop > 0, _ulp32(out), 0.0)
+                    r = _ulp32(out)
+                    if o.op == "add3":   # (a + b) is rounded before c is added
+                        r = r + _ulp32(np.abs(a[0]) + np.abs(a[1]))
+                    e = prop + np.where(prop > 0, r, 0.0)
         e = np.where(np.isfinite(out), np.asarray(e, dtype=np.float64), 0.0)
         b_raw[o.output] = e
         d = graph.tensors[o.output]
