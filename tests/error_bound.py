@@ -49,8 +49,11 @@ def _ulp_bf16(v):
 
 
 def _sigmoid_d(z):
-    s = 1.0 / (1.0 + np.exp(-z))
-    return s * (1.0 - s)
+    # sigmoid'(z) = e / (1 + e)^2 with e = exp(-|z|): no 1 - s, which is 0
+    # in float64 from |z| ~ 37 on while the derivative is still ~1e-16 there
+    # and, against sigmoid's own tiny tail values, far from negligible
+    e = np.exp(-np.abs(z))
+    return e / (1.0 + e) ** 2
 
 
 def _propagate(op, a, b, imm, out_shape):

@@ -142,3 +142,24 @@ def test_a_row_sum_outside_its_bar_is_caught():
         bad = _fake_run(g, ins)
     with pytest.raises(AssertionError):
         _check_all(g, ins, bad)
+
+
+def test_sigmoid_and_add3_bounds_in_the_tails():
+    """The derivative bound of sigmoid stays positive far in the tail (where
+    sigmoid itself is tiny but not 0), and add3's bound counts the rounding
+    of a + b as well as the result's."""
+    from tests.error_bound import _sigmoid_d, _propagate, _ulp32
+    z = np.array([0.0, 10.0, 40.0, 64.5, 100.0])
+    assert np.allclose(_sigmoid_d(z), np.exp(-z) / (1 + np.exp(-z)) ** 2, rtol=1e-12, atol=0)
+    assert (_sigmoid_d(z) > 0).all() and _sigmoid_d(64.5) == pytest.approx(np.exp(-64.5), rel=1e-12)
+    # a graph whose add3 reads a value already off by a little
+    g = Graph()
+    x0 = g.input("x0", "f32", (1, 1))
+    x1 = g.input("x1", "f32", (1, 1))
+    t = g.op("exp", [x0], "t", "f32", (1, 1))
+    g.op("add3", [x1, t, x0], "y", "f32", (1, 1), role="out")
+    ins = {x0: np.full((1, 1), -4.0, np.float32), x1: np.full((1, 1), -0.34, np.float32)}
+    vals, bound = run_with_bounds(g, ins, [[0], [1]])
+    y = g.outputs()[0]
+    a_plus_b = abs(-0.34) + float(np.exp(-4.0))
+    assert bound[y][0, 0] >= float(_ulp32(vals[y])[0, 0] + _ulp32(np.array(a_plus_b))), bound[y]
