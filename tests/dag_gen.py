@@ -27,6 +27,11 @@ def _gelu(x):
     return 0.5 * x * math.erfc(-x / math.sqrt(2.0))
 
 
+def _sigmoid(x):
+    # no exp of a large positive argument (an overflow in math.exp)
+    return 1 / (1 + math.exp(-x)) if x >= 0 else math.exp(x) / (1 + math.exp(x))
+
+
 def result_range(op, ranges, imm=0.0):
     """(lo, hi) of the op's result over its operands' intervals, or None
     when the op is not safe there."""
@@ -37,7 +42,7 @@ def result_range(op, ranges, imm=0.0):
         elif op == "tanh":
             r = (math.tanh(lo), math.tanh(hi))
         elif op == "sigmoid":
-            r = (1 / (1 + math.exp(-lo)), 1 / (1 + math.exp(-hi)))
+            r = (_sigmoid(lo), _sigmoid(hi))
         elif op == "relu":
             r = (max(lo, 0.0), max(hi, 0.0))
         elif op == "gelu":
