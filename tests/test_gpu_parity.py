@@ -424,6 +424,31 @@ def test_random_dags_over_every_opcode():
     assert n == 480
 
 
+@pytest.mark.parametrize("n_ops", [8, 12, 16])
+def test_random_dags_with_more_ops(n_ops):
+    """Longer DAGs over every elementwise opcode (values that pass through
+    several transcendentals and roundings before a group reads them), at a
+    shape of several row blocks with a ragged panel, fused and unfused."""
+    from tests import dag_gen
+    for gi, g in enumerate(dag_gen.random_dags(2500 + n_ops, 40, n_ops)):
+        gg = _reshape(g, 37, 1000)
+        announce("dag", n_ops, gi)
+        _check_graph(gg, _inputs_for(gg, 2600 + gi))
+
+
+def test_bound_regressions():
+    """Two graphs on which the GPU stays within every stated bar but the
+    per-element bound was once tighter than the bars allow: add3 reading a
+    GELU value (the rounding of a + b tipped by an in-bar difference) and
+    sigmoid far in its tail reading exp(exp(x)) (its derivative bound had
+    cancelled to 0)."""
+    from tests import dag_gen
+    for seed, n_ops, k in ((948, 8, 0), (952, 12, 9)):
+        g = list(dag_gen.random_dags(seed, 10, n_ops))[k]
+        gg = _reshape(g, 37, 1000)
+        _check_graph(gg, _inputs_for(gg, 3000 + k))
+
+
 def test_random_broadcast_dags():
     for gi, g in enumerate(_broadcast_dags(7, 60)):
         for R, C in [(3, 5), (2, 67), (5, 130), (1, 9)]:
