@@ -163,7 +163,8 @@ def assert_within(got, want_vals, bound, dtype, what=""):
     w = np.asarray(want_vals, dtype=np.float64)
     bnd = np.broadcast_to(bound, w.shape)
     same = (g == w) | (np.isnan(g) & np.isnan(w))
-    err = np.where(same, 0.0, np.abs(g - w))
+    with np.errstate(invalid="ignore"):   # inf - inf where both are the same infinity
+        err = np.where(same, 0.0, np.abs(g - w))
     bad = ~(err <= bnd)
     if bad.any():
         i = tuple(int(k) for k in np.argwhere(bad)[0])
