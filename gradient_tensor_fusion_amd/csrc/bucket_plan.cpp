@@ -6,7 +6,7 @@
 // AllReduce combiner passage in section 1, Horovod's fusion threshold in
 // section 7).  Buckets are filled next-fit in production order with dense
 // offsets; the chunk table then cuts every tensor into runs of at most
-// kChunkElems elements so one launch balances tensors of any size.
+// kChunkBytes bytes so one launch balances tensors of any size.
 #include <algorithm>
 
 #include "gtf.h"
@@ -51,12 +51,13 @@ int build_bucket_plan(BucketPlan* b) {
     L.b1 = b->bucket_of[t1 - 1];
     L.c0 = (int64_t)b->chunks.size();
     const int nt = t1 - t0;
+    const int64_t per_chunk = kChunkBytes / eb;
     for (int i = t0; i < t1; ++i) {
-      for (int64_t s = 0; s < b->numel[i]; s += kChunkElems) {
+      for (int64_t s = 0; s < b->numel[i]; s += per_chunk) {
         Chunk c;
         c.t_off = s;
         c.b_off = b->offset[i] + s;
-        c.n = (int32_t)std::min<int64_t>(kChunkElems, b->numel[i] - s);
+        c.n = (int32_t)std::min<int64_t>(per_chunk, b->numel[i] - s);
         c.t_slot = (uint16_t)(i - t0);
         c.b_slot = (uint16_t)(nt + (b->bucket_of[i] - L.b0));
         b->chunks.push_back(c);

@@ -172,8 +172,10 @@ struct ExecArgs {
 
 static_assert(sizeof(ExecArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
-// Bucket chunk: a run of at most kChunkElems elements of one tensor.
-constexpr int kChunkElems = 16384;
+// Bucket chunk: a run of one tensor of at most kChunkBytes bytes (4096 fp32
+// or 8192 bf16 elements), what one workgroup of the bucket kernel moves
+// with all of its loads in flight together.
+constexpr int kChunkBytes = 16384;
 constexpr int kMaxBucketPtrs = 256;  // tensor + bucket pointers per launch
 
 struct Chunk {

@@ -1253,14 +1253,18 @@ template __global__ void exec_kernel<kWideK, kWideNS, false>(const ExecArgs a);
 template __global__ void exec_kernel<1, kNS, false>(const ExecArgs a);
 
 // ---------------------------------------------------------------- buckets
-// One workgroup per chunk: a run of up to kChunkElems elements of one tensor
+// One workgroup per chunk: a run of up to kChunkBytes bytes of one tensor
 // copied to or from its place in its bucket, times the scale.  The side that
 // lives in the bucket is usually not 16-byte aligned (offsets are dense), so
 // a few head elements bring the destination to a 16-byte boundary, the body
-// moves 16 bytes per lane per step, and a tail finishes.  The body's loads
-// and stores are nontemporal: every byte is read once and written once (on
-// this part nontemporal stores took the packing of 194 gradients, 151M fp32
-// elements, from 5.3 to 5.7 TB/s).
+// moves 16 bytes per lane per step, and a tail finishes.  A whole chunk's
+// body is one round of kU loads per thread, all in flight before the first
+// store, and the workgroup then exits: on this part one short-lived
+// workgroup per 16 KiB moved faster than workgroups that loop (the packing
+// of 194 gradients, 151M fp32 elements, 5.7 -> 6.2 TB/s against 64 KiB
+// chunks in rounds of four).  The body's loads and stores are nontemporal:
+// every byte is read once and written once (nontemporal stores took the
+// same packing from 5.3 to 5.7 TB/s).
 template <typename T>
 __device__ __forceinline__ T scale_elem(T v, float s, bool one);
 
@@ -1302,7 +1306,8 @@ template <typename T>
 __device__ __forceinline__ void move_run(T* __restrict__ dst, const T* __restrict__ src, int n,
                                          float s) {
   constexpr int per16 = 16 / sizeof(T);
-  constexpr int kU = 4;  // 16-byte moves in flight per thread
+  constexpr int kU = kChunkBytes / (16 * kBlock);  // 16-byte moves per thread per round
+  static_assert(kU * 16 * kBlock == kChunkBytes, "a chunk's body is whole rounds of the workgroup");
   const bool one = s == 1.0f;
   const int tid = threadIdx.x;
   int head = (int)(((16 - ((uintptr_t)dst & 15)) & 15) / sizeof(T));
@@ -1311,20 +1316,20 @@ __device__ __forceinline__ void move_run(T* __restrict__ dst, const T* __restric
   const int body = (n - head) / per16;
   T* d = dst + head;
   const T* q = src + head;
-  int u = tid;
-  for (; u + (kU - 1) * kBlock < body; u += kU * kBlock) {
+  // rounds of kU words per thread (one round for a chunk of kChunkBytes),
+  // each word predicated, so a thread's loads are all in flight together
+  for (int u = tid; u < body; u += kU * kBlock) {
     uint4 w[kU];
 #pragma unroll
-    for (int j = 0; j < kU; ++j) w[j] = load16(q + (size_t)(u + j * kBlock) * per16);
+    for (int j = 0; j < kU; ++j)
+      if (u + j * kBlock < body) w[j] = load16(q + (size_t)(u + j * kBlock) * per16);
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
-      const uint4 o = scale_vec<T>(w[j], s, one);
-      __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, (v4u*)(d + (size_t)(u + j * kBlock) * per16));
+      if (u + j * kBlock < body) {
+        const uint4 o = scale_vec<T>(w[j], s, one);
+        __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, (v4u*)(d + (size_t)(u + j * kBlock) * per16));
+      }
     }
-  }
-  for (; u < body; u += kBlock) {
-    const uint4 o = scale_vec<T>(load16(q + (size_t)u * per16), s, one);
-    __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, (v4u*)(d + (size_t)u * per16));
   }
   const int done = head + body * per16;
   const int tail = n - done;
@@ -1349,9 +1354,10 @@ __global__ void __launch_bounds__(kBlock) bucket_kernel(const BucketArgs a) {
 }
 
 // Plain copy of n16 16-byte words, streamed past the caches: each thread
-// has kCopyUnroll loads in flight before it stores; the last partial round
-// is predicated.
-constexpr int kCopyUnroll = 4;
+// has kCopyUnroll loads in flight before it stores, and the grid gives each
+// workgroup one span of kBlock * kCopyUnroll words (the fastest copy of the
+// streaming probes below); the last partial round is predicated.
+constexpr int kCopyUnroll = 8;
 __global__ void __launch_bounds__(kBlock) copy_kernel(uint4* __restrict__ dst,
                                                       const uint4* __restrict__ src, size_t n16) {
   const size_t span = (size_t)kBlock * kCopyUnroll;
@@ -1595,7 +1601,7 @@ int launch_bucket(const BucketPlan& b, const void* const* tens, void* const* bk,
 // hipGetSymbolAddress (with that device current) and only that address is
 // ever handed to a kernel or a copy.  Every call on one GPU shares the one
 // array, so calls that overlap on a GPU race.
-constexpr size_t kStaticChunkBytes = size_t(1) << 20;  // 43,690 chunks of <= 16384 elements
+constexpr size_t kStaticChunkBytes = size_t(1) << 20;  // 43,690 chunks of <= 16 KiB
 static __device__ __align__(256) unsigned char scratch[kStaticChunkBytes];
 
 namespace {
@@ -1683,15 +1689,11 @@ int launch_stream_probe(int kind, int depth, int nontemporal, int grid_per_cu, v
 int launch_copy(void* dst, const void* src, size_t nbytes, hipStream_t stream) {
   const size_t n16 = nbytes / 16;
   if (n16 == 0) return GTF_OK;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   size_t grid = (n16 + (size_t)kBlock * kCopyUnroll - 1) / ((size_t)kBlock * kCopyUnroll);
-  const size_t cap = (size_t)device_cus(dev) * 8;
-  if (grid > cap) grid = cap;
+  if (grid > 0x7fffffffu) grid = 0x7fffffffu;  // the kernel's loop covers the rest
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream, (uint4*)dst,
                      (const uint4*)src, n16);
-  e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "copy_kernel launch");
   return GTF_OK;
 }

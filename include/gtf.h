@@ -488,7 +488,8 @@ int bucket_unpack_per_tensor(const gtf_bucket_plan* plan, const void* const* buc
  * results as bucket_pack.
  * Errors: GTF_E_INVALID (NULL plan or pointer arrays, NULL tensor or bucket
  * pointer of nonzero size), GTF_E_LIMIT (a chunk table over 1 MiB: more
- * than 43,690 chunks of at most 16384 elements), GTF_E_HIP. */
+ * than 43,690 chunks of at most 16 KiB of payload each, so at most about
+ * 179M fp32 or 358M bf16 elements), GTF_E_HIP. */
 int bucket_pack_static(const gtf_bucket_plan* plan, const void* const* src, void* const* buckets,
                        float scale, void* hip_stream);
 

@@ -245,7 +245,8 @@ def test_bucket_plans_match_the_oracle():
     for numel, eb, cap in cases:
         bp = gtf.BucketPlan(numel, "f32" if eb == 4 else "bf16", cap)
         assert bp.query() == obucket.plan(numel, eb, cap)
-        chunks = sum((n + 16383) // 16384 for n in numel)
+        per = 16384 // eb  # a chunk carries at most 16 KiB
+        chunks = sum((n + per - 1) // per for n in numel)
         assert bp.workspace_bytes == 24 * chunks
 
 

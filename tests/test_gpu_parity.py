@@ -190,6 +190,60 @@ def test_bucket_bf16_pack():
         assert_bits_equal(seg, want)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bucket_sizes_around_chunk_boundaries(dtype):
+    """Tensors one element short of, at and past whole chunks (16 KiB of
+    payload: 4096 fp32 or 8192 bf16 elements), behind odd-sized neighbours so
+    their bucket offsets take every misalignment: packed x 0.25 to the
+    oracle's bits at the oracle's offsets, unpacked x 1 back bit for bit."""
+    per = 16384 // (4 if dtype == "f32" else 2)
+    numel = [1, per - 1, 3, per, 2, per + 1, 5, 2 * per - 3, 7, 2 * per, 1, 3 * per + 5, 0, per + 7]
+    eb = 4 if dtype == "f32" else 2
+    cap = 4 * per * eb
+    vals = configs.gradient_values(numel, 47)
+    if dtype == "f32":
+        host = [v.astype(np.float32) for v in vals]
+    else:
+        host = [configs.to_bf16_bits(v.astype(np.float64) * 1e3) for v in vals]
+    dev = [to_device(h, dtype) for h in host]
+    bp = gtf.BucketPlan(numel, dtype, cap)
+    bof, off, bn = bp.query()
+    assert (bof, off, bn) == obucket.plan(numel, eb, cap)
+    ws = torch.empty(max(16, bp.workspace_bytes), dtype=torch.uint8, device="cuda")
+    bp.bind(ws)
+    tdt = torch.float32 if dtype == "f32" else torch.int16
+    bks = [torch.zeros((n,), dtype=tdt, device="cuda") for n in bn]
+    bp.pack(dev, bks, 0.25)
+    outs = [torch.zeros((n,), dtype=tdt, device="cuda") for n in numel]
+    bp.unpack(bks, outs, 1.0)
+    torch.cuda.synchronize()
+    if dtype == "f32":
+        want = obucket.pack(numel, 4, cap, host, 0.25)
+        for a, b in zip(bks, want):
+            assert_bits_equal(a.cpu().numpy(), b)
+    else:
+        for i, n in enumerate(numel):
+            seg = bks[bof[i]].cpu().numpy().view(np.uint16)[off[i]:off[i] + n]
+            assert_bits_equal(seg, numerics.f32_to_bf16(numerics.bf16_to_f32(host[i]) * np.float32(0.25)))
+    for i, o in enumerate(outs):
+        seg = bks[bof[i]][off[i]:off[i] + numel[i]]
+        assert_bits_equal(o.cpu().numpy(), seg.cpu().numpy())
+
+
+@pytest.mark.parametrize("n16", [1, 255, 2048, 2049, 3 * 2048 + 77, 1 << 20])
+def test_device_copy_bit_exact(n16):
+    """The measurement copy kernel: whole spans of 2048 16-byte words per
+    workgroup, a partial last span, and a single word, copied bit for bit
+    without touching the word after the end."""
+    src = torch.randint(-(1 << 31), (1 << 31) - 1, (4 * n16,), dtype=torch.int32, device="cuda")
+    dst = torch.full((4 * n16 + 4,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    gtf.device_copy(dst, src, 16 * n16)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy()
+    assert np.array_equal(got[:4 * n16], src.cpu().numpy())
+    assert np.all(got[4 * n16:] == 0x5A5A5A5A)
+
+
 # ---------------------------------------------------------------- c5
 @pytest.mark.parametrize("rows,hidden", [(8192, 1024), (37, 1024), (16, 264), (3, 5)])
 def test_c5_layernorm_group_by_group(rows, hidden):
