@@ -230,6 +230,34 @@ def test_bucket_sizes_around_chunk_boundaries(dtype):
         assert_bits_equal(o.cpu().numpy(), seg.cpu().numpy())
 
 
+@pytest.mark.parametrize("reuse_x", [False, True])
+def test_flat_group_with_more_items_than_resident_workgroups(reuse_x):
+    """A flat group (no broadcast, no reduction) of 8192 x 4096 fp32
+    elements: 4096 items, more than the workgroups resident at once, each
+    taken by a workgroup of its own; relu(x * y), and relu(x * y) - x,
+    which holds x in a spill slot (the executor instance with slots).
+    IEEE-only ops, so every element is checked bit for bit against the
+    oracle, not a sample."""
+    g = Graph()
+    x = g.input("x", "f32", (8192, 4096))
+    y = g.input("y", "f32", (8192, 4096))
+    m = g.op("mul", [x, y], "m", "f32", (8192, 4096))
+    if reuse_x:
+        r = g.op("relu", [m], "r", "f32", (8192, 4096))
+        g.op("sub", [r, x], "out", "f32", (8192, 4096), role="out")
+    else:
+        g.op("relu", [m], "out", "f32", (8192, 4096), role="out")
+    ins = _inputs_for(g, 310)
+    plan = gtf.FusePlan(g)
+    assert plan.num_groups == 1
+    geo = plan.geometry(0)
+    assert geo["items"] == 4096 and (geo["spill_slots"] > 0) == reuse_x, geo
+    _, got = gpu_run(g, ins, plan=plan)
+    _, want = oracle_run(g, ins)
+    o = _out(g)
+    assert_bits_equal(got[o], want[o])
+
+
 @pytest.mark.parametrize("n16", [1, 255, 2048, 2049, 3 * 2048 + 77, 1 << 20])
 def test_device_copy_bit_exact(n16):
     """The measurement copy kernel: whole spans of 2048 16-byte words per
