@@ -1293,8 +1293,11 @@ __device__ __forceinline__ uint4 scale_vec(uint4 w, float s, bool one) {
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-// 16 bytes from a 4-byte aligned address: the run's source side (the
-// destination side is the one the head aligns to 16 bytes).
+// 16 bytes from the run's source side, which is aligned only to its element
+// (4 bytes for fp32, 2 for bf16; the destination side is the one the head
+// aligns to 16 bytes).  The 4-byte alignment the type declares keeps the
+// load one dwordx4; the part's memory system serves such loads at 2-byte
+// alignment too (the bf16 bucket tests put sources at both alignments).
 // Nontemporal: every byte is read once (see ld_nt16).
 typedef unsigned int u4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 __device__ __forceinline__ uint4 load16(const void* p) {
